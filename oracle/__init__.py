@@ -1,0 +1,232 @@
+"""CPU oracle for the MoE router and token dispatch -- TEST INFRASTRUCTURE.
+
+A numpy front end over ``oracle.c`` (plain fp64 C, see ``oracle.h`` for the
+sources it follows).  Only the tests, ``__graft_entry__.smoke()`` and the
+benchmark's CPU-baseline leg may import this package; the HIP library never
+does, and this package never imports the HIP library.
+
+bf16 inputs are numpy ``uint16`` arrays of bf16 bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_SOURCES = [os.path.join(_HERE, "oracle.c")]
+
+SCORE = {"softmax": 0, "sigmoid": 1, "sqrt_softplus": 2, "softmax_topk": 3}
+GROUP = {"max": 0, "top2_sum": 1}
+DTYPE = {"f32": 0, "bf16": 1}
+
+
+def build(verbose: bool = False) -> str:
+    """Compile liboracle.so with gcc (fp64, no fast-math, no FMA contraction)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+           "-Wall", "-Wextra", "-fPIC", "-shared", "-o", _LIB_PATH + ".tmp",
+           *_SOURCES, "-lm", "-lpthread"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
+    global _lib
+    _lib = None
+    return _LIB_PATH
+
+
+class _Params(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("score", ctypes.c_int32), ("n_groups", ctypes.c_int32),
+                ("topk_groups", ctypes.c_int32), ("group_score", ctypes.c_int32),
+                ("renormalize", ctypes.c_int32), ("route_scale", ctypes.c_double)]
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        vp = ctypes.c_void_p
+        i32 = ctypes.c_int32
+        lib.orc_gate.argtypes = [ctypes.POINTER(_Params), vp, vp, vp, vp]
+        lib.orc_gate.restype = None
+        lib.orc_route_logits.argtypes = [ctypes.POINTER(_Params)] + [vp] * 11
+        lib.orc_route_logits.restype = i32
+        lib.orc_weights_for_ids.argtypes = [ctypes.POINTER(_Params), vp, vp, vp]
+        lib.orc_weights_for_ids.restype = None
+        lib.orc_hash_ids.argtypes = [i32, i32, i32, vp, vp, i32, vp]
+        lib.orc_hash_ids.restype = i32
+        lib.orc_dispatch.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp]
+        lib.orc_dispatch.restype = i32
+        lib.orc_maxvio.argtypes = [vp, i32]
+        lib.orc_maxvio.restype = ctypes.c_double
+        lib.orc_route_full.argtypes = [ctypes.POINTER(_Params)] + [vp] * 11 + [i32]
+        lib.orc_route_full.restype = i32
+        _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def _params(T, d, E, k, dtype="f32", score="softmax", n_groups=1, topk_groups=None,
+            group_score="max", renormalize=True, route_scale=1.0):
+    if topk_groups is None:
+        topk_groups = n_groups
+    return _Params(int(T), int(d), int(E), int(k), DTYPE[dtype], SCORE[score],
+                   int(n_groups), int(topk_groups), GROUP[group_score],
+                   int(bool(renormalize)), float(route_scale))
+
+
+def _check_route_args(E, k, n_groups, topk_groups, group_score):
+    if topk_groups is None:
+        topk_groups = n_groups
+    if E < 1 or k < 1:
+        raise ValueError("need E >= 1 and k >= 1")
+    if n_groups < 1 or E % n_groups:
+        raise ValueError("n_groups must divide E")
+    if not 1 <= topk_groups <= n_groups:
+        raise ValueError("need 1 <= topk_groups <= n_groups")
+    if k > topk_groups * (E // n_groups):
+        raise ValueError("k exceeds the experts of the kept groups")
+    if n_groups > 1 and group_score == "top2_sum" and E // n_groups < 2:
+        raise ValueError("top2_sum needs groups of at least 2 experts")
+
+
+def gate(x, W, logit_bias=None, dtype=None):
+    """fp64 logits[T][E] of x[T][d] and W[E][d] (float32, or uint16 = bf16 bits)."""
+    if dtype is None:
+        dtype = "bf16" if x.dtype == np.uint16 else "f32"
+    npdt = np.uint16 if dtype == "bf16" else np.float32
+    x = _c(x, npdt)
+    W = _c(W, npdt)
+    T, d = x.shape
+    E = W.shape[0]
+    assert W.shape[1] == d
+    out = np.empty((T, E), dtype=np.float64)
+    p = _params(T, d, E, 1, dtype)
+    _load().orc_gate(ctypes.byref(p), _ptr(x), _ptr(W), _ptr(_c(logit_bias, np.float32)),
+                     _ptr(out))
+    return out
+
+
+def route_logits(logits, k, score="softmax", select_bias=None, k_per_token=None,
+                 n_groups=1, topk_groups=None, group_score=None, renormalize=True,
+                 route_scale=1.0):
+    """Select and weight from fp64 logits.  Returns a dict with ids, weights,
+    margin_k, margin_g, margin_s, margin_o, q (masked selection quantity),
+    g (group scores) and nbad (tokens with k_t outside [1, k])."""
+    logits = _c(logits, np.float64)
+    T, E = logits.shape
+    if group_score is None:
+        group_score = "top2_sum" if select_bias is not None else "max"
+    _check_route_args(E, k, n_groups, topk_groups, group_score)
+    p = _params(T, 1, E, k, "f32", score, n_groups, topk_groups, group_score,
+                renormalize, route_scale)
+    ids = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float64)
+    mk, mg, ms, mo = (np.empty(T, np.float64) for _ in range(4))
+    q = np.empty((T, E), np.float64)
+    g = np.empty((T, n_groups), np.float64)
+    nbad = _load().orc_route_logits(
+        ctypes.byref(p), _ptr(logits), _ptr(_c(select_bias, np.float32)),
+        _ptr(_c(k_per_token, np.int32)), _ptr(ids), _ptr(w), _ptr(mk), _ptr(mg),
+        _ptr(ms), _ptr(mo), _ptr(q), _ptr(g))
+    return {"ids": ids, "weights": w, "margin_k": mk, "margin_g": mg,
+            "margin_s": ms, "margin_o": mo, "q": q, "g": g, "nbad": int(nbad),
+            "logits": logits}
+
+
+def route(x, W, k, logit_bias=None, **kw):
+    """Gate + selection + weights (fp64) for every row of x."""
+    return route_logits(gate(x, W, logit_bias), k, **kw)
+
+
+def weights_for_ids(logits, ids, score="softmax", renormalize=True, route_scale=1.0):
+    logits = _c(logits, np.float64)
+    ids = _c(ids, np.int32)
+    T, E = logits.shape
+    k = ids.shape[1]
+    p = _params(T, 1, E, k, "f32", score, 1, 1, "max", renormalize, route_scale)
+    w = np.empty((T, k), np.float64)
+    _load().orc_weights_for_ids(ctypes.byref(p), _ptr(logits), _ptr(ids), _ptr(w))
+    return w
+
+
+def hash_ids(token_ids, tid2eid, E):
+    """ids[T][k] from a row-major [vocab][k] table; returns (ids, n_errors)."""
+    tok = _c(token_ids, np.int32)
+    tab = _c(tid2eid, np.int32)
+    V, k = tab.shape
+    T = tok.shape[0]
+    ids = np.empty((T, k), np.int32)
+    nerr = _load().orc_hash_ids(T, k, E, _ptr(tok), _ptr(tab), V, _ptr(ids))
+    return ids, int(nerr)
+
+
+def dispatch(ids, E):
+    """Stable counting sort of route indices by expert.
+
+    Returns counts[E], offsets[E+1], perm[offsets[E]], inv[T*k], n_errors."""
+    ids = _c(ids, np.int32)
+    T, ks = ids.shape
+    counts = np.empty(E, np.int32)
+    offsets = np.empty(E + 1, np.int32)
+    perm = np.full(max(T * ks, 1), -1, np.int32)
+    inv = np.empty(max(T * ks, 1), np.int32)
+    nerr = _load().orc_dispatch(_ptr(ids), T, ks, E, _ptr(counts), _ptr(offsets),
+                                _ptr(perm), _ptr(inv))
+    R = int(offsets[E])
+    return {"counts": counts, "offsets": offsets, "perm": perm[:R].copy(),
+            "inv": inv[:T * ks].copy(), "nerr": int(nerr)}
+
+
+def maxvio(counts):
+    c = _c(counts, np.int32)
+    return float(_load().orc_maxvio(_ptr(c), c.shape[0]))
+
+
+def route_full(x, W, k, *, score, logit_bias=None, select_bias=None, k_per_token=None,
+               n_groups=1, topk_groups=None, group_score=None, renormalize=True,
+               route_scale=1.0, nthreads=None):
+    """Whole path (gate + route + dispatch) on nthreads host threads."""
+    dtype = "bf16" if x.dtype == np.uint16 else "f32"
+    npdt = np.uint16 if dtype == "bf16" else np.float32
+    x = _c(x, npdt)
+    W = _c(W, npdt)
+    T, d = x.shape
+    E = W.shape[0]
+    if group_score is None:
+        group_score = "top2_sum" if select_bias is not None else "max"
+    _check_route_args(E, k, n_groups, topk_groups, group_score)
+    if nthreads is None:
+        nthreads = os.cpu_count() or 1
+    p = _params(T, d, E, k, dtype, score, n_groups, topk_groups, group_score,
+                renormalize, route_scale)
+    ids = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float64)
+    counts = np.empty(E, np.int32)
+    offsets = np.empty(E + 1, np.int32)
+    perm = np.empty(max(T * k, 1), np.int32)
+    inv = np.empty(max(T * k, 1), np.int32)
+    nbad = _load().orc_route_full(
+        ctypes.byref(p), _ptr(x), _ptr(W), _ptr(_c(logit_bias, np.float32)),
+        _ptr(_c(select_bias, np.float32)), _ptr(_c(k_per_token, np.int32)), _ptr(ids),
+        _ptr(w), _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(inv), int(nthreads))
+    return {"ids": ids, "weights": w, "counts": counts, "offsets": offsets,
+            "perm": perm[:int(offsets[E])].copy(), "inv": inv[:T * k].copy(),
+            "nbad": int(nbad), "nthreads": int(nthreads)}
