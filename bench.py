@@ -1,0 +1,227 @@
+#!/usr/bin/env python3
+"""Routed tokens/s of the MoE router + dispatch hot path on one MI355X.
+
+One step = moe_route (gate contraction, scoring, selection, weights) followed
+by moe_dispatch (histogram, offsets, permutation, inverse) over one batch of
+seeded synthetic tokens.  Inputs are resident in HBM before timing; each step
+routes a different copy of x (rotating through copies totalling more than the
+256 MB last-level cache) so the gate reads x from HBM, not from cache.
+
+Prints one JSON line with the throughput, the dominant kernel's roofline
+fraction (kernel time from HIP events recorded on the launch stream by the
+library's per-kernel timing) and the CPU oracle's throughput on a bounded
+sample of the same workload.
+
+Usage: python bench.py [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2516.6
+LLC_BYTES = 256 << 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def stage_bytes(w, T, R, R_valid, nt):
+    """Algorithmic HBM bytes per launch of each kernel (inputs read once,
+    outputs written once)."""
+    xb = 2 if w.dtype == "bf16" else 4
+    E, d, k = w.E, w.d, w.k
+    return {
+        "gate": T * d * xb + E * d * xb + T * E * 4,
+        "select": T * E * 4 + T * k * 8 + (T * 4 if w.dynamic_k else 0),
+        "disp_hist": R * 4 + nt * E * 4,
+        "disp_scan": 2 * nt * E * 4 + E * 8,
+        "disp_scatter": R * 4 + nt * E * 4 + R * 4 + R_valid * 4,
+    }
+
+
+def cpu_baseline(w, inp, seconds, threads):
+    """Time the oracle (gate + route + dispatch, fp64) on a bounded sample."""
+    import numpy as np
+
+    import oracle
+    import workloads as wl
+
+    def run(n):
+        sl = np.arange(n)
+        kw = dict(score=w.score, logit_bias=inp["logit_bias"], select_bias=inp["select_bias"],
+                  k_per_token=None if inp["k_per_token"] is None else inp["k_per_token"][:n],
+                  n_groups=w.n_groups, topk_groups=w.topk_groups,
+                  group_score=w.group_score if w.n_groups > 1 else None,
+                  renormalize=w.renormalize, route_scale=w.route_scale, nthreads=threads)
+        t0 = time.perf_counter()
+        oracle.route_full(wl.rows(inp["x"], sl), inp["W"], w.k, **kw)
+        return time.perf_counter() - t0
+
+    n0 = min(w.T, 256)
+    t0 = run(n0)
+    n = int(min(w.T, max(n0, n0 * seconds / max(t0, 1e-6))))
+    t = run(n) if n > n0 else t0
+    return {"value": n / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of {w.T} tokens of the same workload (gate + route + "
+                      f"dispatch, fp64), {t:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="qwen3_dynk")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic", default=None,
+                    help="JSON file with measured FETCH/WRITE bytes per launch of the "
+                         "dominant kernel (from rocprofv3 --pmc)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the router and dispatch run on one device "
+              "(no collectives); run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import token_dispatch_amd as tda
+    import workloads as wl
+
+    w = wl.WORKLOADS[args.workload]
+    if w.hash_vocab:
+        raise SystemExit("bench.py times the learned-router workloads; hash mode is a test case")
+    log(f"[bench] generating {w.name} inputs (T={w.T}, d={w.d}, E={w.E})")
+    inp = wl.make_inputs(w)
+    dev = torch.device("cuda:0")
+
+    def up(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(
+                torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    x0 = up(inp["x"])
+    xbytes = x0.numel() * x0.element_size()
+    n_copies = max(1, min(64, math.ceil(3 * LLC_BYTES / xbytes)))
+    xs = [x0] + [torch.roll(x0, shifts=97 * i, dims=0).contiguous() for i in range(1, n_copies)]
+    W = up(inp["W"])
+    lb, sb, kpt = up(inp["logit_bias"]), up(inp["select_bias"]), up(inp["k_per_token"])
+    T, E, k = w.T, w.E, w.k
+    logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    weights = torch.empty((T, k), dtype=torch.float32, device=dev)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(T * k, dtype=torch.int32, device=dev)
+    inv = torch.empty(T * k, dtype=torch.int32, device=dev)
+    ws = torch.empty(max(1, tda.dispatch_workspace_size(T, k, E)), dtype=torch.uint8, device=dev)
+    rkw = dict(score=w.score, logit_bias=lb, select_bias=sb, k_per_token=kpt,
+               n_groups=w.n_groups, topk_groups=w.topk_groups,
+               group_score=w.group_score if w.n_groups > 1 else None,
+               renormalize=w.renormalize, route_scale=w.route_scale)
+
+    def step(i):
+        tda.route(xs[i % n_copies], W, k, logits=logits, ids=ids, weights=weights, **rkw)
+        tda.dispatch(ids, E, counts=counts, offsets=offsets, perm=perm, inv=inv, workspace=ws)
+
+    log(f"[bench] {n_copies} rotating copies of x ({xbytes / 1e6:.1f} MB each); "
+        f"warmup {args.warmup}, steps {args.steps}")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = ev0.elapsed_time(ev1)
+    ms_per_step = ms_total / args.steps
+    value = T / (ms_per_step / 1e3)
+    log(f"[bench] {ms_per_step * 1e3:.2f} us/step (wall {wall / args.steps * 1e6:.2f} us/step)")
+
+    # per-kernel times from HIP events the library records on the launch stream
+    n_prof = min(args.steps, 100)
+    tda.profile_enable(True)
+    for i in range(n_prof):
+        step(i)
+    torch.cuda.synchronize()
+    prof = tda.profile_read()
+    tda.profile_enable(False)
+
+    R = T * k
+    R_valid = int(counts.sum().item())
+    nt = (R + 1023) // 1024
+    sbytes = stage_bytes(w, T, R, R_valid, nt)
+    stages = {}
+    for name, (ms, n) in prof.items():
+        if n:
+            avg_us = ms / n * 1e3
+            stages[name] = {"avg_us": round(avg_us, 3), "launches": n,
+                            "bytes": sbytes.get(name),
+                            "GBs": round(sbytes[name] / (avg_us * 1e-6) / 1e9, 1)
+                            if name in sbytes else None}
+    dom = max(stages, key=lambda s: stages[s]["avg_us"])
+    dom_us = stages[dom]["avg_us"]
+    achieved = sbytes[dom] / (dom_us * 1e-6) / 1e9
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            traffic = json.load(f).get(dom)
+    gate_flops = 2.0 * T * w.d * E
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic,
+                "gate_mfma_frac": round(gate_flops / (stages["gate"]["avg_us"] * 1e-6) / 1e12
+                                        / MFMA_BF16_PEAK_TFLOPS, 4) if "gate" in stages else None}
+    for s, v in stages.items():
+        log(f"[bench] {s:13s} {v['avg_us']:9.2f} us  {v['GBs']} GB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        try:
+            threads = min(16, len(os.sched_getaffinity(0)))
+        except AttributeError:
+            threads = min(16, os.cpu_count() or 1)
+        log(f"[bench] timing the CPU oracle on {threads} threads (~{args.cpu_seconds:.0f} s)")
+        cpu = cpu_baseline(w, inp, args.cpu_seconds, threads)
+
+    out = {
+        "metric": "routed tokens/sec (gate+select+dispatch) and % of MFMA/HBM roofline, 1 MI355X",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": f"{w.name}: T={T} tokens, d={w.d}, E={E}, "
+                               f"k={'/'.join(map(str, w.dynamic_k)) + ' per request' if w.dynamic_k else k}, "
+                               f"score={w.score}, groups={w.n_groups}/{w.topk_groups}, "
+                               f"dispatch over {E} experts",
+                   "T": T, "d": w.d, "E": E, "k_max": k, "x_copies": n_copies},
+        "stages": stages,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

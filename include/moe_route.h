@@ -1,0 +1,213 @@
+/*
+ * moe_route.h -- C ABI of the MI355X (gfx950) MoE router and token dispatch.
+ *
+ * A Mixture-of-Experts router scores every routed expert for each token,
+ * keeps k of them and returns, per token, which experts fire and their
+ * combination weights (ferrox_moe crate docs, "RoutingDecision"; the gate of
+ * "DeepSeek-V3.2-Exp - Select experts" returns (weights, indices)).  Dispatch
+ * then groups the routed (token, slot) pairs by expert.
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers are DEVICE pointers (hipMalloc / torch CUDA tensors) unless
+ *    stated otherwise; arrays are dense, row-major, caller-owned.  The
+ *    library never allocates, frees or synchronises and keeps no state
+ *    between calls; inputs are never modified.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    the call returns without waiting.  Results are valid once the stream
+ *    reaches them.
+ *  - Argument errors are detected on the host before anything is enqueued:
+ *    the call returns MOE_EINVAL or MOE_EUNSUPPORTED and moe_last_error()
+ *    describes the problem.  A failed launch returns MOE_EDEVICE.
+ *  - Data-dependent errors (a token id outside the vocabulary, a table entry
+ *    or expert id outside [0, E), a per-token k outside [1, k]) cannot be seen
+ *    without a sync: the affected slots get id -1 and weight 0, and, when
+ *    `dev_err` is not NULL, the kernels add the number of such errors to the
+ *    device int32 *dev_err (the caller zeroes it).
+ *  - T == 0 is valid and enqueues nothing (moe_dispatch still writes zero
+ *    counts and offsets).
+ */
+#ifndef MOE_ROUTE_H
+#define MOE_ROUTE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+/* return codes */
+#define MOE_OK 0
+#define MOE_EINVAL (-1)       /* bad shape, flag, pointer or workspace size */
+#define MOE_EUNSUPPORTED (-2) /* valid but beyond the documented limits */
+#define MOE_EDEVICE (-3)      /* HIP launch failure */
+
+/* documented limits */
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_K 32
+#define MOE_MAX_GROUPS 64
+
+/* dtype of x and W */
+#define MOE_F32 0
+#define MOE_BF16 1
+
+/* score functions.
+ * SOFTMAX        softmax over all E logits; select the top-k probabilities
+ *                (ferrox_moe docs, route_top_k_softmax; DeepSeek-V3.2-Exp
+ *                gate-forward excerpt, softmax branch).
+ * SIGMOID        sigmoid(logit) per expert (DeepSeek-V3.2-Exp gate-forward
+ *                excerpt; ferrox_moe route_top_k_sigmoid).
+ * SQRT_SOFTPLUS  sqrt(softplus(logit)) per expert (ferrox_moe
+ *                route_top_k_sqrtsoftplus; DeepSeek-V4 non-hash layers).
+ * SOFTMAX_TOPK   select by raw logit, weights = softmax over just the k
+ *                selected logits (ferrox_moe route_top_k_softmax_weight;
+ *                gpt-oss). */
+#define MOE_SCORE_SOFTMAX 0
+#define MOE_SCORE_SIGMOID 1
+#define MOE_SCORE_SQRT_SOFTPLUS 2
+#define MOE_SCORE_SOFTMAX_TOPK 3
+
+/* group score (DeepSeek-V3.2-Exp - Select experts, gate-forward excerpt): the
+ * largest selection score of the group, or the sum of its two largest.  The
+ * excerpt uses TOP2_SUM exactly when a selection bias exists. */
+#define MOE_GROUP_MAX 0
+#define MOE_GROUP_TOP2_SUM 1
+
+typedef struct {
+  int32_t T;            /* tokens */
+  int32_t d;            /* hidden size */
+  int32_t E;            /* routed experts, 1..MOE_MAX_EXPERTS */
+  int32_t k;            /* experts per token; with k_per_token, k_max = the
+                           row stride of ids/weights */
+  int32_t dtype;        /* MOE_F32 or MOE_BF16: element type of x and W */
+  int32_t score;        /* MOE_SCORE_* */
+  int32_t n_groups;     /* contiguous expert groups; 1 = no group limit */
+  int32_t topk_groups;  /* groups kept, 1..n_groups */
+  int32_t group_score;  /* MOE_GROUP_* */
+  int32_t renormalize;  /* 1: selected weights renormalised to sum to one
+                           (norm_topk_prob, ferrox_moe route_top_k_softmax) */
+  float route_scale;    /* weights multiplied by this after renormalising
+                           (route_scale / routed_scaling_factor); 1 = none */
+} moe_route_params;
+
+/*
+ * moe_route -- gate, scoring, selection and weights.
+ *
+ * Computes, for each token t (DeepSeek-V3.2-Exp - Select experts: formula,
+ * "Explanation" and gate-forward excerpt; ferrox_moe route_top_k_* items;
+ * per-request k: llama.cpp issue 13572 "dynamic number of experts"):
+ *   l[t][e] = sum_i x[t][i] * W[e][i]  (+ logit_bias[e]),  fp32 accumulate;
+ *   s = score(l);  q = s + select_bias  (the bias only chooses);
+ *   with n_groups > 1: group score = max q or top-2 sum of q per group of
+ *     E/n_groups contiguous experts; keep the topk_groups best groups, drop
+ *     the experts of the others;
+ *   ids[t][0..k_t-1] = the k_t largest q, larger first, equal q -> lower id;
+ *   weights[t][j] = s[ids[t][j]] (unbiased; SOFTMAX_TOPK: softmax over the
+ *     selected logits), renormalised when p->renormalize, times route_scale.
+ * Slots j >= k_t hold id -1 and weight 0.
+ *
+ * Arguments:
+ *   x            [T][d] MOE_F32 or MOE_BF16, or NULL (select-only mode)
+ *   W            [E][d] same dtype as x, or NULL (select-only mode; x and W
+ *                are both NULL or both set)
+ *   logit_bias   [E] fp32 or NULL: added to every logit (moves selection and
+ *                weights alike)
+ *   select_bias  [E] fp32 or NULL: added to the selection score only
+ *   k_per_token  [T] int32 in [1, k] or NULL (= k for every token)
+ *   logits       [T][E] fp32.  With x and W: the gate writes l here (logit
+ *                bias included); may be NULL, then the fused gate+select path
+ *                runs and no logits are written.  Select-only mode: the
+ *                input logits (logit_bias, if given, is added on read).
+ *   ids          [T][k] int32 out
+ *   weights      [T][k] fp32 out
+ *   dev_err      [1] int32 or NULL: incremented per token whose k_per_token
+ *                entry is outside [1, k]
+ * Limits: k <= MOE_MAX_K, E <= MOE_MAX_EXPERTS, n_groups <= MOE_MAX_GROUPS,
+ * k <= topk_groups * E / n_groups, TOP2_SUM needs groups of >= 2 experts,
+ * T*d, T*E and T*k below 2^31.
+ */
+int32_t moe_route(const moe_route_params* p, const void* x, const void* W,
+                  const float* logit_bias, const float* select_bias,
+                  const int32_t* k_per_token, float* logits, int32_t* ids,
+                  float* weights, int32_t* dev_err, void* stream);
+
+/*
+ * moe_route_hash -- hash routing (ferrox_moe docs, route_hash: a DeepSeek-V4
+ * hash layer takes its expert ids from a fixed token-id -> expert-id table
+ * instead of a learned selection, with no selection bias).
+ *
+ *   ids[t][j] = tid2eid[token_ids[t]][j]
+ * tid2eid is row-major [vocab][k] int32 (row v = the k experts of token id
+ * v).  A token id outside [0, vocab) empties its row (ids -1, weights 0,
+ * one error); a table entry outside [0, E) empties its slot (one error).
+ * When x and W are given, weights[t][j] = score(l[t][ids[t][j]]) with
+ * l = x.W^T (+ logit_bias) computed only for the k table experts,
+ * renormalised over the row's valid slots when p->renormalize, times
+ * route_scale; SOFTMAX needs renormalize = 1 (it then equals SOFTMAX_TOPK).
+ * When x and W are NULL only ids are written (weights may be NULL).
+ * Uses p->T, d, E, k, dtype, score, renormalize, route_scale.
+ */
+int32_t moe_route_hash(const moe_route_params* p, const int32_t* token_ids,
+                       const int32_t* tid2eid, int32_t vocab, const void* x,
+                       const void* W, const float* logit_bias, int32_t* ids,
+                       float* weights, int32_t* dev_err, void* stream);
+
+/* Bytes of device workspace moe_dispatch needs for these sizes. */
+size_t moe_dispatch_workspace_size(int32_t T, int32_t k_stride, int32_t E);
+
+/*
+ * moe_dispatch -- group routes by expert (the step that sends each token only
+ * to its selected experts; under expert parallelism it feeds the all-to-all).
+ *
+ * Route r = t*k_stride + j is slot j of token t.  Routes with ids[r] < 0 are
+ * empty and skipped; ids[r] >= E are errors (skipped, counted in *dev_err).
+ *   counts[e]     number of routes to expert e                       [E]
+ *   offsets[e]    exclusive prefix sum of counts; offsets[E] = R     [E+1]
+ *   perm[p]       route index at position p: the routes of expert e
+ *                 fill perm[offsets[e] .. offsets[e+1]) in ascending r
+ *                 (a stable counting sort)          [T*k_stride], first R set
+ *   inv[r]        position of route r in perm, -1 for skipped slots
+ *                 [T*k_stride], may be NULL
+ *   workspace     device memory of at least
+ *                 moe_dispatch_workspace_size(T, k_stride, E) bytes; its
+ *                 contents need no initialisation and are clobbered
+ * Limits: E <= MOE_MAX_EXPERTS, T*k_stride < 2^31.
+ */
+int32_t moe_dispatch(const int32_t* ids, int32_t T, int32_t k_stride, int32_t E,
+                     int32_t* counts, int32_t* offsets, int32_t* perm,
+                     int32_t* inv, void* workspace, size_t workspace_bytes,
+                     int32_t* dev_err, void* stream);
+
+/*
+ * Per-kernel timing, for benchmarks and profiling only.
+ * moe_profile_enable(1) clears earlier records and, from then on, brackets
+ * every kernel the library launches with a pair of HIP events recorded on
+ * that launch's stream (the events are created on the host per launch);
+ * moe_profile_enable(0) stops recording.  moe_profile_read waits for the
+ * recorded events and fills ms[i] (summed kernel time, milliseconds) and
+ * launches[i] for the kernels MOE_STAGE_* = i < n; it returns
+ * MOE_NUM_STAGES.  Records are process-wide.
+ */
+#define MOE_STAGE_GATE 0         /* gate contraction */
+#define MOE_STAGE_SELECT 1       /* score + select + weights */
+#define MOE_STAGE_HASH 2         /* hash routing */
+#define MOE_STAGE_DISP_HIST 3    /* dispatch: tile histograms */
+#define MOE_STAGE_DISP_SCAN 4    /* dispatch: scans */
+#define MOE_STAGE_DISP_SCATTER 5 /* dispatch: permutation */
+#define MOE_NUM_STAGES 6
+int32_t moe_profile_enable(int32_t enable);
+int32_t moe_profile_read(double* ms, int64_t* launches, int32_t n);
+
+/* Text describing the last non-zero return of a call on this thread. */
+const char* moe_last_error(void);
+
+/* MOE_ABI_VERSION of the loaded library. */
+int32_t moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_ROUTE_H */

@@ -1,0 +1,140 @@
+"""The C-ABI library loads, exports every symbol its header declares, and
+rejects bad arguments on the host (no GPU needed: nothing is enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import token_dispatch_amd as tda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_route.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(moe_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    assert {"moe_route", "moe_route_hash", "moe_dispatch", "moe_dispatch_workspace_size",
+            "moe_last_error", "moe_abi_version"} <= set(names), names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = tda.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) <= set(tda.EXPORTS) | {"moe_abi_version"}
+
+
+def test_abi_version():
+    assert tda.lib().moe_abi_version() == tda.ABI_VERSION
+
+
+def test_header_constants_match_binding():
+    src = open(HEADER).read()
+    consts = dict(re.findall(r"#define (MOE_\w+) \(?(-?\d+)\)?", src))
+    assert int(consts["MOE_ABI_VERSION"]) == tda.ABI_VERSION
+    assert int(consts["MOE_MAX_EXPERTS"]) == tda.MAX_EXPERTS
+    assert int(consts["MOE_MAX_K"]) == tda.MAX_K
+    assert int(consts["MOE_MAX_GROUPS"]) == tda.MAX_GROUPS
+    for name, code in tda.SCORES.items():
+        assert int(consts["MOE_SCORE_" + name.upper()]) == code
+    for name, code in tda.GROUP_SCORES.items():
+        assert int(consts["MOE_GROUP_" + name.upper()]) == code
+    assert ctypes.sizeof(tda.RouteParams) == 44
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def call_route(**over):
+    kw = dict(T=16, d=64, E=8, k=2, dtype=1, score="softmax", n_groups=1, topk_groups=1,
+              group_score="max", renormalize=True, route_scale=1.0)
+    kw.update(over)
+    p = tda.make_params(**kw)
+    return tda.lib().moe_route(ctypes.byref(p), FAKE, FAKE, None, None, None, FAKE, FAKE,
+                               FAKE, None, None)
+
+
+@pytest.mark.parametrize("over,code,text", [
+    (dict(T=-1), tda.MOE_EINVAL, "T="),
+    (dict(d=0), tda.MOE_EINVAL, "d="),
+    (dict(E=0), tda.MOE_EINVAL, "E="),
+    (dict(E=2048, k=2), tda.MOE_EUNSUPPORTED, "MOE_MAX_EXPERTS"),
+    (dict(k=0), tda.MOE_EINVAL, "k="),
+    (dict(k=9), tda.MOE_EINVAL, "exceeds E"),
+    (dict(E=64, k=33), tda.MOE_EUNSUPPORTED, "MOE_MAX_K"),
+    (dict(dtype=7), tda.MOE_EINVAL, "dtype"),
+    (dict(n_groups=3), tda.MOE_EINVAL, "does not divide"),
+    (dict(n_groups=4, topk_groups=5), tda.MOE_EINVAL, "topk_groups"),
+    (dict(n_groups=4, topk_groups=0), tda.MOE_EINVAL, "topk_groups"),
+    (dict(n_groups=4, topk_groups=1, k=3), tda.MOE_EINVAL, "kept groups"),
+    (dict(n_groups=8, topk_groups=2, group_score="top2_sum"), tda.MOE_EINVAL, "at least 2"),
+    (dict(route_scale=float("inf")), tda.MOE_EINVAL, "finite"),
+    (dict(E=128, k=4, n_groups=128, topk_groups=4), tda.MOE_EUNSUPPORTED, "MOE_MAX_GROUPS"),
+])
+def test_route_rejects_bad_params(over, code, text):
+    assert call_route(**over) == code
+    assert text in tda.lib().moe_last_error().decode()
+
+
+def test_route_rejects_half_select_only_and_missing_outputs():
+    p = tda.make_params(16, 64, 8, 2)
+    L = tda.lib()
+    assert L.moe_route(ctypes.byref(p), FAKE, None, None, None, None, FAKE, FAKE, FAKE, None,
+                       None) == tda.MOE_EINVAL
+    assert L.moe_route(ctypes.byref(p), None, None, None, None, None, None, FAKE, FAKE, None,
+                       None) == tda.MOE_EINVAL
+    assert L.moe_route(ctypes.byref(p), FAKE, FAKE, None, None, None, FAKE, None, FAKE, None,
+                       None) == tda.MOE_EINVAL
+    assert L.moe_route(None, FAKE, FAKE, None, None, None, FAKE, FAKE, FAKE, None,
+                       None) == tda.MOE_EINVAL
+
+
+def test_route_T0_is_a_noop():
+    p = tda.make_params(0, 64, 8, 2)
+    assert tda.lib().moe_route(ctypes.byref(p), FAKE, FAKE, None, None, None, None, None, None,
+                               None, None) == tda.MOE_OK
+
+
+def test_route_hash_validation():
+    L = tda.lib()
+    p = tda.make_params(4, 64, 8, 2, score="softmax", renormalize=False)
+    assert L.moe_route_hash(ctypes.byref(p), FAKE, FAKE, 10, FAKE, FAKE, None, FAKE, FAKE, None,
+                            None) == tda.MOE_EUNSUPPORTED
+    p = tda.make_params(4, 64, 8, 2, score="sigmoid")
+    assert L.moe_route_hash(ctypes.byref(p), FAKE, FAKE, 0, FAKE, FAKE, None, FAKE, FAKE, None,
+                            None) == tda.MOE_EINVAL
+    assert L.moe_route_hash(ctypes.byref(p), None, FAKE, 10, None, None, None, FAKE, None, None,
+                            None) == tda.MOE_EINVAL
+    p0 = tda.make_params(0, 64, 8, 2, score="sigmoid")
+    assert L.moe_route_hash(ctypes.byref(p0), None, None, 10, None, None, None, None, None, None,
+                            None) == tda.MOE_OK
+
+
+def test_dispatch_validation_and_workspace_size():
+    L = tda.lib()
+    assert tda.dispatch_workspace_size(100, 8, 64) >= 2 * 64 * 4
+    assert tda.dispatch_workspace_size(0, 8, 64) == 0
+    assert tda.dispatch_workspace_size(-1, 8, 64) == 0
+    ws = tda.dispatch_workspace_size(100, 8, 64)
+    assert L.moe_dispatch(FAKE, 100, 8, 64, FAKE, FAKE, FAKE, None, FAKE, ws - 1, None,
+                          None) == tda.MOE_EINVAL
+    assert "workspace" in L.moe_last_error().decode()
+    assert L.moe_dispatch(FAKE, 100, 0, 64, FAKE, FAKE, FAKE, None, FAKE, ws, None,
+                          None) == tda.MOE_EINVAL
+    assert L.moe_dispatch(FAKE, 100, 8, 4096, FAKE, FAKE, FAKE, None, FAKE, ws, None,
+                          None) == tda.MOE_EUNSUPPORTED
+    assert L.moe_dispatch(FAKE, 100, 8, 64, None, FAKE, FAKE, None, FAKE, ws, None,
+                          None) == tda.MOE_EINVAL
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        tda.route(torch.zeros(4, 8), torch.zeros(2, 8), 1)

@@ -1,0 +1,251 @@
+"""MI355X MoE router and token dispatch: thin Python binding of libmoe_route.so.
+
+Every step of the path runs in the library's HIP kernels.  This module only
+checks shapes and dtypes, allocates outputs with torch (device memory), and
+passes raw pointers plus torch's current HIP stream to the C ABI declared in
+include/moe_route.h.  It raises if the library has not been built; there is
+no fallback path.
+
+    ids, weights = route(x, W, k=8, score="sigmoid", select_bias=b,
+                         n_groups=8, topk_groups=4, route_scale=2.5)
+    counts, offsets, perm, inv = dispatch(ids, E)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_route.so")
+
+ABI_VERSION = 1
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EDEVICE = 0, -1, -2, -3
+MAX_EXPERTS, MAX_K, MAX_GROUPS = 1024, 32, 64
+SCORES = {"softmax": 0, "sigmoid": 1, "sqrt_softplus": 2, "softmax_topk": 3}
+GROUP_SCORES = {"max": 0, "top2_sum": 1}
+EXPORTS = ("moe_route", "moe_route_hash", "moe_dispatch_workspace_size", "moe_dispatch",
+           "moe_profile_enable", "moe_profile_read", "moe_last_error", "moe_abi_version")
+STAGES = ("gate", "select", "hash", "disp_hist", "disp_scan", "disp_scatter")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+class RouteParams(ctypes.Structure):
+    """Mirror of moe_route_params."""
+    _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("dtype", ctypes.c_int32), ("score", ctypes.c_int32),
+                ("n_groups", ctypes.c_int32), ("topk_groups", ctypes.c_int32),
+                ("group_score", ctypes.c_int32), ("renormalize", ctypes.c_int32),
+                ("route_scale", ctypes.c_float)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe_route.so (built by token_dispatch_amd._build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m token_dispatch_amd._build` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, P = ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(RouteParams)
+        L.moe_route.argtypes = [P] + [vp] * 10
+        L.moe_route.restype = i32
+        L.moe_route_hash.argtypes = [P, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp]
+        L.moe_route_hash.restype = i32
+        L.moe_dispatch_workspace_size.argtypes = [i32, i32, i32]
+        L.moe_dispatch_workspace_size.restype = ctypes.c_size_t
+        L.moe_dispatch.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, ctypes.c_size_t, vp, vp]
+        L.moe_dispatch.restype = i32
+        L.moe_last_error.argtypes = []
+        L.moe_last_error.restype = ctypes.c_char_p
+        L.moe_profile_enable.argtypes = [i32]
+        L.moe_profile_enable.restype = i32
+        L.moe_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double),
+                                       ctypes.POINTER(ctypes.c_int64), i32]
+        L.moe_profile_read.restype = i32
+        L.moe_abi_version.argtypes = []
+        L.moe_abi_version.restype = i32
+        v = L.moe_abi_version()
+        if v != ABI_VERSION:
+            raise ImportError(f"libmoe_route ABI {v}, binding expects {ABI_VERSION}")
+        _lib = L
+    return _lib
+
+
+def _check(rc: int):
+    if rc != MOE_OK:
+        raise MoeError(rc, lib().moe_last_error().decode())
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, shape=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return 0
+    if t.dtype == torch.bfloat16:
+        return 1
+    raise ValueError(f"x and W must be float32 or bfloat16, got {t.dtype}")
+
+
+def make_params(T, d, E, k, dtype=1, score="softmax", n_groups=1, topk_groups=None,
+                group_score="max", renormalize=True, route_scale=1.0) -> RouteParams:
+    return RouteParams(int(T), int(d), int(E), int(k), int(dtype), SCORES[score],
+                       int(n_groups), int(n_groups if topk_groups is None else topk_groups),
+                       GROUP_SCORES[group_score], int(bool(renormalize)), float(route_scale))
+
+
+def route(x: Optional[torch.Tensor], W: Optional[torch.Tensor], k: int, *,
+          score: str = "softmax", logit_bias=None, select_bias=None, k_per_token=None,
+          n_groups: int = 1, topk_groups: Optional[int] = None,
+          group_score: Optional[str] = None, renormalize: bool = True,
+          route_scale: float = 1.0, logits: Optional[torch.Tensor] = None,
+          E: Optional[int] = None, ids=None, weights=None, dev_err=None,
+          return_logits: bool = False):
+    """Gate + score + (grouped) top-k + weights.  Returns (ids, weights[, logits]).
+
+    x [T][d] and W [E][d] (float32 or bfloat16); or x = W = None with
+    ``logits`` [T][E] float32 as the input (select-only mode).
+    group_score defaults to "top2_sum" when select_bias is given, else "max".
+    """
+    if group_score is None:
+        group_score = "top2_sum" if select_bias is not None else "max"
+    if x is None:
+        if W is not None or logits is None:
+            raise ValueError("select-only mode needs x = W = None and logits")
+        _dev(logits, "logits", torch.float32)
+        T, E_ = logits.shape
+        d, dt, device = 1, 1, logits.device
+    else:
+        _dev(x, "x")
+        _dev(W, "W", x.dtype)
+        T, d = x.shape
+        E_ = W.shape[0]
+        if W.shape[1] != d:
+            raise ValueError("W must be [E][d] with the d of x")
+        dt, device = _dtype_code(x), x.device
+        if logits is None:
+            logits = torch.empty((T, E_), dtype=torch.float32, device=device)
+        _dev(logits, "logits", torch.float32, (T, E_))
+    if E is not None and E != E_:
+        raise ValueError("E does not match W / logits")
+    for name, b in (("logit_bias", logit_bias), ("select_bias", select_bias)):
+        if b is not None:
+            _dev(b, name, torch.float32, (E_,))
+    if k_per_token is not None:
+        _dev(k_per_token, "k_per_token", torch.int32, (T,))
+    if ids is None:
+        ids = torch.empty((T, k), dtype=torch.int32, device=device)
+    if weights is None:
+        weights = torch.empty((T, k), dtype=torch.float32, device=device)
+    _dev(ids, "ids", torch.int32, (T, k))
+    _dev(weights, "weights", torch.float32, (T, k))
+    if dev_err is not None:
+        _dev(dev_err, "dev_err", torch.int32, (1,))
+    p = make_params(T, d, E_, k, dt, score, n_groups, topk_groups, group_score, renormalize,
+                    route_scale)
+    _check(lib().moe_route(ctypes.byref(p), _p(x), _p(W), _p(logit_bias), _p(select_bias),
+                           _p(k_per_token), _p(logits), _p(ids), _p(weights), _p(dev_err),
+                           _stream(device)))
+    return (ids, weights, logits) if return_logits else (ids, weights)
+
+
+def route_hash(token_ids: torch.Tensor, tid2eid: torch.Tensor, E: int, *, x=None, W=None,
+               score: str = "sqrt_softplus", logit_bias=None, renormalize: bool = True,
+               route_scale: float = 1.0, ids=None, weights=None, dev_err=None):
+    """Hash routing: ids = tid2eid[token_ids] ([vocab][k] row-major table), plus
+    weights from the k gathered gate logits when x and W are given."""
+    _dev(token_ids, "token_ids", torch.int32)
+    _dev(tid2eid, "tid2eid", torch.int32)
+    T = token_ids.shape[0]
+    vocab, k = tid2eid.shape
+    device = token_ids.device
+    d, dt = 1, 1
+    if x is not None:
+        _dev(x, "x")
+        _dev(W, "W", x.dtype, (E, x.shape[1]))
+        d, dt = x.shape[1], _dtype_code(x)
+        if x.shape[0] != T:
+            raise ValueError("x must have one row per token id")
+    if logit_bias is not None:
+        _dev(logit_bias, "logit_bias", torch.float32, (E,))
+    if ids is None:
+        ids = torch.empty((T, k), dtype=torch.int32, device=device)
+    if weights is None and x is not None:
+        weights = torch.empty((T, k), dtype=torch.float32, device=device)
+    p = make_params(T, d, E, k, dt, score, 1, 1, "max", renormalize, route_scale)
+    _check(lib().moe_route_hash(ctypes.byref(p), _p(token_ids), _p(tid2eid), vocab, _p(x),
+                                _p(W), _p(logit_bias), _p(ids), _p(weights), _p(dev_err),
+                                _stream(device)))
+    return ids, weights
+
+
+def dispatch_workspace_size(T: int, k_stride: int, E: int) -> int:
+    return int(lib().moe_dispatch_workspace_size(T, k_stride, E))
+
+
+def dispatch(ids: torch.Tensor, E: int, *, with_inv: bool = True, counts=None, offsets=None,
+             perm=None, inv=None, workspace=None, dev_err=None):
+    """Stable grouping of routes by expert.  Returns (counts, offsets, perm, inv);
+    perm has T*k_stride entries of which the first offsets[E] are set."""
+    _dev(ids, "ids", torch.int32)
+    T, ks = ids.shape
+    device = ids.device
+    R = T * ks
+    if counts is None:
+        counts = torch.empty(E, dtype=torch.int32, device=device)
+    if offsets is None:
+        offsets = torch.empty(E + 1, dtype=torch.int32, device=device)
+    if perm is None:
+        perm = torch.empty(R, dtype=torch.int32, device=device)
+    if inv is None and with_inv:
+        inv = torch.empty(R, dtype=torch.int32, device=device)
+    ws_bytes = dispatch_workspace_size(T, ks, E)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=device)
+    _check(lib().moe_dispatch(_p(ids), T, ks, E, _p(counts), _p(offsets), _p(perm), _p(inv),
+                              _p(workspace), workspace.numel(), _p(dev_err), _stream(device)))
+    return counts, offsets, perm, inv
+
+
+def profile_enable(on: bool = True) -> None:
+    """Start (clearing old records) or stop per-kernel event timing."""
+    _check(lib().moe_profile_enable(int(bool(on))))
+
+
+def profile_read() -> dict:
+    """{stage: (total_ms, launches)} for the kernels timed since profile_enable."""
+    n = len(STAGES)
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int64 * n)()
+    rc = lib().moe_profile_read(ms, cnt, n)
+    if rc < 0:
+        _check(rc)
+    return {STAGES[i]: (ms[i], cnt[i]) for i in range(n)}

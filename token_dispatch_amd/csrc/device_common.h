@@ -1,0 +1,93 @@
+// Device helpers for the gfx950 routing kernels: wave64 reductions, ordered
+// keys and score functions.  Internal to the HIP library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+// Score function ids (same values as MOE_SCORE_* / MOE_GROUP_* in the ABI).
+enum : int32_t { kSoftmax = 0, kSigmoid = 1, kSqrtSoftplus = 2, kSoftmaxTopk = 3 };
+enum : int32_t { kGroupMax = 0, kGroupTop2Sum = 1 };
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Order-preserving map float -> uint32: a < b (as floats, no NaN) iff
+// key(a) < key(b) (as unsigned).  Key 0 is below every float, -inf included,
+// and marks an empty / removed candidate.
+__device__ __forceinline__ uint32_t ordered_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint32_t o = __shfl_xor(v, off, kWave);
+    v = v > o ? v : o;
+  }
+  return v;
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum_i32(int v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ int wave_incl_scan_i32(int v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    int o = __shfl_up(v, off, kWave);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int readlane_i32(int v, int lane) {
+  return __builtin_amdgcn_readlane(v, lane);
+}
+__device__ __forceinline__ float readlane_f32(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// Lanes below this one, as a 64-bit mask.
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int lane = lane_id();
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+__device__ __forceinline__ float sigmoid_f32(float l) { return 1.0f / (1.0f + expf(-l)); }
+
+__device__ __forceinline__ float softplus_f32(float l) {
+  return fmaxf(l, 0.0f) + log1pf(expf(-fabsf(l)));
+}
+
+// Per-expert score for the element-wise score functions.  SOFTMAX needs the
+// whole row and is handled by the callers.
+__device__ __forceinline__ float elementwise_score(int32_t score, float l) {
+  switch (score) {
+    case kSigmoid: return sigmoid_f32(l);
+    case kSqrtSoftplus: return sqrtf(softplus_f32(l));
+    default: return l;
+  }
+}
+
+}  // namespace moe

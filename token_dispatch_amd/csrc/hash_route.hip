@@ -1,0 +1,153 @@
+// Hash routing on gfx950 (ferrox_moe crate docs, route_hash: in a
+// DeepSeek-V4 hash layer the expert ids are the token id's row of a fixed
+// token-id -> expert-id table, with no learned selection and no selection
+// bias).
+//
+// One wavefront per token: lanes 0..k-1 gather the table row (validating the
+// token id and every entry), then, when x and W are given, the wave computes
+// only the k gate logits the row needs -- k dot products of length d, the
+// lanes striding over d with 16-byte loads -- and turns them into weights
+// with the layer's score function.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int kWavesPerBlock = 4;
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+
+template <typename In>
+__device__ __forceinline__ float to_f32(In v);
+template <>
+__device__ __forceinline__ float to_f32<uint16_t>(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+template <>
+__device__ __forceinline__ float to_f32<float>(float v) { return v; }
+
+// Partial dot product of x row and W row held by this lane.
+template <typename In, bool VEC>
+__device__ __forceinline__ float lane_dot(const In* __restrict__ xr, const In* __restrict__ wr,
+                                          int d, int lane) {
+  float acc = 0.f;
+  if (VEC) {
+    constexpr int P = 16 / sizeof(In);
+    for (int i = lane * P; i < d; i += kWave * P) {
+      const u32x4_t a = *reinterpret_cast<const u32x4_t*>(xr + i);
+      const u32x4_t b = *reinterpret_cast<const u32x4_t*>(wr + i);
+      if constexpr (sizeof(In) == 2) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc = fmaf(bf16_lo(a[q]), bf16_lo(b[q]), acc);
+          acc = fmaf(bf16_hi(a[q]), bf16_hi(b[q]), acc);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc = fmaf(__uint_as_float(a[q]), __uint_as_float(b[q]), acc);
+      }
+    }
+  } else {
+    for (int i = lane; i < d; i += kWave) acc = fmaf(to_f32<In>(xr[i]), to_f32<In>(wr[i]), acc);
+  }
+  return acc;
+}
+
+template <typename In, bool VEC>
+__global__ __launch_bounds__(kWavesPerBlock * kWave) void hash_route_kernel(
+    RouteCfg c, const int32_t* __restrict__ token_ids,
+    const int32_t* __restrict__ tid2eid, int32_t vocab, const In* __restrict__ x,
+    const In* __restrict__ W, const float* __restrict__ logit_bias,
+    int32_t* __restrict__ ids, float* __restrict__ weights,
+    int32_t* __restrict__ dev_err) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (t >= c.T) return;
+  const int k = c.k;
+
+  const int v = token_ids[t];
+  const bool tok_ok = v >= 0 && v < vocab;
+  int e = -1;
+  bool bad_slot = false;
+  if (lane < k && tok_ok) {
+    e = tid2eid[(int64_t)v * k + lane];
+    if (e < 0 || e >= c.E) {
+      bad_slot = true;
+      e = -1;
+    }
+  }
+  const int nerr = tok_ok ? __popcll(__ballot(bad_slot)) : 1;
+  if (lane == 0 && nerr && dev_err) atomicAdd(dev_err, nerr);
+  if (lane < k) ids[t * k + lane] = e;
+  if (x == nullptr) return;
+
+  const In* xr = x + t * (int64_t)c.d;
+  float my_l = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int ej = readlane_i32(e, j);
+    if (ej < 0) continue;
+    float acc = wave_sum_f32(lane_dot<In, VEC>(xr, W + (int64_t)ej * c.d, c.d, lane));
+    if (logit_bias) acc += logit_bias[ej];
+    if (lane == j) my_l = acc;
+  }
+
+  const bool sel = lane < k && e >= 0;
+  float w;
+  if (c.score == kSoftmax || c.score == kSoftmaxTopk) {
+    const float m = wave_max_f32(sel ? my_l : -INFINITY);
+    const float ex = sel ? expf(my_l - m) : 0.f;
+    const float tot = wave_sum_f32(ex);
+    w = sel ? ex / tot : 0.f;
+  } else {
+    w = sel ? elementwise_score(c.score, my_l) : 0.f;
+    if (c.renormalize) {
+      const float tot = wave_sum_f32(w);
+      w = sel ? w / tot : 0.f;
+    }
+  }
+  if (lane < k) weights[t * k + lane] = sel ? w * c.route_scale : 0.f;
+}
+
+template <typename In>
+hipError_t launch_typed(const RouteCfg& c, const int32_t* tok, const int32_t* tab, int32_t vocab,
+                        const void* x, const void* W, const float* lb, int32_t* ids,
+                        float* w, int32_t* err, hipStream_t s) {
+  const int64_t blocks = ((int64_t)c.T + kWavesPerBlock - 1) / kWavesPerBlock;
+  const bool vec = x != nullptr && (c.d % (16 / sizeof(In)) == 0) &&
+                   reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(W) % 16 == 0;
+  if (vec) {
+    prof_begin(kStageHash, s);
+    hipLaunchKernelGGL((hash_route_kernel<In, true>), dim3((uint32_t)blocks),
+                       dim3(kWavesPerBlock * kWave), 0, s, c, tok, tab, vocab, (const In*)x,
+                       (const In*)W, lb, ids, w, err);
+    prof_end(kStageHash, s);
+  } else {
+    prof_begin(kStageHash, s);
+    hipLaunchKernelGGL((hash_route_kernel<In, false>), dim3((uint32_t)blocks),
+                       dim3(kWavesPerBlock * kWave), 0, s, c, tok, tab, vocab, (const In*)x,
+                       (const In*)W, lb, ids, w, err);
+    prof_end(kStageHash, s);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_hash_route(const RouteCfg& c, int32_t dtype,
+                             const int32_t* token_ids, const int32_t* tid2eid,
+                             int32_t vocab, const void* x, const void* W,
+                             const float* logit_bias, int32_t* ids,
+                             float* weights, int32_t* dev_err,
+                             hipStream_t stream) {
+  if (c.T == 0) return hipSuccess;
+  if (dtype == 1)
+    return launch_typed<uint16_t>(c, token_ids, tid2eid, vocab, x, W, logit_bias, ids, weights,
+                                  dev_err, stream);
+  return launch_typed<float>(c, token_ids, tid2eid, vocab, x, W, logit_bias, ids, weights,
+                             dev_err, stream);
+}
+
+}  // namespace moe

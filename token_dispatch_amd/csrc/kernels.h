@@ -1,0 +1,63 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+// Each launcher enqueues on `stream` and returns the hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Kernel ids for the optional per-kernel event timing (MOE_STAGE_* values).
+enum Stage : int32_t {
+  kStageGate = 0,
+  kStageSelect = 1,
+  kStageHash = 2,
+  kStageDispHist = 3,
+  kStageDispScan = 4,
+  kStageDispScatter = 5,
+  kNumStages = 6
+};
+
+// When timing is enabled these record a HIP event on `stream` before and
+// after a launch; otherwise they do nothing.
+void prof_begin(Stage st, hipStream_t stream);
+void prof_end(Stage st, hipStream_t stream);
+
+// Flattened routing configuration handed to the select kernels.
+struct RouteCfg {
+  int32_t T, d, E, k;
+  int32_t score;        // MOE_SCORE_*
+  int32_t n_groups;     // 1 = no group limit
+  int32_t topk_groups;
+  int32_t group_score;  // MOE_GROUP_*
+  int32_t renormalize;
+  float route_scale;
+};
+
+// logits[T][E] = x[T][d] . W[E][d]^T (+ logit_bias); dtype MOE_F32 / MOE_BF16.
+hipError_t launch_gate_gemm(int32_t dtype, const void* x, const void* W,
+                            const float* logit_bias, float* logits, int32_t T,
+                            int32_t d, int32_t E, hipStream_t stream);
+
+// Score + (grouped) top-k + weights from fp32 logits.
+hipError_t launch_select(const RouteCfg& c, const float* logits,
+                         const float* logit_bias, const float* select_bias,
+                         const int32_t* k_per_token, int32_t* ids,
+                         float* weights, int32_t* dev_err, hipStream_t stream);
+
+// Hash routing: table gather (+ k gathered gate dot products and weights).
+hipError_t launch_hash_route(const RouteCfg& c, int32_t dtype,
+                             const int32_t* token_ids, const int32_t* tid2eid,
+                             int32_t vocab, const void* x, const void* W,
+                             const float* logit_bias, int32_t* ids,
+                             float* weights, int32_t* dev_err,
+                             hipStream_t stream);
+
+// Dispatch: tile histograms -> scan -> stable scatter.
+size_t dispatch_workspace_bytes(int64_t R, int32_t E);
+hipError_t launch_dispatch(const int32_t* ids, int64_t R, int32_t E,
+                           int32_t* counts, int32_t* offsets, int32_t* perm,
+                           int32_t* inv, void* workspace, int32_t* dev_err,
+                           hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,258 @@
+// C ABI of the MoE router / dispatch library: argument validation on the
+// host, thread-local error text, and kernel launches on the caller's stream.
+// Every check here runs before anything is enqueued and touches no device
+// state, so an invalid call never reaches the GPU.
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "moe_route.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int32_t device_fail(hipError_t e, const char* what) {
+  return fail(MOE_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t kI32Max = 2147483647;
+
+// Checks shared by moe_route and moe_route_hash.
+int32_t check_common(const moe_route_params* p, bool need_d) {
+  if (!p) return fail(MOE_EINVAL, "params is NULL");
+  if (p->T < 0) return fail(MOE_EINVAL, "T=%d must be >= 0", p->T);
+  if (need_d && p->d < 1) return fail(MOE_EINVAL, "d=%d must be >= 1", p->d);
+  if (p->E < 1) return fail(MOE_EINVAL, "E=%d must be >= 1", p->E);
+  if (p->E > MOE_MAX_EXPERTS)
+    return fail(MOE_EUNSUPPORTED, "E=%d exceeds MOE_MAX_EXPERTS=%d", p->E, MOE_MAX_EXPERTS);
+  if (p->k < 1) return fail(MOE_EINVAL, "k=%d must be >= 1", p->k);
+  if (p->k > MOE_MAX_K) return fail(MOE_EUNSUPPORTED, "k=%d exceeds MOE_MAX_K=%d", p->k, MOE_MAX_K);
+  if (p->dtype != MOE_F32 && p->dtype != MOE_BF16)
+    return fail(MOE_EINVAL, "dtype=%d is not MOE_F32 or MOE_BF16", p->dtype);
+  if (p->score < MOE_SCORE_SOFTMAX || p->score > MOE_SCORE_SOFTMAX_TOPK)
+    return fail(MOE_EINVAL, "score=%d is not a MOE_SCORE_* value", p->score);
+  if (p->renormalize != 0 && p->renormalize != 1)
+    return fail(MOE_EINVAL, "renormalize=%d must be 0 or 1", p->renormalize);
+  if (!std::isfinite(p->route_scale))
+    return fail(MOE_EINVAL, "route_scale must be finite");
+  if ((int64_t)p->T * p->k > kI32Max)
+    return fail(MOE_EUNSUPPORTED, "T*k=%lld must be below 2^31", (long long)p->T * p->k);
+  if (need_d && (int64_t)p->T * p->d > kI32Max)
+    return fail(MOE_EUNSUPPORTED, "T*d must be below 2^31");
+  return MOE_OK;
+}
+
+moe::RouteCfg to_cfg(const moe_route_params* p) {
+  moe::RouteCfg c;
+  c.T = p->T;
+  c.d = p->d;
+  c.E = p->E;
+  c.k = p->k;
+  c.score = p->score;
+  c.n_groups = p->n_groups;
+  c.topk_groups = p->topk_groups;
+  c.group_score = p->group_score;
+  c.renormalize = p->renormalize;
+  c.route_scale = p->route_scale;
+  return c;
+}
+
+// ---- optional per-kernel event timing --------------------------------------
+struct ProfRecord {
+  int32_t stage;
+  hipEvent_t begin, end;
+};
+std::atomic<bool> g_prof_on{false};
+std::mutex g_prof_mu;
+std::vector<ProfRecord> g_prof_records;
+thread_local hipEvent_t g_prof_open = nullptr;
+
+void prof_clear_locked() {
+  for (auto& r : g_prof_records) {
+    hipEventDestroy(r.begin);
+    hipEventDestroy(r.end);
+  }
+  g_prof_records.clear();
+}
+
+}  // namespace
+
+namespace moe {
+
+void prof_begin(Stage, hipStream_t stream) {
+  if (!g_prof_on.load(std::memory_order_relaxed)) return;
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return;
+  hipEventRecord(e, stream);
+  g_prof_open = e;
+}
+
+void prof_end(Stage st, hipStream_t stream) {
+  if (!g_prof_on.load(std::memory_order_relaxed) || g_prof_open == nullptr) return;
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return;
+  hipEventRecord(e, stream);
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_records.push_back({(int32_t)st, g_prof_open, e});
+  g_prof_open = nullptr;
+}
+
+}  // namespace moe
+
+extern "C" {
+
+int32_t moe_profile_enable(int32_t enable) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  prof_clear_locked();
+  g_prof_on.store(enable != 0);
+  return MOE_OK;
+}
+
+int32_t moe_profile_read(double* ms, int64_t* launches, int32_t n) {
+  if (!ms || !launches || n < 0) return fail(MOE_EINVAL, "ms and launches are required");
+  for (int32_t i = 0; i < n; ++i) {
+    ms[i] = 0.0;
+    launches[i] = 0;
+  }
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (auto& r : g_prof_records) {
+    hipError_t e = hipEventSynchronize(r.end);
+    if (e != hipSuccess) return device_fail(e, "event synchronize");
+    float t = 0.f;
+    e = hipEventElapsedTime(&t, r.begin, r.end);
+    if (e != hipSuccess) return device_fail(e, "event elapsed time");
+    if (r.stage < n) {
+      ms[r.stage] += t;
+      launches[r.stage] += 1;
+    }
+  }
+  return moe::kNumStages;
+}
+
+int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+int32_t moe_route(const moe_route_params* p, const void* x, const void* W,
+                  const float* logit_bias, const float* select_bias,
+                  const int32_t* k_per_token, float* logits, int32_t* ids,
+                  float* weights, int32_t* dev_err, void* stream) {
+  const bool select_only = (x == nullptr && W == nullptr);
+  int32_t rc = check_common(p, !select_only);
+  if (rc != MOE_OK) return rc;
+  if (p->T > 0 && (x == nullptr) != (W == nullptr))
+    return fail(MOE_EINVAL, "x and W must both be set or both be NULL");
+  if (p->k > p->E) return fail(MOE_EINVAL, "k=%d exceeds E=%d", p->k, p->E);
+  if (p->n_groups < 1) return fail(MOE_EINVAL, "n_groups=%d must be >= 1", p->n_groups);
+  if (p->n_groups > MOE_MAX_GROUPS)
+    return fail(MOE_EUNSUPPORTED, "n_groups=%d exceeds MOE_MAX_GROUPS=%d", p->n_groups,
+                MOE_MAX_GROUPS);
+  if (p->E % p->n_groups != 0)
+    return fail(MOE_EINVAL, "n_groups=%d does not divide E=%d", p->n_groups, p->E);
+  if (p->topk_groups < 1 || p->topk_groups > p->n_groups)
+    return fail(MOE_EINVAL, "topk_groups=%d must be in [1, n_groups=%d]", p->topk_groups,
+                p->n_groups);
+  if (p->group_score != MOE_GROUP_MAX && p->group_score != MOE_GROUP_TOP2_SUM)
+    return fail(MOE_EINVAL, "group_score=%d is not a MOE_GROUP_* value", p->group_score);
+  const int32_t gs = p->E / p->n_groups;
+  if ((int64_t)p->k > (int64_t)p->topk_groups * gs)
+    return fail(MOE_EINVAL, "k=%d exceeds the %d experts of the kept groups", p->k,
+                p->topk_groups * gs);
+  if (p->n_groups > 1 && p->group_score == MOE_GROUP_TOP2_SUM && gs < 2)
+    return fail(MOE_EINVAL, "MOE_GROUP_TOP2_SUM needs groups of at least 2 experts");
+  if ((int64_t)p->T * p->E > kI32Max)
+    return fail(MOE_EUNSUPPORTED, "T*E must be below 2^31");
+  if (p->T > 0) {
+    if (!ids || !weights) return fail(MOE_EINVAL, "ids and weights are required");
+    if (!logits) {
+      if (select_only) return fail(MOE_EINVAL, "select-only mode (x = W = NULL) needs logits");
+      return fail(MOE_EUNSUPPORTED, "logits == NULL (fused gate+select) is not available");
+    }
+  }
+  if (p->T == 0) return MOE_OK;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const moe::RouteCfg c = to_cfg(p);
+  hipError_t e;
+  if (!select_only) {
+    e = moe::launch_gate_gemm(p->dtype, x, W, logit_bias, logits, p->T, p->d, p->E, s);
+    if (e != hipSuccess) return device_fail(e, "gate GEMM launch");
+  }
+  e = moe::launch_select(c, logits, select_only ? logit_bias : nullptr, select_bias,
+                         k_per_token, ids, weights, dev_err, s);
+  if (e != hipSuccess) return device_fail(e, "select launch");
+  return MOE_OK;
+}
+
+int32_t moe_route_hash(const moe_route_params* p, const int32_t* token_ids,
+                       const int32_t* tid2eid, int32_t vocab, const void* x,
+                       const void* W, const float* logit_bias, int32_t* ids,
+                       float* weights, int32_t* dev_err, void* stream) {
+  const bool ids_only = (x == nullptr && W == nullptr);
+  int32_t rc = check_common(p, !ids_only);
+  if (rc != MOE_OK) return rc;
+  if (p->T > 0 && (x == nullptr) != (W == nullptr))
+    return fail(MOE_EINVAL, "x and W must both be set or both be NULL");
+  if (vocab < 1) return fail(MOE_EINVAL, "vocab=%d must be >= 1", vocab);
+  if (!ids_only && p->score == MOE_SCORE_SOFTMAX && !p->renormalize)
+    return fail(MOE_EUNSUPPORTED,
+                "hash routing with MOE_SCORE_SOFTMAX needs renormalize=1 (the full-softmax "
+                "denominator needs every expert's logit)");
+  if (p->T > 0) {
+    if (!token_ids || !tid2eid || !ids)
+      return fail(MOE_EINVAL, "token_ids, tid2eid and ids are required");
+    if (!ids_only && !weights) return fail(MOE_EINVAL, "weights are required with x and W");
+  }
+  if (p->T == 0) return MOE_OK;
+  hipError_t e = moe::launch_hash_route(to_cfg(p), p->dtype, token_ids, tid2eid, vocab, x, W,
+                                        logit_bias, ids, weights, dev_err,
+                                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail(e, "hash route launch");
+  return MOE_OK;
+}
+
+size_t moe_dispatch_workspace_size(int32_t T, int32_t k_stride, int32_t E) {
+  if (T < 0 || k_stride < 1 || E < 1) return 0;
+  return moe::dispatch_workspace_bytes((int64_t)T * k_stride, E);
+}
+
+int32_t moe_dispatch(const int32_t* ids, int32_t T, int32_t k_stride, int32_t E,
+                     int32_t* counts, int32_t* offsets, int32_t* perm,
+                     int32_t* inv, void* workspace, size_t workspace_bytes,
+                     int32_t* dev_err, void* stream) {
+  if (T < 0) return fail(MOE_EINVAL, "T=%d must be >= 0", T);
+  if (k_stride < 1) return fail(MOE_EINVAL, "k_stride=%d must be >= 1", k_stride);
+  if (E < 1) return fail(MOE_EINVAL, "E=%d must be >= 1", E);
+  if (E > MOE_MAX_EXPERTS)
+    return fail(MOE_EUNSUPPORTED, "E=%d exceeds MOE_MAX_EXPERTS=%d", E, MOE_MAX_EXPERTS);
+  const int64_t R = (int64_t)T * k_stride;
+  if (R > kI32Max) return fail(MOE_EUNSUPPORTED, "T*k_stride must be below 2^31");
+  if (!counts || !offsets) return fail(MOE_EINVAL, "counts and offsets are required");
+  if (R > 0 && (!ids || !perm)) return fail(MOE_EINVAL, "ids and perm are required");
+  const size_t need = moe::dispatch_workspace_bytes(R, E);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(MOE_EINVAL, "workspace of %zu bytes is below the %zu needed", workspace_bytes,
+                need);
+  hipError_t e = moe::launch_dispatch(ids, R, E, counts, offsets, perm, inv, workspace, dev_err,
+                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail(e, "dispatch launch");
+  return MOE_OK;
+}
+
+}  // extern "C"
