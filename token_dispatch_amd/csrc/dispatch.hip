@@ -1,19 +1,21 @@
 // Token dispatch on gfx950: group routes r = t*k_stride + j by expert with a
 // stable counting sort (counts, exclusive-scan offsets, permutation, inverse).
 //
-// Three kernels over tiles of kTile routes (4 waves x 4 chunks of 64):
-//  1. histogram: each wave counts its chunks without atomics -- the lanes
-//     holding the same expert are found with one ballot per distinct expert
-//     (the leader lane adds the popcount to the wave's own LDS row), and the
-//     tile's per-expert totals go to tile_hist[e][tile];
-//  2. scan (one workgroup): per expert, the exclusive scan of its counts over
-//     tiles (wave-wide scans, 64 tiles at a time), then the exclusive scan of
-//     the per-expert totals over experts -> counts, offsets;
-//  3. scatter: each tile recounts per wave, turns the counts into per-wave
-//     starting positions (offsets[e] + earlier tiles + earlier waves), and
-//     places every route at start + (same-expert lanes below it in the
-//     ballot), advancing the start by the ballot's popcount -- so positions
-//     rise with r inside every expert and nothing depends on scheduling.
+// Routes are cut into tiles of kTile (4 waves x kChunksPerWave chunks of 64
+// lanes).  Lanes that hold the same expert id ("peers") are found without
+// atomics: one ballot per bit of the id narrows each lane's peer mask, so a
+// chunk of 64 routes costs ceil(log2 E) ballots.  A lane's rank among its
+// peers is the popcount of the peers below it, and the lowest peer (the
+// leader) alone updates the wave's own LDS row for that expert.
+//
+//  1. histogram: per-tile, per-expert counts -> tile_hist[e][tile].
+//  2. tile scan: one wave per expert scans its counts over tiles
+//     (exclusive) -> tile_base[e][tile], and its total -> totals[e].
+//  3. scatter: every workgroup scans totals over experts (offsets; workgroup
+//     0 writes counts and offsets), recounts its tile per wave, and places
+//     route r at offsets[e] + tile_base[e][tile] + (earlier waves) + (earlier
+//     chunks) + rank -- positions rise with r inside each expert and do not
+//     depend on how workgroups are scheduled.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -21,13 +23,15 @@ namespace moe {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kChunksPerWave = 4;
-constexpr int kTile = kWaves * kChunksPerWave * kWave;  // routes per tile
+constexpr int kThreads = kWaves * kWave;
+constexpr int kChunksPerWave = 2;
+constexpr int kTile = kWaves * kChunksPerWave * kWave;  // 512 routes per tile
 constexpr int kMaxE = 1024;
-constexpr int kScanThreads = 1024;
+constexpr int kScanWaves = 16;                          // experts per scan workgroup
+constexpr int kScanPrefetch = 8;                        // chunks of 64 tiles in registers
 
-__device__ __forceinline__ int load_id(const int32_t* ids, int64_t r, int64_t R, int E,
-                                       int* err) {
+__device__ __forceinline__ int load_id(const int32_t* __restrict__ ids, int64_t r, int64_t R,
+                                       int E, int* err) {
   int e = (r < R) ? ids[r] : -1;
   if (e >= E) {
     ++*err;
@@ -36,25 +40,31 @@ __device__ __forceinline__ int load_id(const int32_t* ids, int64_t r, int64_t R,
   return e;
 }
 
-// Count this wave's chunks into its LDS row (leader-per-distinct-id ballots).
-__device__ __forceinline__ void count_chunks(const int32_t* ids, int64_t r0, int64_t R, int E,
-                                             int32_t* row, int* err) {
-  const int lane = lane_id();
+// Mask of the lanes whose (valid) id equals this lane's id.
+__device__ __forceinline__ uint64_t peer_mask(int e, int nbits) {
+  uint64_t p = __ballot(e >= 0);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t m = __ballot(bit);
+    p &= bit ? m : ~m;
+  }
+  return p;
+}
+
+// Count this wave's chunks into its LDS row.
+__device__ __forceinline__ void count_chunks(const int32_t* __restrict__ ids, int64_t r0,
+                                             int64_t R, int E, int nbits, int32_t* row,
+                                             int* err) {
+  const uint64_t below = lanemask_lt();
   for (int ch = 0; ch < kChunksPerWave; ++ch) {
-    const int e = load_id(ids, r0 + ch * kWave + lane, R, E, err);
-    uint64_t mask = __ballot(e >= 0);
-    while (mask) {
-      const int leader = __ffsll((unsigned long long)mask) - 1;
-      const int v = readlane_i32(e, leader);
-      const uint64_t m = __ballot(e == v);
-      if (lane == leader) row[v] += __popcll(m);
-      mask &= ~m;
-    }
+    const int e = load_id(ids, r0 + ch * kWave + __lane_id(), R, E, err);
+    const uint64_t p = peer_mask(e, nbits);
+    if (e >= 0 && (p & below) == 0) row[e] += __popcll(p);
   }
 }
 
-__global__ __launch_bounds__(kWaves * kWave) void disp_hist_kernel(
-    const int32_t* __restrict__ ids, int64_t R, int E, int nt,
+__global__ __launch_bounds__(kThreads) void disp_hist_kernel(
+    const int32_t* __restrict__ ids, int64_t R, int E, int nbits, int nt,
     int32_t* __restrict__ tile_hist, int32_t* __restrict__ dev_err) {
   __shared__ int32_t wh[kWaves][kMaxE];
   const int tid = threadIdx.x, wave = tid >> 6;
@@ -62,68 +72,93 @@ __global__ __launch_bounds__(kWaves * kWave) void disp_hist_kernel(
   __syncthreads();
   int err = 0;
   const int64_t r0 = (int64_t)blockIdx.x * kTile + wave * (kChunksPerWave * kWave);
-  count_chunks(ids, r0, R, E, wh[wave], &err);
+  count_chunks(ids, r0, R, E, nbits, wh[wave], &err);
   __syncthreads();
-  for (int e = tid; e < E; e += kWaves * kWave)
+  for (int e = tid; e < E; e += kThreads)
     tile_hist[(int64_t)e * nt + blockIdx.x] = wh[0][e] + wh[1][e] + wh[2][e] + wh[3][e];
   err = wave_sum_i32(err);
   if ((tid & 63) == 0 && err && dev_err) atomicAdd(dev_err, err);
 }
 
-__global__ __launch_bounds__(kScanThreads) void disp_scan_kernel(
+// One wave per expert: exclusive scan of its per-tile counts, and its total.
+__global__ __launch_bounds__(kScanWaves * kWave) void disp_tile_scan_kernel(
     const int32_t* __restrict__ tile_hist, int nt, int E, int32_t* __restrict__ tile_base,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
-  __shared__ int32_t tot[kMaxE];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  constexpr int nwaves = kScanThreads / kWave;
-  for (int e = wave; e < E; e += nwaves) {
-    int carry = 0;
-    for (int b = 0; b < nt; b += kWave) {
-      const int i = b + lane;
-      const int v = (i < nt) ? tile_hist[(int64_t)e * nt + i] : 0;
-      const int inc = wave_incl_scan_i32(v);
-      if (i < nt) tile_base[(int64_t)e * nt + i] = carry + inc - v;
+    int32_t* __restrict__ totals) {
+  const int lane = threadIdx.x & 63;
+  const int e = blockIdx.x * kScanWaves + (threadIdx.x >> 6);
+  if (e >= E) return;
+  const int32_t* src = tile_hist + (int64_t)e * nt;
+  int32_t* dst = tile_base + (int64_t)e * nt;
+  int carry = 0;
+  for (int b0 = 0; b0 < nt; b0 += kScanPrefetch * kWave) {
+    int v[kScanPrefetch];
+#pragma unroll
+    for (int c = 0; c < kScanPrefetch; ++c) {
+      const int i = b0 + c * kWave + lane;
+      v[c] = (i < nt) ? src[i] : 0;
+    }
+#pragma unroll
+    for (int c = 0; c < kScanPrefetch; ++c) {
+      const int i = b0 + c * kWave + lane;
+      const int inc = wave_incl_scan_i32(v[c]);
+      if (i < nt) dst[i] = carry + inc - v[c];
       carry += readlane_i32(inc, 63);
     }
-    if (lane == 0) tot[e] = carry;
   }
-  __syncthreads();
-  if (wave == 0) {
-    int carry = 0;
-    for (int b = 0; b < E; b += kWave) {
-      const int e = b + lane;
-      const int v = (e < E) ? tot[e] : 0;
-      const int inc = wave_incl_scan_i32(v);
-      if (e < E) {
-        counts[e] = v;
-        offsets[e] = carry + inc - v;
-      }
-      carry += readlane_i32(inc, 63);
-    }
-    if (lane == 0) offsets[E] = carry;
-  }
+  if (lane == 0) totals[e] = carry;
 }
 
-__global__ __launch_bounds__(kWaves * kWave) void disp_scatter_kernel(
-    const int32_t* __restrict__ ids, int64_t R, int E, int nt,
-    const int32_t* __restrict__ tile_base, const int32_t* __restrict__ offsets,
-    int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+__global__ __launch_bounds__(kThreads) void disp_scatter_kernel(
+    const int32_t* __restrict__ ids, int64_t R, int E, int nbits, int nt,
+    const int32_t* __restrict__ tile_base, const int32_t* __restrict__ totals,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+    int32_t* __restrict__ inv) {
   __shared__ int32_t wh[kWaves][kMaxE];
+  __shared__ int32_t off[kMaxE];
+  __shared__ int32_t wsum[kWaves];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+
+  // offsets: exclusive scan of totals over experts (4 experts per thread)
+  int t4[4], s = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid * 4 + i;
+    t4[i] = (e < E && totals != nullptr) ? totals[e] : 0;
+    s += t4[i];
+  }
+  const int inc = wave_incl_scan_i32(s);
+  if (lane == 63) wsum[wave] = inc;
   for (int e = lane; e < E; e += kWave) wh[wave][e] = 0;
   __syncthreads();
+  int base = inc - s;
+  for (int w = 0; w < wave; ++w) base += wsum[w];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid * 4 + i;
+    if (e < E) {
+      off[e] = base;
+      if (blockIdx.x == 0) {
+        counts[e] = t4[i];
+        offsets[e] = base;
+      }
+    }
+    base += t4[i];
+  }
+  if (blockIdx.x == 0 && tid == kThreads - 1) offsets[E] = base;
+  if ((int)blockIdx.x >= nt) return;  // only when there are no routes at all
+
   int err = 0;
   const int64_t r0 = (int64_t)blockIdx.x * kTile + wave * (kChunksPerWave * kWave);
-  count_chunks(ids, r0, R, E, wh[wave], &err);
+  count_chunks(ids, r0, R, E, nbits, wh[wave], &err);
   __syncthreads();
   // per-wave starting positions of each expert inside this tile
-  for (int e = tid; e < E; e += kWaves * kWave) {
+  for (int e = tid; e < E; e += kThreads) {
     const int c0 = wh[0][e], c1 = wh[1][e], c2 = wh[2][e];
-    const int base = offsets[e] + tile_base[(int64_t)e * nt + blockIdx.x];
-    wh[0][e] = base;
-    wh[1][e] = base + c0;
-    wh[2][e] = base + c0 + c1;
-    wh[3][e] = base + c0 + c1 + c2;
+    const int b = off[e] + tile_base[(int64_t)e * nt + blockIdx.x];
+    wh[0][e] = b;
+    wh[1][e] = b + c0;
+    wh[2][e] = b + c0 + c1;
+    wh[3][e] = b + c0 + c1 + c2;
   }
   __syncthreads();
   const uint64_t below = lanemask_lt();
@@ -131,16 +166,12 @@ __global__ __launch_bounds__(kWaves * kWave) void disp_scatter_kernel(
   for (int ch = 0; ch < kChunksPerWave; ++ch) {
     const int64_t r = r0 + ch * kWave + lane;
     const int e = load_id(ids, r, R, E, &err);
+    const uint64_t p = peer_mask(e, nbits);
     int pos = -1;
-    uint64_t mask = __ballot(e >= 0);
-    while (mask) {
-      const int leader = __ffsll((unsigned long long)mask) - 1;
-      const int v = readlane_i32(e, leader);
-      const uint64_t m = __ballot(e == v);
-      const int start = row[v];
-      if (e == v) pos = start + __popcll(m & below);
-      if (lane == leader) row[v] = start + __popcll(m);
-      mask &= ~m;
+    if (e >= 0) {
+      const int start = row[e];
+      pos = start + __popcll(p & below);
+      if ((p & below) == 0) row[e] = start + __popcll(p);
     }
     if (r < R) {
       if (inv) inv[r] = pos;
@@ -149,11 +180,18 @@ __global__ __launch_bounds__(kWaves * kWave) void disp_scatter_kernel(
   }
 }
 
+int bits_for(int E) {
+  int b = 0;
+  while ((1 << b) < E) ++b;
+  return b;
+}
+
 }  // namespace
 
 size_t dispatch_workspace_bytes(int64_t R, int32_t E) {
   const int64_t nt = (R + kTile - 1) / kTile;
-  return (size_t)(2 * nt * (int64_t)E * sizeof(int32_t));
+  if (nt == 0) return 0;  // no routes: only counts and offsets are written
+  return (size_t)((2 * nt + 1) * (int64_t)E * sizeof(int32_t));
 }
 
 hipError_t launch_dispatch(const int32_t* ids, int64_t R, int32_t E,
@@ -161,25 +199,29 @@ hipError_t launch_dispatch(const int32_t* ids, int64_t R, int32_t E,
                            int32_t* inv, void* workspace, int32_t* dev_err,
                            hipStream_t stream) {
   const int nt = (int)((R + kTile - 1) / kTile);
+  const int nbits = bits_for(E);
   int32_t* tile_hist = static_cast<int32_t*>(workspace);
   int32_t* tile_base = tile_hist + (int64_t)nt * E;
+  int32_t* totals = tile_base + (int64_t)nt * E;
+  hipError_t e;
   if (nt > 0) {
     prof_begin(kStageDispHist, stream);
-    hipLaunchKernelGGL(disp_hist_kernel, dim3(nt), dim3(kWaves * kWave), 0, stream, ids, R, E,
+    hipLaunchKernelGGL(disp_hist_kernel, dim3(nt), dim3(kThreads), 0, stream, ids, R, E, nbits,
                        nt, tile_hist, dev_err);
     prof_end(kStageDispHist, stream);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    prof_begin(kStageDispScan, stream);
+    hipLaunchKernelGGL(disp_tile_scan_kernel, dim3((E + kScanWaves - 1) / kScanWaves),
+                       dim3(kScanWaves * kWave), 0, stream, tile_hist, nt, E, tile_base, totals);
+    prof_end(kStageDispScan, stream);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  prof_begin(kStageDispScan, stream);
-  hipLaunchKernelGGL(disp_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, tile_hist, nt, E,
-                     tile_base, counts, offsets);
-  prof_end(kStageDispScan, stream);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || nt == 0) return e;
+  // with no routes the scatter kernel runs one workgroup that only writes
+  // zero counts and offsets (totals is not read then)
   prof_begin(kStageDispScatter, stream);
-  hipLaunchKernelGGL(disp_scatter_kernel, dim3(nt), dim3(kWaves * kWave), 0, stream, ids, R, E,
-                     nt, tile_base, offsets, perm, inv);
+  hipLaunchKernelGGL(disp_scatter_kernel, dim3(nt > 0 ? nt : 1), dim3(kThreads), 0, stream, ids,
+                     R, E, nbits, nt, tile_base, nt > 0 ? totals : nullptr, counts, offsets,
+                     perm, inv);
   prof_end(kStageDispScatter, stream);
   return hipGetLastError();
 }

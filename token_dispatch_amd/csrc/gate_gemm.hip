@@ -6,14 +6,23 @@
 // in fp32, so bf16 inputs go through v_mfma_f32_16x16x32_bf16 and fp32
 // inputs through v_mfma_f32_16x16x4_f32 (never rounded to bf16).
 //
-// Shape: M = T tokens (thousands), N = E experts (8..1024), K = d.  A
-// workgroup of 4 waves owns BM tokens x BN experts (BN = all of E when
-// E <= 384) so x, the large operand, streams from HBM once.  Each stage moves
-// a 128-byte K slice of the x rows and W rows into LDS (16-byte loads, rows
-// padded to 144 bytes so the 16 lanes of an MFMA row group hit distinct
-// banks); the next stage's global loads are issued before the MFMAs of the
-// current one.  Wave w computes all BM rows against experts
-// [w*BN/4, (w+1)*BN/4).
+// Shape: M = T tokens (thousands), N = E experts (8..1024), K = d.  The
+// contraction is skinny (E flop per byte of x), so x must stream from HBM
+// once and the chip must be filled: a workgroup (4 waves, 2 x 2) owns a
+// BM x BN tile, and N is split into E/BN tiles when whole-E tiles would leave
+// CUs idle.  Tiles are ordered so that the N tiles of one M tile -- which read
+// the same x rows -- run together on one XCD and share its L2 (workgroups
+// are handed to the 8 XCDs round-robin).
+//
+// Two kernels share the tiling.  The pipelined one (16-byte aligned rows, d
+// a multiple of the 128-byte stage) copies each stage's x and W row slices
+// straight into an LDS ring with buffer_load ... lds and keeps NS-1 stages
+// in flight.  The general one (any d, any alignment) stages through
+// registers into two padded LDS buffers, one stage ahead.
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -25,9 +34,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kRowBytes = 128;             // K slice per stage, bytes
-constexpr int kLdsStride = kRowBytes + 16; // padded LDS row, bytes
-constexpr int kChunks = kRowBytes / 16;    // 16-byte chunks per row slice
+constexpr int kXcds = 8;
 
 template <typename In>
 struct ElemInfo;
@@ -40,12 +47,11 @@ struct ElemInfo<float> {
   static constexpr int kPerChunk = 4;
 };
 
-// Load one 16-byte chunk (elements [k, k+kPerChunk) of row `row`), zero
-// outside [0, rows) x [0, d).  VEC: the row pitch and base are 16-byte
-// aligned and d is a multiple of kPerChunk.
+// One 16-byte chunk (elements [k, k + kPerChunk) of row `row`), zero outside
+// [0, rows) x [0, d).  VEC: rows are 16-byte aligned and d % kPerChunk == 0.
 template <typename In, bool VEC>
-__device__ __forceinline__ u32x4_t load_chunk(const In* base, int64_t row,
-                                              int rows, int k, int d) {
+__device__ __forceinline__ u32x4_t load_chunk(const In* base, int64_t row, int rows, int k,
+                                              int d) {
   constexpr int P = ElemInfo<In>::kPerChunk;
   u32x4_t v = {0u, 0u, 0u, 0u};
   if (row >= rows) return v;
@@ -61,56 +67,61 @@ __device__ __forceinline__ u32x4_t load_chunk(const In* base, int64_t row,
   return v;
 }
 
-template <typename In, int BM, int BN, bool VEC>
+// BM x BN tile, KB bytes of K per stage.
+template <typename In, int BM, int BN, int KB, bool VEC>
 __global__ __launch_bounds__(kThreads) void gate_gemm_kernel(
-    const In* __restrict__ x, const In* __restrict__ W,
-    const float* __restrict__ logit_bias, float* __restrict__ logits, int T,
-    int d, int E) {
+    const In* __restrict__ x, const In* __restrict__ W, const float* __restrict__ logit_bias,
+    float* __restrict__ logits, int T, int d, int E, int n_m, int n_n, int per_xcd) {
   constexpr int P = ElemInfo<In>::kPerChunk;
-  constexpr int BK = kRowBytes / sizeof(In);  // K elements per stage
-  constexpr int MB = BM / 16;                 // 16-row blocks per wave
-  constexpr int NW = BN / 4;                  // experts per wave
-  constexpr int NB = NW / 16;                 // 16-col blocks per wave
-  constexpr int A_CHUNKS = BM * kChunks / kThreads;
-  constexpr int B_CHUNKS = BN * kChunks / kThreads;
-  static_assert(BM % 16 == 0 && BN % 64 == 0, "tile shape");
-  static_assert(A_CHUNKS >= 1 && BM * kChunks % kThreads == 0, "A tile chunks");
-  static_assert(BN * kChunks % kThreads == 0, "B tile chunks");
+  constexpr int BK = KB / (int)sizeof(In);  // K elements per stage
+  constexpr int CPR = KB / 16;              // 16-byte chunks per row per stage
+  constexpr int STRIDE = KB + 16;           // padded LDS row (bytes)
+  constexpr int MB = BM / 32;               // 16-row blocks per wave
+  constexpr int NB = BN / 32;               // 16-col blocks per wave
+  constexpr int A_CH = BM * CPR / kThreads;
+  constexpr int B_CH = BN * CPR / kThreads;
+  static_assert(BM % 32 == 0 && BN % 32 == 0, "tile shape");
+  static_assert(BM * CPR % kThreads == 0 && BN * CPR % kThreads == 0, "chunk split");
+  static_assert(KB % 64 == 0, "stage size");
 
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[BM * kLdsStride];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[BN * kLdsStride];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][(BM + BN) * STRIDE];
+
+  // XCD-aware tile order: consecutive tile ids (the N tiles of one M tile,
+  // then the next M tile) go to one XCD.
+  const int L = blockIdx.x;
+  const int tile = (L % kXcds) * per_xcd + L / kXcds;
+  if (tile >= n_m * n_n) return;
+  const int64_t m0 = (int64_t)(tile / n_n) * BM;
+  const int n0 = (tile % n_n) * BN;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int64_t m0 = (int64_t)blockIdx.y * BM;
-  const int n0 = blockIdx.x * BN;
+  const int wm = wave >> 1, wn = wave & 1;
 
-  u32x4_t ra[A_CHUNKS], rb[B_CHUNKS];
+  u32x4_t ra[A_CH], rb[B_CH];
   auto fetch = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < A_CHUNKS; ++i) {
+    for (int i = 0; i < A_CH; ++i) {
       const int c = tid + i * kThreads;
-      const int r = c / kChunks, ck = c % kChunks;
-      ra[i] = load_chunk<In, VEC>(x, m0 + r, T, k0 + ck * P, d);
+      ra[i] = load_chunk<In, VEC>(x, m0 + c / CPR, T, k0 + (c % CPR) * P, d);
     }
 #pragma unroll
-    for (int i = 0; i < B_CHUNKS; ++i) {
+    for (int i = 0; i < B_CH; ++i) {
       const int c = tid + i * kThreads;
-      const int r = c / kChunks, ck = c % kChunks;
-      rb[i] = load_chunk<In, VEC>(W, (int64_t)n0 + r, E, k0 + ck * P, d);
+      rb[i] = load_chunk<In, VEC>(W, (int64_t)n0 + c / CPR, E, k0 + (c % CPR) * P, d);
     }
   };
-  auto stash = [&]() {
+  auto stash = [&](uint8_t* buf) {
 #pragma unroll
-    for (int i = 0; i < A_CHUNKS; ++i) {
+    for (int i = 0; i < A_CH; ++i) {
       const int c = tid + i * kThreads;
-      *reinterpret_cast<u32x4_t*>(lds_a + (c / kChunks) * kLdsStride + (c % kChunks) * 16) = ra[i];
+      *reinterpret_cast<u32x4_t*>(buf + (c / CPR) * STRIDE + (c % CPR) * 16) = ra[i];
     }
 #pragma unroll
-    for (int i = 0; i < B_CHUNKS; ++i) {
+    for (int i = 0; i < B_CH; ++i) {
       const int c = tid + i * kThreads;
-      *reinterpret_cast<u32x4_t*>(lds_b + (c / kChunks) * kLdsStride + (c % kChunks) * 16) = rb[i];
+      *reinterpret_cast<u32x4_t*>(buf + (BM + c / CPR) * STRIDE + (c % CPR) * 16) = rb[i];
     }
   };
 
@@ -122,46 +133,37 @@ __global__ __launch_bounds__(kThreads) void gate_gemm_kernel(
 
   const int row16 = lane & 15;  // row of A / column of B this lane feeds
   const int kq = lane >> 4;     // which quarter of the MFMA's K this lane feeds
-  const uint8_t* a_base = lds_a + row16 * kLdsStride;
-  const uint8_t* b_base = lds_b + (wave * NW + row16) * kLdsStride;
+  const int a_off = (wm * (BM / 2) + row16) * STRIDE + kq * 16;
+  const int b_off = (BM + wn * (BN / 2) + row16) * STRIDE + kq * 16;
 
-  fetch(0);
-  for (int k0 = 0; k0 < d; k0 += BK) {
-    __syncthreads();  // previous stage's MFMAs are done with LDS
-    stash();
-    __syncthreads();
-    if (k0 + BK < d) fetch(k0 + BK);  // in flight while the MFMAs run
-
-    if constexpr (sizeof(In) == 2) {
-      // two K=32 steps; lane feeds elements [kq*8, kq*8+8) of each step
+  auto compute = [&](const uint8_t* buf) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < KB / 64; ++ks) {
+      if constexpr (sizeof(In) == 2) {
+        // one K=32 MFMA step: lane feeds elements [kq*8, kq*8+8)
         bf16x8_t af[MB], bfr[NB];
 #pragma unroll
         for (int i = 0; i < MB; ++i)
-          af[i] = *reinterpret_cast<const bf16x8_t*>(a_base + i * 16 * kLdsStride + ks * 64 + kq * 16);
+          af[i] = *reinterpret_cast<const bf16x8_t*>(buf + a_off + i * 16 * STRIDE + ks * 64);
 #pragma unroll
         for (int j = 0; j < NB; ++j)
-          bfr[j] = *reinterpret_cast<const bf16x8_t*>(b_base + j * 16 * kLdsStride + ks * 64 + kq * 16);
+          bfr[j] = *reinterpret_cast<const bf16x8_t*>(buf + b_off + j * 16 * STRIDE + ks * 64);
 #pragma unroll
         for (int i = 0; i < MB; ++i)
 #pragma unroll
           for (int j = 0; j < NB; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-      }
-    } else {
-      // two 16-wide K steps of four K=4 MFMAs.  A and B use the same
-      // permutation of K: MFMA s takes element kq*4 + s of the step, so the
-      // lane reads one float4 per operand and the sum is unchanged.
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+      } else {
+        // a 16-wide K step as four K=4 MFMAs.  A and B use the same
+        // permutation of K: MFMA s takes element kq*4 + s of the step, so
+        // each lane reads one float4 per operand and the sum is unchanged.
         f32x4_t af[MB], bfr[NB];
 #pragma unroll
         for (int i = 0; i < MB; ++i)
-          af[i] = *reinterpret_cast<const f32x4_t*>(a_base + i * 16 * kLdsStride + ks * 64 + kq * 16);
+          af[i] = *reinterpret_cast<const f32x4_t*>(buf + a_off + i * 16 * STRIDE + ks * 64);
 #pragma unroll
         for (int j = 0; j < NB; ++j)
-          bfr[j] = *reinterpret_cast<const f32x4_t*>(b_base + j * 16 * kLdsStride + ks * 64 + kq * 16);
+          bfr[j] = *reinterpret_cast<const f32x4_t*>(buf + b_off + j * 16 * STRIDE + ks * 64);
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -171,55 +173,314 @@ __global__ __launch_bounds__(kThreads) void gate_gemm_kernel(
               acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i][s], bfr[j][s], acc[i][j], 0, 0, 0);
       }
     }
+  };
+
+  const int n_stages = (d + BK - 1) / BK;
+  fetch(0);
+  stash(lds[0]);
+  __syncthreads();
+  for (int s = 0; s < n_stages; ++s) {
+    const bool more = s + 1 < n_stages;
+    if (more) fetch((s + 1) * BK);  // in flight during this stage's MFMAs
+    compute(lds[s & 1]);
+    if (more) stash(lds[(s + 1) & 1]);
+    __syncthreads();
   }
 
   // D layout of a 16x16 MFMA: lane holds rows 4*(lane/16) + r, column lane%16.
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
-    const int e = n0 + wave * NW + j * 16 + row16;
+    const int e = n0 + wn * (BN / 2) + j * 16 + row16;
     if (e >= E) continue;
     const float b = logit_bias ? logit_bias[e] : 0.0f;
 #pragma unroll
     for (int i = 0; i < MB; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t t = m0 + i * 16 + kq * 4 + r;
+        const int64_t t = m0 + wm * (BM / 2) + i * 16 + kq * 4 + r;
         if (t < T) logits[t * E + e] = acc[i][j][r] + b;
       }
   }
 }
 
-template <typename In, int BM, int BN>
-hipError_t launch_tile(const void* x, const void* W, const float* logit_bias,
-                       float* logits, int T, int d, int E, hipStream_t s) {
-  dim3 grid((E + BN - 1) / BN, (T + BM - 1) / BM);
-  const bool vec = (d % ElemInfo<In>::kPerChunk == 0) &&
-                   (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
-                   (reinterpret_cast<uintptr_t>(W) % 16 == 0);
-  if (vec) {
-    prof_begin(kStageGate, s);
-    hipLaunchKernelGGL((gate_gemm_kernel<In, BM, BN, true>), grid, dim3(kThreads), 0, s,
-                       (const In*)x, (const In*)W, logit_bias, logits, T, d, E);
-    prof_end(kStageGate, s);
-  } else {
-    prof_begin(kStageGate, s);
-    hipLaunchKernelGGL((gate_gemm_kernel<In, BM, BN, false>), grid, dim3(kThreads), 0, s,
-                       (const In*)x, (const In*)W, logit_bias, logits, T, d, E);
-    prof_end(kStageGate, s);
+
+// ---------------------------------------------------------------------------
+// Deep pipeline for 16-byte aligned inputs with d a multiple of the stage
+// (the common case): global -> LDS copies with buffer_load ... lds, an
+// NS-stage ring, NS-1 stages in flight while one is multiplied.
+//
+// LDS layout of a stage: the tile's BM x rows then BN W rows, 128 bytes each,
+// no padding; the 16-byte chunk c of row r sits in slot c ^ (r % 8), so the
+// 16 rows an MFMA operand read touches spread over the banks.  One load
+// instruction of a wave fills 1 KB = 8 rows: lane l writes slot l % 8 of row
+// l / 8 (the hardware places lane data contiguously), so it fetches chunk
+// (l % 8) ^ (l / 8) of that row.  Rows past T or E, and the unused stages
+// after the last one, read past the buffer descriptor's range and load zeros
+// without touching memory.
+// gfx9 s_waitcnt immediate: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] |
+// vmcnt[5:4] << 14.
+template <int VM, int LGKM>
+__device__ __forceinline__ void wait_counts() {
+  static_assert(VM >= 0 && VM < 64 && LGKM >= 0 && LGKM < 16, "counter range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (LGKM << 8) | ((VM >> 4) << 14));
+}
+
+// Barrier between pipeline stages.  __syncthreads() would add a release
+// fence, i.e. wait for every copy still in flight; here each wave waits only
+// until at most VM of its copies are outstanding (the older ones -- the stage
+// about to be read -- have landed in LDS) and its own LDS reads are done
+// (the stage about to be overwritten is no longer read), then meets the
+// other waves.
+template <int VM>
+__device__ __forceinline__ void stage_barrier() {
+  wait_counts<VM, 0>();
+  __builtin_amdgcn_s_barrier();
+}
+
+template <typename In, int BM, int BN, int NS>
+__global__ __launch_bounds__(kThreads) void gate_gemm_pipe_kernel(
+    const In* __restrict__ x, const In* __restrict__ W, const float* __restrict__ logit_bias,
+    float* __restrict__ logits, int T, int d, int E, int n_m, int n_n, int per_xcd) {
+  constexpr int RB = 128;                      // bytes of K per row per stage
+  constexpr int BK = RB / (int)sizeof(In);     // K elements per stage
+  constexpr int ROWS = BM + BN;
+  constexpr int STAGE = ROWS * RB;             // bytes per stage
+  constexpr int LPS = ROWS / 8 / 4;            // load instructions per wave per stage
+  constexpr int MB = BM / 32;
+  constexpr int NB = BN / 32;
+  static_assert(BM % 32 == 0 && BN % 32 == 0 && (ROWS / 8) % 4 == 0, "tile shape");
+  static_assert(NS >= 2 && (NS - 2) * LPS < 64, "pipeline depth");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * STAGE];
+
+  const int L = blockIdx.x;
+  const int tile = (L % kXcds) * per_xcd + L / kXcds;
+  if (tile >= n_m * n_n) return;
+  const int m0 = (tile / n_n) * BM;
+  const int n0 = (tile % n_n) * BN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+
+  const uint32_t row_bytes = (uint32_t)d * sizeof(In);
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)x, (short)0, (int)((uint32_t)T * row_bytes), 0x00020000);
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)W, (short)0, (int)((uint32_t)E * row_bytes), 0x00020000);
+  const int n_stages = d / BK;
+
+  // per-lane source offsets (bytes, stage 0) of this wave's load instructions
+  uint32_t src_off[LPS];
+  bool src_is_x[LPS];
+#pragma unroll
+  for (int i = 0; i < LPS; ++i) {
+    const int blk = wave + 4 * i;            // 8-row block of the tile
+    const int r = blk * 8 + (lane >> 3);     // tile row
+    const int chunk = (lane & 7) ^ (lane >> 3);
+    src_is_x[i] = r < BM;
+    const uint32_t grow = src_is_x[i] ? (uint32_t)(m0 + r) : (uint32_t)(n0 + r - BM);
+    const uint32_t nrows = src_is_x[i] ? (uint32_t)T : (uint32_t)E;
+    // rows past the end: an offset past the descriptor range reads zeros
+    src_off[i] = grow < nrows ? grow * row_bytes + chunk * 16 : 0x80000000u;
   }
+  auto issue = [&](int st) {
+    uint8_t* buf = lds + (st % NS) * STAGE;
+    const uint32_t koff = st < n_stages ? (uint32_t)st * RB : 0x80000000u;
+#pragma unroll
+    for (int i = 0; i < LPS; ++i) {
+      auto* dst = (__attribute__((address_space(3))) void*)(buf + (wave + 4 * i) * 1024);
+      const uint32_t off = (src_off[i] | koff) >= 0x80000000u ? 0x80000000u : src_off[i] + koff;
+      if (src_is_x[i])
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, dst, 16, off, 0, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, dst, 16, off, 0, 0, 0);
+    }
+  };
+
+  f32x4_t acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int row16 = lane & 15;
+  const int kq = lane >> 4;
+  const int sw = row16 & 7;  // row % 8 of every row this lane reads
+  const int a_row = wm * (BM / 2) + row16;
+  const int b_row = BM + wn * (BN / 2) + row16;
+
+  auto compute = [&](const uint8_t* buf) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int slot = ((ks * 4 + kq) ^ sw) * 16;
+      if constexpr (sizeof(In) == 2) {
+        bf16x8_t af[MB], bfr[NB];
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+          af[i] = *reinterpret_cast<const bf16x8_t*>(buf + (a_row + i * 16) * RB + slot);
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          bfr[j] = *reinterpret_cast<const bf16x8_t*>(buf + (b_row + j * 16) * RB + slot);
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+          for (int j = 0; j < NB; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      } else {
+        f32x4_t af[MB], bfr[NB];
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+          af[i] = *reinterpret_cast<const f32x4_t*>(buf + (a_row + i * 16) * RB + slot);
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          bfr[j] = *reinterpret_cast<const f32x4_t*>(buf + (b_row + j * 16) * RB + slot);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i][s], bfr[j][s], acc[i][j], 0, 0, 0);
+      }
+    }
+  };
+
+#pragma unroll
+  for (int st = 0; st < NS - 1; ++st) issue(st);
+  for (int s = 0; s < n_stages; ++s) {
+    stage_barrier<(NS - 2) * LPS>();  // stage s is in LDS; stage s-1 is consumed
+    issue(s + NS - 1);                // refill the buffer stage s-1 used
+    compute(lds + (s % NS) * STAGE);
+  }
+  wait_counts<0, 15>();  // no copy may still target LDS when the workgroup ends
+
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int e = n0 + wn * (BN / 2) + j * 16 + row16;
+    if (e >= E) continue;
+    const float b = logit_bias ? logit_bias[e] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t t = (int64_t)m0 + wm * (BM / 2) + i * 16 + kq * 4 + r;
+        if (t < T) logits[t * E + e] = acc[i][j][r] + b;
+      }
+  }
+}
+
+template <typename In, int BM, int BN, int NS>
+hipError_t launch_pipe(const void* x, const void* W, const float* logit_bias, float* logits,
+                       int T, int d, int E, hipStream_t s) {
+  const int n_m = (T + BM - 1) / BM;
+  const int n_n = (E + BN - 1) / BN;
+  const int tiles = n_m * n_n;
+  const int per_xcd = (tiles + kXcds - 1) / kXcds;
+  prof_begin(kStageGate, s);
+  hipLaunchKernelGGL((gate_gemm_pipe_kernel<In, BM, BN, NS>), dim3(per_xcd * kXcds),
+                     dim3(kThreads), 0, s, (const In*)x, (const In*)W, logit_bias, logits, T, d,
+                     E, n_m, n_n, per_xcd);
+  prof_end(kStageGate, s);
   return hipGetLastError();
 }
 
+template <typename In, int BM, int BN, int KB>
+hipError_t launch_tile(const void* x, const void* W, const float* logit_bias, float* logits,
+                       int T, int d, int E, hipStream_t s) {
+  const int n_m = (T + BM - 1) / BM;
+  const int n_n = (E + BN - 1) / BN;
+  const int tiles = n_m * n_n;
+  const int per_xcd = (tiles + kXcds - 1) / kXcds;
+  const dim3 grid(per_xcd * kXcds);
+  const bool vec = (d % ElemInfo<In>::kPerChunk == 0) &&
+                   (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
+                   (reinterpret_cast<uintptr_t>(W) % 16 == 0);
+  prof_begin(kStageGate, s);
+  if (vec)
+    hipLaunchKernelGGL((gate_gemm_kernel<In, BM, BN, KB, true>), grid, dim3(kThreads), 0, s,
+                       (const In*)x, (const In*)W, logit_bias, logits, T, d, E, n_m, n_n,
+                       per_xcd);
+  else
+    hipLaunchKernelGGL((gate_gemm_kernel<In, BM, BN, KB, false>), grid, dim3(kThreads), 0, s,
+                       (const In*)x, (const In*)W, logit_bias, logits, T, d, E, n_m, n_n,
+                       per_xcd);
+  prof_end(kStageGate, s);
+  return hipGetLastError();
+}
+
+// Tile shapes (BM x BN) and pipeline depth.  The default takes the largest
+// useful tile that still gives at least kMinTiles workgroups;
+// MOE_GATE_TILE="BMxBN" overrides it (tuning sweeps).
+struct TileChoice {
+  int bm, bn;
+};
+constexpr TileChoice kTiles[] = {{128, 256}, {128, 192}, {64, 384}, {128, 128}, {64, 256},
+                                 {64, 192}, {64, 128}, {32, 256}, {64, 64}, {32, 128},
+                                 {32, 64}, {32, 32}};
+constexpr int kMinTiles = 256;
+
+template <typename In, int BM, int BN, int KB>
+hipError_t launch_ns(int ns, bool pipe, const void* x, const void* W, const float* lb,
+                     float* logits, int T, int d, int E, hipStream_t s) {
+  constexpr int kStage = (BM + BN) * 128;
+  constexpr int kMaxNs = (150 * 1024) / kStage;  // stages that fit in LDS
+  if (!pipe) return launch_tile<In, BM, BN, KB>(x, W, lb, logits, T, d, E, s);
+  if (ns >= 4 && kMaxNs >= 4) return launch_pipe<In, BM, BN, (kMaxNs >= 4 ? 4 : 2)>(x, W, lb, logits, T, d, E, s);
+  if (ns >= 3 && kMaxNs >= 3) return launch_pipe<In, BM, BN, (kMaxNs >= 3 ? 3 : 2)>(x, W, lb, logits, T, d, E, s);
+  return launch_pipe<In, BM, BN, 2>(x, W, lb, logits, T, d, E, s);
+}
+
 template <typename In>
-hipError_t launch_typed(const void* x, const void* W, const float* logit_bias,
-                        float* logits, int T, int d, int E, hipStream_t s) {
-  if (E <= 64) return launch_tile<In, 64, 64>(x, W, logit_bias, logits, T, d, E, s);
-  if (E <= 128) {
-    if (T >= 32768) return launch_tile<In, 128, 128>(x, W, logit_bias, logits, T, d, E, s);
-    return launch_tile<In, 64, 128>(x, W, logit_bias, logits, T, d, E, s);
+hipError_t launch_choice(TileChoice c, int ns, bool pipe, const void* x, const void* W,
+                         const float* lb, float* logits, int T, int d, int E, hipStream_t s) {
+#define MOE_TILE(BM_, BN_, KB_) \
+  if (c.bm == BM_ && c.bn == BN_) return launch_ns<In, BM_, BN_, KB_>(ns, pipe, x, W, lb, logits, T, d, E, s);
+  MOE_TILE(128, 256, 128)
+  MOE_TILE(128, 192, 128)
+  MOE_TILE(64, 384, 128)
+  MOE_TILE(128, 128, 128)
+  MOE_TILE(64, 256, 128)
+  MOE_TILE(64, 192, 128)
+  MOE_TILE(64, 128, 128)
+  MOE_TILE(32, 256, 128)
+  MOE_TILE(64, 64, 256)
+  MOE_TILE(32, 128, 256)
+  MOE_TILE(32, 64, 256)
+  MOE_TILE(32, 32, 256)
+#undef MOE_TILE
+  return hipErrorInvalidValue;
+}
+
+TileChoice choose_tile(int T, int E) {
+  if (const char* env = std::getenv("MOE_GATE_TILE")) {
+    int bm = 0, bn = 0;
+    if (std::sscanf(env, "%dx%d", &bm, &bn) == 2)
+      for (const auto& t : kTiles)
+        if (t.bm == bm && t.bn == bn) return t;
   }
-  if (E <= 256) return launch_tile<In, 32, 256>(x, W, logit_bias, logits, T, d, E, s);
-  return launch_tile<In, 32, 384>(x, W, logit_bias, logits, T, d, E, s);
+  TileChoice best = {0, 0};
+  double best_work = -1.0;
+  TileChoice fallback = {32, 32};
+  double fallback_work = -1.0;
+  for (const auto& t : kTiles) {
+    const int n_n = (E + t.bn - 1) / t.bn;
+    const double useful = (double)E / (n_n * t.bn);  // share of non-padding columns
+    if (useful < 0.74) continue;
+    const long tiles = (long)((T + t.bm - 1) / t.bm) * n_n;
+    const double work = (double)t.bm * t.bn * useful;
+    if (tiles >= kMinTiles && work > best_work) {
+      best = t;
+      best_work = work;
+    }
+    // few tokens: the smallest tile rows with the widest useful N
+    if (t.bm == 32 && work > fallback_work) {
+      fallback = t;
+      fallback_work = work;
+    }
+  }
+  return best_work > 0 ? best : fallback;
 }
 
 }  // namespace
@@ -228,8 +489,22 @@ hipError_t launch_gate_gemm(int32_t dtype, const void* x, const void* W,
                             const float* logit_bias, float* logits, int32_t T,
                             int32_t d, int32_t E, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  if (dtype == 1) return launch_typed<uint16_t>(x, W, logit_bias, logits, T, d, E, stream);
-  return launch_typed<float>(x, W, logit_bias, logits, T, d, E, stream);
+  const TileChoice c = choose_tile(T, E);
+  const int esz = dtype == 1 ? 2 : 4;
+  // the pipelined kernel needs 16-byte aligned rows, whole 128-byte stages
+  // and byte offsets below 2^31
+  const bool pipe = (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
+                    (reinterpret_cast<uintptr_t>(W) % 16 == 0) && ((int64_t)d * esz % 128 == 0) &&
+                    (int64_t)T * d * esz < (1ll << 31) && (int64_t)E * d * esz < (1ll << 31) &&
+                    std::getenv("MOE_GATE_NOPIPE") == nullptr;
+  // pipeline depth: deep rings for small stages; two stages for tiles of
+  // >= 32 KB per stage, which keeps two workgroups per CU (measured best)
+  const int stage_kb = (c.bm + c.bn) * 128 / 1024;
+  int ns = stage_kb >= 32 ? 2 : stage_kb >= 20 ? 3 : 4;
+  if (const char* env = std::getenv("MOE_GATE_NS")) ns = std::atoi(env);
+  if (dtype == 1)
+    return launch_choice<uint16_t>(c, ns, pipe, x, W, logit_bias, logits, T, d, E, stream);
+  return launch_choice<float>(c, ns, pipe, x, W, logit_bias, logits, T, d, E, stream);
 }
 
 }  // namespace moe
