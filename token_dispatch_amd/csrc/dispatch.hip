@@ -30,14 +30,27 @@ constexpr int kMaxE = 1024;
 constexpr int kScanWaves = 16;                          // experts per scan workgroup
 constexpr int kScanPrefetch = 8;                        // chunks of 64 tiles in registers
 
-__device__ __forceinline__ int load_id(const int32_t* __restrict__ ids, int64_t r, int64_t R,
-                                       int E, int* err) {
-  int e = (r < R) ? ids[r] : -1;
-  if (e >= E) {
-    ++*err;
-    e = -1;
+// This wave's kChunksPerWave chunks of 64 routes starting at r0 (ids >= E
+// count as errors and become -1).  All loads are issued before any is used:
+// clamped addresses, validity applied afterwards.
+__device__ __forceinline__ void load_chunks(const int32_t* __restrict__ ids, int64_t r0,
+                                            int64_t R, int E, int (&e)[kChunksPerWave],
+                                            int* err) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int ch = 0; ch < kChunksPerWave; ++ch) {
+    const int64_t r = r0 + ch * kWave + lane;
+    e[ch] = ids[r < R ? r : R - 1];
   }
-  return e;
+#pragma unroll
+  for (int ch = 0; ch < kChunksPerWave; ++ch) {
+    const int64_t r = r0 + ch * kWave + lane;
+    if (r >= R) e[ch] = -1;
+    if (e[ch] >= E) {
+      ++*err;
+      e[ch] = -1;
+    }
+  }
 }
 
 // Mask of the lanes whose (valid) id equals this lane's id.
@@ -52,14 +65,13 @@ __device__ __forceinline__ uint64_t peer_mask(int e, int nbits) {
 }
 
 // Count this wave's chunks into its LDS row.
-__device__ __forceinline__ void count_chunks(const int32_t* __restrict__ ids, int64_t r0,
-                                             int64_t R, int E, int nbits, int32_t* row,
-                                             int* err) {
+__device__ __forceinline__ void count_chunks(const int (&e)[kChunksPerWave], int nbits,
+                                             int32_t* row) {
   const uint64_t below = lanemask_lt();
+#pragma unroll
   for (int ch = 0; ch < kChunksPerWave; ++ch) {
-    const int e = load_id(ids, r0 + ch * kWave + __lane_id(), R, E, err);
-    const uint64_t p = peer_mask(e, nbits);
-    if (e >= 0 && (p & below) == 0) row[e] += __popcll(p);
+    const uint64_t p = peer_mask(e[ch], nbits);
+    if (e[ch] >= 0 && (p & below) == 0) row[e[ch]] += __popcll(p);
   }
 }
 
@@ -68,11 +80,12 @@ __global__ __launch_bounds__(kThreads) void disp_hist_kernel(
     int32_t* __restrict__ tile_hist, int32_t* __restrict__ dev_err) {
   __shared__ int32_t wh[kWaves][kMaxE];
   const int tid = threadIdx.x, wave = tid >> 6;
+  int err = 0;
+  int ev[kChunksPerWave];
+  load_chunks(ids, (int64_t)blockIdx.x * kTile + wave * (kChunksPerWave * kWave), R, E, ev, &err);
   for (int e = tid & 63; e < E; e += kWave) wh[wave][e] = 0;
   __syncthreads();
-  int err = 0;
-  const int64_t r0 = (int64_t)blockIdx.x * kTile + wave * (kChunksPerWave * kWave);
-  count_chunks(ids, r0, R, E, nbits, wh[wave], &err);
+  count_chunks(ev, nbits, wh[wave]);
   __syncthreads();
   for (int e = tid; e < E; e += kThreads)
     tile_hist[(int64_t)e * nt + blockIdx.x] = wh[0][e] + wh[1][e] + wh[2][e] + wh[3][e];
@@ -118,6 +131,11 @@ __global__ __launch_bounds__(kThreads) void disp_scatter_kernel(
   __shared__ int32_t wsum[kWaves];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
 
+  int err = 0;
+  int ev[kChunksPerWave];
+  const int64_t r0 = (int64_t)blockIdx.x * kTile + wave * (kChunksPerWave * kWave);
+  if ((int)blockIdx.x < nt) load_chunks(ids, r0, R, E, ev, &err);
+
   // offsets: exclusive scan of totals over experts (4 experts per thread)
   int t4[4], s = 0;
 #pragma unroll
@@ -147,9 +165,7 @@ __global__ __launch_bounds__(kThreads) void disp_scatter_kernel(
   if (blockIdx.x == 0 && tid == kThreads - 1) offsets[E] = base;
   if ((int)blockIdx.x >= nt) return;  // only when there are no routes at all
 
-  int err = 0;
-  const int64_t r0 = (int64_t)blockIdx.x * kTile + wave * (kChunksPerWave * kWave);
-  count_chunks(ids, r0, R, E, nbits, wh[wave], &err);
+  count_chunks(ev, nbits, wh[wave]);
   __syncthreads();
   // per-wave starting positions of each expert inside this tile
   for (int e = tid; e < E; e += kThreads) {
@@ -163,9 +179,10 @@ __global__ __launch_bounds__(kThreads) void disp_scatter_kernel(
   __syncthreads();
   const uint64_t below = lanemask_lt();
   int32_t* row = wh[wave];
+#pragma unroll
   for (int ch = 0; ch < kChunksPerWave; ++ch) {
     const int64_t r = r0 + ch * kWave + lane;
-    const int e = load_id(ids, r, R, E, &err);
+    const int e = ev[ch];
     const uint64_t p = peer_mask(e, nbits);
     int pos = -1;
     if (e >= 0) {
