@@ -156,7 +156,6 @@ def main():
     W = up(inp["W"])
     lb, sb, kpt = up(inp["logit_bias"]), up(inp["select_bias"]), up(inp["k_per_token"])
     T, E, k = w.T, w.E, w.k
-    logits = torch.empty((T, E), dtype=torch.float32, device=dev)
     ids = torch.empty((T, k), dtype=torch.int32, device=dev)
     weights = torch.empty((T, k), dtype=torch.float32, device=dev)
     counts = torch.empty(E, dtype=torch.int32, device=dev)
@@ -164,13 +163,17 @@ def main():
     perm = torch.empty(T * k, dtype=torch.int32, device=dev)
     inv = torch.empty(T * k, dtype=torch.int32, device=dev)
     ws = torch.empty(max(1, tda.dispatch_workspace_size(T, k, E)), dtype=torch.uint8, device=dev)
+    route_ws = torch.empty(max(1, tda.route_workspace_size(
+        T, w.d, E, k, 1 if w.dtype == "bf16" else 0, score=w.score, n_groups=w.n_groups,
+        topk_groups=w.topk_groups, group_score=w.group_score if w.n_groups > 1 else "max",
+        renormalize=w.renormalize, route_scale=w.route_scale)), dtype=torch.uint8, device=dev)
     rkw = dict(score=w.score, logit_bias=lb, select_bias=sb, k_per_token=kpt,
                n_groups=w.n_groups, topk_groups=w.topk_groups,
                group_score=w.group_score if w.n_groups > 1 else None,
                renormalize=w.renormalize, route_scale=w.route_scale)
 
     def step(i):
-        tda.route(xs[i % n_copies], W, k, logits=logits, ids=ids, weights=weights, **rkw)
+        tda.route(xs[i % n_copies], W, k, ids=ids, weights=weights, workspace=route_ws, **rkw)
         tda.dispatch(ids, E, counts=counts, offsets=offsets, perm=perm, inv=inv, workspace=ws)
 
     log(f"[bench] {n_copies} rotating copies of x ({xbytes / 1e6:.1f} MB each); "

@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 /* return codes */
 #define MOE_OK 0
@@ -116,12 +116,19 @@ typedef struct {
  *                weights alike)
  *   select_bias  [E] fp32 or NULL: added to the selection score only
  *   k_per_token  [T] int32 in [1, k] or NULL (= k for every token)
- *   logits       [T][E] fp32.  With x and W: the gate writes l here (logit
- *                bias included); may be NULL, then the fused gate+select path
- *                runs and no logits are written.  Select-only mode: the
- *                input logits (logit_bias, if given, is added on read).
+ *   logits       [T][E] fp32 or NULL.  With x and W: if not NULL, the gate
+ *                logits l (logit bias included) are written here.  Select-only
+ *                mode: the input logits (required; logit_bias, if given, is
+ *                added on read).
  *   ids          [T][k] int32 out
  *   weights      [T][k] fp32 out
+ *   workspace    device scratch of workspace_bytes >=
+ *                moe_route_workspace_size(p) bytes, or NULL/0.  It carries the
+ *                gate's fp32 hand-off (split over K when that moves fewer
+ *                bytes).  With logits given and too small a workspace the gate
+ *                runs unsplit and hands off through logits; with neither it is
+ *                MOE_EINVAL.  Contents need no initialisation and are
+ *                clobbered.
  *   dev_err      [1] int32 or NULL: incremented per token whose k_per_token
  *                entry is outside [1, k]
  * Limits: k <= MOE_MAX_K, E <= MOE_MAX_EXPERTS, n_groups <= MOE_MAX_GROUPS,
@@ -131,7 +138,12 @@ typedef struct {
 int32_t moe_route(const moe_route_params* p, const void* x, const void* W,
                   const float* logit_bias, const float* select_bias,
                   const int32_t* k_per_token, float* logits, int32_t* ids,
-                  float* weights, int32_t* dev_err, void* stream);
+                  float* weights, void* workspace, size_t workspace_bytes,
+                  int32_t* dev_err, void* stream);
+
+/* Bytes of device workspace moe_route uses for these parameters (16-byte
+ * aligned x and W assumed; 0 when none is needed). */
+size_t moe_route_workspace_size(const moe_route_params* p);
 
 /*
  * moe_route_hash -- hash routing (ferrox_moe docs, route_hash: a DeepSeek-V4

@@ -20,8 +20,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    assert {"moe_route", "moe_route_hash", "moe_dispatch", "moe_dispatch_workspace_size",
-            "moe_last_error", "moe_abi_version"} <= set(names), names
+    assert {"moe_route", "moe_route_workspace_size", "moe_route_hash", "moe_dispatch",
+            "moe_dispatch_workspace_size", "moe_last_error", "moe_abi_version"} <= set(names), names
 
 
 def test_library_exports_every_declared_symbol():
@@ -58,7 +58,7 @@ def call_route(**over):
     kw.update(over)
     p = tda.make_params(**kw)
     return tda.lib().moe_route(ctypes.byref(p), FAKE, FAKE, None, None, None, FAKE, FAKE,
-                               FAKE, None, None)
+                               FAKE, None, 0, None, None)
 
 
 @pytest.mark.parametrize("over,code,text", [
@@ -86,20 +86,33 @@ def test_route_rejects_bad_params(over, code, text):
 def test_route_rejects_half_select_only_and_missing_outputs():
     p = tda.make_params(16, 64, 8, 2)
     L = tda.lib()
-    assert L.moe_route(ctypes.byref(p), FAKE, None, None, None, None, FAKE, FAKE, FAKE, None,
-                       None) == tda.MOE_EINVAL
-    assert L.moe_route(ctypes.byref(p), None, None, None, None, None, None, FAKE, FAKE, None,
-                       None) == tda.MOE_EINVAL
-    assert L.moe_route(ctypes.byref(p), FAKE, FAKE, None, None, None, FAKE, None, FAKE, None,
-                       None) == tda.MOE_EINVAL
-    assert L.moe_route(None, FAKE, FAKE, None, None, None, FAKE, FAKE, FAKE, None,
-                       None) == tda.MOE_EINVAL
+    assert L.moe_route(ctypes.byref(p), FAKE, None, None, None, None, FAKE, FAKE, FAKE, None, 0,
+                       None, None) == tda.MOE_EINVAL
+    assert L.moe_route(ctypes.byref(p), None, None, None, None, None, None, FAKE, FAKE, None, 0,
+                       None, None) == tda.MOE_EINVAL
+    assert L.moe_route(ctypes.byref(p), FAKE, FAKE, None, None, None, FAKE, None, FAKE, None, 0,
+                       None, None) == tda.MOE_EINVAL
+    assert L.moe_route(None, FAKE, FAKE, None, None, None, FAKE, FAKE, FAKE, None, 0,
+                       None, None) == tda.MOE_EINVAL
+    # neither logits nor enough workspace for the gate hand-off
+    assert L.moe_route(ctypes.byref(p), FAKE, FAKE, None, None, None, None, FAKE, FAKE, FAKE, 16,
+                       None, None) == tda.MOE_EINVAL
+    assert "workspace" in L.moe_last_error().decode()
 
 
 def test_route_T0_is_a_noop():
     p = tda.make_params(0, 64, 8, 2)
     assert tda.lib().moe_route(ctypes.byref(p), FAKE, FAKE, None, None, None, None, None, None,
-                               None, None) == tda.MOE_OK
+                               None, 0, None, None) == tda.MOE_OK
+    assert tda.route_workspace_size(0, 64, 8, 2) == 0
+
+
+def test_route_workspace_size_covers_the_hand_off():
+    # at least one fp32 logit per (token, expert); a multiple of it (K split)
+    for T, d, E, k in [(4096, 2048, 128, 16), (8192, 7168, 256, 8), (256, 1024, 8, 2),
+                       (65536, 2880, 128, 4), (5, 7, 3, 1)]:
+        n = tda.route_workspace_size(T, d, E, k)
+        assert n >= T * E * 4 and n % (T * E * 4) == 0 and n // (T * E * 4) <= 8
 
 
 def test_route_hash_validation():

@@ -39,9 +39,13 @@ def test_graph_replays_match_eager(name):
     perm = torch.empty(T * k, dtype=torch.int32, device=dev)
     inv = torch.empty(T * k, dtype=torch.int32, device=dev)
     ws = torch.empty(max(1, tda.dispatch_workspace_size(T, k, E)), dtype=torch.uint8, device=dev)
+    rws = torch.empty(max(1, tda.route_workspace_size(T, w.d, E, k, 1, score=w.score,
+                                                      n_groups=w.n_groups,
+                                                      topk_groups=w.topk_groups)),
+                      dtype=torch.uint8, device=dev)
 
     def step():
-        tda.route(x, W, k, logits=logits, ids=ids, weights=weights, **kw)
+        tda.route(x, W, k, logits=logits, ids=ids, weights=weights, workspace=rws, **kw)
         tda.dispatch(ids, E, counts=counts, offsets=offsets, perm=perm, inv=inv, workspace=ws)
 
     say("graph", name)

@@ -250,3 +250,42 @@ def test_workload_full_size_sampled(name):
     assert np.all(srt[:, 1:] != srt[:, :-1])  # distinct experts per token
     d = tda.dispatch(ids, w.E)
     check_dispatch(d, oracle.dispatch(gids, w.E))
+
+
+@pytest.mark.parametrize("splits", ["1", "2", "4", "8"])
+def test_gate_k_split_matches_oracle(splits, monkeypatch):
+    """Every K split of the gate (partial sums added in order by the select
+    kernel) gives the oracle's routes; integer inputs stay bit-exact."""
+    monkeypatch.setenv("MOE_GATE_SPLITS", splits)
+    monkeypatch.setenv("MOE_GATE_TILE", "64x128")
+    w = wl.WORKLOADS["qwen3_dynk"]
+    inp = wl.make_inputs(w, T=520)
+    say("gate split", splits)
+    ids, stats = route_case(w, inp)
+    rng = np.random.default_rng(int(splits))
+    x = rng.integers(-4, 5, size=(130, 2048)).astype(np.float32)
+    Wi = rng.integers(-4, 5, size=(128, 2048)).astype(np.float32)
+    exp = (x.astype(np.int64) @ Wi.astype(np.int64).T).astype(np.float32)
+    _, _, logits = tda.route(up(wl.f32_to_bf16_bits(x)), up(wl.f32_to_bf16_bits(Wi)), 4,
+                             return_logits=True)
+    np.testing.assert_array_equal(down(logits), exp)
+
+
+@pytest.mark.parametrize("rb", ["128", "256", "512"])
+@pytest.mark.parametrize("tile,d", [("32x64", 2880), ("64x128", 1000), ("128x128", 2056),
+                                    ("32x256", 7168)])
+def test_gate_stage_lengths_exact(rb, tile, d, monkeypatch):
+    """Every stage length of the pipelined gate, on rows that end inside a
+    stage (d * 2 bytes not a multiple of the stage): integer bf16 inputs make
+    the fp32 result exact, so logits must equal the integer product."""
+    monkeypatch.setenv("MOE_GATE_RB", rb)
+    monkeypatch.setenv("MOE_GATE_TILE", tile)
+    rng = np.random.default_rng([int(rb), d])
+    T, E = 300, 136
+    x = rng.integers(-3, 4, size=(T, d)).astype(np.float32)
+    Wi = rng.integers(-3, 4, size=(E, d)).astype(np.float32)
+    exp = (x.astype(np.int64) @ Wi.astype(np.int64).T).astype(np.float32)
+    say("gate stage", rb, tile, d)
+    _, _, logits = tda.route(up(wl.f32_to_bf16_bits(x)), up(wl.f32_to_bf16_bits(Wi)), 4,
+                             return_logits=True)
+    np.testing.assert_array_equal(down(logits), exp)

@@ -21,12 +21,13 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe_route.so")
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EDEVICE = 0, -1, -2, -3
 MAX_EXPERTS, MAX_K, MAX_GROUPS = 1024, 32, 64
 SCORES = {"softmax": 0, "sigmoid": 1, "sqrt_softplus": 2, "softmax_topk": 3}
 GROUP_SCORES = {"max": 0, "top2_sum": 1}
-EXPORTS = ("moe_route", "moe_route_hash", "moe_dispatch_workspace_size", "moe_dispatch",
+EXPORTS = ("moe_route", "moe_route_workspace_size", "moe_route_hash",
+           "moe_dispatch_workspace_size", "moe_dispatch",
            "moe_profile_enable", "moe_profile_read", "moe_last_error", "moe_abi_version")
 STAGES = ("gate", "select", "hash", "disp_hist", "disp_scan", "disp_scatter")
 
@@ -58,8 +59,10 @@ def lib() -> ctypes.CDLL:
                               "`python -m token_dispatch_amd._build` (hipcc, gfx950)")
         L = ctypes.CDLL(LIB_PATH)
         vp, i32, P = ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(RouteParams)
-        L.moe_route.argtypes = [P] + [vp] * 10
+        L.moe_route.argtypes = [P] + [vp] * 9 + [ctypes.c_size_t, vp, vp]
         L.moe_route.restype = i32
+        L.moe_route_workspace_size.argtypes = [P]
+        L.moe_route_workspace_size.restype = ctypes.c_size_t
         L.moe_route_hash.argtypes = [P, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp]
         L.moe_route_hash.restype = i32
         L.moe_dispatch_workspace_size.argtypes = [i32, i32, i32]
@@ -122,18 +125,27 @@ def make_params(T, d, E, k, dtype=1, score="softmax", n_groups=1, topk_groups=No
                        GROUP_SCORES[group_score], int(bool(renormalize)), float(route_scale))
 
 
+def route_workspace_size(T, d, E, k, dtype=1, **kw) -> int:
+    """Device bytes moe_route uses as its gate hand-off for these shapes."""
+    p = make_params(T, d, E, k, dtype, **kw)
+    return int(lib().moe_route_workspace_size(ctypes.byref(p)))
+
+
 def route(x: Optional[torch.Tensor], W: Optional[torch.Tensor], k: int, *,
           score: str = "softmax", logit_bias=None, select_bias=None, k_per_token=None,
           n_groups: int = 1, topk_groups: Optional[int] = None,
           group_score: Optional[str] = None, renormalize: bool = True,
           route_scale: float = 1.0, logits: Optional[torch.Tensor] = None,
-          E: Optional[int] = None, ids=None, weights=None, dev_err=None,
+          E: Optional[int] = None, ids=None, weights=None, workspace=None, dev_err=None,
           return_logits: bool = False):
     """Gate + score + (grouped) top-k + weights.  Returns (ids, weights[, logits]).
 
     x [T][d] and W [E][d] (float32 or bfloat16); or x = W = None with
-    ``logits`` [T][E] float32 as the input (select-only mode).
-    group_score defaults to "top2_sum" when select_bias is given, else "max".
+    ``logits`` [T][E] float32 as the input (select-only mode).  The gate
+    logits are written to ``logits`` when one is passed (or return_logits).
+    ``workspace`` (uint8 device tensor) carries the gate's hand-off; it is
+    allocated when not given.  group_score defaults to "top2_sum" when
+    select_bias is given, else "max".
     """
     if group_score is None:
         group_score = "top2_sum" if select_bias is not None else "max"
@@ -151,9 +163,10 @@ def route(x: Optional[torch.Tensor], W: Optional[torch.Tensor], k: int, *,
         if W.shape[1] != d:
             raise ValueError("W must be [E][d] with the d of x")
         dt, device = _dtype_code(x), x.device
-        if logits is None:
+        if logits is None and return_logits:
             logits = torch.empty((T, E_), dtype=torch.float32, device=device)
-        _dev(logits, "logits", torch.float32, (T, E_))
+        if logits is not None:
+            _dev(logits, "logits", torch.float32, (T, E_))
     if E is not None and E != E_:
         raise ValueError("E does not match W / logits")
     for name, b in (("logit_bias", logit_bias), ("select_bias", select_bias)):
@@ -171,9 +184,14 @@ def route(x: Optional[torch.Tensor], W: Optional[torch.Tensor], k: int, *,
         _dev(dev_err, "dev_err", torch.int32, (1,))
     p = make_params(T, d, E_, k, dt, score, n_groups, topk_groups, group_score, renormalize,
                     route_scale)
+    if workspace is None and x is not None:
+        nbytes = int(lib().moe_route_workspace_size(ctypes.byref(p)))
+        if nbytes:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().moe_route(ctypes.byref(p), _p(x), _p(W), _p(logit_bias), _p(select_bias),
-                           _p(k_per_token), _p(logits), _p(ids), _p(weights), _p(dev_err),
-                           _stream(device)))
+                           _p(k_per_token), _p(logits), _p(ids), _p(weights), _p(workspace),
+                           ws_bytes, _p(dev_err), _stream(device)))
     return (ids, weights, logits) if return_logits else (ids, weights)
 
 

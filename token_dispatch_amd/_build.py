@@ -3,7 +3,10 @@
 Every source is compiled with hipcc for gfx950 only, in parallel, then
 linked into one shared library exporting the C ABI of include/moe_route.h.
 Packed-fp32 instructions are disabled in device code
-(``-target-feature -packed-fp32-ops``).
+(``-target-feature -packed-fp32-ops``).  Matrix-core results are formed in
+ordinary VGPRs (``-amdgpu-mfma-vgpr-form``): with accumulators in AGPRs the
+register allocator rotates the gate's accumulator tiles through copies on
+every pipeline stage.
 """
 from __future__ import annotations
 
@@ -24,6 +27,7 @@ ARCH = "gfx950"
 
 CFLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form=1",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC,
           "-Wall", "-Wno-unused-result"]
 

@@ -34,15 +34,29 @@ struct RouteCfg {
   float route_scale;
 };
 
-// logits[T][E] = x[T][d] . W[E][d]^T (+ logit_bias); dtype MOE_F32 / MOE_BF16.
-hipError_t launch_gate_gemm(int32_t dtype, const void* x, const void* W,
-                            const float* logit_bias, float* logits, int32_t T,
-                            int32_t d, int32_t E, hipStream_t stream);
+// How the gate contraction is tiled: BM x BN tiles, an NS-stage LDS ring of
+// stages holding RB bytes of K per tile row, K split over `splits`
+// workgroups (partial sums added by the select kernel), pipelined (buffer ->
+// LDS copies) or the general register-staged kernel.
+struct GatePlan {
+  int bm, bn, ns, rb, splits;
+  bool pipe;
+};
+GatePlan plan_gate(int32_t T, int32_t d, int32_t E, int32_t dtype, bool aligned,
+                   bool allow_split);
 
-// Score + (grouped) top-k + weights from fp32 logits.
-hipError_t launch_select(const RouteCfg& c, const float* logits,
-                         const float* logit_bias, const float* select_bias,
-                         const int32_t* k_per_token, int32_t* ids,
+// out[s][T][E] (s < g.splits) = partial x[T][d] . W[E][d]^T over the s-th K
+// range (+ logit_bias in s = 0); dtype MOE_F32 / MOE_BF16.
+hipError_t launch_gate_gemm(const GatePlan& g, int32_t dtype, const void* x, const void* W,
+                            const float* logit_bias, float* out, int32_t T, int32_t d,
+                            int32_t E, hipStream_t stream);
+
+// Score + (grouped) top-k + weights.  The logits are the sum of `splits`
+// fp32 partial arrays `split_stride` floats apart (summed in order); when
+// logits_out is not NULL the summed logits are written there.
+hipError_t launch_select(const RouteCfg& c, const float* logits, int32_t splits,
+                         int64_t split_stride, float* logits_out, const float* logit_bias,
+                         const float* select_bias, const int32_t* k_per_token, int32_t* ids,
                          float* weights, int32_t* dev_err, hipStream_t stream);
 
 // Hash routing: table gather (+ k gathered gate dot products and weights).

@@ -91,6 +91,32 @@ void prof_clear_locked() {
   g_prof_records.clear();
 }
 
+// Every check of moe_route's parameters (shape, flags, limits).
+int32_t check_route_params(const moe_route_params* p, bool need_d) {
+  int32_t rc = check_common(p, need_d);
+  if (rc != MOE_OK) return rc;
+  if (p->k > p->E) return fail(MOE_EINVAL, "k=%d exceeds E=%d", p->k, p->E);
+  if (p->n_groups < 1) return fail(MOE_EINVAL, "n_groups=%d must be >= 1", p->n_groups);
+  if (p->n_groups > MOE_MAX_GROUPS)
+    return fail(MOE_EUNSUPPORTED, "n_groups=%d exceeds MOE_MAX_GROUPS=%d", p->n_groups,
+                MOE_MAX_GROUPS);
+  if (p->E % p->n_groups != 0)
+    return fail(MOE_EINVAL, "n_groups=%d does not divide E=%d", p->n_groups, p->E);
+  if (p->topk_groups < 1 || p->topk_groups > p->n_groups)
+    return fail(MOE_EINVAL, "topk_groups=%d must be in [1, n_groups=%d]", p->topk_groups,
+                p->n_groups);
+  if (p->group_score != MOE_GROUP_MAX && p->group_score != MOE_GROUP_TOP2_SUM)
+    return fail(MOE_EINVAL, "group_score=%d is not a MOE_GROUP_* value", p->group_score);
+  const int32_t gs = p->E / p->n_groups;
+  if ((int64_t)p->k > (int64_t)p->topk_groups * gs)
+    return fail(MOE_EINVAL, "k=%d exceeds the %d experts of the kept groups", p->k,
+                p->topk_groups * gs);
+  if (p->n_groups > 1 && p->group_score == MOE_GROUP_TOP2_SUM && gs < 2)
+    return fail(MOE_EINVAL, "MOE_GROUP_TOP2_SUM needs groups of at least 2 experts");
+  if ((int64_t)p->T * p->E > kI32Max) return fail(MOE_EUNSUPPORTED, "T*E must be below 2^31");
+  return MOE_OK;
+}
+
 }  // namespace
 
 namespace moe {
@@ -152,52 +178,55 @@ const char* moe_last_error(void) { return g_last_error.c_str(); }
 int32_t moe_route(const moe_route_params* p, const void* x, const void* W,
                   const float* logit_bias, const float* select_bias,
                   const int32_t* k_per_token, float* logits, int32_t* ids,
-                  float* weights, int32_t* dev_err, void* stream) {
+                  float* weights, void* workspace, size_t workspace_bytes,
+                  int32_t* dev_err, void* stream) {
   const bool select_only = (x == nullptr && W == nullptr);
-  int32_t rc = check_common(p, !select_only);
+  int32_t rc = check_route_params(p, !select_only);
   if (rc != MOE_OK) return rc;
   if (p->T > 0 && (x == nullptr) != (W == nullptr))
     return fail(MOE_EINVAL, "x and W must both be set or both be NULL");
-  if (p->k > p->E) return fail(MOE_EINVAL, "k=%d exceeds E=%d", p->k, p->E);
-  if (p->n_groups < 1) return fail(MOE_EINVAL, "n_groups=%d must be >= 1", p->n_groups);
-  if (p->n_groups > MOE_MAX_GROUPS)
-    return fail(MOE_EUNSUPPORTED, "n_groups=%d exceeds MOE_MAX_GROUPS=%d", p->n_groups,
-                MOE_MAX_GROUPS);
-  if (p->E % p->n_groups != 0)
-    return fail(MOE_EINVAL, "n_groups=%d does not divide E=%d", p->n_groups, p->E);
-  if (p->topk_groups < 1 || p->topk_groups > p->n_groups)
-    return fail(MOE_EINVAL, "topk_groups=%d must be in [1, n_groups=%d]", p->topk_groups,
-                p->n_groups);
-  if (p->group_score != MOE_GROUP_MAX && p->group_score != MOE_GROUP_TOP2_SUM)
-    return fail(MOE_EINVAL, "group_score=%d is not a MOE_GROUP_* value", p->group_score);
-  const int32_t gs = p->E / p->n_groups;
-  if ((int64_t)p->k > (int64_t)p->topk_groups * gs)
-    return fail(MOE_EINVAL, "k=%d exceeds the %d experts of the kept groups", p->k,
-                p->topk_groups * gs);
-  if (p->n_groups > 1 && p->group_score == MOE_GROUP_TOP2_SUM && gs < 2)
-    return fail(MOE_EINVAL, "MOE_GROUP_TOP2_SUM needs groups of at least 2 experts");
-  if ((int64_t)p->T * p->E > kI32Max)
-    return fail(MOE_EUNSUPPORTED, "T*E must be below 2^31");
-  if (p->T > 0) {
-    if (!ids || !weights) return fail(MOE_EINVAL, "ids and weights are required");
-    if (!logits) {
-      if (select_only) return fail(MOE_EINVAL, "select-only mode (x = W = NULL) needs logits");
-      return fail(MOE_EUNSUPPORTED, "logits == NULL (fused gate+select) is not available");
-    }
-  }
   if (p->T == 0) return MOE_OK;
+  if (!ids || !weights) return fail(MOE_EINVAL, "ids and weights are required");
+  if (select_only && !logits)
+    return fail(MOE_EINVAL, "select-only mode (x = W = NULL) needs logits");
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const moe::RouteCfg c = to_cfg(p);
   hipError_t e;
-  if (!select_only) {
-    e = moe::launch_gate_gemm(p->dtype, x, W, logit_bias, logits, p->T, p->d, p->E, s);
-    if (e != hipSuccess) return device_fail(e, "gate GEMM launch");
+  if (select_only) {
+    e = moe::launch_select(c, logits, 1, 0, nullptr, logit_bias, select_bias, k_per_token, ids,
+                           weights, dev_err, s);
+    if (e != hipSuccess) return device_fail(e, "select launch");
+    return MOE_OK;
   }
-  e = moe::launch_select(c, logits, select_only ? logit_bias : nullptr, select_bias,
-                         k_per_token, ids, weights, dev_err, s);
+  const bool aligned = reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
+                       reinterpret_cast<uintptr_t>(W) % 16 == 0;
+  moe::GatePlan g = moe::plan_gate(p->T, p->d, p->E, p->dtype, aligned, true);
+  const size_t te = (size_t)p->T * p->E * sizeof(float);
+  float* hand_off = nullptr;
+  if (workspace && workspace_bytes >= te * g.splits) {
+    hand_off = static_cast<float*>(workspace);
+    if (g.splits == 1 && logits) hand_off = logits;
+  } else if (logits) {
+    g = moe::plan_gate(p->T, p->d, p->E, p->dtype, aligned, false);
+    hand_off = logits;  // no room for partial sums: unsplit, through logits
+  } else {
+    return fail(MOE_EINVAL, "workspace of %zu bytes is below the %zu needed (or pass logits)",
+                workspace_bytes, te * g.splits);
+  }
+  e = moe::launch_gate_gemm(g, p->dtype, x, W, logit_bias, hand_off, p->T, p->d, p->E, s);
+  if (e != hipSuccess) return device_fail(e, "gate GEMM launch");
+  e = moe::launch_select(c, hand_off, g.splits, (int64_t)p->T * p->E,
+                         g.splits > 1 ? logits : nullptr, nullptr, select_bias, k_per_token, ids,
+                         weights, dev_err, s);
   if (e != hipSuccess) return device_fail(e, "select launch");
   return MOE_OK;
+}
+
+size_t moe_route_workspace_size(const moe_route_params* p) {
+  if (check_route_params(p, true) != MOE_OK || p->T == 0) return 0;
+  const moe::GatePlan g = moe::plan_gate(p->T, p->d, p->E, p->dtype, true, true);
+  return (size_t)p->T * p->E * sizeof(float) * g.splits;
 }
 
 int32_t moe_route_hash(const moe_route_params* p, const int32_t* token_ids,

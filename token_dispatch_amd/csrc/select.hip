@@ -144,10 +144,13 @@ __device__ __forceinline__ Top2 shfl_xor_top2(Top2 x, int off) {
   return r;
 }
 
-// Requires n_groups <= LPT (one lane per group for the ranking).
-template <int LPT, int VPL>
+// Requires n_groups <= LPT (one lane per group for the ranking).  The
+// logits are the sum of NSPLIT partial arrays `split_stride` floats apart (a K
+// split of the gate), added in a fixed order.
+template <int LPT, int VPL, int NSPLIT>
 __global__ __launch_bounds__(kWavesPerBlock * kWave) void select_kernel(
-    RouteCfg c, const float* __restrict__ logits, const float* __restrict__ logit_bias,
+    RouteCfg c, const float* __restrict__ logits, int64_t split_stride,
+    float* __restrict__ logits_out, const float* __restrict__ logit_bias,
     const float* __restrict__ select_bias, const int32_t* __restrict__ k_per_token,
     int32_t* __restrict__ ids, float* __restrict__ weights, int32_t* __restrict__ dev_err) {
   using S = Seg<LPT>;
@@ -165,9 +168,24 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void select_kernel(
   // Unconditional loads from clamped addresses, masked afterwards: a load
   // under a per-slot condition would be waited on before the next one.
   const int64_t trow = tok_ok ? t : t0;
+  float pv[NSPLIT][VPL];
+#pragma unroll
+  for (int sp = 0; sp < NSPLIT; ++sp)
+#pragma unroll
+    for (int j = 0; j < VPL; ++j)
+      pv[sp][j] = logits[sp * split_stride + trow * E + min(e0 + j, E - 1)];
   float lv[VPL];
 #pragma unroll
-  for (int j = 0; j < VPL; ++j) lv[j] = logits[trow * E + min(e0 + j, E - 1)];
+  for (int j = 0; j < VPL; ++j) {
+    lv[j] = pv[0][j];
+#pragma unroll
+    for (int sp = 1; sp < NSPLIT; ++sp) lv[j] += pv[sp][j];
+  }
+  if (NSPLIT > 1 && logits_out && tok_ok) {
+#pragma unroll
+    for (int j = 0; j < VPL; ++j)
+      if (e0 + j < E) logits_out[t * E + e0 + j] = lv[j];
+  }
   if (logit_bias) {
 #pragma unroll
     for (int j = 0; j < VPL; ++j) lv[j] += logit_bias[min(e0 + j, E - 1)];
@@ -335,32 +353,51 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void select_kernel(
   }
 }
 
-template <int LPT, int VPL>
-hipError_t launch_vpl(const RouteCfg& c, const float* logits, const float* logit_bias,
-                      const float* select_bias, const int32_t* k_per_token, int32_t* ids,
-                      float* weights, int32_t* dev_err, hipStream_t s) {
+template <int LPT, int VPL, int S>
+hipError_t launch_vpl(const RouteCfg& c, const float* logits, int64_t stride, float* logits_out,
+                      const float* logit_bias, const float* select_bias,
+                      const int32_t* k_per_token, int32_t* ids, float* weights, int32_t* dev_err,
+                      hipStream_t s) {
   constexpr int tokens_per_block = kWavesPerBlock * (kWave / LPT);
   const int64_t blocks = ((int64_t)c.T + tokens_per_block - 1) / tokens_per_block;
   prof_begin(kStageSelect, s);
-  hipLaunchKernelGGL((select_kernel<LPT, VPL>), dim3((uint32_t)blocks),
-                     dim3(kWavesPerBlock * kWave), 0, s, c, logits, logit_bias, select_bias,
-                     k_per_token, ids, weights, dev_err);
+  hipLaunchKernelGGL((select_kernel<LPT, VPL, S>), dim3((uint32_t)blocks),
+                     dim3(kWavesPerBlock * kWave), 0, s, c, logits, stride, logits_out,
+                     logit_bias, select_bias, k_per_token, ids, weights, dev_err);
   prof_end(kStageSelect, s);
   return hipGetLastError();
 }
 
+template <int LPT, int VPL>
+hipError_t launch_splits(const RouteCfg& c, const float* logits, int splits, int64_t stride,
+                         float* logits_out, const float* logit_bias, const float* select_bias,
+                         const int32_t* k_per_token, int32_t* ids, float* weights,
+                         int32_t* dev_err, hipStream_t s) {
+#define MOE_S(S_)                                                                              \
+  return launch_vpl<LPT, VPL, S_>(c, logits, stride, logits_out, logit_bias, select_bias,      \
+                                  k_per_token, ids, weights, dev_err, s)
+  if constexpr (VPL <= 8) {
+    if (splits == 2) MOE_S(2);
+    if (splits == 4) MOE_S(4);
+    if (splits == 8) MOE_S(8);
+  }
+  if (splits != 1) return hipErrorInvalidValue;
+  MOE_S(1);
+#undef MOE_S
+}
+
 }  // namespace
 
-hipError_t launch_select(const RouteCfg& c, const float* logits,
-                         const float* logit_bias, const float* select_bias,
-                         const int32_t* k_per_token, int32_t* ids,
+hipError_t launch_select(const RouteCfg& c, const float* logits, int32_t splits,
+                         int64_t split_stride, float* logits_out, const float* logit_bias,
+                         const float* select_bias, const int32_t* k_per_token, int32_t* ids,
                          float* weights, int32_t* dev_err, hipStream_t stream) {
   if (c.T == 0) return hipSuccess;
   const int E = c.E;
   const bool few_groups = c.n_groups <= 16 || c.topk_groups >= c.n_groups;
-#define MOE_SEL(LPT_, VPL_)                                                                \
-  return launch_vpl<LPT_, VPL_>(c, logits, logit_bias, select_bias, k_per_token, ids, weights, \
-                                dev_err, stream)
+#define MOE_SEL(LPT_, VPL_)                                                                  \
+  return launch_splits<LPT_, VPL_>(c, logits, splits, split_stride, logits_out, logit_bias, \
+                                   select_bias, k_per_token, ids, weights, dev_err, stream)
   if (few_groups) {  // 16-lane segments rank at most 16 groups
     if (E <= 16) MOE_SEL(16, 1);
     if (E <= 32) MOE_SEL(16, 2);
