@@ -182,7 +182,7 @@ size_t moe_dispatch_workspace_size(int32_t T, int32_t k_stride, int32_t E);
  *                 (a stable counting sort)          [T*k_stride], first R set
  *   inv[r]        position of route r in perm, -1 for skipped slots
  *                 [T*k_stride], may be NULL
- *   workspace     device memory of at least
+ *   workspace     16-byte aligned device memory of at least
  *                 moe_dispatch_workspace_size(T, k_stride, E) bytes; its
  *                 contents need no initialisation and are clobbered
  * Limits: E <= MOE_MAX_EXPERTS, T*k_stride < 2^31.

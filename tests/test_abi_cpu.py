@@ -151,3 +151,25 @@ def test_binding_rejects_host_tensors():
     import torch
     with pytest.raises(ValueError):
         tda.route(torch.zeros(4, 8), torch.zeros(2, 8), 1)
+
+
+def test_dispatch_rejects_unaligned_workspace():
+    L = tda.lib()
+    ws = tda.dispatch_workspace_size(100, 8, 64)
+    assert L.moe_dispatch(FAKE, 100, 8, 64, FAKE, FAKE, FAKE, None, ctypes.c_void_p(0x1004), ws,
+                          None, None) == tda.MOE_EINVAL
+    assert "aligned" in L.moe_last_error().decode()
+
+
+@pytest.mark.parametrize("T,k,E", [(4096, 16, 128), (65536, 4, 128), (16384, 6, 384),
+                                   (8192, 8, 256), (256, 2, 8), (70000, 30, 1024), (5, 3, 7)])
+def test_dispatch_workspace_size_per_path(T, k, E):
+    # two-kernel path: one tile-major histogram of at most 20 Ki counts;
+    # otherwise tile histograms, tile bases and totals (tiles of 512 routes)
+    n = tda.dispatch_workspace_size(T, k, E)
+    R = T * k
+    if E % 4 == 0 and any(-(-R // t) * E <= 20480 for t in (512, 1024, 2048)):
+        assert n <= 20480 * 4 and n % (4 * E) == 0
+    else:
+        nt = -(-R // 512)
+        assert n == (2 * nt + 1) * E * 4

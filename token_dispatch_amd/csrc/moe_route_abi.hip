@@ -278,6 +278,8 @@ int32_t moe_dispatch(const int32_t* ids, int32_t T, int32_t k_stride, int32_t E,
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(MOE_EINVAL, "workspace of %zu bytes is below the %zu needed", workspace_bytes,
                 need);
+  if (need > 0 && reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+    return fail(MOE_EINVAL, "workspace must be 16-byte aligned");
   hipError_t e = moe::launch_dispatch(ids, R, E, counts, offsets, perm, inv, workspace, dev_err,
                                       static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_fail(e, "dispatch launch");
