@@ -34,12 +34,14 @@ struct RouteCfg {
   float route_scale;
 };
 
-// How the gate contraction is tiled: BM x BN tiles, an NS-stage LDS ring of
-// stages holding RB bytes of K per tile row, K split over `splits`
-// workgroups (partial sums added by the select kernel), pipelined (buffer ->
-// LDS copies) or the general register-staged kernel.
+// How the gate contraction is tiled: BM x BN tiles worked by wm x wn
+// wavefronts, an NS-stage LDS ring of stages holding RB bytes of K per tile
+// row, K split over `splits` workgroups (partial sums added by the select
+// kernel), pipelined (buffer -> LDS copies) or the general register-staged
+// kernel.
 struct GatePlan {
   int bm, bn, ns, rb, splits;
+  int wm = 2, wn = 2;
   bool pipe;
 };
 GatePlan plan_gate(int32_t T, int32_t d, int32_t E, int32_t dtype, bool aligned,
