@@ -1,9 +1,10 @@
 #!/usr/bin/env python3
 """Routed tokens/s of the MoE router + dispatch hot path on one MI355X.
 
-One step = moe_route (gate contraction, scoring, selection, weights) followed
-by moe_dispatch (histogram, offsets, permutation, inverse) over one batch of
-seeded synthetic tokens.  Inputs are resident in HBM before timing; each step
+One step = one moe_route_dispatch call -- the gate contraction, scoring,
+selection and weights of moe_route, then the histogram, offsets,
+permutation and inverse of moe_dispatch -- over one batch of seeded
+synthetic tokens.  Inputs are resident in HBM before timing; each step
 routes a different copy of x (rotating through copies totalling more than the
 256 MB last-level cache) so the gate reads x from HBM, not from cache.
 
@@ -36,17 +37,18 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def stage_bytes(w, T, R, R_valid, nt):
+def stage_bytes(w, T, R, R_valid, tile_bytes):
     """Algorithmic HBM bytes per launch of each kernel (inputs read once,
-    outputs written once)."""
+    outputs written once); tile_bytes: the dispatch's per-tile histogram
+    data (written once, read once by the placement)."""
     xb = 2 if w.dtype == "bf16" else 4
     E, d, k = w.E, w.d, w.k
     return {
         "gate": T * d * xb + E * d * xb + T * E * 4,
         "select": T * E * 4 + T * k * 8 + (T * 4 if w.dynamic_k else 0),
-        "disp_hist": R * 4 + nt * E * 4,
-        "disp_scan": 2 * nt * E * 4 + E * 4,
-        "disp_scatter": nt * E * 4 + E * 4 + R * 4 + R * 4 + R_valid * 4 + E * 8,
+        "disp_hist": R * 4 + tile_bytes,
+        "disp_scan": 2 * tile_bytes + E * 4,
+        "disp_scatter": tile_bytes + E * 4 + R * 4 + R * 4 + R_valid * 4 + E * 8,
     }
 
 
@@ -162,19 +164,21 @@ def main():
     offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
     perm = torch.empty(T * k, dtype=torch.int32, device=dev)
     inv = torch.empty(T * k, dtype=torch.int32, device=dev)
-    ws = torch.empty(max(1, tda.dispatch_workspace_size(T, k, E)), dtype=torch.uint8, device=dev)
-    route_ws = torch.empty(max(1, tda.route_workspace_size(
-        T, w.d, E, k, 1 if w.dtype == "bf16" else 0, score=w.score, n_groups=w.n_groups,
-        topk_groups=w.topk_groups, group_score=w.group_score if w.n_groups > 1 else "max",
-        renormalize=w.renormalize, route_scale=w.route_scale)), dtype=torch.uint8, device=dev)
+    pkw = dict(score=w.score, n_groups=w.n_groups, topk_groups=w.topk_groups,
+               group_score=w.group_score if w.n_groups > 1 else "max",
+               renormalize=w.renormalize, route_scale=w.route_scale)
+    dt = 1 if w.dtype == "bf16" else 0
+    ws_bytes = tda.route_dispatch_workspace_size(T, w.d, E, k, dt, **pkw)
+    ws = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device=dev)
+    route_bytes = (tda.route_workspace_size(T, w.d, E, k, dt, **pkw) + 255) // 256 * 256
     rkw = dict(score=w.score, logit_bias=lb, select_bias=sb, k_per_token=kpt,
                n_groups=w.n_groups, topk_groups=w.topk_groups,
                group_score=w.group_score if w.n_groups > 1 else None,
                renormalize=w.renormalize, route_scale=w.route_scale)
 
-    def step(i):
-        tda.route(xs[i % n_copies], W, k, ids=ids, weights=weights, workspace=route_ws, **rkw)
-        tda.dispatch(ids, E, counts=counts, offsets=offsets, perm=perm, inv=inv, workspace=ws)
+    def step(i):  # one moe_route_dispatch call: gate, selection, dispatch
+        tda.route_dispatch(xs[i % n_copies], W, k, ids=ids, weights=weights, counts=counts,
+                           offsets=offsets, perm=perm, inv=inv, workspace=ws, **rkw)
 
     log(f"[bench] {n_copies} rotating copies of x ({xbytes / 1e6:.1f} MB each); "
         f"warmup {args.warmup}, steps {args.steps}")
@@ -235,8 +239,9 @@ def main():
 
     R = T * k
     R_valid = int(counts.sum().item())
-    nt = (tda.dispatch_workspace_size(T, k, E) // (4 * E) - 1) // 2  # dispatch tiles
-    sbytes = stage_bytes(w, T, R, R_valid, nt)
+    disp_ws = ws_bytes - route_bytes  # the dispatch's tile data
+    tile_bytes = disp_ws if "disp_scan" not in prof or not prof["disp_scan"][1] else (disp_ws - 4 * E) // 2
+    sbytes = stage_bytes(w, T, R, R_valid, tile_bytes)
     stages = {}
     for name, (ms, n) in prof.items():
         if n:

@@ -193,6 +193,33 @@ int32_t moe_dispatch(const int32_t* ids, int32_t T, int32_t k_stride, int32_t E,
                      int32_t* dev_err, void* stream);
 
 /*
+ * moe_route_dispatch -- moe_route followed by moe_dispatch of its ids
+ * (k_stride = p->k): one pass of the router and the grouping of its routes,
+ * with the results of the two calls (same arguments, same values, bit for
+ * bit).  When the tokens routed by one workgroup of the selection kernel
+ * form exactly one dispatch tile and the tile histograms are small, the
+ * selection kernel also writes those histograms, saving the dispatch's
+ * counting kernel.
+ *   workspace    256-byte aligned device memory of at least
+ *                moe_route_dispatch_workspace_size(p) bytes (the gate
+ *                hand-off, then the dispatch's tile data); contents need no
+ *                initialisation and are clobbered
+ *   counts, offsets, perm, inv, dev_err: as for moe_dispatch (dev_err also
+ *                as for moe_route)
+ * Limits: those of moe_route and moe_dispatch.
+ */
+int32_t moe_route_dispatch(const moe_route_params* p, const void* x, const void* W,
+                           const float* logit_bias, const float* select_bias,
+                           const int32_t* k_per_token, float* logits, int32_t* ids,
+                           float* weights, int32_t* counts, int32_t* offsets, int32_t* perm,
+                           int32_t* inv, void* workspace, size_t workspace_bytes,
+                           int32_t* dev_err, void* stream);
+
+/* Bytes of device workspace moe_route_dispatch needs for these parameters
+ * (16-byte aligned x and W assumed). */
+size_t moe_route_dispatch_workspace_size(const moe_route_params* p);
+
+/*
  * Per-kernel timing, for benchmarks and profiling only.
  * moe_profile_enable(1) clears earlier records and, from then on, brackets
  * every kernel the library launches with a pair of HIP events recorded on

@@ -164,12 +164,44 @@ def test_dispatch_rejects_unaligned_workspace():
 @pytest.mark.parametrize("T,k,E", [(4096, 16, 128), (65536, 4, 128), (16384, 6, 384),
                                    (8192, 8, 256), (256, 2, 8), (70000, 30, 1024), (5, 3, 7)])
 def test_dispatch_workspace_size_per_path(T, k, E):
-    # two-kernel path: one tile-major histogram of at most 20 Ki counts;
+    # two-kernel path: one tile-major histogram of at most 32 Ki counts;
     # otherwise tile histograms, tile bases and totals (tiles of 512 routes)
     n = tda.dispatch_workspace_size(T, k, E)
     R = T * k
-    if E % 4 == 0 and any(-(-R // t) * E <= 20480 for t in (512, 1024, 2048)):
-        assert n <= 20480 * 4 and n % (4 * E) == 0
+    if E % 4 == 0 and any(-(-R // t) * E <= 32768 for t in (512, 1024, 2048)):
+        assert n <= 32768 * 4 and n % (4 * E) == 0
     else:
         nt = -(-R // 512)
         assert n == (2 * nt + 1) * E * 4
+
+
+def test_route_dispatch_workspace_size():
+    # the gate hand-off (256-byte aligned), then either the selection-written
+    # tile histograms (whole-tile shapes) or the dispatch's own workspace
+    for T, d, E, k in [(4096, 2048, 128, 16), (65536, 2880, 128, 4), (256, 1024, 8, 2),
+                       (16384, 7168, 384, 6), (5, 7, 4, 1)]:
+        route = tda.route_workspace_size(T, d, E, k)
+        route = (route + 255) // 256 * 256
+        n = tda.route_dispatch_workspace_size(T, d, E, k)
+        disp = tda.dispatch_workspace_size(T, k, E)
+        assert n >= route and (n == route + disp or (n - route) % (4 * E) == 0), (T, n)
+    # Qwen3-like shape: 16-token tiles of 256 routes -> 256 histogram rows
+    assert tda.route_dispatch_workspace_size(4096, 2048, 128, 16) == \
+        (4096 * 128 * 4 + 255) // 256 * 256 + 256 * 128 * 4
+
+
+def test_route_dispatch_validation():
+    L = tda.lib()
+    p = tda.make_params(64, 128, 16, 2)
+    n = tda.route_dispatch_workspace_size(64, 128, 16, 2)
+    args = lambda counts, ws, nbytes: (ctypes.byref(p), FAKE, FAKE, None, None, None, None, FAKE,
+                                       FAKE, counts, FAKE, FAKE, None, ws, nbytes, None, None)
+    assert L.moe_route_dispatch(*args(None, ctypes.c_void_p(0x1000), n)) == tda.MOE_EINVAL
+    assert "counts" in L.moe_last_error().decode()
+    assert L.moe_route_dispatch(*args(FAKE, ctypes.c_void_p(0x1000), n - 1)) == tda.MOE_EINVAL
+    assert "workspace" in L.moe_last_error().decode()
+    assert L.moe_route_dispatch(*args(FAKE, ctypes.c_void_p(0x1010), n)) == tda.MOE_EINVAL
+    assert "aligned" in L.moe_last_error().decode()
+    bad = tda.make_params(64, 128, 16, 0)
+    assert L.moe_route_dispatch(ctypes.byref(bad), FAKE, FAKE, None, None, None, None, FAKE, FAKE,
+                                FAKE, FAKE, FAKE, None, FAKE, n, None, None) == tda.MOE_EINVAL

@@ -1,0 +1,96 @@
+"""moe_route_dispatch equals moe_route followed by moe_dispatch, bit for bit,
+on the shapes where the selection kernel writes the dispatch histograms
+(Qwen3-like: 16-token tiles of 256 routes) and on those where it does not;
+the fused results also match the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import token_dispatch_amd as tda
+import workloads as wl
+from tests.gpu_util import down, route_kwargs, say, up
+from tests.parity import check_dispatch, check_route, oracle_route
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    tda.lib()
+
+
+def both(x, W, k, E, **kw):
+    """(fused outputs, separate-call outputs, fused dev_err, separate dev_err)."""
+    err1 = torch.zeros(1, dtype=torch.int32, device=DEV)
+    err2 = torch.zeros(1, dtype=torch.int32, device=DEV)
+    fused = tda.route_dispatch(x, W, k, dev_err=err1, **kw)
+    ids, w = tda.route(x, W, k, dev_err=err2, **kw)
+    sep = (ids, w) + tuple(tda.dispatch(ids, E))
+    torch.cuda.synchronize()
+    return fused, sep, int(err1.item()), int(err2.item())
+
+
+def assert_same(fused, sep):
+    """Bit-equal outputs; perm only over its defined prefix (offsets[E])."""
+    n = int(fused[3][-1].item())
+    assert int(sep[3][-1].item()) == n
+    for name, a, b in zip(("ids", "weights", "counts", "offsets", "perm", "inv"), fused, sep):
+        if name == "perm":
+            a, b = a[:n], b[:n]
+        assert torch.equal(a, b), name
+
+
+@pytest.mark.parametrize("name,T", [("qwen3_dynk", None), ("qwen3_dynk", 4091),
+                                    ("qwen3_dynk", 33), ("mixtral", None),
+                                    ("gptoss_skew", 3000), ("dsv3_grouped", 700)])
+def test_route_dispatch_matches_separate_calls_and_oracle(name, T):
+    w = wl.WORKLOADS[name]
+    inp = wl.make_inputs(w, T=T)
+    say("route_dispatch", name, inp["x"].shape[0])
+    kw = route_kwargs(w)
+    if kw["group_score"] is None:
+        kw.pop("group_score")
+    kw.update(logit_bias=up(inp["logit_bias"]), select_bias=up(inp["select_bias"]),
+              k_per_token=up(inp["k_per_token"]))
+    fused, sep, e1, e2 = both(up(inp["x"]), up(inp["W"]), w.k, w.E, **kw)
+    assert_same(fused, sep)
+    assert e1 == e2 == 0
+    l64 = oracle.gate(inp["x"], inp["W"], inp["logit_bias"])
+    ref = oracle_route(oracle, l64, w.k, score=w.score, select_bias=inp["select_bias"],
+                       k_per_token=inp["k_per_token"], n_groups=w.n_groups,
+                       topk_groups=w.topk_groups,
+                       group_score=w.group_score if w.n_groups > 1 else None,
+                       renormalize=w.renormalize, route_scale=w.route_scale)
+    check_route(down(fused[0]), down(fused[1]), ref, oracle, score=w.score,
+                renormalize=w.renormalize, route_scale=w.route_scale,
+                k_per_token=inp["k_per_token"], n_groups=w.n_groups, topk_groups=w.topk_groups,
+                where=name)
+    check_dispatch(tuple(fused[2:]), oracle.dispatch(down(fused[0]), w.E))
+
+
+def test_route_dispatch_select_only_and_bad_k():
+    rng = np.random.default_rng(5)
+    T, E, K = 4096, 128, 16
+    lg = up(rng.standard_normal((T, E)).astype(np.float32))
+    kpt = rng.choice([4, 8, 16], size=T).astype(np.int32)
+    kpt[[3, 100, 4095]] = [0, 17, -2]
+    say("route_dispatch select-only")
+    fused, sep, e1, e2 = both(None, None, K, E, logits=lg, k_per_token=up(kpt))
+    assert_same(fused, sep)
+    assert e1 == e2 == 3
+    assert np.all(down(fused[0])[[3, 100, 4095]] == -1)
+    check_dispatch(tuple(fused[2:]), oracle.dispatch(down(fused[0]), E))
+
+
+def test_route_dispatch_empty():
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
+    W = up(wl.f32_to_bf16_bits(np.ones((8, 64), np.float32)))
+    say("route_dispatch empty")
+    ids, wts, counts, offsets, perm, inv = tda.route_dispatch(x, W, 2)
+    torch.cuda.synchronize()
+    assert ids.shape == (0, 2)
+    assert np.all(down(counts) == 0) and np.all(down(offsets) == 0)

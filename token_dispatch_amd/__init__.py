@@ -28,6 +28,7 @@ SCORES = {"softmax": 0, "sigmoid": 1, "sqrt_softplus": 2, "softmax_topk": 3}
 GROUP_SCORES = {"max": 0, "top2_sum": 1}
 EXPORTS = ("moe_route", "moe_route_workspace_size", "moe_route_hash",
            "moe_dispatch_workspace_size", "moe_dispatch",
+           "moe_route_dispatch", "moe_route_dispatch_workspace_size",
            "moe_profile_enable", "moe_profile_read", "moe_last_error", "moe_abi_version")
 STAGES = ("gate", "select", "hash", "disp_hist", "disp_scan", "disp_scatter")
 
@@ -69,6 +70,10 @@ def lib() -> ctypes.CDLL:
         L.moe_dispatch_workspace_size.restype = ctypes.c_size_t
         L.moe_dispatch.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, ctypes.c_size_t, vp, vp]
         L.moe_dispatch.restype = i32
+        L.moe_route_dispatch.argtypes = [P] + [vp] * 13 + [ctypes.c_size_t, vp, vp]
+        L.moe_route_dispatch.restype = i32
+        L.moe_route_dispatch_workspace_size.argtypes = [P]
+        L.moe_route_dispatch_workspace_size.restype = ctypes.c_size_t
         L.moe_last_error.argtypes = []
         L.moe_last_error.restype = ctypes.c_char_p
         L.moe_profile_enable.argtypes = [i32]
@@ -131,22 +136,10 @@ def route_workspace_size(T, d, E, k, dtype=1, **kw) -> int:
     return int(lib().moe_route_workspace_size(ctypes.byref(p)))
 
 
-def route(x: Optional[torch.Tensor], W: Optional[torch.Tensor], k: int, *,
-          score: str = "softmax", logit_bias=None, select_bias=None, k_per_token=None,
-          n_groups: int = 1, topk_groups: Optional[int] = None,
-          group_score: Optional[str] = None, renormalize: bool = True,
-          route_scale: float = 1.0, logits: Optional[torch.Tensor] = None,
-          E: Optional[int] = None, ids=None, weights=None, workspace=None, dev_err=None,
-          return_logits: bool = False):
-    """Gate + score + (grouped) top-k + weights.  Returns (ids, weights[, logits]).
-
-    x [T][d] and W [E][d] (float32 or bfloat16); or x = W = None with
-    ``logits`` [T][E] float32 as the input (select-only mode).  The gate
-    logits are written to ``logits`` when one is passed (or return_logits).
-    ``workspace`` (uint8 device tensor) carries the gate's hand-off; it is
-    allocated when not given.  group_score defaults to "top2_sum" when
-    select_bias is given, else "max".
-    """
+def _route_args(x, W, k, score, logit_bias, select_bias, k_per_token, n_groups, topk_groups,
+                group_score, renormalize, route_scale, logits, E, ids, weights, dev_err,
+                return_logits):
+    """Checks and output allocation shared by route() and route_dispatch()."""
     if group_score is None:
         group_score = "top2_sum" if select_bias is not None else "max"
     if x is None:
@@ -184,6 +177,28 @@ def route(x: Optional[torch.Tensor], W: Optional[torch.Tensor], k: int, *,
         _dev(dev_err, "dev_err", torch.int32, (1,))
     p = make_params(T, d, E_, k, dt, score, n_groups, topk_groups, group_score, renormalize,
                     route_scale)
+    return p, device, logits, ids, weights
+
+
+def route(x: Optional[torch.Tensor], W: Optional[torch.Tensor], k: int, *,
+          score: str = "softmax", logit_bias=None, select_bias=None, k_per_token=None,
+          n_groups: int = 1, topk_groups: Optional[int] = None,
+          group_score: Optional[str] = None, renormalize: bool = True,
+          route_scale: float = 1.0, logits: Optional[torch.Tensor] = None,
+          E: Optional[int] = None, ids=None, weights=None, workspace=None, dev_err=None,
+          return_logits: bool = False):
+    """Gate + score + (grouped) top-k + weights.  Returns (ids, weights[, logits]).
+
+    x [T][d] and W [E][d] (float32 or bfloat16); or x = W = None with
+    ``logits`` [T][E] float32 as the input (select-only mode).  The gate
+    logits are written to ``logits`` when one is passed (or return_logits).
+    ``workspace`` (uint8 device tensor) carries the gate's hand-off; it is
+    allocated when not given.  group_score defaults to "top2_sum" when
+    select_bias is given, else "max".
+    """
+    p, device, logits, ids, weights = _route_args(
+        x, W, k, score, logit_bias, select_bias, k_per_token, n_groups, topk_groups,
+        group_score, renormalize, route_scale, logits, E, ids, weights, dev_err, return_logits)
     if workspace is None and x is not None:
         nbytes = int(lib().moe_route_workspace_size(ctypes.byref(p)))
         if nbytes:
@@ -193,6 +208,45 @@ def route(x: Optional[torch.Tensor], W: Optional[torch.Tensor], k: int, *,
                            _p(k_per_token), _p(logits), _p(ids), _p(weights), _p(workspace),
                            ws_bytes, _p(dev_err), _stream(device)))
     return (ids, weights, logits) if return_logits else (ids, weights)
+
+
+def route_dispatch_workspace_size(T, d, E, k, dtype=1, **kw) -> int:
+    """Device bytes moe_route_dispatch needs for these shapes."""
+    p = make_params(T, d, E, k, dtype, **kw)
+    return int(lib().moe_route_dispatch_workspace_size(ctypes.byref(p)))
+
+
+def route_dispatch(x: Optional[torch.Tensor], W: Optional[torch.Tensor], k: int, *,
+                   score: str = "softmax", logit_bias=None, select_bias=None,
+                   k_per_token=None, n_groups: int = 1, topk_groups: Optional[int] = None,
+                   group_score: Optional[str] = None, renormalize: bool = True,
+                   route_scale: float = 1.0, logits: Optional[torch.Tensor] = None,
+                   E: Optional[int] = None, ids=None, weights=None, counts=None, offsets=None,
+                   perm=None, inv=None, with_inv: bool = True, workspace=None, dev_err=None):
+    """route() then dispatch() of its ids in one library call.  Returns
+    (ids, weights, counts, offsets, perm, inv); ``workspace`` (256-byte
+    aligned uint8 device tensor) is allocated when not given."""
+    p, device, logits, ids, weights = _route_args(
+        x, W, k, score, logit_bias, select_bias, k_per_token, n_groups, topk_groups,
+        group_score, renormalize, route_scale, logits, E, ids, weights, dev_err, False)
+    E_, R = p.E, p.T * p.k
+    if counts is None:
+        counts = torch.empty(E_, dtype=torch.int32, device=device)
+    if offsets is None:
+        offsets = torch.empty(E_ + 1, dtype=torch.int32, device=device)
+    if perm is None:
+        perm = torch.empty(R, dtype=torch.int32, device=device)
+    if inv is None and with_inv:
+        inv = torch.empty(R, dtype=torch.int32, device=device)
+    if workspace is None:
+        nbytes = int(lib().moe_route_dispatch_workspace_size(ctypes.byref(p)))
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().moe_route_dispatch(ctypes.byref(p), _p(x), _p(W), _p(logit_bias),
+                                    _p(select_bias), _p(k_per_token), _p(logits), _p(ids),
+                                    _p(weights), _p(counts), _p(offsets), _p(perm), _p(inv),
+                                    _p(workspace), ws_bytes, _p(dev_err), _stream(device)))
+    return ids, weights, counts, offsets, perm, inv
 
 
 def route_hash(token_ids: torch.Tensor, tid2eid: torch.Tensor, E: int, *, x=None, W=None,

@@ -74,6 +74,18 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
+// Mask of the lanes whose id (>= 0) equals this lane's id, without atomics:
+// one ballot per bit of the id narrows the set (lanes with id < 0 get 0s).
+__device__ __forceinline__ uint64_t peer_mask(int e, int nbits) {
+  uint64_t p = __ballot(e >= 0);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t m = __ballot(bit);
+    p &= bit ? m : ~m;
+  }
+  return p;
+}
+
 __device__ __forceinline__ float sigmoid_f32(float l) { return 1.0f / (1.0f + expf(-l)); }
 
 __device__ __forceinline__ float softplus_f32(float l) {

@@ -8,7 +8,7 @@
 // among its peers is the popcount of the peers below it, and the lowest peer
 // (the leader) alone updates the wave's own LDS row for that expert.
 //
-// Two kernels when the tile histograms are small (tiles x E <= 20 Ki
+// Two kernels when the tile histograms are small (tiles x E <= 32 Ki
 // counts, the tile size grown to get there):
 //  1. histogram: per-tile, per-expert counts -> tile_hist[tile][e].
 //  2. scatter: every workgroup reads the whole (L2-resident) histogram once,
@@ -33,7 +33,7 @@ constexpr int kThreads = kWaves * kWave;
 constexpr int kChunksPerWave = 2;                       // three-kernel path
 constexpr int kTile = kWaves * kChunksPerWave * kWave;  // 512 routes per tile
 constexpr int kMaxE = 1024;
-constexpr int kFusedMaxCounts = 20 * 1024;              // tiles x E, two-kernel path
+constexpr int kFusedMaxCounts = 32 * 1024;              // tiles x E, two-kernel path
 constexpr int kFusedBatch = 16;                         // 16-byte loads in flight per thread
 constexpr int kScanWaves = 16;                          // experts per scan workgroup
 constexpr int kScanPrefetch = 8;                        // chunks of 64 tiles in registers
@@ -59,17 +59,6 @@ __device__ __forceinline__ void load_chunks(const int32_t* __restrict__ ids, int
       e[ch] = -1;
     }
   }
-}
-
-// Mask of the lanes whose (valid) id equals this lane's id.
-__device__ __forceinline__ uint64_t peer_mask(int e, int nbits) {
-  uint64_t p = __ballot(e >= 0);
-  for (int b = 0; b < nbits; ++b) {
-    const bool bit = (e >> b) & 1;
-    const uint64_t m = __ballot(bit);
-    p &= bit ? m : ~m;
-  }
-  return p;
 }
 
 // Count this wave's chunks into its LDS row.
@@ -302,7 +291,40 @@ hipError_t launch_fused(const int32_t* ids, int64_t R, int32_t E, int nbits, int
   return hipGetLastError();
 }
 
+template <int CPW>
+hipError_t launch_placement(const int32_t* ids, int64_t R, int32_t E, int nbits, int nt,
+                            const int32_t* tile_hist, int32_t* counts, int32_t* offsets,
+                            int32_t* perm, int32_t* inv, hipStream_t stream) {
+  prof_begin(kStageDispScatter, stream);
+  hipLaunchKernelGGL((disp_scatter_kernel<CPW, true>), dim3(nt), dim3(kThreads), 0, stream, ids,
+                     R, E, nbits, nt, tile_hist, nullptr, nullptr, counts, offsets, perm, inv);
+  prof_end(kStageDispScatter, stream);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+bool dispatch_hist_ok(int64_t R, int32_t E, int32_t tile_routes) {
+  if (R <= 0 || E % 4 != 0 || E > kMaxE) return false;
+  if (tile_routes != 256 && tile_routes != 512 && tile_routes != 1024 && tile_routes != 2048)
+    return false;
+  return (R + tile_routes - 1) / tile_routes * E <= kFusedMaxCounts;
+}
+
+hipError_t launch_dispatch_from_hist(const int32_t* ids, int64_t R, int32_t E,
+                                     int32_t* counts, int32_t* offsets, int32_t* perm,
+                                     int32_t* inv, const int32_t* tile_hist,
+                                     int32_t tile_routes, hipStream_t stream) {
+  if (!dispatch_hist_ok(R, E, tile_routes)) return hipErrorInvalidValue;
+  const int nt = (int)((R + tile_routes - 1) / tile_routes);
+  const int nbits = bits_for(E);
+  switch (tile_routes) {
+    case 256: return launch_placement<1>(ids, R, E, nbits, nt, tile_hist, counts, offsets, perm, inv, stream);
+    case 512: return launch_placement<2>(ids, R, E, nbits, nt, tile_hist, counts, offsets, perm, inv, stream);
+    case 1024: return launch_placement<4>(ids, R, E, nbits, nt, tile_hist, counts, offsets, perm, inv, stream);
+    default: return launch_placement<8>(ids, R, E, nbits, nt, tile_hist, counts, offsets, perm, inv, stream);
+  }
+}
 
 size_t dispatch_workspace_bytes(int64_t R, int32_t E) {
   if (R <= 0) return 0;  // no routes: only counts and offsets are written

@@ -55,11 +55,16 @@ hipError_t launch_gate_gemm(const GatePlan& g, int32_t dtype, const void* x, con
 
 // Score + (grouped) top-k + weights.  The logits are the sum of `splits`
 // fp32 partial arrays `split_stride` floats apart (summed in order); when
-// logits_out is not NULL the summed logits are written there.
+// logits_out is not NULL the summed logits are written there.  With `hist`
+// (only when select_hist_tokens(c) > 0) the kernel also writes
+// hist[b][e] = picks of expert e among tokens [b*n, (b+1)*n), n =
+// select_hist_tokens(c): the per-tile histograms of a dispatch whose tiles
+// hold n*k routes.
 hipError_t launch_select(const RouteCfg& c, const float* logits, int32_t splits,
                          int64_t split_stride, float* logits_out, const float* logit_bias,
                          const float* select_bias, const int32_t* k_per_token, int32_t* ids,
-                         float* weights, int32_t* dev_err, hipStream_t stream);
+                         float* weights, int32_t* dev_err, int32_t* hist, hipStream_t stream);
+int select_hist_tokens(const RouteCfg& c);  // 0: no histogram option
 
 // Hash routing: table gather (+ k gathered gate dot products and weights).
 hipError_t launch_hash_route(const RouteCfg& c, int32_t dtype,
@@ -68,6 +73,14 @@ hipError_t launch_hash_route(const RouteCfg& c, int32_t dtype,
                              const float* logit_bias, int32_t* ids,
                              float* weights, int32_t* dev_err,
                              hipStream_t stream);
+
+// Dispatch placement from per-tile histograms already in tile_hist
+// ([ceil(R / tile_routes)][E], tile-major), when dispatch_hist_ok.
+bool dispatch_hist_ok(int64_t R, int32_t E, int32_t tile_routes);
+hipError_t launch_dispatch_from_hist(const int32_t* ids, int64_t R, int32_t E,
+                                     int32_t* counts, int32_t* offsets, int32_t* perm,
+                                     int32_t* inv, const int32_t* tile_hist,
+                                     int32_t tile_routes, hipStream_t stream);
 
 // Dispatch: tile histograms -> scan -> stable scatter.
 size_t dispatch_workspace_bytes(int64_t R, int32_t E);

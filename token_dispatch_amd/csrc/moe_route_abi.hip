@@ -175,27 +175,23 @@ int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
 
 const char* moe_last_error(void) { return g_last_error.c_str(); }
 
-int32_t moe_route(const moe_route_params* p, const void* x, const void* W,
-                  const float* logit_bias, const float* select_bias,
-                  const int32_t* k_per_token, float* logits, int32_t* ids,
-                  float* weights, void* workspace, size_t workspace_bytes,
-                  int32_t* dev_err, void* stream) {
-  const bool select_only = (x == nullptr && W == nullptr);
-  int32_t rc = check_route_params(p, !select_only);
-  if (rc != MOE_OK) return rc;
-  if (p->T > 0 && (x == nullptr) != (W == nullptr))
-    return fail(MOE_EINVAL, "x and W must both be set or both be NULL");
-  if (p->T == 0) return MOE_OK;
-  if (!ids || !weights) return fail(MOE_EINVAL, "ids and weights are required");
-  if (select_only && !logits)
-    return fail(MOE_EINVAL, "select-only mode (x = W = NULL) needs logits");
+}  // extern "C"
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
+namespace {
+
+// Gate + select of moe_route on validated arguments (T > 0, ids and weights
+// set, logits set in select-only mode).  `hist`: optional per-tile expert
+// histograms for a fused dispatch (launch_select).
+int32_t route_core(const moe_route_params* p, const void* x, const void* W,
+                   const float* logit_bias, const float* select_bias,
+                   const int32_t* k_per_token, float* logits, int32_t* ids, float* weights,
+                   void* workspace, size_t workspace_bytes, int32_t* dev_err, int32_t* hist,
+                   hipStream_t s) {
   const moe::RouteCfg c = to_cfg(p);
   hipError_t e;
-  if (select_only) {
+  if (x == nullptr) {  // select-only
     e = moe::launch_select(c, logits, 1, 0, nullptr, logit_bias, select_bias, k_per_token, ids,
-                           weights, dev_err, s);
+                           weights, dev_err, hist, s);
     if (e != hipSuccess) return device_fail(e, "select launch");
     return MOE_OK;
   }
@@ -218,15 +214,111 @@ int32_t moe_route(const moe_route_params* p, const void* x, const void* W,
   if (e != hipSuccess) return device_fail(e, "gate GEMM launch");
   e = moe::launch_select(c, hand_off, g.splits, (int64_t)p->T * p->E,
                          g.splits > 1 ? logits : nullptr, nullptr, select_bias, k_per_token, ids,
-                         weights, dev_err, s);
+                         weights, dev_err, hist, s);
   if (e != hipSuccess) return device_fail(e, "select launch");
+  return MOE_OK;
+}
+
+// Argument checks shared by moe_route and moe_route_dispatch.
+int32_t check_route_call(const moe_route_params* p, const void* x, const void* W,
+                         const float* logits, const int32_t* ids, const float* weights) {
+  const bool select_only = (x == nullptr && W == nullptr);
+  int32_t rc = check_route_params(p, !select_only);
+  if (rc != MOE_OK) return rc;
+  if (p->T > 0 && (x == nullptr) != (W == nullptr))
+    return fail(MOE_EINVAL, "x and W must both be set or both be NULL");
+  if (p->T == 0) return MOE_OK;
+  if (!ids || !weights) return fail(MOE_EINVAL, "ids and weights are required");
+  if (select_only && !logits)
+    return fail(MOE_EINVAL, "select-only mode (x = W = NULL) needs logits");
+  return MOE_OK;
+}
+
+size_t route_ws_bytes(const moe_route_params* p) {
+  const moe::GatePlan g = moe::plan_gate(p->T, p->d, p->E, p->dtype, true, true);
+  return (size_t)p->T * p->E * sizeof(float) * g.splits;
+}
+
+// Tokens per dispatch tile when the select kernel can write the dispatch's
+// tile histograms itself, else 0.
+int fused_hist_tokens(const moe_route_params* p) {
+  const int n = moe::select_hist_tokens(to_cfg(p));
+  if (n == 0) return 0;
+  return moe::dispatch_hist_ok((int64_t)p->T * p->k, p->E, n * p->k) ? n : 0;
+}
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_route(const moe_route_params* p, const void* x, const void* W,
+                  const float* logit_bias, const float* select_bias,
+                  const int32_t* k_per_token, float* logits, int32_t* ids,
+                  float* weights, void* workspace, size_t workspace_bytes,
+                  int32_t* dev_err, void* stream) {
+  int32_t rc = check_route_call(p, x, W, logits, ids, weights);
+  if (rc != MOE_OK || p->T == 0) return rc;
+  return route_core(p, x, W, logit_bias, select_bias, k_per_token, logits, ids, weights,
+                    workspace, workspace_bytes, dev_err, nullptr,
+                    static_cast<hipStream_t>(stream));
+}
+
+size_t moe_route_dispatch_workspace_size(const moe_route_params* p) {
+  if (check_route_params(p, true) != MOE_OK) return 0;
+  const int64_t R = (int64_t)p->T * p->k;
+  if (R > kI32Max) return 0;
+  const size_t route = p->T > 0 ? align256(route_ws_bytes(p)) : 0;
+  const int n = p->T > 0 ? fused_hist_tokens(p) : 0;
+  const size_t disp = n > 0 ? (size_t)((p->T + n - 1) / n) * p->E * sizeof(int32_t)
+                            : moe::dispatch_workspace_bytes(R, p->E);
+  return route + disp;
+}
+
+int32_t moe_route_dispatch(const moe_route_params* p, const void* x, const void* W,
+                           const float* logit_bias, const float* select_bias,
+                           const int32_t* k_per_token, float* logits, int32_t* ids,
+                           float* weights, int32_t* counts, int32_t* offsets, int32_t* perm,
+                           int32_t* inv, void* workspace, size_t workspace_bytes,
+                           int32_t* dev_err, void* stream) {
+  int32_t rc = check_route_call(p, x, W, logits, ids, weights);
+  if (rc != MOE_OK) return rc;
+  const int64_t R = (int64_t)p->T * p->k;
+  if (R > kI32Max) return fail(MOE_EUNSUPPORTED, "T*k must be below 2^31");
+  if (!counts || !offsets) return fail(MOE_EINVAL, "counts and offsets are required");
+  if (R > 0 && !perm) return fail(MOE_EINVAL, "perm is required");
+  const size_t need = moe_route_dispatch_workspace_size(p);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(MOE_EINVAL, "workspace of %zu bytes is below the %zu needed", workspace_bytes,
+                need);
+  if (need > 0 && reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(MOE_EINVAL, "workspace must be 256-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (p->T == 0) {  // zero counts and offsets only
+    e = moe::launch_dispatch(ids, 0, p->E, counts, offsets, perm, inv, nullptr, dev_err, s);
+    if (e != hipSuccess) return device_fail(e, "dispatch launch");
+    return MOE_OK;
+  }
+  const size_t route = align256(route_ws_bytes(p));
+  int32_t* disp_ws = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + route);
+  const int n = fused_hist_tokens(p);
+  rc = route_core(p, x, W, logit_bias, select_bias, k_per_token, logits, ids, weights,
+                  workspace, route, dev_err, n > 0 ? disp_ws : nullptr, s);
+  if (rc != MOE_OK) return rc;
+  if (n > 0)
+    e = moe::launch_dispatch_from_hist(ids, R, p->E, counts, offsets, perm, inv, disp_ws,
+                                       n * p->k, s);
+  else
+    e = moe::launch_dispatch(ids, R, p->E, counts, offsets, perm, inv, disp_ws, dev_err, s);
+  if (e != hipSuccess) return device_fail(e, "dispatch launch");
   return MOE_OK;
 }
 
 size_t moe_route_workspace_size(const moe_route_params* p) {
   if (check_route_params(p, true) != MOE_OK || p->T == 0) return 0;
-  const moe::GatePlan g = moe::plan_gate(p->T, p->d, p->E, p->dtype, true, true);
-  return (size_t)p->T * p->E * sizeof(float) * g.splits;
+  return route_ws_bytes(p);
 }
 
 int32_t moe_route_hash(const moe_route_params* p, const int32_t* token_ids,

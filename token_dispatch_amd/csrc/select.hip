@@ -32,8 +32,8 @@
 namespace moe {
 namespace {
 
-constexpr int kWavesPerBlock = 4;
 constexpr int kMaxK = 32;  // MOE_MAX_K
+constexpr int kHistMaxE = 256;  // experts of the per-block histogram option
 
 // ---- DPP helpers ------------------------------------------------------------
 template <int CTRL>
@@ -188,28 +188,33 @@ __device__ __forceinline__ void load_vals(const float* __restrict__ row, int e0,
 // logits are the sum of NSPLIT partial arrays `split_stride` floats apart (a
 // K split of the gate), added in a fixed order.  `vec`: the logits, their
 // split stride and the bias arrays allow 16-byte loads (E % 4 == 0).
-template <int LPT, int VPL, int NSPLIT, bool MONO>
-__global__ __launch_bounds__(kWavesPerBlock * kWave) void select_kernel(
+// HIST (E <= kHistMaxE): also hist[block][e] = number of picks of expert e
+// among the workgroup's TPB tokens -- the routes t*k + j of those tokens are
+// one tile of the dispatch (counted with ballot peer masks, no atomics).
+template <int LPT, int VPL, int NSPLIT, bool MONO, int WPB, bool HIST>
+__global__ __launch_bounds__(WPB * kWave) void select_kernel(
     RouteCfg c, const float* __restrict__ logits, int64_t split_stride,
     float* __restrict__ logits_out, const float* __restrict__ logit_bias,
     const float* __restrict__ select_bias, const int32_t* __restrict__ k_per_token,
     int32_t* __restrict__ ids, float* __restrict__ weights, int32_t* __restrict__ dev_err,
-    int vec) {
+    int vec, int32_t* __restrict__ hist) {
   using S = Seg<LPT>;
   constexpr int TPW = kWave / LPT;               // tokens per wavefront
-  constexpr int TPB = kWavesPerBlock * TPW;      // tokens per workgroup
+  constexpr int TPB = WPB * TPW;                 // tokens per workgroup
   constexpr int ROW = LPT * VPL;                 // >= E
   constexpr int KPL = (kMaxK + LPT - 1) / LPT;   // output slots per lane
   __shared__ __attribute__((aligned(16))) float lrow[TPB][ROW];  // logits (+ logit_bias)
   __shared__ int32_t pick[TPB][kMaxK];                          // expert of each rank
+  __shared__ int32_t whist[HIST ? WPB : 1][HIST ? kHistMaxE : 1];  // per-wave pick counts
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int seg = lane / LPT;  // token slot in the wavefront
   const int sl = lane % LPT;   // lane inside the segment
   const int tb = wave * TPW + seg;
-  const int64_t t0 = ((int64_t)blockIdx.x * kWavesPerBlock + wave) * TPW;
-  if (t0 >= c.T) return;  // whole wavefront past the end; no block sync below
+  const int64_t t0 = ((int64_t)blockIdx.x * WPB + wave) * TPW;
+  // a whole wavefront past the end leaves at once, unless HIST (block syncs)
+  if (!HIST && t0 >= c.T) return;
   const int64_t t = t0 + seg;
   const bool tok_ok = t < c.T;
   const int E = c.E, K = c.k;
@@ -218,7 +223,7 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void select_kernel(
   const bool lvec = vec && nval == VPL;
 
   // logits (NSPLIT partial sums added in order), + logit_bias
-  const int64_t trow = tok_ok ? t : t0;
+  const int64_t trow = tok_ok ? t : (t0 < c.T ? t0 : (int64_t)c.T - 1);
   float lv[VPL];
   {
     float pv[NSPLIT][VPL];
@@ -410,19 +415,53 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void select_kernel(
       }
     }
   }
+  if constexpr (HIST) {
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    for (int e = lane; e < E; e += kWave) whist[wave][e] = 0;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint64_t below = lanemask_lt();
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {  // chunk i: every lane's i-th pick
+      const int e = (sl + i * LPT < K) ? pid[i] : -1;
+      const uint64_t p = peer_mask(e, nbits);
+      if (e >= 0 && (p & below) == 0) whist[wave][e] += __popcll(p);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += WPB * kWave) {
+      int n = 0;
+#pragma unroll
+      for (int w8 = 0; w8 < WPB; ++w8) n += whist[w8][e];
+      hist[(int64_t)blockIdx.x * E + e] = n;
+    }
+  }
 }
 
 template <int LPT, int VPL, int NS, bool MONO>
 hipError_t launch_vpl(const RouteCfg& c, const float* logits, int64_t stride, float* logits_out,
                       const float* logit_bias, const float* select_bias,
                       const int32_t* k_per_token, int32_t* ids, float* weights, int32_t* dev_err,
-                      int vec, hipStream_t s) {
-  constexpr int tokens_per_block = kWavesPerBlock * (kWave / LPT);
-  const int64_t blocks = ((int64_t)c.T + tokens_per_block - 1) / tokens_per_block;
+                      int vec, int32_t* hist, hipStream_t s) {
   prof_begin(kStageSelect, s);
-  hipLaunchKernelGGL((select_kernel<LPT, VPL, NS, MONO>), dim3((uint32_t)blocks),
-                     dim3(kWavesPerBlock * kWave), 0, s, c, logits, stride, logits_out,
-                     logit_bias, select_bias, k_per_token, ids, weights, dev_err, vec);
+  if constexpr (LPT <= 16 && LPT * VPL <= kHistMaxE) {
+    if (hist) {  // one dispatch tile per workgroup
+      constexpr int tpb = 4 * (kWave / LPT);
+      const int64_t blocks = ((int64_t)c.T + tpb - 1) / tpb;
+      hipLaunchKernelGGL((select_kernel<LPT, VPL, NS, MONO, 4, true>), dim3((uint32_t)blocks),
+                         dim3(4 * kWave), 0, s, c, logits, stride, logits_out, logit_bias,
+                         select_bias, k_per_token, ids, weights, dev_err, vec, hist);
+      prof_end(kStageSelect, s);
+      return hipGetLastError();
+    }
+  }
+  if (hist) return hipErrorInvalidValue;
+  constexpr int tpb = 4 * (kWave / LPT);
+  const int64_t blocks = ((int64_t)c.T + tpb - 1) / tpb;
+  hipLaunchKernelGGL((select_kernel<LPT, VPL, NS, MONO, 4, false>), dim3((uint32_t)blocks),
+                     dim3(4 * kWave), 0, s, c, logits, stride, logits_out, logit_bias,
+                     select_bias, k_per_token, ids, weights, dev_err, vec, nullptr);
   prof_end(kStageSelect, s);
   return hipGetLastError();
 }
@@ -431,11 +470,11 @@ template <int LPT, int VPL, bool MONO>
 hipError_t launch_splits(const RouteCfg& c, const float* logits, int splits, int64_t stride,
                          float* logits_out, const float* logit_bias, const float* select_bias,
                          const int32_t* k_per_token, int32_t* ids, float* weights,
-                         int32_t* dev_err, int vec, hipStream_t s) {
+                         int32_t* dev_err, int vec, int32_t* hist, hipStream_t s) {
 #define MOE_S(S_)                                                                        \
   return launch_vpl<LPT, VPL, S_, MONO>(c, logits, stride, logits_out, logit_bias,       \
                                         select_bias, k_per_token, ids, weights, dev_err, \
-                                        vec, s)
+                                        vec, hist, s)
   if (splits == 2) MOE_S(2);
   if (splits == 4) MOE_S(4);
   if (splits == 8) MOE_S(8);
@@ -448,22 +487,65 @@ template <int LPT, int VPL>
 hipError_t launch_mono(const RouteCfg& c, bool mono, const float* logits, int splits,
                        int64_t stride, float* logits_out, const float* logit_bias,
                        const float* select_bias, const int32_t* k_per_token, int32_t* ids,
-                       float* weights, int32_t* dev_err, int vec, hipStream_t s) {
+                       float* weights, int32_t* dev_err, int vec, int32_t* hist,
+                       hipStream_t s) {
   if (mono)
     return launch_splits<LPT, VPL, true>(c, logits, splits, stride, logits_out, logit_bias,
-                                         select_bias, k_per_token, ids, weights, dev_err, vec, s);
+                                         select_bias, k_per_token, ids, weights, dev_err, vec,
+                                         hist, s);
   return launch_splits<LPT, VPL, false>(c, logits, splits, stride, logits_out, logit_bias,
-                                        select_bias, k_per_token, ids, weights, dev_err, vec, s);
+                                        select_bias, k_per_token, ids, weights, dev_err, vec,
+                                        hist, s);
 }
 
 bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
 
+// Segment width (lanes per token) and experts per lane for these routing
+// parameters: the narrowest segment (about 16 experts per lane) that still
+// ranks the groups with one lane per group -- unless that leaves fewer than
+// 8 wavefronts per CU (2048 on the chip): then 16-lane segments, whose
+// shorter per-lane scans cut the serial latency of each round.
+void select_shape(const RouteCfg& c, int* lpt, int* vpl) {
+  const int E = c.E;
+  const bool grouped = c.n_groups > 1 && c.topk_groups < c.n_groups;
+  const int G = grouped ? c.n_groups : 1;
+  const bool few = (int64_t)c.T * 8 < 2048 * kWave;  // 8-lane segments: T / 8 wavefronts
+  int l = 64, v = 16;
+  if (few && G <= 16 && E <= 128) {
+    l = 16;
+    v = E <= 16 ? 1 : E <= 32 ? 2 : E <= 64 ? 4 : 8;
+  } else if (E <= 16 && G <= 4) {
+    l = 4, v = 4;
+  } else if (E <= 32 && G <= 4) {
+    l = 4, v = 8;
+  } else if (E <= 64 && G <= 8) {
+    l = 8, v = 8;
+  } else if (E <= 128 && G <= 8) {
+    l = 8, v = 16;
+  } else if (E <= 256 && G <= 16) {
+    l = 16, v = 16;
+  } else if (E <= 384 && G <= 16) {
+    l = 16, v = 24;
+  } else {
+    v = E <= 64 ? 1 : E <= 128 ? 2 : E <= 256 ? 4 : E <= 512 ? 8 : 16;
+  }
+  *lpt = l;
+  *vpl = v;
+}
+
 }  // namespace
+
+int select_hist_tokens(const RouteCfg& c) {
+  int lpt, vpl;
+  select_shape(c, &lpt, &vpl);
+  if (lpt > 16 || lpt * vpl > kHistMaxE) return 0;
+  return 4 * (kWave / lpt);
+}
 
 hipError_t launch_select(const RouteCfg& c, const float* logits, int32_t splits,
                          int64_t split_stride, float* logits_out, const float* logit_bias,
                          const float* select_bias, const int32_t* k_per_token, int32_t* ids,
-                         float* weights, int32_t* dev_err, hipStream_t stream) {
+                         float* weights, int32_t* dev_err, int32_t* hist, hipStream_t stream) {
   if (c.T == 0) return hipSuccess;
   const int E = c.E;
   const bool grouped = c.n_groups > 1 && c.topk_groups < c.n_groups;
@@ -471,33 +553,30 @@ hipError_t launch_select(const RouteCfg& c, const float* logits, int32_t splits,
   const int vec = E % 4 == 0 && aligned16(logits) && split_stride % 4 == 0 &&
                   (!logit_bias || aligned16(logit_bias)) &&
                   (!select_bias || aligned16(select_bias));
-  // The narrowest segment (about 16 experts per lane) that still ranks the
-  // groups with one lane per group -- unless that leaves fewer than 8
-  // wavefronts per CU (2048 on the chip): then 16-lane segments, whose
-  // shorter per-lane scans cut the serial latency of each round.
-  const int G = grouped ? c.n_groups : 1;
-  const bool few = (int64_t)c.T * 8 < 2048 * kWave;  // 8-lane segments: T / 8 wavefronts
-#define MOE_SEL(LPT_, VPL_)                                                                    \
-  return launch_mono<LPT_, VPL_>(c, mono, logits, splits, split_stride, logits_out, logit_bias, \
-                                 select_bias, k_per_token, ids, weights, dev_err, vec, stream)
-  if (few && G <= 16) {
-    if (E <= 16) MOE_SEL(16, 1);
-    if (E <= 32) MOE_SEL(16, 2);
-    if (E <= 64) MOE_SEL(16, 4);
-    if (E <= 128) MOE_SEL(16, 8);
-  }
-  if (E <= 16 && G <= 4) MOE_SEL(4, 4);
-  if (E <= 32 && G <= 4) MOE_SEL(4, 8);
-  if (E <= 64 && G <= 8) MOE_SEL(8, 8);
-  if (E <= 128 && G <= 8) MOE_SEL(8, 16);
-  if (E <= 256 && G <= 16) MOE_SEL(16, 16);
-  if (E <= 384 && G <= 16) MOE_SEL(16, 24);
-  if (E <= 64) MOE_SEL(64, 1);
-  if (E <= 128) MOE_SEL(64, 2);
-  if (E <= 256) MOE_SEL(64, 4);
-  if (E <= 512) MOE_SEL(64, 8);
-  MOE_SEL(64, 16);
+  int lpt, vpl;
+  select_shape(c, &lpt, &vpl);
+#define MOE_SEL(LPT_, VPL_)                                                                  \
+  if (lpt == LPT_ && vpl == VPL_)                                                            \
+    return launch_mono<LPT_, VPL_>(c, mono, logits, splits, split_stride, logits_out,        \
+                                   logit_bias, select_bias, k_per_token, ids, weights, dev_err, \
+                                   vec, hist, stream);
+  MOE_SEL(16, 1)
+  MOE_SEL(16, 2)
+  MOE_SEL(16, 4)
+  MOE_SEL(16, 8)
+  MOE_SEL(4, 4)
+  MOE_SEL(4, 8)
+  MOE_SEL(8, 8)
+  MOE_SEL(8, 16)
+  MOE_SEL(16, 16)
+  MOE_SEL(16, 24)
+  MOE_SEL(64, 1)
+  MOE_SEL(64, 2)
+  MOE_SEL(64, 4)
+  MOE_SEL(64, 8)
+  MOE_SEL(64, 16)
 #undef MOE_SEL
+  return hipErrorInvalidValue;
 }
 
 }  // namespace moe
