@@ -221,10 +221,11 @@ size_t moe_route_dispatch_workspace_size(const moe_route_params* p);
 
 /*
  * Per-kernel timing, for benchmarks and profiling only.
- * moe_profile_enable(1) clears earlier records and, from then on, brackets
- * every kernel the library launches with a pair of HIP events recorded on
- * that launch's stream (the events are created on the host per launch);
- * moe_profile_enable(0) stops recording.  moe_profile_read waits for the
+ * moe_profile_enable(1) clears earlier records and, from then on, gives
+ * every kernel the library launches a start and a stop HIP event that the
+ * runtime sets when the kernel itself starts and ends (hipExtLaunchKernel;
+ * the events are created on the host per launch); moe_profile_enable(0)
+ * stops recording.  moe_profile_read waits for the
  * recorded events and fills ms[i] (summed kernel time, milliseconds) and
  * launches[i] for the kernels MOE_STAGE_* = i < n; it returns
  * MOE_NUM_STAGES.  Records are process-wide.

@@ -278,28 +278,21 @@ hipError_t launch_fused(const int32_t* ids, int64_t R, int32_t E, int nbits, int
                         int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* tile_hist,
                         int32_t* dev_err, hipStream_t stream) {
   const int nt = (int)((R + kWaves * CPW * kWave - 1) / (kWaves * CPW * kWave));
-  prof_begin(kStageDispHist, stream);
-  hipLaunchKernelGGL((disp_hist_kernel<CPW, true>), dim3(nt), dim3(kThreads), 0, stream, ids, R,
-                     E, nbits, nt, tile_hist, dev_err);
-  prof_end(kStageDispHist, stream);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch(kStageDispHist, disp_hist_kernel<CPW, true>, dim3(nt), dim3(kThreads),
+                        stream, ids, R, E, nbits, nt, tile_hist, dev_err);
   if (e != hipSuccess) return e;
-  prof_begin(kStageDispScatter, stream);
-  hipLaunchKernelGGL((disp_scatter_kernel<CPW, true>), dim3(nt), dim3(kThreads), 0, stream, ids,
-                     R, E, nbits, nt, tile_hist, nullptr, nullptr, counts, offsets, perm, inv);
-  prof_end(kStageDispScatter, stream);
-  return hipGetLastError();
+  return launch(kStageDispScatter, disp_scatter_kernel<CPW, true>, dim3(nt), dim3(kThreads),
+                stream, ids, R, E, nbits, nt, (const int32_t*)tile_hist, (const int32_t*)nullptr,
+                (const int32_t*)nullptr, counts, offsets, perm, inv);
 }
 
 template <int CPW>
 hipError_t launch_placement(const int32_t* ids, int64_t R, int32_t E, int nbits, int nt,
                             const int32_t* tile_hist, int32_t* counts, int32_t* offsets,
                             int32_t* perm, int32_t* inv, hipStream_t stream) {
-  prof_begin(kStageDispScatter, stream);
-  hipLaunchKernelGGL((disp_scatter_kernel<CPW, true>), dim3(nt), dim3(kThreads), 0, stream, ids,
-                     R, E, nbits, nt, tile_hist, nullptr, nullptr, counts, offsets, perm, inv);
-  prof_end(kStageDispScatter, stream);
-  return hipGetLastError();
+  return launch(kStageDispScatter, disp_scatter_kernel<CPW, true>, dim3(nt), dim3(kThreads),
+                stream, ids, R, E, nbits, nt, tile_hist, (const int32_t*)nullptr,
+                (const int32_t*)nullptr, counts, offsets, perm, inv);
 }
 
 }  // namespace
@@ -356,25 +349,20 @@ hipError_t launch_dispatch(const int32_t* ids, int64_t R, int32_t E,
   int32_t* totals = tile_base + (int64_t)nt * E;
   hipError_t e;
   if (nt > 0) {
-    prof_begin(kStageDispHist, stream);
-    hipLaunchKernelGGL((disp_hist_kernel<kChunksPerWave, false>), dim3(nt), dim3(kThreads), 0,
-                       stream, ids, R, E, nbits, nt, tile_hist, dev_err);
-    prof_end(kStageDispHist, stream);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    prof_begin(kStageDispScan, stream);
-    hipLaunchKernelGGL(disp_tile_scan_kernel, dim3((E + kScanWaves - 1) / kScanWaves),
-                       dim3(kScanWaves * kWave), 0, stream, tile_hist, nt, E, tile_base, totals);
-    prof_end(kStageDispScan, stream);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    e = launch(kStageDispHist, disp_hist_kernel<kChunksPerWave, false>, dim3(nt),
+               dim3(kThreads), stream, ids, R, E, nbits, nt, tile_hist, dev_err);
+    if (e != hipSuccess) return e;
+    e = launch(kStageDispScan, disp_tile_scan_kernel, dim3((E + kScanWaves - 1) / kScanWaves),
+               dim3(kScanWaves * kWave), stream, (const int32_t*)tile_hist, nt, E, tile_base,
+               totals);
+    if (e != hipSuccess) return e;
   }
   // with no routes the scatter kernel runs one workgroup that only writes
   // zero counts and offsets (totals is not read then)
-  prof_begin(kStageDispScatter, stream);
-  hipLaunchKernelGGL((disp_scatter_kernel<kChunksPerWave, false>), dim3(nt > 0 ? nt : 1),
-                     dim3(kThreads), 0, stream, ids, R, E, nbits, nt, nullptr, tile_base,
-                     nt > 0 ? totals : nullptr, counts, offsets, perm, inv);
-  prof_end(kStageDispScatter, stream);
-  return hipGetLastError();
+  return launch(kStageDispScatter, disp_scatter_kernel<kChunksPerWave, false>,
+                dim3(nt > 0 ? nt : 1), dim3(kThreads), stream, ids, R, E, nbits, nt,
+                (const int32_t*)nullptr, (const int32_t*)tile_base,
+                (const int32_t*)(nt > 0 ? totals : nullptr), counts, offsets, perm, inv);
 }
 
 }  // namespace moe

@@ -403,12 +403,9 @@ hipError_t launch_pipe(const void* x, const void* W, const float* logit_bias, fl
   const int per_split = (n_stages + splits - 1) / splits;
   const int tiles = n_m * n_n * splits;
   const int per_xcd = (tiles + kXcds - 1) / kXcds;
-  prof_begin(kStageGate, s);
-  hipLaunchKernelGGL((gate_gemm_pipe_kernel<In, BM, BN, NS, RB, WM, WN>),
-                     dim3(per_xcd * kXcds), dim3(WM * WN * kWave), 0, s, (const In*)x, (const In*)W, logit_bias, out, T, d, E,
-                     n_m, n_n, splits, per_xcd, per_split);
-  prof_end(kStageGate, s);
-  return hipGetLastError();
+  return launch(kStageGate, gate_gemm_pipe_kernel<In, BM, BN, NS, RB, WM, WN>,
+                dim3(per_xcd * kXcds), dim3(WM * WN * kWave), s, (const In*)x, (const In*)W,
+                logit_bias, out, T, d, E, n_m, n_n, splits, per_xcd, per_split);
 }
 
 template <typename In, int BM, int BN, int KB>
@@ -422,17 +419,11 @@ hipError_t launch_tile(const void* x, const void* W, const float* logit_bias, fl
   const bool vec = (d % ElemInfo<In>::kPerChunk == 0) &&
                    (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
                    (reinterpret_cast<uintptr_t>(W) % 16 == 0);
-  prof_begin(kStageGate, s);
   if (vec)
-    hipLaunchKernelGGL((gate_gemm_kernel<In, BM, BN, KB, true>), grid, dim3(kThreads), 0, s,
-                       (const In*)x, (const In*)W, logit_bias, logits, T, d, E, n_m, n_n,
-                       per_xcd);
-  else
-    hipLaunchKernelGGL((gate_gemm_kernel<In, BM, BN, KB, false>), grid, dim3(kThreads), 0, s,
-                       (const In*)x, (const In*)W, logit_bias, logits, T, d, E, n_m, n_n,
-                       per_xcd);
-  prof_end(kStageGate, s);
-  return hipGetLastError();
+    return launch(kStageGate, gate_gemm_kernel<In, BM, BN, KB, true>, grid, dim3(kThreads), s,
+                  (const In*)x, (const In*)W, logit_bias, logits, T, d, E, n_m, n_n, per_xcd);
+  return launch(kStageGate, gate_gemm_kernel<In, BM, BN, KB, false>, grid, dim3(kThreads), s,
+                (const In*)x, (const In*)W, logit_bias, logits, T, d, E, n_m, n_n, per_xcd);
 }
 
 // Tile shapes (BM x BN) and pipeline depth.  The default takes the largest

@@ -119,19 +119,13 @@ hipError_t launch_typed(const RouteCfg& c, const int32_t* tok, const int32_t* ta
                    reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
                    reinterpret_cast<uintptr_t>(W) % 16 == 0;
   if (vec) {
-    prof_begin(kStageHash, s);
-    hipLaunchKernelGGL((hash_route_kernel<In, true>), dim3((uint32_t)blocks),
-                       dim3(kWavesPerBlock * kWave), 0, s, c, tok, tab, vocab, (const In*)x,
-                       (const In*)W, lb, ids, w, err);
-    prof_end(kStageHash, s);
-  } else {
-    prof_begin(kStageHash, s);
-    hipLaunchKernelGGL((hash_route_kernel<In, false>), dim3((uint32_t)blocks),
-                       dim3(kWavesPerBlock * kWave), 0, s, c, tok, tab, vocab, (const In*)x,
-                       (const In*)W, lb, ids, w, err);
-    prof_end(kStageHash, s);
+    return launch(kStageHash, hash_route_kernel<In, true>, dim3((uint32_t)blocks),
+                  dim3(kWavesPerBlock * kWave), s, c, tok, tab, vocab, (const In*)x, (const In*)W,
+                  lb, ids, w, err);
   }
-  return hipGetLastError();
+  return launch(kStageHash, hash_route_kernel<In, false>, dim3((uint32_t)blocks),
+                dim3(kWavesPerBlock * kWave), s, c, tok, tab, vocab, (const In*)x, (const In*)W,
+                lb, ids, w, err);
 }
 
 }  // namespace

@@ -2,6 +2,7 @@
 // Each launcher enqueues on `stream` and returns the hipError_t of the launch.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -18,10 +19,21 @@ enum Stage : int32_t {
   kNumStages = 6
 };
 
-// When timing is enabled these record a HIP event on `stream` before and
-// after a launch; otherwise they do nothing.
-void prof_begin(Stage st, hipStream_t stream);
-void prof_end(Stage st, hipStream_t stream);
+// Per-kernel timing (moe_profile_enable): the start/stop events of the next
+// launch of stage `st`, both null while timing is off.
+void prof_events(Stage st, hipEvent_t* start, hipEvent_t* stop);
+
+// Launch `kernel` on `stream`; while per-kernel timing is on, the launch
+// carries start/stop events that the runtime sets when the kernel itself
+// starts and ends (hipExtLaunchKernel), not when the stream reaches them.
+template <typename... KArgs, typename... Args>
+hipError_t launch(Stage st, void (*kernel)(KArgs...), dim3 grid, dim3 block,
+                  hipStream_t stream, Args... args) {
+  hipEvent_t start = nullptr, stop = nullptr;
+  prof_events(st, &start, &stop);
+  hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, start, stop, 0, args...);
+  return hipGetLastError();
+}
 
 // Flattened routing configuration handed to the select kernels.
 struct RouteCfg {

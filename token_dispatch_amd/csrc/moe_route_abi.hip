@@ -81,12 +81,11 @@ struct ProfRecord {
 std::atomic<bool> g_prof_on{false};
 std::mutex g_prof_mu;
 std::vector<ProfRecord> g_prof_records;
-thread_local hipEvent_t g_prof_open = nullptr;
 
 void prof_clear_locked() {
   for (auto& r : g_prof_records) {
-    hipEventDestroy(r.begin);
-    hipEventDestroy(r.end);
+    (void)hipEventDestroy(r.begin);
+    (void)hipEventDestroy(r.end);
   }
   g_prof_records.clear();
 }
@@ -121,22 +120,19 @@ int32_t check_route_params(const moe_route_params* p, bool need_d) {
 
 namespace moe {
 
-void prof_begin(Stage, hipStream_t stream) {
+void prof_events(Stage st, hipEvent_t* start, hipEvent_t* stop) {
+  *start = *stop = nullptr;
   if (!g_prof_on.load(std::memory_order_relaxed)) return;
-  hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return;
-  hipEventRecord(e, stream);
-  g_prof_open = e;
-}
-
-void prof_end(Stage st, hipStream_t stream) {
-  if (!g_prof_on.load(std::memory_order_relaxed) || g_prof_open == nullptr) return;
-  hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return;
-  hipEventRecord(e, stream);
+  hipEvent_t a = nullptr, b = nullptr;
+  if (hipEventCreate(&a) != hipSuccess) return;
+  if (hipEventCreate(&b) != hipSuccess) {
+    (void)hipEventDestroy(a);
+    return;
+  }
   std::lock_guard<std::mutex> lk(g_prof_mu);
-  g_prof_records.push_back({(int32_t)st, g_prof_open, e});
-  g_prof_open = nullptr;
+  g_prof_records.push_back({(int32_t)st, a, b});
+  *start = a;
+  *stop = b;
 }
 
 }  // namespace moe

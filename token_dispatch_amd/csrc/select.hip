@@ -444,26 +444,18 @@ hipError_t launch_vpl(const RouteCfg& c, const float* logits, int64_t stride, fl
                       const float* logit_bias, const float* select_bias,
                       const int32_t* k_per_token, int32_t* ids, float* weights, int32_t* dev_err,
                       int vec, int32_t* hist, hipStream_t s) {
-  prof_begin(kStageSelect, s);
-  if constexpr (LPT <= 16 && LPT * VPL <= kHistMaxE) {
-    if (hist) {  // one dispatch tile per workgroup
-      constexpr int tpb = 4 * (kWave / LPT);
-      const int64_t blocks = ((int64_t)c.T + tpb - 1) / tpb;
-      hipLaunchKernelGGL((select_kernel<LPT, VPL, NS, MONO, 4, true>), dim3((uint32_t)blocks),
-                         dim3(4 * kWave), 0, s, c, logits, stride, logits_out, logit_bias,
-                         select_bias, k_per_token, ids, weights, dev_err, vec, hist);
-      prof_end(kStageSelect, s);
-      return hipGetLastError();
-    }
-  }
-  if (hist) return hipErrorInvalidValue;
   constexpr int tpb = 4 * (kWave / LPT);
   const int64_t blocks = ((int64_t)c.T + tpb - 1) / tpb;
-  hipLaunchKernelGGL((select_kernel<LPT, VPL, NS, MONO, 4, false>), dim3((uint32_t)blocks),
-                     dim3(4 * kWave), 0, s, c, logits, stride, logits_out, logit_bias,
-                     select_bias, k_per_token, ids, weights, dev_err, vec, nullptr);
-  prof_end(kStageSelect, s);
-  return hipGetLastError();
+  if constexpr (LPT <= 16 && LPT * VPL <= kHistMaxE) {
+    if (hist)  // one dispatch tile per workgroup
+      return launch(kStageSelect, select_kernel<LPT, VPL, NS, MONO, 4, true>,
+                    dim3((uint32_t)blocks), dim3(4 * kWave), s, c, logits, stride, logits_out,
+                    logit_bias, select_bias, k_per_token, ids, weights, dev_err, vec, hist);
+  }
+  if (hist) return hipErrorInvalidValue;
+  return launch(kStageSelect, select_kernel<LPT, VPL, NS, MONO, 4, false>, dim3((uint32_t)blocks),
+                dim3(4 * kWave), s, c, logits, stride, logits_out, logit_bias, select_bias,
+                k_per_token, ids, weights, dev_err, vec, (int32_t*)nullptr);
 }
 
 template <int LPT, int VPL, bool MONO>
