@@ -4,7 +4,9 @@
 One step = one moe_route_dispatch call -- the gate contraction, scoring,
 selection and weights of moe_route, then the histogram, offsets,
 permutation and inverse of moe_dispatch -- over one batch of seeded
-synthetic tokens.  Inputs are resident in HBM before timing; each step
+synthetic tokens (hash workloads: moe_route_hash, whose ids come from the
+token-id table and whose weights from the k gathered gate logits, then
+moe_dispatch).  Inputs are resident in HBM before timing; each step
 routes a different copy of x (rotating through copies totalling more than the
 256 MB last-level cache) so the gate reads x from HBM, not from cache.
 
@@ -45,6 +47,7 @@ def stage_bytes(w, T, R, R_valid, tile_bytes):
     E, d, k = w.E, w.d, w.k
     return {
         "gate": T * d * xb + E * d * xb + T * E * 4,
+        "hash": T * 4 + T * k * 4 + T * d * xb + E * d * xb + T * k * 8,
         "select": T * E * 4 + T * k * 8 + (T * 4 if w.dynamic_k else 0),
         "disp_hist": R * 4 + tile_bytes,
         "disp_scan": 2 * tile_bytes + E * 4,
@@ -74,7 +77,18 @@ def cpu_baseline(w, inp, seconds, threads):
     import oracle
     import workloads as wl
 
+    def run_hash(n):  # table ids, the gate, the gathered weights, dispatch
+        t0 = time.perf_counter()
+        ids, _ = oracle.hash_ids(inp["token_ids"][:n], inp["tid2eid"], w.E)
+        lg = oracle.gate(wl.rows(inp["x"], np.arange(n)), inp["W"], inp["logit_bias"])
+        oracle.weights_for_ids(lg, ids, score=w.score, renormalize=w.renormalize,
+                               route_scale=w.route_scale)
+        oracle.dispatch(ids, w.E)
+        return time.perf_counter() - t0
+
     def run(n):
+        if w.hash_vocab:
+            return run_hash(n)
         sl = np.arange(n)
         kw = dict(score=w.score, logit_bias=inp["logit_bias"], select_bias=inp["select_bias"],
                   k_per_token=None if inp["k_per_token"] is None else inp["k_per_token"][:n],
@@ -93,9 +107,12 @@ def cpu_baseline(w, inp, seconds, threads):
     while n == w.T and total < seconds:  # one pass is short: repeat it
         total += run(n)
         reps += 1
-    return {"value": reps * n / total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    what = ("hash ids + gate + gathered weights + dispatch" if w.hash_vocab
+            else "gate + route + dispatch")
+    return {"value": reps * n / total, "unit": "tokens/s",
+            "cores": 1 if w.hash_vocab else threads, "kind": "oracle",
             "sample": f"{'first %d of ' % n if n < w.T else 'all '}{w.T} tokens of the same "
-                      f"workload x {reps} (gate + route + dispatch, fp64), {total:.1f} s"}
+                      f"workload x {reps} ({what}, fp64), {total:.1f} s"}
 
 
 def main():
@@ -137,8 +154,6 @@ def main():
     import workloads as wl
 
     w = wl.WORKLOADS[args.workload]
-    if w.hash_vocab:
-        raise SystemExit("bench.py times the learned-router workloads; hash mode is a test case")
     log(f"[bench] generating {w.name} inputs (T={w.T}, d={w.d}, E={w.E})")
     inp = wl.make_inputs(w)
     dev = torch.device("cuda:0")
@@ -179,6 +194,19 @@ def main():
     def step(i):  # one moe_route_dispatch call: gate, selection, dispatch
         tda.route_dispatch(xs[i % n_copies], W, k, ids=ids, weights=weights, counts=counts,
                            offsets=offsets, perm=perm, inv=inv, workspace=ws, **rkw)
+
+    disp_ws = ws_bytes - route_bytes  # the dispatch's tile data
+    if w.hash_vocab:
+        tok, tab = up(inp["token_ids"]), up(inp["tid2eid"])
+        disp_ws = tda.dispatch_workspace_size(T, k, E)
+        dws = torch.empty(max(1, disp_ws), dtype=torch.uint8, device=dev)
+
+        def step(i):  # noqa: F811 -- moe_route_hash then moe_dispatch
+            tda.route_hash(tok, tab, E, x=xs[i % n_copies], W=W, score=w.score,
+                           logit_bias=lb, renormalize=w.renormalize,
+                           route_scale=w.route_scale, ids=ids, weights=weights)
+            tda.dispatch(ids, E, counts=counts, offsets=offsets, perm=perm, inv=inv,
+                         workspace=dws)
 
     log(f"[bench] {n_copies} rotating copies of x ({xbytes / 1e6:.1f} MB each); "
         f"warmup {args.warmup}, steps {args.steps}")
@@ -239,7 +267,6 @@ def main():
 
     R = T * k
     R_valid = int(counts.sum().item())
-    disp_ws = ws_bytes - route_bytes  # the dispatch's tile data
     tile_bytes = disp_ws if "disp_scan" not in prof or not prof["disp_scan"][1] else (disp_ws - 4 * E) // 2
     sbytes = stage_bytes(w, T, R, R_valid, tile_bytes)
     stages = {}
@@ -255,6 +282,7 @@ def main():
     achieved = sbytes[dom] / (dom_us * 1e-6) / 1e9
     traffic = measured_traffic(args.traffic, w.name, dom)
     gate_flops = 2.0 * T * w.d * E
+    maxvio = float(counts.max().item()) / (R_valid / E) - 1.0 if R_valid else 0.0
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic,
@@ -283,9 +311,12 @@ def main():
         "config": {"workload": f"{w.name}: T={T} tokens, d={w.d}, E={E}, "
                                f"k={'/'.join(map(str, w.dynamic_k)) + ' per request' if w.dynamic_k else k}, "
                                f"score={w.score}, groups={w.n_groups}/{w.topk_groups}, "
-                               f"dispatch over {E} experts",
+                               + (f"hash ids from tid2eid[{w.hash_vocab}][{k}], "
+                                  if w.hash_vocab else "")
+                               + f"dispatch over {E} experts",
                    "T": T, "d": w.d, "E": E, "k_max": k, "x_copies": n_copies},
         "stages": stages,
+        "maxvio": round(maxvio, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 /* return codes */
 #define MOE_OK 0
@@ -155,16 +155,25 @@ size_t moe_route_workspace_size(const moe_route_params* p);
  * v).  A token id outside [0, vocab) empties its row (ids -1, weights 0,
  * one error); a table entry outside [0, E) empties its slot (one error).
  * When x and W are given, weights[t][j] = score(l[t][ids[t][j]]) with
- * l = x.W^T (+ logit_bias) computed only for the k table experts,
- * renormalised over the row's valid slots when p->renormalize, times
- * route_scale; SOFTMAX needs renormalize = 1 (it then equals SOFTMAX_TOPK).
- * When x and W are NULL only ids are written (weights may be NULL).
+ * l = x.W^T (+ logit_bias), renormalised over the row's valid slots when
+ * p->renormalize, times route_scale; SOFTMAX needs renormalize = 1 (it then
+ * equals SOFTMAX_TOPK).  With a workspace of at least
+ * moe_route_hash_workspace_size(p) bytes the logits of every expert come
+ * from the tiled gate contraction (as in moe_route; the fastest way, since
+ * the rows of W are shared by many tokens); with none (NULL / 0) only the k
+ * table experts' logits are computed, as k dot products per token.  When x
+ * and W are NULL only ids are written (weights may be NULL).
  * Uses p->T, d, E, k, dtype, score, renormalize, route_scale.
  */
 int32_t moe_route_hash(const moe_route_params* p, const int32_t* token_ids,
                        const int32_t* tid2eid, int32_t vocab, const void* x,
                        const void* W, const float* logit_bias, int32_t* ids,
-                       float* weights, int32_t* dev_err, void* stream);
+                       float* weights, void* workspace, size_t workspace_bytes,
+                       int32_t* dev_err, void* stream);
+
+/* Bytes of device workspace moe_route_hash uses for the gate logits with
+ * these parameters (16-byte aligned x and W assumed). */
+size_t moe_route_hash_workspace_size(const moe_route_params* p);
 
 /* Bytes of device workspace moe_dispatch needs for these sizes. */
 size_t moe_dispatch_workspace_size(int32_t T, int32_t k_stride, int32_t E);

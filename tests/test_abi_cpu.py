@@ -20,8 +20,10 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    assert {"moe_route", "moe_route_workspace_size", "moe_route_hash", "moe_dispatch",
-            "moe_dispatch_workspace_size", "moe_last_error", "moe_abi_version"} <= set(names), names
+    assert {"moe_route", "moe_route_workspace_size", "moe_route_hash",
+            "moe_route_hash_workspace_size", "moe_dispatch", "moe_dispatch_workspace_size",
+            "moe_route_dispatch", "moe_route_dispatch_workspace_size", "moe_last_error",
+            "moe_abi_version"} <= set(names), names
 
 
 def test_library_exports_every_declared_symbol():
@@ -119,15 +121,19 @@ def test_route_hash_validation():
     L = tda.lib()
     p = tda.make_params(4, 64, 8, 2, score="softmax", renormalize=False)
     assert L.moe_route_hash(ctypes.byref(p), FAKE, FAKE, 10, FAKE, FAKE, None, FAKE, FAKE, None,
-                            None) == tda.MOE_EUNSUPPORTED
+                            0, None, None) == tda.MOE_EUNSUPPORTED
     p = tda.make_params(4, 64, 8, 2, score="sigmoid")
     assert L.moe_route_hash(ctypes.byref(p), FAKE, FAKE, 0, FAKE, FAKE, None, FAKE, FAKE, None,
-                            None) == tda.MOE_EINVAL
+                            0, None, None) == tda.MOE_EINVAL
     assert L.moe_route_hash(ctypes.byref(p), None, FAKE, 10, None, None, None, FAKE, None, None,
-                            None) == tda.MOE_EINVAL
+                            0, None, None) == tda.MOE_EINVAL
     p0 = tda.make_params(0, 64, 8, 2, score="sigmoid")
     assert L.moe_route_hash(ctypes.byref(p0), None, None, 10, None, None, None, None, None, None,
-                            None) == tda.MOE_OK
+                            0, None, None) == tda.MOE_OK
+    # the gate logits of every expert, per K split
+    n = tda.route_hash_workspace_size(16384, 7168, 384, 6, score="sqrt_softplus")
+    assert n >= 16384 * 384 * 4 and n % (16384 * 384 * 4) == 0
+    assert tda.route_hash_workspace_size(0, 64, 8, 2) == 0
 
 
 def test_dispatch_validation_and_workspace_size():

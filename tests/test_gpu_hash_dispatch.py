@@ -58,7 +58,8 @@ def test_hash_full_size_sampled():
 
 @pytest.mark.parametrize("score", ["sigmoid", "sqrt_softplus", "softmax_topk", "softmax"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_hash_scores_ragged_and_duplicates(score, dtype):
+@pytest.mark.parametrize("gate", [True, False], ids=["gate-logits", "dot-products"])
+def test_hash_scores_ragged_and_duplicates(score, dtype, gate):
     rng = np.random.default_rng([len(score), len(dtype)])
     T, d, E, k, V = 77, 100, 24, 5, 50
     tab = rng.integers(0, E, size=(V, k)).astype(np.int32)  # duplicates allowed
@@ -68,9 +69,10 @@ def test_hash_scores_ragged_and_duplicates(score, dtype):
     lb = (0.5 * rng.standard_normal(E)).astype(np.float32)
     if dtype == "bf16":
         x, W = wl.f32_to_bf16_bits(x), wl.f32_to_bf16_bits(W)
-    say("hash scores", score, dtype)
+    say("hash scores", score, dtype, gate)
+    ws = None if gate else torch.empty(0, dtype=torch.uint8, device=DEV)
     ids, wts = tda.route_hash(up(tok), up(tab), E, x=up(x), W=up(W), score=score,
-                              logit_bias=up(lb), route_scale=1.5)
+                              logit_bias=up(lb), route_scale=1.5, workspace=ws)
     ref_ids, _ = oracle.hash_ids(tok, tab, E)
     np.testing.assert_array_equal(down(ids), ref_ids)
     ref_w = oracle.weights_for_ids(oracle.gate(x, W, lb), ref_ids, score=score, route_scale=1.5)

@@ -21,12 +21,13 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe_route.so")
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EDEVICE = 0, -1, -2, -3
 MAX_EXPERTS, MAX_K, MAX_GROUPS = 1024, 32, 64
 SCORES = {"softmax": 0, "sigmoid": 1, "sqrt_softplus": 2, "softmax_topk": 3}
 GROUP_SCORES = {"max": 0, "top2_sum": 1}
 EXPORTS = ("moe_route", "moe_route_workspace_size", "moe_route_hash",
+           "moe_route_hash_workspace_size",
            "moe_dispatch_workspace_size", "moe_dispatch",
            "moe_route_dispatch", "moe_route_dispatch_workspace_size",
            "moe_profile_enable", "moe_profile_read", "moe_last_error", "moe_abi_version")
@@ -64,8 +65,11 @@ def lib() -> ctypes.CDLL:
         L.moe_route.restype = i32
         L.moe_route_workspace_size.argtypes = [P]
         L.moe_route_workspace_size.restype = ctypes.c_size_t
-        L.moe_route_hash.argtypes = [P, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp]
+        L.moe_route_hash.argtypes = [P, vp, vp, i32, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                     vp, vp]
         L.moe_route_hash.restype = i32
+        L.moe_route_hash_workspace_size.argtypes = [P]
+        L.moe_route_hash_workspace_size.restype = ctypes.c_size_t
         L.moe_dispatch_workspace_size.argtypes = [i32, i32, i32]
         L.moe_dispatch_workspace_size.restype = ctypes.c_size_t
         L.moe_dispatch.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, ctypes.c_size_t, vp, vp]
@@ -251,9 +255,14 @@ def route_dispatch(x: Optional[torch.Tensor], W: Optional[torch.Tensor], k: int,
 
 def route_hash(token_ids: torch.Tensor, tid2eid: torch.Tensor, E: int, *, x=None, W=None,
                score: str = "sqrt_softplus", logit_bias=None, renormalize: bool = True,
-               route_scale: float = 1.0, ids=None, weights=None, dev_err=None):
+               route_scale: float = 1.0, ids=None, weights=None, workspace=None,
+               dev_err=None):
     """Hash routing: ids = tid2eid[token_ids] ([vocab][k] row-major table), plus
-    weights from the k gathered gate logits when x and W are given."""
+    weights from the k gathered gate logits when x and W are given.
+
+    ``workspace`` (uint8 device tensor) holds the gate logits of every expert
+    (the tiled gate contraction); it is allocated when not given.  An empty
+    tensor asks for the k dot products per token instead."""
     _dev(token_ids, "token_ids", torch.int32)
     _dev(tid2eid, "tid2eid", torch.int32)
     T = token_ids.shape[0]
@@ -273,10 +282,22 @@ def route_hash(token_ids: torch.Tensor, tid2eid: torch.Tensor, E: int, *, x=None
     if weights is None and x is not None:
         weights = torch.empty((T, k), dtype=torch.float32, device=device)
     p = make_params(T, d, E, k, dt, score, 1, 1, "max", renormalize, route_scale)
+    if workspace is None and x is not None:
+        nbytes = int(lib().moe_route_hash_workspace_size(ctypes.byref(p)))
+        if nbytes:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ws = None if not ws_bytes else workspace
     _check(lib().moe_route_hash(ctypes.byref(p), _p(token_ids), _p(tid2eid), vocab, _p(x),
-                                _p(W), _p(logit_bias), _p(ids), _p(weights), _p(dev_err),
-                                _stream(device)))
+                                _p(W), _p(logit_bias), _p(ids), _p(weights), _p(ws), ws_bytes,
+                                _p(dev_err), _stream(device)))
     return ids, weights
+
+
+def route_hash_workspace_size(T, d, E, k, dtype=1, **kw) -> int:
+    """Device bytes moe_route_hash uses for the gate logits of these shapes."""
+    p = make_params(T, d, E, k, dtype, **kw)
+    return int(lib().moe_route_hash_workspace_size(ctypes.byref(p)))
 
 
 def dispatch_workspace_size(T: int, k_stride: int, E: int) -> int:

@@ -4,10 +4,14 @@
 // bias).
 //
 // One wavefront per token: lanes 0..k-1 gather the table row (validating the
-// token id and every entry), then, when x and W are given, the wave computes
-// only the k gate logits the row needs -- k dot products of length d, the
-// lanes striding over d with 16-byte loads -- and turns them into weights
-// with the layer's score function.
+// token id and every entry), then, when weights are wanted, lane j takes the
+// logit of slot j and the wave turns the k logits into weights with the
+// layer's score function.  The logits come either from the gate contraction
+// of every expert (the tiled matrix-core kernel, into a workspace; NSPLIT
+// K-split partial arrays added in order) -- the k dot products alone would
+// re-read k rows of W from L2 for every token, about 64 times the gate's L2
+// traffic at E = 384, k = 6 -- or, with no workspace, from k dot products of
+// length d computed here (the lanes striding over d with 16-byte loads).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -55,11 +59,15 @@ __device__ __forceinline__ float lane_dot(const In* __restrict__ xr, const In* _
   return acc;
 }
 
-template <typename In, bool VEC>
+// NSPLIT == 0: dot products from x and W (+ logit_bias); NSPLIT > 0: the
+// logits (bias included) are the sum of NSPLIT arrays [T][E], split_stride
+// floats apart.
+template <typename In, bool VEC, int NSPLIT>
 __global__ __launch_bounds__(kWavesPerBlock * kWave) void hash_route_kernel(
     RouteCfg c, const int32_t* __restrict__ token_ids,
     const int32_t* __restrict__ tid2eid, int32_t vocab, const In* __restrict__ x,
     const In* __restrict__ W, const float* __restrict__ logit_bias,
+    const float* __restrict__ logits, int64_t split_stride,
     int32_t* __restrict__ ids, float* __restrict__ weights,
     int32_t* __restrict__ dev_err) {
   const int lane = threadIdx.x & 63;
@@ -81,16 +89,27 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void hash_route_kernel(
   const int nerr = tok_ok ? __popcll(__ballot(bad_slot)) : 1;
   if (lane == 0 && nerr && dev_err) atomicAdd(dev_err, nerr);
   if (lane < k) ids[t * k + lane] = e;
-  if (x == nullptr) return;
+  if (weights == nullptr) return;
 
-  const In* xr = x + t * (int64_t)c.d;
   float my_l = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const int ej = readlane_i32(e, j);
-    if (ej < 0) continue;
-    float acc = wave_sum_f32(lane_dot<In, VEC>(xr, W + (int64_t)ej * c.d, c.d, lane));
-    if (logit_bias) acc += logit_bias[ej];
-    if (lane == j) my_l = acc;
+  if constexpr (NSPLIT > 0) {
+    if (e >= 0) {
+      float pv[NSPLIT];
+#pragma unroll
+      for (int sp = 0; sp < NSPLIT; ++sp) pv[sp] = logits[sp * split_stride + t * c.E + e];
+      my_l = pv[0];
+#pragma unroll
+      for (int sp = 1; sp < NSPLIT; ++sp) my_l += pv[sp];
+    }
+  } else {
+    const In* xr = x + t * (int64_t)c.d;
+    for (int j = 0; j < k; ++j) {
+      const int ej = readlane_i32(e, j);
+      if (ej < 0) continue;
+      float acc = wave_sum_f32(lane_dot<In, VEC>(xr, W + (int64_t)ej * c.d, c.d, lane));
+      if (logit_bias) acc += logit_bias[ej];
+      if (lane == j) my_l = acc;
+    }
   }
 
   const bool sel = lane < k && e >= 0;
@@ -112,20 +131,33 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void hash_route_kernel(
 
 template <typename In>
 hipError_t launch_typed(const RouteCfg& c, const int32_t* tok, const int32_t* tab, int32_t vocab,
-                        const void* x, const void* W, const float* lb, int32_t* ids,
-                        float* w, int32_t* err, hipStream_t s) {
-  const int64_t blocks = ((int64_t)c.T + kWavesPerBlock - 1) / kWavesPerBlock;
+                        const void* x, const void* W, const float* lb, const float* logits,
+                        int32_t splits, int64_t split_stride, int32_t* ids, float* w,
+                        int32_t* err, hipStream_t s) {
+  const dim3 grid((uint32_t)(((int64_t)c.T + kWavesPerBlock - 1) / kWavesPerBlock));
+  const dim3 block(kWavesPerBlock * kWave);
+  const In* xi = (const In*)x;
+  const In* Wi = (const In*)W;
+  if (logits) {
+#define MOE_H(S_)                                                                              \
+  if (splits == S_)                                                                            \
+    return launch(kStageHash, hash_route_kernel<In, false, S_>, grid, block, s, c, tok, tab,  \
+                  vocab, xi, Wi, lb, logits, split_stride, ids, w, err);
+    MOE_H(1)
+    MOE_H(2)
+    MOE_H(4)
+    MOE_H(8)
+#undef MOE_H
+    return hipErrorInvalidValue;
+  }
   const bool vec = x != nullptr && (c.d % (16 / sizeof(In)) == 0) &&
                    reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
                    reinterpret_cast<uintptr_t>(W) % 16 == 0;
-  if (vec) {
-    return launch(kStageHash, hash_route_kernel<In, true>, dim3((uint32_t)blocks),
-                  dim3(kWavesPerBlock * kWave), s, c, tok, tab, vocab, (const In*)x, (const In*)W,
-                  lb, ids, w, err);
-  }
-  return launch(kStageHash, hash_route_kernel<In, false>, dim3((uint32_t)blocks),
-                dim3(kWavesPerBlock * kWave), s, c, tok, tab, vocab, (const In*)x, (const In*)W,
-                lb, ids, w, err);
+  if (vec)
+    return launch(kStageHash, hash_route_kernel<In, true, 0>, grid, block, s, c, tok, tab, vocab,
+                  xi, Wi, lb, (const float*)nullptr, (int64_t)0, ids, w, err);
+  return launch(kStageHash, hash_route_kernel<In, false, 0>, grid, block, s, c, tok, tab, vocab,
+                xi, Wi, lb, (const float*)nullptr, (int64_t)0, ids, w, err);
 }
 
 }  // namespace
@@ -133,15 +165,15 @@ hipError_t launch_typed(const RouteCfg& c, const int32_t* tok, const int32_t* ta
 hipError_t launch_hash_route(const RouteCfg& c, int32_t dtype,
                              const int32_t* token_ids, const int32_t* tid2eid,
                              int32_t vocab, const void* x, const void* W,
-                             const float* logit_bias, int32_t* ids,
-                             float* weights, int32_t* dev_err,
-                             hipStream_t stream) {
+                             const float* logit_bias, const float* logits, int32_t splits,
+                             int64_t split_stride, int32_t* ids, float* weights,
+                             int32_t* dev_err, hipStream_t stream) {
   if (c.T == 0) return hipSuccess;
   if (dtype == 1)
-    return launch_typed<uint16_t>(c, token_ids, tid2eid, vocab, x, W, logit_bias, ids, weights,
-                                  dev_err, stream);
-  return launch_typed<float>(c, token_ids, tid2eid, vocab, x, W, logit_bias, ids, weights,
-                             dev_err, stream);
+    return launch_typed<uint16_t>(c, token_ids, tid2eid, vocab, x, W, logit_bias, logits, splits,
+                                  split_stride, ids, weights, dev_err, stream);
+  return launch_typed<float>(c, token_ids, tid2eid, vocab, x, W, logit_bias, logits, splits,
+                             split_stride, ids, weights, dev_err, stream);
 }
 
 }  // namespace moe

@@ -79,12 +79,15 @@ hipError_t launch_select(const RouteCfg& c, const float* logits, int32_t splits,
 int select_hist_tokens(const RouteCfg& c);  // 0: no histogram option
 
 // Hash routing: table gather (+ k gathered gate dot products and weights).
+// With `logits` (the sum of `splits` arrays [T][E], split_stride floats
+// apart, logit bias included) the weights come from those; otherwise, when
+// weights is not NULL, from k dot products of x and W (+ logit_bias).
 hipError_t launch_hash_route(const RouteCfg& c, int32_t dtype,
                              const int32_t* token_ids, const int32_t* tid2eid,
                              int32_t vocab, const void* x, const void* W,
-                             const float* logit_bias, int32_t* ids,
-                             float* weights, int32_t* dev_err,
-                             hipStream_t stream);
+                             const float* logit_bias, const float* logits, int32_t splits,
+                             int64_t split_stride, int32_t* ids, float* weights,
+                             int32_t* dev_err, hipStream_t stream);
 
 // Dispatch placement from per-tile histograms already in tile_hist
 // ([ceil(R / tile_routes)][E], tile-major), when dispatch_hist_ok.

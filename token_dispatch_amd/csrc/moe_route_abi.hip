@@ -320,7 +320,8 @@ size_t moe_route_workspace_size(const moe_route_params* p) {
 int32_t moe_route_hash(const moe_route_params* p, const int32_t* token_ids,
                        const int32_t* tid2eid, int32_t vocab, const void* x,
                        const void* W, const float* logit_bias, int32_t* ids,
-                       float* weights, int32_t* dev_err, void* stream) {
+                       float* weights, void* workspace, size_t workspace_bytes,
+                       int32_t* dev_err, void* stream) {
   const bool ids_only = (x == nullptr && W == nullptr);
   int32_t rc = check_common(p, !ids_only);
   if (rc != MOE_OK) return rc;
@@ -337,11 +338,37 @@ int32_t moe_route_hash(const moe_route_params* p, const int32_t* token_ids,
     if (!ids_only && !weights) return fail(MOE_EINVAL, "weights are required with x and W");
   }
   if (p->T == 0) return MOE_OK;
-  hipError_t e = moe::launch_hash_route(to_cfg(p), p->dtype, token_ids, tid2eid, vocab, x, W,
-                                        logit_bias, ids, weights, dev_err,
-                                        static_cast<hipStream_t>(stream));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  // logits of every expert from the tiled gate contraction when the
+  // workspace holds them, else k dot products per token in the hash kernel
+  float* lg = nullptr;
+  int32_t splits = 1;
+  if (!ids_only && workspace) {
+    const bool aligned = reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
+                         reinterpret_cast<uintptr_t>(W) % 16 == 0;
+    const size_t te = (size_t)p->T * p->E * sizeof(float);
+    moe::GatePlan g = moe::plan_gate(p->T, p->d, p->E, p->dtype, aligned, true);
+    if (workspace_bytes < te * g.splits)
+      g = moe::plan_gate(p->T, p->d, p->E, p->dtype, aligned, false);
+    if (workspace_bytes >= te * g.splits) {
+      lg = static_cast<float*>(workspace);
+      splits = g.splits;
+      e = moe::launch_gate_gemm(g, p->dtype, x, W, logit_bias, lg, p->T, p->d, p->E, s);
+      if (e != hipSuccess) return device_fail(e, "gate GEMM launch");
+    }
+  }
+  e = moe::launch_hash_route(to_cfg(p), p->dtype, token_ids, tid2eid, vocab, x, W, logit_bias,
+                             lg, splits, (int64_t)p->T * p->E, ids, ids_only ? nullptr : weights,
+                             dev_err, s);
   if (e != hipSuccess) return device_fail(e, "hash route launch");
   return MOE_OK;
+}
+
+size_t moe_route_hash_workspace_size(const moe_route_params* p) {
+  if (check_common(p, true) != MOE_OK || p->T == 0) return 0;
+  if ((int64_t)p->T * p->E > kI32Max) return 0;
+  return route_ws_bytes(p);
 }
 
 size_t moe_dispatch_workspace_size(int32_t T, int32_t k_stride, int32_t E) {
