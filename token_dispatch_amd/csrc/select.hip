@@ -26,6 +26,8 @@
 // two largest) come from a butterfly over the group's lanes when a group is
 // a power-of-two run of whole lanes, else from one segment reduction per
 // group.
+#include <cstdlib>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -520,6 +522,24 @@ void select_shape(const RouteCfg& c, int* lpt, int* vpl) {
     l = 16, v = 24;
   } else {
     v = E <= 64 ? 1 : E <= 128 ? 2 : E <= 256 ? 4 : E <= 512 ? 8 : 16;
+  }
+  // MOE_SELECT_LPT=4|8|16|64 forces the segment width (tuning sweeps)
+  if (const char* env = std::getenv("MOE_SELECT_LPT")) {
+    const int want = std::atoi(env);
+    const int vw = (E + want - 1) / want;
+    if (want == 64 && vw <= 16) {
+      l = 64;
+      v = vw <= 1 ? 1 : vw <= 2 ? 2 : vw <= 4 ? 4 : vw <= 8 ? 8 : 16;
+    } else if (want == 16 && G <= 16 && vw <= 24) {
+      l = 16;
+      v = vw <= 1 ? 1 : vw <= 2 ? 2 : vw <= 4 ? 4 : vw <= 8 ? 8 : vw <= 16 ? 16 : 24;
+    } else if (want == 8 && G <= 8 && vw <= 16) {
+      l = 8;
+      v = vw <= 8 ? 8 : 16;
+    } else if (want == 4 && G <= 4 && vw <= 8) {
+      l = 4;
+      v = vw <= 4 ? 4 : 8;
+    }
   }
   *lpt = l;
   *vpl = v;
