@@ -191,9 +191,12 @@ def test_route_dispatch_workspace_size():
         n = tda.route_dispatch_workspace_size(T, d, E, k)
         disp = tda.dispatch_workspace_size(T, k, E)
         assert n >= route and (n == route + disp or (n - route) % (4 * E) == 0), (T, n)
-    # Qwen3-like shape: 16-token tiles of 256 routes -> 256 histogram rows
+    # Qwen3-like shape: the gate hand-off holds whole T x E partial arrays
+    # (one per K split); then 16-token tiles of 256 routes -> 256 histogram rows
+    route = tda.route_workspace_size(4096, 2048, 128, 16)
+    assert route % (4096 * 128 * 4) == 0 and 1 <= route // (4096 * 128 * 4) <= 8
     assert tda.route_dispatch_workspace_size(4096, 2048, 128, 16) == \
-        (4096 * 128 * 4 + 255) // 256 * 256 + 256 * 128 * 4
+        (route + 255) // 256 * 256 + 256 * 128 * 4
 
 
 def test_route_dispatch_validation():

@@ -291,27 +291,31 @@ def test_gate_stage_lengths_exact(rb, tile, d, monkeypatch):
     np.testing.assert_array_equal(down(logits), exp)
 
 
-@pytest.mark.parametrize("tile,rb", [("256x256w8", "128"), ("256x192w8", "128"),
-                                     ("128x384w8", "128"), ("256x128w8", "128"),
-                                     ("128x256w8", "128"), ("128x192w8", "128"),
-                                     ("128x128w8", "128"), ("32x64w8", "256"),
-                                     ("32x64w8", "512"), ("64x64w8", "128"),
-                                     ("64x64w8", "256"), ("32x128w8", "256"),
-                                     ("32x128w8", "512")])
+@pytest.mark.parametrize("tile,rb,ns", [
+    ("256x256w8", "128", "2"), ("256x192w8", "128", "2"), ("128x384w8", "128", "2"),
+    ("256x128w8", "128", "3"), ("128x256w8", "128", "3"), ("128x192w8", "128", "3"),
+    ("128x128w8", "128", "4"), ("32x64w8", "256", "3"), ("32x64w8", "512", "2"),
+    ("64x64w8", "128", "4"), ("64x64w8", "256", "3"), ("32x128w8", "256", "3"),
+    ("32x128w8", "512", "2"), ("32x128w8", "128", "3"), ("128x192w8", "256", "2"),
+    # 64-byte stages, deep rings; some split their load blocks unevenly
+    ("128x192w8", "64", "5"), ("128x192w8", "64", "8"), ("256x192w8", "64", "4"),
+    ("128x384w8", "64", "5"), ("256x256w8", "64", "3"), ("256x128w8", "64", "6"),
+    ("64x64w8", "64", "7"), ("128x128w8", "64", "2")])
 @pytest.mark.parametrize("splits", ["1", "2"])
-def test_gate_eight_wave_tiles_exact(tile, rb, splits, monkeypatch):
-    """Eight-wavefront tiles (4 x 2 or 2 x 4 waves) at each stage length they
-    take: ragged T, E and d, integer bf16 inputs, logits equal to the integer
-    product."""
+def test_gate_eight_wave_tiles_exact(tile, rb, ns, splits, monkeypatch):
+    """Eight-wavefront tiles (4 x 2 or 2 x 4 waves) at each stage length and
+    ring depth they take: ragged T, E and d, integer bf16 inputs, logits
+    equal to the integer product."""
     monkeypatch.setenv("MOE_GATE_TILE", tile)
     monkeypatch.setenv("MOE_GATE_SPLITS", splits)
     monkeypatch.setenv("MOE_GATE_RB", rb)
-    rng = np.random.default_rng([len(tile), int(splits)])
+    monkeypatch.setenv("MOE_GATE_NS", ns)
+    rng = np.random.default_rng([len(tile), int(splits), int(rb), int(ns)])
     T, E, d = 777, 420, 1480
     x = rng.integers(-3, 4, size=(T, d)).astype(np.float32)
     Wi = rng.integers(-3, 4, size=(E, d)).astype(np.float32)
     exp = (x.astype(np.int64) @ Wi.astype(np.int64).T).astype(np.float32)
-    say("gate 8-wave", tile, rb, splits)
+    say("gate 8-wave", tile, rb, ns, splits)
     _, _, logits = tda.route(up(wl.f32_to_bf16_bits(x)), up(wl.f32_to_bf16_bits(Wi)), 4,
                              return_logits=True)
     np.testing.assert_array_equal(down(logits), exp)

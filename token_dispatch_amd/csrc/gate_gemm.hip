@@ -22,6 +22,7 @@
 #include <algorithm>
 #include <cstdio>
 #include <cstdlib>
+#include <type_traits>
 
 #include "device_common.h"
 #include "kernels.h"
@@ -34,6 +35,9 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
+#ifndef MOE_GATE_NT
+#define MOE_GATE_NT 1
+#endif
 constexpr int kXcds = 8;
 
 template <typename In>
@@ -208,20 +212,21 @@ __global__ __launch_bounds__(kThreads) void gate_gemm_kernel(
 // Deep pipeline for 16-byte aligned rows (the common case): global -> LDS
 // copies with buffer_load ... lds, an NS-stage ring, NS-1 stages in flight
 // while one is multiplied.  A stage holds RB bytes of K of every tile row:
-// 128, 256 or 512.  Longer row segments keep more of each DRAM page per
-// request when x streams from HBM (measured: a cold 16.8 MB x read in 128-B
-// row pieces runs at half the rate of 512-B pieces) and give each barrier
-// RB / 64 matrix-core k-steps of work.
+// 64, 128, 256 or 512.  Longer row segments give each barrier RB / 64
+// matrix-core k-steps of work; shorter ones let large tiles keep a deep ring
+// (x streams from HBM at about 3 TB/s with 8 KB in flight per CU and at
+// about 5.9 TB/s from 32 KB on).
 //
 // LDS layout of a stage: the tile's BM x rows then BN W rows, RB bytes each,
-// no padding; the 16-byte chunk c of row r sits in slot c ^ (r % 8), so the
-// rows an MFMA operand read touches spread over the banks.  One load
-// instruction of a wave fills 1 KB = 1024 / RB rows: lane l writes slot
-// l % (RB / 16) of row l / (RB / 16) (the hardware places lane data
-// contiguously), so it fetches chunk slot ^ (row % 8) of that row.  Rows past
-// T or E, chunks past the end of a row (d need not fill the last stage) and
-// the unused stages after the last one read past the buffer descriptor's
-// range and load zeros without touching memory.
+// no padding; the 16-byte chunk c of row r sits in slot c ^ swz(r), so the
+// eight rows one ds_read_b128 pass touches cover all banks: swz(r) = r % 8
+// for rows of 128 bytes or more, (r / 2) % 4 for 64-byte rows (two rows per
+// bank sweep).  One load instruction of a wave fills 1 KB = 1024 / RB rows:
+// lane l writes slot l % (RB / 16) of row l / (RB / 16) (the hardware places
+// lane data contiguously), so it fetches chunk slot ^ swz(row) of that row.
+// Rows past T or E, chunks past the end of a row (d need not fill the last
+// stage) and the unused stages after the last one read past the buffer
+// descriptor's range and load zeros without touching memory.
 // gfx9 s_waitcnt immediate: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] |
 // vmcnt[5:4] << 14.
 template <int VM, int LGKM>
@@ -242,6 +247,22 @@ __device__ __forceinline__ void stage_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
+template <int RB>
+__device__ __forceinline__ int stage_swizzle(int row) {
+  return RB >= 128 ? (row & 7) : ((row >> 1) & 3);
+}
+
+template <typename In>
+struct Frag;
+template <>
+struct Frag<uint16_t> {
+  typedef bf16x8_t type;
+};
+template <>
+struct Frag<float> {
+  typedef f32x4_t type;
+};
+
 template <typename In, int BM, int BN, int NS, int RB, int WM, int WN>
 __global__ __launch_bounds__(WM * WN * kWave) void gate_gemm_pipe_kernel(
     const In* __restrict__ x, const In* __restrict__ W, const float* __restrict__ logit_bias,
@@ -252,14 +273,16 @@ __global__ __launch_bounds__(WM * WN * kWave) void gate_gemm_pipe_kernel(
   constexpr int RPI = 1024 / RB;               // rows per load instruction
   constexpr int CPR = RB / 16;                 // 16-byte chunks per row and stage
   constexpr int NW = WM * WN;                  // waves: WM along M x WN along N
-  constexpr int LPS = ROWS / RPI / NW;         // load instructions per wave per stage
+  constexpr int BLOCKS = ROWS / RPI;           // load instructions per stage
+  constexpr int LPS = (BLOCKS + NW - 1) / NW;  // ... per wave (the last one by some waves)
+  constexpr int LPS_SHORT = BLOCKS / NW;       // ... per wave without the last one
   constexpr int KSTEPS = RB / 64;              // 64-byte matrix-core k-steps per stage
   constexpr int MB = BM / WM / 16;             // 16-row blocks per wave
   constexpr int NB = BN / WN / 16;             // 16-column blocks per wave
-  static_assert(RB == 128 || RB == 256 || RB == 512, "stage row bytes");
-  static_assert(BM % (16 * WM) == 0 && BN % (16 * WN) == 0 && (ROWS / RPI) % NW == 0,
-                "tile shape");
+  static_assert(RB == 64 || RB == 128 || RB == 256 || RB == 512, "stage row bytes");
+  static_assert(BM % (16 * WM) == 0 && BN % (16 * WN) == 0 && ROWS % RPI == 0, "tile shape");
   static_assert(NS >= 2 && (NS - 2) * LPS < 64, "pipeline depth");
+  typedef typename Frag<In>::type FragT;
 
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * STAGE];
 
@@ -280,6 +303,8 @@ __global__ __launch_bounds__(WM * WN * kWave) void gate_gemm_pipe_kernel(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
+  // waves that own a copy in the last, partial round of a stage's blocks
+  const bool full = LPS == LPS_SHORT || wave + NW * (LPS - 1) < BLOCKS;
 
   const uint32_t row_bytes = (uint32_t)d * sizeof(In);
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
@@ -298,8 +323,8 @@ __global__ __launch_bounds__(WM * WN * kWave) void gate_gemm_pipe_kernel(
 #pragma unroll
   for (int i = 0; i < LPS; ++i) {
     const int blk = wave + NW * i;             // RPI-row block of the tile
-    const int r = blk * RPI + lane / CPR;      // tile row
-    const int chunk = (lane % CPR) ^ (r & 7);
+    const int r = blk * RPI + lane / CPR;      // tile row (past ROWS: no such copy)
+    const int chunk = (lane % CPR) ^ stage_swizzle<RB>(r);
     src_is_x[i] = r < BM;
     const uint32_t grow = src_is_x[i] ? (uint32_t)(m0 + r) : (uint32_t)(n0 + r - BM);
     const uint32_t nrows = src_is_x[i] ? (uint32_t)T : (uint32_t)E;
@@ -312,6 +337,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void gate_gemm_pipe_kernel(
     const uint32_t koff = st < st_end ? (uint32_t)st * RB : 0x80000000u;
 #pragma unroll
     for (int i = 0; i < LPS; ++i) {
+      if (i == LPS - 1 && !full) break;  // wave-uniform
       auto* dst = (__attribute__((address_space(3))) void*)(buf + (wave + NW * i) * 1024);
       const bool live = (src_off[i] | koff) < 0x80000000u && koff + chunk_b[i] < row_bytes;
       const uint32_t off = live ? src_off[i] + koff : 0x80000000u;
@@ -320,6 +346,13 @@ __global__ __launch_bounds__(WM * WN * kWave) void gate_gemm_pipe_kernel(
       else
         __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, dst, 16, off, 0, 0, 0);
     }
+  };
+  // each wave waits for its own copies: NS - 2 later stages may stay in flight
+  auto barrier = [&]() {
+    if (full)
+      stage_barrier<(NS - 2) * LPS>();
+    else
+      stage_barrier<(NS - 2) * LPS_SHORT>();
   };
 
   f32x4_t acc[MB][NB];
@@ -330,67 +363,151 @@ __global__ __launch_bounds__(WM * WN * kWave) void gate_gemm_pipe_kernel(
 
   const int row16 = lane & 15;
   const int kq = lane >> 4;
-  const int sw = row16 & 7;  // row % 8 of every row this lane reads
+  const int sw = stage_swizzle<RB>(row16);  // swz of every row this lane reads
   const int a_row = wm * (BM / WM) + row16;
   const int b_row = BM + wn * (BN / WN) + row16;
 
-  auto compute = [&](const uint8_t* buf) {
+  // Operand fragments of one k-step, double-buffered so that the LDS reads
+  // of the next k-step are in flight while this one's MFMAs run.
+  FragT fa[2][MB], fb[2][NB];
+  auto load = [&](int p, const uint8_t* buf, int ks) {
+    const int slot = ((ks * 4 + kq) ^ sw) * 16;
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      const int slot = ((ks * 4 + kq) ^ sw) * 16;
-      if constexpr (sizeof(In) == 2) {
-        bf16x8_t af[MB], bfr[NB];
+    for (int i = 0; i < MB; ++i)
+      fa[p][i] = *reinterpret_cast<const FragT*>(buf + (a_row + i * 16) * RB + slot);
 #pragma unroll
-        for (int i = 0; i < MB; ++i)
-          af[i] = *reinterpret_cast<const bf16x8_t*>(buf + (a_row + i * 16) * RB + slot);
+    for (int j = 0; j < NB; ++j)
+      fb[p][j] = *reinterpret_cast<const FragT*>(buf + (b_row + j * 16) * RB + slot);
+  };
+  auto mma = [&](int p) {
+    if constexpr (sizeof(In) == 2) {
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
 #pragma unroll
         for (int j = 0; j < NB; ++j)
-          bfr[j] = *reinterpret_cast<const bf16x8_t*>(buf + (b_row + j * 16) * RB + slot);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[p][i], fb[p][j], acc[i][j], 0, 0, 0);
+    } else {
+      // a 16-wide K step as four K=4 MFMAs.  A and B use the same
+      // permutation of K: MFMA s takes element kq*4 + s of the step, so each
+      // lane reads one float4 per operand and the sum is unchanged.
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
         for (int i = 0; i < MB; ++i)
 #pragma unroll
           for (int j = 0; j < NB; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-      } else {
-        f32x4_t af[MB], bfr[NB];
-#pragma unroll
-        for (int i = 0; i < MB; ++i)
-          af[i] = *reinterpret_cast<const f32x4_t*>(buf + (a_row + i * 16) * RB + slot);
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-          bfr[j] = *reinterpret_cast<const f32x4_t*>(buf + (b_row + j * 16) * RB + slot);
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-          for (int i = 0; i < MB; ++i)
-#pragma unroll
-            for (int j = 0; j < NB; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i][s], bfr[j][s], acc[i][j], 0, 0, 0);
-      }
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[p][i][s4], fb[p][j][s4], acc[i][j],
+                                                              0, 0, 0);
     }
   };
 
+  // One stage; P0: the fragment buffer its first k-step reads (a constant,
+  // so the fragment arrays stay in registers).
+  auto run_stage = [&](int s, auto p0) {
+    constexpr int P0 = decltype(p0)::value;
+    const uint8_t* buf = lds + ((s - st_begin) % NS) * STAGE;
 #pragma unroll
-  for (int st = 0; st < NS - 1; ++st) issue(st_begin + st);
-  for (int s = st_begin; s < st_end; ++s) {
-    stage_barrier<(NS - 2) * LPS>();  // stage s is in LDS; stage s-1 is consumed
-    issue(s + NS - 1);                // refill the buffer stage s-1 used
-    compute(lds + ((s - st_begin) % NS) * STAGE);
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const int p = (P0 + ks) & 1;
+      if (ks + 1 < KSTEPS) {
+        load(p ^ 1, buf, ks + 1);
+      } else if (s + 1 < st_end) {
+        // stage s + 1 is in LDS and every wave has read all of stage s (this
+        // wave's last reads included): refill stage s's buffer, then read the
+        // next stage's first k-step behind this one's MFMAs
+        barrier();
+        issue(s + NS);
+        load(p ^ 1, lds + ((s + 1 - st_begin) % NS) * STAGE, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mma(p);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  if (st_begin < st_end) {
+#pragma unroll
+    for (int st = 0; st < NS - 1; ++st) issue(st_begin + st);
+    barrier();                  // stage st_begin is in LDS
+    issue(st_begin + NS - 1);   // into the one buffer not yet used
+    load(0, lds, 0);
+    if constexpr (KSTEPS % 2 == 0) {
+      for (int s = st_begin; s < st_end; ++s) run_stage(s, std::integral_constant<int, 0>());
+    } else {  // one k-step per stage: the buffers alternate between stages
+      for (int s = st_begin; s < st_end; s += 2) {
+        run_stage(s, std::integral_constant<int, 0>());
+        if (s + 1 < st_end) run_stage(s + 1, std::integral_constant<int, 1>());
+      }
+    }
   }
   wait_counts<0, 15>();  // no copy may still target LDS when the workgroup ends
 
+  // Epilogue.  A 16 x 16 MFMA result gives a lane one column of four rows,
+  // so direct stores write 64-byte row pieces from scattered lanes (measured:
+  // about 1.5 TB/s for a 33.5 MB logits array).  Instead the tile goes
+  // through the ring, now free, and whole rows leave with 16-byte stores
+  // from consecutive lanes.  PITCH: padded LDS row, so the four lane groups
+  // of one accumulator write hit different banks.
+  constexpr int PITCH = BN + 4;                         // floats
+  constexpr int WROWS = BM / WM;                        // rows of one wave row
+  constexpr int G = NS * STAGE / (WROWS * PITCH * 4);   // wave rows per pass
+  if constexpr (G >= 1) {
+    constexpr int GP = G < WM ? G : WM;
+    constexpr int PASSES = (WM + GP - 1) / GP;
+    constexpr int C4 = BN / 4;  // float4 per tile row
+    float* lo = reinterpret_cast<float*>(lds);
+    const bool vec = E % 4 == 0 && reinterpret_cast<uintptr_t>(logits) % 16 == 0;
+    const bool bias = logit_bias != nullptr && split == 0;
 #pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    const int e = n0 + wn * (BN / WN) + j * 16 + row16;
-    if (e >= E) continue;
-    const float b = (logit_bias && split == 0) ? logit_bias[e] : 0.0f;
+    for (int p = 0; p < PASSES; ++p) {
+      __syncthreads();  // the ring (or the previous pass) is no longer read
+      if (wm / GP == p) {
+        const int rbase = (wm - p * GP) * WROWS;
 #pragma unroll
-    for (int i = 0; i < MB; ++i)
+        for (int i = 0; i < MB; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t t = (int64_t)m0 + wm * (BM / WM) + i * 16 + kq * 4 + r;
-        if (t < T) logits[t * E + e] = acc[i][j][r] + b;
+          for (int j = 0; j < NB; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              lo[(rbase + i * 16 + kq * 4 + r) * PITCH + wn * (BN / WN) + j * 16 + row16] =
+                  acc[i][j][r];
       }
+      __syncthreads();
+      const int prow0 = p * GP * WROWS;
+      const int prows = (WM - p * GP < GP ? WM - p * GP : GP) * WROWS;
+      for (int idx = tid; idx < prows * C4; idx += NW * kWave) {
+        const int rr = idx / C4, c4 = idx % C4;
+        const int64_t t = (int64_t)m0 + prow0 + rr;
+        const int e0 = n0 + c4 * 4;
+        if (t >= T || e0 >= E) continue;
+        f32x4_t v = *reinterpret_cast<const f32x4_t*>(lo + rr * PITCH + c4 * 4);
+        if (vec && e0 + 4 <= E) {
+          if (bias) v += f32x4_t{logit_bias[e0], logit_bias[e0 + 1], logit_bias[e0 + 2],
+                                 logit_bias[e0 + 3]};
+          if (MOE_GATE_NT)
+            __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(logits + t * E + e0));
+          else
+            *reinterpret_cast<f32x4_t*>(logits + t * E + e0) = v;
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (e0 + q < E) logits[t * E + e0 + q] = v[q] + (bias ? logit_bias[e0 + q] : 0.0f);
+        }
+      }
+    }
+  } else {  // the ring cannot hold one wave row of the tile: direct stores
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int e = n0 + wn * (BN / WN) + j * 16 + row16;
+      if (e >= E) continue;
+      const float b = (logit_bias && split == 0) ? logit_bias[e] : 0.0f;
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t t = (int64_t)m0 + wm * (BM / WM) + i * 16 + kq * 4 + r;
+          if (t < T) logits[t * E + e] = acc[i][j][r] + b;
+        }
+    }
   }
 }
 
@@ -452,9 +569,11 @@ constexpr int kMinTiles = 256;
 constexpr int kLdsBytes = 160 * 1024;
 constexpr int kLdsBudget = kLdsBytes - 8 * 1024;
 
-// `waves` is the tile's wave count (4: 2 x 2, 8: 4 x 2 or 2 x 4).
+// `waves` is the tile's wave count (4: 2 x 2, 8: 4 x 2 or 2 x 4); a wave
+// issues at most ceil(load blocks / waves) copies per stage.
 constexpr bool depth_ok(int bm, int bn, int ns, int rb, int waves = 4) {
-  return ns * (bm + bn) * rb <= kLdsBytes && (ns - 2) * ((bm + bn) * rb / 1024 / waves) < 64;
+  return ns * (bm + bn) * rb <= kLdsBytes &&
+         (ns - 2) * (((bm + bn) * rb / 1024 + waves - 1) / waves) < 64;
 }
 
 template <typename In, int BM, int BN, int NS, int RB, int WM, int WN>
@@ -465,9 +584,19 @@ hipError_t launch_depth(const void* x, const void* W, const float* lb, float* ou
   return hipErrorInvalidValue;
 }
 
+// Ring depths 2..4; 64-byte stages (the deep rings of large tiles) also 5..8.
 template <typename In, int BM, int BN, int RB, int WM, int WN>
 hipError_t launch_rb(const GatePlan& g, const void* x, const void* W, const float* lb,
                      float* out, int T, int d, int E, hipStream_t s) {
+  if constexpr (RB == 64) {
+    switch (g.ns) {
+      case 8: return launch_depth<In, BM, BN, 8, RB, WM, WN>(x, W, lb, out, T, d, E, g.splits, s);
+      case 7: return launch_depth<In, BM, BN, 7, RB, WM, WN>(x, W, lb, out, T, d, E, g.splits, s);
+      case 6: return launch_depth<In, BM, BN, 6, RB, WM, WN>(x, W, lb, out, T, d, E, g.splits, s);
+      case 5: return launch_depth<In, BM, BN, 5, RB, WM, WN>(x, W, lb, out, T, d, E, g.splits, s);
+      default: break;
+    }
+  }
   switch (g.ns) {
     case 4: return launch_depth<In, BM, BN, 4, RB, WM, WN>(x, W, lb, out, T, d, E, g.splits, s);
     case 3: return launch_depth<In, BM, BN, 3, RB, WM, WN>(x, W, lb, out, T, d, E, g.splits, s);
@@ -482,20 +611,16 @@ hipError_t launch_ns(const GatePlan& g, const void* x, const void* W, const floa
     if constexpr (WM == 2 && WN == 2) return launch_tile<In, BM, BN, KB>(x, W, lb, out, T, d, E, s);
     return hipErrorInvalidValue;  // 8-wave tiles are planned for the pipelined kernel only
   }
-  if constexpr (WM * WN == 8) {  // bf16 only; stages whose load blocks split over 8 waves
-    if constexpr (sizeof(In) == 2) {
-      if constexpr ((BM + BN) / 8 % 8 == 0)
-        if (g.rb == 128) return launch_rb<In, BM, BN, 128, WM, WN>(g, x, W, lb, out, T, d, E, s);
-      if constexpr ((BM + BN) / 4 % 8 == 0)
-        if (g.rb == 256) return launch_rb<In, BM, BN, 256, WM, WN>(g, x, W, lb, out, T, d, E, s);
-      if constexpr ((BM + BN) / 2 % 8 == 0)
-        if (g.rb == 512) return launch_rb<In, BM, BN, 512, WM, WN>(g, x, W, lb, out, T, d, E, s);
-    }
-    return hipErrorInvalidValue;
+  if constexpr (WM * WN == 8 && sizeof(In) != 2) {
+    return hipErrorInvalidValue;  // 8-wave tiles: bf16 only
   } else {
     switch (g.rb) {
       case 512: return launch_rb<In, BM, BN, 512, WM, WN>(g, x, W, lb, out, T, d, E, s);
       case 256: return launch_rb<In, BM, BN, 256, WM, WN>(g, x, W, lb, out, T, d, E, s);
+      case 64:
+        if constexpr (WM * WN == 8)
+          return launch_rb<In, BM, BN, 64, WM, WN>(g, x, W, lb, out, T, d, E, s);
+        return hipErrorInvalidValue;  // 64-byte stages: 8-wave tiles only
       default: return launch_rb<In, BM, BN, 128, WM, WN>(g, x, W, lb, out, T, d, E, s);
     }
   }
@@ -584,51 +709,84 @@ TileChoice choose_tile(int T, int E) {
   return fallback;
 }
 
-// Eight-wave tiles for large bf16 contractions (measured on the DeepSeek-V3,
-// DeepSeek-V4 and gpt-oss shapes: 17-30 % faster gates than four-wave
-// tiles).  The tile with the most useful outputs that still gives one
-// workgroup per CU (fewer padded columns on ties), else 128 x 128 with K
-// split in two when that gives at least 128 tiles over a K of >= 32
-// 128-byte pieces per split.  {0, 0} when neither applies.
-TileChoice choose_tile8(int T, int E, int64_t pieces, int* splits) {
+// Eight-wave tiles (two waves per SIMD) for bf16 contractions that fill the
+// chip: the tile and K split with the lowest estimated time.  Row pieces
+// re-read from L2 bound these kernels (measured: about 21 bytes per clock
+// per CU, 13 TB/s on the chip) unless x's single pass from HBM (about
+// 6 TB/s) takes longer; a K split cuts each workgroup's share of the rows
+// but writes one more T x E fp32 partial array, which the selection reads
+// back.  Candidates give one or two workgroups per CU and leave at least
+// eight 128-byte row pieces per split.  {0, 0}: none qualifies.
+TileChoice choose_tile8(int T, int d, int E, bool allow_split, int* splits) {
+  constexpr double kL2PerCu = 21.0 * 2.4e9;  // bytes/s
+  constexpr double kHbm = 6.0e12;            // bytes/s
+  constexpr int kCus = 256;
+  const double row = 2.0 * d;                // bf16 row bytes
+  const int64_t pieces = ((int64_t)d * 2 + 127) / 128;
   TileChoice best = {0, 0};
-  double best_work = -1.0, best_useful = 0.0;
+  double best_est = 0.0;
+  int best_nn = 0;
+  *splits = 1;
   for (const auto& t : kTiles) {
-    if (t.wm * t.wn != 8 || t.bm * t.bn < 128 * 128) continue;
+    if (t.wm * t.wn != 8) continue;
     const int n_n = (E + t.bn - 1) / t.bn;
-    const double useful = (double)E / (n_n * t.bn);
-    if (useful < 0.74) continue;
+    if ((double)E / (n_n * t.bn) < 0.74) continue;
     const long tiles = (long)((T + t.bm - 1) / t.bm) * n_n;
-    const double work = (double)t.bm * t.bn * useful;
-    if (tiles >= kMinTiles && (work > best_work || (work == best_work && useful > best_useful))) {
-      best = t;
-      best_work = work;
-      best_useful = useful;
+    for (int S = 1; S <= 8; S *= 2) {
+      if (S > 1 && !allow_split) break;
+      const long wgs = tiles * S;
+      if (wgs < kMinTiles || wgs > 2 * kCus || pieces / S < 8) continue;
+      const double per_cu = (double)((wgs + kCus - 1) / kCus) * (t.bm + t.bn) * row / S;
+      const double t_l2 = per_cu / kL2PerCu;
+      const double t_hbm = ((double)T * row + (double)E * row + (double)S * T * E * 4) / kHbm;
+      const double t_part = (double)(S - 1) * T * E * 4 / kHbm;
+      const double est = std::max(t_l2, t_hbm) + t_part;
+      // ties: fewer N tiles (whole rows of logits per workgroup)
+      if (best.bm == 0 || est < best_est * 0.999 ||
+          (est <= best_est * 1.001 && n_n < best_nn)) {
+        best = t;
+        best_est = est;
+        best_nn = n_n;
+        *splits = S;
+      }
     }
   }
-  *splits = 1;
-  if (best.bm > 0) return best;
-  const long t128 = (long)((T + 127) / 128) * ((E + 127) / 128);
-  if (E % 128 == 0 && t128 * 2 >= kMinTiles && pieces / 2 >= 32) {
-    *splits = 2;
-    return {128, 128, 2, 4, false};
-  }
-  return {0, 0};
+  return best;
 }
 
-// Stage length and ring depth of the pipelined kernel.  The kernel runs four
-// waves per workgroup and hides memory latency with its ring alone, so the
-// ring takes the LDS that the workgroups sharing a CU leave it (all of it at
-// one workgroup per CU, half at two): the longest row segment that still
-// keeps two stages in flight (NS >= 3), else the longest with NS = 2.
+// Stage length and ring depth of the pipelined kernel.  The ring hides
+// memory latency and takes the LDS that the workgroups sharing a CU leave it
+// (all of it at one workgroup per CU, half at two).  Four-wave tiles: the
+// longest row segment that still keeps two stages in flight (NS >= 3), else
+// the longest with NS = 2.  Eight-wave tiles: small ones 256-byte stages
+// three deep (measured on the Qwen3-like shape), large ones 128-byte stages
+// as deep as fits.
 void choose_ring(GatePlan& g, long wgs) {
-  const int budget = (wgs > kMinTiles ? kLdsBytes / 2 : kLdsBudget);
+  const int budget = (wgs > kMinTiles ? kLdsBytes / 2 : kLdsBytes);
   const int waves = g.wm * g.wn;
+  if (waves == 8) {
+    if (g.bm * g.bn < 128 * 128 && depth_ok(g.bm, g.bn, 3, 256, 8) &&
+        3 * (g.bm + g.bn) * 256 <= budget) {
+      g.rb = 256;
+      g.ns = 3;
+      return;
+    }
+    for (int ns : {4, 3, 2})
+      if (depth_ok(g.bm, g.bn, ns, 128, 8) && ns * (g.bm + g.bn) * 128 <= budget) {
+        g.rb = 128;
+        g.ns = ns;
+        return;
+      }
+    g.rb = 64;
+    g.ns = 2;
+    return;
+  }
+  const int budget4 = (wgs > kMinTiles ? kLdsBytes / 2 : kLdsBudget);
   for (int ns_min : {3, 2})
     for (int rb : {256, 128})
       for (int ns : {4, 3, 2})
-        if (ns >= ns_min && (waves == 4 || (rb == 128 && ns <= 3)) &&
-            depth_ok(g.bm, g.bn, ns, rb, waves) && ns * (g.bm + g.bn) * rb <= budget) {
+        if (ns >= ns_min && depth_ok(g.bm, g.bn, ns, rb, waves) &&
+            ns * (g.bm + g.bn) * rb <= budget4) {
           g.rb = rb;
           g.ns = ns;
           return;
@@ -660,9 +818,8 @@ GatePlan plan_gate(int32_t T, int32_t d, int32_t E, int32_t dtype, bool aligned,
   const int64_t pieces = ((int64_t)d * esz + 127) / 128;
   int splits8 = 1;
   const TileChoice c8 =
-      (g.pipe && dtype == 1) ? choose_tile8(T, E, pieces, &splits8) : TileChoice{0, 0};
-  bool twin8 = false;  // a small four-wave tile replaced by its eight-wave twin
-  if (c8.bm > 0 && (splits8 == 1 || allow_split)) {
+      (g.pipe && dtype == 1) ? choose_tile8(T, d, E, allow_split, &splits8) : TileChoice{0, 0};
+  if (c8.bm > 0) {
     g.bm = c8.bm;
     g.bn = c8.bn;
     g.wm = c8.wm;
@@ -675,7 +832,6 @@ GatePlan plan_gate(int32_t T, int32_t d, int32_t E, int32_t dtype, bool aligned,
       if (t.wm * t.wn == 8 && t.bm == g.bm && t.bn == g.bn) {
         g.wm = t.wm;
         g.wn = t.wn;
-        twin8 = true;
       }
   }
   if (c8.bm == 0 && g.pipe && allow_split) {
@@ -694,27 +850,22 @@ GatePlan plan_gate(int32_t T, int32_t d, int32_t E, int32_t dtype, bool aligned,
           g.bn = bn;
           g.wm = t.wm;
           g.wn = t.wn;
-          twin8 = false;
         }
   }
   if (const char* env = std::getenv("MOE_GATE_SPLITS"))
     if (g.pipe && allow_split) g.splits = std::max(1, std::min(8, std::atoi(env)));
   const long wgs = (long)((T + g.bm - 1) / g.bm) * ((E + g.bn - 1) / g.bn) * g.splits;
   choose_ring(g, wgs);
-  if (twin8) {  // 256-byte stages when their load blocks split over 8 waves, 3 deep
-    g.rb = (g.bm + g.bn) / 4 % 8 == 0 ? 256 : 128;
-    g.ns = 3;
-  }
   const int waves = g.wm * g.wn;
   if (const char* env = std::getenv("MOE_GATE_RB")) {
     const int rb = std::atoi(env);
-    if ((rb == 128 || rb == 256 || rb == 512) && depth_ok(g.bm, g.bn, 2, rb, waves) &&
-        (waves == 4 || (g.bm + g.bn) / (1024 / rb) % 8 == 0))
+    if ((rb == 128 || rb == 256 || rb == 512 || (rb == 64 && waves == 8)) &&
+        depth_ok(g.bm, g.bn, 2, rb, waves))
       g.rb = rb;
   }
   if (const char* env = std::getenv("MOE_GATE_NS")) {
     const int ns = std::atoi(env);
-    if (ns >= 2 && ns <= 4) g.ns = ns;
+    if (ns >= 2 && ns <= (g.rb == 64 ? 8 : 4)) g.ns = ns;
   }
   if (!depth_ok(g.bm, g.bn, g.ns, g.rb, waves)) g.ns = 2;
   return g;
