@@ -44,13 +44,20 @@ def assert_same(fused, sep):
         assert torch.equal(a, b), name
 
 
-@pytest.mark.parametrize("name,T", [("qwen3_dynk", None), ("qwen3_dynk", 4091),
-                                    ("qwen3_dynk", 33), ("mixtral", None),
-                                    ("gptoss_skew", 3000), ("dsv3_grouped", 700)])
-def test_route_dispatch_matches_separate_calls_and_oracle(name, T):
+@pytest.mark.parametrize("name,T,lpt", [("qwen3_dynk", None, None), ("qwen3_dynk", 4091, None),
+                                        ("qwen3_dynk", 33, None), ("qwen3_dynk", None, "64"),
+                                        ("qwen3_dynk", 4091, "64"), ("qwen3_dynk", 4091, "16"),
+                                        ("mixtral", None, None), ("gptoss_skew", 3000, None),
+                                        ("dsv3_grouped", 700, None)])
+def test_route_dispatch_matches_separate_calls_and_oracle(name, T, lpt, monkeypatch):
+    """The fused call (selection-written dispatch histograms where the shape
+    allows) against separate moe_route + moe_dispatch calls and the oracle;
+    lpt: a forced selection segment width (16-wave workgroups at 64)."""
+    if lpt:
+        monkeypatch.setenv("MOE_SELECT_LPT", lpt)
     w = wl.WORKLOADS[name]
     inp = wl.make_inputs(w, T=T)
-    say("route_dispatch", name, inp["x"].shape[0])
+    say("route_dispatch", name, inp["x"].shape[0], lpt)
     kw = route_kwargs(w)
     if kw["group_score"] is None:
         kw.pop("group_score")

@@ -441,6 +441,11 @@ __global__ __launch_bounds__(WPB * kWave) void select_kernel(
   }
 }
 
+// Waves of a workgroup that also counts its picks for the dispatch: 4, or
+// 16 for one-token wavefronts (16 tokens, so that 16 tokens x k routes make
+// a whole dispatch tile at k = 16).
+constexpr int hist_waves(int lpt) { return lpt == kWave ? 16 : 4; }
+
 template <int LPT, int VPL, int NS, bool MONO>
 hipError_t launch_vpl(const RouteCfg& c, const float* logits, int64_t stride, float* logits_out,
                       const float* logit_bias, const float* select_bias,
@@ -448,11 +453,15 @@ hipError_t launch_vpl(const RouteCfg& c, const float* logits, int64_t stride, fl
                       int vec, int32_t* hist, hipStream_t s) {
   constexpr int tpb = 4 * (kWave / LPT);
   const int64_t blocks = ((int64_t)c.T + tpb - 1) / tpb;
-  if constexpr (LPT <= 16 && LPT * VPL <= kHistMaxE) {
-    if (hist)  // one dispatch tile per workgroup
-      return launch(kStageSelect, select_kernel<LPT, VPL, NS, MONO, 4, true>,
-                    dim3((uint32_t)blocks), dim3(4 * kWave), s, c, logits, stride, logits_out,
+  if constexpr (LPT * VPL <= kHistMaxE) {
+    if (hist) {  // one dispatch tile per workgroup: hist_waves(LPT) waves
+      constexpr int HW = hist_waves(LPT);
+      constexpr int htpb = HW * (kWave / LPT);
+      const int64_t hblocks = ((int64_t)c.T + htpb - 1) / htpb;
+      return launch(kStageSelect, select_kernel<LPT, VPL, NS, MONO, HW, true>,
+                    dim3((uint32_t)hblocks), dim3(HW * kWave), s, c, logits, stride, logits_out,
                     logit_bias, select_bias, k_per_token, ids, weights, dev_err, vec, hist);
+    }
   }
   if (hist) return hipErrorInvalidValue;
   return launch(kStageSelect, select_kernel<LPT, VPL, NS, MONO, 4, false>, dim3((uint32_t)blocks),
@@ -550,8 +559,8 @@ void select_shape(const RouteCfg& c, int* lpt, int* vpl) {
 int select_hist_tokens(const RouteCfg& c) {
   int lpt, vpl;
   select_shape(c, &lpt, &vpl);
-  if (lpt > 16 || lpt * vpl > kHistMaxE) return 0;
-  return 4 * (kWave / lpt);
+  if (lpt * vpl > kHistMaxE) return 0;
+  return hist_waves(lpt) * (kWave / lpt);
 }
 
 hipError_t launch_select(const RouteCfg& c, const float* logits, int32_t splits,
