@@ -47,6 +47,9 @@ def stage_bytes(w, T, R, R_valid, tile_bytes):
     E, d, k = w.E, w.d, w.k
     return {
         "gate": T * d * xb + E * d * xb + T * E * 4,
+        # the gate kernel with the selection fused: no logits leave the chip
+        "gate_select": T * d * xb + E * d * xb + T * k * 8 + (T * 4 if w.dynamic_k else 0)
+        + tile_bytes,
         "hash": T * 4 + T * k * 4 + T * d * xb + E * d * xb + T * k * 8,
         "select": T * E * 4 + T * k * 8 + (T * 4 if w.dynamic_k else 0),
         "disp_hist": R * 4 + tile_bytes,
@@ -282,12 +285,13 @@ def main():
     achieved = sbytes[dom] / (dom_us * 1e-6) / 1e9
     traffic = measured_traffic(args.traffic, w.name, dom)
     gate_flops = 2.0 * T * w.d * E
+    gs = "gate_select" if "gate_select" in stages else ("gate" if "gate" in stages else None)
     maxvio = float(counts.max().item()) / (R_valid / E) - 1.0 if R_valid else 0.0
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic,
-                "gate_mfma_frac": round(gate_flops / (stages["gate"]["avg_us"] * 1e-6) / 1e12
-                                        / MFMA_BF16_PEAK_TFLOPS, 4) if "gate" in stages else None}
+                "gate_mfma_frac": round(gate_flops / (stages[gs]["avg_us"] * 1e-6) / 1e12
+                                        / MFMA_BF16_PEAK_TFLOPS, 4) if gs else None}
     for s, v in stages.items():
         log(f"[bench] {s:13s} {v['avg_us']:9.2f} us  {v['GBs']} GB/s")
 

@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 /* return codes */
 #define MOE_OK 0
@@ -245,7 +245,8 @@ size_t moe_route_dispatch_workspace_size(const moe_route_params* p);
 #define MOE_STAGE_DISP_HIST 3    /* dispatch: tile histograms */
 #define MOE_STAGE_DISP_SCAN 4    /* dispatch: scans */
 #define MOE_STAGE_DISP_SCATTER 5 /* dispatch: permutation */
-#define MOE_NUM_STAGES 6
+#define MOE_STAGE_GATE_SELECT 6  /* gate contraction with the selection fused */
+#define MOE_NUM_STAGES 7
 int32_t moe_profile_enable(int32_t enable);
 int32_t moe_profile_read(double* ms, int64_t* launches, int32_t n);
 

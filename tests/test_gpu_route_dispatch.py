@@ -101,3 +101,63 @@ def test_route_dispatch_empty():
     torch.cuda.synchronize()
     assert ids.shape == (0, 2)
     assert np.all(down(counts) == 0) and np.all(down(offsets) == 0)
+
+
+
+@pytest.mark.parametrize("T,E,tile,ns,score,bias_groups,dynk", [
+    (2000, 128, "256x128w8", "3", "softmax_topk", False, False),   # 16 lanes x 8, monotone
+    (2000, 128, "256x128w8", "3", "sigmoid", True, True),          # biased, grouped, per-token k
+    (1777, 124, "128x128w8", "4", "softmax", False, True),         # ragged T and E, padded tile
+    (16500, 128, "256x128w8", "3", "sqrt_softplus", True, False),  # 8 lanes x 16
+    (16500, 128, "128x128w8", "4", "softmax", False, True),
+])
+def test_fused_gate_select_matches_separate_kernels(T, E, tile, ns, score, bias_groups, dynk,
+                                                    monkeypatch):
+    """The gate kernel with the selection in its epilogue (whole-row tiles, no
+    K split) against the gate kernel followed by the select kernel on the
+    same plan: ids, weights, logits and the dispatch bit for bit; and the
+    oracle."""
+    monkeypatch.setenv("MOE_GATE_TILE", tile)
+    monkeypatch.setenv("MOE_GATE_SPLITS", "1")
+    monkeypatch.setenv("MOE_GATE_RB", "128")
+    monkeypatch.setenv("MOE_GATE_NS", ns)
+    rng = np.random.default_rng([T, E])
+    d, k = 1024, (8 if dynk else 4)
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    Wf = (rng.standard_normal((E, d)) / np.sqrt(d)).astype(np.float32)
+    xb, Wb = wl.f32_to_bf16_bits(x), wl.f32_to_bf16_bits(Wf)
+    lb = (0.1 * rng.standard_normal(E)).astype(np.float32)
+    sb = (0.01 * rng.standard_normal(E)).astype(np.float32) if bias_groups else None
+    kpt = rng.choice([2, 4, 8], size=T).astype(np.int32) if dynk else None
+    rkw = dict(score=score, select_bias=sb, k_per_token=kpt,
+               n_groups=4 if bias_groups else 1, topk_groups=2 if bias_groups else None,
+               group_score="top2_sum" if bias_groups else None, renormalize=True,
+               route_scale=2.5 if bias_groups else 1.0)
+    kw = {key: (up(v) if isinstance(v, np.ndarray) else v) for key, v in rkw.items()
+          if v is not None}
+    kw["logit_bias"] = up(lb)
+    say("fused gate+select", T, E, tile, score, bias_groups, dynk)
+    outs = []
+    for fused in (True, False):
+        if fused:
+            monkeypatch.delenv("MOE_NO_FUSED_SELECT", raising=False)
+        else:
+            monkeypatch.setenv("MOE_NO_FUSED_SELECT", "1")
+        tda.profile_enable(True)
+        lg = torch.empty((T, E), dtype=torch.float32, device=DEV)
+        r = tda.route_dispatch(up(xb), up(Wb), k, logits=lg, **kw)
+        ids2, w2 = tda.route(up(xb), up(Wb), k, **kw)
+        torch.cuda.synchronize()
+        prof = tda.profile_read()
+        tda.profile_enable(False)
+        staged = (prof["gate_select"][1], prof["select"][1])
+        assert staged == ((2, 0) if fused else (0, 2)), staged
+        assert torch.equal(r[0], ids2) and torch.equal(r[1], w2)
+        outs.append(tuple(r) + (lg,))
+    assert_same(outs[0][:6], outs[1][:6])
+    assert torch.equal(outs[0][6], outs[1][6]), "logits"
+    ref = oracle_route(oracle, oracle.gate(xb, Wb, lb), k, **rkw)
+    check_route(down(outs[0][0]), down(outs[0][1]), ref, oracle, score=score, renormalize=True,
+                route_scale=rkw["route_scale"], k_per_token=kpt, n_groups=rkw["n_groups"],
+                topk_groups=rkw["topk_groups"], where="fused gate+select")
+    check_dispatch(tuple(outs[0][2:6]), oracle.dispatch(down(outs[0][0]), E))

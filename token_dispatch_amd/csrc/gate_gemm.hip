@@ -26,6 +26,7 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "select_core.h"
 
 namespace moe {
 namespace {
@@ -263,11 +264,81 @@ struct Frag<float> {
   typedef f32x4_t type;
 };
 
-template <typename In, int BM, int BN, int NS, int RB, int WM, int WN>
+// The fused selection: the tile's BM rows of logits (+ logit bias) are in
+// LDS (lo, PITCH floats per row, all of E); the workgroup's NW wavefronts
+// route NW * 64 / LPT tokens per pass with the select kernel's per-token
+// code, and with HIST count their picks into the tile's dispatch histogram
+// (row mt: the tile's BM tokens x k routes form one dispatch tile).
+// `pick` ([NW * 64 / LPT][kMaxK]) and `whist` ([NW][kFusedMaxE]) are LDS
+// scratch carved from the ring behind the tile's rows.
+constexpr int kFusedMaxE = 128;  // experts of the fused selection
+
+template <class EPI, int BM, int NW, int PITCH>
+__device__ __forceinline__ void fused_select(const float* lo, int32_t (*pick)[sel::kMaxK],
+                                             int32_t (*whist)[kFusedMaxE], int m0, int T,
+                                             int lane, int wave, int mt, const SelectArgs& sa) {
+  constexpr int LPT = EPI::kLpt, VPL = EPI::kVpl;
+  constexpr int TPW = kWave / LPT;  // tokens per wavefront and pass
+  constexpr int TPP = NW * TPW;     // tokens per pass
+  constexpr int KPL = (sel::kMaxK + LPT - 1) / LPT;
+  static_assert(BM % TPP == 0, "passes");
+  const int E = sa.c.E;
+  const int seg = lane / LPT, sl = lane % LPT;
+  const int e0 = sl * VPL;
+  const int nval = min(max(E - e0, 0), VPL);
+  const bool lvec = sa.vec && nval == VPL;
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  if constexpr (EPI::kHist)
+    for (int e = lane; e < E; e += kWave) whist[wave][e] = 0;
+  for (int ps = 0; ps < BM / TPP; ++ps) {
+    const int tw = ps * TPP + wave * TPW;  // the wavefront's first tile row
+    if (m0 + tw >= T) break;              // wave-uniform
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();      // pick rows (and histogram) reused
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int tb = tw + seg;
+    const int64_t t = (int64_t)m0 + tb;
+    const bool tok_ok = t < T;
+    const int64_t trow = tok_ok ? t : (int64_t)m0 + tw;
+    const float* row = lo + tb * PITCH;
+    float lv[VPL];
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) lv[j] = (tok_ok && j < nval) ? row[e0 + j] : -INFINITY;
+    int pid[KPL];
+    sel::select_token<LPT, VPL, EPI::kMono>(sa.c, sl, seg, tok_ok, t, trow, lv, nval, lvec, row,
+                                            pick[wave * TPW + seg], sa.select_bias,
+                                            sa.k_per_token, sa.ids, sa.weights, sa.dev_err, pid);
+    if constexpr (EPI::kHist) sel::count_picks<LPT>(pid, sl, sa.c.k, nbits, whist[wave]);
+  }
+  if constexpr (EPI::kHist) {
+    __syncthreads();
+    for (int e = wave * kWave + lane; e < E; e += NW * kWave) {
+      int n = 0;
+#pragma unroll
+      for (int w8 = 0; w8 < NW; ++w8) n += whist[w8][e];
+      sa.hist[(int64_t)mt * E + e] = n;
+    }
+  }
+}
+
+// Epilogue policies of the pipelined kernel: store the logits (NoSel), or
+// also run the selection on the tile's rows in LDS (FusedSel: LPT lanes per
+// token, VPL experts per lane, the monotone-key case, dispatch histograms).
+struct NoSel {
+  static constexpr bool kOn = false;
+};
+template <int LPT, int VPL, bool MONO, bool HIST>
+struct FusedSel {
+  static constexpr bool kOn = true, kMono = MONO, kHist = HIST;
+  static constexpr int kLpt = LPT, kVpl = VPL;
+};
+
+template <typename In, int BM, int BN, int NS, int RB, int WM, int WN, class EPI = NoSel>
 __global__ __launch_bounds__(WM * WN * kWave) void gate_gemm_pipe_kernel(
     const In* __restrict__ x, const In* __restrict__ W, const float* __restrict__ logit_bias,
     float* __restrict__ out, int T, int d, int E, int n_m, int n_n, int splits, int per_xcd,
-    int stages_per_split) {
+    int stages_per_split, SelectArgs sa) {
   constexpr int ROWS = BM + BN;
   constexpr int STAGE = ROWS * RB;             // bytes per stage
   constexpr int RPI = 1024 / RB;               // rows per load instruction
@@ -443,13 +514,14 @@ __global__ __launch_bounds__(WM * WN * kWave) void gate_gemm_pipe_kernel(
 
   // Epilogue.  A 16 x 16 MFMA result gives a lane one column of four rows,
   // so direct stores write 64-byte row pieces from scattered lanes (measured:
-  // about 1.5 TB/s for a 33.5 MB logits array).  Instead the tile goes
-  // through the ring, now free, and whole rows leave with 16-byte stores
-  // from consecutive lanes.  PITCH: padded LDS row, so the four lane groups
-  // of one accumulator write hit different banks.
+  // about 1.5 TB/s for a 33.5 MB logits array).  Instead the tile (+ logit
+  // bias) goes through the ring, now free, and whole rows leave with 16-byte
+  // stores from consecutive lanes.  PITCH: padded LDS row, so the four lane
+  // groups of one accumulator write hit different banks.
   constexpr int PITCH = BN + 4;                         // floats
   constexpr int WROWS = BM / WM;                        // rows of one wave row
   constexpr int G = NS * STAGE / (WROWS * PITCH * 4);   // wave rows per pass
+  static_assert(!EPI::kOn || G >= WM, "the fused selection needs the whole tile in LDS");
   if constexpr (G >= 1) {
     constexpr int GP = G < WM ? G : WM;
     constexpr int PASSES = (WM + GP - 1) / GP;
@@ -457,21 +529,25 @@ __global__ __launch_bounds__(WM * WN * kWave) void gate_gemm_pipe_kernel(
     float* lo = reinterpret_cast<float*>(lds);
     const bool vec = E % 4 == 0 && reinterpret_cast<uintptr_t>(logits) % 16 == 0;
     const bool bias = logit_bias != nullptr && split == 0;
+    const bool store = !EPI::kOn || sa.write_logits;
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
       __syncthreads();  // the ring (or the previous pass) is no longer read
       if (wm / GP == p) {
         const int rbase = (wm - p * GP) * WROWS;
 #pragma unroll
-        for (int i = 0; i < MB; ++i)
+        for (int j = 0; j < NB; ++j) {
+          const int col = wn * (BN / WN) + j * 16 + row16;
+          const float b = (bias && n0 + col < E) ? logit_bias[n0 + col] : 0.0f;
 #pragma unroll
-          for (int j = 0; j < NB; ++j)
+          for (int i = 0; i < MB; ++i)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-              lo[(rbase + i * 16 + kq * 4 + r) * PITCH + wn * (BN / WN) + j * 16 + row16] =
-                  acc[i][j][r];
+              lo[(rbase + i * 16 + kq * 4 + r) * PITCH + col] = acc[i][j][r] + b;
+        }
       }
       __syncthreads();
+      if (!store) continue;
       const int prow0 = p * GP * WROWS;
       const int prows = (WM - p * GP < GP ? WM - p * GP : GP) * WROWS;
       for (int idx = tid; idx < prows * C4; idx += NW * kWave) {
@@ -479,10 +555,8 @@ __global__ __launch_bounds__(WM * WN * kWave) void gate_gemm_pipe_kernel(
         const int64_t t = (int64_t)m0 + prow0 + rr;
         const int e0 = n0 + c4 * 4;
         if (t >= T || e0 >= E) continue;
-        f32x4_t v = *reinterpret_cast<const f32x4_t*>(lo + rr * PITCH + c4 * 4);
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(lo + rr * PITCH + c4 * 4);
         if (vec && e0 + 4 <= E) {
-          if (bias) v += f32x4_t{logit_bias[e0], logit_bias[e0 + 1], logit_bias[e0 + 2],
-                                 logit_bias[e0 + 3]};
           if (MOE_GATE_NT)
             __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(logits + t * E + e0));
           else
@@ -490,9 +564,20 @@ __global__ __launch_bounds__(WM * WN * kWave) void gate_gemm_pipe_kernel(
         } else {
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            if (e0 + q < E) logits[t * E + e0 + q] = v[q] + (bias ? logit_bias[e0 + q] : 0.0f);
+            if (e0 + q < E) logits[t * E + e0 + q] = v[q];
         }
       }
+    }
+    if constexpr (EPI::kOn) {
+      // the selection's LDS scratch lies in the ring behind the tile's rows
+      // (a workgroup above 144 KB of LDS measured 25-35 % slower)
+      constexpr int TPP = NW * (kWave / EPI::kLpt);
+      constexpr int PICK_OFF = BM * PITCH * 4;
+      constexpr int HIST_OFF = PICK_OFF + TPP * sel::kMaxK * 4;
+      static_assert(HIST_OFF + NW * kFusedMaxE * 4 <= NS * STAGE, "fused scratch in the ring");
+      fused_select<EPI, BM, NW, PITCH>(lo, reinterpret_cast<int32_t(*)[sel::kMaxK]>(lds + PICK_OFF),
+                                       reinterpret_cast<int32_t(*)[kFusedMaxE]>(lds + HIST_OFF),
+                                       m0, T, lane, wave, mt, sa);
     }
   } else {  // the ring cannot hold one wave row of the tile: direct stores
 #pragma unroll
@@ -511,18 +596,20 @@ __global__ __launch_bounds__(WM * WN * kWave) void gate_gemm_pipe_kernel(
   }
 }
 
-template <typename In, int BM, int BN, int NS, int RB, int WM, int WN>
+template <typename In, int BM, int BN, int NS, int RB, int WM, int WN, class EPI = NoSel>
 hipError_t launch_pipe(const void* x, const void* W, const float* logit_bias, float* out,
-                       int T, int d, int E, int splits, hipStream_t s) {
+                       int T, int d, int E, int splits, hipStream_t s,
+                       const SelectArgs& sa = SelectArgs{}) {
   const int n_m = (T + BM - 1) / BM;
   const int n_n = (E + BN - 1) / BN;
   const int n_stages = (int)(((int64_t)d * sizeof(In) + RB - 1) / RB);
   const int per_split = (n_stages + splits - 1) / splits;
   const int tiles = n_m * n_n * splits;
   const int per_xcd = (tiles + kXcds - 1) / kXcds;
-  return launch(kStageGate, gate_gemm_pipe_kernel<In, BM, BN, NS, RB, WM, WN>,
-                dim3(per_xcd * kXcds), dim3(WM * WN * kWave), s, (const In*)x, (const In*)W,
-                logit_bias, out, T, d, E, n_m, n_n, splits, per_xcd, per_split);
+  return launch(EPI::kOn ? kStageGateSelect : kStageGate,
+                gate_gemm_pipe_kernel<In, BM, BN, NS, RB, WM, WN, EPI>, dim3(per_xcd * kXcds),
+                dim3(WM * WN * kWave), s, (const In*)x, (const In*)W, logit_bias, out, T, d, E,
+                n_m, n_n, splits, per_xcd, per_split, sa);
 }
 
 template <typename In, int BM, int BN, int KB>
@@ -567,7 +654,9 @@ constexpr int kMinTiles = 256;
 // combination is usable when the ring fits in LDS and its outstanding copies
 // fit the vmcnt counter.
 constexpr int kLdsBytes = 160 * 1024;
-constexpr int kLdsBudget = kLdsBytes - 8 * 1024;
+// Rings stay within 144 KB: a workgroup with more LDS (152 or 160 KB)
+// measured 25-35 % slower on the same work.
+constexpr int kLdsBudget = 144 * 1024;
 
 // `waves` is the tile's wave count (4: 2 x 2, 8: 4 x 2 or 2 x 4); a wave
 // issues at most ceil(load blocks / waves) copies per stage.
@@ -762,7 +851,7 @@ TileChoice choose_tile8(int T, int d, int E, bool allow_split, int* splits) {
 // three deep (measured on the Qwen3-like shape), large ones 128-byte stages
 // as deep as fits.
 void choose_ring(GatePlan& g, long wgs) {
-  const int budget = (wgs > kMinTiles ? kLdsBytes / 2 : kLdsBytes);
+  const int budget = (wgs > kMinTiles ? kLdsBytes / 2 : kLdsBudget);
   const int waves = g.wm * g.wn;
   if (waves == 8) {
     if (g.bm * g.bn < 128 * 128 && depth_ok(g.bm, g.bn, 3, 256, 8) &&
@@ -869,6 +958,82 @@ GatePlan plan_gate(int32_t T, int32_t d, int32_t E, int32_t dtype, bool aligned,
   }
   if (!depth_ok(g.bm, g.bn, g.ns, g.rb, waves)) g.ns = 2;
   return g;
+}
+
+// Gate + selection in one kernel.  Built for the whole-row eight-wave tiles
+// of E <= 128 experts (256 x 128 at a 3-deep ring, 128 x 128 at a 4-deep
+// ring, 128-byte stages) and the selection shapes of such E (8 lanes x 16
+// experts, 16 x 8).
+namespace {
+
+struct FusedTile {
+  int bm, bn, wm, wn, ns, rb;
+};
+constexpr FusedTile kFusedTiles[] = {{256, 128, 4, 2, 3, 128}, {128, 128, 2, 4, 4, 128}};
+
+template <int BM, int BN, int WM, int WN, int NS, int RB, int LPT, int VPL>
+hipError_t launch_fused_shape(bool mono, bool hist, const void* x, const void* W,
+                              const float* lb, float* logits, int T, int d, int E,
+                              const SelectArgs& sa, hipStream_t s) {
+#define MOE_F(M_, H_)                                                                   \
+  if (mono == M_ && hist == H_)                                                         \
+    return launch_pipe<uint16_t, BM, BN, NS, RB, WM, WN, FusedSel<LPT, VPL, M_, H_>>(   \
+        x, W, lb, logits, T, d, E, 1, s, sa);
+  MOE_F(true, true)
+  MOE_F(true, false)
+  MOE_F(false, true)
+  MOE_F(false, false)
+#undef MOE_F
+  return hipErrorInvalidValue;
+}
+
+template <int BM, int BN, int WM, int WN, int NS, int RB>
+hipError_t launch_fused_tile(int lpt, int vpl, bool mono, bool hist, const void* x,
+                             const void* W, const float* lb, float* logits, int T, int d, int E,
+                             const SelectArgs& sa, hipStream_t s) {
+  if (lpt == 8 && vpl == 16)
+    return launch_fused_shape<BM, BN, WM, WN, NS, RB, 8, 16>(mono, hist, x, W, lb, logits, T, d,
+                                                             E, sa, s);
+  if (lpt == 16 && vpl == 8)
+    return launch_fused_shape<BM, BN, WM, WN, NS, RB, 16, 8>(mono, hist, x, W, lb, logits, T, d,
+                                                             E, sa, s);
+  return hipErrorInvalidValue;
+}
+
+bool grouped_cfg(const RouteCfg& c) { return c.n_groups > 1 && c.topk_groups < c.n_groups; }
+
+}  // namespace
+
+int gate_select_tokens(const GatePlan& g, int32_t dtype, const RouteCfg& c) {
+  if (!g.pipe || dtype != 1 || g.splits != 1 || g.bn < c.E || c.E > kFusedMaxE ||
+      std::getenv("MOE_NO_FUSED_SELECT"))
+    return 0;
+  int lpt = 0, vpl = 0;
+  select_shape(c, &lpt, &vpl);
+  if (!((lpt == 8 && vpl == 16) || (lpt == 16 && vpl == 8))) return 0;
+  for (const auto& f : kFusedTiles)
+    if (f.bm == g.bm && f.bn == g.bn && f.wm == g.wm && f.wn == g.wn && f.ns == g.ns &&
+        f.rb == g.rb)
+      return g.bm;
+  return 0;
+}
+
+hipError_t launch_gate_select(const GatePlan& g, int32_t dtype, const void* x, const void* W,
+                              const float* logit_bias, float* logits, const SelectArgs& sa,
+                              hipStream_t stream) {
+  const RouteCfg& c = sa.c;
+  if (gate_select_tokens(g, dtype, c) == 0 || (sa.write_logits && !logits))
+    return hipErrorInvalidValue;
+  if (c.T == 0) return hipSuccess;
+  int lpt = 0, vpl = 0;
+  select_shape(c, &lpt, &vpl);
+  const bool mono = sa.select_bias == nullptr && !grouped_cfg(c);
+  const bool hist = sa.hist != nullptr;
+  if (g.bm == 256)
+    return launch_fused_tile<256, 128, 4, 2, 3, 128>(lpt, vpl, mono, hist, x, W, logit_bias,
+                                                     logits, c.T, c.d, c.E, sa, stream);
+  return launch_fused_tile<128, 128, 2, 4, 4, 128>(lpt, vpl, mono, hist, x, W, logit_bias,
+                                                   logits, c.T, c.d, c.E, sa, stream);
 }
 
 hipError_t launch_gate_gemm(const GatePlan& g, int32_t dtype, const void* x, const void* W,

@@ -16,7 +16,8 @@ enum Stage : int32_t {
   kStageDispHist = 3,
   kStageDispScan = 4,
   kStageDispScatter = 5,
-  kNumStages = 6
+  kStageGateSelect = 6,
+  kNumStages = 7
 };
 
 // Per-kernel timing (moe_profile_enable): the start/stop events of the next
@@ -64,6 +65,35 @@ GatePlan plan_gate(int32_t T, int32_t d, int32_t E, int32_t dtype, bool aligned,
 hipError_t launch_gate_gemm(const GatePlan& g, int32_t dtype, const void* x, const void* W,
                             const float* logit_bias, float* out, int32_t T, int32_t d,
                             int32_t E, hipStream_t stream);
+
+// Selection arguments of the gate kernel's fused epilogue (whole-row tiles:
+// the selection runs on the tile's logits in LDS).  hist: per-M-tile expert
+// histograms of the dispatch (tiles of BM tokens x k routes), or NULL;
+// write_logits: also store the logits; vec: 16-byte select_bias loads.
+struct SelectArgs {
+  RouteCfg c;
+  const float* select_bias;
+  const int32_t* k_per_token;
+  int32_t* ids;
+  float* weights;
+  int32_t* dev_err;
+  int32_t* hist;
+  int32_t write_logits;
+  int32_t vec;
+};
+
+// Tokens per tile (BM) when the gate kernel of plan g can run the selection
+// of c in its epilogue (one workgroup holds whole rows of logits, no K
+// split), else 0.
+int gate_select_tokens(const GatePlan& g, int32_t dtype, const RouteCfg& c);
+// Gate + selection in one kernel (gate_select_tokens(g, dtype, sa.c) > 0);
+// logits (written when sa.write_logits) may be NULL otherwise.
+hipError_t launch_gate_select(const GatePlan& g, int32_t dtype, const void* x, const void* W,
+                              const float* logit_bias, float* logits, const SelectArgs& sa,
+                              hipStream_t stream);
+
+// Lanes per token and experts per lane of the select kernel for c.
+void select_shape(const RouteCfg& c, int* lpt, int* vpl);
 
 // Score + (grouped) top-k + weights.  The logits are the sum of `splits`
 // fp32 partial arrays `split_stride` floats apart (summed in order); when

@@ -2,6 +2,7 @@
 // host, thread-local error text, and kernel launches on the caller's stream.
 // Every check here runs before anything is enqueued and touches no device
 // state, so an invalid call never reaches the GPU.
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
@@ -194,6 +195,21 @@ int32_t route_core(const moe_route_params* p, const void* x, const void* W,
   const bool aligned = reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
                        reinterpret_cast<uintptr_t>(W) % 16 == 0;
   moe::GatePlan g = moe::plan_gate(p->T, p->d, p->E, p->dtype, aligned, true);
+  if (moe::gate_select_tokens(g, p->dtype, c) > 0) {  // one kernel: the logits stay in LDS
+    moe::SelectArgs sa{};
+    sa.c = c;
+    sa.select_bias = select_bias;
+    sa.k_per_token = k_per_token;
+    sa.ids = ids;
+    sa.weights = weights;
+    sa.dev_err = dev_err;
+    sa.hist = hist;
+    sa.write_logits = logits != nullptr;
+    sa.vec = p->E % 4 == 0 && (!select_bias || reinterpret_cast<uintptr_t>(select_bias) % 16 == 0);
+    e = moe::launch_gate_select(g, p->dtype, x, W, logit_bias, logits, sa, s);
+    if (e != hipSuccess) return device_fail(e, "gate + select launch");
+    return MOE_OK;
+  }
   const size_t te = (size_t)p->T * p->E * sizeof(float);
   float* hand_off = nullptr;
   if (workspace && workspace_bytes >= te * g.splits) {
@@ -235,12 +251,26 @@ size_t route_ws_bytes(const moe_route_params* p) {
   return (size_t)p->T * p->E * sizeof(float) * g.splits;
 }
 
-// Tokens per dispatch tile when the select kernel can write the dispatch's
-// tile histograms itself, else 0.
-int fused_hist_tokens(const moe_route_params* p) {
-  const int n = moe::select_hist_tokens(to_cfg(p));
+// Tokens per dispatch tile when the routing kernels write the dispatch's
+// tile histograms themselves, else 0: the gate kernel with the selection
+// fused (tiles of BM tokens) or the select kernel.  `gate`: x and W are
+// given; `aligned`: both are 16-byte aligned.
+int fused_hist_tokens(const moe_route_params* p, bool gate, bool aligned) {
+  const moe::RouteCfg c = to_cfg(p);
+  int n = 0;
+  if (gate) {
+    const moe::GatePlan g = moe::plan_gate(p->T, p->d, p->E, p->dtype, aligned, true);
+    n = moe::gate_select_tokens(g, p->dtype, c);
+  }
+  if (n == 0) n = moe::select_hist_tokens(c);
   if (n == 0) return 0;
   return moe::dispatch_hist_ok((int64_t)p->T * p->k, p->E, n * p->k) ? n : 0;
+}
+
+// Dispatch part of the moe_route_dispatch workspace for a given path.
+size_t disp_ws_bytes(const moe_route_params* p, int n) {
+  return n > 0 ? (size_t)((p->T + n - 1) / n) * p->E * sizeof(int32_t)
+               : moe::dispatch_workspace_bytes((int64_t)p->T * p->k, p->E);
 }
 
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
@@ -265,11 +295,12 @@ size_t moe_route_dispatch_workspace_size(const moe_route_params* p) {
   if (check_route_params(p, true) != MOE_OK) return 0;
   const int64_t R = (int64_t)p->T * p->k;
   if (R > kI32Max) return 0;
-  const size_t route = p->T > 0 ? align256(route_ws_bytes(p)) : 0;
-  const int n = p->T > 0 ? fused_hist_tokens(p) : 0;
-  const size_t disp = n > 0 ? (size_t)((p->T + n - 1) / n) * p->E * sizeof(int32_t)
-                            : moe::dispatch_workspace_bytes(R, p->E);
-  return route + disp;
+  if (p->T == 0) return moe::dispatch_workspace_bytes(R, p->E);
+  // enough for every path the call may take (aligned or not, gate or not)
+  size_t disp = 0;
+  for (int path = 0; path < 3; ++path)
+    disp = std::max(disp, disp_ws_bytes(p, fused_hist_tokens(p, path < 2, path == 0)));
+  return align256(route_ws_bytes(p)) + disp;
 }
 
 int32_t moe_route_dispatch(const moe_route_params* p, const void* x, const void* W,
@@ -299,7 +330,10 @@ int32_t moe_route_dispatch(const moe_route_params* p, const void* x, const void*
   }
   const size_t route = align256(route_ws_bytes(p));
   int32_t* disp_ws = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + route);
-  const int n = fused_hist_tokens(p);
+  const bool gate = x != nullptr;
+  const bool aligned = reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
+                       reinterpret_cast<uintptr_t>(W) % 16 == 0;
+  const int n = fused_hist_tokens(p, gate, aligned);
   rc = route_core(p, x, W, logit_bias, select_bias, k_per_token, logits, ids, weights,
                   workspace, route, dev_err, n > 0 ? disp_ws : nullptr, s);
   if (rc != MOE_OK) return rc;
