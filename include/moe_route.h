@@ -25,6 +25,16 @@
  *    device int32 *dev_err (the caller zeroes it).
  *  - T == 0 is valid and enqueues nothing (moe_dispatch still writes zero
  *    counts and offsets).
+ *  - Results do not depend on the kernel plan (tiling, K split, fused or
+ *    separate selection) beyond fp32 summation order inside the gate, which
+ *    is fixed per plan; plans are chosen from the shapes.  For tuning, these
+ *    environment variables override the choice: MOE_GATE_TILE ("BMxBN", or
+ *    "BMxBNw8" for eight wavefronts), MOE_GATE_SPLITS (1-8), MOE_GATE_RB
+ *    (64/128/256/512-byte stages), MOE_GATE_NS (ring depth), MOE_GATE_NOPIPE
+ *    (the register-staged gate kernel), MOE_SELECT_LPT (4/8/16/64 lanes per
+ *    token), MOE_NO_FUSED_SELECT (selection in its own kernel),
+ *    MOE_DISPATCH_UNFUSED (the three-kernel dispatch).  Values that do not
+ *    fit the shapes are ignored; workspace sizes follow the same variables.
  */
 #ifndef MOE_ROUTE_H
 #define MOE_ROUTE_H

@@ -170,12 +170,16 @@ def test_dispatch_rejects_unaligned_workspace():
 @pytest.mark.parametrize("T,k,E", [(4096, 16, 128), (65536, 4, 128), (16384, 6, 384),
                                    (8192, 8, 256), (256, 2, 8), (70000, 30, 1024), (5, 3, 7)])
 def test_dispatch_workspace_size_per_path(T, k, E):
-    # two-kernel path: one tile-major histogram of at most 32 Ki counts;
+    # two-kernel path: one tile-major histogram of at most 32 Ki counts (the
+    # smallest tiles of 512, 1024 or 2048 routes that fit), unless those
+    # tiles are fewer than 128 while 512-route tiles are at least 128;
     # otherwise tile histograms, tile bases and totals (tiles of 512 routes)
     n = tda.dispatch_workspace_size(T, k, E)
     R = T * k
-    if E % 4 == 0 and any(-(-R // t) * E <= 32768 for t in (512, 1024, 2048)):
-        assert n <= 32768 * 4 and n % (4 * E) == 0
+    fits = [-(-R // t) for t in (512, 1024, 2048) if -(-R // t) * E <= 32768]
+    two = E % 4 == 0 and fits and not (fits[0] < 128 and -(-R // 512) >= 128)
+    if two:
+        assert n == fits[0] * E * 4
     else:
         nt = -(-R // 512)
         assert n == (2 * nt + 1) * E * 4
