@@ -52,6 +52,9 @@ def stage_bytes(w, T, R, R_valid, tile_bytes):
         + tile_bytes,
         "hash": T * 4 + T * k * 4 + T * d * xb + E * d * xb + T * k * 8,
         "select": T * E * 4 + T * k * 8 + (T * 4 if w.dynamic_k else 0),
+        # small batches: selection and the whole dispatch in one workgroup
+        "select_dispatch": T * E * 4 + T * k * 8 + (T * 4 if w.dynamic_k else 0)
+        + R * 4 + R_valid * 4 + E * 8,
         "disp_hist": R * 4 + tile_bytes,
         "disp_scan": 2 * tile_bytes + E * 4,
         "disp_scatter": tile_bytes + E * 4 + R * 4 + R * 4 + R_valid * 4 + E * 8,

@@ -33,7 +33,8 @@
  *    (64/128/256/512-byte stages), MOE_GATE_NS (ring depth), MOE_GATE_NOPIPE
  *    (the register-staged gate kernel), MOE_SELECT_LPT (4/8/16/64 lanes per
  *    token), MOE_NO_FUSED_SELECT (selection in its own kernel),
- *    MOE_DISPATCH_UNFUSED (the three-kernel dispatch).  Values that do not
+ *    MOE_DISPATCH_UNFUSED (the three-kernel dispatch), MOE_NO_SMALL_DISPATCH
+ *    (no one-workgroup selection + dispatch for small batches).  Values that do not
  *    fit the shapes are ignored; workspace sizes follow the same variables.
  */
 #ifndef MOE_ROUTE_H
@@ -46,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 /* return codes */
 #define MOE_OK 0
@@ -256,7 +257,8 @@ size_t moe_route_dispatch_workspace_size(const moe_route_params* p);
 #define MOE_STAGE_DISP_SCAN 4    /* dispatch: scans */
 #define MOE_STAGE_DISP_SCATTER 5 /* dispatch: permutation */
 #define MOE_STAGE_GATE_SELECT 6  /* gate contraction with the selection fused */
-#define MOE_NUM_STAGES 7
+#define MOE_STAGE_SELECT_DISPATCH 7 /* selection + dispatch of a small batch */
+#define MOE_NUM_STAGES 8
 int32_t moe_profile_enable(int32_t enable);
 int32_t moe_profile_read(double* ms, int64_t* launches, int32_t n);
 

@@ -161,3 +161,51 @@ def test_fused_gate_select_matches_separate_kernels(T, E, tile, ns, score, bias_
                 route_scale=rkw["route_scale"], k_per_token=kpt, n_groups=rkw["n_groups"],
                 topk_groups=rkw["topk_groups"], where="fused gate+select")
     check_dispatch(tuple(outs[0][2:6]), oracle.dispatch(down(outs[0][0]), E))
+
+
+@pytest.mark.parametrize("T,E,k,score,bias_groups,dynk,dt", [
+    (256, 8, 2, "softmax", False, False, "f32"),       # Mixtral-like
+    (33, 128, 16, "softmax", False, True, "bf16"),     # a few Qwen3-like tokens, per-token k
+    (100, 64, 8, "sigmoid", True, False, "bf16"),      # biased, grouped
+    (511, 30, 4, "sqrt_softplus", False, False, "f32"),  # E not a multiple of 4
+    (256, 128, 8, "softmax_topk", False, True, "bf16"),  # exactly 2048 routes
+    (1, 16, 3, "softmax", False, False, "f32"),
+    (2049, 16, 1, "softmax", False, False, "f32"),     # 2049 routes: the regular path
+])
+def test_small_batch_route_dispatch(T, E, k, score, bias_groups, dynk, dt):
+    """Small batches (T * k <= 2048, E <= 128): selection and the whole
+    dispatch in one workgroup, against separate moe_route + moe_dispatch calls
+    (bit for bit) and the oracle; invalid per-token k values count as
+    errors."""
+    rng = np.random.default_rng([T, E, k])
+    d = 256
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    Wf = (rng.standard_normal((E, d)) / np.sqrt(d)).astype(np.float32)
+    if dt == "bf16":
+        x, Wf = wl.f32_to_bf16_bits(x), wl.f32_to_bf16_bits(Wf)
+    sb = (0.01 * rng.standard_normal(E)).astype(np.float32) if bias_groups else None
+    kpt = rng.integers(1, k + 1, size=T).astype(np.int32) if dynk else None
+    nbad = 0
+    if dynk and T > 3:
+        kpt[[1, 2]] = [0, k + 1]
+        nbad = 2
+    rkw = dict(score=score, select_bias=sb, k_per_token=kpt,
+               n_groups=4 if bias_groups else 1, topk_groups=2 if bias_groups else None,
+               group_score="top2_sum" if bias_groups else None, renormalize=True,
+               route_scale=2.5 if bias_groups else 1.0)
+    kw = {key: (up(v) if isinstance(v, np.ndarray) else v) for key, v in rkw.items()
+          if v is not None}
+    say("small route_dispatch", T, E, k, score, bias_groups, dynk, dt)
+    tda.profile_enable(True)
+    fused, sep, e1, e2 = both(up(x), up(Wf), k, E, **kw)
+    prof = tda.profile_read()
+    tda.profile_enable(False)
+    small = T * k <= 2048
+    assert prof["select_dispatch"][1] == (1 if small else 0), prof["select_dispatch"]
+    assert_same(fused, sep)
+    assert e1 == e2 == nbad
+    ref = oracle_route(oracle, oracle.gate(x, Wf), k, **rkw)
+    check_route(down(fused[0]), down(fused[1]), ref, oracle, score=score, renormalize=True,
+                route_scale=rkw["route_scale"], k_per_token=kpt, n_groups=rkw["n_groups"],
+                topk_groups=rkw["topk_groups"], where="small route_dispatch")
+    check_dispatch(tuple(fused[2:6]), oracle.dispatch(down(fused[0]), E))

@@ -21,7 +21,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe_route.so")
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EDEVICE = 0, -1, -2, -3
 MAX_EXPERTS, MAX_K, MAX_GROUPS = 1024, 32, 64
 SCORES = {"softmax": 0, "sigmoid": 1, "sqrt_softplus": 2, "softmax_topk": 3}
@@ -31,7 +31,8 @@ EXPORTS = ("moe_route", "moe_route_workspace_size", "moe_route_hash",
            "moe_dispatch_workspace_size", "moe_dispatch",
            "moe_route_dispatch", "moe_route_dispatch_workspace_size",
            "moe_profile_enable", "moe_profile_read", "moe_last_error", "moe_abi_version")
-STAGES = ("gate", "select", "hash", "disp_hist", "disp_scan", "disp_scatter", "gate_select")
+STAGES = ("gate", "select", "hash", "disp_hist", "disp_scan", "disp_scatter", "gate_select",
+          "select_dispatch")
 
 
 class MoeError(RuntimeError):

@@ -289,6 +289,8 @@ __device__ __forceinline__ void fused_select(const float* lo, int32_t (*pick)[se
   const bool lvec = sa.vec && nval == VPL;
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
+  float sb[VPL];  // the same experts for every token of this lane
+  sel::load_sbias<VPL, EPI::kMono>(sa.select_bias, e0, E, lvec, sb);
   if constexpr (EPI::kHist)
     for (int e = lane; e < E; e += kWave) whist[wave][e] = 0;
   for (int ps = 0; ps < BM / TPP; ++ps) {
@@ -305,10 +307,11 @@ __device__ __forceinline__ void fused_select(const float* lo, int32_t (*pick)[se
     float lv[VPL];
 #pragma unroll
     for (int j = 0; j < VPL; ++j) lv[j] = (tok_ok && j < nval) ? row[e0 + j] : -INFINITY;
+    const int kraw = sa.k_per_token ? sa.k_per_token[trow] : sa.c.k;
     int pid[KPL];
-    sel::select_token<LPT, VPL, EPI::kMono>(sa.c, sl, seg, tok_ok, t, trow, lv, nval, lvec, row,
-                                            pick[wave * TPW + seg], sa.select_bias,
-                                            sa.k_per_token, sa.ids, sa.weights, sa.dev_err, pid);
+    sel::select_token<LPT, VPL, EPI::kMono>(sa.c, sl, seg, tok_ok, t, lv, nval, sb, kraw, row,
+                                            pick[wave * TPW + seg], sa.ids, sa.weights,
+                                            sa.dev_err, pid);
     if constexpr (EPI::kHist) sel::count_picks<LPT>(pid, sl, sa.c.k, nbits, whist[wave]);
   }
   if constexpr (EPI::kHist) {

@@ -17,7 +17,8 @@ enum Stage : int32_t {
   kStageDispScan = 4,
   kStageDispScatter = 5,
   kStageGateSelect = 6,
-  kNumStages = 7
+  kStageSelectDispatch = 7,
+  kNumStages = 8
 };
 
 // Per-kernel timing (moe_profile_enable): the start/stop events of the next
@@ -107,6 +108,18 @@ hipError_t launch_select(const RouteCfg& c, const float* logits, int32_t splits,
                          const float* select_bias, const int32_t* k_per_token, int32_t* ids,
                          float* weights, int32_t* dev_err, int32_t* hist, hipStream_t stream);
 int select_hist_tokens(const RouteCfg& c);  // 0: no histogram option
+
+// Selection and the whole dispatch of a small batch in one workgroup (when
+// small_dispatch_ok(c)): the select kernel's outputs plus moe_dispatch's
+// counts, offsets, perm and inv (inv may be NULL).
+bool small_dispatch_ok(const RouteCfg& c);
+hipError_t launch_route_dispatch_small(const RouteCfg& c, const float* logits, int32_t splits,
+                                       int64_t split_stride, float* logits_out,
+                                       const float* logit_bias, const float* select_bias,
+                                       const int32_t* k_per_token, int32_t* ids,
+                                       float* weights, int32_t* dev_err, int32_t* counts,
+                                       int32_t* offsets, int32_t* perm, int32_t* inv,
+                                       hipStream_t stream);
 
 // Hash routing: table gather (+ k gathered gate dot products and weights).
 // With `logits` (the sum of `splits` arrays [T][E], split_stride floats

@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -176,26 +177,37 @@ const char* moe_last_error(void) { return g_last_error.c_str(); }
 
 namespace {
 
+// Dispatch outputs when a small batch is routed and dispatched by one kernel.
+struct SmallDispatch {
+  int32_t *counts, *offsets, *perm, *inv;
+};
+
 // Gate + select of moe_route on validated arguments (T > 0, ids and weights
 // set, logits set in select-only mode).  `hist`: optional per-tile expert
-// histograms for a fused dispatch (launch_select).
+// histograms for a fused dispatch (launch_select).  `sd` (small_dispatch_ok
+// batches only): the selection kernel also performs the dispatch.
 int32_t route_core(const moe_route_params* p, const void* x, const void* W,
                    const float* logit_bias, const float* select_bias,
                    const int32_t* k_per_token, float* logits, int32_t* ids, float* weights,
                    void* workspace, size_t workspace_bytes, int32_t* dev_err, int32_t* hist,
-                   hipStream_t s) {
+                   hipStream_t s, const SmallDispatch* sd = nullptr) {
   const moe::RouteCfg c = to_cfg(p);
   hipError_t e;
   if (x == nullptr) {  // select-only
-    e = moe::launch_select(c, logits, 1, 0, nullptr, logit_bias, select_bias, k_per_token, ids,
-                           weights, dev_err, hist, s);
+    if (sd)
+      e = moe::launch_route_dispatch_small(c, logits, 1, 0, nullptr, logit_bias, select_bias,
+                                           k_per_token, ids, weights, dev_err, sd->counts,
+                                           sd->offsets, sd->perm, sd->inv, s);
+    else
+      e = moe::launch_select(c, logits, 1, 0, nullptr, logit_bias, select_bias, k_per_token,
+                             ids, weights, dev_err, hist, s);
     if (e != hipSuccess) return device_fail(e, "select launch");
     return MOE_OK;
   }
   const bool aligned = reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
                        reinterpret_cast<uintptr_t>(W) % 16 == 0;
   moe::GatePlan g = moe::plan_gate(p->T, p->d, p->E, p->dtype, aligned, true);
-  if (moe::gate_select_tokens(g, p->dtype, c) > 0) {  // one kernel: the logits stay in LDS
+  if (!sd && moe::gate_select_tokens(g, p->dtype, c) > 0) {  // one kernel: logits stay in LDS
     moe::SelectArgs sa{};
     sa.c = c;
     sa.select_bias = select_bias;
@@ -224,9 +236,15 @@ int32_t route_core(const moe_route_params* p, const void* x, const void* W,
   }
   e = moe::launch_gate_gemm(g, p->dtype, x, W, logit_bias, hand_off, p->T, p->d, p->E, s);
   if (e != hipSuccess) return device_fail(e, "gate GEMM launch");
-  e = moe::launch_select(c, hand_off, g.splits, (int64_t)p->T * p->E,
-                         g.splits > 1 ? logits : nullptr, nullptr, select_bias, k_per_token, ids,
-                         weights, dev_err, hist, s);
+  if (sd)
+    e = moe::launch_route_dispatch_small(c, hand_off, g.splits, (int64_t)p->T * p->E,
+                                         g.splits > 1 ? logits : nullptr, nullptr, select_bias,
+                                         k_per_token, ids, weights, dev_err, sd->counts,
+                                         sd->offsets, sd->perm, sd->inv, s);
+  else
+    e = moe::launch_select(c, hand_off, g.splits, (int64_t)p->T * p->E,
+                           g.splits > 1 ? logits : nullptr, nullptr, select_bias, k_per_token,
+                           ids, weights, dev_err, hist, s);
   if (e != hipSuccess) return device_fail(e, "select launch");
   return MOE_OK;
 }
@@ -329,6 +347,11 @@ int32_t moe_route_dispatch(const moe_route_params* p, const void* x, const void*
     return MOE_OK;
   }
   const size_t route = align256(route_ws_bytes(p));
+  if (moe::small_dispatch_ok(to_cfg(p)) && !std::getenv("MOE_NO_SMALL_DISPATCH")) {
+    const SmallDispatch sd{counts, offsets, perm, inv};
+    return route_core(p, x, W, logit_bias, select_bias, k_per_token, logits, ids, weights,
+                      workspace, route, dev_err, nullptr, s, &sd);
+  }
   int32_t* disp_ws = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + route);
   const bool gate = x != nullptr;
   const bool aligned = reinterpret_cast<uintptr_t>(x) % 16 == 0 &&

@@ -27,6 +27,7 @@
 // a power-of-two run of whole lanes, else from one segment reduction per
 // group.
 #include <cstdlib>
+#include <type_traits>
 
 #include "device_common.h"
 #include "kernels.h"
@@ -79,11 +80,15 @@ __global__ __launch_bounds__(WPB * kWave) void select_kernel(
   // logits (NSPLIT partial sums added in order), + logit_bias
   const int64_t trow = tok_ok ? t : (t0 < c.T ? t0 : (int64_t)c.T - 1);
   float lv[VPL];
+  float sb[VPL];
+  int kraw;
   {
     float pv[NSPLIT][VPL];
 #pragma unroll
     for (int sp = 0; sp < NSPLIT; ++sp)
       load_vals<VPL>(logits + sp * split_stride + trow * E, e0, E, lvec, 0.f, pv[sp]);
+    sel::load_sbias<VPL, MONO>(select_bias, e0, E, lvec, sb);
+    kraw = k_per_token ? k_per_token[trow] : c.k;
 #pragma unroll
     for (int j = 0; j < VPL; ++j) {
       lv[j] = pv[0][j];
@@ -109,9 +114,8 @@ __global__ __launch_bounds__(WPB * kWave) void select_kernel(
   for (int j = 0; j < VPL; ++j) lrow[tb][e0 + j] = lv[j];
 
   int pid[KPL];
-  sel::select_token<LPT, VPL, MONO>(c, sl, seg, tok_ok, t, trow, lv, nval, lvec, lrow[tb],
-                                    pick[tb], select_bias, k_per_token, ids, weights, dev_err,
-                                    pid);
+  sel::select_token<LPT, VPL, MONO>(c, sl, seg, tok_ok, t, lv, nval, sb, kraw, lrow[tb],
+                                    pick[tb], ids, weights, dev_err, pid);
   if constexpr (HIST) {
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
@@ -126,6 +130,168 @@ __global__ __launch_bounds__(WPB * kWave) void select_kernel(
 #pragma unroll
       for (int w8 = 0; w8 < WPB; ++w8) n += whist[w8][e];
       hist[(int64_t)blockIdx.x * E + e] = n;
+    }
+  }
+}
+
+// Routing and dispatch of a small batch in one workgroup (T * k <=
+// kSmallRoutes routes, E <= kSmallE): the selection as in select_kernel,
+// pass by pass over the tokens, each route's expert kept in LDS; then the
+// dispatch of moe_dispatch in LDS -- per-chunk (64 routes) counts from
+// ballot peer masks, per-expert exclusive scans over the chunks (one
+// wavefront per expert), the scan over experts, and the stable placement
+// (position = expert offset + earlier chunks + peers below in the chunk).
+// One launch instead of three for decode-sized batches.
+constexpr int kSmallWaves = 8;
+constexpr int kSmallRoutes = 2048;
+constexpr int kSmallE = 128;
+
+template <int LPT, int VPL, int NSPLIT, bool MONO>
+__global__ __launch_bounds__(kSmallWaves * kWave) void route_dispatch_small_kernel(
+    RouteCfg c, const float* __restrict__ logits, int64_t split_stride,
+    float* __restrict__ logits_out, const float* __restrict__ logit_bias,
+    const float* __restrict__ select_bias, const int32_t* __restrict__ k_per_token,
+    int32_t* __restrict__ ids, float* __restrict__ weights, int32_t* __restrict__ dev_err,
+    int vec, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+  constexpr int TPW = kWave / LPT;               // tokens per wavefront and pass
+  constexpr int TPP = kSmallWaves * TPW;         // tokens per pass
+  constexpr int ROW = LPT * VPL;
+  constexpr int KPL = (kMaxK + LPT - 1) / LPT;
+  constexpr int NCH = kSmallRoutes / kWave;      // chunks of 64 routes, at most
+  __shared__ __attribute__((aligned(16))) float lrow[TPP][ROW];
+  __shared__ int32_t pick[TPP][kMaxK];
+  __shared__ int32_t rid[kSmallRoutes];          // expert of each route, -1: none
+  __shared__ int32_t cbase[NCH][kSmallE];        // per-chunk counts, then bases
+  __shared__ int32_t off[kSmallE + 1];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int seg = lane / LPT, sl = lane % LPT;
+  const int E = c.E, K = c.k;
+  const int e0 = sl * VPL;
+  const int nval = min(max(E - e0, 0), VPL);
+  const bool lvec = vec && nval == VPL;
+  const int T = c.T;
+
+  // Pass by pass; the logits and per-token k of the next pass are loaded
+  // while this one is selected (two register buffers, alternating passes).
+  float sb[VPL], lb[VPL];
+  sel::load_sbias<VPL, MONO>(select_bias, e0, E, lvec, sb);
+  if (logit_bias) {
+    load_vals<VPL>(logit_bias, e0, E, lvec, 0.f, lb);
+  } else {
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) lb[j] = 0.f;
+  }
+  float pv[2][NSPLIT][VPL];
+  int kr[2];
+  auto fetch = [&](int pass, auto bc) {
+    constexpr int B = decltype(bc)::value;
+    const int tw = pass * TPP + wave * TPW;
+    const int64_t t = tw + seg;
+    const int64_t trow = t < T ? t : (tw < T ? tw : T - 1);  // a row inside the batch
+#pragma unroll
+    for (int sp = 0; sp < NSPLIT; ++sp)
+      load_vals<VPL>(logits + sp * split_stride + trow * E, e0, E, lvec, 0.f, pv[B][sp]);
+    kr[B] = k_per_token ? k_per_token[trow] : K;
+  };
+  auto run = [&](int pass, auto bc) {
+    constexpr int B = decltype(bc)::value;
+    const int tw = pass * TPP + wave * TPW;
+    if ((pass + 1) * TPP < T) fetch(pass + 1, std::integral_constant<int, 1 - B>());
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();  // lrow / pick rows reused
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int tb = wave * TPW + seg;
+    const int64_t t = tw + seg;
+    const bool tok_ok = t < T;
+    float lv[VPL];
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      lv[j] = pv[B][0][j];
+#pragma unroll
+      for (int sp = 1; sp < NSPLIT; ++sp) lv[j] += pv[B][sp][j];
+    }
+    if (NSPLIT > 1 && logits_out && tok_ok) {
+#pragma unroll
+      for (int j = 0; j < VPL; ++j)
+        if (j < nval) logits_out[t * E + e0 + j] = lv[j];
+    }
+    if (logit_bias) {
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) lv[j] += lb[j];
+    }
+#pragma unroll
+    for (int j = 0; j < VPL; ++j)
+      if (!tok_ok || j >= nval) lv[j] = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) lrow[tb][e0 + j] = lv[j];
+    int pid[KPL];
+    sel::select_token<LPT, VPL, MONO>(c, sl, seg, tok_ok, t, lv, nval, sb, kr[B], lrow[tb],
+                                      pick[tb], ids, weights, dev_err, pid);
+    if (tok_ok) {
+#pragma unroll
+      for (int i = 0; i < KPL; ++i) {
+        const int r = sl + i * LPT;
+        if (r < K) rid[t * K + r] = pid[i];
+      }
+    }
+  };
+  fetch(0, std::integral_constant<int, 0>());
+  for (int pass = 0; pass * TPP + wave * TPW < T; pass += 2) {  // wave-uniform
+    run(pass, std::integral_constant<int, 0>());
+    if ((pass + 1) * TPP + wave * TPW >= T) break;
+    run(pass + 1, std::integral_constant<int, 1>());
+  }
+  __syncthreads();
+
+  // dispatch of the R routes held in rid
+  const int R = T * K;
+  const int nch = (R + kWave - 1) / kWave;
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  for (int i = tid; i < nch * kSmallE; i += kSmallWaves * kWave) cbase[i / kSmallE][i % kSmallE] = 0;
+  __syncthreads();
+  const uint64_t below = lanemask_lt();
+  for (int ch = wave; ch < nch; ch += kSmallWaves) {
+    const int r = ch * kWave + lane;
+    const int e = r < R ? rid[r] : -1;
+    const uint64_t p = peer_mask(e, nbits);
+    if (e >= 0 && (p & below) == 0) cbase[ch][e] = __popcll(p);  // one leader per expert
+  }
+  __syncthreads();
+  // wavefront w: experts w, w + kSmallWaves, ...: exclusive scan over the chunks
+  for (int e = wave; e < E; e += kSmallWaves) {
+    const int v = lane < nch ? cbase[lane][e] : 0;
+    const int inc = wave_incl_scan_i32(v);
+    if (lane < nch) cbase[lane][e] = inc - v;
+    if (lane == 63) off[e] = inc;  // the expert's total, for now
+  }
+  __syncthreads();
+  if (wave == 0) {  // totals -> exclusive offsets over the experts (two per lane)
+    const int a = 2 * lane < E ? off[2 * lane] : 0;
+    const int b = 2 * lane + 1 < E ? off[2 * lane + 1] : 0;
+    const int inc = wave_incl_scan_i32(a + b);
+    __builtin_amdgcn_wave_barrier();
+    if (2 * lane < E) {
+      counts[2 * lane] = a;
+      offsets[2 * lane] = off[2 * lane] = inc - a - b;
+    }
+    if (2 * lane + 1 < E) {
+      counts[2 * lane + 1] = b;
+      offsets[2 * lane + 1] = off[2 * lane + 1] = inc - b;
+    }
+    if (lane == 63) offsets[E] = off[E] = inc;
+  }
+  __syncthreads();
+  for (int ch = wave; ch < nch; ch += kSmallWaves) {
+    const int r = ch * kWave + lane;
+    const int e = r < R ? rid[r] : -1;
+    const uint64_t p = peer_mask(e, nbits);
+    const int pos = e >= 0 ? off[e] + cbase[ch][e] + __popcll(p & below) : -1;
+    if (r < R) {
+      if (inv) inv[r] = pos;
+      if (pos >= 0) perm[pos] = r;
     }
   }
 }
@@ -204,8 +370,16 @@ void select_shape(const RouteCfg& c, int* lpt, int* vpl) {
   const bool grouped = c.n_groups > 1 && c.topk_groups < c.n_groups;
   const int G = grouped ? c.n_groups : 1;
   const bool few = (int64_t)c.T * 8 < 2048 * kWave;  // 8-lane segments: T / 8 wavefronts
+  // a batch small enough for one workgroup: the narrowest segment holding
+  // at most 8 experts per lane (more tokens per wavefront, fewer passes)
+  const bool tiny = (int64_t)c.T * c.k <= kSmallRoutes;
   int l = 64, v = 16;
-  if (few && G <= 16 && E <= 128) {
+  if (tiny && E <= 32 && G <= 4) {
+    l = 4;
+    v = E <= 4 ? 1 : E <= 8 ? 2 : E <= 16 ? 4 : 8;
+  } else if (tiny && E <= 64 && G <= 8) {
+    l = 8, v = 8;
+  } else if (few && G <= 16 && E <= 128) {
     l = 16;
     v = E <= 16 ? 1 : E <= 32 ? 2 : E <= 64 ? 4 : 8;
   } else if (E <= 16 && G <= 4) {
@@ -252,6 +426,57 @@ int select_hist_tokens(const RouteCfg& c) {
   return hist_waves(lpt) * (kWave / lpt);
 }
 
+bool small_dispatch_ok(const RouteCfg& c) {
+  if ((int64_t)c.T * c.k > kSmallRoutes || c.E > kSmallE || c.T == 0) return false;
+  int lpt, vpl;
+  select_shape(c, &lpt, &vpl);
+  return lpt <= 16 && vpl <= 8;
+}
+
+hipError_t launch_route_dispatch_small(const RouteCfg& c, const float* logits, int32_t splits,
+                                       int64_t split_stride, float* logits_out,
+                                       const float* logit_bias, const float* select_bias,
+                                       const int32_t* k_per_token, int32_t* ids,
+                                       float* weights, int32_t* dev_err, int32_t* counts,
+                                       int32_t* offsets, int32_t* perm, int32_t* inv,
+                                       hipStream_t stream) {
+  if (!small_dispatch_ok(c)) return hipErrorInvalidValue;
+  const bool grouped = c.n_groups > 1 && c.topk_groups < c.n_groups;
+  const bool mono = select_bias == nullptr && !grouped;
+  const int vec = c.E % 4 == 0 && aligned16(logits) && split_stride % 4 == 0 &&
+                  (!logit_bias || aligned16(logit_bias)) &&
+                  (!select_bias || aligned16(select_bias));
+  int lpt, vpl;
+  select_shape(c, &lpt, &vpl);
+#define MOE_SD(L_, V_, S_, M_)                                                                \
+  if (lpt == L_ && vpl == V_ && splits == S_ && mono == M_)                                   \
+    return launch(kStageSelectDispatch, route_dispatch_small_kernel<L_, V_, S_, M_>, dim3(1),  \
+                  dim3(kSmallWaves * kWave), stream, c, logits, split_stride, logits_out,     \
+                  logit_bias, select_bias, k_per_token, ids, weights, dev_err, vec, counts,  \
+                  offsets, perm, inv);
+#define MOE_SDV(L_, V_)   \
+  MOE_SD(L_, V_, 1, true) \
+  MOE_SD(L_, V_, 1, false) \
+  MOE_SD(L_, V_, 2, true) \
+  MOE_SD(L_, V_, 2, false) \
+  MOE_SD(L_, V_, 4, true) \
+  MOE_SD(L_, V_, 4, false) \
+  MOE_SD(L_, V_, 8, true) \
+  MOE_SD(L_, V_, 8, false)
+  MOE_SDV(4, 1)
+  MOE_SDV(4, 2)
+  MOE_SDV(4, 4)
+  MOE_SDV(4, 8)
+  MOE_SDV(8, 8)
+  MOE_SDV(16, 1)
+  MOE_SDV(16, 2)
+  MOE_SDV(16, 4)
+  MOE_SDV(16, 8)
+#undef MOE_SDV
+#undef MOE_SD
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_select(const RouteCfg& c, const float* logits, int32_t splits,
                          int64_t split_stride, float* logits_out, const float* logit_bias,
                          const float* select_bias, const int32_t* k_per_token, int32_t* ids,
@@ -274,6 +499,8 @@ hipError_t launch_select(const RouteCfg& c, const float* logits, int32_t splits,
   MOE_SEL(16, 2)
   MOE_SEL(16, 4)
   MOE_SEL(16, 8)
+  MOE_SEL(4, 1)
+  MOE_SEL(4, 2)
   MOE_SEL(4, 4)
   MOE_SEL(4, 8)
   MOE_SEL(8, 8)

@@ -161,19 +161,31 @@ __device__ __forceinline__ void load_vals(const float* __restrict__ row, int e0,
     if (e0 + j >= E) v[j] = fill;
 }
 
+// Selection bias of a lane's experts (zeros without one; not read when MONO).
+template <int VPL, bool MONO>
+__device__ __forceinline__ void load_sbias(const float* __restrict__ select_bias, int e0, int E,
+                                           bool vec, float (&sb)[VPL]) {
+  if (!MONO && select_bias) {
+    load_vals<VPL>(select_bias, e0, E, vec, 0.f, sb);
+  } else {
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) sb[j] = 0.f;
+  }
+}
+
 // One token's selection by a segment of LPT lanes of a wavefront.  Lane sl
 // holds experts [e0, e0 + nval), e0 = sl * VPL, in lv: logits (+ logit
-// bias), -inf past E and for a missing token (tok_ok false).  lrow: the
-// token's row of those values in LDS (the picks' logits are read back from
-// it); pick: kMaxK ints of LDS for the token.  Writes ids[t][*] and
-// weights[t][*] (trow: a valid row for the per-token k when t is past the
-// end) and leaves in pid the experts this lane wrote (ranks sl, sl + LPT,
-// ...; -1: none).  Every lane of the wavefront takes part.
+// bias), -inf past E and for a missing token (tok_ok false), and in sb their
+// selection bias (zeros without one; unused when MONO).  kraw: the token's
+// requested k (its per-token k, or k).  lrow: the token's row of lv in LDS
+// (the picks' logits are read back from it); pick: kMaxK ints of LDS for the
+// token.  Writes ids[t][*] and weights[t][*] and leaves in pid the experts
+// this lane wrote (ranks sl, sl + LPT, ...; -1: none).  Every lane of the
+// wavefront takes part.
 template <int LPT, int VPL, bool MONO>
 __device__ __forceinline__ void select_token(
-    const RouteCfg& c, int sl, int seg, bool tok_ok, int64_t t, int64_t trow,
-    const float (&lv)[VPL], int nval, bool lvec, const float* lrow, int32_t* pick,
-    const float* __restrict__ select_bias, const int32_t* __restrict__ k_per_token,
+    const RouteCfg& c, int sl, int seg, bool tok_ok, int64_t t, const float (&lv)[VPL],
+    int nval, const float (&sb)[VPL], int kraw, const float* lrow, int32_t* pick,
     int32_t* __restrict__ ids, float* __restrict__ weights, int32_t* __restrict__ dev_err,
     int (&pid)[(kMaxK + LPT - 1) / LPT]) {
   using S = Seg<LPT>;
@@ -200,18 +212,12 @@ __device__ __forceinline__ void select_token(
 #pragma unroll
     for (int j = 0; j < VPL; ++j) key[j] = (j < nval) ? ordered_key(lv[j]) : 0u;
   } else {
-    float q[VPL], b[VPL];
-    if (select_bias) {
-      load_vals<VPL>(select_bias, e0, E, lvec, 0.f, b);
-    } else {
-#pragma unroll
-      for (int j = 0; j < VPL; ++j) b[j] = 0.f;
-    }
+    float q[VPL];
 #pragma unroll
     for (int j = 0; j < VPL; ++j) {
       const float s = (c.score == kSoftmax) ? expf(lv[j] - m_all) * inv_sum_all
                                             : elementwise_score(c.score, lv[j]);
-      q[j] = (j < nval) ? s + b[j] : -INFINITY;
+      q[j] = (j < nval) ? s + sb[j] : -INFINITY;
     }
     const bool grouped = c.n_groups > 1 && c.topk_groups < c.n_groups;
     if (grouped) {
@@ -261,7 +267,7 @@ __device__ __forceinline__ void select_token(
     }
   }
 
-  int kt = k_per_token ? k_per_token[trow] : K;
+  int kt = kraw;
   if (!tok_ok) kt = 0;
   if (tok_ok && (kt < 1 || kt > K)) {
     if (sl == 0 && dev_err) atomicAdd(dev_err, 1);
@@ -298,18 +304,23 @@ __device__ __forceinline__ void select_token(
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  // weights of the picks this lane writes: ranks sl, sl + LPT, ...
+  // weights of the picks this lane writes: ranks sl, sl + LPT, ...; slots
+  // whose ranks are all >= K are skipped (wave-uniform), they hold no pick
+  const int nslots = (K + LPT - 1) / LPT;
   float pl[KPL];
 #pragma unroll
   for (int i = 0; i < KPL; ++i) {
     const int r = sl + i * LPT;
-    pid[i] = r < kt ? pick[r] : -1;
+    pid[i] = (i < nslots && r < kt) ? pick[r] : -1;
     pl[i] = pid[i] >= 0 ? lrow[pid[i]] : -INFINITY;
   }
   float w[KPL];
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) w[i] = 0.f;
   if (c.score == kSoftmax && need_full_softmax) {
 #pragma unroll
-    for (int i = 0; i < KPL; ++i) w[i] = pid[i] >= 0 ? expf(pl[i] - m_all) * inv_sum_all : 0.f;
+    for (int i = 0; i < KPL; ++i)
+      if (i < nslots) w[i] = pid[i] >= 0 ? expf(pl[i] - m_all) * inv_sum_all : 0.f;
   } else if (c.score == kSoftmax || c.score == kSoftmaxTopk) {
     // softmax restricted to the picked logits; for SOFTMAX it equals the
     // renormalised full softmax because the full denominator cancels
@@ -318,10 +329,12 @@ __device__ __forceinline__ void select_token(
     for (int i = 0; i < KPL; ++i) m = fmaxf(m, pl[i]);
     const float m_sel = S::max_f32(m);
 #pragma unroll
-    for (int i = 0; i < KPL; ++i) w[i] = pid[i] >= 0 ? expf(pl[i] - m_sel) : 0.f;
+    for (int i = 0; i < KPL; ++i)
+      if (i < nslots) w[i] = pid[i] >= 0 ? expf(pl[i] - m_sel) : 0.f;
   } else {
 #pragma unroll
-    for (int i = 0; i < KPL; ++i) w[i] = pid[i] >= 0 ? elementwise_score(c.score, pl[i]) : 0.f;
+    for (int i = 0; i < KPL; ++i)
+      if (i < nslots) w[i] = pid[i] >= 0 ? elementwise_score(c.score, pl[i]) : 0.f;
   }
   float part = 0.f;
 #pragma unroll
@@ -352,6 +365,7 @@ __device__ __forceinline__ void count_picks(const int (&pid)[(kMaxK + LPT - 1) /
   const uint64_t below = lanemask_lt();
 #pragma unroll
   for (int i = 0; i < KPL; ++i) {  // chunk i: every lane's i-th pick
+    if (i * LPT >= K) break;      // wave-uniform: no rank below K in this chunk
     const int e = (sl + i * LPT < K) ? pid[i] : -1;
     const uint64_t p = peer_mask(e, nbits);
     if (e >= 0 && (p & below) == 0) whist_w[e] += __popcll(p);
