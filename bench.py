@@ -206,11 +206,14 @@ def main():
         tok, tab = up(inp["token_ids"]), up(inp["tid2eid"])
         disp_ws = tda.dispatch_workspace_size(T, k, E)
         dws = torch.empty(max(1, disp_ws), dtype=torch.uint8, device=dev)
+        hws = torch.empty(max(1, tda.route_hash_workspace_size(T, w.d, E, k, dt, **pkw)),
+                          dtype=torch.uint8, device=dev)
 
         def step(i):  # noqa: F811 -- moe_route_hash then moe_dispatch
             tda.route_hash(tok, tab, E, x=xs[i % n_copies], W=W, score=w.score,
                            logit_bias=lb, renormalize=w.renormalize,
-                           route_scale=w.route_scale, ids=ids, weights=weights)
+                           route_scale=w.route_scale, ids=ids, weights=weights,
+                           workspace=hws)
             tda.dispatch(ids, E, counts=counts, offsets=offsets, perm=perm, inv=inv,
                          workspace=dws)
 
