@@ -26,6 +26,12 @@
 // two largest) come from a butterfly over the group's lanes when a group is
 // a power-of-two run of whole lanes, else from one segment reduction per
 // group.
+//
+// The per-token code lives in select_core.h and serves three kernels: the
+// select kernel here (optionally also counting its picks into the
+// dispatch's tile histograms), the gate kernel's fused epilogue, and the
+// one-workgroup kernel below that also performs the whole dispatch of a
+// small batch.
 #include <cstdlib>
 #include <type_traits>
 
