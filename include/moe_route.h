@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 5
+#define MOE_ABI_VERSION 6
 
 /* return codes */
 #define MOE_OK 0
@@ -238,6 +238,31 @@ int32_t moe_route_dispatch(const moe_route_params* p, const void* x, const void*
 /* Bytes of device workspace moe_route_dispatch needs for these parameters
  * (16-byte aligned x and W assumed). */
 size_t moe_route_dispatch_workspace_size(const moe_route_params* p);
+
+/*
+ * How moe_route_dispatch runs for these parameters, with x and W given
+ * (16-byte aligned when `aligned` is non-zero): host-side planning only,
+ * nothing is enqueued.  For inspection and tests.  Returns MOE_OK, or the
+ * error moe_route_dispatch would return for the parameters.
+ */
+#define MOE_PATH_SEPARATE 0    /* gate, select, then the dispatch's own kernels */
+#define MOE_PATH_SELECT_HIST 1 /* the select kernel writes the dispatch's tile histograms */
+#define MOE_PATH_FUSED 2       /* the gate kernel runs the selection on its tile's rows */
+#define MOE_PATH_SMALL 3       /* one workgroup selects and performs the whole dispatch */
+typedef struct {
+  int32_t path;                    /* MOE_PATH_* */
+  int32_t gate_bm, gate_bn;        /* gate tile: tokens x experts */
+  int32_t gate_waves;              /* wavefronts per gate workgroup (4 or 8) */
+  int32_t gate_splits;             /* K split: partial sum arrays */
+  int32_t gate_stage_bytes;        /* bytes of each tile row per stage; 0: register-staged */
+  int32_t gate_ring_depth;         /* stages of the LDS ring */
+  int32_t gate_lds_bytes;          /* LDS of the ring */
+  int32_t select_lanes;            /* lanes per token of the selection */
+  int32_t select_experts_per_lane;
+  int32_t hist_tokens;             /* tokens per dispatch tile the routing kernels count; 0: none */
+  int32_t kernels;                 /* kernels enqueued per call */
+} moe_plan_info;
+int32_t moe_route_dispatch_plan(const moe_route_params* p, int32_t aligned, moe_plan_info* out);
 
 /*
  * Per-kernel timing, for benchmarks and profiling only.

@@ -4,6 +4,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import token_dispatch_amd as tda
@@ -218,3 +219,81 @@ def test_route_dispatch_validation():
     bad = tda.make_params(64, 128, 16, 0)
     assert L.moe_route_dispatch(ctypes.byref(bad), FAKE, FAKE, None, None, None, None, FAKE, FAKE,
                                 FAKE, FAKE, FAKE, None, FAKE, n, None, None) == tda.MOE_EINVAL
+
+
+def test_plan_constants_match_binding():
+    src = open(HEADER).read()
+    consts = dict(re.findall(r"#define (MOE_\w+) \(?(-?\d+)\)?", src))
+    for i, name in enumerate(tda.PATHS):
+        assert int(consts["MOE_PATH_" + name.upper()]) == i
+    assert ctypes.sizeof(tda.PlanInfo) == 4 * len(tda.PLAN_FIELDS)
+    for i, name in enumerate(tda.STAGES):
+        assert int(consts["MOE_STAGE_" + name.upper()]) == i
+    assert int(consts["MOE_NUM_STAGES"]) == len(tda.STAGES)
+
+
+WORKLOAD_PLANS = {  # path, kernels per moe_route_dispatch call
+    "mixtral": ("small", 2),
+    "qwen3_dynk": ("select_hist", 3),
+    "dsv3_grouped": ("separate", 4),
+    "dsv4": ("separate", 5),
+    "gptoss_skew": ("fused", 2),
+}
+
+
+@pytest.mark.parametrize("name", sorted(WORKLOAD_PLANS))
+def test_workload_plans(name):
+    """The kernel sequence moe_route_dispatch takes for each workload shape."""
+    import workloads as wl
+    w = wl.WORKLOADS[name]
+    kw = dict(score=w.score, n_groups=w.n_groups, topk_groups=w.topk_groups,
+              group_score=w.group_score if w.n_groups > 1 else "max",
+              renormalize=w.renormalize, route_scale=w.route_scale)
+    plan = tda.route_dispatch_plan(w.T, w.d, w.E, w.k, 1 if w.dtype == "bf16" else 0, **kw)
+    assert (plan["path"], plan["kernels"]) == WORKLOAD_PLANS[name], plan
+    # unaligned x or W: the register-staged gate, no K split, no fused selection
+    plan_u = tda.route_dispatch_plan(w.T, w.d, w.E, w.k, 1 if w.dtype == "bf16" else 0,
+                                     aligned=False, **kw)
+    assert plan_u["gate_stage_bytes"] == 0 and plan_u["gate_splits"] == 1
+    assert plan_u["path"] != "fused"
+
+
+def test_planner_invariants_on_random_shapes():
+    """Every plan the host chooses is one the kernels are built for: the ring
+    within 144 KB of LDS, tiles split into whole 16 x 16 blocks per wave,
+    eight-wave tiles only for bf16, a K split of 1-8 that leaves every split
+    some of K, fused selection only on whole-row unsplit tiles of <= 128
+    experts, the small path only up to 2048 routes, and dispatch tiles the
+    placement kernel takes."""
+    rng = np.random.default_rng(11)
+    paths = set()
+    for _ in range(600):
+        E = int(rng.choice([4, 8, 16, 30, 64, 100, 128, 160, 256, 384, 512, 1000]))
+        k = int(rng.integers(1, min(E, 32) + 1))
+        T = int(rng.choice([1, 7, 100, 255, 1000, 4096, 8192, 16384, 65536, 200000]))
+        d = int(rng.choice([8, 64, 512, 1024, 2048, 2880, 4096, 7168]))
+        dt = int(rng.integers(0, 2))
+        G = int(rng.choice([g for g in (1, 2, 4, 8) if E % g == 0 and g <= E]))
+        kw = dict(score="sigmoid", n_groups=G, topk_groups=G,
+                  group_score="max", renormalize=True, route_scale=1.0)
+        plan = tda.route_dispatch_plan(T, d, E, k, dt, **kw)
+        paths.add(plan["path"])
+        bm, bn, waves, S = plan["gate_bm"], plan["gate_bn"], plan["gate_waves"], plan["gate_splits"]
+        assert waves in (4, 8) and (waves == 4 or dt == 1), plan
+        assert bm % 32 == 0 and bn % 32 == 0, plan
+        assert S in (1, 2, 4, 8), plan
+        if plan["gate_stage_bytes"]:
+            rb, ns = plan["gate_stage_bytes"], plan["gate_ring_depth"]
+            assert rb in (64, 128, 256, 512) and 2 <= ns <= 8, plan
+            assert plan["gate_lds_bytes"] == ns * (bm + bn) * rb <= 144 * 1024, plan
+            assert (d * (2 if dt else 4) + rb - 1) // rb >= S, plan  # every split has K
+        if plan["path"] == "fused":
+            assert S == 1 and bn >= E and E <= 128 and dt == 1, plan
+        if plan["path"] == "small":
+            assert T * k <= 2048 and E <= 128 and plan["kernels"] == 2, plan
+        if plan["hist_tokens"]:
+            assert plan["hist_tokens"] * k in (256, 512, 1024, 2048), plan
+            assert -(-T * k // (plan["hist_tokens"] * k)) * E <= 32 * 1024, plan
+        assert plan["select_lanes"] in (4, 8, 16, 64), plan
+        assert plan["select_lanes"] * plan["select_experts_per_lane"] >= E, plan
+    assert {"small", "separate", "select_hist", "fused"} <= paths, paths

@@ -21,7 +21,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe_route.so")
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EDEVICE = 0, -1, -2, -3
 MAX_EXPERTS, MAX_K, MAX_GROUPS = 1024, 32, 64
 SCORES = {"softmax": 0, "sigmoid": 1, "sqrt_softplus": 2, "softmax_topk": 3}
@@ -30,7 +30,12 @@ EXPORTS = ("moe_route", "moe_route_workspace_size", "moe_route_hash",
            "moe_route_hash_workspace_size",
            "moe_dispatch_workspace_size", "moe_dispatch",
            "moe_route_dispatch", "moe_route_dispatch_workspace_size",
-           "moe_profile_enable", "moe_profile_read", "moe_last_error", "moe_abi_version")
+           "moe_route_dispatch_plan", "moe_profile_enable", "moe_profile_read",
+           "moe_last_error", "moe_abi_version")
+PATHS = ("separate", "select_hist", "fused", "small")
+PLAN_FIELDS = ("path", "gate_bm", "gate_bn", "gate_waves", "gate_splits", "gate_stage_bytes",
+               "gate_ring_depth", "gate_lds_bytes", "select_lanes", "select_experts_per_lane",
+               "hist_tokens", "kernels")
 STAGES = ("gate", "select", "hash", "disp_hist", "disp_scan", "disp_scatter", "gate_select",
           "select_dispatch")
 
@@ -79,6 +84,8 @@ def lib() -> ctypes.CDLL:
         L.moe_route_dispatch.restype = i32
         L.moe_route_dispatch_workspace_size.argtypes = [P]
         L.moe_route_dispatch_workspace_size.restype = ctypes.c_size_t
+        L.moe_route_dispatch_plan.argtypes = [P, i32, ctypes.POINTER(PlanInfo)]
+        L.moe_route_dispatch_plan.restype = i32
         L.moe_last_error.argtypes = []
         L.moe_last_error.restype = ctypes.c_char_p
         L.moe_profile_enable.argtypes = [i32]
@@ -219,6 +226,24 @@ def route_dispatch_workspace_size(T, d, E, k, dtype=1, **kw) -> int:
     """Device bytes moe_route_dispatch needs for these shapes."""
     p = make_params(T, d, E, k, dtype, **kw)
     return int(lib().moe_route_dispatch_workspace_size(ctypes.byref(p)))
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int32) for name in PLAN_FIELDS]
+
+
+def route_dispatch_plan(T, d, E, k, dtype=1, aligned=True, **kw) -> dict:
+    """How moe_route_dispatch runs for these shapes (host-side planning only):
+    {"path": "separate" | "select_hist" | "fused" | "small", gate tile,
+    waves, splits, stage bytes, ring depth and LDS, selection lanes and
+    experts per lane, tokens per counted dispatch tile, kernels per call}."""
+    p = make_params(T, d, E, k, dtype, **kw)
+    info = PlanInfo()
+    _check(lib().moe_route_dispatch_plan(ctypes.byref(p), int(bool(aligned)),
+                                         ctypes.byref(info)))
+    out = {name: int(getattr(info, name)) for name in PLAN_FIELDS}
+    out["path"] = PATHS[out["path"]]
+    return out
 
 
 def route_dispatch(x: Optional[torch.Tensor], W: Optional[torch.Tensor], k: int, *,

@@ -327,6 +327,11 @@ hipError_t launch_dispatch_from_hist(const int32_t* ids, int64_t R, int32_t E,
   }
 }
 
+int dispatch_kernels(int64_t R, int32_t E) {
+  if (R <= 0) return 1;  // zero counts and offsets only
+  return fused_cpw(R, E) ? 2 : 3;
+}
+
 size_t dispatch_workspace_bytes(int64_t R, int32_t E) {
   if (R <= 0) return 0;  // no routes: only counts and offsets are written
   if (const int cpw = fused_cpw(R, E)) {

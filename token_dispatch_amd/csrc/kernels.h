@@ -142,6 +142,7 @@ hipError_t launch_dispatch_from_hist(const int32_t* ids, int64_t R, int32_t E,
 
 // Dispatch: tile histograms -> scan -> stable scatter.
 size_t dispatch_workspace_bytes(int64_t R, int32_t E);
+int dispatch_kernels(int64_t R, int32_t E);  // kernels launch_dispatch enqueues
 hipError_t launch_dispatch(const int32_t* ids, int64_t R, int32_t E,
                            int32_t* counts, int32_t* offsets, int32_t* perm,
                            int32_t* inv, void* workspace, int32_t* dev_err,

@@ -369,6 +369,42 @@ int32_t moe_route_dispatch(const moe_route_params* p, const void* x, const void*
   return MOE_OK;
 }
 
+int32_t moe_route_dispatch_plan(const moe_route_params* p, int32_t aligned,
+                                moe_plan_info* out) {
+  if (!out) return fail(MOE_EINVAL, "out is required");
+  int32_t rc = check_route_params(p, true);
+  if (rc != MOE_OK) return rc;
+  const int64_t R = (int64_t)p->T * p->k;
+  if (R > kI32Max) return fail(MOE_EUNSUPPORTED, "T*k must be below 2^31");
+  *out = moe_plan_info{};
+  const moe::RouteCfg c = to_cfg(p);
+  const moe::GatePlan g = moe::plan_gate(p->T, p->d, p->E, p->dtype, aligned != 0, true);
+  out->gate_bm = g.bm;
+  out->gate_bn = g.bn;
+  out->gate_waves = g.wm * g.wn;
+  out->gate_splits = g.pipe ? g.splits : 1;
+  out->gate_stage_bytes = g.pipe ? g.rb : 0;
+  out->gate_ring_depth = g.pipe ? g.ns : 2;
+  out->gate_lds_bytes = g.pipe ? g.ns * (g.bm + g.bn) * g.rb : 0;
+  moe::select_shape(c, &out->select_lanes, &out->select_experts_per_lane);
+  if (p->T == 0) {
+    out->path = MOE_PATH_SEPARATE;
+    out->kernels = 1;  // the dispatch writes zero counts and offsets
+    return MOE_OK;
+  }
+  if (moe::small_dispatch_ok(c) && !std::getenv("MOE_NO_SMALL_DISPATCH")) {
+    out->path = MOE_PATH_SMALL;
+    out->kernels = 2;
+    return MOE_OK;
+  }
+  const int n = fused_hist_tokens(p, true, aligned != 0);
+  out->hist_tokens = n;
+  const bool fused = moe::gate_select_tokens(g, p->dtype, c) > 0;
+  out->path = fused ? MOE_PATH_FUSED : (n > 0 ? MOE_PATH_SELECT_HIST : MOE_PATH_SEPARATE);
+  out->kernels = (fused ? 1 : 2) + (n > 0 ? 1 : moe::dispatch_kernels(R, p->E));
+  return MOE_OK;
+}
+
 size_t moe_route_workspace_size(const moe_route_params* p) {
   if (check_route_params(p, true) != MOE_OK || p->T == 0) return 0;
   return route_ws_bytes(p);
