@@ -139,7 +139,8 @@ def test_route_hash_validation():
 
 def test_dispatch_validation_and_workspace_size():
     L = tda.lib()
-    assert tda.dispatch_workspace_size(100, 8, 64) >= 2 * 64 * 4
+    # two tiles of 512 routes: a [2][64] histogram of 16-bit counts
+    assert tda.dispatch_workspace_size(100, 8, 64) >= 2 * 64 * 2
     assert tda.dispatch_workspace_size(0, 8, 64) == 0
     assert tda.dispatch_workspace_size(-1, 8, 64) == 0
     ws = tda.dispatch_workspace_size(100, 8, 64)
@@ -171,16 +172,17 @@ def test_dispatch_rejects_unaligned_workspace():
 @pytest.mark.parametrize("T,k,E", [(4096, 16, 128), (65536, 4, 128), (16384, 6, 384),
                                    (8192, 8, 256), (256, 2, 8), (70000, 30, 1024), (5, 3, 7)])
 def test_dispatch_workspace_size_per_path(T, k, E):
-    # two-kernel path: one tile-major histogram of at most 32 Ki counts (the
-    # smallest tiles of 512, 1024 or 2048 routes that fit), unless those
-    # tiles are fewer than 128 while 512-route tiles are at least 128;
-    # otherwise tile histograms, tile bases and totals (tiles of 512 routes)
+    # two-kernel path (E % 8 == 0): one tile-major histogram of at most 32 Ki
+    # 16-bit counts (the smallest tiles of 512, 1024 or 2048 routes that
+    # fit), unless those tiles are fewer than 128 while 512-route tiles are
+    # at least 128; otherwise 32-bit tile histograms, tile bases and totals
+    # (tiles of 512 routes)
     n = tda.dispatch_workspace_size(T, k, E)
     R = T * k
     fits = [-(-R // t) for t in (512, 1024, 2048) if -(-R // t) * E <= 32768]
-    two = E % 4 == 0 and fits and not (fits[0] < 128 and -(-R // 512) >= 128)
+    two = E % 8 == 0 and fits and not (fits[0] < 128 and -(-R // 512) >= 128)
     if two:
-        assert n == fits[0] * E * 4
+        assert n == fits[0] * E * 2
     else:
         nt = -(-R // 512)
         assert n == (2 * nt + 1) * E * 4
@@ -195,13 +197,14 @@ def test_route_dispatch_workspace_size():
         route = (route + 255) // 256 * 256
         n = tda.route_dispatch_workspace_size(T, d, E, k)
         disp = tda.dispatch_workspace_size(T, k, E)
-        assert n >= route and (n == route + disp or (n - route) % (4 * E) == 0), (T, n)
+        assert n >= route and (n == route + disp or (n - route) % (2 * E) == 0), (T, n)
     # Qwen3-like shape: the gate hand-off holds whole T x E partial arrays
     # (one per K split); then 16-token tiles of 256 routes -> 256 histogram rows
+    # of 128 16-bit counts
     route = tda.route_workspace_size(4096, 2048, 128, 16)
     assert route % (4096 * 128 * 4) == 0 and 1 <= route // (4096 * 128 * 4) <= 8
     assert tda.route_dispatch_workspace_size(4096, 2048, 128, 16) == \
-        (route + 255) // 256 * 256 + 256 * 128 * 4
+        (route + 255) // 256 * 256 + 256 * 128 * 2
 
 
 def test_route_dispatch_validation():

@@ -108,7 +108,10 @@ def dispatch_case(ids_np, E, with_inv=True):
 
 @pytest.mark.parametrize("T,k,E", [(1, 1, 1), (3, 2, 8), (1023, 1, 8), (1024, 1, 8), (1025, 1, 8),
                                    (4096, 16, 128), (8192, 8, 256), (16384, 6, 384),
-                                   (2000, 3, 1024), (65536, 4, 128), (70000, 30, 1024)])
+                                   (2000, 3, 1024), (65536, 4, 128), (70000, 30, 1024),
+                                   # 16-bit histograms: 64 groups of 8 experts, and
+                                   # group counts that do not divide a wavefront
+                                   (3000, 8, 512), (5000, 3, 40), (50000, 6, 24)])
 def test_dispatch_random(T, k, E):
     rng = np.random.default_rng([T, k, E])
     ids = rng.integers(0, E, size=(T, k)).astype(np.int32)

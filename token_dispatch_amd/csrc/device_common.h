@@ -74,11 +74,16 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
-// Mask of the lanes whose id (>= 0) equals this lane's id, without atomics:
-// one ballot per bit of the id narrows the set (lanes with id < 0 get 0s).
-__device__ __forceinline__ uint64_t peer_mask(int e, int nbits) {
+// Mask of the lanes whose id (0 <= id < 2^NB) equals this lane's id,
+// without atomics: one ballot per bit of the id narrows the set (meaningless
+// for a lane whose id is < 0; callers test that).  A fixed bit count keeps
+// the code straight-line: bits above an id's width are 0 in every valid id
+// and leave the mask unchanged.
+template <int NB>
+__device__ __forceinline__ uint64_t peer_mask(int e) {
   uint64_t p = __ballot(e >= 0);
-  for (int b = 0; b < nbits; ++b) {
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
     const bool bit = (e >> b) & 1;
     const uint64_t m = __ballot(bit);
     p &= bit ? m : ~m;

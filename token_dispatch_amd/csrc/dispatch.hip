@@ -1,28 +1,32 @@
 // Token dispatch on gfx950: group routes r = t*k_stride + j by expert with a
 // stable counting sort (counts, exclusive-scan offsets, permutation, inverse).
 //
-// Routes are cut into tiles of 4 waves x CPW chunks of 64 lanes (512, 1024 or
-// 2048 routes).  Lanes that hold the same expert id ("peers") are found
-// without atomics: one ballot per bit of the id narrows each lane's peer
-// mask, so a chunk of 64 routes costs ceil(log2 E) ballots.  A lane's rank
-// among its peers is the popcount of the peers below it, and the lowest peer
-// (the leader) alone updates the wave's own LDS row for that expert.
+// Routes are cut into tiles of 256 to 2048 routes, chunks of 64 lanes.
+// Lanes that hold the same expert id ("peers") are found without atomics:
+// one ballot per bit of the id narrows each lane's peer mask, so a chunk of
+// 64 routes costs ceil(log2 E) ballots.  A lane's rank among its peers is
+// the popcount of the peers below it, and the lowest peer (the leader)
+// alone updates the wave's own LDS row for that expert.
 //
 // Two kernels when the tile histograms are small (tiles x E <= 32 Ki
-// counts, the tile size grown to get there):
-//  1. histogram: per-tile, per-expert counts -> tile_hist[tile][e].
-//  2. scatter: every workgroup reads the whole (L2-resident) histogram once,
+// counts, E % 8 == 0, the tile size grown to get there):
+//  1. histogram: per-tile, per-expert counts -> tile_hist[tile][e], 16-bit
+//     (or written by the routing kernels themselves, see kernels.h).
+//  2. placement: every workgroup reads the whole (L2-resident) histogram,
 //     with all loads in flight together, and forms each expert's total and
 //     its count in earlier tiles; scans the totals over experts (offsets;
-//     workgroup 0 writes counts and offsets); recounts its tile per wave and
+//     workgroup 0 writes counts and offsets); recounts its tile (up to 16
+//     waves of one chunk, keeping each route's offset inside its wave) and
 //     places route r at offsets[e] + (earlier tiles) + (earlier waves) +
-//     (earlier chunks) + rank.
-// Three kernels otherwise (tiles of 512): the histogram as tile_hist[e][tile],
-// one wave per expert scanning its counts over tiles (exclusive) ->
-// tile_base[e][tile] and totals[e], then the same scatter reading those.
-// Positions rise with r inside each expert and do not depend on how
-// workgroups are scheduled; integer sums make every path exact.
+//     (offset in the wave).
+// Three kernels otherwise (tiles of 512): the histogram as 32-bit
+// tile_hist[e][tile], one wave per expert scanning its counts over tiles
+// (exclusive) -> tile_base[e][tile] and totals[e], then the same placement
+// reading those.  Positions rise with r inside each expert and do not
+// depend on how workgroups are scheduled; integer sums make every path
+// exact.
 #include <cstdlib>
+#include <type_traits>
 
 #include "device_common.h"
 #include "kernels.h"
@@ -35,23 +39,34 @@ constexpr int kThreads = kWaves * kWave;
 constexpr int kChunksPerWave = 2;                       // three-kernel path
 constexpr int kTile = kWaves * kChunksPerWave * kWave;  // 512 routes per tile
 constexpr int kMaxE = 1024;
+constexpr int kIdBits = 10;                             // bits of an expert id below kMaxE
+
+// Ballots per peer mask: the bits of the largest id (fewer instructions for
+// small E; the kernels take it as a template argument).
+int id_bits(int32_t E) { return E <= 128 ? 7 : E <= 256 ? 8 : kIdBits; }
 constexpr int kFusedMaxCounts = 32 * 1024;              // tiles x E, two-kernel path
 constexpr int kFusedBatch = 16;                         // 16-byte loads in flight per thread
 constexpr int kScanWaves = 16;                          // experts per scan workgroup
 constexpr int kScanPrefetch = 8;                        // chunks of 64 tiles in registers
 
-// This wave's CPW chunks of 64 routes starting at r0 (ids >= E
-// count as errors and become -1).  All loads are issued before any is used:
-// clamped addresses, validity applied afterwards.
+// This wave's CPW chunks of 64 routes starting at r0: issue_chunks issues
+// the loads (clamped addresses, so that other loads can follow before any
+// is used), check_chunks applies validity (routes past R and ids >= E
+// become -1; the latter count as errors).
 template <int CPW>
-__device__ __forceinline__ void load_chunks(const int32_t* __restrict__ ids, int64_t r0,
-                                            int64_t R, int E, int (&e)[CPW], int* err) {
+__device__ __forceinline__ void issue_chunks(const int32_t* __restrict__ ids, int64_t r0,
+                                             int64_t R, int (&e)[CPW]) {
   const int lane = __lane_id();
 #pragma unroll
   for (int ch = 0; ch < CPW; ++ch) {
     const int64_t r = r0 + ch * kWave + lane;
     e[ch] = ids[r < R ? r : R - 1];
   }
+}
+template <int CPW>
+__device__ __forceinline__ void check_chunks(int64_t r0, int64_t R, int E, int (&e)[CPW],
+                                             int* err) {
+  const int lane = __lane_id();
 #pragma unroll
   for (int ch = 0; ch < CPW; ++ch) {
     const int64_t r = r0 + ch * kWave + lane;
@@ -62,24 +77,32 @@ __device__ __forceinline__ void load_chunks(const int32_t* __restrict__ ids, int
     }
   }
 }
-
-// Count this wave's chunks into its LDS row.
 template <int CPW>
-__device__ __forceinline__ void count_chunks(const int (&e)[CPW], int nbits, int32_t* row) {
+__device__ __forceinline__ void load_chunks(const int32_t* __restrict__ ids, int64_t r0,
+                                            int64_t R, int E, int (&e)[CPW], int* err) {
+  issue_chunks<CPW>(ids, r0, R, e);
+  check_chunks<CPW>(r0, R, E, e, err);
+}
+
+// Count this wave's chunks into its LDS row (ids < 2^NB).
+template <int CPW, int NB>
+__device__ __forceinline__ void count_chunks(const int (&e)[CPW], int32_t* row) {
   const uint64_t below = lanemask_lt();
 #pragma unroll
   for (int ch = 0; ch < CPW; ++ch) {
-    const uint64_t p = peer_mask(e[ch], nbits);
+    const uint64_t p = peer_mask<NB>(e[ch]);
     if (e[ch] >= 0 && (p & below) == 0) row[e[ch]] += __popcll(p);
   }
 }
 
-// Per-tile histogram; tile-major (tile_hist[tile][e]) for the two-kernel
-// path, expert-major (tile_hist[e][tile]) for the tile scan.
-template <int CPW, bool TILE_MAJOR>
+// Per-tile histogram; tile-major 16-bit counts (tile_hist[tile][e]) for the
+// two-kernel path, expert-major 32-bit counts (tile_hist[e][tile]) for the
+// tile scan.
+template <int CPW, bool TILE_MAJOR, int NB>
 __global__ __launch_bounds__(kThreads) void disp_hist_kernel(
-    const int32_t* __restrict__ ids, int64_t R, int E, int nbits, int nt,
-    int32_t* __restrict__ tile_hist, int32_t* __restrict__ dev_err) {
+    const int32_t* __restrict__ ids, int64_t R, int E, int nt,
+    std::conditional_t<TILE_MAJOR, hist_t, int32_t>* __restrict__ tile_hist,
+    int32_t* __restrict__ dev_err) {
   __shared__ int32_t wh[kWaves][kMaxE];
   const int tid = threadIdx.x, wave = tid >> 6;
   int err = 0;
@@ -88,11 +111,15 @@ __global__ __launch_bounds__(kThreads) void disp_hist_kernel(
                    E, ev, &err);
   for (int e = tid & 63; e < E; e += kWave) wh[wave][e] = 0;
   __syncthreads();
-  count_chunks<CPW>(ev, nbits, wh[wave]);
+  count_chunks<CPW, NB>(ev, wh[wave]);
   __syncthreads();
-  for (int e = tid; e < E; e += kThreads)
-    tile_hist[TILE_MAJOR ? (int64_t)blockIdx.x * E + e : (int64_t)e * nt + blockIdx.x] =
-        wh[0][e] + wh[1][e] + wh[2][e] + wh[3][e];
+  for (int e = tid; e < E; e += kThreads) {
+    const int n = wh[0][e] + wh[1][e] + wh[2][e] + wh[3][e];
+    if constexpr (TILE_MAJOR)
+      tile_hist[(int64_t)blockIdx.x * E + e] = (hist_t)n;
+    else
+      tile_hist[(int64_t)e * nt + blockIdx.x] = n;
+  }
   err = wave_sum_i32(err);
   if ((tid & 63) == 0 && err && dev_err) atomicAdd(dev_err, err);
 }
@@ -125,72 +152,181 @@ __global__ __launch_bounds__(kScanWaves * kWave) void disp_tile_scan_kernel(
   if (lane == 0) totals[e] = carry;
 }
 
-// Stable placement.  FUSED: totals and earlier-tile counts come from the
-// tile-major histogram (tile_hist[nt][E], E % 4 == 0, nt * E <=
-// kFusedMaxCounts); otherwise from tile_base[e][tile] and totals[e].
-template <int CPW, bool FUSED>
-__global__ __launch_bounds__(kThreads) void disp_scatter_kernel(
-    const int32_t* __restrict__ ids, int64_t R, int E, int nbits, int nt,
-    const int32_t* __restrict__ tile_hist, const int32_t* __restrict__ tile_base,
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+// Sum over aligned groups of Q lanes (Q = 1, 2, 4, 8 or 16, the same in the
+// whole wave) inside 16-lane DPP rows: quad_perm [1,0,3,2] and [2,3,0,1],
+// then row_half_mirror and row_mirror pair each partial sum with the one
+// of the other half; every lane of a group ends with the group's sum.
+__device__ __forceinline__ int group_sum_i32(int v, int Q) {
+  if (Q >= 2) v += dpp_i32<0xB1>(v);
+  if (Q >= 4) v += dpp_i32<0x4E>(v);
+  if (Q >= 8) v += dpp_i32<0x141>(v);
+  if (Q >= 16) v += dpp_i32<0x140>(v);
+  return v;
+}
+
+// Sum over the lanes l' = l (mod G) of a wave, G = 1, 2, 4, ..., 64: DPP
+// row rotations by 1, 2, 4, 8 fold the lanes of a 16-lane row, then
+// permlane16_swap and permlane32_swap (each lane receives the other row's,
+// or the other half's, value in one of the two results) fold the four rows.
+template <int G>
+__device__ __forceinline__ int lanes_sum_i32(int v) {
+  if constexpr (G <= 1) v += dpp_i32<0x121>(v);  // row_ror:1
+  if constexpr (G <= 2) v += dpp_i32<0x122>(v);  // row_ror:2
+  if constexpr (G <= 4) v += dpp_i32<0x124>(v);  // row_ror:4
+  if constexpr (G <= 8) v += dpp_i32<0x128>(v);  // row_ror:8
+  if constexpr (G <= 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = r[0] + r[1];
+  }
+  if constexpr (G <= 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    v = r[0] + r[1];
+  }
+  return v;
+}
+template <int G>
+__device__ __forceinline__ void lanes_sum_all(int (&a)[8], int (&b)[8]) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    a[c] = lanes_sum_i32<G>(a[c]);
+    b[c] = lanes_sum_i32<G>(b[c]);
+  }
+}
+
+// Stable placement of tiles of TILE routes by WAVES waves (one chunk of 64
+// routes per wave up to 16 waves, then CPW chunks per wave; a wave past the
+// tile holds no routes).  FUSED: totals and earlier-tile counts come from
+// the tile-major histogram (tile_hist[nt][E] 16-bit counts, E % 8 == 0, nt *
+// E <= kFusedMaxCounts); otherwise from tile_base[e][tile] and totals[e].
+// NB: bits of the ballot peer masks (ids < 2^NB).  These kernels run for a
+// few microseconds, so their cost is mostly latency: one round trip for all
+// loads, straight-line code (branches and runtime loops cost instruction
+// fetches), short LDS chains.
+template <int WAVES, int TILE, bool FUSED, int NB>
+__global__ __launch_bounds__(WAVES * kWave) void disp_scatter_kernel(
+    const int32_t* __restrict__ ids, int64_t R, int E, int nt,
+    const hist_t* __restrict__ tile_hist, const int32_t* __restrict__ tile_base,
     const int32_t* __restrict__ totals, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
-  __shared__ int32_t wh[kWaves][kMaxE];
+  constexpr int NT = WAVES * kWave;
+  static_assert(NT >= kMaxE / 4, "offsets scan: 4 experts per thread");
+  __shared__ int32_t wh[WAVES][kMaxE];
   __shared__ int32_t off[kMaxE];
   __shared__ int32_t tot[FUSED ? kMaxE : 1];
-  __shared__ int32_t wsum[kWaves];
+  __shared__ int32_t wsum[WAVES];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int tile = blockIdx.x;
 
+  constexpr int CPW = TILE / (WAVES * kWave) > 0 ? TILE / (WAVES * kWave) : 1;
+  static_assert(TILE % (CPW * kWave) == 0 && TILE / (CPW * kWave) <= WAVES, "tile shape");
+  const bool routes = wave * CPW * kWave < TILE;  // wave-uniform
   int err = 0;
   int ev[CPW];
-  const int64_t r0 = (int64_t)tile * (kWaves * CPW * kWave) + wave * (CPW * kWave);
-  if (tile < nt) load_chunks<CPW>(ids, r0, R, E, ev, &err);
+#pragma unroll
+  for (int ch = 0; ch < CPW; ++ch) ev[ch] = -1;
+  const int64_t r0 = (int64_t)tile * TILE + wave * (CPW * kWave);
+  if (tile < nt && routes) issue_chunks<CPW>(ids, r0, R, ev);  // checked after the counts' loads
 
   if constexpr (FUSED) {
-    // Thread (g, p) owns experts 4g .. 4g+3 and tiles p, p + P, p + 2P, ...
-    // (P = 1024 / E threads per expert group): 16-byte loads, 16 in flight,
-    // register sums of all tiles and of the tiles before this one, then the
-    // P partial sums of each expert added through LDS (wh rows 0 and 1).
-    using i32x4 = int __attribute__((ext_vector_type(4)));
-    const int G = E / 4, P = kMaxE / E;
+    // Every workgroup reads all nt x E counts (from L2), so this read is
+    // most of the kernel: neighbouring lanes load neighbouring 16 bytes of a
+    // row (the loads coalesce) and the arithmetic per load is kept small.
+    // A 16-byte load holds the counts of 8 experts (group g), two per dword.
+    // The first RW waves read (RW * 64 threads, 16 rows each at 256 x 128
+    // counts: the per-thread work after the loads is paid by few threads).
+    // Thread (g, p), g = tid % G: rows p, p + P, p + 2P, ... (P = RW*64 / G
+    // row lanes), B loads in flight.  Within a batch the dwords are added as
+    // they are (at most 16 counts of at most 2048 per half: no carry
+    // between the halves) and the sum over rows before this tile is the
+    // running sum taken at the last such row (rows rise within a thread);
+    // the halves are split once per batch.  When G divides 64 the lanes of
+    // one group in a wave can be folded together in registers (one partial
+    // set per wave); otherwise every row lane is a set.  J threads per
+    // expert then add the NS sets from LDS.
+    using u32x4 = uint32_t __attribute__((ext_vector_type(4)));
+    constexpr int B = kFusedBatch, RW = 4;
+    static_assert(B * 2048 < 65536, "packed 16-bit sums per batch");
+    const int G = E / 8, P = RW * kWave / G;  // G <= kMaxE / 8 <= RW * 64 / 2
     const int g = tid % G, p = tid / G;
-    i32x4 all = {0, 0, 0, 0}, before = {0, 0, 0, 0};
-    if (p < P) {
-      const i32x4* src = reinterpret_cast<const i32x4*>(tile_hist) + g;
-      for (int t0 = p; t0 < nt; t0 += kFusedBatch * P) {
-        i32x4 v[kFusedBatch];
+    // fold in registers when few threads per expert would add the sets
+    // (4-wave tiles); with 16 waves the LDS sum over 8 threads per expert is
+    // cheaper (measured)
+    const bool fold = (G & (G - 1)) == 0 && G <= kWave && 4 * E > NT;
+    const int NS = fold ? RW : P, set = fold ? wave : p;
+    int all[8], before[8];
 #pragma unroll
-        for (int i = 0; i < kFusedBatch; ++i) {
-          const int t = t0 + i * P;
-          v[i] = src[(int64_t)(t < nt ? t : 0) * G];  // tile 0 always exists
+    for (int c = 0; c < 8; ++c) all[c] = before[c] = 0;
+    if (p < P) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(tile_hist) + g;
+      for (int t0 = p; t0 < nt; t0 += B * P) {
+        u32x4 v[B];
+#pragma unroll
+        for (int i = 0; i < B; ++i)  // clamped rows: no branches between the loads
+          v[i] = src[(int64_t)min(t0 + i * P, nt - 1) * G];
+        u32x4 pa = {0, 0, 0, 0}, pb = {0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < B; ++i) {
+          if (t0 + i * P < nt) pa += v[i];
+          if (t0 + i * P < tile) pb = pa;
         }
 #pragma unroll
-        for (int i = 0; i < kFusedBatch; ++i) {
-          const int t = t0 + i * P;
-          if (t < nt) all += v[i];
-          if (t < tile) before += v[i];
+        for (int c = 0; c < 4; ++c) {
+          all[2 * c] += (int)(pa[c] & 0xFFFFu);
+          all[2 * c + 1] += (int)(pa[c] >> 16);
+          before[2 * c] += (int)(pb[c] & 0xFFFFu);
+          before[2 * c + 1] += (int)(pb[c] >> 16);
         }
       }
     }
-    int32_t* part_all = wh[0];     // [P][E], P * E <= kMaxE
-    int32_t* part_before = wh[1];
-    if (p < P)
-      for (int c = 0; c < 4; ++c) {
-        part_all[p * E + 4 * g + c] = all[c];
-        part_before[p * E + 4 * g + c] = before[c];
+    if (fold && wave < RW) {  // one branch on G, then straight-line code
+      switch (G) {
+        case 1: lanes_sum_all<1>(all, before); break;
+        case 2: lanes_sum_all<2>(all, before); break;
+        case 4: lanes_sum_all<4>(all, before); break;
+        case 8: lanes_sum_all<8>(all, before); break;
+        case 16: lanes_sum_all<16>(all, before); break;
+        case 32: lanes_sum_all<32>(all, before); break;
+        default: break;  // 64: one lane per group
+      }
+    }
+    // set partial sums: [NS][pitch] each (NS * E * 2 <= WAVES * kMaxE); a
+    // pitch of E + 1 where it fits spreads the J readers of one expert over
+    // the LDS banks
+    int J = 1;
+    while (J < 16 && 2 * J <= NS && 2 * E * J <= NT) J *= 2;
+    const int pitch = J > 1 && NS * (E + 1) * 2 <= WAVES * kMaxE ? E + 1 : E;
+    int32_t* part_all = &wh[0][0];
+    int32_t* part_before = part_all + NS * pitch;
+    if (fold ? wave < RW && lane < G : p < P)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        part_all[set * pitch + 8 * g + c] = all[c];
+        part_before[set * pitch + 8 * g + c] = before[c];
       }
     __syncthreads();
-    for (int e = tid; e < E; e += kThreads) {
+    for (int i0 = 0; i0 < E * J; i0 += NT) {  // the same trip count in every lane
+      const int idx = i0 + tid, e = idx / J, j = idx % J;
       int a = 0, b = 0;
-      for (int q = 0; q < P; ++q) {
-        a += part_all[q * E + e];
-        b += part_before[q * E + e];
+      if (e < E)
+        for (int s2 = j; s2 < NS; s2 += J) {
+          a += part_all[s2 * pitch + e];
+          b += part_before[s2 * pitch + e];
+        }
+      a = group_sum_i32(a, J);
+      b = group_sum_i32(b, J);
+      if (e < E && j == 0) {
+        tot[e] = a;
+        off[e] = b;
       }
-      tot[e] = a;
-      off[e] = b;
     }
     __syncthreads();
   }
+
+  if (tile < nt) check_chunks<CPW>(r0, R, E, ev, &err);
 
   // offsets: exclusive scan of totals over experts (4 experts per thread)
   int t4[4], s = 0;
@@ -208,7 +344,8 @@ __global__ __launch_bounds__(kThreads) void disp_scatter_kernel(
   for (int e = lane; e < E; e += kWave) wh[wave][e] = 0;
   __syncthreads();
   int base = inc - s;
-  for (int w = 0; w < wave; ++w) base += wsum[w];
+#pragma unroll
+  for (int w = 0; w < WAVES; ++w) base += w < wave ? wsum[w] : 0;  // straight-line
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = tid * 4 + i;
@@ -223,51 +360,55 @@ __global__ __launch_bounds__(kThreads) void disp_scatter_kernel(
     }
     base += t4[i];
   }
-  if (blockIdx.x == 0 && tid == kThreads - 1) offsets[E] = base;
+  if (blockIdx.x == 0 && tid == NT - 1) offsets[E] = base;
   if (tile >= nt) return;  // only when there are no routes at all
 
-  count_chunks<CPW>(ev, nbits, wh[wave]);
-  __syncthreads();
-  // per-wave starting positions of each expert inside this tile
-  for (int e = tid; e < E; e += kThreads) {
-    const int c0 = wh[0][e], c1 = wh[1][e], c2 = wh[2][e];
-    const int b = FUSED ? off[e] : off[e] + tile_base[(int64_t)e * nt + tile];
-    wh[0][e] = b;
-    wh[1][e] = b + c0;
-    wh[2][e] = b + c0 + c1;
-    wh[3][e] = b + c0 + c1 + c2;
+  // count this wave's chunks into its row, keeping each route's offset in
+  // the wave (the expert's count in earlier chunks plus the peers below it)
+  int32_t* row = wh[wave];
+  int in_wave[CPW];
+  {
+    const uint64_t below = lanemask_lt();
+#pragma unroll
+    for (int ch = 0; ch < CPW; ++ch) {
+      const int e = ev[ch];
+      const uint64_t p = peer_mask<NB>(e);
+      in_wave[ch] = 0;
+      if (e >= 0) {
+        const int start = row[e];
+        in_wave[ch] = start + __popcll(p & below);
+        if ((p & below) == 0) row[e] = start + __popcll(p);
+      }
+    }
   }
   __syncthreads();
-  const uint64_t below = lanemask_lt();
-  int32_t* row = wh[wave];
+  // per-wave starting positions of each expert inside this tile
+  for (int e = tid; e < E; e += NT) {
+    int b = FUSED ? off[e] : off[e] + tile_base[(int64_t)e * nt + tile];
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+      const int c = wh[w][e];
+      wh[w][e] = b;
+      b += c;
+    }
+  }
+  __syncthreads();
 #pragma unroll
   for (int ch = 0; ch < CPW; ++ch) {
     const int64_t r = r0 + ch * kWave + lane;
     const int e = ev[ch];
-    const uint64_t p = peer_mask(e, nbits);
-    int pos = -1;
-    if (e >= 0) {
-      const int start = row[e];
-      pos = start + __popcll(p & below);
-      if ((p & below) == 0) row[e] = start + __popcll(p);
-    }
-    if (r < R) {
+    const int pos = e >= 0 ? row[e] + in_wave[ch] : -1;
+    if (routes && r < R) {
       if (inv) inv[r] = pos;
       if (pos >= 0 && pos < R) perm[pos] = (int32_t)r;
     }
   }
 }
 
-int bits_for(int E) {
-  int b = 0;
-  while ((1 << b) < E) ++b;
-  return b;
-}
-
 // Chunks per wave for the two-kernel path: the smallest tile that keeps the
 // histogram within kFusedMaxCounts, or 0 (three-kernel path).
 int fused_cpw(int64_t R, int32_t E) {
-  if (E % 4 != 0 || std::getenv("MOE_DISPATCH_UNFUSED")) return 0;  // tuning: 3 kernels
+  if (E % 8 != 0 || std::getenv("MOE_DISPATCH_UNFUSED")) return 0;  // tuning: 3 kernels
   for (int cpw : {2, 4, 8}) {
     const int64_t nt = (R + kWaves * cpw * kWave - 1) / (kWaves * cpw * kWave);
     if (nt * E > kFusedMaxCounts) continue;
@@ -281,32 +422,76 @@ int fused_cpw(int64_t R, int32_t E) {
   return 0;
 }
 
-template <int CPW>
-hipError_t launch_fused(const int32_t* ids, int64_t R, int32_t E, int nbits, int32_t* counts,
-                        int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* tile_hist,
-                        int32_t* dev_err, hipStream_t stream) {
-  const int nt = (int)((R + kWaves * CPW * kWave - 1) / (kWaves * CPW * kWave));
-  hipError_t e = launch(kStageDispHist, disp_hist_kernel<CPW, true>, dim3(nt), dim3(kThreads),
-                        stream, ids, R, E, nbits, nt, tile_hist, dev_err);
-  if (e != hipSuccess) return e;
-  return launch(kStageDispScatter, disp_scatter_kernel<CPW, true>, dim3(nt), dim3(kThreads),
-                stream, ids, R, E, nbits, nt, (const int32_t*)tile_hist, (const int32_t*)nullptr,
-                (const int32_t*)nullptr, counts, offsets, perm, inv);
+// The placement kernel for tiles of TILE routes: one chunk per wave up to 16
+// waves, then more chunks per wave.
+template <int TILE, bool FUSED>
+hipError_t launch_scatter(const int32_t* ids, int64_t R, int32_t E, int nt,
+                          const hist_t* tile_hist, const int32_t* tile_base,
+                          const int32_t* totals, int32_t* counts, int32_t* offsets,
+                          int32_t* perm, int32_t* inv, hipStream_t stream) {
+  constexpr int W = TILE / kWave >= 16 ? 16 : TILE / kWave;
+  // with no routes (three-kernel path only) one workgroup writes zero
+  // counts and offsets
+  auto go = [&](auto kernel) {
+    return launch(kStageDispScatter, kernel, dim3(nt > 0 ? nt : 1), dim3(W * kWave), stream,
+                  ids, R, E, nt, tile_hist, tile_base, totals, counts, offsets, perm, inv);
+  };
+  switch (id_bits(E)) {
+    case 7: return go(disp_scatter_kernel<W, TILE, FUSED, 7>);
+    case 8: return go(disp_scatter_kernel<W, TILE, FUSED, 8>);
+    default: return go(disp_scatter_kernel<W, TILE, FUSED, kIdBits>);
+  }
+}
+
+// The histogram kernel (tiles of kWaves x CPW x 64 routes).
+template <int CPW, bool TILE_MAJOR>
+hipError_t launch_hist(const int32_t* ids, int64_t R, int32_t E, int nt,
+                       std::conditional_t<TILE_MAJOR, hist_t, int32_t>* tile_hist,
+                       int32_t* dev_err, hipStream_t stream) {
+  auto go = [&](auto kernel) {
+    return launch(kStageDispHist, kernel, dim3(nt), dim3(kThreads), stream, ids, R, E, nt,
+                  tile_hist, dev_err);
+  };
+  switch (id_bits(E)) {
+    case 7: return go(disp_hist_kernel<CPW, TILE_MAJOR, 7>);
+    case 8: return go(disp_hist_kernel<CPW, TILE_MAJOR, 8>);
+    default: return go(disp_hist_kernel<CPW, TILE_MAJOR, kIdBits>);
+  }
+}
+
+hipError_t launch_placement(int tile_routes, const int32_t* ids, int64_t R, int32_t E, int nt,
+                            const hist_t* tile_hist, int32_t* counts, int32_t* offsets,
+                            int32_t* perm, int32_t* inv, hipStream_t stream) {
+  switch (tile_routes) {
+#define MOE_PLACE(T_)                                                                        \
+  case T_:                                                                                   \
+    return launch_scatter<T_, true>(ids, R, E, nt, tile_hist, nullptr, nullptr, counts, \
+                                    offsets, perm, inv, stream);
+    MOE_PLACE(256)
+    MOE_PLACE(512)
+    MOE_PLACE(1024)
+    MOE_PLACE(2048)
+#undef MOE_PLACE
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <int CPW>
-hipError_t launch_placement(const int32_t* ids, int64_t R, int32_t E, int nbits, int nt,
-                            const int32_t* tile_hist, int32_t* counts, int32_t* offsets,
-                            int32_t* perm, int32_t* inv, hipStream_t stream) {
-  return launch(kStageDispScatter, disp_scatter_kernel<CPW, true>, dim3(nt), dim3(kThreads),
-                stream, ids, R, E, nbits, nt, tile_hist, (const int32_t*)nullptr,
-                (const int32_t*)nullptr, counts, offsets, perm, inv);
+hipError_t launch_fused(const int32_t* ids, int64_t R, int32_t E, int32_t* counts,
+                        int32_t* offsets, int32_t* perm, int32_t* inv, hist_t* tile_hist,
+                        int32_t* dev_err, hipStream_t stream) {
+  constexpr int kRoutes = kWaves * CPW * kWave;
+  const int nt = (int)((R + kRoutes - 1) / kRoutes);
+  hipError_t e = launch_hist<CPW, true>(ids, R, E, nt, tile_hist, dev_err, stream);
+  if (e != hipSuccess) return e;
+  return launch_placement(kRoutes, ids, R, E, nt, tile_hist, counts, offsets, perm, inv,
+                          stream);
 }
 
 }  // namespace
 
 bool dispatch_hist_ok(int64_t R, int32_t E, int32_t tile_routes) {
-  if (R <= 0 || E % 4 != 0 || E > kMaxE) return false;
+  if (R <= 0 || E % 8 != 0 || E > kMaxE) return false;
   if (tile_routes != 256 && tile_routes != 512 && tile_routes != 1024 && tile_routes != 2048)
     return false;
   return (R + tile_routes - 1) / tile_routes * E <= kFusedMaxCounts;
@@ -314,17 +499,12 @@ bool dispatch_hist_ok(int64_t R, int32_t E, int32_t tile_routes) {
 
 hipError_t launch_dispatch_from_hist(const int32_t* ids, int64_t R, int32_t E,
                                      int32_t* counts, int32_t* offsets, int32_t* perm,
-                                     int32_t* inv, const int32_t* tile_hist,
+                                     int32_t* inv, const hist_t* tile_hist,
                                      int32_t tile_routes, hipStream_t stream) {
   if (!dispatch_hist_ok(R, E, tile_routes)) return hipErrorInvalidValue;
   const int nt = (int)((R + tile_routes - 1) / tile_routes);
-  const int nbits = bits_for(E);
-  switch (tile_routes) {
-    case 256: return launch_placement<1>(ids, R, E, nbits, nt, tile_hist, counts, offsets, perm, inv, stream);
-    case 512: return launch_placement<2>(ids, R, E, nbits, nt, tile_hist, counts, offsets, perm, inv, stream);
-    case 1024: return launch_placement<4>(ids, R, E, nbits, nt, tile_hist, counts, offsets, perm, inv, stream);
-    default: return launch_placement<8>(ids, R, E, nbits, nt, tile_hist, counts, offsets, perm, inv, stream);
-  }
+  return launch_placement(tile_routes, ids, R, E, nt, tile_hist, counts, offsets,
+                          perm, inv, stream);
 }
 
 int dispatch_kernels(int64_t R, int32_t E) {
@@ -336,7 +516,7 @@ size_t dispatch_workspace_bytes(int64_t R, int32_t E) {
   if (R <= 0) return 0;  // no routes: only counts and offsets are written
   if (const int cpw = fused_cpw(R, E)) {
     const int64_t nt = (R + kWaves * cpw * kWave - 1) / (kWaves * cpw * kWave);
-    return (size_t)(nt * E * (int64_t)sizeof(int32_t));
+    return (size_t)(nt * E * (int64_t)sizeof(hist_t));
   }
   const int64_t nt = (R + kTile - 1) / kTile;
   return (size_t)((2 * nt + 1) * (int64_t)E * sizeof(int32_t));
@@ -346,13 +526,12 @@ hipError_t launch_dispatch(const int32_t* ids, int64_t R, int32_t E,
                            int32_t* counts, int32_t* offsets, int32_t* perm,
                            int32_t* inv, void* workspace, int32_t* dev_err,
                            hipStream_t stream) {
-  const int nbits = bits_for(E);
   int32_t* ws = static_cast<int32_t*>(workspace);
   if (R > 0) {
     switch (fused_cpw(R, E)) {
-      case 2: return launch_fused<2>(ids, R, E, nbits, counts, offsets, perm, inv, ws, dev_err, stream);
-      case 4: return launch_fused<4>(ids, R, E, nbits, counts, offsets, perm, inv, ws, dev_err, stream);
-      case 8: return launch_fused<8>(ids, R, E, nbits, counts, offsets, perm, inv, ws, dev_err, stream);
+      case 2: return launch_fused<2>(ids, R, E, counts, offsets, perm, inv, static_cast<hist_t*>(workspace), dev_err, stream);
+      case 4: return launch_fused<4>(ids, R, E, counts, offsets, perm, inv, static_cast<hist_t*>(workspace), dev_err, stream);
+      case 8: return launch_fused<8>(ids, R, E, counts, offsets, perm, inv, static_cast<hist_t*>(workspace), dev_err, stream);
       default: break;
     }
   }
@@ -362,8 +541,7 @@ hipError_t launch_dispatch(const int32_t* ids, int64_t R, int32_t E,
   int32_t* totals = tile_base + (int64_t)nt * E;
   hipError_t e;
   if (nt > 0) {
-    e = launch(kStageDispHist, disp_hist_kernel<kChunksPerWave, false>, dim3(nt),
-               dim3(kThreads), stream, ids, R, E, nbits, nt, tile_hist, dev_err);
+    e = launch_hist<kChunksPerWave, false>(ids, R, E, nt, tile_hist, dev_err, stream);
     if (e != hipSuccess) return e;
     e = launch(kStageDispScan, disp_tile_scan_kernel, dim3((E + kScanWaves - 1) / kScanWaves),
                dim3(kScanWaves * kWave), stream, (const int32_t*)tile_hist, nt, E, tile_base,
@@ -372,10 +550,9 @@ hipError_t launch_dispatch(const int32_t* ids, int64_t R, int32_t E,
   }
   // with no routes the scatter kernel runs one workgroup that only writes
   // zero counts and offsets (totals is not read then)
-  return launch(kStageDispScatter, disp_scatter_kernel<kChunksPerWave, false>,
-                dim3(nt > 0 ? nt : 1), dim3(kThreads), stream, ids, R, E, nbits, nt,
-                (const int32_t*)nullptr, (const int32_t*)tile_base,
-                (const int32_t*)(nt > 0 ? totals : nullptr), counts, offsets, perm, inv);
+  return launch_scatter<kTile, false>(ids, R, E, nt, nullptr, tile_base,
+                                      nt > 0 ? totals : nullptr, counts, offsets, perm, inv,
+                                      stream);
 }
 
 }  // namespace moe

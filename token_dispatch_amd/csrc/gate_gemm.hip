@@ -273,6 +273,7 @@ struct Frag<float> {
 // `pick` ([NW * 64 / LPT][kMaxK]) and `whist` ([NW][kFusedMaxE]) are LDS
 // scratch carved from the ring behind the tile's rows.
 constexpr int kFusedMaxE = 128;  // experts of the fused selection
+constexpr int kFusedIdBits = 7;  // bits of an expert id below kFusedMaxE
 
 template <class EPI, int BM, int NW, int PITCH>
 __device__ __forceinline__ void fused_select(const float* lo, int32_t (*pick)[sel::kMaxK],
@@ -288,8 +289,6 @@ __device__ __forceinline__ void fused_select(const float* lo, int32_t (*pick)[se
   const int e0 = sl * VPL;
   const int nval = min(max(E - e0, 0), VPL);
   const bool lvec = sa.vec && nval == VPL;
-  int nbits = 0;
-  while ((1 << nbits) < E) ++nbits;
   float sb[VPL];  // the same experts for every token of this lane
   sel::load_sbias<VPL, EPI::kMono>(sa.select_bias, e0, E, lvec, sb);
   if constexpr (EPI::kHist)
@@ -313,7 +312,7 @@ __device__ __forceinline__ void fused_select(const float* lo, int32_t (*pick)[se
     sel::select_token<LPT, VPL, EPI::kMono>(sa.c, sl, seg, tok_ok, t, lv, nval, sb, kraw, row,
                                             pick[wave * TPW + seg], sa.ids, sa.weights,
                                             sa.dev_err, pid);
-    if constexpr (EPI::kHist) sel::count_picks<LPT>(pid, sl, sa.c.k, nbits, whist[wave]);
+    if constexpr (EPI::kHist) sel::count_picks<LPT, kFusedIdBits>(pid, sl, sa.c.k, whist[wave]);
   }
   if constexpr (EPI::kHist) {
     __syncthreads();
@@ -321,7 +320,7 @@ __device__ __forceinline__ void fused_select(const float* lo, int32_t (*pick)[se
       int n = 0;
 #pragma unroll
       for (int w8 = 0; w8 < NW; ++w8) n += whist[w8][e];
-      sa.hist[(int64_t)mt * E + e] = n;
+      sa.hist[(int64_t)mt * E + e] = (hist_t)n;
     }
   }
 }

@@ -67,6 +67,12 @@ hipError_t launch_gate_gemm(const GatePlan& g, int32_t dtype, const void* x, con
                             const float* logit_bias, float* out, int32_t T, int32_t d,
                             int32_t E, hipStream_t stream);
 
+// Count of one expert in one dispatch tile of the tile-major histograms
+// that the routing kernels write for the placement kernel: at most the
+// routes of a tile (<= 2048), so 16 bits; every placement workgroup reads
+// all of them, half as many bytes as 32-bit counts.
+using hist_t = uint16_t;
+
 // Selection arguments of the gate kernel's fused epilogue (whole-row tiles:
 // the selection runs on the tile's logits in LDS).  hist: per-M-tile expert
 // histograms of the dispatch (tiles of BM tokens x k routes), or NULL;
@@ -78,7 +84,7 @@ struct SelectArgs {
   int32_t* ids;
   float* weights;
   int32_t* dev_err;
-  int32_t* hist;
+  hist_t* hist;
   int32_t write_logits;
   int32_t vec;
 };
@@ -106,7 +112,7 @@ void select_shape(const RouteCfg& c, int* lpt, int* vpl);
 hipError_t launch_select(const RouteCfg& c, const float* logits, int32_t splits,
                          int64_t split_stride, float* logits_out, const float* logit_bias,
                          const float* select_bias, const int32_t* k_per_token, int32_t* ids,
-                         float* weights, int32_t* dev_err, int32_t* hist, hipStream_t stream);
+                         float* weights, int32_t* dev_err, hist_t* hist, hipStream_t stream);
 int select_hist_tokens(const RouteCfg& c);  // 0: no histogram option
 
 // Selection and the whole dispatch of a small batch in one workgroup (when
@@ -133,11 +139,12 @@ hipError_t launch_hash_route(const RouteCfg& c, int32_t dtype,
                              int32_t* dev_err, hipStream_t stream);
 
 // Dispatch placement from per-tile histograms already in tile_hist
-// ([ceil(R / tile_routes)][E], tile-major), when dispatch_hist_ok.
+// ([ceil(R / tile_routes)][E] hist_t, tile-major), when dispatch_hist_ok
+// (E % 8 == 0: 16-byte rows).
 bool dispatch_hist_ok(int64_t R, int32_t E, int32_t tile_routes);
 hipError_t launch_dispatch_from_hist(const int32_t* ids, int64_t R, int32_t E,
                                      int32_t* counts, int32_t* offsets, int32_t* perm,
-                                     int32_t* inv, const int32_t* tile_hist,
+                                     int32_t* inv, const hist_t* tile_hist,
                                      int32_t tile_routes, hipStream_t stream);
 
 // Dispatch: tile histograms -> scan -> stable scatter.

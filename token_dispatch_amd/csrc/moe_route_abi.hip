@@ -189,7 +189,7 @@ struct SmallDispatch {
 int32_t route_core(const moe_route_params* p, const void* x, const void* W,
                    const float* logit_bias, const float* select_bias,
                    const int32_t* k_per_token, float* logits, int32_t* ids, float* weights,
-                   void* workspace, size_t workspace_bytes, int32_t* dev_err, int32_t* hist,
+                   void* workspace, size_t workspace_bytes, int32_t* dev_err, moe::hist_t* hist,
                    hipStream_t s, const SmallDispatch* sd = nullptr) {
   const moe::RouteCfg c = to_cfg(p);
   hipError_t e;
@@ -287,7 +287,7 @@ int fused_hist_tokens(const moe_route_params* p, bool gate, bool aligned) {
 
 // Dispatch part of the moe_route_dispatch workspace for a given path.
 size_t disp_ws_bytes(const moe_route_params* p, int n) {
-  return n > 0 ? (size_t)((p->T + n - 1) / n) * p->E * sizeof(int32_t)
+  return n > 0 ? (size_t)((p->T + n - 1) / n) * p->E * sizeof(moe::hist_t)
                : moe::dispatch_workspace_bytes((int64_t)p->T * p->k, p->E);
 }
 
@@ -352,16 +352,18 @@ int32_t moe_route_dispatch(const moe_route_params* p, const void* x, const void*
     return route_core(p, x, W, logit_bias, select_bias, k_per_token, logits, ids, weights,
                       workspace, route, dev_err, nullptr, s, &sd);
   }
-  int32_t* disp_ws = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + route);
+  void* disp_ws = static_cast<char*>(workspace) + route;
   const bool gate = x != nullptr;
   const bool aligned = reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
                        reinterpret_cast<uintptr_t>(W) % 16 == 0;
   const int n = fused_hist_tokens(p, gate, aligned);
   rc = route_core(p, x, W, logit_bias, select_bias, k_per_token, logits, ids, weights,
-                  workspace, route, dev_err, n > 0 ? disp_ws : nullptr, s);
+                  workspace, route, dev_err, n > 0 ? static_cast<moe::hist_t*>(disp_ws) : nullptr,
+                  s);
   if (rc != MOE_OK) return rc;
   if (n > 0)
-    e = moe::launch_dispatch_from_hist(ids, R, p->E, counts, offsets, perm, inv, disp_ws,
+    e = moe::launch_dispatch_from_hist(ids, R, p->E, counts, offsets, perm, inv,
+                                       static_cast<const moe::hist_t*>(disp_ws),
                                        n * p->k, s);
   else
     e = moe::launch_dispatch(ids, R, p->E, counts, offsets, perm, inv, disp_ws, dev_err, s);

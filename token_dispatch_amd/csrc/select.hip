@@ -59,7 +59,7 @@ __global__ __launch_bounds__(WPB * kWave) void select_kernel(
     float* __restrict__ logits_out, const float* __restrict__ logit_bias,
     const float* __restrict__ select_bias, const int32_t* __restrict__ k_per_token,
     int32_t* __restrict__ ids, float* __restrict__ weights, int32_t* __restrict__ dev_err,
-    int vec, int32_t* __restrict__ hist) {
+    int vec, hist_t* __restrict__ hist) {
   constexpr int TPW = kWave / LPT;               // tokens per wavefront
   constexpr int TPB = WPB * TPW;                 // tokens per workgroup
   constexpr int ROW = LPT * VPL;                 // >= E
@@ -123,19 +123,17 @@ __global__ __launch_bounds__(WPB * kWave) void select_kernel(
   sel::select_token<LPT, VPL, MONO>(c, sl, seg, tok_ok, t, lv, nval, sb, kraw, lrow[tb],
                                     pick[tb], ids, weights, dev_err, pid);
   if constexpr (HIST) {
-    int nbits = 0;
-    while ((1 << nbits) < E) ++nbits;
     for (int e = lane; e < E; e += kWave) whist[wave][e] = 0;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    sel::count_picks<LPT>(pid, sl, c.k, nbits, whist[wave]);
+    sel::count_picks<LPT, sel::kHistIdBits>(pid, sl, c.k, whist[wave]);
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += WPB * kWave) {
       int n = 0;
 #pragma unroll
       for (int w8 = 0; w8 < WPB; ++w8) n += whist[w8][e];
-      hist[(int64_t)blockIdx.x * E + e] = n;
+      hist[(int64_t)blockIdx.x * E + e] = (hist_t)n;
     }
   }
 }
@@ -151,6 +149,7 @@ __global__ __launch_bounds__(WPB * kWave) void select_kernel(
 constexpr int kSmallWaves = 8;
 constexpr int kSmallRoutes = 2048;
 constexpr int kSmallE = 128;
+constexpr int kSmallIdBits = 7;  // bits of an expert id below kSmallE
 
 template <int LPT, int VPL, int NSPLIT, bool MONO>
 __global__ __launch_bounds__(kSmallWaves * kWave) void route_dispatch_small_kernel(
@@ -254,15 +253,13 @@ __global__ __launch_bounds__(kSmallWaves * kWave) void route_dispatch_small_kern
   // dispatch of the R routes held in rid
   const int R = T * K;
   const int nch = (R + kWave - 1) / kWave;
-  int nbits = 0;
-  while ((1 << nbits) < E) ++nbits;
   for (int i = tid; i < nch * kSmallE; i += kSmallWaves * kWave) cbase[i / kSmallE][i % kSmallE] = 0;
   __syncthreads();
   const uint64_t below = lanemask_lt();
   for (int ch = wave; ch < nch; ch += kSmallWaves) {
     const int r = ch * kWave + lane;
     const int e = r < R ? rid[r] : -1;
-    const uint64_t p = peer_mask(e, nbits);
+    const uint64_t p = peer_mask<kSmallIdBits>(e);
     if (e >= 0 && (p & below) == 0) cbase[ch][e] = __popcll(p);  // one leader per expert
   }
   __syncthreads();
@@ -293,7 +290,7 @@ __global__ __launch_bounds__(kSmallWaves * kWave) void route_dispatch_small_kern
   for (int ch = wave; ch < nch; ch += kSmallWaves) {
     const int r = ch * kWave + lane;
     const int e = r < R ? rid[r] : -1;
-    const uint64_t p = peer_mask(e, nbits);
+    const uint64_t p = peer_mask<kSmallIdBits>(e);
     const int pos = e >= 0 ? off[e] + cbase[ch][e] + __popcll(p & below) : -1;
     if (r < R) {
       if (inv) inv[r] = pos;
@@ -311,7 +308,7 @@ template <int LPT, int VPL, int NS, bool MONO>
 hipError_t launch_vpl(const RouteCfg& c, const float* logits, int64_t stride, float* logits_out,
                       const float* logit_bias, const float* select_bias,
                       const int32_t* k_per_token, int32_t* ids, float* weights, int32_t* dev_err,
-                      int vec, int32_t* hist, hipStream_t s) {
+                      int vec, hist_t* hist, hipStream_t s) {
   constexpr int tpb = 4 * (kWave / LPT);
   const int64_t blocks = ((int64_t)c.T + tpb - 1) / tpb;
   if constexpr (LPT * VPL <= kHistMaxE) {
@@ -327,14 +324,14 @@ hipError_t launch_vpl(const RouteCfg& c, const float* logits, int64_t stride, fl
   if (hist) return hipErrorInvalidValue;
   return launch(kStageSelect, select_kernel<LPT, VPL, NS, MONO, 4, false>, dim3((uint32_t)blocks),
                 dim3(4 * kWave), s, c, logits, stride, logits_out, logit_bias, select_bias,
-                k_per_token, ids, weights, dev_err, vec, (int32_t*)nullptr);
+                k_per_token, ids, weights, dev_err, vec, (hist_t*)nullptr);
 }
 
 template <int LPT, int VPL, bool MONO>
 hipError_t launch_splits(const RouteCfg& c, const float* logits, int splits, int64_t stride,
                          float* logits_out, const float* logit_bias, const float* select_bias,
                          const int32_t* k_per_token, int32_t* ids, float* weights,
-                         int32_t* dev_err, int vec, int32_t* hist, hipStream_t s) {
+                         int32_t* dev_err, int vec, hist_t* hist, hipStream_t s) {
 #define MOE_S(S_)                                                                        \
   return launch_vpl<LPT, VPL, S_, MONO>(c, logits, stride, logits_out, logit_bias,       \
                                         select_bias, k_per_token, ids, weights, dev_err, \
@@ -351,7 +348,7 @@ template <int LPT, int VPL>
 hipError_t launch_mono(const RouteCfg& c, bool mono, const float* logits, int splits,
                        int64_t stride, float* logits_out, const float* logit_bias,
                        const float* select_bias, const int32_t* k_per_token, int32_t* ids,
-                       float* weights, int32_t* dev_err, int vec, int32_t* hist,
+                       float* weights, int32_t* dev_err, int vec, hist_t* hist,
                        hipStream_t s) {
   if (mono)
     return launch_splits<LPT, VPL, true>(c, logits, splits, stride, logits_out, logit_bias,
@@ -486,7 +483,7 @@ hipError_t launch_route_dispatch_small(const RouteCfg& c, const float* logits, i
 hipError_t launch_select(const RouteCfg& c, const float* logits, int32_t splits,
                          int64_t split_stride, float* logits_out, const float* logit_bias,
                          const float* select_bias, const int32_t* k_per_token, int32_t* ids,
-                         float* weights, int32_t* dev_err, int32_t* hist, hipStream_t stream) {
+                         float* weights, int32_t* dev_err, hist_t* hist, hipStream_t stream) {
   if (c.T == 0) return hipSuccess;
   const int E = c.E;
   const bool grouped = c.n_groups > 1 && c.topk_groups < c.n_groups;

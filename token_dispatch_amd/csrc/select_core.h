@@ -11,6 +11,7 @@ namespace sel {
 
 constexpr int kMaxK = 32;        // MOE_MAX_K
 constexpr int kHistMaxE = 256;   // experts of the per-block histogram option
+constexpr int kHistIdBits = 8;   // bits of an expert id below kHistMaxE
 
 // ---- DPP helpers ------------------------------------------------------------
 template <int CTRL>
@@ -355,19 +356,19 @@ __device__ __forceinline__ void select_token(
   }
 }
 
-// Adds a wavefront's picks (pid of each lane, ranks below K) to whist_w[e]:
+// Adds a wavefront's picks (pid of each lane, ranks below K, ids < 2^NB) to whist_w[e]:
 // ballot peer masks give one leader per expert and chunk, so no two lanes
 // update one entry at once (no atomics).
-template <int LPT>
+template <int LPT, int NB>
 __device__ __forceinline__ void count_picks(const int (&pid)[(kMaxK + LPT - 1) / LPT], int sl,
-                                            int K, int nbits, int32_t* whist_w) {
+                                            int K, int32_t* whist_w) {
   constexpr int KPL = (kMaxK + LPT - 1) / LPT;
   const uint64_t below = lanemask_lt();
 #pragma unroll
   for (int i = 0; i < KPL; ++i) {  // chunk i: every lane's i-th pick
     if (i * LPT >= K) break;      // wave-uniform: no rank below K in this chunk
     const int e = (sl + i * LPT < K) ? pid[i] : -1;
-    const uint64_t p = peer_mask(e, nbits);
+    const uint64_t p = peer_mask<NB>(e);
     if (e >= 0 && (p & below) == 0) whist_w[e] += __popcll(p);
   }
 }
