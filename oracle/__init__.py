@@ -69,6 +69,8 @@ def _load():
         lib.orc_dispatch.restype = i32
         lib.orc_maxvio.argtypes = [vp, i32]
         lib.orc_maxvio.restype = ctypes.c_double
+        lib.orc_combine.argtypes = [i32, i32, i32, i32, vp, i32, vp, vp, vp, vp]
+        lib.orc_combine.restype = i32
         lib.orc_route_full.argtypes = [ctypes.POINTER(_Params)] + [vp] * 11 + [i32]
         lib.orc_route_full.restype = i32
         _lib = lib
@@ -193,6 +195,30 @@ def dispatch(ids, E):
     R = int(offsets[E])
     return {"counts": counts, "offsets": offsets, "perm": perm[:R].copy(),
             "inv": inv[:T * ks].copy(), "nerr": int(nerr)}
+
+
+def combine(Yp, inv, weights, shared=None):
+    """y[T][d] (fp64) = sum_j weights[t][j] * Yp[inv[t][j]] (+ shared[t]).
+
+    Yp[R][d] are the expert outputs in dispatch order (float32, or uint16 =
+    bf16 bits); inv[T][k] as returned by dispatch (-1: empty slot);
+    weights[T][k] float32.  Returns (y, n_errors) -- n_errors counts slots
+    with inv >= R."""
+    dtype = "bf16" if Yp.dtype == np.uint16 else "f32"
+    npdt = np.uint16 if dtype == "bf16" else np.float32
+    Yp = _c(Yp, npdt)
+    inv = _c(inv, np.int32)
+    weights = _c(weights, np.float32)
+    R, d = Yp.shape
+    T, k = inv.shape
+    assert weights.shape == (T, k)
+    if shared is not None:
+        shared = _c(shared, npdt)
+        assert shared.shape == (T, d)
+    y = np.empty((T, d), np.float64)
+    nerr = _load().orc_combine(T, k, d, DTYPE[dtype], _ptr(Yp), R, _ptr(inv),
+                               _ptr(weights), _ptr(shared), _ptr(y))
+    return y, int(nerr)
 
 
 def maxvio(counts):

@@ -318,6 +318,36 @@ double orc_maxvio(const int32_t* counts, int32_t E) {
   return (double)mx / ((double)R / (double)E) - 1.0;
 }
 
+/* ---- combine: [dyn-k] "Possible Implementation" (the output is the sum of
+ * the selected experts' outputs, each times its weight) and [ferrox]
+ * combine_expert_outputs (routed plus shared expert outputs of a token).
+ * Row p of Yp is the expert output for the route placed at position p by
+ * the dispatch, so slot j of token t reads row inv[t*k + j]; the shared
+ * output enters with weight 1, after the routed slots. */
+int32_t orc_combine(int32_t T, int32_t k, int32_t d, int32_t dtype, const void* Yp, int32_t R,
+                    const int32_t* inv, const float* weights, const void* shared,
+                    double* y) {
+  int32_t nerr = 0;
+  for (int32_t t = 0; t < T; ++t) {
+    for (int32_t i = 0; i < d; ++i) y[(size_t)t * d + i] = 0.0;
+    for (int32_t j = 0; j < k; ++j) {
+      const int32_t p = inv[(size_t)t * k + j];
+      if (p < 0) continue;          /* empty slot */
+      if (p >= R) {                 /* no such row: counted, left out */
+        ++nerr;
+        continue;
+      }
+      const double w = (double)weights[(size_t)t * k + j];
+      for (int32_t i = 0; i < d; ++i)
+        y[(size_t)t * d + i] += w * input_at(dtype, Yp, (size_t)p * d + i);
+    }
+    if (shared)
+      for (int32_t i = 0; i < d; ++i)
+        y[(size_t)t * d + i] += input_at(dtype, shared, (size_t)t * d + i);
+  }
+  return nerr;
+}
+
 /* ---- whole path, threaded over tokens ------------------------------------- */
 typedef struct {
   const orc_params* p;

@@ -20,7 +20,11 @@
  *            request)" (llama.cpp issue 13572): k chosen per request over the
  *            same gate scores.
  *  [router-survey] "I modelli MoE open hanno router opposti" (millebit.com):
- *            MaxVio as the load statistic; the routed-expert configurations.
+ *            MaxVio as the load statistic; the routed-expert configurations;
+ *            shared experts kept always on beside the routed ones.
+ *  [ferrox] also: combine_expert_outputs (routed + shared outputs of a
+ *            token); [dyn-k] "Possible Implementation": the output is the
+ *            weighted sum of the selected experts' outputs.
  *
  * Readings where the pages are silent are fixed here and listed in the design doc:
  * ties go to the lower expert (group) id; slot order is descending selection
@@ -100,6 +104,16 @@ int32_t orc_dispatch(const int32_t* ids, int32_t T, int32_t k_stride, int32_t E,
 
 /* MaxVio = max_e counts[e] / (R / E) - 1, R = sum of counts. */
 double orc_maxvio(const int32_t* counts, int32_t E);
+
+/* Combine: y[t][i] = sum over slots j with 0 <= inv[t*k+j] < R of
+ * weights[t][j] * Yp[inv[t*k+j]][i], plus shared[t][i] (weight 1) when
+ * shared is not NULL, in fp64 (slots in order, the shared term last).
+ * Yp[R][d] holds the expert outputs in dispatch order; Yp and shared are
+ * ORC_F32 or ORC_BF16 (dtype).  inv < 0 marks an empty slot; inv >= R is an
+ * error (counted and left out).  Returns the number of errors. */
+int32_t orc_combine(int32_t T, int32_t k, int32_t d, int32_t dtype, const void* Yp, int32_t R,
+                    const int32_t* inv, const float* weights, const void* shared,
+                    double* y);
 
 /* Whole path (gate + route + dispatch) split over nthreads host threads by
  * token; dispatch runs on one thread.  Used to time the oracle. */
