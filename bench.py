@@ -13,7 +13,10 @@ routes a different copy of x (rotating through copies totalling more than the
 Prints one JSON line with the throughput, the dominant kernel's roofline
 fraction (kernel time from HIP events recorded on the launch stream by the
 library's per-kernel timing) and the CPU oracle's throughput on a bounded
-sample of the same workload.
+sample of the same workload.  The combine that follows the experts (the
+weighted sum of each token's expert outputs, moe_combine) is not part of a
+step; it is timed separately on synthetic expert outputs in the step's
+dispatch order and reported with its own HBM fraction ("combine").
 
 Usage: python bench.py [--steps K] [--warmup W] [--workload NAME]
 """
@@ -129,6 +132,8 @@ def main():
     ap.add_argument("--workload", default="qwen3_dynk")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-combine", action="store_true",
+                    help="skip the separate measurement of the combine kernel")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches only (no HIP graph replay)")
     ap.add_argument("--calibrate-copy-mb", type=float, default=0.0,
@@ -301,6 +306,38 @@ def main():
     for s, v in stages.items():
         log(f"[bench] {s:13s} {v['avg_us']:9.2f} us  {v['GBs']} GB/s")
 
+    # the combine that follows the experts, timed on its own (not part of a
+    # step): synthetic expert outputs in this step's dispatch order plus a
+    # shared expert's output; rotating copies of the rows keep them from
+    # being served out of the last-level cache
+    combine = None
+    if not args.no_combine and R_valid > 0:
+        eb = 2 if w.dtype == "bf16" else 4
+        Y0 = up(wl.expert_outputs(w, R_valid))
+        n_yc = max(1, min(16, math.ceil(3 * LLC_BYTES / (R_valid * w.d * eb))))
+        Ys = [Y0] + [torch.roll(Y0, shifts=89 * i, dims=0).contiguous() for i in range(1, n_yc)]
+        sh = up(wl.shared_output(w))
+        yout = torch.empty((T, w.d), dtype=Y0.dtype, device=dev)
+        for i in range(20):
+            tda.combine(Ys[i % n_yc], inv, weights, shared=sh, out=yout)
+        torch.cuda.synchronize()
+        tda.profile_enable(True)
+        n_c = 50
+        for i in range(n_c):
+            tda.combine(Ys[i % n_yc], inv, weights, shared=sh, out=yout)
+        torch.cuda.synchronize()
+        cms, cn = tda.profile_read()["combine"]
+        tda.profile_enable(False)
+        c_us = cms / cn * 1e3
+        cbytes = R_valid * w.d * eb + T * k * 8 + 2 * T * w.d * eb  # rows, inv+weights, shared, y
+        c_gbs = cbytes / (c_us * 1e-6) / 1e9
+        combine = {"kernel": "combine", "avg_us": round(c_us, 3), "launches": cn,
+                   "bytes": cbytes, "achieved": round(c_gbs, 1), "peak": HBM_PEAK_GBS,
+                   "unit": "GB/s", "frac": round(c_gbs / HBM_PEAK_GBS, 4), "rows": R_valid,
+                   "d": w.d, "shared": True, "row_copies": n_yc}
+        log(f"[bench] combine       {c_us:9.2f} us  {c_gbs:.1f} GB/s ({R_valid} rows of {w.d})")
+        del Ys, Y0
+
     cpu = None
     if not args.no_cpu_baseline:
         try:
@@ -328,6 +365,7 @@ def main():
         "stages": stages,
         "maxvio": round(maxvio, 4),
         "roofline": roofline,
+        "combine": combine,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 6
+#define MOE_ABI_VERSION 7
 
 /* return codes */
 #define MOE_OK 0
@@ -217,9 +217,9 @@ int32_t moe_dispatch(const int32_t* ids, int32_t T, int32_t k_stride, int32_t E,
  * (k_stride = p->k): one pass of the router and the grouping of its routes,
  * with the results of the two calls (same arguments, same values, bit for
  * bit).  When the tokens routed by one workgroup of the selection kernel
- * form exactly one dispatch tile and the tile histograms are small, the
- * selection kernel also writes those histograms, saving the dispatch's
- * counting kernel.
+ * form exactly one dispatch tile and the tile histograms are small (tiles x
+ * E <= 32768 counts, E a multiple of 8), the selection kernel also writes
+ * those histograms, saving the dispatch's counting kernel.
  *   workspace    256-byte aligned device memory of at least
  *                moe_route_dispatch_workspace_size(p) bytes (the gate
  *                hand-off, then the dispatch's tile data); contents need no
@@ -265,6 +265,32 @@ typedef struct {
 int32_t moe_route_dispatch_plan(const moe_route_params* p, int32_t aligned, moe_plan_info* out);
 
 /*
+ * moe_combine -- a token's layer output from the outputs its experts
+ * produced for it: the weighted sum over its selected experts, plus a
+ * shared expert's output ("Feature Request: dynamic number of experts",
+ * Possible Implementation: the selected experts' outputs combined with
+ * their weights; "ferrox_moe", combine_expert_outputs: routed plus shared
+ * expert outputs of one token).  Expert outputs come in dispatch order, so
+ * slot j of token t reads row inv[t*k_stride + j] of Yp.
+ *   Yp       [R][d] expert outputs; row p is the output for route perm[p]
+ *            (R = offsets[E] of the dispatch; dtype MOE_F32 or MOE_BF16)
+ *   inv      [T*k_stride] as written by moe_dispatch; < 0: empty slot
+ *   weights  [T][k_stride] fp32 combine weights (as written by moe_route)
+ *   shared   [T][d] a shared expert's output (weight 1), or NULL
+ *   y        [T][d] out, dtype as Yp: sum over the valid slots, in slot
+ *            order, of weights[t][j] * Yp[inv[t*k_stride+j]], then +
+ *            shared[t]; accumulated in fp32, stored rounded to nearest (even)
+ *   dev_err  [1] or NULL: += number of slots with inv >= R (left out)
+ * All pointers are caller-owned device memory; y must not overlap the
+ * inputs.  Asynchronous on `stream`.  Limits: k_stride <= MOE_MAX_K,
+ * T*k_stride < 2^31.  Returns MOE_OK, MOE_EINVAL (bad sizes, dtype or a
+ * required NULL pointer) or MOE_EDEVICE.
+ */
+int32_t moe_combine(int32_t T, int32_t k_stride, int32_t d, int32_t dtype, const void* Yp,
+                    int32_t R, const int32_t* inv, const float* weights, const void* shared,
+                    void* y, int32_t* dev_err, void* stream);
+
+/*
  * Per-kernel timing, for benchmarks and profiling only.
  * moe_profile_enable(1) clears earlier records and, from then on, gives
  * every kernel the library launches a start and a stop HIP event that the
@@ -283,7 +309,8 @@ int32_t moe_route_dispatch_plan(const moe_route_params* p, int32_t aligned, moe_
 #define MOE_STAGE_DISP_SCATTER 5 /* dispatch: permutation */
 #define MOE_STAGE_GATE_SELECT 6  /* gate contraction with the selection fused */
 #define MOE_STAGE_SELECT_DISPATCH 7 /* selection + dispatch of a small batch */
-#define MOE_NUM_STAGES 8
+#define MOE_STAGE_COMBINE 8      /* combine of expert outputs */
+#define MOE_NUM_STAGES 9
 int32_t moe_profile_enable(int32_t enable);
 int32_t moe_profile_read(double* ms, int64_t* launches, int32_t n);
 

@@ -300,3 +300,23 @@ def test_planner_invariants_on_random_shapes():
         assert plan["select_lanes"] in (4, 8, 16, 64), plan
         assert plan["select_lanes"] * plan["select_experts_per_lane"] >= E, plan
     assert {"small", "separate", "select_hist", "fused"} <= paths, paths
+
+
+def test_combine_validation():
+    # every check runs on the host before a launch; T = 0 or d = 0 launch nothing
+    L = tda.lib()
+    ok = (FAKE, 5, FAKE, FAKE, None, FAKE, None, None)  # Yp, R, inv, weights, shared, y, dev_err, stream
+    assert L.moe_combine(0, 4, 16, 1, *ok) == tda.MOE_OK
+    assert L.moe_combine(3, 4, 0, 1, *ok) == tda.MOE_OK
+    assert L.moe_combine(-1, 4, 16, 1, *ok) == tda.MOE_EINVAL
+    assert L.moe_combine(3, 0, 16, 1, *ok) == tda.MOE_EINVAL
+    assert L.moe_combine(3, tda.MAX_K + 1, 16, 1, *ok) == tda.MOE_EUNSUPPORTED
+    assert L.moe_combine(3, 4, 16, 2, *ok) == tda.MOE_EINVAL
+    assert "dtype" in L.moe_last_error().decode()
+    assert L.moe_combine(3, 4, -2, 1, *ok) == tda.MOE_EINVAL
+    assert L.moe_combine(3, 4, 16, 1, FAKE, -1, FAKE, FAKE, None, FAKE, None, None) == tda.MOE_EINVAL
+    assert L.moe_combine(3, 4, 16, 1, None, 5, FAKE, FAKE, None, FAKE, None, None) == tda.MOE_EINVAL
+    assert "Yp" in L.moe_last_error().decode()
+    assert L.moe_combine(3, 4, 16, 1, FAKE, 5, FAKE, FAKE, None, None, None, None) == tda.MOE_EINVAL
+    assert L.moe_combine(3, 4, 16, 1, FAKE, 5, None, FAKE, None, FAKE, None, None) == tda.MOE_EINVAL
+    assert L.moe_combine(1 << 30, 4, 16, 1, *ok) == tda.MOE_EUNSUPPORTED

@@ -21,7 +21,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe_route.so")
 
-ABI_VERSION = 6
+ABI_VERSION = 7
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EDEVICE = 0, -1, -2, -3
 MAX_EXPERTS, MAX_K, MAX_GROUPS = 1024, 32, 64
 SCORES = {"softmax": 0, "sigmoid": 1, "sqrt_softplus": 2, "softmax_topk": 3}
@@ -30,14 +30,14 @@ EXPORTS = ("moe_route", "moe_route_workspace_size", "moe_route_hash",
            "moe_route_hash_workspace_size",
            "moe_dispatch_workspace_size", "moe_dispatch",
            "moe_route_dispatch", "moe_route_dispatch_workspace_size",
-           "moe_route_dispatch_plan", "moe_profile_enable", "moe_profile_read",
+           "moe_route_dispatch_plan", "moe_combine", "moe_profile_enable", "moe_profile_read",
            "moe_last_error", "moe_abi_version")
 PATHS = ("separate", "select_hist", "fused", "small")
 PLAN_FIELDS = ("path", "gate_bm", "gate_bn", "gate_waves", "gate_splits", "gate_stage_bytes",
                "gate_ring_depth", "gate_lds_bytes", "select_lanes", "select_experts_per_lane",
                "hist_tokens", "kernels")
 STAGES = ("gate", "select", "hash", "disp_hist", "disp_scan", "disp_scatter", "gate_select",
-          "select_dispatch")
+          "select_dispatch", "combine")
 
 
 class MoeError(RuntimeError):
@@ -86,6 +86,8 @@ def lib() -> ctypes.CDLL:
         L.moe_route_dispatch_workspace_size.restype = ctypes.c_size_t
         L.moe_route_dispatch_plan.argtypes = [P, i32, ctypes.POINTER(PlanInfo)]
         L.moe_route_dispatch_plan.restype = i32
+        L.moe_combine.argtypes = [i32, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp]
+        L.moe_combine.restype = i32
         L.moe_last_error.argtypes = []
         L.moe_last_error.restype = ctypes.c_char_p
         L.moe_profile_enable.argtypes = [i32]
@@ -352,6 +354,33 @@ def dispatch(ids: torch.Tensor, E: int, *, with_inv: bool = True, counts=None, o
     _check(lib().moe_dispatch(_p(ids), T, ks, E, _p(counts), _p(offsets), _p(perm), _p(inv),
                               _p(workspace), workspace.numel(), _p(dev_err), _stream(device)))
     return counts, offsets, perm, inv
+
+
+def combine(Yp: torch.Tensor, inv: torch.Tensor, weights: torch.Tensor, *,
+            shared: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+            dev_err: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y[T][d] = sum_j weights[t][j] * Yp[inv[t][j]] (+ shared[t]).
+
+    Yp[R][d] (float32 or bfloat16): expert outputs in dispatch order;
+    inv[T][k] or [T*k] int32 from dispatch; weights[T][k] float32."""
+    _dev(weights, "weights", torch.float32)
+    T, k = weights.shape
+    _dev(inv, "inv", torch.int32)
+    if inv.numel() != T * k:
+        raise ValueError(f"inv must have {T * k} entries, got {inv.numel()}")
+    _dev(Yp, "Yp")
+    if Yp.dim() != 2:
+        raise ValueError("Yp must be [R][d]")
+    R, d = Yp.shape
+    dt = _dtype_code(Yp)
+    if shared is not None:
+        _dev(shared, "shared", Yp.dtype, (T, d))
+    if out is None:
+        out = torch.empty((T, d), dtype=Yp.dtype, device=Yp.device)
+    _dev(out, "out", Yp.dtype, (T, d))
+    _check(lib().moe_combine(T, k, d, dt, _p(Yp), R, _p(inv), _p(weights), _p(shared), _p(out),
+                             _p(dev_err), _stream(Yp.device)))
+    return out
 
 
 def profile_enable(on: bool = True) -> None:

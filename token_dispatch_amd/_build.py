@@ -20,7 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_route.so")
-SOURCES = ["gate_gemm.hip", "select.hip", "hash_route.hip", "dispatch.hip",
+SOURCES = ["gate_gemm.hip", "select.hip", "hash_route.hip", "dispatch.hip", "combine.hip",
            "moe_route_abi.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

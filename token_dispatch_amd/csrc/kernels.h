@@ -18,7 +18,8 @@ enum Stage : int32_t {
   kStageDispScatter = 5,
   kStageGateSelect = 6,
   kStageSelectDispatch = 7,
-  kNumStages = 8
+  kStageCombine = 8,
+  kNumStages = 9
 };
 
 // Per-kernel timing (moe_profile_enable): the start/stop events of the next
@@ -146,6 +147,13 @@ hipError_t launch_dispatch_from_hist(const int32_t* ids, int64_t R, int32_t E,
                                      int32_t* counts, int32_t* offsets, int32_t* perm,
                                      int32_t* inv, const hist_t* tile_hist,
                                      int32_t tile_routes, hipStream_t stream);
+
+// Combine: y[t] = sum_j weights[t][j] * Yp[inv[t*k+j]] (+ shared[t]), fp32
+// accumulation, dtype 0 = fp32 / 1 = bf16 for Yp, shared and y; slots with
+// inv >= R are counted in *dev_err and left out.
+hipError_t launch_combine(int32_t T, int32_t k, int32_t d, int32_t dtype, const void* Yp,
+                          int32_t R, const int32_t* inv, const float* weights,
+                          const void* shared, void* y, int32_t* dev_err, hipStream_t stream);
 
 // Dispatch: tile histograms -> scan -> stable scatter.
 size_t dispatch_workspace_bytes(int64_t R, int32_t E);

@@ -496,4 +496,26 @@ int32_t moe_dispatch(const int32_t* ids, int32_t T, int32_t k_stride, int32_t E,
   return MOE_OK;
 }
 
+int32_t moe_combine(int32_t T, int32_t k_stride, int32_t d, int32_t dtype, const void* Yp,
+                    int32_t R, const int32_t* inv, const float* weights, const void* shared,
+                    void* y, int32_t* dev_err, void* stream) {
+  if (T < 0) return fail(MOE_EINVAL, "T=%d must be >= 0", T);
+  if (d < 0) return fail(MOE_EINVAL, "d=%d must be >= 0", d);
+  if (R < 0) return fail(MOE_EINVAL, "R=%d must be >= 0", R);
+  if (k_stride < 1) return fail(MOE_EINVAL, "k_stride=%d must be >= 1", k_stride);
+  if (k_stride > MOE_MAX_K)
+    return fail(MOE_EUNSUPPORTED, "k_stride=%d exceeds MOE_MAX_K=%d", k_stride, MOE_MAX_K);
+  if (dtype != MOE_F32 && dtype != MOE_BF16)
+    return fail(MOE_EINVAL, "dtype=%d is not MOE_F32 or MOE_BF16", dtype);
+  if ((int64_t)T * k_stride > kI32Max)
+    return fail(MOE_EUNSUPPORTED, "T*k_stride must be below 2^31");
+  if (T == 0 || d == 0) return MOE_OK;
+  if (!inv || !weights || !y) return fail(MOE_EINVAL, "inv, weights and y are required");
+  if (R > 0 && !Yp) return fail(MOE_EINVAL, "Yp is required when R > 0");
+  hipError_t e = moe::launch_combine(T, k_stride, d, dtype, Yp, R, inv, weights, shared, y,
+                                     dev_err, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail(e, "combine launch");
+  return MOE_OK;
+}
+
 }  // extern "C"

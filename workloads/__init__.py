@@ -10,7 +10,8 @@ shifts another):
 
 * ``numpy.random.default_rng([seed, stream])`` with streams
   0 = x, 1 = W, 2 = selection bias, 3 = per-request k, 4 = token ids,
-  5 = tid2eid table, 6 = Zipf rank permutation.
+  5 = tid2eid table, 6 = Zipf rank permutation, 7 = expert outputs,
+  8 = shared expert output.
 * x ~ N(0, 1) and W ~ N(0, 1/d) (std 1/sqrt(d), so logits are ~N(0, 1)),
   drawn as float32; bf16 inputs are the round-to-nearest-even of those
   float32 values.
@@ -20,6 +21,9 @@ shifts another):
   experts drawn uniformly without replacement.
 * Skewed load: ``logit_bias[e] = 2.0 * rank_e ** -1.1`` with ranks 1..E
   from a seeded permutation (a Zipf(s=1.1) ranking scaled to 2.0).
+* Combine inputs (no trained experts): the expert outputs in dispatch
+  order, ``Yp[R][d]``, and a shared expert's output ``[T][d]``, both
+  ~N(0, 1) in the workload's dtype -- hidden-state-sized rows, like x.
 
 The routing configurations follow the ones the pages describe: Mixtral
 (8 experts, top-2), Qwen3-MoE (128 experts), DeepSeek-V3 (256 experts in
@@ -34,7 +38,8 @@ from typing import Optional
 
 import numpy as np
 
-STREAM_X, STREAM_W, STREAM_BIAS, STREAM_K, STREAM_TOK, STREAM_TABLE, STREAM_ZIPF = range(7)
+(STREAM_X, STREAM_W, STREAM_BIAS, STREAM_K, STREAM_TOK, STREAM_TABLE, STREAM_ZIPF,
+ STREAM_YP, STREAM_SHARED) = range(9)
 
 # score-function names shared by both sides as plain strings
 SCORES = ("softmax", "sigmoid", "sqrt_softplus", "softmax_topk")
@@ -176,6 +181,16 @@ def make_inputs(w: Workload, seed: int = 0, T: Optional[int] = None) -> dict:
         out["token_ids"] = token_ids(seed, w.T, w.hash_vocab)
         out["tid2eid"] = tid2eid_table(seed, w.hash_vocab, w.k, w.E)
     return out
+
+
+def expert_outputs(w: Workload, R: int, seed: int = 0) -> np.ndarray:
+    """Yp[R][d]: synthetic expert outputs in dispatch order (workload dtype)."""
+    return draw_matrix(seed, STREAM_YP, (int(R), w.d), 1.0, w.dtype)
+
+
+def shared_output(w: Workload, seed: int = 0, T: Optional[int] = None) -> np.ndarray:
+    """[T][d]: a synthetic shared expert's output (workload dtype)."""
+    return draw_matrix(seed, STREAM_SHARED, (w.T if T is None else int(T), w.d), 1.0, w.dtype)
 
 
 def rows(x: np.ndarray, idx) -> np.ndarray:
