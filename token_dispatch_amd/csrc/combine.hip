@@ -11,15 +11,20 @@
 // dispatch wrote).  The work is a gather and a short reduction, HBM-bound:
 // every valid slot reads one row of d elements, every token writes one.
 //
-// One wavefront per token.  Lanes 0..k-1 read the token's inv and weights;
-// each valid slot's row index and weight then come to every lane with
-// readlane (scalar registers), in slot order.  Each lane owns 16-byte units
-// of the row (8 bf16 or 4 fp32), UPL of them per pass, and accumulates in
-// fp32 with one fma per element per slot: sum_j w_j * Y_j, slots in order,
-// then + shared.  Two slots' loads are issued before either is used.  The
-// result is stored in the input type (bf16: round to nearest even).  Rows
-// whose length is not a whole number of 16-byte units, or unaligned
+// One wavefront per (token, chunk of 64 16-byte units of its row).  Lanes
+// 0..k-1 read the token's inv and weights; each valid slot's row index and
+// weight then come to every lane with readlane (scalar registers), in slot
+// order.  The loads of up to 16 slots are issued together (one memory round
+// trip for a token's slots, not one per slot), then added in fp32 with one
+// fma per element per slot: sum_j w_j * Y_j, slots in order, then + shared.
+// The result is stored in the input type (bf16: round to nearest even).
+// Rows are read once and outputs written once, so 16-byte units go through
+// non-temporal loads and stores (Qwen3-like rows: 5.5 -> 6.2 TB/s;
+// DeepSeek-V3-like: 5.2 -> 6.5 TB/s).
+// Rows whose length is not a whole number of 16-byte units, or unaligned
 // pointers, take the same loop with one element per unit.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -27,7 +32,7 @@ namespace moe {
 namespace {
 
 constexpr int kCombineWaves = 4;
-constexpr int kUPL = 4;  // units per lane per pass
+constexpr int kSlotsInFlight = 16;  // slots whose rows are loaded together
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
@@ -41,10 +46,30 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
 }
 
 // One unit of a row: N = 8 (bf16) or 4 (fp32) elements from 16 bytes, or a
-// single element (N = 1).
+// single element (N = 1).  raw() loads it as it is in memory (so that many
+// units can be in flight in few registers), at() reads element i of it.
 template <class Elem, int N>
 struct Unit {
-  static constexpr int kBytes = N * (int)sizeof(Elem);
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  using Raw = std::conditional_t<(N > 1), u32x4, Elem>;
+  __device__ static Raw raw(const Elem* row, int64_t u) {
+    if constexpr (N > 1)  // read once: non-temporal
+      return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row) + u);
+    else
+      return row[u];
+  }
+  __device__ static float at(const Raw& q, int i) {
+    if constexpr (N == 1) {
+      if constexpr (sizeof(Elem) == 2)
+        return bf16_to_f32(q);
+      else
+        return q;
+    } else if constexpr (sizeof(Elem) == 2) {
+      return __uint_as_float(i % 2 ? q[i / 2] & 0xFFFF0000u : q[i / 2] << 16);
+    } else {
+      return __uint_as_float(q[i]);
+    }
+  }
   __device__ static void load(const Elem* row, int64_t u, float (&v)[N]) {
     if constexpr (N == 1) {
       if constexpr (sizeof(Elem) == 2)
@@ -82,21 +107,24 @@ struct Unit {
 #pragma unroll
         for (int i = 0; i < 4; ++i) q[i] = __float_as_uint(v[i]);
       }
-      reinterpret_cast<u32x4*>(row)[u] = q;
+      __builtin_nontemporal_store(q, reinterpret_cast<u32x4*>(row) + u);  // written once
     }
   }
 };
 
 // Elem: float or uint16_t (bf16 bits); N elements per unit (N * sizeof(Elem)
-// = 16, or 1).
+// = 16, or 1).  Wavefront g handles chunk c = g % nchunks (64 units) of the
+// row of token t = g / nchunks.
 template <class Elem, int N>
 __global__ __launch_bounds__(kCombineWaves * kWave) void combine_kernel(
-    int32_t T, int32_t k, int32_t d, const Elem* __restrict__ Yp, int32_t R,
+    int32_t T, int32_t k, int32_t d, int32_t nchunks, const Elem* __restrict__ Yp, int32_t R,
     const int32_t* __restrict__ inv, const float* __restrict__ weights,
     const Elem* __restrict__ shared, Elem* __restrict__ y, int32_t* __restrict__ dev_err) {
   using U = Unit<Elem, N>;
   const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * kCombineWaves + (threadIdx.x >> 6);
+  const int64_t g = (int64_t)blockIdx.x * kCombineWaves + (threadIdx.x >> 6);
+  const int64_t t = g / nchunks;
+  const int c = (int)(g - t * nchunks);
   if (t >= T) return;  // whole wavefronts leave together
 
   // the token's slots: lane j < k holds slot j
@@ -106,71 +134,52 @@ __global__ __launch_bounds__(kCombineWaves * kWave) void combine_kernel(
     p = inv[t * k + lane];
     w = weights[t * k + lane];
   }
-  const bool bad = lane < k && p >= R;
-  const uint64_t bad_mask = __ballot(bad);
-  if (bad_mask && lane == 0 && dev_err) atomicAdd(dev_err, (int)__popcll(bad_mask));
-  uint64_t slots = __ballot(lane < k && p >= 0 && p < R);  // valid slots, in order
+  if (c == 0) {  // one chunk of the token counts its bad slots
+    const uint64_t bad = __ballot(lane < k && p >= R);
+    if (bad && lane == 0 && dev_err) atomicAdd(dev_err, (int)__popcll(bad));
+  }
+  uint64_t rest = __ballot(lane < k && p >= 0 && p < R);  // valid slots, in order
 
   const int64_t units = d / N;  // N divides d
-  const Elem* sh = shared ? shared + t * d : nullptr;
-  Elem* out = y + t * d;
-  for (int64_t u0 = 0; u0 < units; u0 += (int64_t)kUPL * kWave) {
-    float acc[kUPL][N];
+  const int64_t u = (int64_t)c * kWave + lane;
+  const int64_t uc = u < units ? u : units - 1;  // clamped: loads stay in the row
+  float acc[N];
 #pragma unroll
-    for (int a = 0; a < kUPL; ++a)
+  for (int i = 0; i < N; ++i) acc[i] = 0.f;
+  while (rest) {  // up to kSlotsInFlight slots: all loads issued, then added in order
+    int32_t row[kSlotsInFlight];
+    float wt[kSlotsInFlight];
+    int m = 0;
 #pragma unroll
-      for (int i = 0; i < N; ++i) acc[a][i] = 0.f;
-    int64_t uu[kUPL];
-#pragma unroll
-    for (int a = 0; a < kUPL; ++a) {
-      const int64_t u = u0 + (int64_t)a * kWave + lane;
-      uu[a] = u < units ? u : units - 1;  // clamped: loads stay in the row
-    }
-    uint64_t rest = slots;
-    while (rest) {  // two slots per step, both loaded before either is used
-      const int j0 = __builtin_ctzll(rest);
-      rest &= rest - 1;
-      const int j1 = rest ? __builtin_ctzll(rest) : -1;
-      if (j1 >= 0) rest &= rest - 1;
-      const int32_t p0 = readlane_i32(p, j0);
-      const float w0 = readlane_f32(w, j0);
-      const int32_t p1 = j1 >= 0 ? readlane_i32(p, j1) : p0;
-      const float w1 = j1 >= 0 ? readlane_f32(w, j1) : 0.f;
-      const Elem* r0 = Yp + (int64_t)p0 * d;
-      const Elem* r1 = Yp + (int64_t)p1 * d;
-      float v0[kUPL][N], v1[kUPL][N];
-#pragma unroll
-      for (int a = 0; a < kUPL; ++a) U::load(r0, uu[a], v0[a]);
-      if (j1 >= 0) {
-#pragma unroll
-        for (int a = 0; a < kUPL; ++a) U::load(r1, uu[a], v1[a]);
-      }
-#pragma unroll
-      for (int a = 0; a < kUPL; ++a)
-#pragma unroll
-        for (int i = 0; i < N; ++i) acc[a][i] = fmaf(w0, v0[a][i], acc[a][i]);
-      if (j1 >= 0) {
-#pragma unroll
-        for (int a = 0; a < kUPL; ++a)
-#pragma unroll
-          for (int i = 0; i < N; ++i) acc[a][i] = fmaf(w1, v1[a][i], acc[a][i]);
+    for (int i = 0; i < kSlotsInFlight; ++i) {
+      row[i] = 0;
+      wt[i] = 0.f;
+      if (rest) {
+        const int j = __builtin_ctzll(rest);
+        rest &= rest - 1;
+        row[i] = readlane_i32(p, j);
+        wt[i] = readlane_f32(w, j);
+        m = i + 1;
       }
     }
-    if (sh) {
+    typename U::Raw v[kSlotsInFlight];
 #pragma unroll
-      for (int a = 0; a < kUPL; ++a) {
-        float s[N];
-        U::load(sh, uu[a], s);
+    for (int i = 0; i < kSlotsInFlight; ++i)
+      if (i < m) v[i] = U::raw(Yp + (int64_t)row[i] * d, uc);
 #pragma unroll
-        for (int i = 0; i < N; ++i) acc[a][i] += s[i];
+    for (int i = 0; i < kSlotsInFlight; ++i)
+      if (i < m) {
+#pragma unroll
+        for (int e = 0; e < N; ++e) acc[e] = fmaf(wt[i], U::at(v[i], e), acc[e]);
       }
-    }
-#pragma unroll
-    for (int a = 0; a < kUPL; ++a) {
-      const int64_t u = u0 + (int64_t)a * kWave + lane;
-      if (u < units) U::store(out, u, acc[a]);
-    }
   }
+  if (shared) {
+    float s[N];
+    U::load(shared + t * d, uc, s);
+#pragma unroll
+    for (int e = 0; e < N; ++e) acc[e] += s[e];
+  }
+  if (u < units) U::store(y + t * d, u, acc);
 }
 
 template <class Elem>
@@ -180,13 +189,17 @@ hipError_t launch_elem(int32_t T, int32_t k, int32_t d, const void* Yp, int32_t 
   constexpr int N = 16 / (int)sizeof(Elem);
   const auto a16 = [](const void* q) { return reinterpret_cast<uintptr_t>(q) % 16 == 0; };
   const bool vec = d % N == 0 && a16(Yp) && a16(y) && (!shared || a16(shared));
-  const dim3 grid((uint32_t)((T + kCombineWaves - 1) / kCombineWaves));
+  const int64_t units = vec ? d / N : d;
+  const int32_t nchunks = (int32_t)((units + kWave - 1) / kWave);
+  const int64_t waves = (int64_t)T * nchunks;
+  if ((waves + kCombineWaves - 1) / kCombineWaves > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid((uint32_t)((waves + kCombineWaves - 1) / kCombineWaves));
   const dim3 block(kCombineWaves * kWave);
   if (vec)
-    return launch(kStageCombine, combine_kernel<Elem, N>, grid, block, stream, T, k, d,
+    return launch(kStageCombine, combine_kernel<Elem, N>, grid, block, stream, T, k, d, nchunks,
                   static_cast<const Elem*>(Yp), R, inv, weights,
                   static_cast<const Elem*>(shared), static_cast<Elem*>(y), dev_err);
-  return launch(kStageCombine, combine_kernel<Elem, 1>, grid, block, stream, T, k, d,
+  return launch(kStageCombine, combine_kernel<Elem, 1>, grid, block, stream, T, k, d, nchunks,
                 static_cast<const Elem*>(Yp), R, inv, weights, static_cast<const Elem*>(shared),
                 static_cast<Elem*>(y), dev_err);
 }

@@ -406,6 +406,12 @@ __global__ __launch_bounds__(WM * WN * kWave) void gate_gemm_pipe_kernel(
     // rows past the end: an offset past the descriptor range reads zeros
     src_off[i] = grow < nrows ? grow * row_bytes + chunk_b[i] : 0x80000000u;
   }
+  // With the selection fused every tile spans all experts, so each x byte is
+  // read by one workgroup: its copies are non-temporal (the nt bit), which
+  // kept the gpt-oss-like gate at 83.5 instead of 85.8 us; with several
+  // expert tiles (x re-read from L2) or a large W it was slower (DeepSeek-
+  // V3-like 41 -> 46 us), so the other shapes keep the default policy.
+  constexpr int kXPolicy = EPI::kOn ? 2 : 0;
   auto issue = [&](int st) {  // st counts from st_begin
     uint8_t* buf = lds + ((st - st_begin) % NS) * STAGE;
     const uint32_t koff = st < st_end ? (uint32_t)st * RB : 0x80000000u;
@@ -416,7 +422,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void gate_gemm_pipe_kernel(
       const bool live = (src_off[i] | koff) < 0x80000000u && koff + chunk_b[i] < row_bytes;
       const uint32_t off = live ? src_off[i] + koff : 0x80000000u;
       if (src_is_x[i])
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, dst, 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, dst, 16, off, 0, 0, kXPolicy);
       else
         __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, dst, 16, off, 0, 0, 0);
     }
