@@ -64,16 +64,25 @@ def stage_bytes(w, T, R, R_valid, tile_bytes):
     }
 
 
+def source_digest(files):
+    """sha256 over the given source files, concatenated in order."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
 def measured_traffic(path, workload, stage):
     """HBM bytes per launch from the committed counter summary, or None when
-    there is none for this kernel or its source changed since it was taken."""
-    import hashlib
+    there is none for this kernel or its sources (the kernel's file and the
+    headers it is built with) changed since it was taken."""
     try:
         with open(path) as f:
             rec = json.load(f)[workload][stage]
-        with open(os.path.join(ROOT, rec["source"]), "rb") as f:
-            if hashlib.sha256(f.read()).hexdigest() != rec["sha256"]:
-                return None
+        if source_digest(rec["sources"]) != rec["sha256"]:
+            return None
         return rec["traffic_bytes"]
     except (OSError, KeyError, ValueError):
         return None

@@ -241,6 +241,9 @@ WORKLOAD_PLANS = {  # path, kernels per moe_route_dispatch call
     "dsv3_grouped": ("separate", 4),
     "dsv4": ("separate", 5),
     "gptoss_skew": ("fused", 2),
+    "dsv4_bias": ("separate", 5),
+    "olmoe": ("separate", 4),
+    "dsv3_groupmax": ("separate", 4),
 }
 
 

@@ -96,7 +96,7 @@ def test_gate_logits_exact_on_integers(dtype, T, d, E):
 # ---- the routing workloads at reduced T (full d and E) ----------------------------
 
 REDUCED = {"mixtral": 256, "qwen3_dynk": 700, "dsv3_grouped": 300, "dsv4": 260,
-           "gptoss_skew": 600}
+           "gptoss_skew": 600, "dsv4_bias": 260, "olmoe": 700, "dsv3_groupmax": 300}
 
 
 def route_case(w, inp):
@@ -217,7 +217,8 @@ def test_T0_and_determinism():
 
 # ---- full sizes, sampled tokens ------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["mixtral", "qwen3_dynk", "dsv3_grouped", "dsv4", "gptoss_skew"])
+@pytest.mark.parametrize("name", ["mixtral", "qwen3_dynk", "dsv3_grouped", "dsv4", "gptoss_skew",
+                                  "dsv4_bias", "olmoe", "dsv3_groupmax"])
 def test_workload_full_size_sampled(name):
     w = wl.WORKLOADS[name]
     inp = wl.make_inputs(w)

@@ -48,7 +48,8 @@ def assert_same(fused, sep):
                                         ("qwen3_dynk", 33, None), ("qwen3_dynk", None, "64"),
                                         ("qwen3_dynk", 4091, "64"), ("qwen3_dynk", 4091, "16"),
                                         ("mixtral", None, None), ("gptoss_skew", 3000, None),
-                                        ("dsv3_grouped", 700, None)])
+                                        ("dsv3_grouped", 700, None), ("dsv4_bias", 500, None),
+                                        ("olmoe", 1000, None), ("dsv3_groupmax", 700, None)])
 def test_route_dispatch_matches_separate_calls_and_oracle(name, T, lpt, monkeypatch):
     """The fused call (selection-written dispatch histograms where the shape
     allows) against separate moe_route + moe_dispatch calls and the oracle;

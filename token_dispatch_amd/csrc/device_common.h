@@ -91,10 +91,31 @@ __device__ __forceinline__ uint64_t peer_mask(int e) {
   return p;
 }
 
-__device__ __forceinline__ float sigmoid_f32(float l) { return 1.0f / (1.0f + expf(-l)); }
+// Score functions from the hardware base-2 exponential and logarithm,
+// reciprocal and square root (v_exp_f32, v_log_f32, v_rcp_f32, v_sqrt_f32,
+// about 1 ulp each) -- a selection bias or a group limit needs the score of
+// every expert of a token, and the library forms cost several times more:
+//   exp(x)      = 2^(x log2 e)  (the product adds about |x| 2^-24 relative)
+//   sigmoid(x)  = 1 / (1 + exp(-x))
+//   softplus(x) = max(x, 0) + log(1 + e),  e = exp(-|x|) in (0, 1]:
+//                 log(1 + e) = log2(1 + e) ln 2, or below e = 2^-7 the series
+//                 e - e^2/2 + e^3/3 (next term < 2^-30), where the rounding
+//                 of 1 + e would cost too much of the small result.
+// The error, a few 1e-7 relative, is far below the 1e-4 bar of scores and
+// weights.
+__device__ __forceinline__ float exp_fast(float x) {
+  return __builtin_amdgcn_exp2f(x * 1.44269504088896341f);
+}
+
+__device__ __forceinline__ float sigmoid_f32(float l) {
+  return __builtin_amdgcn_rcpf(1.0f + exp_fast(-l));
+}
 
 __device__ __forceinline__ float softplus_f32(float l) {
-  return fmaxf(l, 0.0f) + log1pf(expf(-fabsf(l)));
+  const float e = exp_fast(-fabsf(l));
+  const float lp = e < 0.0078125f ? e * (1.0f - e * (0.5f - e * (1.0f / 3.0f)))
+                                  : __builtin_amdgcn_logf(1.0f + e) * 0.693147180559945309f;
+  return fmaxf(l, 0.0f) + lp;
 }
 
 // Per-expert score for the element-wise score functions.  SOFTMAX needs the
@@ -102,7 +123,7 @@ __device__ __forceinline__ float softplus_f32(float l) {
 __device__ __forceinline__ float elementwise_score(int32_t score, float l) {
   switch (score) {
     case kSigmoid: return sigmoid_f32(l);
-    case kSqrtSoftplus: return sqrtf(softplus_f32(l));
+    case kSqrtSoftplus: return __builtin_amdgcn_sqrtf(softplus_f32(l));
     default: return l;
   }
 }

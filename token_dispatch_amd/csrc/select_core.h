@@ -204,7 +204,7 @@ __device__ __forceinline__ void select_token(
     m_all = S::max_f32(m);
     float s = 0.f;
 #pragma unroll
-    for (int j = 0; j < VPL; ++j) s += (j < nval) ? expf(lv[j] - m_all) : 0.f;
+    for (int j = 0; j < VPL; ++j) s += (j < nval) ? exp_fast(lv[j] - m_all) : 0.f;
     inv_sum_all = 1.0f / S::sum_f32(s);
   }
 
@@ -216,7 +216,7 @@ __device__ __forceinline__ void select_token(
     float q[VPL];
 #pragma unroll
     for (int j = 0; j < VPL; ++j) {
-      const float s = (c.score == kSoftmax) ? expf(lv[j] - m_all) * inv_sum_all
+      const float s = (c.score == kSoftmax) ? exp_fast(lv[j] - m_all) * inv_sum_all
                                             : elementwise_score(c.score, lv[j]);
       q[j] = (j < nval) ? s + sb[j] : -INFINITY;
     }
@@ -321,7 +321,7 @@ __device__ __forceinline__ void select_token(
   if (c.score == kSoftmax && need_full_softmax) {
 #pragma unroll
     for (int i = 0; i < KPL; ++i)
-      if (i < nslots) w[i] = pid[i] >= 0 ? expf(pl[i] - m_all) * inv_sum_all : 0.f;
+      if (i < nslots) w[i] = pid[i] >= 0 ? exp_fast(pl[i] - m_all) * inv_sum_all : 0.f;
   } else if (c.score == kSoftmax || c.score == kSoftmaxTopk) {
     // softmax restricted to the picked logits; for SOFTMAX it equals the
     // renormalised full softmax because the full denominator cancels

@@ -94,6 +94,21 @@ WORKLOADS = {
     "gptoss_skew": Workload("gptoss_skew", T=65536, d=2880, E=128, k=4,
                             dtype="bf16", score="softmax_topk",
                             zipf_offsets=True),
+    # Routing variants on the same kernels.  DeepSeek-V4-like with the
+    # selection-only bias and a weight scale (sqrt-softplus + bias, weights
+    # from the unbiased scores, renormalised, then scaled; the scale's value
+    # is not given, 1.5 stands in).
+    "dsv4_bias": Workload("dsv4_bias", T=16384, d=7168, E=384, k=6, dtype="bf16",
+                          score="sqrt_softplus", select_bias=True, route_scale=1.5),
+    # OLMoE-like: softmax over all 64 experts, top-8, probabilities kept as
+    # they are (not renormalised).
+    "olmoe": Workload("olmoe", T=4096, d=2048, E=64, k=8, dtype="bf16", score="softmax",
+                      renormalize=False),
+    # DeepSeek-V3-like grouping without a bias: each group scored by its
+    # largest sigmoid, keep 4 of 8, top-8, renormalised x2.5.
+    "dsv3_groupmax": Workload("dsv3_groupmax", T=8192, d=7168, E=256, k=8, dtype="bf16",
+                              score="sigmoid", n_groups=8, topk_groups=4, group_score="max",
+                              route_scale=2.5),
 }
 
 
