@@ -133,6 +133,23 @@ def cpu_baseline(w, inp, seconds, threads):
                       f"workload x {reps} ({what}, fp64), {total:.1f} s"}
 
 
+def combine_cpu_baseline(Yp, inv, weights, shared, seconds=3.0):
+    """Time the oracle's combine (fp64, one thread) on the first tokens."""
+    import oracle
+
+    T = weights.shape[0]
+    n = min(T, 64)
+    while True:
+        t0 = time.perf_counter()
+        oracle.combine(Yp, inv[:n], weights[:n], shared[:n])
+        t = time.perf_counter() - t0
+        if t >= seconds / 4 or n == T:
+            break
+        n = min(T, n * 4)
+    return {"value": n / t, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n} of {T} tokens (combine, fp64), {t:.2f} s"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -322,10 +339,11 @@ def main():
     combine = None
     if not args.no_combine and R_valid > 0:
         eb = 2 if w.dtype == "bf16" else 4
-        Y0 = up(wl.expert_outputs(w, R_valid))
+        Y_np, sh_np = wl.expert_outputs(w, R_valid), wl.shared_output(w)
+        Y0 = up(Y_np)
         n_yc = max(1, min(16, math.ceil(3 * LLC_BYTES / (R_valid * w.d * eb))))
         Ys = [Y0] + [torch.roll(Y0, shifts=89 * i, dims=0).contiguous() for i in range(1, n_yc)]
-        sh = up(wl.shared_output(w))
+        sh = up(sh_np)
         yout = torch.empty((T, w.d), dtype=Y0.dtype, device=dev)
         for i in range(20):
             tda.combine(Ys[i % n_yc], inv, weights, shared=sh, out=yout)
@@ -345,7 +363,10 @@ def main():
                    "unit": "GB/s", "frac": round(c_gbs / HBM_PEAK_GBS, 4), "rows": R_valid,
                    "d": w.d, "shared": True, "row_copies": n_yc}
         log(f"[bench] combine       {c_us:9.2f} us  {c_gbs:.1f} GB/s ({R_valid} rows of {w.d})")
-        del Ys, Y0
+        if not args.no_cpu_baseline:
+            combine["cpu_baseline"] = combine_cpu_baseline(
+                Y_np, inv.cpu().numpy().reshape(T, k), weights.cpu().numpy(), sh_np)
+        del Ys, Y0, Y_np
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -69,6 +69,8 @@ def _load():
         lib.orc_dispatch.restype = i32
         lib.orc_maxvio.argtypes = [vp, i32]
         lib.orc_maxvio.restype = ctypes.c_double
+        lib.orc_capacity.argtypes = [vp, i32, i32, i32, i32, vp, vp]
+        lib.orc_capacity.restype = i32
         lib.orc_combine.argtypes = [i32, i32, i32, i32, vp, i32, vp, vp, vp, vp]
         lib.orc_combine.restype = i32
         lib.orc_route_full.argtypes = [ctypes.POINTER(_Params)] + [vp] * 11 + [i32]
@@ -195,6 +197,17 @@ def dispatch(ids, E):
     R = int(offsets[E])
     return {"counts": counts, "offsets": offsets, "perm": perm[:R].copy(),
             "inv": inv[:T * ks].copy(), "nerr": int(nerr)}
+
+
+def capacity(ids, E, C):
+    """Capacity-limited dispatch: each expert keeps its first C routes in
+    route order.  Returns slot[T*k] (e*C + rank, or -1), kept[E], dropped."""
+    ids = _c(ids, np.int32)
+    T, ks = ids.shape
+    slot = np.empty(max(T * ks, 1), np.int32)
+    kept = np.empty(max(E, 1), np.int32)
+    dropped = _load().orc_capacity(_ptr(ids), T, ks, E, int(C), _ptr(slot), _ptr(kept))
+    return {"slot": slot[:T * ks].copy(), "kept": kept[:E].copy(), "dropped": int(dropped)}
 
 
 def combine(Yp, inv, weights, shared=None):

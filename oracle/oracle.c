@@ -318,6 +318,31 @@ double orc_maxvio(const int32_t* counts, int32_t E) {
   return (double)mx / ((double)R / (double)E) - 1.0;
 }
 
+/* ---- capacity: [router-survey] names top-1 routing with a capacity in the
+ * manner of the Switch Transformer and gives no rule; the plainest one: an
+ * expert takes its routes in route order (ascending r, the order of the
+ * stable dispatch) up to its capacity C and drops the rest.  A kept route
+ * of expert e with rank q among e's routes goes to slot e*C + q. */
+int32_t orc_capacity(const int32_t* ids, int32_t T, int32_t k_stride, int32_t E, int32_t C,
+                     int32_t* slot, int32_t* kept) {
+  const int64_t R = (int64_t)T * k_stride;
+  int32_t* seen = (int32_t*)calloc((size_t)(E > 0 ? E : 1), sizeof(int32_t));
+  int32_t dropped = 0;
+  for (int64_t r = 0; r < R; ++r) {
+    const int32_t e = ids[r];
+    slot[r] = -1;
+    if (e < 0 || e >= E) continue;  /* empty slot or error: not a route */
+    const int32_t q = seen[e]++;
+    if (q < C)
+      slot[r] = e * C + q;
+    else
+      ++dropped;
+  }
+  for (int32_t e = 0; e < E; ++e) kept[e] = seen[e] < C ? seen[e] : C;
+  free(seen);
+  return dropped;
+}
+
 /* ---- combine: [dyn-k] "Possible Implementation" (the output is the sum of
  * the selected experts' outputs, each times its weight) and [ferrox]
  * combine_expert_outputs (routed plus shared expert outputs of a token).

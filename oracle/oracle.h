@@ -21,7 +21,8 @@
  *            same gate scores.
  *  [router-survey] "I modelli MoE open hanno router opposti" (millebit.com):
  *            MaxVio as the load statistic; the routed-expert configurations;
- *            shared experts kept always on beside the routed ones.
+ *            shared experts kept always on beside the routed ones; top-1
+ *            routing with a Switch-style capacity.
  *  [ferrox] also: combine_expert_outputs (routed + shared outputs of a
  *            token); [dyn-k] "Possible Implementation": the output is the
  *            weighted sum of the selected experts' outputs.
@@ -104,6 +105,14 @@ int32_t orc_dispatch(const int32_t* ids, int32_t T, int32_t k_stride, int32_t E,
 
 /* MaxVio = max_e counts[e] / (R / E) - 1, R = sum of counts. */
 double orc_maxvio(const int32_t* counts, int32_t E);
+
+/* Capacity-limited dispatch: expert e keeps the first C of its routes in
+ * route order; route r of expert e with rank q < C gets slot[r] = e*C + q,
+ * a later route slot[r] = -1 (dropped); ids < 0 or >= E are not routes
+ * (slot -1, not counted).  kept[e] = min(routes of e, C).  Returns the
+ * number of dropped routes. */
+int32_t orc_capacity(const int32_t* ids, int32_t T, int32_t k_stride, int32_t E, int32_t C,
+                     int32_t* slot, int32_t* kept);
 
 /* Combine: y[t][i] = sum over slots j with 0 <= inv[t*k+j] < R of
  * weights[t][j] * Yp[inv[t*k+j]][i], plus shared[t][i] (weight 1) when
