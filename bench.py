@@ -61,6 +61,8 @@ def stage_bytes(w, T, R, R_valid, tile_bytes):
         "disp_hist": R * 4 + tile_bytes,
         "disp_scan": 2 * tile_bytes + E * 4,
         "disp_scatter": tile_bytes + E * 4 + R * 4 + R * 4 + R_valid * 4 + E * 8,
+        # capacity limit: ids and positions read, slots written, kept counts
+        "capacity": R * 12 + E * 8 + 4,
     }
 
 
@@ -232,6 +234,18 @@ def main():
         tda.route_dispatch(xs[i % n_copies], W, k, ids=ids, weights=weights, counts=counts,
                            offsets=offsets, perm=perm, inv=inv, workspace=ws, **rkw)
 
+    if w.capacity_factor:  # the dispatch ends with the capacity limit
+        C = wl.capacity(w)
+        slot = torch.empty(T * k, dtype=torch.int32, device=dev)
+        kept = torch.empty(E, dtype=torch.int32, device=dev)
+        dropped = torch.empty(1, dtype=torch.int32, device=dev)
+
+        def step(i):  # noqa: F811 -- moe_route_dispatch, then the capacity limit
+            tda.route_dispatch(xs[i % n_copies], W, k, ids=ids, weights=weights, counts=counts,
+                               offsets=offsets, perm=perm, inv=inv, workspace=ws, **rkw)
+            tda.dispatch_capacity(ids, E, C, offsets, inv, slot=slot, kept=kept,
+                                  dropped=dropped)
+
     disp_ws = ws_bytes - route_bytes  # the dispatch's tile data
     if w.hash_vocab:
         tok, tab = up(inp["token_ids"]), up(inp["tid2eid"])
@@ -390,7 +404,8 @@ def main():
                                f"score={w.score}, groups={w.n_groups}/{w.topk_groups}, "
                                + (f"hash ids from tid2eid[{w.hash_vocab}][{k}], "
                                   if w.hash_vocab else "")
-                               + f"dispatch over {E} experts",
+                               + f"dispatch over {E} experts"
+                               + (f" with capacity {wl.capacity(w)}" if w.capacity_factor else ""),
                    "T": T, "d": w.d, "E": E, "k_max": k, "x_copies": n_copies},
         "stages": stages,
         "maxvio": round(maxvio, 4),

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 7
+#define MOE_ABI_VERSION 8
 
 /* return codes */
 #define MOE_OK 0
@@ -213,6 +213,27 @@ int32_t moe_dispatch(const int32_t* ids, int32_t T, int32_t k_stride, int32_t E,
                      int32_t* dev_err, void* stream);
 
 /*
+ * moe_dispatch_capacity -- a capacity limit on a dispatch: top-1 routing with
+ * a capacity in the manner of the Switch Transformer ("I modelli MoE open
+ * hanno router opposti"; the page gives no rule, the one taken here: each
+ * expert keeps its first `capacity` routes in route order -- the order
+ * moe_dispatch places them in -- and drops the rest).
+ *   ids, offsets, inv  the ids given to moe_dispatch and its offsets[E+1]
+ *                and inv[T*k_stride] for them
+ *   slot     [T*k_stride] out: e*capacity + rank for a kept route of expert
+ *            e (rank among e's routes), -1 for a dropped route and for slots
+ *            that are not routes; it can serve as moe_combine's inv over
+ *            expert rows [E*capacity][d]
+ *   kept     [E] out: min(routes of e, capacity)
+ *   dropped  [1] out (device): routes over capacity
+ * Limits: E <= MOE_MAX_EXPERTS, E*capacity < 2^31, T*k_stride < 2^31.
+ * Returns MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED or MOE_EDEVICE.
+ */
+int32_t moe_dispatch_capacity(const int32_t* ids, int32_t T, int32_t k_stride, int32_t E,
+                              int32_t capacity, const int32_t* offsets, const int32_t* inv,
+                              int32_t* slot, int32_t* kept, int32_t* dropped, void* stream);
+
+/*
  * moe_route_dispatch -- moe_route followed by moe_dispatch of its ids
  * (k_stride = p->k): one pass of the router and the grouping of its routes,
  * with the results of the two calls (same arguments, same values, bit for
@@ -310,7 +331,8 @@ int32_t moe_combine(int32_t T, int32_t k_stride, int32_t d, int32_t dtype, const
 #define MOE_STAGE_GATE_SELECT 6  /* gate contraction with the selection fused */
 #define MOE_STAGE_SELECT_DISPATCH 7 /* selection + dispatch of a small batch */
 #define MOE_STAGE_COMBINE 8      /* combine of expert outputs */
-#define MOE_NUM_STAGES 9
+#define MOE_STAGE_CAPACITY 9     /* capacity limit on a dispatch */
+#define MOE_NUM_STAGES 10
 int32_t moe_profile_enable(int32_t enable);
 int32_t moe_profile_read(double* ms, int64_t* launches, int32_t n);
 

@@ -323,3 +323,17 @@ def test_combine_validation():
     assert L.moe_combine(3, 4, 16, 1, FAKE, 5, FAKE, FAKE, None, None, None, None) == tda.MOE_EINVAL
     assert L.moe_combine(3, 4, 16, 1, FAKE, 5, None, FAKE, None, FAKE, None, None) == tda.MOE_EINVAL
     assert L.moe_combine(1 << 30, 4, 16, 1, *ok) == tda.MOE_EUNSUPPORTED
+
+
+def test_capacity_validation():
+    L = tda.lib()
+    d = (FAKE, FAKE, FAKE, FAKE, FAKE, None)  # offsets, inv, slot, kept, dropped, stream
+    assert L.moe_dispatch_capacity(FAKE, -1, 1, 8, 4, *d) == tda.MOE_EINVAL
+    assert L.moe_dispatch_capacity(FAKE, 10, 0, 8, 4, *d) == tda.MOE_EINVAL
+    assert L.moe_dispatch_capacity(FAKE, 10, 1, 0, 4, *d) == tda.MOE_EINVAL
+    assert L.moe_dispatch_capacity(FAKE, 10, 1, tda.MAX_EXPERTS + 1, 4, *d) == tda.MOE_EUNSUPPORTED
+    assert L.moe_dispatch_capacity(FAKE, 10, 1, 8, -1, *d) == tda.MOE_EINVAL
+    assert "capacity" in L.moe_last_error().decode()
+    assert L.moe_dispatch_capacity(FAKE, 10, 1, 1024, 1 << 22, *d) == tda.MOE_EUNSUPPORTED
+    assert L.moe_dispatch_capacity(FAKE, 10, 1, 8, 4, None, FAKE, FAKE, FAKE, FAKE, None) == tda.MOE_EINVAL
+    assert L.moe_dispatch_capacity(None, 10, 1, 8, 4, *d) == tda.MOE_EINVAL

@@ -21,7 +21,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe_route.so")
 
-ABI_VERSION = 7
+ABI_VERSION = 8
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EDEVICE = 0, -1, -2, -3
 MAX_EXPERTS, MAX_K, MAX_GROUPS = 1024, 32, 64
 SCORES = {"softmax": 0, "sigmoid": 1, "sqrt_softplus": 2, "softmax_topk": 3}
@@ -30,14 +30,15 @@ EXPORTS = ("moe_route", "moe_route_workspace_size", "moe_route_hash",
            "moe_route_hash_workspace_size",
            "moe_dispatch_workspace_size", "moe_dispatch",
            "moe_route_dispatch", "moe_route_dispatch_workspace_size",
-           "moe_route_dispatch_plan", "moe_combine", "moe_profile_enable", "moe_profile_read",
+           "moe_route_dispatch_plan", "moe_combine", "moe_dispatch_capacity",
+           "moe_profile_enable", "moe_profile_read",
            "moe_last_error", "moe_abi_version")
 PATHS = ("separate", "select_hist", "fused", "small")
 PLAN_FIELDS = ("path", "gate_bm", "gate_bn", "gate_waves", "gate_splits", "gate_stage_bytes",
                "gate_ring_depth", "gate_lds_bytes", "select_lanes", "select_experts_per_lane",
                "hist_tokens", "kernels")
 STAGES = ("gate", "select", "hash", "disp_hist", "disp_scan", "disp_scatter", "gate_select",
-          "select_dispatch", "combine")
+          "select_dispatch", "combine", "capacity")
 
 
 class MoeError(RuntimeError):
@@ -88,6 +89,8 @@ def lib() -> ctypes.CDLL:
         L.moe_route_dispatch_plan.restype = i32
         L.moe_combine.argtypes = [i32, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp]
         L.moe_combine.restype = i32
+        L.moe_dispatch_capacity.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]
+        L.moe_dispatch_capacity.restype = i32
         L.moe_last_error.argtypes = []
         L.moe_last_error.restype = ctypes.c_char_p
         L.moe_profile_enable.argtypes = [i32]
@@ -354,6 +357,27 @@ def dispatch(ids: torch.Tensor, E: int, *, with_inv: bool = True, counts=None, o
     _check(lib().moe_dispatch(_p(ids), T, ks, E, _p(counts), _p(offsets), _p(perm), _p(inv),
                               _p(workspace), workspace.numel(), _p(dev_err), _stream(device)))
     return counts, offsets, perm, inv
+
+
+def dispatch_capacity(ids: torch.Tensor, E: int, capacity: int, offsets: torch.Tensor,
+                      inv: torch.Tensor, *, slot=None, kept=None, dropped=None):
+    """Capacity limit on a dispatch of ids (offsets, inv from dispatch): each
+    expert keeps its first `capacity` routes in route order.  Returns
+    (slot[T*k], kept[E], dropped[1]); slot = e*capacity + rank, or -1."""
+    _dev(ids, "ids", torch.int32)
+    T, ks = ids.shape
+    device = ids.device
+    _dev(offsets, "offsets", torch.int32)
+    _dev(inv, "inv", torch.int32)
+    if slot is None:
+        slot = torch.empty(T * ks, dtype=torch.int32, device=device)
+    if kept is None:
+        kept = torch.empty(E, dtype=torch.int32, device=device)
+    if dropped is None:
+        dropped = torch.empty(1, dtype=torch.int32, device=device)
+    _check(lib().moe_dispatch_capacity(_p(ids), T, ks, E, int(capacity), _p(offsets), _p(inv),
+                                       _p(slot), _p(kept), _p(dropped), _stream(device)))
+    return slot, kept, dropped
 
 
 def combine(Yp: torch.Tensor, inv: torch.Tensor, weights: torch.Tensor, *,

@@ -488,7 +488,54 @@ hipError_t launch_fused(const int32_t* ids, int64_t R, int32_t E, int32_t* count
                           stream);
 }
 
+// Capacity limit on a dispatch (top-1 routing with a Switch-style capacity;
+// the rule taken: each expert keeps its first C routes in route order).  The
+// stable dispatch puts route r of expert e at inv[r] = offsets[e] + (its rank
+// among e's routes), so slot[r] = e*C + rank when the rank is below C, else
+// -1.  Workgroup 0 also writes kept[e] = min(count_e, C) and the number of
+// routes over capacity.  Ids and positions are re-checked, so inputs that do
+// not come from one dispatch cannot lead outside the arrays.
+__global__ __launch_bounds__(kThreads) void disp_capacity_kernel(
+    const int32_t* __restrict__ ids, int64_t R, int32_t E, int32_t C,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ inv,
+    int32_t* __restrict__ slot, int32_t* __restrict__ kept, int32_t* __restrict__ dropped) {
+  const int64_t r = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (r < R) {
+    const int32_t p = inv[r];
+    int32_t s = -1;
+    if (p >= 0) {
+      const int32_t e = ids[r];
+      if (e >= 0 && e < E) {
+        const int32_t q = p - offsets[e];
+        if (q >= 0 && q < C) s = e * C + q;
+      }
+    }
+    slot[r] = s;
+  }
+  if (blockIdx.x == 0) {  // the whole workgroup: the barrier below is uniform
+    __shared__ int32_t part[kWaves];
+    int32_t over = 0;
+    for (int e = threadIdx.x; e < E; e += kThreads) {
+      const int32_t n = offsets[e + 1] - offsets[e];
+      kept[e] = min(n, C);
+      over += max(n - C, 0);
+    }
+    over = wave_sum_i32(over);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = over;
+    __syncthreads();
+    if (threadIdx.x == 0) *dropped = part[0] + part[1] + part[2] + part[3];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_capacity(const int32_t* ids, int64_t R, int32_t E, int32_t C,
+                           const int32_t* offsets, const int32_t* inv, int32_t* slot,
+                           int32_t* kept, int32_t* dropped, hipStream_t stream) {
+  const int64_t blocks = R > 0 ? (R + kThreads - 1) / kThreads : 1;
+  return launch(kStageCapacity, disp_capacity_kernel, dim3((uint32_t)blocks), dim3(kThreads),
+                stream, ids, R, E, C, offsets, inv, slot, kept, dropped);
+}
 
 bool dispatch_hist_ok(int64_t R, int32_t E, int32_t tile_routes) {
   if (R <= 0 || E % 8 != 0 || E > kMaxE) return false;

@@ -19,7 +19,8 @@ enum Stage : int32_t {
   kStageGateSelect = 6,
   kStageSelectDispatch = 7,
   kStageCombine = 8,
-  kNumStages = 9
+  kStageCapacity = 9,
+  kNumStages = 10
 };
 
 // Per-kernel timing (moe_profile_enable): the start/stop events of the next
@@ -154,6 +155,12 @@ hipError_t launch_dispatch_from_hist(const int32_t* ids, int64_t R, int32_t E,
 hipError_t launch_combine(int32_t T, int32_t k, int32_t d, int32_t dtype, const void* Yp,
                           int32_t R, const int32_t* inv, const float* weights,
                           const void* shared, void* y, int32_t* dev_err, hipStream_t stream);
+
+// Capacity limit on a dispatch: slot[r] = e*C + rank for the first C routes
+// of each expert (route order), else -1; kept[E]; *dropped (device).
+hipError_t launch_capacity(const int32_t* ids, int64_t R, int32_t E, int32_t C,
+                           const int32_t* offsets, const int32_t* inv, int32_t* slot,
+                           int32_t* kept, int32_t* dropped, hipStream_t stream);
 
 // Dispatch: tile histograms -> scan -> stable scatter.
 size_t dispatch_workspace_bytes(int64_t R, int32_t E);

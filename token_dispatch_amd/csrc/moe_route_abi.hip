@@ -518,4 +518,25 @@ int32_t moe_combine(int32_t T, int32_t k_stride, int32_t d, int32_t dtype, const
   return MOE_OK;
 }
 
+int32_t moe_dispatch_capacity(const int32_t* ids, int32_t T, int32_t k_stride, int32_t E,
+                              int32_t capacity, const int32_t* offsets, const int32_t* inv,
+                              int32_t* slot, int32_t* kept, int32_t* dropped, void* stream) {
+  if (T < 0) return fail(MOE_EINVAL, "T=%d must be >= 0", T);
+  if (k_stride < 1) return fail(MOE_EINVAL, "k_stride=%d must be >= 1", k_stride);
+  if (E < 1) return fail(MOE_EINVAL, "E=%d must be >= 1", E);
+  if (E > MOE_MAX_EXPERTS)
+    return fail(MOE_EUNSUPPORTED, "E=%d exceeds MOE_MAX_EXPERTS=%d", E, MOE_MAX_EXPERTS);
+  if (capacity < 0) return fail(MOE_EINVAL, "capacity=%d must be >= 0", capacity);
+  if ((int64_t)E * capacity > kI32Max)
+    return fail(MOE_EUNSUPPORTED, "E*capacity must be below 2^31");
+  const int64_t R = (int64_t)T * k_stride;
+  if (R > kI32Max) return fail(MOE_EUNSUPPORTED, "T*k_stride must be below 2^31");
+  if (!offsets || !kept || !dropped) return fail(MOE_EINVAL, "offsets, kept and dropped are required");
+  if (R > 0 && (!ids || !inv || !slot)) return fail(MOE_EINVAL, "ids, inv and slot are required");
+  hipError_t e = moe::launch_capacity(ids, R, E, capacity, offsets, inv, slot, kept, dropped,
+                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail(e, "capacity launch");
+  return MOE_OK;
+}
+
 }  // extern "C"

@@ -66,6 +66,7 @@ class Workload:
     zipf_s: float = 1.1
     zipf_scale: float = 2.0
     hash_vocab: int = 0         # >0: hash routing over this vocabulary
+    capacity_factor: float = 0  # >0: capacity-limited dispatch, C = ceil(f * T * k / E)
 
     def with_T(self, T: int) -> "Workload":
         return dataclasses.replace(self, T=int(T))
@@ -109,6 +110,12 @@ WORKLOADS = {
     "dsv3_groupmax": Workload("dsv3_groupmax", T=8192, d=7168, E=256, k=8, dtype="bf16",
                               score="sigmoid", n_groups=8, topk_groups=4, group_score="max",
                               route_scale=2.5),
+    # Top-1 of 128 routed experts (Llama-4-Maverick-like) with an expert
+    # capacity in the manner of the Switch Transformer: the chosen expert's
+    # softmax probability as its weight, capacity ceil(1.25 * T * k / E); the
+    # hidden size is not given, 4096 stands in.
+    "switch_top1": Workload("switch_top1", T=16384, d=4096, E=128, k=1, dtype="bf16",
+                            score="softmax", renormalize=False, capacity_factor=1.25),
 }
 
 
@@ -196,6 +203,11 @@ def make_inputs(w: Workload, seed: int = 0, T: Optional[int] = None) -> dict:
         out["token_ids"] = token_ids(seed, w.T, w.hash_vocab)
         out["tid2eid"] = tid2eid_table(seed, w.hash_vocab, w.k, w.E)
     return out
+
+
+def capacity(w: Workload) -> int:
+    """Expert capacity of a capacity-limited workload: ceil(f * T * k / E)."""
+    return int(np.ceil(w.capacity_factor * w.T * w.k / w.E))
 
 
 def expert_outputs(w: Workload, R: int, seed: int = 0) -> np.ndarray:
