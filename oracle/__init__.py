@@ -69,6 +69,10 @@ def _load():
         lib.orc_dispatch.restype = i32
         lib.orc_maxvio.argtypes = [vp, i32]
         lib.orc_maxvio.restype = ctypes.c_double
+        lib.orc_ep_layout.argtypes = [vp, i32, i32, vp, vp]
+        lib.orc_ep_layout.restype = None
+        lib.orc_permute_rows.argtypes = [i32, i32, i32, vp, vp, i32, vp]
+        lib.orc_permute_rows.restype = None
         lib.orc_capacity.argtypes = [vp, i32, i32, i32, i32, vp, vp]
         lib.orc_capacity.restype = i32
         lib.orc_combine.argtypes = [i32, i32, i32, i32, vp, i32, vp, vp, vp, vp]
@@ -197,6 +201,31 @@ def dispatch(ids, E):
     R = int(offsets[E])
     return {"counts": counts, "offsets": offsets, "perm": perm[:R].copy(),
             "inv": inv[:T * ks].copy(), "nerr": int(nerr)}
+
+
+def ep_layout(offsets, N):
+    """Per-rank send counts[N] and offsets[N+1] for N ranks owning E/N
+    contiguous experts each (offsets[E+1] from dispatch)."""
+    offsets = _c(offsets, np.int32)
+    E = offsets.shape[0] - 1
+    if N < 1 or E % N:
+        raise ValueError("N must divide E")
+    cnt = np.empty(N, np.int32)
+    off = np.empty(N + 1, np.int32)
+    _load().orc_ep_layout(_ptr(offsets), E, int(N), _ptr(cnt), _ptr(off))
+    return cnt, off
+
+
+def permute_rows(x, perm, k_stride):
+    """out[p] = x[perm[p] // k_stride] (fp64) for every p of perm."""
+    dtype = "bf16" if x.dtype == np.uint16 else "f32"
+    x = _c(x, np.uint16 if dtype == "bf16" else np.float32)
+    perm = _c(perm, np.int32)
+    R = perm.shape[0]
+    d = x.shape[1]
+    out = np.empty((R, d), np.float64)
+    _load().orc_permute_rows(int(k_stride), d, DTYPE[dtype], _ptr(x), _ptr(perm), R, _ptr(out))
+    return out
 
 
 def capacity(ids, E, C):

@@ -318,6 +318,25 @@ double orc_maxvio(const int32_t* counts, int32_t E) {
   return (double)mx / ((double)R / (double)E) - 1.0;
 }
 
+/* ---- expert parallelism: [router-survey] -- with experts spread over GPUs
+ * every routing choice becomes all-to-all traffic.  With N ranks owning E/N
+ * contiguous experts each, the dispatch order (by expert) is already the
+ * send order: rank n's share is the block of experts [n*E/N, (n+1)*E/N),
+ * and the send buffer holds each route's token row in dispatch order. */
+void orc_ep_layout(const int32_t* offsets, int32_t E, int32_t N, int32_t* send_counts,
+                   int32_t* send_offsets) {
+  for (int32_t n = 0; n <= N; ++n) send_offsets[n] = offsets[(int64_t)n * E / N];
+  for (int32_t n = 0; n < N; ++n) send_counts[n] = send_offsets[n + 1] - send_offsets[n];
+}
+
+void orc_permute_rows(int32_t k_stride, int32_t d, int32_t dtype, const void* x,
+                      const int32_t* perm, int32_t R, double* out) {
+  for (int32_t p = 0; p < R; ++p) {
+    const int32_t t = perm[p] / k_stride;
+    for (int32_t i = 0; i < d; ++i) out[(size_t)p * d + i] = input_at(dtype, x, (size_t)t * d + i);
+  }
+}
+
 /* ---- capacity: [router-survey] names top-1 routing with a capacity in the
  * manner of the Switch Transformer and gives no rule; the plainest one: an
  * expert takes its routes in route order (ascending r, the order of the

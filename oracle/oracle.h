@@ -22,7 +22,8 @@
  *  [router-survey] "I modelli MoE open hanno router opposti" (millebit.com):
  *            MaxVio as the load statistic; the routed-expert configurations;
  *            shared experts kept always on beside the routed ones; top-1
- *            routing with a Switch-style capacity.
+ *            routing with a Switch-style capacity; under expert parallelism
+ *            every routing choice becomes all-to-all traffic.
  *  [ferrox] also: combine_expert_outputs (routed + shared outputs of a
  *            token); [dyn-k] "Possible Implementation": the output is the
  *            weighted sum of the selected experts' outputs.
@@ -105,6 +106,17 @@ int32_t orc_dispatch(const int32_t* ids, int32_t T, int32_t k_stride, int32_t E,
 
 /* MaxVio = max_e counts[e] / (R / E) - 1, R = sum of counts. */
 double orc_maxvio(const int32_t* counts, int32_t E);
+
+/* Expert-parallel send layout over N ranks owning E/N contiguous experts
+ * each (N divides E): send_offsets[n] = offsets[n*E/N] (n <= N) and
+ * send_counts[n] = the routes of rank n's experts. */
+void orc_ep_layout(const int32_t* offsets, int32_t E, int32_t N, int32_t* send_counts,
+                   int32_t* send_offsets);
+
+/* The send buffer: out[p][i] = x[perm[p] / k_stride][i] for p < R (the
+ * token row of each route, in dispatch order); x is ORC_F32 or ORC_BF16. */
+void orc_permute_rows(int32_t k_stride, int32_t d, int32_t dtype, const void* x,
+                      const int32_t* perm, int32_t R, double* out);
 
 /* Capacity-limited dispatch: expert e keeps the first C of its routes in
  * route order; route r of expert e with rank q < C gets slot[r] = e*C + q,
