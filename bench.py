@@ -16,7 +16,9 @@ library's per-kernel timing) and the CPU oracle's throughput on a bounded
 sample of the same workload.  The combine that follows the experts (the
 weighted sum of each token's expert outputs, moe_combine) is not part of a
 step; it is timed separately on synthetic expert outputs in the step's
-dispatch order and reported with its own HBM fraction ("combine").
+dispatch order and reported with its own HBM fraction ("combine"), and so
+is the send buffer of token rows in dispatch order (moe_permute_rows,
+"permute").
 
 Usage: python bench.py [--steps K] [--warmup W] [--workload NAME]
 """
@@ -350,7 +352,7 @@ def main():
     # step): synthetic expert outputs in this step's dispatch order plus a
     # shared expert's output; rotating copies of the rows keep them from
     # being served out of the last-level cache
-    combine = None
+    combine = permute = None
     if not args.no_combine and R_valid > 0:
         eb = 2 if w.dtype == "bf16" else 4
         Y_np, sh_np = wl.expert_outputs(w, R_valid), wl.shared_output(w)
@@ -377,6 +379,32 @@ def main():
                    "unit": "GB/s", "frac": round(c_gbs / HBM_PEAK_GBS, 4), "rows": R_valid,
                    "d": w.d, "shared": True, "row_copies": n_yc}
         log(f"[bench] combine       {c_us:9.2f} us  {c_gbs:.1f} GB/s ({R_valid} rows of {w.d})")
+        # the send buffer (token rows in dispatch order, the all-to-all's
+        # input under expert parallelism), timed the same way
+        x0 = up(inp["x"])
+        n_xc = max(1, min(16, math.ceil(3 * LLC_BYTES / (T * w.d * eb))))
+        xs = [x0] + [torch.roll(x0, shifts=89 * i, dims=0).contiguous() for i in range(1, n_xc)]
+        sbuf = torch.empty((T * k, w.d), dtype=x0.dtype, device=dev)
+        for i in range(20):
+            tda.permute_rows(xs[i % n_xc], inv, k, T * k, out=sbuf)
+        torch.cuda.synchronize()
+        tda.profile_enable(True)
+        for i in range(n_c):
+            tda.permute_rows(xs[i % n_xc], inv, k, T * k, out=sbuf)
+        torch.cuda.synchronize()
+        pms, pn = tda.profile_read()["permute"]
+        tda.profile_enable(False)
+        p_us = pms / pn * 1e3
+        # each token row read once, every placed route's row written once,
+        # inv read
+        pbytes = T * w.d * eb + R_valid * w.d * eb + T * k * 4
+        p_gbs = pbytes / (p_us * 1e-6) / 1e9
+        permute = {"kernel": "permute", "avg_us": round(p_us, 3), "launches": pn,
+                   "bytes": pbytes, "achieved": round(p_gbs, 1), "peak": HBM_PEAK_GBS,
+                   "unit": "GB/s", "frac": round(p_gbs / HBM_PEAK_GBS, 4), "rows": R_valid,
+                   "d": w.d, "row_copies": n_xc}
+        log(f"[bench] permute       {p_us:9.2f} us  {p_gbs:.1f} GB/s ({R_valid} rows of {w.d})")
+        del sbuf, xs, x0
         if not args.no_cpu_baseline:
             combine["cpu_baseline"] = combine_cpu_baseline(
                 Y_np, inv.cpu().numpy().reshape(T, k), weights.cpu().numpy(), sh_np)
@@ -411,6 +439,7 @@ def main():
         "maxvio": round(maxvio, 4),
         "roofline": roofline,
         "combine": combine,
+        "permute": permute,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

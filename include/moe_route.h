@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 8
+#define MOE_ABI_VERSION 9
 
 /* return codes */
 #define MOE_OK 0
@@ -213,6 +213,41 @@ int32_t moe_dispatch(const int32_t* ids, int32_t T, int32_t k_stride, int32_t E,
                      int32_t* dev_err, void* stream);
 
 /*
+ * moe_permute_rows -- the send buffer: each route's token row at the place
+ * the dispatch gave the route, out[inv[r]] = x[r / k_stride] ("I modelli MoE
+ * open hanno router opposti": under expert parallelism every routing choice
+ * becomes all-to-all traffic; this buffer, in dispatch order, is what each
+ * rank sends, and on one GPU the grouped input of the experts).
+ *   x        [T][d] token rows (dtype MOE_F32 or MOE_BF16)
+ *   inv      [T*k_stride] the place of route r: moe_dispatch's inv (rows
+ *            0 .. offsets[E]-1 in dispatch order) or moe_dispatch_capacity's
+ *            slot (expert-major rows e*capacity + rank); inv[r] < 0: not
+ *            placed, skipped
+ *   out      [out_rows][d]; rows no route is placed at are not written; the
+ *            bytes of each row are copied unchanged.  Two routes placed at
+ *            one row race (the dispatch and capacity inverses never do)
+ *   dev_err  optional device counter: += places inv[r] >= out_rows (skipped)
+ * Each token row is read once, whatever its number of routes.
+ * Limits: T*k_stride < 2^31.  Returns MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED
+ * or MOE_EDEVICE.
+ */
+int32_t moe_permute_rows(int32_t T, int32_t k_stride, int32_t d, int32_t dtype, const void* x,
+                         const int32_t* inv, int32_t out_rows, void* out, int32_t* dev_err,
+                         void* stream);
+
+/*
+ * moe_ep_layout -- per-rank send counts and offsets for expert parallelism
+ * over n_ranks ranks owning E/n_ranks contiguous experts each (n_ranks
+ * divides E): send_offsets[n] = offsets[n*E/n_ranks] (n <= n_ranks),
+ * send_counts[n] = routes to rank n's experts.  The dispatch order is the
+ * send order, so rank n's rows are send_offsets[n] .. send_offsets[n+1] of
+ * moe_permute_rows' buffer.  offsets[E+1] from moe_dispatch; all device
+ * memory.  The exchange itself needs more than one GPU and is not here.
+ */
+int32_t moe_ep_layout(const int32_t* offsets, int32_t E, int32_t n_ranks, int32_t* send_counts,
+                      int32_t* send_offsets, void* stream);
+
+/*
  * moe_dispatch_capacity -- a capacity limit on a dispatch: top-1 routing with
  * a capacity in the manner of the Switch Transformer ("I modelli MoE open
  * hanno router opposti"; the page gives no rule, the one taken here: each
@@ -332,7 +367,9 @@ int32_t moe_combine(int32_t T, int32_t k_stride, int32_t d, int32_t dtype, const
 #define MOE_STAGE_SELECT_DISPATCH 7 /* selection + dispatch of a small batch */
 #define MOE_STAGE_COMBINE 8      /* combine of expert outputs */
 #define MOE_STAGE_CAPACITY 9     /* capacity limit on a dispatch */
-#define MOE_NUM_STAGES 10
+#define MOE_STAGE_PERMUTE 10     /* send buffer rows */
+#define MOE_STAGE_EP_LAYOUT 11   /* per-rank send layout */
+#define MOE_NUM_STAGES 12
 int32_t moe_profile_enable(int32_t enable);
 int32_t moe_profile_read(double* ms, int64_t* launches, int32_t n);
 

@@ -337,3 +337,23 @@ def test_capacity_validation():
     assert L.moe_dispatch_capacity(FAKE, 10, 1, 1024, 1 << 22, *d) == tda.MOE_EUNSUPPORTED
     assert L.moe_dispatch_capacity(FAKE, 10, 1, 8, 4, None, FAKE, FAKE, FAKE, FAKE, None) == tda.MOE_EINVAL
     assert L.moe_dispatch_capacity(None, 10, 1, 8, 4, *d) == tda.MOE_EINVAL
+
+
+def test_permute_and_ep_layout_validation():
+    L = tda.lib()
+    assert L.moe_permute_rows(0, 2, 16, 1, FAKE, FAKE, 8, FAKE, None, None) == tda.MOE_OK
+    assert L.moe_permute_rows(-1, 2, 16, 1, FAKE, FAKE, 8, FAKE, None, None) == tda.MOE_EINVAL
+    assert L.moe_permute_rows(4, 0, 16, 1, FAKE, FAKE, 8, FAKE, None, None) == tda.MOE_EINVAL
+    assert L.moe_permute_rows(4, 2, 16, 3, FAKE, FAKE, 8, FAKE, None, None) == tda.MOE_EINVAL
+    assert L.moe_permute_rows(4, 2, -1, 1, FAKE, FAKE, 8, FAKE, None, None) == tda.MOE_EINVAL
+    assert L.moe_permute_rows(4, 2, 16, 1, FAKE, FAKE, -1, FAKE, None, None) == tda.MOE_EINVAL
+    assert L.moe_permute_rows(4, 2, 16, 1, FAKE, None, 8, FAKE, None, None) == tda.MOE_EINVAL
+    assert L.moe_permute_rows(4, 2, 16, 1, None, FAKE, 8, FAKE, None, None) == tda.MOE_EINVAL
+    assert L.moe_permute_rows(4, 2, 16, 1, FAKE, FAKE, 8, None, None, None) == tda.MOE_EINVAL
+    assert "out" in L.moe_last_error().decode()
+    assert L.moe_permute_rows(1 << 30, 4, 16, 1, FAKE, FAKE, 8, FAKE, None, None) == tda.MOE_EUNSUPPORTED
+    assert L.moe_ep_layout(FAKE, 8, 3, FAKE, FAKE, None) == tda.MOE_EINVAL
+    assert "divide" in L.moe_last_error().decode()
+    assert L.moe_ep_layout(FAKE, 8, 0, FAKE, FAKE, None) == tda.MOE_EINVAL
+    assert L.moe_ep_layout(FAKE, 0, 1, FAKE, FAKE, None) == tda.MOE_EINVAL
+    assert L.moe_ep_layout(FAKE, 8, 2, FAKE, None, None) == tda.MOE_EINVAL

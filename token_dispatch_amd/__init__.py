@@ -21,7 +21,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe_route.so")
 
-ABI_VERSION = 8
+ABI_VERSION = 9
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EDEVICE = 0, -1, -2, -3
 MAX_EXPERTS, MAX_K, MAX_GROUPS = 1024, 32, 64
 SCORES = {"softmax": 0, "sigmoid": 1, "sqrt_softplus": 2, "softmax_topk": 3}
@@ -31,6 +31,7 @@ EXPORTS = ("moe_route", "moe_route_workspace_size", "moe_route_hash",
            "moe_dispatch_workspace_size", "moe_dispatch",
            "moe_route_dispatch", "moe_route_dispatch_workspace_size",
            "moe_route_dispatch_plan", "moe_combine", "moe_dispatch_capacity",
+           "moe_permute_rows", "moe_ep_layout",
            "moe_profile_enable", "moe_profile_read",
            "moe_last_error", "moe_abi_version")
 PATHS = ("separate", "select_hist", "fused", "small")
@@ -38,7 +39,7 @@ PLAN_FIELDS = ("path", "gate_bm", "gate_bn", "gate_waves", "gate_splits", "gate_
                "gate_ring_depth", "gate_lds_bytes", "select_lanes", "select_experts_per_lane",
                "hist_tokens", "kernels")
 STAGES = ("gate", "select", "hash", "disp_hist", "disp_scan", "disp_scatter", "gate_select",
-          "select_dispatch", "combine", "capacity")
+          "select_dispatch", "combine", "capacity", "permute", "ep_layout")
 
 
 class MoeError(RuntimeError):
@@ -91,6 +92,10 @@ def lib() -> ctypes.CDLL:
         L.moe_combine.restype = i32
         L.moe_dispatch_capacity.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]
         L.moe_dispatch_capacity.restype = i32
+        L.moe_permute_rows.argtypes = [i32, i32, i32, i32, vp, vp, i32, vp, vp, vp]
+        L.moe_permute_rows.restype = i32
+        L.moe_ep_layout.argtypes = [vp, i32, i32, vp, vp, vp]
+        L.moe_ep_layout.restype = i32
         L.moe_last_error.argtypes = []
         L.moe_last_error.restype = ctypes.c_char_p
         L.moe_profile_enable.argtypes = [i32]
@@ -357,6 +362,41 @@ def dispatch(ids: torch.Tensor, E: int, *, with_inv: bool = True, counts=None, o
     _check(lib().moe_dispatch(_p(ids), T, ks, E, _p(counts), _p(offsets), _p(perm), _p(inv),
                               _p(workspace), workspace.numel(), _p(dev_err), _stream(device)))
     return counts, offsets, perm, inv
+
+
+def permute_rows(x: torch.Tensor, inv: torch.Tensor, k_stride: int, out_rows: int, *,
+                 out: Optional[torch.Tensor] = None,
+                 dev_err: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Send buffer: out[inv[r]] = x[r // k_stride] for 0 <= inv[r] < out_rows
+    (dispatch's inv: dispatch order; dispatch_capacity's slot: expert-major
+    rows).  Rows no route is placed at are left as they are."""
+    _dev(x, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be [T][d]")
+    T, d = x.shape
+    dt = _dtype_code(x)
+    _dev(inv, "inv", torch.int32)
+    if inv.numel() != T * k_stride:
+        raise ValueError(f"inv has {inv.numel()} entries, expected T*k_stride={T * k_stride}")
+    if out is None:
+        out = torch.empty((out_rows, d), dtype=x.dtype, device=x.device)
+    _dev(out, "out", x.dtype, (out_rows, d))
+    if dev_err is not None:
+        _dev(dev_err, "dev_err", torch.int32)
+    _check(lib().moe_permute_rows(T, int(k_stride), d, dt, _p(x), _p(inv), int(out_rows),
+                                  _p(out), _p(dev_err), _stream(x.device)))
+    return out
+
+
+def ep_layout(offsets: torch.Tensor, n_ranks: int):
+    """Per-rank (send_counts[N], send_offsets[N+1]) for N ranks of E/N experts."""
+    _dev(offsets, "offsets", torch.int32)
+    E = offsets.numel() - 1
+    cnt = torch.empty(n_ranks, dtype=torch.int32, device=offsets.device)
+    off = torch.empty(n_ranks + 1, dtype=torch.int32, device=offsets.device)
+    _check(lib().moe_ep_layout(_p(offsets), E, int(n_ranks), _p(cnt), _p(off),
+                               _stream(offsets.device)))
+    return cnt, off
 
 
 def dispatch_capacity(ids: torch.Tensor, E: int, capacity: int, offsets: torch.Tensor,

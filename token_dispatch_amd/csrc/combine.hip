@@ -1,4 +1,7 @@
-// Combine on gfx950: the output row of each token is the weighted sum of the
+// Row movement around the experts on gfx950: the send buffer (token rows in
+// dispatch order) and its per-rank layout, and the combine.
+//
+// Combine: the output row of each token is the weighted sum of the
 // outputs its selected experts produced for it, plus a shared expert's
 // output.  Sources: "Feature Request: dynamic number of experts (hyperparam
 // per request)" (llama.cpp issue 13572), "Possible Implementation" -- the
@@ -204,7 +207,116 @@ hipError_t launch_elem(int32_t T, int32_t k, int32_t d, const void* Yp, int32_t 
                 static_cast<Elem*>(y), dev_err);
 }
 
+// The send buffer of expert parallelism ("I modelli MoE open hanno router
+// opposti": with experts spread over GPUs every routing choice becomes
+// all-to-all traffic; the dispatch order is the send order): the row of
+// route r is the hidden state of its token, placed at row inv[r] of out --
+// dispatch order with the dispatch's inverse, the expert-major slots
+// e*C + rank with a capacity limit's.  It is written from the token side:
+// each token row is read once and stored once per placed route, so x moves
+// over HBM once (T*d) and the buffer once (R*d); a gather over the dispatch
+// order would read each token row k times.
+// One wavefront per (token, 256 units of its row): each lane loads its 4
+// units (non-temporal: read once), lanes 0..63 read 64 of the token's
+// places at a time, and each placed route's row index comes to every lane
+// with readlane; the stores are non-temporal too (the buffer is written
+// once).  Bytes are moved as they are, in 16-byte units where rows and
+// pointers allow (U = u32x4), else in elements.
+constexpr int kPermuteUPL = 4;
+template <class U>
+__global__ __launch_bounds__(kCombineWaves * kWave) void permute_kernel(
+    int32_t T, int32_t k, int64_t units, int32_t nchunks, int32_t out_rows,
+    const U* __restrict__ x, const int32_t* __restrict__ inv, U* __restrict__ out,
+    int32_t* __restrict__ dev_err) {
+  const int lane = threadIdx.x & 63;
+  const int64_t g = (int64_t)blockIdx.x * kCombineWaves + (threadIdx.x >> 6);
+  const int64_t t = g / nchunks;
+  const int c = (int)(g - t * nchunks);
+  if (t >= T) return;  // whole wavefronts
+  U v[kPermuteUPL];
+#pragma unroll
+  for (int a = 0; a < kPermuteUPL; ++a) {
+    const int64_t u = ((int64_t)c * kPermuteUPL + a) * kWave + lane;
+    if (u < units) {
+      if constexpr (sizeof(U) == 16)
+        v[a] = __builtin_nontemporal_load(x + t * units + u);
+      else
+        v[a] = x[t * units + u];
+    }
+  }
+  for (int j0 = 0; j0 < k; j0 += kWave) {
+    const int n = min(kWave, k - j0);
+    const int32_t q_l = lane < n ? inv[t * k + j0 + lane] : -1;
+    if (c == 0 && lane == 0 && dev_err) {
+      int bad = 0;
+      for (int jj = 0; jj < n; ++jj) bad += inv[t * k + j0 + jj] >= out_rows;
+      if (bad) atomicAdd(dev_err, bad);
+    }
+    for (int jj = 0; jj < n; ++jj) {
+      const int32_t q = __builtin_amdgcn_readlane(q_l, jj);
+      if (q < 0 || q >= out_rows) continue;  // not placed, or no such row
+      U* __restrict__ row = out + (int64_t)q * units;
+#pragma unroll
+      for (int a = 0; a < kPermuteUPL; ++a) {
+        const int64_t u = ((int64_t)c * kPermuteUPL + a) * kWave + lane;
+        if (u < units) {
+          if constexpr (sizeof(U) == 16)
+            __builtin_nontemporal_store(v[a], row + u);
+          else
+            row[u] = v[a];
+        }
+      }
+    }
+  }
+}
+
+// Per-rank send counts and offsets: rank n owns experts [n*E/N, (n+1)*E/N),
+// so its block of the dispatch order starts at offsets[n*E/N].
+__global__ __launch_bounds__(256) void ep_layout_kernel(const int32_t* __restrict__ offsets,
+                                                        int32_t E, int32_t N,
+                                                        int32_t* __restrict__ send_counts,
+                                                        int32_t* __restrict__ send_offsets) {
+  for (int n = threadIdx.x; n <= N; n += 256) {
+    const int32_t o = offsets[(int64_t)n * E / N];
+    send_offsets[n] = o;
+    if (n < N) send_counts[n] = offsets[(int64_t)(n + 1) * E / N] - o;
+  }
+}
+
+template <class U>
+hipError_t launch_permute_units(int32_t T, int32_t k, int64_t units, const void* x,
+                                const int32_t* inv, int32_t out_rows, void* out,
+                                int32_t* dev_err, hipStream_t stream) {
+  const int32_t nchunks = (int32_t)((units + kPermuteUPL * kWave - 1) / (kPermuteUPL * kWave));
+  const int64_t blocks = ((int64_t)T * nchunks + kCombineWaves - 1) / kCombineWaves;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  return launch(kStagePermute, permute_kernel<U>, dim3((uint32_t)blocks),
+                dim3(kCombineWaves * kWave), stream, T, k, units, nchunks, out_rows,
+                static_cast<const U*>(x), inv, static_cast<U*>(out), dev_err);
+}
+
 }  // namespace
+
+hipError_t launch_permute(int32_t T, int32_t k, int32_t d, int32_t dtype, const void* x,
+                          const int32_t* inv, int32_t out_rows, void* out, int32_t* dev_err,
+                          hipStream_t stream) {
+  if (T == 0 || d == 0) return hipSuccess;
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const int64_t row_bytes = (int64_t)d * (dtype == 1 ? 2 : 4);
+  const auto a16 = [](const void* q) { return reinterpret_cast<uintptr_t>(q) % 16 == 0; };
+  if (row_bytes % 16 == 0 && a16(x) && a16(out))
+    return launch_permute_units<u32x4>(T, k, row_bytes / 16, x, inv, out_rows, out, dev_err,
+                                       stream);
+  if (dtype == 1)
+    return launch_permute_units<uint16_t>(T, k, d, x, inv, out_rows, out, dev_err, stream);
+  return launch_permute_units<uint32_t>(T, k, d, x, inv, out_rows, out, dev_err, stream);
+}
+
+hipError_t launch_ep_layout(const int32_t* offsets, int32_t E, int32_t N, int32_t* send_counts,
+                            int32_t* send_offsets, hipStream_t stream) {
+  return launch(kStageEpLayout, ep_layout_kernel, dim3(1), dim3(256), stream, offsets, E, N,
+                send_counts, send_offsets);
+}
 
 hipError_t launch_combine(int32_t T, int32_t k, int32_t d, int32_t dtype, const void* Yp,
                           int32_t R, const int32_t* inv, const float* weights,

@@ -20,7 +20,9 @@ enum Stage : int32_t {
   kStageSelectDispatch = 7,
   kStageCombine = 8,
   kStageCapacity = 9,
-  kNumStages = 10
+  kStagePermute = 10,
+  kStageEpLayout = 11,
+  kNumStages = 12
 };
 
 // Per-kernel timing (moe_profile_enable): the start/stop events of the next
@@ -155,6 +157,15 @@ hipError_t launch_dispatch_from_hist(const int32_t* ids, int64_t R, int32_t E,
 hipError_t launch_combine(int32_t T, int32_t k, int32_t d, int32_t dtype, const void* Yp,
                           int32_t R, const int32_t* inv, const float* weights,
                           const void* shared, void* y, int32_t* dev_err, hipStream_t stream);
+
+// Send buffer rows out[p] = x[perm[p] / k] for p < *count (device), out
+// sized for T*k rows; dtype 0 = fp32 / 1 = bf16.
+hipError_t launch_permute(int32_t T, int32_t k, int32_t d, int32_t dtype, const void* x,
+                          const int32_t* inv, int32_t out_rows, void* out, int32_t* dev_err,
+                          hipStream_t stream);
+// Per-rank send counts[N] and offsets[N+1] for N ranks of E/N experts.
+hipError_t launch_ep_layout(const int32_t* offsets, int32_t E, int32_t N, int32_t* send_counts,
+                            int32_t* send_offsets, hipStream_t stream);
 
 // Capacity limit on a dispatch: slot[r] = e*C + rank for the first C routes
 // of each expert (route order), else -1; kept[E]; *dropped (device).

@@ -539,4 +539,37 @@ int32_t moe_dispatch_capacity(const int32_t* ids, int32_t T, int32_t k_stride, i
   return MOE_OK;
 }
 
+int32_t moe_permute_rows(int32_t T, int32_t k_stride, int32_t d, int32_t dtype, const void* x,
+                         const int32_t* inv, int32_t out_rows, void* out, int32_t* dev_err,
+                         void* stream) {
+  if (T < 0) return fail(MOE_EINVAL, "T=%d must be >= 0", T);
+  if (k_stride < 1) return fail(MOE_EINVAL, "k_stride=%d must be >= 1", k_stride);
+  if (d < 0) return fail(MOE_EINVAL, "d=%d must be >= 0", d);
+  if (out_rows < 0) return fail(MOE_EINVAL, "out_rows=%d must be >= 0", out_rows);
+  if (dtype != MOE_F32 && dtype != MOE_BF16)
+    return fail(MOE_EINVAL, "dtype=%d is not MOE_F32 or MOE_BF16", dtype);
+  if ((int64_t)T * k_stride > kI32Max)
+    return fail(MOE_EUNSUPPORTED, "T*k_stride must be below 2^31");
+  if (T == 0 || d == 0) return MOE_OK;
+  if (!x || !inv) return fail(MOE_EINVAL, "x and inv are required");
+  if (out_rows > 0 && !out) return fail(MOE_EINVAL, "out is required when out_rows > 0");
+  hipError_t e = moe::launch_permute(T, k_stride, d, dtype, x, inv, out_rows, out, dev_err,
+                                     static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail(e, "permute launch");
+  return MOE_OK;
+}
+
+int32_t moe_ep_layout(const int32_t* offsets, int32_t E, int32_t n_ranks, int32_t* send_counts,
+                      int32_t* send_offsets, void* stream) {
+  if (E < 1) return fail(MOE_EINVAL, "E=%d must be >= 1", E);
+  if (n_ranks < 1 || E % n_ranks != 0)
+    return fail(MOE_EINVAL, "n_ranks=%d must divide E=%d", n_ranks, E);
+  if (!offsets || !send_counts || !send_offsets)
+    return fail(MOE_EINVAL, "offsets, send_counts and send_offsets are required");
+  hipError_t e = moe::launch_ep_layout(offsets, E, n_ranks, send_counts, send_offsets,
+                                       static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail(e, "ep layout launch");
+  return MOE_OK;
+}
+
 }  // extern "C"
