@@ -217,11 +217,13 @@ hipError_t launch_elem(int32_t T, int32_t k, int32_t d, const void* Yp, int32_t 
 // over HBM once (T*d) and the buffer once (R*d); a gather over the dispatch
 // order would read each token row k times.
 // One wavefront per (token, 256 units of its row): each lane loads its 4
-// units (non-temporal: read once), lanes 0..63 read 64 of the token's
-// places at a time, and each placed route's row index comes to every lane
-// with readlane; the stores are non-temporal too (the buffer is written
-// once).  Bytes are moved as they are, in 16-byte units where rows and
-// pointers allow (U = u32x4), else in elements.
+// units, lanes 0..63 read 64 of the token's places at a time, and each
+// placed route's row index comes to every lane with readlane; the stores are
+// non-temporal (the buffer is written once; non-temporal loads of x measured
+// 2-3% slower).  2, 4 or 8 units per lane and 2, 4 or 8 wavefronts per
+// workgroup all run within 5% of each other (4.8-5.4 TB/s): the stream of
+// row writes sets the pace.  Bytes are moved as they are, in 16-byte units
+// where rows and pointers allow (U = u32x4), else in elements.
 constexpr int kPermuteUPL = 4;
 template <class U>
 __global__ __launch_bounds__(kCombineWaves * kWave) void permute_kernel(
@@ -237,12 +239,7 @@ __global__ __launch_bounds__(kCombineWaves * kWave) void permute_kernel(
 #pragma unroll
   for (int a = 0; a < kPermuteUPL; ++a) {
     const int64_t u = ((int64_t)c * kPermuteUPL + a) * kWave + lane;
-    if (u < units) {
-      if constexpr (sizeof(U) == 16)
-        v[a] = __builtin_nontemporal_load(x + t * units + u);
-      else
-        v[a] = x[t * units + u];
-    }
+    if (u < units) v[a] = x[t * units + u];
   }
   for (int j0 = 0; j0 < k; j0 += kWave) {
     const int n = min(kWave, k - j0);
