@@ -61,9 +61,11 @@ def rand_case(rng, T, k, R, d, dtype, empty=0.2):
 @pytest.mark.parametrize("shared", [False, True], ids=["routed", "routed+shared"])
 @pytest.mark.parametrize("T,k,R,d", [(1, 1, 1, 8), (37, 2, 50, 64), (130, 8, 700, 2048),
                                      (61, 16, 400, 2880), (9, 32, 300, 1000),
-                                     (21, 4, 90, 100), (5, 3, 7, 7)])
+                                     (21, 4, 90, 100), (5, 3, 7, 7), (13, 2, 40, 2056),
+                                     (17, 3, 60, 2888), (9, 1, 20, 4104), (6, 5, 30, 520)])
 def test_combine_random(dtype, shared, T, k, R, d):
-    """Several 16-byte passes per row, ragged rows (scalar units), every k."""
+    """Several 16-byte passes per row, ragged rows (scalar units), every k;
+    k <= 2 and k <= 4 (4 and 2 units per lane) with a ragged last chunk."""
     rng = np.random.default_rng([T, k, R, d])
     Yp, inv, w = rand_case(rng, T, k, R, d, dtype)
     sh = as_dtype(rng.standard_normal((T, d)).astype(np.float32), dtype) if shared else None

@@ -14,16 +14,18 @@
 // dispatch wrote).  The work is a gather and a short reduction, HBM-bound:
 // every valid slot reads one row of d elements, every token writes one.
 //
-// One wavefront per (token, chunk of 64 16-byte units of its row).  Lanes
-// 0..k-1 read the token's inv and weights; each valid slot's row index and
-// weight then come to every lane with readlane (scalar registers), in slot
-// order.  The loads of up to 16 slots are issued together (one memory round
-// trip for a token's slots, not one per slot), then added in fp32 with one
-// fma per element per slot: sum_j w_j * Y_j, slots in order, then + shared.
+// One wavefront per (token, chunk of 64 x UPL 16-byte units of its row).
+// Lanes 0..k-1 read the token's inv and weights; each valid slot's row index
+// and weight then come to every lane with readlane (scalar registers), in
+// slot order.  The loads of up to 16 row pieces per lane (16 / UPL slots)
+// are issued together with the shared row's (one memory round trip for a
+// token's slots, not one per slot), then added in fp32 with one fma per
+// element per slot: sum_j w_j * Y_j, slots in order, then + shared.
 // The result is stored in the input type (bf16: round to nearest even).
-// Rows are read once and outputs written once, so 16-byte units go through
-// non-temporal loads and stores (Qwen3-like rows: 5.5 -> 6.2 TB/s;
-// DeepSeek-V3-like: 5.2 -> 6.5 TB/s).
+// Expert rows are read once and outputs written once, so 16-byte units go
+// through non-temporal loads and stores (Qwen3-like rows: 5.5 -> 6.2 TB/s;
+// DeepSeek-V3-like: 5.2 -> 6.5 TB/s); the shared rows keep the default
+// policy.
 // Rows whose length is not a whole number of 16-byte units, or unaligned
 // pointers, take the same loop with one element per unit.
 #include <type_traits>
@@ -49,8 +51,9 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
 }
 
 // One unit of a row: N = 8 (bf16) or 4 (fp32) elements from 16 bytes, or a
-// single element (N = 1).  raw() loads it as it is in memory (so that many
-// units can be in flight in few registers), at() reads element i of it.
+// single element (N = 1).  raw() and raw_cached() load it as it is in memory
+// (so that many units can be in flight in few registers; raw() is
+// non-temporal), at() reads element i of it.
 template <class Elem, int N>
 struct Unit {
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -58,6 +61,12 @@ struct Unit {
   __device__ static Raw raw(const Elem* row, int64_t u) {
     if constexpr (N > 1)  // read once: non-temporal
       return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row) + u);
+    else
+      return row[u];
+  }
+  __device__ static Raw raw_cached(const Elem* row, int64_t u) {
+    if constexpr (N > 1)
+      return reinterpret_cast<const u32x4*>(row)[u];
     else
       return row[u];
   }
@@ -71,27 +80,6 @@ struct Unit {
       return __uint_as_float(i % 2 ? q[i / 2] & 0xFFFF0000u : q[i / 2] << 16);
     } else {
       return __uint_as_float(q[i]);
-    }
-  }
-  __device__ static void load(const Elem* row, int64_t u, float (&v)[N]) {
-    if constexpr (N == 1) {
-      if constexpr (sizeof(Elem) == 2)
-        v[0] = bf16_to_f32(row[u]);
-      else
-        v[0] = row[u];
-    } else {
-      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-      const u32x4 q = reinterpret_cast<const u32x4*>(row)[u];
-      if constexpr (sizeof(Elem) == 2) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v[2 * i] = __uint_as_float(q[i] << 16);
-          v[2 * i + 1] = __uint_as_float(q[i] & 0xFFFF0000u);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(q[i]);
-      }
     }
   }
   __device__ static void store(Elem* row, int64_t u, const float (&v)[N]) {
@@ -116,14 +104,18 @@ struct Unit {
 };
 
 // Elem: float or uint16_t (bf16 bits); N elements per unit (N * sizeof(Elem)
-// = 16, or 1).  Wavefront g handles chunk c = g % nchunks (64 units) of the
-// row of token t = g / nchunks.
-template <class Elem, int N>
+// = 16, or 1); UPL units per lane, so wavefront g handles chunk
+// c = g % nchunks (UPL * 64 units) of the row of token t = g / nchunks.
+// Slots are loaded kSlotsInFlight / UPL at a time: the row pieces in flight
+// per wavefront stay at 16 (registers), and few slots (k = 1, 2) still
+// keep several pieces in flight.
+template <class Elem, int N, int UPL>
 __global__ __launch_bounds__(kCombineWaves * kWave) void combine_kernel(
     int32_t T, int32_t k, int32_t d, int32_t nchunks, const Elem* __restrict__ Yp, int32_t R,
     const int32_t* __restrict__ inv, const float* __restrict__ weights,
     const Elem* __restrict__ shared, Elem* __restrict__ y, int32_t* __restrict__ dev_err) {
   using U = Unit<Elem, N>;
+  constexpr int kSIF = kSlotsInFlight / UPL;
   const int lane = threadIdx.x & 63;
   const int64_t g = (int64_t)blockIdx.x * kCombineWaves + (threadIdx.x >> 6);
   const int64_t t = g / nchunks;
@@ -144,17 +136,30 @@ __global__ __launch_bounds__(kCombineWaves * kWave) void combine_kernel(
   uint64_t rest = __ballot(lane < k && p >= 0 && p < R);  // valid slots, in order
 
   const int64_t units = d / N;  // N divides d
-  const int64_t u = (int64_t)c * kWave + lane;
-  const int64_t uc = u < units ? u : units - 1;  // clamped: loads stay in the row
-  float acc[N];
+  int64_t uc[UPL];  // clamped: loads stay in the row
 #pragma unroll
-  for (int i = 0; i < N; ++i) acc[i] = 0.f;
-  while (rest) {  // up to kSlotsInFlight slots: all loads issued, then added in order
-    int32_t row[kSlotsInFlight];
-    float wt[kSlotsInFlight];
+  for (int a = 0; a < UPL; ++a) {
+    const int64_t u = ((int64_t)c * UPL + a) * kWave + lane;
+    uc[a] = u < units ? u : units - 1;
+  }
+  // the shared row's loads go out first, with the first slots', through the
+  // cache (non-temporal loads of the shared rows measured 8-15% slower)
+  typename U::Raw sh[UPL];
+  if (shared) {
+#pragma unroll
+    for (int a = 0; a < UPL; ++a) sh[a] = U::raw_cached(shared + t * d, uc[a]);
+  }
+  float acc[UPL][N];
+#pragma unroll
+  for (int a = 0; a < UPL; ++a)
+#pragma unroll
+    for (int i = 0; i < N; ++i) acc[a][i] = 0.f;
+  while (rest) {  // up to kSIF slots: all loads issued, then added in order
+    int32_t row[kSIF];
+    float wt[kSIF];
     int m = 0;
 #pragma unroll
-    for (int i = 0; i < kSlotsInFlight; ++i) {
+    for (int i = 0; i < kSIF; ++i) {
       row[i] = 0;
       wt[i] = 0.f;
       if (rest) {
@@ -165,24 +170,46 @@ __global__ __launch_bounds__(kCombineWaves * kWave) void combine_kernel(
         m = i + 1;
       }
     }
-    typename U::Raw v[kSlotsInFlight];
+    typename U::Raw v[kSIF][UPL];
 #pragma unroll
-    for (int i = 0; i < kSlotsInFlight; ++i)
-      if (i < m) v[i] = U::raw(Yp + (int64_t)row[i] * d, uc);
-#pragma unroll
-    for (int i = 0; i < kSlotsInFlight; ++i)
+    for (int i = 0; i < kSIF; ++i)
       if (i < m) {
 #pragma unroll
-        for (int e = 0; e < N; ++e) acc[e] = fmaf(wt[i], U::at(v[i], e), acc[e]);
+        for (int a = 0; a < UPL; ++a) v[i][a] = U::raw(Yp + (int64_t)row[i] * d, uc[a]);
+      }
+#pragma unroll
+    for (int i = 0; i < kSIF; ++i)
+      if (i < m) {
+#pragma unroll
+        for (int a = 0; a < UPL; ++a)
+#pragma unroll
+          for (int e = 0; e < N; ++e) acc[a][e] = fmaf(wt[i], U::at(v[i][a], e), acc[a][e]);
       }
   }
-  if (shared) {
-    float s[N];
-    U::load(shared + t * d, uc, s);
 #pragma unroll
-    for (int e = 0; e < N; ++e) acc[e] += s[e];
+  for (int a = 0; a < UPL; ++a) {
+    if (shared) {
+#pragma unroll
+      for (int e = 0; e < N; ++e) acc[a][e] += U::at(sh[a], e);
+    }
+    const int64_t u = ((int64_t)c * UPL + a) * kWave + lane;
+    if (u < units) U::store(y + t * d, u, acc[a]);
   }
-  if (u < units) U::store(y + t * d, u, acc);
+}
+
+template <class Elem, int N, int UPL>
+hipError_t launch_combine_upl(int32_t T, int32_t k, int32_t d, int64_t units, const void* Yp,
+                              int32_t R, const int32_t* inv, const float* weights,
+                              const void* shared, void* y, int32_t* dev_err,
+                              hipStream_t stream) {
+  const int32_t nchunks = (int32_t)((units + UPL * kWave - 1) / (UPL * kWave));
+  const int64_t waves = (int64_t)T * nchunks;
+  if ((waves + kCombineWaves - 1) / kCombineWaves > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid((uint32_t)((waves + kCombineWaves - 1) / kCombineWaves));
+  const dim3 block(kCombineWaves * kWave);
+  return launch(kStageCombine, combine_kernel<Elem, N, UPL>, grid, block, stream, T, k, d,
+                nchunks, static_cast<const Elem*>(Yp), R, inv, weights,
+                static_cast<const Elem*>(shared), static_cast<Elem*>(y), dev_err);
 }
 
 template <class Elem>
@@ -192,19 +219,21 @@ hipError_t launch_elem(int32_t T, int32_t k, int32_t d, const void* Yp, int32_t 
   constexpr int N = 16 / (int)sizeof(Elem);
   const auto a16 = [](const void* q) { return reinterpret_cast<uintptr_t>(q) % 16 == 0; };
   const bool vec = d % N == 0 && a16(Yp) && a16(y) && (!shared || a16(shared));
-  const int64_t units = vec ? d / N : d;
-  const int32_t nchunks = (int32_t)((units + kWave - 1) / kWave);
-  const int64_t waves = (int64_t)T * nchunks;
-  if ((waves + kCombineWaves - 1) / kCombineWaves > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const dim3 grid((uint32_t)((waves + kCombineWaves - 1) / kCombineWaves));
-  const dim3 block(kCombineWaves * kWave);
-  if (vec)
-    return launch(kStageCombine, combine_kernel<Elem, N>, grid, block, stream, T, k, d, nchunks,
-                  static_cast<const Elem*>(Yp), R, inv, weights,
-                  static_cast<const Elem*>(shared), static_cast<Elem*>(y), dev_err);
-  return launch(kStageCombine, combine_kernel<Elem, 1>, grid, block, stream, T, k, d, nchunks,
-                static_cast<const Elem*>(Yp), R, inv, weights, static_cast<const Elem*>(shared),
-                static_cast<Elem*>(y), dev_err);
+  if (!vec)
+    return launch_combine_upl<Elem, 1, 1>(T, k, d, d, Yp, R, inv, weights, shared, y, dev_err,
+                                          stream);
+  // units per lane by slot count: 1 or 2 slots take 4, 3 or 4 take 2 (a
+  // Switch-like top-1 combine 88.7 -> 61.9 us, gpt-oss-like k = 4
+  // 374 -> 363 us; 5 or more slots fill the loads with one unit per lane)
+  const int64_t units = d / N;
+  if (k <= 2)
+    return launch_combine_upl<Elem, N, 4>(T, k, d, units, Yp, R, inv, weights,
+                                      shared, y, dev_err, stream);
+  if (k <= 4)
+    return launch_combine_upl<Elem, N, 2>(T, k, d, units, Yp, R, inv, weights,
+                                      shared, y, dev_err, stream);
+  return launch_combine_upl<Elem, N, 1>(T, k, d, units, Yp, R, inv, weights, shared, y,
+                                        dev_err, stream);
 }
 
 // The send buffer of expert parallelism ("I modelli MoE open hanno router
