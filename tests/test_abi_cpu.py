@@ -244,6 +244,7 @@ WORKLOAD_PLANS = {  # path, kernels per moe_route_dispatch call
     "dsv4_bias": ("separate", 5),
     "olmoe": ("separate", 4),
     "dsv3_groupmax": ("separate", 4),
+    "switch_top1": ("separate", 4),
 }
 
 
