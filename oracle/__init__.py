@@ -43,7 +43,8 @@ class _Params(ctypes.Structure):
                 ("k", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("score", ctypes.c_int32), ("n_groups", ctypes.c_int32),
                 ("topk_groups", ctypes.c_int32), ("group_score", ctypes.c_int32),
-                ("renormalize", ctypes.c_int32), ("route_scale", ctypes.c_double)]
+                ("renormalize", ctypes.c_int32), ("route_scale", ctypes.c_double),
+                ("k_per_group", ctypes.c_int32)]
 
 
 _lib = None
@@ -92,17 +93,22 @@ def _c(a, dtype):
 
 
 def _params(T, d, E, k, dtype="f32", score="softmax", n_groups=1, topk_groups=None,
-            group_score="max", renormalize=True, route_scale=1.0):
+            group_score="max", renormalize=True, route_scale=1.0, k_per_group=0):
     if topk_groups is None:
         topk_groups = n_groups
     return _Params(int(T), int(d), int(E), int(k), DTYPE[dtype], SCORE[score],
                    int(n_groups), int(topk_groups), GROUP[group_score],
-                   int(bool(renormalize)), float(route_scale))
+                   int(bool(renormalize)), float(route_scale), int(k_per_group))
 
 
-def _check_route_args(E, k, n_groups, topk_groups, group_score):
+def _check_route_args(E, k, n_groups, topk_groups, group_score, k_per_group=0):
     if topk_groups is None:
         topk_groups = n_groups
+    if k_per_group:
+        if k_per_group < 0 or topk_groups != n_groups:
+            raise ValueError("k_per_group > 0 takes no group limit (topk_groups = n_groups)")
+        if k > n_groups * min(k_per_group, E // max(n_groups, 1)):
+            raise ValueError("k exceeds the experts the groups keep")
     if E < 1 or k < 1:
         raise ValueError("need E >= 1 and k >= 1")
     if n_groups < 1 or E % n_groups:
@@ -134,17 +140,18 @@ def gate(x, W, logit_bias=None, dtype=None):
 
 def route_logits(logits, k, score="softmax", select_bias=None, k_per_token=None,
                  n_groups=1, topk_groups=None, group_score=None, renormalize=True,
-                 route_scale=1.0):
+                 route_scale=1.0, k_per_group=0):
     """Select and weight from fp64 logits.  Returns a dict with ids, weights,
     margin_k, margin_g, margin_s, margin_o, q (masked selection quantity),
-    g (group scores) and nbad (tokens with k_t outside [1, k])."""
+    g (group scores; with k_per_group, each group's last kept q) and nbad
+    (tokens with k_t outside [1, k])."""
     logits = _c(logits, np.float64)
     T, E = logits.shape
-    if group_score is None:
-        group_score = "top2_sum" if select_bias is not None else "max"
-    _check_route_args(E, k, n_groups, topk_groups, group_score)
+    if group_score is None or k_per_group:
+        group_score = "top2_sum" if select_bias is not None and not k_per_group else "max"
+    _check_route_args(E, k, n_groups, topk_groups, group_score, k_per_group)
     p = _params(T, 1, E, k, "f32", score, n_groups, topk_groups, group_score,
-                renormalize, route_scale)
+                renormalize, route_scale, k_per_group)
     ids = np.empty((T, k), np.int32)
     w = np.empty((T, k), np.float64)
     mk, mg, ms, mo = (np.empty(T, np.float64) for _ in range(4))
@@ -270,7 +277,7 @@ def maxvio(counts):
 
 def route_full(x, W, k, *, score, logit_bias=None, select_bias=None, k_per_token=None,
                n_groups=1, topk_groups=None, group_score=None, renormalize=True,
-               route_scale=1.0, nthreads=None):
+               route_scale=1.0, k_per_group=0, nthreads=None):
     """Whole path (gate + route + dispatch) on nthreads host threads."""
     dtype = "bf16" if x.dtype == np.uint16 else "f32"
     npdt = np.uint16 if dtype == "bf16" else np.float32
@@ -278,13 +285,13 @@ def route_full(x, W, k, *, score, logit_bias=None, select_bias=None, k_per_token
     W = _c(W, npdt)
     T, d = x.shape
     E = W.shape[0]
-    if group_score is None:
-        group_score = "top2_sum" if select_bias is not None else "max"
-    _check_route_args(E, k, n_groups, topk_groups, group_score)
+    if group_score is None or k_per_group:
+        group_score = "top2_sum" if select_bias is not None and not k_per_group else "max"
+    _check_route_args(E, k, n_groups, topk_groups, group_score, k_per_group)
     if nthreads is None:
         nthreads = os.cpu_count() or 1
     p = _params(T, d, E, k, dtype, score, n_groups, topk_groups, group_score,
-                renormalize, route_scale)
+                renormalize, route_scale, k_per_group)
     ids = np.empty((T, k), np.int32)
     w = np.empty((T, k), np.float64)
     counts = np.empty(E, np.int32)

@@ -141,7 +141,10 @@ void orc_weights_for_ids(const orc_params* p, const double* logits,
  * with groups, view q as [groups][E/groups]; a group's score is the sum of its
  * two largest q when a bias exists, else its largest q; keep the best
  * topk_groups groups, drop every expert of the others, take the top-k of
- * what is left.  [dyn-k]: k_t can differ per request over the same scores.
+ * what is left.  [ferrox] route_top_k_grouped (k_per_group > 0): split the
+ * experts into the same contiguous groups, keep the k_per_group largest q of
+ * each group (by the flat rule's score), then the global top-k of those.
+ * [dyn-k]: k_t can differ per request over the same scores.
  * Returns 0, or 1 when k_t is outside [1, k] (then the row is emptied). */
 static int route_token(const orc_params* p, const double* l, const float* sb,
                        int32_t kt, int32_t* ids, double* w, double* mk,
@@ -174,7 +177,7 @@ static int route_token(const orc_params* p, const double* l, const float* sb,
       if (g_out) g_out[g] = gscore;
     }
     qsort(gorder, G, sizeof(keyed), by_key_desc_id_asc);
-    if (TG < G) {
+    if (TG < G && p->k_per_group <= 0) {
       *mg = gorder[TG - 1].key - gorder[TG].key;
       for (int32_t r = TG; r < G; ++r) {
         const int32_t g = gorder[r].id;
@@ -183,6 +186,26 @@ static int route_token(const orc_params* p, const double* l, const float* sb,
     }
     free(member);
     free(gorder);
+  }
+  if (p->k_per_group > 0) {
+    /* each group keeps its k_per_group largest q; g_out holds the last kept
+     * value (-inf when the group keeps every member), margin_g the smallest
+     * gap at a group's cut */
+    const int32_t gs = E / G, kpg = p->k_per_group;
+    keyed* member = (keyed*)malloc(sizeof(keyed) * gs);
+    for (int32_t g = 0; g < G; ++g) {
+      for (int32_t i = 0; i < gs; ++i) {
+        member[i].key = q[g * gs + i];
+        member[i].id = g * gs + i;
+      }
+      qsort(member, gs, sizeof(keyed), by_key_desc_id_asc);
+      if (g_out) g_out[g] = kpg < gs ? member[kpg - 1].key : -INFINITY;
+      if (kpg < gs) {
+        *mg = fmin(*mg, member[kpg - 1].key - member[kpg].key);
+        for (int32_t i = kpg; i < gs; ++i) q[member[i].id] = -INFINITY;
+      }
+    }
+    free(member);
   }
   if (q_out) memcpy(q_out, q, sizeof(double) * E);
 
@@ -198,7 +221,7 @@ static int route_token(const orc_params* p, const double* l, const float* sb,
 
   /* margins at the k-th boundary */
   *ms = (!bad && kt < ncand) ? order[kt - 1].key - order[kt].key : INFINITY;
-  const int monotone = (sb == NULL) && !(G > 1 && TG < G);
+  const int monotone = (sb == NULL) && !(G > 1 && TG < G) && p->k_per_group <= 0;
   *mo = INFINITY;
   if (bad) {
     *mk = INFINITY;

@@ -58,6 +58,9 @@ typedef struct {
   int32_t group_score;  /* ORC_GROUP_MAX / ORC_GROUP_TOP2_SUM */
   int32_t renormalize;
   double route_scale;
+  int32_t k_per_group;  /* > 0: at most this many experts per group, the
+                           global top-k over the groups' best (ferrox
+                           route_top_k_grouped); 0 = off */
 } orc_params;
 
 /* logits[T][E] = x[T][d] . W[E][d]^T (+ logit_bias[E]) in fp64, index order. */
