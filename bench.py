@@ -116,7 +116,8 @@ def cpu_baseline(w, inp, seconds, threads):
                   k_per_token=None if inp["k_per_token"] is None else inp["k_per_token"][:n],
                   n_groups=w.n_groups, topk_groups=w.topk_groups,
                   group_score=w.group_score if w.n_groups > 1 else None,
-                  renormalize=w.renormalize, route_scale=w.route_scale, nthreads=threads)
+                  renormalize=w.renormalize, route_scale=w.route_scale,
+                  k_per_group=w.k_per_group, nthreads=threads)
         t0 = time.perf_counter()
         oracle.route_full(wl.rows(inp["x"], sl), inp["W"], w.k, **kw)
         return time.perf_counter() - t0
@@ -222,7 +223,7 @@ def main():
     inv = torch.empty(T * k, dtype=torch.int32, device=dev)
     pkw = dict(score=w.score, n_groups=w.n_groups, topk_groups=w.topk_groups,
                group_score=w.group_score if w.n_groups > 1 else "max",
-               renormalize=w.renormalize, route_scale=w.route_scale)
+               renormalize=w.renormalize, route_scale=w.route_scale, k_per_group=w.k_per_group)
     dt = 1 if w.dtype == "bf16" else 0
     ws_bytes = tda.route_dispatch_workspace_size(T, w.d, E, k, dt, **pkw)
     ws = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device=dev)
@@ -230,7 +231,7 @@ def main():
     rkw = dict(score=w.score, logit_bias=lb, select_bias=sb, k_per_token=kpt,
                n_groups=w.n_groups, topk_groups=w.topk_groups,
                group_score=w.group_score if w.n_groups > 1 else None,
-               renormalize=w.renormalize, route_scale=w.route_scale)
+               renormalize=w.renormalize, route_scale=w.route_scale, k_per_group=w.k_per_group)
 
     def step(i):  # one moe_route_dispatch call: gate, selection, dispatch
         tda.route_dispatch(xs[i % n_copies], W, k, ids=ids, weights=weights, counts=counts,

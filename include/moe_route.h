@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 9
+#define MOE_ABI_VERSION 10
 
 /* return codes */
 #define MOE_OK 0
@@ -101,6 +101,11 @@ typedef struct {
                            (norm_topk_prob, ferrox_moe route_top_k_softmax) */
   float route_scale;    /* weights multiplied by this after renormalising
                            (route_scale / routed_scaling_factor); 1 = none */
+  int32_t k_per_group;  /* 0, or > 0 for grouped top-k with a quota (ferrox_moe
+                           route_top_k_grouped): each of the n_groups groups
+                           keeps its k_per_group largest q, and ids are the k
+                           largest of those; needs topk_groups = n_groups and
+                           k <= n_groups * min(k_per_group, E / n_groups) */
 } moe_route_params;
 
 /*

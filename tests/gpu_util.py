@@ -30,8 +30,9 @@ def down(t):
 def route_kwargs(w):
     """Keyword arguments of the routing rule of a workloads.Workload."""
     return dict(score=w.score, n_groups=w.n_groups, topk_groups=w.topk_groups,
-                group_score=w.group_score if w.n_groups > 1 else None,
-                renormalize=w.renormalize, route_scale=w.route_scale)
+                group_score=w.group_score if w.n_groups > 1 and not w.k_per_group else None,
+                renormalize=w.renormalize, route_scale=w.route_scale,
+                k_per_group=w.k_per_group)
 
 
 def gpu_route(w, inp, device="cuda:0", return_logits=True):

@@ -23,7 +23,7 @@ def to_numpy(t):
 
 
 def check_route(gpu_ids, gpu_w, ref, orc, *, score, renormalize=True, route_scale=1.0,
-                k_per_token=None, n_groups=1, topk_groups=None, where=""):
+                k_per_token=None, n_groups=1, topk_groups=None, k_per_group=0, where=""):
     """Compare a route result with oracle output `ref` (oracle.route_logits dict).
 
     Returns statistics; raises AssertionError on any violation."""
@@ -64,7 +64,16 @@ def check_route(gpu_ids, gpu_w, ref, orc, *, score, renormalize=True, route_scal
             row = ids[t, :kt]
             assert len(set(row.tolist())) == kt and row.min() >= 0, (where, t, ids[t])
             assert np.all(ids[t, kt:] == -1)
-            if mg[t] < NEAR and n_groups > 1:
+            if mg[t] < NEAR and k_per_group:
+                # a near-tie at a group's cut: at most k_per_group per group,
+                # each pick within NEAR of its group's last kept q and of the
+                # global boundary (in the unmasked q)
+                gs = ref["q"].shape[1] // n_groups
+                assert np.bincount(row // gs, minlength=n_groups).max() <= k_per_group, (where, t)
+                qr = ref["q_raw"][t]
+                assert np.all(qr[row] >= ref["g"][t][row // gs] - NEAR), (where, t, "group cut")
+                assert np.all(qr[row] >= ref["q_boundary"][t] - NEAR), (where, t, "k boundary")
+            elif mg[t] < NEAR and n_groups > 1:
                 g = ref["g"][t]
                 gb = np.sort(g)[::-1][topk_groups - 1]
                 gs = ref["q"].shape[1] // n_groups
@@ -78,14 +87,18 @@ def check_route(gpu_ids, gpu_w, ref, orc, *, score, renormalize=True, route_scal
 
 
 def oracle_route(orc, logits64, k, *, score, select_bias=None, k_per_token=None, n_groups=1,
-                 topk_groups=None, group_score=None, renormalize=True, route_scale=1.0):
-    """oracle.route_logits plus the boundary value used by check_route."""
+                 topk_groups=None, group_score=None, renormalize=True, route_scale=1.0,
+                 k_per_group=0):
+    """oracle.route_logits plus the boundary value used by check_route (and,
+    with a per-group quota, the unmasked q)."""
     ref = orc.route_logits(logits64, k, score=score, select_bias=select_bias,
                            k_per_token=k_per_token, n_groups=n_groups, topk_groups=topk_groups,
                            group_score=group_score, renormalize=renormalize,
-                           route_scale=route_scale)
+                           route_scale=route_scale, k_per_group=k_per_group)
+    if k_per_group:
+        ref["q_raw"] = orc.route_logits(logits64, 1, score=score, select_bias=select_bias)["q"]
     grouped = n_groups > 1 and (topk_groups or n_groups) < n_groups
-    monotone = select_bias is None and not grouped
+    monotone = select_bias is None and not grouped and not k_per_group
     T = logits64.shape[0]
     kt = np.full(T, k) if k_per_token is None else np.asarray(k_per_token)
     qb = np.empty(T)

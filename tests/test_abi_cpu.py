@@ -49,7 +49,7 @@ def test_header_constants_match_binding():
         assert int(consts["MOE_SCORE_" + name.upper()]) == code
     for name, code in tda.GROUP_SCORES.items():
         assert int(consts["MOE_GROUP_" + name.upper()]) == code
-    assert ctypes.sizeof(tda.RouteParams) == 44
+    assert ctypes.sizeof(tda.RouteParams) == 48
 
 
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
@@ -358,3 +358,27 @@ def test_permute_and_ep_layout_validation():
     assert L.moe_ep_layout(FAKE, 8, 0, FAKE, FAKE, None) == tda.MOE_EINVAL
     assert L.moe_ep_layout(FAKE, 0, 1, FAKE, FAKE, None) == tda.MOE_EINVAL
     assert L.moe_ep_layout(FAKE, 8, 2, FAKE, None, None) == tda.MOE_EINVAL
+
+
+def test_k_per_group_validation():
+    """Grouped top-k with a quota: rejected with a group limit, a negative
+    quota or more experts than the groups keep; accepted otherwise."""
+    L = tda.lib()
+
+    def rc(**kw):
+        base = dict(T=0, d=64, E=64, k=4, dtype=1, score="sigmoid", n_groups=8)
+        base.update(kw)
+        p = tda.make_params(**base)
+        return L.moe_route_workspace_size(ctypes.byref(p)), L.moe_route(
+            ctypes.byref(p), FAKE, FAKE, None, None, None, None, FAKE, FAKE, None, 0, None, None)
+
+    assert rc(k_per_group=1)[1] == tda.MOE_OK
+    assert rc(k_per_group=-1)[1] == tda.MOE_EINVAL
+    assert rc(k_per_group=1, topk_groups=4)[1] == tda.MOE_EINVAL
+    assert "topk_groups" in L.moe_last_error().decode()
+    assert rc(k_per_group=1, k=9)[1] == tda.MOE_EINVAL  # 8 groups keep 8
+    assert rc(k_per_group=1, k=8)[1] == tda.MOE_OK
+    assert rc(k_per_group=20, k=32)[1] == tda.MOE_OK   # quota above the group size
+    plan = tda.route_dispatch_plan(4096, 2048, 128, 8, 1, score="sigmoid", n_groups=16,
+                                   topk_groups=16, k_per_group=1)
+    assert plan["select_lanes"] >= 16  # a lane per group

@@ -96,7 +96,8 @@ def test_gate_logits_exact_on_integers(dtype, T, d, E):
 # ---- the routing workloads at reduced T (full d and E) ----------------------------
 
 REDUCED = {"mixtral": 256, "qwen3_dynk": 700, "dsv3_grouped": 300, "dsv4": 260,
-           "gptoss_skew": 600, "dsv4_bias": 260, "olmoe": 700, "dsv3_groupmax": 300}
+           "gptoss_skew": 600, "dsv4_bias": 260, "olmoe": 700, "dsv3_groupmax": 300,
+           "grouped_quota": 300}
 
 
 def route_case(w, inp):
@@ -112,11 +113,12 @@ def route_case(w, inp):
                        k_per_token=inp["k_per_token"], n_groups=w.n_groups,
                        topk_groups=w.topk_groups,
                        group_score=w.group_score if w.n_groups > 1 else None,
-                       renormalize=w.renormalize, route_scale=w.route_scale)
+                       renormalize=w.renormalize, route_scale=w.route_scale,
+                       k_per_group=w.k_per_group)
     stats = check_route(down(ids), down(wts), ref, oracle, score=w.score,
                         renormalize=w.renormalize, route_scale=w.route_scale,
                         k_per_token=inp["k_per_token"], n_groups=w.n_groups,
-                        topk_groups=w.topk_groups, where=w.name)
+                        topk_groups=w.topk_groups, k_per_group=w.k_per_group, where=w.name)
     return ids, stats
 
 
@@ -218,7 +220,7 @@ def test_T0_and_determinism():
 # ---- full sizes, sampled tokens ------------------------------------------------------
 
 @pytest.mark.parametrize("name", ["mixtral", "qwen3_dynk", "dsv3_grouped", "dsv4", "gptoss_skew",
-                                  "dsv4_bias", "olmoe", "dsv3_groupmax"])
+                                  "dsv4_bias", "olmoe", "dsv3_groupmax", "grouped_quota"])
 def test_workload_full_size_sampled(name):
     w = wl.WORKLOADS[name]
     inp = wl.make_inputs(w)
@@ -235,10 +237,12 @@ def test_workload_full_size_sampled(name):
     ref = oracle_route(oracle, l64, w.k, score=w.score, select_bias=inp["select_bias"],
                        k_per_token=kpt, n_groups=w.n_groups, topk_groups=w.topk_groups,
                        group_score=w.group_score if w.n_groups > 1 else None,
-                       renormalize=w.renormalize, route_scale=w.route_scale)
+                       renormalize=w.renormalize, route_scale=w.route_scale,
+                       k_per_group=w.k_per_group)
     stats = check_route(gids[sample], gw[sample], ref, oracle, score=w.score,
                         renormalize=w.renormalize, route_scale=w.route_scale, k_per_token=kpt,
-                        n_groups=w.n_groups, topk_groups=w.topk_groups, where=name)
+                        n_groups=w.n_groups, topk_groups=w.topk_groups,
+                        k_per_group=w.k_per_group, where=name)
     print(name, "sampled", stats)
     # properties at every token: row structure and weight sums
     kt = np.full(w.T, w.k) if inp["k_per_token"] is None else inp["k_per_token"]

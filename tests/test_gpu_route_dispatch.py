@@ -49,7 +49,8 @@ def assert_same(fused, sep):
                                         ("qwen3_dynk", 4091, "64"), ("qwen3_dynk", 4091, "16"),
                                         ("mixtral", None, None), ("gptoss_skew", 3000, None),
                                         ("dsv3_grouped", 700, None), ("dsv4_bias", 500, None),
-                                        ("olmoe", 1000, None), ("dsv3_groupmax", 700, None)])
+                                        ("olmoe", 1000, None), ("dsv3_groupmax", 700, None),
+                                        ("grouped_quota", 700, None)])
 def test_route_dispatch_matches_separate_calls_and_oracle(name, T, lpt, monkeypatch):
     """The fused call (selection-written dispatch histograms where the shape
     allows) against separate moe_route + moe_dispatch calls and the oracle;
@@ -72,11 +73,12 @@ def test_route_dispatch_matches_separate_calls_and_oracle(name, T, lpt, monkeypa
                        k_per_token=inp["k_per_token"], n_groups=w.n_groups,
                        topk_groups=w.topk_groups,
                        group_score=w.group_score if w.n_groups > 1 else None,
-                       renormalize=w.renormalize, route_scale=w.route_scale)
+                       renormalize=w.renormalize, route_scale=w.route_scale,
+                       k_per_group=w.k_per_group)
     check_route(down(fused[0]), down(fused[1]), ref, oracle, score=w.score,
                 renormalize=w.renormalize, route_scale=w.route_scale,
                 k_per_token=inp["k_per_token"], n_groups=w.n_groups, topk_groups=w.topk_groups,
-                where=name)
+                k_per_group=w.k_per_group, where=name)
     check_dispatch(tuple(fused[2:]), oracle.dispatch(down(fused[0]), w.E))
 
 
@@ -210,3 +212,62 @@ def test_small_batch_route_dispatch(T, E, k, score, bias_groups, dynk, dt):
                 route_scale=rkw["route_scale"], k_per_token=kpt, n_groups=rkw["n_groups"],
                 topk_groups=rkw["topk_groups"], where="small route_dispatch")
     check_dispatch(tuple(fused[2:6]), oracle.dispatch(down(fused[0]), E))
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_quota_random_shapes_every_path(seed):
+    """Grouped top-k with a per-group quota (k_per_group) over random shapes:
+    moe_route_dispatch (small, selection-histogram or separate path by shape)
+    equals moe_route + moe_dispatch bit for bit, and both match the oracle."""
+    rng = np.random.default_rng(500 + seed)
+    E = int(rng.choice([8, 16, 32, 64, 96, 128, 256, 384]))
+    G = int(rng.choice([g for g in (1, 2, 4, 8, 16) if E % g == 0]))
+    gs = E // G
+    kpg = int(rng.integers(1, min(gs, 4) + 2))
+    k = int(rng.integers(1, min(32, G * min(kpg, gs)) + 1))
+    T = int(rng.choice([5, 64, 129, 700, 2100]))
+    d = int(rng.choice([64, 200, 256]))
+    score = str(rng.choice(["softmax", "sigmoid", "sqrt_softplus"]))
+    x = wl.f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+    Wf = wl.f32_to_bf16_bits((rng.standard_normal((E, d)) / np.sqrt(d)).astype(np.float32))
+    sb = (0.1 * rng.standard_normal(E)).astype(np.float32) if rng.random() < 0.5 else None
+    kpt = rng.integers(1, k + 1, size=T).astype(np.int32) if rng.random() < 0.3 else None
+    rkw = dict(score=score, select_bias=sb, k_per_token=kpt, n_groups=G, renormalize=True,
+               route_scale=1.0, k_per_group=kpg)
+    kw = {key: (up(v) if isinstance(v, np.ndarray) else v) for key, v in rkw.items()
+          if v is not None}
+    say("quota route_dispatch", seed, dict(E=E, G=G, kpg=kpg, k=k, T=T, d=d, score=score))
+    fused, sep, e1, e2 = both(up(x), up(Wf), k, E, **kw)
+    assert_same(fused, sep)
+    assert e1 == e2 == 0
+    ref = oracle_route(oracle, oracle.gate(x, Wf), k, **rkw)
+    check_route(down(fused[0]), down(fused[1]), ref, oracle, score=score, renormalize=True,
+                route_scale=1.0, k_per_token=kpt, n_groups=G, k_per_group=kpg,
+                where=f"quota seed {seed}")
+    check_dispatch(tuple(fused[2:6]), oracle.dispatch(down(fused[0]), E))
+
+
+@pytest.mark.parametrize("path,T,d,E,k,G,kpg", [("fused", 32768, 512, 128, 4, 8, 1),
+                                                 ("select_hist", 700, 2048, 128, 16, 16, 2)])
+def test_quota_fused_paths(path, T, d, E, k, G, kpg):
+    """The gate kernel with the selection in its epilogue (whole-row 128 x 128
+    tiles), and the select kernel writing the dispatch's tile histograms, under
+    a per-group quota: equal to separate moe_route + moe_dispatch calls bit for
+    bit, and to the oracle on sampled tokens."""
+    plan = tda.route_dispatch_plan(T, d, E, k, 1, score="sigmoid", n_groups=G, topk_groups=G,
+                                   k_per_group=kpg)
+    assert plan["path"] == path, plan
+    rng = np.random.default_rng(77)
+    x = wl.f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+    Wf = wl.f32_to_bf16_bits((rng.standard_normal((E, d)) / np.sqrt(d)).astype(np.float32))
+    sb = (0.1 * rng.standard_normal(E)).astype(np.float32)
+    say("quota", path, T, d, E, k, G, kpg)
+    fused, sep, e1, e2 = both(up(x), up(Wf), k, E, score="sigmoid", select_bias=up(sb),
+                              n_groups=G, k_per_group=kpg)
+    assert_same(fused, sep)
+    assert e1 == e2 == 0
+    pick = np.sort(rng.choice(T, size=min(T, 300), replace=False))
+    ref = oracle_route(oracle, oracle.gate(wl.rows(x, pick), Wf), k, score="sigmoid",
+                       select_bias=sb, n_groups=G, k_per_group=kpg)
+    check_route(down(fused[0])[pick], down(fused[1])[pick], ref, oracle, score="sigmoid",
+                n_groups=G, k_per_group=kpg, where=f"quota {path}")

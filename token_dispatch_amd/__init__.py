@@ -21,7 +21,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe_route.so")
 
-ABI_VERSION = 9
+ABI_VERSION = 10
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EDEVICE = 0, -1, -2, -3
 MAX_EXPERTS, MAX_K, MAX_GROUPS = 1024, 32, 64
 SCORES = {"softmax": 0, "sigmoid": 1, "sqrt_softplus": 2, "softmax_topk": 3}
@@ -54,7 +54,7 @@ class RouteParams(ctypes.Structure):
                 ("k", ctypes.c_int32), ("dtype", ctypes.c_int32), ("score", ctypes.c_int32),
                 ("n_groups", ctypes.c_int32), ("topk_groups", ctypes.c_int32),
                 ("group_score", ctypes.c_int32), ("renormalize", ctypes.c_int32),
-                ("route_scale", ctypes.c_float)]
+                ("route_scale", ctypes.c_float), ("k_per_group", ctypes.c_int32)]
 
 
 _lib = None
@@ -146,10 +146,12 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 
 def make_params(T, d, E, k, dtype=1, score="softmax", n_groups=1, topk_groups=None,
-                group_score="max", renormalize=True, route_scale=1.0) -> RouteParams:
+                group_score="max", renormalize=True, route_scale=1.0,
+                k_per_group=0) -> RouteParams:
     return RouteParams(int(T), int(d), int(E), int(k), int(dtype), SCORES[score],
                        int(n_groups), int(n_groups if topk_groups is None else topk_groups),
-                       GROUP_SCORES[group_score], int(bool(renormalize)), float(route_scale))
+                       GROUP_SCORES[group_score], int(bool(renormalize)), float(route_scale),
+                       int(k_per_group))
 
 
 def route_workspace_size(T, d, E, k, dtype=1, **kw) -> int:
@@ -160,10 +162,10 @@ def route_workspace_size(T, d, E, k, dtype=1, **kw) -> int:
 
 def _route_args(x, W, k, score, logit_bias, select_bias, k_per_token, n_groups, topk_groups,
                 group_score, renormalize, route_scale, logits, E, ids, weights, dev_err,
-                return_logits):
+                return_logits, k_per_group=0):
     """Checks and output allocation shared by route() and route_dispatch()."""
     if group_score is None:
-        group_score = "top2_sum" if select_bias is not None else "max"
+        group_score = "top2_sum" if select_bias is not None and not k_per_group else "max"
     if x is None:
         if W is not None or logits is None:
             raise ValueError("select-only mode needs x = W = None and logits")
@@ -198,7 +200,7 @@ def _route_args(x, W, k, score, logit_bias, select_bias, k_per_token, n_groups, 
     if dev_err is not None:
         _dev(dev_err, "dev_err", torch.int32, (1,))
     p = make_params(T, d, E_, k, dt, score, n_groups, topk_groups, group_score, renormalize,
-                    route_scale)
+                    route_scale, k_per_group)
     return p, device, logits, ids, weights
 
 
@@ -208,7 +210,7 @@ def route(x: Optional[torch.Tensor], W: Optional[torch.Tensor], k: int, *,
           group_score: Optional[str] = None, renormalize: bool = True,
           route_scale: float = 1.0, logits: Optional[torch.Tensor] = None,
           E: Optional[int] = None, ids=None, weights=None, workspace=None, dev_err=None,
-          return_logits: bool = False):
+          return_logits: bool = False, k_per_group: int = 0):
     """Gate + score + (grouped) top-k + weights.  Returns (ids, weights[, logits]).
 
     x [T][d] and W [E][d] (float32 or bfloat16); or x = W = None with
@@ -216,11 +218,13 @@ def route(x: Optional[torch.Tensor], W: Optional[torch.Tensor], k: int, *,
     logits are written to ``logits`` when one is passed (or return_logits).
     ``workspace`` (uint8 device tensor) carries the gate's hand-off; it is
     allocated when not given.  group_score defaults to "top2_sum" when
-    select_bias is given, else "max".
+    select_bias is given, else "max".  k_per_group > 0: grouped top-k with a
+    quota (each group keeps its k_per_group best, then the top-k of those).
     """
     p, device, logits, ids, weights = _route_args(
         x, W, k, score, logit_bias, select_bias, k_per_token, n_groups, topk_groups,
-        group_score, renormalize, route_scale, logits, E, ids, weights, dev_err, return_logits)
+        group_score, renormalize, route_scale, logits, E, ids, weights, dev_err, return_logits,
+        k_per_group)
     if workspace is None and x is not None:
         nbytes = int(lib().moe_route_workspace_size(ctypes.byref(p)))
         if nbytes:
@@ -262,13 +266,15 @@ def route_dispatch(x: Optional[torch.Tensor], W: Optional[torch.Tensor], k: int,
                    group_score: Optional[str] = None, renormalize: bool = True,
                    route_scale: float = 1.0, logits: Optional[torch.Tensor] = None,
                    E: Optional[int] = None, ids=None, weights=None, counts=None, offsets=None,
-                   perm=None, inv=None, with_inv: bool = True, workspace=None, dev_err=None):
+                   perm=None, inv=None, with_inv: bool = True, workspace=None, dev_err=None,
+                   k_per_group: int = 0):
     """route() then dispatch() of its ids in one library call.  Returns
     (ids, weights, counts, offsets, perm, inv); ``workspace`` (256-byte
     aligned uint8 device tensor) is allocated when not given."""
     p, device, logits, ids, weights = _route_args(
         x, W, k, score, logit_bias, select_bias, k_per_token, n_groups, topk_groups,
-        group_score, renormalize, route_scale, logits, E, ids, weights, dev_err, False)
+        group_score, renormalize, route_scale, logits, E, ids, weights, dev_err, False,
+        k_per_group)
     E_, R = p.E, p.T * p.k
     if counts is None:
         counts = torch.empty(E_, dtype=torch.int32, device=device)

@@ -1036,7 +1036,7 @@ hipError_t launch_gate_select(const GatePlan& g, int32_t dtype, const void* x, c
   if (c.T == 0) return hipSuccess;
   int lpt = 0, vpl = 0;
   select_shape(c, &lpt, &vpl);
-  const bool mono = sa.select_bias == nullptr && !grouped_cfg(c);
+  const bool mono = sa.select_bias == nullptr && !grouped_cfg(c) && c.k_per_group == 0;
   const bool hist = sa.hist != nullptr;
   if (g.bm == 256)
     return launch_fused_tile<256, 128, 4, 2, 3, 128>(lpt, vpl, mono, hist, x, W, logit_bias,

@@ -50,6 +50,7 @@ struct RouteCfg {
   int32_t group_score;  // MOE_GROUP_*
   int32_t renormalize;
   float route_scale;
+  int32_t k_per_group = 0;  // > 0: grouped top-k, at most this many per group
 };
 
 // How the gate contraction is tiled: BM x BN tiles worked by wm x wn

@@ -72,6 +72,7 @@ moe::RouteCfg to_cfg(const moe_route_params* p) {
   c.group_score = p->group_score;
   c.renormalize = p->renormalize;
   c.route_scale = p->route_scale;
+  c.k_per_group = p->k_per_group;
   return c;
 }
 
@@ -109,6 +110,14 @@ int32_t check_route_params(const moe_route_params* p, bool need_d) {
   if (p->group_score != MOE_GROUP_MAX && p->group_score != MOE_GROUP_TOP2_SUM)
     return fail(MOE_EINVAL, "group_score=%d is not a MOE_GROUP_* value", p->group_score);
   const int32_t gs = p->E / p->n_groups;
+  if (p->k_per_group < 0) return fail(MOE_EINVAL, "k_per_group=%d must be >= 0", p->k_per_group);
+  if (p->k_per_group > 0) {
+    if (p->topk_groups != p->n_groups)
+      return fail(MOE_EINVAL, "k_per_group > 0 takes no group limit (topk_groups = n_groups)");
+    const int32_t keep = p->n_groups * std::min(p->k_per_group, gs);
+    if (p->k > keep)
+      return fail(MOE_EINVAL, "k=%d exceeds the %d experts the groups keep", p->k, keep);
+  }
   if ((int64_t)p->k > (int64_t)p->topk_groups * gs)
     return fail(MOE_EINVAL, "k=%d exceeds the %d experts of the kept groups", p->k,
                 p->topk_groups * gs);

@@ -370,8 +370,8 @@ bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0;
 // shorter per-lane scans cut the serial latency of each round.
 void select_shape(const RouteCfg& c, int* lpt, int* vpl) {
   const int E = c.E;
-  const bool grouped = c.n_groups > 1 && c.topk_groups < c.n_groups;
-  const int G = grouped ? c.n_groups : 1;
+  const bool grouped = c.n_groups > 1 && (c.topk_groups < c.n_groups || c.k_per_group > 0);
+  const int G = grouped ? c.n_groups : 1;  // segments hold a lane per group
   const bool few = (int64_t)c.T * 8 < 2048 * kWave;  // 8-lane segments: T / 8 wavefronts
   // a batch small enough for one workgroup: the narrowest segment holding
   // at most 8 experts per lane (more tokens per wavefront, fewer passes)
@@ -445,7 +445,7 @@ hipError_t launch_route_dispatch_small(const RouteCfg& c, const float* logits, i
                                        hipStream_t stream) {
   if (!small_dispatch_ok(c)) return hipErrorInvalidValue;
   const bool grouped = c.n_groups > 1 && c.topk_groups < c.n_groups;
-  const bool mono = select_bias == nullptr && !grouped;
+  const bool mono = select_bias == nullptr && !grouped && c.k_per_group == 0;
   const int vec = c.E % 4 == 0 && aligned16(logits) && split_stride % 4 == 0 &&
                   (!logit_bias || aligned16(logit_bias)) &&
                   (!select_bias || aligned16(select_bias));
@@ -487,7 +487,7 @@ hipError_t launch_select(const RouteCfg& c, const float* logits, int32_t splits,
   if (c.T == 0) return hipSuccess;
   const int E = c.E;
   const bool grouped = c.n_groups > 1 && c.topk_groups < c.n_groups;
-  const bool mono = select_bias == nullptr && !grouped;
+  const bool mono = select_bias == nullptr && !grouped && c.k_per_group == 0;
   const int vec = E % 4 == 0 && aligned16(logits) && split_stride % 4 == 0 &&
                   (!logit_bias || aligned16(logit_bias)) &&
                   (!select_bias || aligned16(select_bias));

@@ -282,6 +282,15 @@ __device__ __forceinline__ void select_token(
       k_rounds = max(k_rounds, __shfl_xor(k_rounds, off, kWave));
   }
 
+  // grouped top-k with a quota of k_per_group picks per group (the rounds
+  // take the largest key left, so a group's picks are its best; once a group
+  // has its quota its other experts leave the race, which gives the top-k of
+  // the groups' best).  Segment lane g (g < n_groups) counts group g's picks.
+  const int kpg = c.k_per_group;
+  const int gsz = kpg > 0 ? E / c.n_groups : 1;
+  const int g_lo = sl * gsz;  // this lane's group: experts [g_lo, g_lo + gsz)
+  int gcount = 0;
+
   for (int r = 0; r < k_rounds; ++r) {
     uint32_t head = key[0];
     int hs = 0;
@@ -298,6 +307,21 @@ __device__ __forceinline__ void select_token(
       for (int j = 0; j < VPL; ++j)
         if (j == hs) key[j] = 0u;
       pick[r] = e0 + hs;
+    }
+    if (kpg > 0) {  // uniform
+      const int e_win = __shfl(e0 + hs, seg * LPT + max(win, 0), kWave);
+      const bool mine = r < kt && sl < c.n_groups && e_win >= g_lo && e_win < g_lo + gsz;
+      gcount += mine;
+      const uint64_t filled = __ballot(mine && gcount == kpg);
+      if (filled) {  // some segment's group reached its quota this round
+        const int gl = S::first(filled, seg);
+        if (gl >= 0) {
+          const int lo = gl * gsz - e0, hi = lo + gsz;  // that group, in this lane's slots
+#pragma unroll
+          for (int j = 0; j < VPL; ++j)
+            if (j >= lo && j < hi) key[j] = 0u;
+        }
+      }
     }
   }
   // the picks and the logit row were written by lanes of this wavefront

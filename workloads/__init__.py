@@ -67,6 +67,7 @@ class Workload:
     zipf_scale: float = 2.0
     hash_vocab: int = 0         # >0: hash routing over this vocabulary
     capacity_factor: float = 0  # >0: capacity-limited dispatch, C = ceil(f * T * k / E)
+    k_per_group: int = 0        # >0: grouped top-k, at most this many per group
 
     def with_T(self, T: int) -> "Workload":
         return dataclasses.replace(self, T=int(T))
@@ -116,6 +117,12 @@ WORKLOADS = {
     # hidden size is not given, 4096 stands in.
     "switch_top1": Workload("switch_top1", T=16384, d=4096, E=128, k=1, dtype="bf16",
                             score="softmax", renormalize=False, capacity_factor=1.25),
+    # Grouped top-k with a per-group quota (ferrox_moe route_top_k_grouped):
+    # the DeepSeek-V3-like shape and 8 groups, the 2 best of each group, then
+    # the global top-8 of those 16, sigmoid scores renormalised.  The page
+    # gives no sizes; these stand in.
+    "grouped_quota": Workload("grouped_quota", T=8192, d=7168, E=256, k=8, dtype="bf16",
+                              score="sigmoid", n_groups=8, topk_groups=8, k_per_group=2),
 }
 
 
