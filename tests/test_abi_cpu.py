@@ -6,6 +6,7 @@ import re
 
 import numpy as np
 import pytest
+import torch
 
 import token_dispatch_amd as tda
 
@@ -382,3 +383,22 @@ def test_k_per_group_validation():
     plan = tda.route_dispatch_plan(4096, 2048, 128, 8, 1, score="sigmoid", n_groups=16,
                                    topk_groups=16, k_per_group=1)
     assert plan["select_lanes"] >= 16  # a lane per group
+
+
+def test_expand_request_k():
+    """A k per request expands to its requests' tokens, in order (checked on
+    host tensors against the workloads' own per-request draw)."""
+    import workloads as wl
+    lens = [256] * 16
+    kt = wl.request_k(0, 4096, (4, 8, 16), 256)
+    kr = kt[::256]
+    got = tda.expand_request_k(kr, lens, "cpu")
+    assert got.dtype == torch.int32 and np.array_equal(got.numpy(), kt)
+    got = tda.expand_request_k([3, 1, 2], [2, 0, 3], "cpu")
+    assert got.tolist() == [3, 3, 2, 2, 2]
+    with pytest.raises(ValueError):
+        tda.expand_request_k([3, 1], [2], "cpu")
+    with pytest.raises(ValueError):
+        tda._request_k(None, [2], None, 5, "cpu")
+    with pytest.raises(ValueError):
+        tda._request_k(None, [2], [4], 5, "cpu")

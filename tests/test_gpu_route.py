@@ -324,3 +324,21 @@ def test_gate_eight_wave_tiles_exact(tile, rb, ns, splits, monkeypatch):
     _, _, logits = tda.route(up(wl.f32_to_bf16_bits(x)), up(wl.f32_to_bf16_bits(Wi)), 4,
                              return_logits=True)
     np.testing.assert_array_equal(down(logits), exp)
+
+
+def test_per_request_k_matches_per_token_k():
+    """route() and route_dispatch() with a k per request equal the calls with
+    the expanded per-token k, bit for bit (Qwen3-like requests of 256)."""
+    w = wl.WORKLOADS["qwen3_dynk"]
+    inp = wl.make_inputs(w, T=1024)
+    kt = inp["k_per_token"]
+    lens = [256] * 4
+    say("per-request k")
+    a = tda.route(up(inp["x"]), up(inp["W"]), w.k, k_per_token=up(kt))
+    b = tda.route(up(inp["x"]), up(inp["W"]), w.k, k_per_request=kt[::256].copy(),
+                  request_lens=lens)
+    c = tda.route_dispatch(up(inp["x"]), up(inp["W"]), w.k, k_per_request=kt[::256].copy(),
+                           request_lens=lens)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    assert torch.equal(a[0], c[0]) and torch.equal(a[1], c[1])

@@ -160,6 +160,34 @@ def route_workspace_size(T, d, E, k, dtype=1, **kw) -> int:
     return int(lib().moe_route_workspace_size(ctypes.byref(p)))
 
 
+def expand_request_k(k_per_request, request_lens, device=None) -> torch.Tensor:
+    """Per-token k [T] int32 from a k per request ("dynamic number of experts",
+    a per-request hyperparameter): request i covers the next request_lens[i]
+    tokens.  k_per_request: sequence or int tensor [n_req]; request_lens: a
+    host sequence of token counts (so the result's size needs no device
+    synchronisation)."""
+    lens = [int(n) for n in request_lens]
+    if any(n < 0 for n in lens):
+        raise ValueError("request_lens must be >= 0")
+    kr = torch.as_tensor(k_per_request, dtype=torch.int32, device=device)
+    if kr.dim() != 1 or kr.numel() != len(lens):
+        raise ValueError("k_per_request must have one entry per request")
+    reps = torch.tensor(lens, dtype=torch.int64, device=kr.device)
+    return torch.repeat_interleave(kr, reps, output_size=sum(lens)).contiguous()
+
+
+def _request_k(k_per_token, k_per_request, request_lens, T, device):
+    if k_per_request is None and request_lens is None:
+        return k_per_token
+    if k_per_request is None or request_lens is None:
+        raise ValueError("k_per_request and request_lens go together")
+    if k_per_token is not None:
+        raise ValueError("give k_per_token or k_per_request, not both")
+    if sum(int(n) for n in request_lens) != T:
+        raise ValueError("request_lens must add up to T")
+    return expand_request_k(k_per_request, request_lens, device)
+
+
 def _route_args(x, W, k, score, logit_bias, select_bias, k_per_token, n_groups, topk_groups,
                 group_score, renormalize, route_scale, logits, E, ids, weights, dev_err,
                 return_logits, k_per_group=0):
@@ -210,7 +238,8 @@ def route(x: Optional[torch.Tensor], W: Optional[torch.Tensor], k: int, *,
           group_score: Optional[str] = None, renormalize: bool = True,
           route_scale: float = 1.0, logits: Optional[torch.Tensor] = None,
           E: Optional[int] = None, ids=None, weights=None, workspace=None, dev_err=None,
-          return_logits: bool = False, k_per_group: int = 0):
+          return_logits: bool = False, k_per_group: int = 0, k_per_request=None,
+          request_lens=None):
     """Gate + score + (grouped) top-k + weights.  Returns (ids, weights[, logits]).
 
     x [T][d] and W [E][d] (float32 or bfloat16); or x = W = None with
@@ -220,7 +249,11 @@ def route(x: Optional[torch.Tensor], W: Optional[torch.Tensor], k: int, *,
     allocated when not given.  group_score defaults to "top2_sum" when
     select_bias is given, else "max".  k_per_group > 0: grouped top-k with a
     quota (each group keeps its k_per_group best, then the top-k of those).
+    k_per_request with request_lens: a k per request, expanded to k_per_token.
     """
+    k_per_token = _request_k(k_per_token, k_per_request, request_lens,
+                             (x if x is not None else logits).shape[0],
+                             (x if x is not None else logits).device)
     p, device, logits, ids, weights = _route_args(
         x, W, k, score, logit_bias, select_bias, k_per_token, n_groups, topk_groups,
         group_score, renormalize, route_scale, logits, E, ids, weights, dev_err, return_logits,
@@ -267,10 +300,14 @@ def route_dispatch(x: Optional[torch.Tensor], W: Optional[torch.Tensor], k: int,
                    route_scale: float = 1.0, logits: Optional[torch.Tensor] = None,
                    E: Optional[int] = None, ids=None, weights=None, counts=None, offsets=None,
                    perm=None, inv=None, with_inv: bool = True, workspace=None, dev_err=None,
-                   k_per_group: int = 0):
+                   k_per_group: int = 0, k_per_request=None, request_lens=None):
     """route() then dispatch() of its ids in one library call.  Returns
     (ids, weights, counts, offsets, perm, inv); ``workspace`` (256-byte
-    aligned uint8 device tensor) is allocated when not given."""
+    aligned uint8 device tensor) is allocated when not given.  k_per_request
+    with request_lens: a k per request, expanded to k_per_token."""
+    k_per_token = _request_k(k_per_token, k_per_request, request_lens,
+                             (x if x is not None else logits).shape[0],
+                             (x if x is not None else logits).device)
     p, device, logits, ids, weights = _route_args(
         x, W, k, score, logit_bias, select_bias, k_per_token, n_groups, topk_groups,
         group_score, renormalize, route_scale, logits, E, ids, weights, dev_err, False,
