@@ -68,6 +68,19 @@ def stage_bytes(w, T, R, R_valid, tile_bytes):
     }
 
 
+def inputs_record(inp):
+    """numpy's version and a sha256 of the synthetic input bytes, in name order."""
+    import hashlib
+    import numpy as np
+    h = hashlib.sha256()
+    for name in sorted(inp):
+        a = inp[name]
+        if isinstance(a, np.ndarray):
+            h.update(name.encode())
+            h.update(np.ascontiguousarray(a).tobytes())
+    return {"numpy": np.__version__, "seed": 0, "sha256": h.hexdigest()}
+
+
 def source_digest(files):
     """sha256 over the given source files, concatenated in order."""
     import hashlib
@@ -286,6 +299,23 @@ def main():
     value = T / (ms_per_step / 1e3)
     log(f"[bench] {ms_per_step * 1e3:.2f} us/step (wall {wall / args.steps * 1e6:.2f} us/step)")
 
+    # the spread of single steps: each of n_each steps between its own pair
+    # of events (after the timed run; the pairs add a little per step)
+    n_each = min(args.steps, 200)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n_each)]
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        step(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    each_us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    step_spread = {"n": n_each, "median": round(float(np.median(each_us)), 3),
+                   "p10": round(float(np.percentile(each_us, 10)), 3),
+                   "p90": round(float(np.percentile(each_us, 90)), 3)}
+    log(f"[bench] single steps: median {step_spread['median']} us, p10 {step_spread['p10']}, "
+        f"p90 {step_spread['p90']}")
+
     # the same steps replayed from HIP graphs (one per copy of x): no Python
     # or launch-API cost between kernels
     graph_ms = None
@@ -436,6 +466,8 @@ def main():
                                + f"dispatch over {E} experts"
                                + (f" with capacity {wl.capacity(w)}" if w.capacity_factor else ""),
                    "T": T, "d": w.d, "E": E, "k_max": k, "x_copies": n_copies},
+        "step_us": step_spread,
+        "inputs": inputs_record(inp),
         "stages": stages,
         "maxvio": round(maxvio, 4),
         "roofline": roofline,
