@@ -81,6 +81,29 @@ def inputs_record(inp):
     return {"numpy": np.__version__, "seed": 0, "sha256": h.hexdigest()}
 
 
+def pipeline_roofline(w, T, R, R_valid, step_us):
+    """Lower bounds on a whole step at the MI355X peaks (8 TB/s, 2.5 PFLOP/s
+    bf16 / 157.3 TFLOP/s fp32) and the step's fraction of each: staged = the
+    gate (max of its flops and its bytes, logits written once) + the
+    selection (logits read once, ids and weights written) + the dispatch
+    (ids read, perm, inv, counts and offsets written) [+ the capacity
+    limit]; fused = no logits hand-off, one pass over x and W."""
+    xb = 2 if w.dtype == "bf16" else 4
+    E, d, k = w.E, w.d, w.k
+    bw = HBM_PEAK_GBS * 1e9
+    peak = (MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else 157.3) * 1e12
+    flops = 2.0 * T * d * E
+    kt = T * 4 if w.dynamic_k else 0
+    xw = T * d * xb + E * d * xb
+    disp = R * 4 + R_valid * 4 + R * 4 + E * 8
+    cap = R * 12 + E * 8 + 4 if w.capacity_factor else 0
+    staged = (max(flops / peak, (xw + T * E * 4) / bw) + (T * E * 4 + T * k * 8 + kt) / bw
+              + (disp + cap) / bw)
+    fused = max(flops / peak, (xw + T * k * 8 + kt + disp + cap) / bw)
+    return {"t_roof_staged_us": round(staged * 1e6, 3), "frac_staged": round(staged * 1e6 / step_us, 4),
+            "t_roof_fused_us": round(fused * 1e6, 3), "frac_fused": round(fused * 1e6 / step_us, 4)}
+
+
 def source_digest(files):
     """sha256 over the given source files, concatenated in order."""
     import hashlib
@@ -378,6 +401,9 @@ def main():
                                         / MFMA_BF16_PEAK_TFLOPS, 4) if gs else None}
     for s, v in stages.items():
         log(f"[bench] {s:13s} {v['avg_us']:9.2f} us  {v['GBs']} GB/s")
+    pipeline = pipeline_roofline(w, T, R, R_valid, ms_per_step * 1e3)
+    log(f"[bench] staged roofline {pipeline['t_roof_staged_us']} us -> pipeline fraction "
+        f"{pipeline['frac_staged']}")
 
     # the combine that follows the experts, timed on its own (not part of a
     # step): synthetic expert outputs in this step's dispatch order plus a
@@ -469,6 +495,7 @@ def main():
         "step_us": step_spread,
         "inputs": inputs_record(inp),
         "stages": stages,
+        "pipeline": pipeline,
         "maxvio": round(maxvio, 4),
         "roofline": roofline,
         "combine": combine,
