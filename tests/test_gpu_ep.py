@@ -153,3 +153,30 @@ def test_ep_send_buffer_full_size():
     assert np.array_equal(to_f64(got), ref)
     rc, ro = oracle.ep_layout(down(offsets), 8)
     assert np.array_equal(down(cnt), rc) and np.array_equal(down(off), ro)
+
+
+def test_row_movement_two_million_routes():
+    """2.1 M routes (T = 262144, k = 8, E = 384): capacity slots, kept and
+    dropped counts and the per-rank layout bit for bit, the send buffer on
+    sampled rows."""
+    T, k, E, d = 262144, 8, 384, 64
+    rng = np.random.default_rng(41)
+    ids = ((rng.zipf(1.2, size=(T, k)) - 1) % E).astype(np.int32)
+    ids[rng.random((T, k)) < 0.02] = -1
+    x = wl.f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+    C = int(np.ceil(1.25 * T * k / E))
+    say("row movement, 2.1 M routes")
+    _, offsets, perm, inv = tda.dispatch(up(ids), E)
+    slot, kept, dropped = tda.dispatch_capacity(up(ids), E, C, offsets, inv)
+    out = tda.permute_rows(up(x), inv, k, T * k)
+    cnt, off = tda.ep_layout(offsets, 16)
+    torch.cuda.synchronize()
+    rc = oracle.capacity(ids, E, C)
+    assert np.array_equal(down(slot), rc["slot"]) and np.array_equal(down(kept), rc["kept"])
+    assert int(dropped.item()) == rc["dropped"] > 0
+    ro, rf = oracle.ep_layout(down(offsets), 16)
+    assert np.array_equal(down(cnt), ro) and np.array_equal(down(off), rf)
+    R = int(offsets[-1].item())
+    pick = np.sort(rng.choice(R, size=512, replace=False))
+    got = down(out.view(torch.int16)).view(np.uint16)[pick]
+    assert np.array_equal(to_f64(got), oracle.permute_rows(x, down(perm)[pick], k))
