@@ -184,3 +184,29 @@ def test_combine_full_size_sampled(name, T):
     inv_np = down(inv).reshape(T, k)
     out = down(y.view(torch.int16)).view(np.uint16)[pick]
     check_combine(out, Yp, inv_np[pick], wts[pick], wl.rows(sh, pick), k)
+
+
+def test_identity_experts_round_trip_full_size():
+    """Route + dispatch (Qwen3-like, full size), the send buffer as the
+    experts' outputs (identity experts), then the combine with dyadic
+    weights: with x small integers every sum is exact, so at every token
+    y = (sum of the token's weights) * x, bit for bit."""
+    w = wl.WORKLOADS["qwen3_dynk"]
+    T, k, d = w.T, w.k, w.d
+    rng = np.random.default_rng(17)
+    x = wl.f32_to_bf16_bits(rng.integers(-4, 5, size=(T, d)).astype(np.float32))
+    Wt = wl.make_inputs(w)["W"]
+    kt = wl.request_k(0, T, w.dynamic_k, w.request_len)
+    say("identity experts round trip", T, k, d)
+    ids, _, _, offsets, _, inv = tda.route_dispatch(up(x), up(Wt), k, k_per_token=up(kt))
+    R = int(offsets[-1].item())
+    send = tda.permute_rows(up(x), inv, k, R)
+    wts = rng.choice(np.array([0.5, 1.0], np.float32), size=(T, k))
+    y = tda.combine(send, inv, up(wts))
+    torch.cuda.synchronize()
+    valid = down(inv).reshape(T, k) >= 0
+    assert np.array_equal(valid.sum(axis=1), kt)
+    wsum = np.where(valid, wts, 0).sum(axis=1).astype(np.float64)
+    want = wsum[:, None] * wl.bf16_bits_to_f32(x).astype(np.float64)
+    got = to_f64(down(y.view(torch.int16)).view(np.uint16))
+    assert np.array_equal(got, want)
