@@ -146,19 +146,25 @@ __global__ __launch_bounds__(WPB * kWave) void select_kernel(
 // wavefront per expert), the scan over experts, and the stable placement
 // (position = expert offset + earlier chunks + peers below in the chunk).
 // One launch instead of three for decode-sized batches.
-constexpr int kSmallWaves = 8;
+// Wavefronts per small workgroup: 16 where a lane's experts and the
+// double-buffered logits of a pass (2 x NSPLIT x VPL registers) leave room
+// under the 128 VGPRs of a 1024-lane workgroup -- one selection pass for 256
+// 4-lane tokens (Mixtral-like: 10.3 -> 9.0 us) --, else 8 (8 experts per
+// lane spill at 16 wavefronts).
+constexpr int small_waves(int vpl, int nsplit) { return vpl <= 4 && vpl * nsplit <= 16 ? 16 : 8; }
 constexpr int kSmallRoutes = 2048;
 constexpr int kSmallE = 128;
 constexpr int kSmallIdBits = 7;  // bits of an expert id below kSmallE
 
 template <int LPT, int VPL, int NSPLIT, bool MONO>
-__global__ __launch_bounds__(kSmallWaves * kWave) void route_dispatch_small_kernel(
+__global__ __launch_bounds__(small_waves(VPL, NSPLIT) * kWave) void route_dispatch_small_kernel(
     RouteCfg c, const float* __restrict__ logits, int64_t split_stride,
     float* __restrict__ logits_out, const float* __restrict__ logit_bias,
     const float* __restrict__ select_bias, const int32_t* __restrict__ k_per_token,
     int32_t* __restrict__ ids, float* __restrict__ weights, int32_t* __restrict__ dev_err,
     int vec, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+  constexpr int kSmallWaves = small_waves(VPL, NSPLIT);
   constexpr int TPW = kWave / LPT;               // tokens per wavefront and pass
   constexpr int TPP = kSmallWaves * TPW;         // tokens per pass
   constexpr int ROW = LPT * VPL;
@@ -454,7 +460,8 @@ hipError_t launch_route_dispatch_small(const RouteCfg& c, const float* logits, i
 #define MOE_SD(L_, V_, S_, M_)                                                                \
   if (lpt == L_ && vpl == V_ && splits == S_ && mono == M_)                                   \
     return launch(kStageSelectDispatch, route_dispatch_small_kernel<L_, V_, S_, M_>, dim3(1),  \
-                  dim3(kSmallWaves * kWave), stream, c, logits, split_stride, logits_out,     \
+                  dim3(small_waves(V_, S_) * kWave), stream, c, logits, split_stride,        \
+                  logits_out,                                                                  \
                   logit_bias, select_bias, k_per_token, ids, weights, dev_err, vec, counts,  \
                   offsets, perm, inv);
 #define MOE_SDV(L_, V_)   \
