@@ -568,8 +568,16 @@ __global__ __launch_bounds__(WM * WN * kWave) void gate_gemm_pipe_kernel(
         if (vec && e0 + 4 <= E) {
           // non-temporal: the next kernel reads the logits from another
           // XCD, and streamed stores leave L2 clean at the end of the
-          // kernel (gpt-oss-like gate: 80.9 -> 74.3 us)
-          __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(logits + t * E + e0));
+          // kernel (gpt-oss-like gate: 80.9 -> 74.3 us).  Rows of 384 or
+          // more experts keep the default policy: the select kernel then
+          // reads the DeepSeek-V4-like partial arrays (50 MB) faster
+          // (14.6 -> 13.3 us; step 118.2 -> 116.0 us), while the Qwen3-,
+          // OLMoE- and DeepSeek-V3-like steps measured equal or slightly
+          // faster with non-temporal stores.
+          if (E >= 384)
+            *reinterpret_cast<f32x4_t*>(logits + t * E + e0) = v;
+          else
+            __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(logits + t * E + e0));
         } else {
 #pragma unroll
           for (int q = 0; q < 4; ++q)
