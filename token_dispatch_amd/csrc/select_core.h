@@ -213,13 +213,29 @@ __device__ __forceinline__ void select_token(
 #pragma unroll
     for (int j = 0; j < VPL; ++j) key[j] = (j < nval) ? ordered_key(lv[j]) : 0u;
   } else {
+    // the score of every expert: one loop per score function (the
+    // wave-uniform branch is taken once, not per expert)
     float q[VPL];
+    switch (c.score) {
+      case kSoftmax:
 #pragma unroll
-    for (int j = 0; j < VPL; ++j) {
-      const float s = (c.score == kSoftmax) ? exp_fast(lv[j] - m_all) * inv_sum_all
-                                            : elementwise_score(c.score, lv[j]);
-      q[j] = (j < nval) ? s + sb[j] : -INFINITY;
+        for (int j = 0; j < VPL; ++j) q[j] = exp_fast(lv[j] - m_all) * inv_sum_all;
+        break;
+      case kSigmoid:
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) q[j] = sigmoid_f32(lv[j]);
+        break;
+      case kSqrtSoftplus:
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) q[j] = __builtin_amdgcn_sqrtf(softplus_f32(lv[j]));
+        break;
+      default:
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) q[j] = lv[j];
+        break;
     }
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) q[j] = (j < nval) ? q[j] + sb[j] : -INFINITY;
     const bool grouped = c.n_groups > 1 && c.topk_groups < c.n_groups;
     if (grouped) {
       const int G = c.n_groups;
