@@ -243,9 +243,10 @@ WORKLOAD_PLANS = {  # path, kernels per moe_route_dispatch call
     "dsv4": ("separate", 5),
     "gptoss_skew": ("fused", 2),
     "dsv4_bias": ("separate", 5),
-    "olmoe": ("separate", 4),
+    "olmoe": ("select_hist", 3),
     "dsv3_groupmax": ("separate", 4),
     "switch_top1": ("separate", 4),
+    "grouped_quota": ("separate", 4),
 }
 
 

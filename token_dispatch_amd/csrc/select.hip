@@ -305,10 +305,22 @@ __global__ __launch_bounds__(small_waves(VPL, NSPLIT) * kWave) void route_dispat
   }
 }
 
-// Waves of a workgroup that also counts its picks for the dispatch: 4, or
-// 16 for one-token wavefronts (16 tokens, so that 16 tokens x k routes make
-// a whole dispatch tile at k = 16).
-constexpr int hist_waves(int lpt) { return lpt == kWave ? 16 : 4; }
+// Waves of a workgroup that also counts its picks for the dispatch: the
+// fewer of 4 or 8 (16 for one-token wavefronts) whose tokens x k_stride
+// routes make a dispatch tile the placement kernel takes (256-2048 routes,
+// tiles x E within its count limit), or 0 -- Qwen3-like 4 (16 tokens x 16),
+// OLMoE-like 8 (32 x 8; step 21.7 -> 18.6 us without the histogram
+// kernel).  16 waves of multi-lane segments measured slower: DeepSeek-V3-
+// like tiles of 64 tokens leave 128 workgroups for 256 CUs on a VALU-heavy
+// selection (select 14 -> 19 us, more than the histogram kernel saves).
+int hist_waves(const RouteCfg& c, int lpt) {
+  const int ws[2] = {lpt == kWave ? 16 : 4, lpt == kWave ? 16 : 8};
+  for (int w : ws) {
+    const int tile = w * (kWave / lpt) * c.k;
+    if (dispatch_hist_ok((int64_t)c.T * c.k, c.E, tile)) return w;
+  }
+  return 0;
+}
 
 template <int LPT, int VPL, int NS, bool MONO>
 hipError_t launch_vpl(const RouteCfg& c, const float* logits, int64_t stride, float* logits_out,
@@ -318,13 +330,25 @@ hipError_t launch_vpl(const RouteCfg& c, const float* logits, int64_t stride, fl
   constexpr int tpb = 4 * (kWave / LPT);
   const int64_t blocks = ((int64_t)c.T + tpb - 1) / tpb;
   if constexpr (LPT * VPL <= kHistMaxE) {
-    if (hist) {  // one dispatch tile per workgroup: hist_waves(LPT) waves
-      constexpr int HW = hist_waves(LPT);
-      constexpr int htpb = HW * (kWave / LPT);
-      const int64_t hblocks = ((int64_t)c.T + htpb - 1) / htpb;
-      return launch(kStageSelect, select_kernel<LPT, VPL, NS, MONO, HW, true>,
-                    dim3((uint32_t)hblocks), dim3(HW * kWave), s, c, logits, stride, logits_out,
-                    logit_bias, select_bias, k_per_token, ids, weights, dev_err, vec, hist);
+    if (hist) {  // one dispatch tile per workgroup: hist_waves(c, LPT) waves
+#define MOE_H(HW_)                                                                            \
+  if (hw == HW_) {                                                                            \
+    constexpr int htpb = HW_ * (kWave / LPT);                                                 \
+    const int64_t hblocks = ((int64_t)c.T + htpb - 1) / htpb;                                 \
+    return launch(kStageSelect, select_kernel<LPT, VPL, NS, MONO, HW_, true>,                 \
+                  dim3((uint32_t)hblocks), dim3(HW_ * kWave), s, c, logits, stride,          \
+                  logits_out, logit_bias, select_bias, k_per_token, ids, weights, dev_err,   \
+                  vec, hist);                                                                 \
+  }
+      const int hw = hist_waves(c, LPT);
+      if constexpr (LPT == kWave) {
+        MOE_H(16)
+      } else {
+        MOE_H(4)
+        MOE_H(8)
+      }
+#undef MOE_H
+      return hipErrorInvalidValue;
     }
   }
   if (hist) return hipErrorInvalidValue;
@@ -432,7 +456,7 @@ int select_hist_tokens(const RouteCfg& c) {
   int lpt, vpl;
   select_shape(c, &lpt, &vpl);
   if (lpt * vpl > kHistMaxE) return 0;
-  return hist_waves(lpt) * (kWave / lpt);
+  return hist_waves(c, lpt) * (kWave / lpt);
 }
 
 bool small_dispatch_ok(const RouteCfg& c) {
