@@ -28,7 +28,7 @@
  *            token); [dyn-k] "Possible Implementation": the output is the
  *            weighted sum of the selected experts' outputs.
  *
- * Readings where the pages are silent are fixed here and listed in the design doc:
+ * Readings where the pages are silent are fixed here:
  * ties go to the lower expert (group) id; slot order is descending selection
  * score; unused dynamic-k slots hold id -1 / weight 0; the token permutation
  * is the stable counting sort of route indices r = t*k_stride + j by expert.
