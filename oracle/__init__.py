@@ -80,6 +80,10 @@ def _load():
         lib.orc_combine.restype = i32
         lib.orc_route_full.argtypes = [ctypes.POINTER(_Params)] + [vp] * 11 + [i32]
         lib.orc_route_full.restype = i32
+        lib.orc_gate_mt.argtypes = [ctypes.POINTER(_Params), vp, vp, vp, vp, i32]
+        lib.orc_gate_mt.restype = None
+        lib.orc_route_logits_mt.argtypes = [ctypes.POINTER(_Params)] + [vp] * 11 + [i32]
+        lib.orc_route_logits_mt.restype = i32
         _lib = lib
     return _lib
 
@@ -121,8 +125,9 @@ def _check_route_args(E, k, n_groups, topk_groups, group_score, k_per_group=0):
         raise ValueError("top2_sum needs groups of at least 2 experts")
 
 
-def gate(x, W, logit_bias=None, dtype=None):
-    """fp64 logits[T][E] of x[T][d] and W[E][d] (float32, or uint16 = bf16 bits)."""
+def gate(x, W, logit_bias=None, dtype=None, nthreads=1):
+    """fp64 logits[T][E] of x[T][d] and W[E][d] (float32, or uint16 = bf16 bits).
+    nthreads > 1 splits the tokens over host threads (same results)."""
     if dtype is None:
         dtype = "bf16" if x.dtype == np.uint16 else "f32"
     npdt = np.uint16 if dtype == "bf16" else np.float32
@@ -133,18 +138,23 @@ def gate(x, W, logit_bias=None, dtype=None):
     assert W.shape[1] == d
     out = np.empty((T, E), dtype=np.float64)
     p = _params(T, d, E, 1, dtype)
-    _load().orc_gate(ctypes.byref(p), _ptr(x), _ptr(W), _ptr(_c(logit_bias, np.float32)),
-                     _ptr(out))
+    lb = _c(logit_bias, np.float32)
+    if nthreads > 1:
+        _load().orc_gate_mt(ctypes.byref(p), _ptr(x), _ptr(W), _ptr(lb), _ptr(out),
+                            int(nthreads))
+    else:
+        _load().orc_gate(ctypes.byref(p), _ptr(x), _ptr(W), _ptr(lb), _ptr(out))
     return out
 
 
 def route_logits(logits, k, score="softmax", select_bias=None, k_per_token=None,
                  n_groups=1, topk_groups=None, group_score=None, renormalize=True,
-                 route_scale=1.0, k_per_group=0):
+                 route_scale=1.0, k_per_group=0, nthreads=1):
     """Select and weight from fp64 logits.  Returns a dict with ids, weights,
     margin_k, margin_g, margin_s, margin_o, q (masked selection quantity),
     g (group scores; with k_per_group, each group's last kept q) and nbad
-    (tokens with k_t outside [1, k])."""
+    (tokens with k_t outside [1, k]).  nthreads > 1 splits the tokens over
+    host threads (same results)."""
     logits = _c(logits, np.float64)
     T, E = logits.shape
     if group_score is None or k_per_group:
@@ -156,11 +166,14 @@ def route_logits(logits, k, score="softmax", select_bias=None, k_per_token=None,
     w = np.empty((T, k), np.float64)
     mk, mg, ms, mo = (np.empty(T, np.float64) for _ in range(4))
     q = np.empty((T, E), np.float64)
-    g = np.empty((T, n_groups), np.float64)
-    nbad = _load().orc_route_logits(
-        ctypes.byref(p), _ptr(logits), _ptr(_c(select_bias, np.float32)),
-        _ptr(_c(k_per_token, np.int32)), _ptr(ids), _ptr(w), _ptr(mk), _ptr(mg),
-        _ptr(ms), _ptr(mo), _ptr(q), _ptr(g))
+    g = np.full((T, n_groups), np.nan)
+    args = (ctypes.byref(p), _ptr(logits), _ptr(_c(select_bias, np.float32)),
+            _ptr(_c(k_per_token, np.int32)), _ptr(ids), _ptr(w), _ptr(mk), _ptr(mg),
+            _ptr(ms), _ptr(mo), _ptr(q), _ptr(g))
+    if nthreads > 1:
+        nbad = _load().orc_route_logits_mt(*args, int(nthreads))
+    else:
+        nbad = _load().orc_route_logits(*args)
     return {"ids": ids, "weights": w, "margin_k": mk, "margin_g": mg,
             "margin_s": ms, "margin_o": mo, "q": q, "g": g, "nbad": int(nbad),
             "logits": logits}

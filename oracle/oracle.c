@@ -415,6 +415,101 @@ int32_t orc_combine(int32_t T, int32_t k, int32_t d, int32_t dtype, const void* 
   return nerr;
 }
 
+/* ---- the same per-token functions, split over host threads by token ------
+ * Tokens are independent, so splitting them over threads changes nothing in
+ * any token's arithmetic; these exist only to make full-size checks fast. */
+typedef struct {
+  const orc_params* p;
+  const void *x, *W;
+  const float* logit_bias;
+  const double* logits_in;
+  const float* select_bias;
+  const int32_t* k_per_token;
+  double* logits_out;
+  int32_t* ids;
+  double *weights, *mk, *mg, *ms, *mo, *q_out, *g_out;
+  int32_t t0, t1;
+  int32_t nbad;
+} token_job;
+
+static void* gate_worker(void* arg) {
+  token_job* j = (token_job*)arg;
+  for (int32_t t = j->t0; t < j->t1; ++t)
+    gate_row(j->p, j->x, j->W, j->logit_bias, t, j->logits_out + (size_t)t * j->p->E);
+  return NULL;
+}
+
+static void* route_worker(void* arg) {
+  token_job* j = (token_job*)arg;
+  const orc_params* p = j->p;
+  for (int32_t t = j->t0; t < j->t1; ++t) {
+    const int32_t kt = j->k_per_token ? j->k_per_token[t] : p->k;
+    j->nbad += route_token(p, j->logits_in + (size_t)t * p->E, j->select_bias, kt,
+                           j->ids + (size_t)t * p->k, j->weights + (size_t)t * p->k,
+                           j->mk + t, j->mg + t, j->ms + t, j->mo + t,
+                           j->q_out ? j->q_out + (size_t)t * p->E : NULL,
+                           j->g_out ? j->g_out + (size_t)t * p->n_groups : NULL);
+  }
+  return NULL;
+}
+
+static int32_t run_token_jobs(const token_job* proto, int32_t T, int32_t nthreads,
+                              void* (*fn)(void*)) {
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > T) nthreads = T > 0 ? T : 1;
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * nthreads);
+  token_job* jobs = (token_job*)malloc(sizeof(token_job) * nthreads);
+  for (int32_t i = 0; i < nthreads; ++i) {
+    jobs[i] = *proto;
+    jobs[i].t0 = (int32_t)((int64_t)T * i / nthreads);
+    jobs[i].t1 = (int32_t)((int64_t)T * (i + 1) / nthreads);
+    jobs[i].nbad = 0;
+    pthread_create(&th[i], NULL, fn, &jobs[i]);
+  }
+  int32_t nbad = 0;
+  for (int32_t i = 0; i < nthreads; ++i) {
+    pthread_join(th[i], NULL);
+    nbad += jobs[i].nbad;
+  }
+  free(jobs);
+  free(th);
+  return nbad;
+}
+
+void orc_gate_mt(const orc_params* p, const void* x, const void* W,
+                 const float* logit_bias, double* logits, int32_t nthreads) {
+  token_job j;
+  memset(&j, 0, sizeof j);
+  j.p = p;
+  j.x = x;
+  j.W = W;
+  j.logit_bias = logit_bias;
+  j.logits_out = logits;
+  run_token_jobs(&j, p->T, nthreads, gate_worker);
+}
+
+int32_t orc_route_logits_mt(const orc_params* p, const double* logits,
+                            const float* select_bias, const int32_t* k_per_token,
+                            int32_t* ids, double* weights, double* margin_k,
+                            double* margin_g, double* margin_s, double* margin_o,
+                            double* q_out, double* g_out, int32_t nthreads) {
+  token_job j;
+  memset(&j, 0, sizeof j);
+  j.p = p;
+  j.logits_in = logits;
+  j.select_bias = select_bias;
+  j.k_per_token = k_per_token;
+  j.ids = ids;
+  j.weights = weights;
+  j.mk = margin_k;
+  j.mg = margin_g;
+  j.ms = margin_s;
+  j.mo = margin_o;
+  j.q_out = q_out;
+  j.g_out = g_out;
+  return run_token_jobs(&j, p->T, nthreads, route_worker);
+}
+
 /* ---- whole path, threaded over tokens ------------------------------------- */
 typedef struct {
   const orc_params* p;

@@ -139,6 +139,17 @@ int32_t orc_combine(int32_t T, int32_t k, int32_t d, int32_t dtype, const void* 
                     const int32_t* inv, const float* weights, const void* shared,
                     double* y);
 
+/* orc_gate and orc_route_logits with the tokens split over nthreads host
+ * threads (tokens are independent: the results are those of the one-thread
+ * calls, bit for bit).  For full-size checks. */
+void orc_gate_mt(const orc_params* p, const void* x, const void* W,
+                 const float* logit_bias, double* logits, int32_t nthreads);
+int32_t orc_route_logits_mt(const orc_params* p, const double* logits,
+                            const float* select_bias, const int32_t* k_per_token,
+                            int32_t* ids, double* weights, double* margin_k,
+                            double* margin_g, double* margin_s, double* margin_o,
+                            double* q_out, double* g_out, int32_t nthreads);
+
 /* Whole path (gate + route + dispatch) split over nthreads host threads by
  * token; dispatch runs on one thread.  Used to time the oracle. */
 int32_t orc_route_full(const orc_params* p, const void* x, const void* W,
