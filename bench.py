@@ -3,24 +3,26 @@
 
 One step = one moe_route_dispatch call -- the gate contraction, scoring,
 selection and weights of moe_route, then the histogram, offsets,
-permutation and inverse of moe_dispatch -- over one batch of seeded
-synthetic tokens (hash workloads: moe_route_hash, whose ids come from the
-token-id table and whose weights from the k gathered gate logits, then
-moe_dispatch).  Inputs are resident in HBM before timing; each step
-routes a different copy of x (rotating through copies totalling more than the
-256 MB last-level cache) so the gate reads x from HBM, not from cache.
+permutation, inverse and load statistic (MaxVio) of moe_dispatch -- over
+one batch of seeded synthetic tokens (hash workloads: moe_route_hash, whose
+ids come from the token-id table and whose weights from the gathered gate
+logits, then moe_dispatch; the capacity workload adds moe_dispatch_capacity).
+Inputs are resident in HBM before timing; each step routes a different copy
+of x (rotating through copies totalling more than the 256 MB last-level
+cache) so the gate reads x from HBM, not from cache.
 
-Prints one JSON line with the throughput, the dominant kernel's roofline
-fraction (kernel time from HIP events recorded on the launch stream by the
-library's per-kernel timing) and the CPU oracle's throughput on a bounded
-sample of the same workload.  The combine that follows the experts (the
-weighted sum of each token's expert outputs, moe_combine) is not part of a
-step; it is timed separately on synthetic expert outputs in the step's
-dispatch order and reported with its own HBM fraction ("combine"), and so
-is the send buffer of token rows in dispatch order (moe_permute_rows,
-"permute").
+The headline (`value`) is the gpt-oss-like configuration, T = 65536 tokens
+(the largest one-GPU configuration).  The `configs` object times every other
+routing configuration in the same run (Mixtral-, Qwen3-, DeepSeek-V3-,
+DeepSeek-V4-like and the V4-like hash layer), each with its per-kernel times,
+binding roofline and the oracle's throughput on the host.
 
-Usage: python bench.py [--steps K] [--warmup W] [--workload NAME]
+Roofline of a kernel: its algorithmic HBM bytes and flops per launch give
+t_bound = max(bytes / 8 TB/s, flops / MFMA peak of its dtype); the binding
+bound is the larger term and frac = t_bound / measured average duration
+(kernel start/stop HIP events the runtime sets on the launch stream).
+
+Usage: python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-configs]
 """
 from __future__ import annotations
 
@@ -36,36 +38,100 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-MFMA_BF16_PEAK_TFLOPS = 2516.6
+MFMA_PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
 LLC_BYTES = 256 << 20
+HEADLINE = "gptoss_skew"
+CONFIGS = ("mixtral", "qwen3_dynk", "dsv3_grouped", "dsv4", "dsv4_hash", "gptoss_skew")
+METRIC = "routed tokens/sec (gate+select+dispatch) and % of MFMA/HBM roofline, 1 MI355X"
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def stage_bytes(w, T, R, R_valid, tile_bytes):
-    """Algorithmic HBM bytes per launch of each kernel (inputs read once,
-    outputs written once); tile_bytes: the dispatch's per-tile histogram
-    data (written once, read once by the placement)."""
+def host_threads():
+    """Host cores this process may use: the affinity mask, or the machine's CPU
+    share when OMP_NUM_THREADS states one."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    return max(1, min(n, int(env))) if env.isdigit() else n
+
+
+def kernel_work(w, T, R, R_valid, tile_bytes):
+    """Algorithmic (HBM bytes, flops) per launch of each kernel: inputs read
+    once, outputs written once.  tile_bytes: the dispatch's per-tile
+    histogram data (written once, read once by the placement).  In a hash
+    layer the gate's work is the method's -- x and W read once and k dot
+    products per token (the table replaces the selection) -- not the dense
+    contraction this design performs."""
     xb = 2 if w.dtype == "bf16" else 4
     E, d, k = w.E, w.d, w.k
+    kt = T * 4 if w.dynamic_k else 0
+    dense = 2.0 * T * d * E
     return {
-        "gate": T * d * xb + E * d * xb + T * E * 4,
+        "gate": (T * d * xb + E * d * xb, 2.0 * T * d * k) if w.hash_vocab
+        else (T * d * xb + E * d * xb + T * E * 4, dense),
         # the gate kernel with the selection fused: no logits leave the chip
-        "gate_select": T * d * xb + E * d * xb + T * k * 8 + (T * 4 if w.dynamic_k else 0)
-        + tile_bytes,
-        "hash": T * 4 + T * k * 4 + T * d * xb + E * d * xb + T * k * 8,
-        "select": T * E * 4 + T * k * 8 + (T * 4 if w.dynamic_k else 0),
+        "gate_select": (T * d * xb + E * d * xb + T * k * 8 + kt + tile_bytes, dense),
+        # table rows, the k gathered logits, ids and weights
+        "hash": (T * 4 + T * k * 4 + T * k * 4 + T * k * 8, 0.0),
+        "select": (T * E * 4 + T * k * 8 + kt, 0.0),
         # small batches: selection and the whole dispatch in one workgroup
-        "select_dispatch": T * E * 4 + T * k * 8 + (T * 4 if w.dynamic_k else 0)
-        + R * 4 + R_valid * 4 + E * 8,
-        "disp_hist": R * 4 + tile_bytes,
-        "disp_scan": 2 * tile_bytes + E * 4,
-        "disp_scatter": tile_bytes + E * 4 + R * 4 + R * 4 + R_valid * 4 + E * 8,
+        "select_dispatch": (T * E * 4 + T * k * 8 + kt + R * 4 + R_valid * 4 + E * 8, 0.0),
+        "disp_hist": (R * 4 + tile_bytes, 0.0),
+        "disp_scan": (2 * tile_bytes + E * 4, 0.0),
+        "disp_scatter": (tile_bytes + E * 4 + R * 4 + R * 4 + R_valid * 4 + E * 8, 0.0),
         # capacity limit: ids and positions read, slots written, kept counts
-        "capacity": R * 12 + E * 8 + 4,
+        "capacity": (R * 12 + E * 8 + 4, 0.0),
     }
+
+
+def roofline(nbytes, flops, us, dtype):
+    """Binding bound of a kernel and its fraction of it."""
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    peak_tf = MFMA_PEAK_TFLOPS[dtype]
+    t_mfma = flops / (peak_tf * 1e12)
+    t = us * 1e-6
+    if t_mfma > t_hbm:
+        return {"bound": "mfma", "achieved": round(flops / t / 1e12, 1), "peak": peak_tf,
+                "unit": "TFLOP/s", "frac": round(t_mfma / t, 4),
+                "hbm_frac": round(t_hbm / t, 4), "mfma_frac": round(t_mfma / t, 4)}
+    return {"bound": "hbm", "achieved": round(nbytes / t / 1e9, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(t_hbm / t, 4), "hbm_frac": round(t_hbm / t, 4),
+            "mfma_frac": round(t_mfma / t, 4)}
+
+
+def pipeline_roofline(w, T, R, R_valid, step_us):
+    """Lower bounds on a whole step at the MI355X peaks and the step's
+    fraction of each: staged = the gate (max of its flops and bytes, logits
+    written once) + the selection (logits read once, ids and weights
+    written) + the dispatch (ids read; perm, inv, counts, offsets written)
+    [+ the capacity limit]; fused = no logits hand-off, one pass over x and
+    W.  A hash layer's bound is the method's: x and W once, table rows,
+    k dot products per token, ids and weights, the dispatch."""
+    xb = 2 if w.dtype == "bf16" else 4
+    E, d, k = w.E, w.d, w.k
+    bw = HBM_PEAK_GBS * 1e9
+    peak = MFMA_PEAK_TFLOPS[w.dtype] * 1e12
+    kt = T * 4 if w.dynamic_k else 0
+    xw = T * d * xb + E * d * xb
+    disp = R * 4 + R_valid * 4 + R * 4 + E * 8
+    cap = R * 12 + E * 8 + 4 if w.capacity_factor else 0
+    if w.hash_vocab:
+        flops = 2.0 * T * d * k
+        staged = max(flops / peak, (xw + T * 4 + T * k * 4 + T * k * 8) / bw) + disp / bw
+        fused = staged
+    else:
+        flops = 2.0 * T * d * E
+        staged = (max(flops / peak, (xw + T * E * 4) / bw) + (T * E * 4 + T * k * 8 + kt) / bw
+                  + (disp + cap) / bw)
+        fused = max(flops / peak, (xw + T * k * 8 + kt + disp + cap) / bw)
+    return {"t_roof_staged_us": round(staged * 1e6, 3),
+            "frac_staged": round(staged * 1e6 / step_us, 4),
+            "t_roof_fused_us": round(fused * 1e6, 3), "frac_fused": round(fused * 1e6 / step_us, 4)}
 
 
 def inputs_record(inp):
@@ -79,29 +145,6 @@ def inputs_record(inp):
             h.update(name.encode())
             h.update(np.ascontiguousarray(a).tobytes())
     return {"numpy": np.__version__, "seed": 0, "sha256": h.hexdigest()}
-
-
-def pipeline_roofline(w, T, R, R_valid, step_us):
-    """Lower bounds on a whole step at the MI355X peaks (8 TB/s, 2.5 PFLOP/s
-    bf16 / 157.3 TFLOP/s fp32) and the step's fraction of each: staged = the
-    gate (max of its flops and its bytes, logits written once) + the
-    selection (logits read once, ids and weights written) + the dispatch
-    (ids read, perm, inv, counts and offsets written) [+ the capacity
-    limit]; fused = no logits hand-off, one pass over x and W."""
-    xb = 2 if w.dtype == "bf16" else 4
-    E, d, k = w.E, w.d, w.k
-    bw = HBM_PEAK_GBS * 1e9
-    peak = (MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else 157.3) * 1e12
-    flops = 2.0 * T * d * E
-    kt = T * 4 if w.dynamic_k else 0
-    xw = T * d * xb + E * d * xb
-    disp = R * 4 + R_valid * 4 + R * 4 + E * 8
-    cap = R * 12 + E * 8 + 4 if w.capacity_factor else 0
-    staged = (max(flops / peak, (xw + T * E * 4) / bw) + (T * E * 4 + T * k * 8 + kt) / bw
-              + (disp + cap) / bw)
-    fused = max(flops / peak, (xw + T * k * 8 + kt + disp + cap) / bw)
-    return {"t_roof_staged_us": round(staged * 1e6, 3), "frac_staged": round(staged * 1e6 / step_us, 4),
-            "t_roof_fused_us": round(fused * 1e6, 3), "frac_fused": round(fused * 1e6 / step_us, 4)}
 
 
 def source_digest(files):
@@ -138,7 +181,8 @@ def cpu_baseline(w, inp, seconds, threads):
     def run_hash(n):  # table ids, the gate, the gathered weights, dispatch
         t0 = time.perf_counter()
         ids, _ = oracle.hash_ids(inp["token_ids"][:n], inp["tid2eid"], w.E)
-        lg = oracle.gate(wl.rows(inp["x"], np.arange(n)), inp["W"], inp["logit_bias"])
+        lg = oracle.gate(wl.rows(inp["x"], np.arange(n)), inp["W"], inp["logit_bias"],
+                         nthreads=threads)
         oracle.weights_for_ids(lg, ids, score=w.score, renormalize=w.renormalize,
                                route_scale=w.route_scale)
         oracle.dispatch(ids, w.E)
@@ -168,10 +212,9 @@ def cpu_baseline(w, inp, seconds, threads):
         reps += 1
     what = ("hash ids + gate + gathered weights + dispatch" if w.hash_vocab
             else "gate + route + dispatch")
-    return {"value": reps * n / total, "unit": "tokens/s",
-            "cores": 1 if w.hash_vocab else threads, "kind": "oracle",
+    return {"value": reps * n / total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{'first %d of ' % n if n < w.T else 'all '}{w.T} tokens of the same "
-                      f"workload x {reps} ({what}, fp64), {total:.1f} s"}
+                      f"workload x {reps} ({what}, fp64, {threads} host threads), {total:.1f} s"}
 
 
 def combine_cpu_baseline(Yp, inv, weights, shared, seconds=3.0):
@@ -191,16 +234,346 @@ def combine_cpu_baseline(Yp, inv, weights, shared, seconds=3.0):
             "sample": f"first {n} of {T} tokens (combine, fp64), {t:.2f} s"}
 
 
+class Case:
+    """One workload on the GPU: inputs, rotating copies of x, outputs and the
+    step (one pass of the hot path)."""
+
+    def __init__(self, w, inp, dev):
+        import numpy as np
+        import torch
+
+        import token_dispatch_amd as tda
+        import workloads as wl
+
+        self.w, self.inp, self.dev = w, inp, dev
+        up = self.up
+        x0 = up(inp["x"])
+        xbytes = x0.numel() * x0.element_size()
+        self.n_copies = max(1, min(64, math.ceil(3 * LLC_BYTES / xbytes)))
+        self.xs = [x0] + [torch.roll(x0, shifts=97 * i, dims=0).contiguous()
+                          for i in range(1, self.n_copies)]
+        W = up(inp["W"])
+        lb, sb, kpt = up(inp["logit_bias"]), up(inp["select_bias"]), up(inp["k_per_token"])
+        T, E, k = w.T, w.E, w.k
+        i32 = torch.int32
+        self.ids = torch.empty((T, k), dtype=i32, device=dev)
+        self.weights = torch.empty((T, k), dtype=torch.float32, device=dev)
+        self.counts = torch.empty(E, dtype=i32, device=dev)
+        self.offsets = torch.empty(E + 1, dtype=i32, device=dev)
+        self.perm = torch.empty(T * k, dtype=i32, device=dev)
+        self.inv = torch.empty(T * k, dtype=i32, device=dev)
+        self.maxvio = torch.zeros(1, dtype=torch.float64, device=dev)
+        pkw = dict(score=w.score, n_groups=w.n_groups, topk_groups=w.topk_groups,
+                   group_score=w.group_score if w.n_groups > 1 else "max",
+                   renormalize=w.renormalize, route_scale=w.route_scale,
+                   k_per_group=w.k_per_group)
+        dt = 1 if w.dtype == "bf16" else 0
+        self.plan = ({"path": "hash", "kernels": None} if w.hash_vocab
+                     else tda.route_dispatch_plan(T, w.d, E, k, dt, **pkw))
+        ws_bytes = tda.route_dispatch_workspace_size(T, w.d, E, k, dt, **pkw)
+        ws = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device=dev)
+        route_bytes = (tda.route_workspace_size(T, w.d, E, k, dt, **pkw) + 255) // 256 * 256
+        rkw = dict(score=w.score, logit_bias=lb, select_bias=sb, k_per_token=kpt,
+                   n_groups=w.n_groups, topk_groups=w.topk_groups,
+                   group_score=w.group_score if w.n_groups > 1 else None,
+                   renormalize=w.renormalize, route_scale=w.route_scale,
+                   k_per_group=w.k_per_group)
+        outs = dict(ids=self.ids, weights=self.weights, counts=self.counts,
+                    offsets=self.offsets, perm=self.perm, inv=self.inv, maxvio=self.maxvio)
+        xs, n = self.xs, self.n_copies
+
+        def step(i):  # one moe_route_dispatch call: gate, selection, dispatch
+            tda.route_dispatch(xs[i % n], W, k, workspace=ws, **outs, **rkw)
+
+        if w.capacity_factor:  # the dispatch ends with the capacity limit
+            C = wl.capacity(w)
+            slot = torch.empty(T * k, dtype=i32, device=dev)
+            kept = torch.empty(E, dtype=i32, device=dev)
+            dropped = torch.empty(1, dtype=i32, device=dev)
+
+            def step(i):  # noqa: F811 -- moe_route_dispatch, then the capacity limit
+                tda.route_dispatch(xs[i % n], W, k, workspace=ws, **outs, **rkw)
+                tda.dispatch_capacity(self.ids, E, C, self.offsets, self.inv, slot=slot,
+                                      kept=kept, dropped=dropped)
+
+        self.disp_ws = ws_bytes - route_bytes  # the dispatch's tile data
+        if w.hash_vocab:
+            tok, tab = up(inp["token_ids"]), up(inp["tid2eid"])
+            self.disp_ws = tda.dispatch_workspace_size(T, k, E)
+            dws = torch.empty(max(1, self.disp_ws), dtype=torch.uint8, device=dev)
+            hws = torch.empty(max(1, tda.route_hash_workspace_size(T, w.d, E, k, dt, **pkw)),
+                              dtype=torch.uint8, device=dev)
+            douts = dict(counts=self.counts, offsets=self.offsets, perm=self.perm,
+                         inv=self.inv, maxvio=self.maxvio)
+
+            def step(i):  # noqa: F811 -- moe_route_hash then moe_dispatch
+                tda.route_hash(tok, tab, E, x=xs[i % n], W=W, score=w.score, logit_bias=lb,
+                               renormalize=w.renormalize, route_scale=w.route_scale,
+                               ids=self.ids, weights=self.weights, workspace=hws)
+                tda.dispatch(self.ids, E, workspace=dws, **douts)
+
+        self.step = step
+        self.xbytes = xbytes
+
+    def up(self, a):
+        import numpy as np
+        import torch
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(self.dev).view(
+                torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(self.dev)
+
+    def timed(self, steps):
+        """Average ms of `steps` steps between two events on the current stream."""
+        import torch
+        stream = torch.cuda.current_stream(self.dev)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(steps):
+            self.step(i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / steps
+
+    def kernels(self, n_prof, traffic_path):
+        """Per-kernel average times (library's start/stop events), bytes, flops
+        and binding roofline; returns (stages, dominant stage)."""
+        import torch
+
+        import token_dispatch_amd as tda
+        w = self.w
+        tda.profile_enable(True)
+        for i in range(n_prof):
+            self.step(i)
+        torch.cuda.synchronize()
+        prof = tda.profile_read()
+        tda.profile_enable(False)
+        T, R = w.T, w.T * w.k
+        self.R_valid = int(self.counts.sum().item())
+        two = "disp_scan" not in prof or not prof["disp_scan"][1]
+        tile_bytes = self.disp_ws if two else (self.disp_ws - 4 * w.E) // 2
+        work = kernel_work(w, T, R, self.R_valid, tile_bytes)
+        stages = {}
+        for name, (ms, n) in prof.items():
+            if n and name in work:
+                us = ms / n * 1e3
+                nbytes, flops = work[name]
+                rf = roofline(nbytes, flops, us, w.dtype)
+                stages[name] = {"avg_us": round(us, 3), "launches": n, "bytes": nbytes,
+                                "flops": flops, **rf,
+                                "traffic": measured_traffic(traffic_path, w.name, name)}
+        dom = max(stages, key=lambda s: stages[s]["avg_us"])
+        return stages, dom
+
+
+def measure(w, inp, dev, args, *, headline):
+    """Time one workload: K eager steps after W warm-up steps, per-kernel
+    roofline, pipeline fractions; the headline also gets the single-step
+    spread, HIP-graph replays and the combine / send-buffer measurements."""
+    import numpy as np
+    import torch
+
+    import token_dispatch_amd as tda
+    import workloads as wl
+
+    case = Case(w, inp, dev)
+    T, E, k = w.T, w.E, w.k
+    warm = args.warmup if headline else max(args.warmup, 200)
+    steps = args.steps if headline else max(args.steps, 100)
+    log(f"[bench] {w.name}: T={T} d={w.d} E={E} k={k}; {case.n_copies} rotating copies of x "
+        f"({case.xbytes / 1e6:.1f} MB each); plan {case.plan['path']} "
+        f"({case.plan['kernels']} kernels); warmup {warm}, steps {steps}")
+    for i in range(warm):
+        case.step(i)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ms_per_step = case.timed(steps)
+    wall = time.perf_counter() - wall0
+    log(f"[bench] {w.name}: {ms_per_step * 1e3:.2f} us/step (wall {wall / steps * 1e6:.2f} us)")
+    out = {"T": T, "d": w.d, "E": E, "k_max": k, "steps": steps, "warmup": warm,
+           "ms_per_step": round(ms_per_step, 6), "tokens_per_s": round(T / (ms_per_step / 1e3), 1),
+           "plan": case.plan["path"], "kernels_per_step": case.plan["kernels"]}
+
+    if headline:
+        # the spread of single steps, each between its own pair of events
+        n_each = min(steps, 200)
+        stream = torch.cuda.current_stream(dev)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n_each)]
+        for i, (a, b) in enumerate(evs):
+            a.record(stream)
+            case.step(i)
+            b.record(stream)
+        torch.cuda.synchronize()
+        each = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+        out["step_us"] = {"n": n_each, "median": round(float(np.median(each)), 3),
+                          "p10": round(float(np.percentile(each, 10)), 3),
+                          "p90": round(float(np.percentile(each, 90)), 3)}
+
+    if not args.no_graph:
+        out["graph"] = graph_replay(case, steps, dev)
+
+    stages, dom = case.kernels(min(steps, 100), args.traffic)
+    for s, v in stages.items():
+        log(f"[bench] {w.name}: {s:15s} {v['avg_us']:9.2f} us  {v['bound']} {v['achieved']} "
+            f"{v['unit']} ({v['frac']:.3f})")
+    d = stages[dom]
+    out["stages"] = stages
+    out["roofline"] = {"bound": d["bound"], "kernel": dom, "achieved": d["achieved"],
+                       "peak": d["peak"], "unit": d["unit"], "frac": d["frac"],
+                       "traffic": d["traffic"], "hbm_frac": d["hbm_frac"],
+                       "mfma_frac": d["mfma_frac"]}
+    out["pipeline"] = pipeline_roofline(w, T, T * k, case.R_valid, ms_per_step * 1e3)
+    out["maxvio"] = round(float(case.maxvio.item()), 6)
+    log(f"[bench] {w.name}: staged roofline {out['pipeline']['t_roof_staged_us']} us -> "
+        f"pipeline fraction {out['pipeline']['frac_staged']}; MaxVio {out['maxvio']}")
+    if headline and not args.no_combine and case.R_valid > 0:
+        out.update(row_movement(case, dev, args))
+    del case
+    torch.cuda.empty_cache()
+    return out
+
+
+def graph_replay(case, steps, dev):
+    """The same steps replayed from HIP graphs: one graph per step (one per
+    copy of x), and one graph holding a step for every copy of x in order."""
+    import torch
+    n = case.n_copies
+    cs = torch.cuda.Stream(dev)
+    cs.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(cs):
+        case.step(0)
+    torch.cuda.current_stream(dev).wait_stream(cs)
+    torch.cuda.synchronize()
+    singles = []
+    for i in range(n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            case.step(i)
+        singles.append(g)
+    many = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(many):
+        for i in range(n):
+            case.step(i)
+    stream = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def run(fn, reps):
+        for i in range(min(reps, 20)):
+            fn(i)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(reps):
+            fn(i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / reps
+
+    one = run(lambda i: singles[i % n].replay(), steps)
+    reps = max(1, steps // n)
+    multi = run(lambda i: many.replay(), reps) / n
+    out = {"one_step_graphs_us": round(one * 1e3, 3), "steps_per_graph": n,
+           "multi_step_graph_us": round(multi * 1e3, 3), "multi_step_replays": reps}
+    log(f"[bench] {case.w.name}: graph replay {out['one_step_graphs_us']} us/step "
+        f"(one step per graph), {out['multi_step_graph_us']} us/step ({n} steps per graph)")
+    del singles, many
+    return out
+
+
+def row_movement(case, dev, args):
+    """The combine that follows the experts and the send buffer, each timed on
+    its own on the step's dispatch (not part of a step): synthetic expert
+    outputs in dispatch order plus a shared expert's output; rotating copies
+    larger than the last-level cache."""
+    import torch
+
+    import token_dispatch_amd as tda
+    import workloads as wl
+    w, T, k = case.w, case.w.T, case.w.k
+    R_valid = case.R_valid
+    eb = 2 if w.dtype == "bf16" else 4
+    Y_np, sh_np = wl.expert_outputs(w, R_valid), wl.shared_output(w)
+    Y0 = case.up(Y_np)
+    n_yc = max(1, min(16, math.ceil(3 * LLC_BYTES / (R_valid * w.d * eb))))
+    Ys = [Y0] + [torch.roll(Y0, shifts=89 * i, dims=0).contiguous() for i in range(1, n_yc)]
+    sh = case.up(sh_np)
+    yout = torch.empty((T, w.d), dtype=Y0.dtype, device=dev)
+    for i in range(20):
+        tda.combine(Ys[i % n_yc], case.inv, case.weights, shared=sh, out=yout)
+    torch.cuda.synchronize()
+    tda.profile_enable(True)
+    n_c = 50
+    for i in range(n_c):
+        tda.combine(Ys[i % n_yc], case.inv, case.weights, shared=sh, out=yout)
+    torch.cuda.synchronize()
+    cms, cn = tda.profile_read()["combine"]
+    tda.profile_enable(False)
+    c_us = cms / cn * 1e3
+    cbytes = R_valid * w.d * eb + T * k * 8 + 2 * T * w.d * eb  # rows, inv+weights, shared, y
+    c_gbs = cbytes / (c_us * 1e-6) / 1e9
+    combine = {"kernel": "combine", "avg_us": round(c_us, 3), "launches": cn, "bytes": cbytes,
+               "achieved": round(c_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+               "frac": round(c_gbs / HBM_PEAK_GBS, 4), "rows": R_valid, "d": w.d,
+               "shared": True, "row_copies": n_yc}
+    log(f"[bench] combine       {c_us:9.2f} us  {c_gbs:.1f} GB/s ({R_valid} rows of {w.d})")
+    del Ys, Y0
+    # the send buffer (token rows in dispatch order, the all-to-all's input
+    # under expert parallelism), timed the same way
+    x0 = case.up(case.inp["x"])
+    n_xc = max(1, min(16, math.ceil(3 * LLC_BYTES / (T * w.d * eb))))
+    xs = [x0] + [torch.roll(x0, shifts=89 * i, dims=0).contiguous() for i in range(1, n_xc)]
+    sbuf = torch.empty((T * k, w.d), dtype=x0.dtype, device=dev)
+    for i in range(20):
+        tda.permute_rows(xs[i % n_xc], case.inv, k, T * k, out=sbuf)
+    torch.cuda.synchronize()
+    tda.profile_enable(True)
+    for i in range(n_c):
+        tda.permute_rows(xs[i % n_xc], case.inv, k, T * k, out=sbuf)
+    torch.cuda.synchronize()
+    pms, pn = tda.profile_read()["permute"]
+    tda.profile_enable(False)
+    p_us = pms / pn * 1e3
+    pbytes = T * w.d * eb + R_valid * w.d * eb + T * k * 4  # rows in once, out once, inv
+    p_gbs = pbytes / (p_us * 1e-6) / 1e9
+    permute = {"kernel": "permute", "avg_us": round(p_us, 3), "launches": pn, "bytes": pbytes,
+               "achieved": round(p_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+               "frac": round(p_gbs / HBM_PEAK_GBS, 4), "rows": R_valid, "d": w.d,
+               "row_copies": n_xc}
+    log(f"[bench] permute       {p_us:9.2f} us  {p_gbs:.1f} GB/s ({R_valid} rows of {w.d})")
+    del sbuf, xs, x0
+    if not args.no_cpu_baseline:
+        combine["cpu_baseline"] = combine_cpu_baseline(
+            Y_np, case.inv.cpu().numpy().reshape(T, k), case.weights.cpu().numpy(), sh_np)
+    return {"combine": combine, "permute": permute}
+
+
+def describe(w):
+    import workloads as wl
+    k = w.k
+    return (f"{w.name}: T={w.T} tokens, d={w.d}, E={w.E}, "
+            f"k={'/'.join(map(str, w.dynamic_k)) + ' per request' if w.dynamic_k else k}, "
+            f"score={w.score}, groups={w.n_groups}/{w.topk_groups}, "
+            + (f"hash ids from tid2eid[{w.hash_vocab}][{k}], " if w.hash_vocab else "")
+            + f"dispatch over {w.E} experts"
+            + (f" with capacity {wl.capacity(w)}" if w.capacity_factor else ""))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=1000)
-    ap.add_argument("--workload", default="qwen3_dynk")
+    ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--config-cpu-seconds", type=float, default=3.0)
+    ap.add_argument("--no-configs", action="store_true",
+                    help="time only --workload (no `configs` object)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-combine", action="store_true",
-                    help="skip the separate measurement of the combine kernel")
+                    help="skip the separate measurement of the combine and send buffer")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches only (no HIP graph replay)")
     ap.add_argument("--calibrate-copy-mb", type=float, default=0.0,
@@ -213,7 +586,6 @@ def main():
               "(no collectives); run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     if args.calibrate_copy_mb > 0:
@@ -231,276 +603,67 @@ def main():
     import token_dispatch_amd as tda
     import workloads as wl
 
+    tda.lib()  # fails loudly when the HIP library is not built
+    dev = torch.device("cuda:0")
+    threads = host_threads()
     w = wl.WORKLOADS[args.workload]
+
+    # the other routing configurations first (their own warm-up and steps;
+    # they also bring the GPU to its working clocks before the headline)
+    configs, config_inputs = {}, {}
+    if not args.no_configs:
+        shared = {}
+        for name in CONFIGS:
+            if name == w.name:
+                continue
+            cw = wl.WORKLOADS[name]
+            key = (cw.T, cw.d, cw.E, cw.dtype)
+            log(f"[bench] generating {name} inputs")
+            cinp = wl.make_inputs(cw)
+            if key in shared:  # the V4-like hash layer shares x and W with the V4-like one
+                cinp["x"], cinp["W"] = shared[key]
+            shared[key] = (cinp["x"], cinp["W"])
+            res = measure(cw, cinp, dev, args, headline=False)
+            res["workload"] = describe(cw)
+            configs[name] = res
+            config_inputs[name] = cinp
+        shared.clear()
+
     log(f"[bench] generating {w.name} inputs (T={w.T}, d={w.d}, E={w.E})")
     inp = wl.make_inputs(w)
-    dev = torch.device("cuda:0")
-
-    def up(a):
-        if a is None:
-            return None
-        if a.dtype == np.uint16:
-            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(
-                torch.bfloat16)
-        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-
-    x0 = up(inp["x"])
-    xbytes = x0.numel() * x0.element_size()
-    n_copies = max(1, min(64, math.ceil(3 * LLC_BYTES / xbytes)))
-    xs = [x0] + [torch.roll(x0, shifts=97 * i, dims=0).contiguous() for i in range(1, n_copies)]
-    W = up(inp["W"])
-    lb, sb, kpt = up(inp["logit_bias"]), up(inp["select_bias"]), up(inp["k_per_token"])
-    T, E, k = w.T, w.E, w.k
-    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
-    weights = torch.empty((T, k), dtype=torch.float32, device=dev)
-    counts = torch.empty(E, dtype=torch.int32, device=dev)
-    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
-    perm = torch.empty(T * k, dtype=torch.int32, device=dev)
-    inv = torch.empty(T * k, dtype=torch.int32, device=dev)
-    pkw = dict(score=w.score, n_groups=w.n_groups, topk_groups=w.topk_groups,
-               group_score=w.group_score if w.n_groups > 1 else "max",
-               renormalize=w.renormalize, route_scale=w.route_scale, k_per_group=w.k_per_group)
-    dt = 1 if w.dtype == "bf16" else 0
-    ws_bytes = tda.route_dispatch_workspace_size(T, w.d, E, k, dt, **pkw)
-    ws = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device=dev)
-    route_bytes = (tda.route_workspace_size(T, w.d, E, k, dt, **pkw) + 255) // 256 * 256
-    rkw = dict(score=w.score, logit_bias=lb, select_bias=sb, k_per_token=kpt,
-               n_groups=w.n_groups, topk_groups=w.topk_groups,
-               group_score=w.group_score if w.n_groups > 1 else None,
-               renormalize=w.renormalize, route_scale=w.route_scale, k_per_group=w.k_per_group)
-
-    def step(i):  # one moe_route_dispatch call: gate, selection, dispatch
-        tda.route_dispatch(xs[i % n_copies], W, k, ids=ids, weights=weights, counts=counts,
-                           offsets=offsets, perm=perm, inv=inv, workspace=ws, **rkw)
-
-    if w.capacity_factor:  # the dispatch ends with the capacity limit
-        C = wl.capacity(w)
-        slot = torch.empty(T * k, dtype=torch.int32, device=dev)
-        kept = torch.empty(E, dtype=torch.int32, device=dev)
-        dropped = torch.empty(1, dtype=torch.int32, device=dev)
-
-        def step(i):  # noqa: F811 -- moe_route_dispatch, then the capacity limit
-            tda.route_dispatch(xs[i % n_copies], W, k, ids=ids, weights=weights, counts=counts,
-                               offsets=offsets, perm=perm, inv=inv, workspace=ws, **rkw)
-            tda.dispatch_capacity(ids, E, C, offsets, inv, slot=slot, kept=kept,
-                                  dropped=dropped)
-
-    disp_ws = ws_bytes - route_bytes  # the dispatch's tile data
-    if w.hash_vocab:
-        tok, tab = up(inp["token_ids"]), up(inp["tid2eid"])
-        disp_ws = tda.dispatch_workspace_size(T, k, E)
-        dws = torch.empty(max(1, disp_ws), dtype=torch.uint8, device=dev)
-        hws = torch.empty(max(1, tda.route_hash_workspace_size(T, w.d, E, k, dt, **pkw)),
-                          dtype=torch.uint8, device=dev)
-
-        def step(i):  # noqa: F811 -- moe_route_hash then moe_dispatch
-            tda.route_hash(tok, tab, E, x=xs[i % n_copies], W=W, score=w.score,
-                           logit_bias=lb, renormalize=w.renormalize,
-                           route_scale=w.route_scale, ids=ids, weights=weights,
-                           workspace=hws)
-            tda.dispatch(ids, E, counts=counts, offsets=offsets, perm=perm, inv=inv,
-                         workspace=dws)
-
-    log(f"[bench] {n_copies} rotating copies of x ({xbytes / 1e6:.1f} MB each); "
-        f"warmup {args.warmup}, steps {args.steps}")
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    stream = torch.cuda.current_stream(dev)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_total = ev0.elapsed_time(ev1)
-    ms_per_step = ms_total / args.steps
-    value = T / (ms_per_step / 1e3)
-    log(f"[bench] {ms_per_step * 1e3:.2f} us/step (wall {wall / args.steps * 1e6:.2f} us/step)")
-
-    # the spread of single steps: each of n_each steps between its own pair
-    # of events (after the timed run; the pairs add a little per step)
-    n_each = min(args.steps, 200)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(n_each)]
-    for i, (a, b) in enumerate(evs):
-        a.record(stream)
-        step(i)
-        b.record(stream)
-    torch.cuda.synchronize()
-    each_us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
-    step_spread = {"n": n_each, "median": round(float(np.median(each_us)), 3),
-                   "p10": round(float(np.percentile(each_us, 10)), 3),
-                   "p90": round(float(np.percentile(each_us, 90)), 3)}
-    log(f"[bench] single steps: median {step_spread['median']} us, p10 {step_spread['p10']}, "
-        f"p90 {step_spread['p90']}")
-
-    # the same steps replayed from HIP graphs (one per copy of x): no Python
-    # or launch-API cost between kernels
-    graph_ms = None
-    if not args.no_graph:
-        graphs = []
-        cs = torch.cuda.Stream(dev)
-        cs.wait_stream(torch.cuda.current_stream(dev))
-        with torch.cuda.stream(cs):
-            step(0)
-        torch.cuda.current_stream(dev).wait_stream(cs)
-        torch.cuda.synchronize()
-        for i in range(n_copies):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                step(i)
-            graphs.append(g)
-        for i in range(args.warmup):
-            graphs[i % n_copies].replay()
-        torch.cuda.synchronize()
-        ev0.record(stream)
-        for i in range(args.steps):
-            graphs[i % n_copies].replay()
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        graph_ms = ev0.elapsed_time(ev1) / args.steps
-        log(f"[bench] graph replay: {graph_ms * 1e3:.2f} us/step")
-
-    # per-kernel times from HIP events the library records on the launch stream
-    n_prof = min(args.steps, 100)
-    tda.profile_enable(True)
-    for i in range(n_prof):
-        step(i)
-    torch.cuda.synchronize()
-    prof = tda.profile_read()
-    tda.profile_enable(False)
-
-    R = T * k
-    R_valid = int(counts.sum().item())
-    tile_bytes = disp_ws if "disp_scan" not in prof or not prof["disp_scan"][1] else (disp_ws - 4 * E) // 2
-    sbytes = stage_bytes(w, T, R, R_valid, tile_bytes)
-    stages = {}
-    for name, (ms, n) in prof.items():
-        if n:
-            avg_us = ms / n * 1e3
-            stages[name] = {"avg_us": round(avg_us, 3), "launches": n,
-                            "bytes": sbytes.get(name),
-                            "GBs": round(sbytes[name] / (avg_us * 1e-6) / 1e9, 1)
-                            if name in sbytes else None}
-    dom = max(stages, key=lambda s: stages[s]["avg_us"])
-    dom_us = stages[dom]["avg_us"]
-    achieved = sbytes[dom] / (dom_us * 1e-6) / 1e9
-    traffic = measured_traffic(args.traffic, w.name, dom)
-    gate_flops = 2.0 * T * w.d * E
-    gs = "gate_select" if "gate_select" in stages else ("gate" if "gate" in stages else None)
-    maxvio = float(counts.max().item()) / (R_valid / E) - 1.0 if R_valid else 0.0
-    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic,
-                "gate_mfma_frac": round(gate_flops / (stages[gs]["avg_us"] * 1e-6) / 1e12
-                                        / MFMA_BF16_PEAK_TFLOPS, 4) if gs else None}
-    for s, v in stages.items():
-        log(f"[bench] {s:13s} {v['avg_us']:9.2f} us  {v['GBs']} GB/s")
-    pipeline = pipeline_roofline(w, T, R, R_valid, ms_per_step * 1e3)
-    log(f"[bench] staged roofline {pipeline['t_roof_staged_us']} us -> pipeline fraction "
-        f"{pipeline['frac_staged']}")
-
-    # the combine that follows the experts, timed on its own (not part of a
-    # step): synthetic expert outputs in this step's dispatch order plus a
-    # shared expert's output; rotating copies of the rows keep them from
-    # being served out of the last-level cache
-    combine = permute = None
-    if not args.no_combine and R_valid > 0:
-        eb = 2 if w.dtype == "bf16" else 4
-        Y_np, sh_np = wl.expert_outputs(w, R_valid), wl.shared_output(w)
-        Y0 = up(Y_np)
-        n_yc = max(1, min(16, math.ceil(3 * LLC_BYTES / (R_valid * w.d * eb))))
-        Ys = [Y0] + [torch.roll(Y0, shifts=89 * i, dims=0).contiguous() for i in range(1, n_yc)]
-        sh = up(sh_np)
-        yout = torch.empty((T, w.d), dtype=Y0.dtype, device=dev)
-        for i in range(20):
-            tda.combine(Ys[i % n_yc], inv, weights, shared=sh, out=yout)
-        torch.cuda.synchronize()
-        tda.profile_enable(True)
-        n_c = 50
-        for i in range(n_c):
-            tda.combine(Ys[i % n_yc], inv, weights, shared=sh, out=yout)
-        torch.cuda.synchronize()
-        cms, cn = tda.profile_read()["combine"]
-        tda.profile_enable(False)
-        c_us = cms / cn * 1e3
-        cbytes = R_valid * w.d * eb + T * k * 8 + 2 * T * w.d * eb  # rows, inv+weights, shared, y
-        c_gbs = cbytes / (c_us * 1e-6) / 1e9
-        combine = {"kernel": "combine", "avg_us": round(c_us, 3), "launches": cn,
-                   "bytes": cbytes, "achieved": round(c_gbs, 1), "peak": HBM_PEAK_GBS,
-                   "unit": "GB/s", "frac": round(c_gbs / HBM_PEAK_GBS, 4), "rows": R_valid,
-                   "d": w.d, "shared": True, "row_copies": n_yc}
-        log(f"[bench] combine       {c_us:9.2f} us  {c_gbs:.1f} GB/s ({R_valid} rows of {w.d})")
-        # the send buffer (token rows in dispatch order, the all-to-all's
-        # input under expert parallelism), timed the same way
-        x0 = up(inp["x"])
-        n_xc = max(1, min(16, math.ceil(3 * LLC_BYTES / (T * w.d * eb))))
-        xs = [x0] + [torch.roll(x0, shifts=89 * i, dims=0).contiguous() for i in range(1, n_xc)]
-        sbuf = torch.empty((T * k, w.d), dtype=x0.dtype, device=dev)
-        for i in range(20):
-            tda.permute_rows(xs[i % n_xc], inv, k, T * k, out=sbuf)
-        torch.cuda.synchronize()
-        tda.profile_enable(True)
-        for i in range(n_c):
-            tda.permute_rows(xs[i % n_xc], inv, k, T * k, out=sbuf)
-        torch.cuda.synchronize()
-        pms, pn = tda.profile_read()["permute"]
-        tda.profile_enable(False)
-        p_us = pms / pn * 1e3
-        # each token row read once, every placed route's row written once,
-        # inv read
-        pbytes = T * w.d * eb + R_valid * w.d * eb + T * k * 4
-        p_gbs = pbytes / (p_us * 1e-6) / 1e9
-        permute = {"kernel": "permute", "avg_us": round(p_us, 3), "launches": pn,
-                   "bytes": pbytes, "achieved": round(p_gbs, 1), "peak": HBM_PEAK_GBS,
-                   "unit": "GB/s", "frac": round(p_gbs / HBM_PEAK_GBS, 4), "rows": R_valid,
-                   "d": w.d, "row_copies": n_xc}
-        log(f"[bench] permute       {p_us:9.2f} us  {p_gbs:.1f} GB/s ({R_valid} rows of {w.d})")
-        del sbuf, xs, x0
-        if not args.no_cpu_baseline:
-            combine["cpu_baseline"] = combine_cpu_baseline(
-                Y_np, inv.cpu().numpy().reshape(T, k), weights.cpu().numpy(), sh_np)
-        del Ys, Y0, Y_np
+    head = measure(w, inp, dev, args, headline=True)
+    configs[w.name] = {k: v for k, v in head.items() if k not in ("combine", "permute")}
+    configs[w.name]["workload"] = describe(w)
 
     cpu = None
     if not args.no_cpu_baseline:
-        try:
-            threads = min(16, len(os.sched_getaffinity(0)))
-        except AttributeError:
-            threads = min(16, os.cpu_count() or 1)
-        log(f"[bench] timing the CPU oracle on {threads} threads (~{args.cpu_seconds:.0f} s)")
+        log(f"[bench] timing the CPU oracle on {threads} host threads")
         cpu = cpu_baseline(w, inp, args.cpu_seconds, threads)
+        configs[w.name]["cpu_baseline"] = cpu
+        for name, cinp in config_inputs.items():
+            configs[name]["cpu_baseline"] = cpu_baseline(wl.WORKLOADS[name], cinp,
+                                                         args.config_cpu_seconds, threads)
 
+    ms = head["ms_per_step"]
     out = {
-        "metric": "routed tokens/sec (gate+select+dispatch) and % of MFMA/HBM roofline, 1 MI355X",
-        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6),
+        "metric": METRIC,
+        "value": round(w.T / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
         "timing": "eager launches on one stream",
-        "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 6),
-        "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": f"{w.name}: T={T} tokens, d={w.d}, E={E}, "
-                               f"k={'/'.join(map(str, w.dynamic_k)) + ' per request' if w.dynamic_k else k}, "
-                               f"score={w.score}, groups={w.n_groups}/{w.topk_groups}, "
-                               + (f"hash ids from tid2eid[{w.hash_vocab}][{k}], "
-                                  if w.hash_vocab else "")
-                               + f"dispatch over {E} experts"
-                               + (f" with capacity {wl.capacity(w)}" if w.capacity_factor else ""),
-                   "T": T, "d": w.d, "E": E, "k_max": k, "x_copies": n_copies},
-        "step_us": step_spread,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": describe(w), "T": w.T, "d": w.d, "E": w.E, "k_max": w.k},
+        "step_us": head.get("step_us"),
+        "graph": head.get("graph"),
         "inputs": inputs_record(inp),
-        "stages": stages,
-        "pipeline": pipeline,
-        "maxvio": round(maxvio, 4),
-        "roofline": roofline,
-        "combine": combine,
-        "permute": permute,
+        "stages": head["stages"],
+        "pipeline": head["pipeline"],
+        "maxvio": head["maxvio"],
+        "roofline": head["roofline"],
+        "combine": head.get("combine"),
+        "permute": head.get("permute"),
         "cpu_baseline": cpu,
+        "configs": configs,
     }
     print(json.dumps(out), flush=True)
 

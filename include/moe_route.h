@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 10
+#define MOE_ABI_VERSION 11
 
 /* return codes */
 #define MOE_OK 0
@@ -207,6 +207,11 @@ size_t moe_dispatch_workspace_size(int32_t T, int32_t k_stride, int32_t E);
  *                 (a stable counting sort)          [T*k_stride], first R set
  *   inv[r]        position of route r in perm, -1 for skipped slots
  *                 [T*k_stride], may be NULL
+ *   maxvio        [1] fp64, or NULL: the load statistic MaxVio =
+ *                 max_e counts[e] / (R / E) - 1, R = offsets[E] (0 when
+ *                 R = 0) -- "I modelli MoE open hanno router opposti", the
+ *                 loss-free balancing paragraph (MaxVio 0.72 -> 0.04); written
+ *                 by the kernel that writes counts, in IEEE fp64 in that order
  *   workspace     16-byte aligned device memory of at least
  *                 moe_dispatch_workspace_size(T, k_stride, E) bytes; its
  *                 contents need no initialisation and are clobbered
@@ -214,7 +219,7 @@ size_t moe_dispatch_workspace_size(int32_t T, int32_t k_stride, int32_t E);
  */
 int32_t moe_dispatch(const int32_t* ids, int32_t T, int32_t k_stride, int32_t E,
                      int32_t* counts, int32_t* offsets, int32_t* perm,
-                     int32_t* inv, void* workspace, size_t workspace_bytes,
+                     int32_t* inv, double* maxvio, void* workspace, size_t workspace_bytes,
                      int32_t* dev_err, void* stream);
 
 /*
@@ -285,16 +290,16 @@ int32_t moe_dispatch_capacity(const int32_t* ids, int32_t T, int32_t k_stride, i
  *                moe_route_dispatch_workspace_size(p) bytes (the gate
  *                hand-off, then the dispatch's tile data); contents need no
  *                initialisation and are clobbered
- *   counts, offsets, perm, inv, dev_err: as for moe_dispatch (dev_err also
- *                as for moe_route)
+ *   counts, offsets, perm, inv, maxvio, dev_err: as for moe_dispatch (dev_err
+ *                also as for moe_route)
  * Limits: those of moe_route and moe_dispatch.
  */
 int32_t moe_route_dispatch(const moe_route_params* p, const void* x, const void* W,
                            const float* logit_bias, const float* select_bias,
                            const int32_t* k_per_token, float* logits, int32_t* ids,
                            float* weights, int32_t* counts, int32_t* offsets, int32_t* perm,
-                           int32_t* inv, void* workspace, size_t workspace_bytes,
-                           int32_t* dev_err, void* stream);
+                           int32_t* inv, double* maxvio, void* workspace,
+                           size_t workspace_bytes, int32_t* dev_err, void* stream);
 
 /* Bytes of device workspace moe_route_dispatch needs for these parameters
  * (16-byte aligned x and W assumed). */

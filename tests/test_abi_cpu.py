@@ -145,14 +145,14 @@ def test_dispatch_validation_and_workspace_size():
     assert tda.dispatch_workspace_size(0, 8, 64) == 0
     assert tda.dispatch_workspace_size(-1, 8, 64) == 0
     ws = tda.dispatch_workspace_size(100, 8, 64)
-    assert L.moe_dispatch(FAKE, 100, 8, 64, FAKE, FAKE, FAKE, None, FAKE, ws - 1, None,
+    assert L.moe_dispatch(FAKE, 100, 8, 64, FAKE, FAKE, FAKE, None, None, FAKE, ws - 1, None,
                           None) == tda.MOE_EINVAL
     assert "workspace" in L.moe_last_error().decode()
-    assert L.moe_dispatch(FAKE, 100, 0, 64, FAKE, FAKE, FAKE, None, FAKE, ws, None,
+    assert L.moe_dispatch(FAKE, 100, 0, 64, FAKE, FAKE, FAKE, None, None, FAKE, ws, None,
                           None) == tda.MOE_EINVAL
-    assert L.moe_dispatch(FAKE, 100, 8, 4096, FAKE, FAKE, FAKE, None, FAKE, ws, None,
+    assert L.moe_dispatch(FAKE, 100, 8, 4096, FAKE, FAKE, FAKE, None, None, FAKE, ws, None,
                           None) == tda.MOE_EUNSUPPORTED
-    assert L.moe_dispatch(FAKE, 100, 8, 64, None, FAKE, FAKE, None, FAKE, ws, None,
+    assert L.moe_dispatch(FAKE, 100, 8, 64, None, FAKE, FAKE, None, None, FAKE, ws, None,
                           None) == tda.MOE_EINVAL
 
 
@@ -165,7 +165,7 @@ def test_binding_rejects_host_tensors():
 def test_dispatch_rejects_unaligned_workspace():
     L = tda.lib()
     ws = tda.dispatch_workspace_size(100, 8, 64)
-    assert L.moe_dispatch(FAKE, 100, 8, 64, FAKE, FAKE, FAKE, None, ctypes.c_void_p(0x1004), ws,
+    assert L.moe_dispatch(FAKE, 100, 8, 64, FAKE, FAKE, FAKE, None, None, ctypes.c_void_p(0x1004), ws,
                           None, None) == tda.MOE_EINVAL
     assert "aligned" in L.moe_last_error().decode()
 
@@ -213,7 +213,8 @@ def test_route_dispatch_validation():
     p = tda.make_params(64, 128, 16, 2)
     n = tda.route_dispatch_workspace_size(64, 128, 16, 2)
     args = lambda counts, ws, nbytes: (ctypes.byref(p), FAKE, FAKE, None, None, None, None, FAKE,
-                                       FAKE, counts, FAKE, FAKE, None, ws, nbytes, None, None)
+                                       FAKE, counts, FAKE, FAKE, None, None, ws, nbytes, None,
+                                       None)
     assert L.moe_route_dispatch(*args(None, ctypes.c_void_p(0x1000), n)) == tda.MOE_EINVAL
     assert "counts" in L.moe_last_error().decode()
     assert L.moe_route_dispatch(*args(FAKE, ctypes.c_void_p(0x1000), n - 1)) == tda.MOE_EINVAL
@@ -222,7 +223,8 @@ def test_route_dispatch_validation():
     assert "aligned" in L.moe_last_error().decode()
     bad = tda.make_params(64, 128, 16, 0)
     assert L.moe_route_dispatch(ctypes.byref(bad), FAKE, FAKE, None, None, None, None, FAKE, FAKE,
-                                FAKE, FAKE, FAKE, None, FAKE, n, None, None) == tda.MOE_EINVAL
+                                FAKE, FAKE, FAKE, None, None, FAKE, n, None,
+                                None) == tda.MOE_EINVAL
 
 
 def test_plan_constants_match_binding():

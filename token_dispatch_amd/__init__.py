@@ -21,7 +21,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe_route.so")
 
-ABI_VERSION = 10
+ABI_VERSION = 11
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EDEVICE = 0, -1, -2, -3
 MAX_EXPERTS, MAX_K, MAX_GROUPS = 1024, 32, 64
 SCORES = {"softmax": 0, "sigmoid": 1, "sqrt_softplus": 2, "softmax_topk": 3}
@@ -80,9 +80,10 @@ def lib() -> ctypes.CDLL:
         L.moe_route_hash_workspace_size.restype = ctypes.c_size_t
         L.moe_dispatch_workspace_size.argtypes = [i32, i32, i32]
         L.moe_dispatch_workspace_size.restype = ctypes.c_size_t
-        L.moe_dispatch.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, ctypes.c_size_t, vp, vp]
+        L.moe_dispatch.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                   vp, vp]
         L.moe_dispatch.restype = i32
-        L.moe_route_dispatch.argtypes = [P] + [vp] * 13 + [ctypes.c_size_t, vp, vp]
+        L.moe_route_dispatch.argtypes = [P] + [vp] * 14 + [ctypes.c_size_t, vp, vp]
         L.moe_route_dispatch.restype = i32
         L.moe_route_dispatch_workspace_size.argtypes = [P]
         L.moe_route_dispatch_workspace_size.restype = ctypes.c_size_t
@@ -300,11 +301,12 @@ def route_dispatch(x: Optional[torch.Tensor], W: Optional[torch.Tensor], k: int,
                    route_scale: float = 1.0, logits: Optional[torch.Tensor] = None,
                    E: Optional[int] = None, ids=None, weights=None, counts=None, offsets=None,
                    perm=None, inv=None, with_inv: bool = True, workspace=None, dev_err=None,
-                   k_per_group: int = 0, k_per_request=None, request_lens=None):
+                   k_per_group: int = 0, k_per_request=None, request_lens=None, maxvio=None):
     """route() then dispatch() of its ids in one library call.  Returns
     (ids, weights, counts, offsets, perm, inv); ``workspace`` (256-byte
     aligned uint8 device tensor) is allocated when not given.  k_per_request
-    with request_lens: a k per request, expanded to k_per_token."""
+    with request_lens: a k per request, expanded to k_per_token.  maxvio:
+    optional float64 device tensor [1] that receives the load statistic."""
     k_per_token = _request_k(k_per_token, k_per_request, request_lens,
                              (x if x is not None else logits).shape[0],
                              (x if x is not None else logits).device)
@@ -324,11 +326,14 @@ def route_dispatch(x: Optional[torch.Tensor], W: Optional[torch.Tensor], k: int,
     if workspace is None:
         nbytes = int(lib().moe_route_dispatch_workspace_size(ctypes.byref(p)))
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    if maxvio is not None:
+        _dev(maxvio, "maxvio", torch.float64, (1,))
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib().moe_route_dispatch(ctypes.byref(p), _p(x), _p(W), _p(logit_bias),
                                     _p(select_bias), _p(k_per_token), _p(logits), _p(ids),
                                     _p(weights), _p(counts), _p(offsets), _p(perm), _p(inv),
-                                    _p(workspace), ws_bytes, _p(dev_err), _stream(device)))
+                                    _p(maxvio), _p(workspace), ws_bytes, _p(dev_err),
+                                    _stream(device)))
     return ids, weights, counts, offsets, perm, inv
 
 
@@ -384,9 +389,11 @@ def dispatch_workspace_size(T: int, k_stride: int, E: int) -> int:
 
 
 def dispatch(ids: torch.Tensor, E: int, *, with_inv: bool = True, counts=None, offsets=None,
-             perm=None, inv=None, workspace=None, dev_err=None):
+             perm=None, inv=None, workspace=None, dev_err=None, maxvio=None):
     """Stable grouping of routes by expert.  Returns (counts, offsets, perm, inv);
-    perm has T*k_stride entries of which the first offsets[E] are set."""
+    perm has T*k_stride entries of which the first offsets[E] are set.  maxvio:
+    optional float64 device tensor [1] that receives the load statistic
+    max_e counts[e] / (R / E) - 1."""
     _dev(ids, "ids", torch.int32)
     T, ks = ids.shape
     device = ids.device
@@ -402,8 +409,11 @@ def dispatch(ids: torch.Tensor, E: int, *, with_inv: bool = True, counts=None, o
     ws_bytes = dispatch_workspace_size(T, ks, E)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=device)
+    if maxvio is not None:
+        _dev(maxvio, "maxvio", torch.float64, (1,))
     _check(lib().moe_dispatch(_p(ids), T, ks, E, _p(counts), _p(offsets), _p(perm), _p(inv),
-                              _p(workspace), workspace.numel(), _p(dev_err), _stream(device)))
+                              _p(maxvio), _p(workspace), workspace.numel(), _p(dev_err),
+                              _stream(device)))
     return counts, offsets, perm, inv
 
 

@@ -211,13 +211,15 @@ __global__ __launch_bounds__(WAVES * kWave) void disp_scatter_kernel(
     const int32_t* __restrict__ ids, int64_t R, int E, int nt,
     const hist_t* __restrict__ tile_hist, const int32_t* __restrict__ tile_base,
     const int32_t* __restrict__ totals, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv,
+    double* __restrict__ maxvio) {
   constexpr int NT = WAVES * kWave;
   static_assert(NT >= kMaxE / 4, "offsets scan: 4 experts per thread");
   __shared__ int32_t wh[WAVES][kMaxE];
   __shared__ int32_t off[kMaxE];
   __shared__ int32_t tot[FUSED ? kMaxE : 1];
   __shared__ int32_t wsum[WAVES];
+  __shared__ int32_t wmax[WAVES];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int tile = blockIdx.x;
 
@@ -341,8 +343,24 @@ __global__ __launch_bounds__(WAVES * kWave) void disp_scatter_kernel(
   }
   const int inc = wave_incl_scan_i32(s);
   if (lane == 63) wsum[wave] = inc;
+  if (blockIdx.x == 0 && maxvio) {  // the busiest expert, for the load statistic
+    const uint32_t mx = wave_max_u32((uint32_t)max(max(t4[0], t4[1]), max(t4[2], t4[3])));
+    if (lane == 0) wmax[wave] = (int32_t)mx;
+  }
   for (int e = lane; e < E; e += kWave) wh[wave][e] = 0;
   __syncthreads();
+  if (blockIdx.x == 0 && maxvio && tid == 0) {
+    // MaxVio = max_e count_e / (R / E) - 1 ("I modelli MoE open hanno router
+    // opposti", loss-free balancing paragraph), 0 without routes
+    int64_t R_all = 0;
+    int32_t mx = 0;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+      R_all += wsum[w];
+      mx = max(mx, wmax[w]);
+    }
+    *maxvio = R_all > 0 ? (double)mx / ((double)R_all / (double)E) - 1.0 : 0.0;
+  }
   int base = inc - s;
 #pragma unroll
   for (int w = 0; w < WAVES; ++w) base += w < wave ? wsum[w] : 0;  // straight-line
@@ -428,13 +446,14 @@ template <int TILE, bool FUSED>
 hipError_t launch_scatter(const int32_t* ids, int64_t R, int32_t E, int nt,
                           const hist_t* tile_hist, const int32_t* tile_base,
                           const int32_t* totals, int32_t* counts, int32_t* offsets,
-                          int32_t* perm, int32_t* inv, hipStream_t stream) {
+                          int32_t* perm, int32_t* inv, double* maxvio, hipStream_t stream) {
   constexpr int W = TILE / kWave >= 16 ? 16 : TILE / kWave;
   // with no routes (three-kernel path only) one workgroup writes zero
   // counts and offsets
   auto go = [&](auto kernel) {
     return launch(kStageDispScatter, kernel, dim3(nt > 0 ? nt : 1), dim3(W * kWave), stream,
-                  ids, R, E, nt, tile_hist, tile_base, totals, counts, offsets, perm, inv);
+                  ids, R, E, nt, tile_hist, tile_base, totals, counts, offsets, perm, inv,
+                  maxvio);
   };
   switch (id_bits(E)) {
     case 7: return go(disp_scatter_kernel<W, TILE, FUSED, 7>);
@@ -461,12 +480,13 @@ hipError_t launch_hist(const int32_t* ids, int64_t R, int32_t E, int nt,
 
 hipError_t launch_placement(int tile_routes, const int32_t* ids, int64_t R, int32_t E, int nt,
                             const hist_t* tile_hist, int32_t* counts, int32_t* offsets,
-                            int32_t* perm, int32_t* inv, hipStream_t stream) {
+                            int32_t* perm, int32_t* inv, double* maxvio,
+                            hipStream_t stream) {
   switch (tile_routes) {
 #define MOE_PLACE(T_)                                                                        \
   case T_:                                                                                   \
     return launch_scatter<T_, true>(ids, R, E, nt, tile_hist, nullptr, nullptr, counts, \
-                                    offsets, perm, inv, stream);
+                                    offsets, perm, inv, maxvio, stream);
     MOE_PLACE(256)
     MOE_PLACE(512)
     MOE_PLACE(1024)
@@ -478,14 +498,14 @@ hipError_t launch_placement(int tile_routes, const int32_t* ids, int64_t R, int3
 
 template <int CPW>
 hipError_t launch_fused(const int32_t* ids, int64_t R, int32_t E, int32_t* counts,
-                        int32_t* offsets, int32_t* perm, int32_t* inv, hist_t* tile_hist,
-                        int32_t* dev_err, hipStream_t stream) {
+                        int32_t* offsets, int32_t* perm, int32_t* inv, double* maxvio,
+                        hist_t* tile_hist, int32_t* dev_err, hipStream_t stream) {
   constexpr int kRoutes = kWaves * CPW * kWave;
   const int nt = (int)((R + kRoutes - 1) / kRoutes);
   hipError_t e = launch_hist<CPW, true>(ids, R, E, nt, tile_hist, dev_err, stream);
   if (e != hipSuccess) return e;
   return launch_placement(kRoutes, ids, R, E, nt, tile_hist, counts, offsets, perm, inv,
-                          stream);
+                          maxvio, stream);
 }
 
 // Capacity limit on a dispatch (top-1 routing with a Switch-style capacity;
@@ -546,12 +566,12 @@ bool dispatch_hist_ok(int64_t R, int32_t E, int32_t tile_routes) {
 
 hipError_t launch_dispatch_from_hist(const int32_t* ids, int64_t R, int32_t E,
                                      int32_t* counts, int32_t* offsets, int32_t* perm,
-                                     int32_t* inv, const hist_t* tile_hist,
+                                     int32_t* inv, double* maxvio, const hist_t* tile_hist,
                                      int32_t tile_routes, hipStream_t stream) {
   if (!dispatch_hist_ok(R, E, tile_routes)) return hipErrorInvalidValue;
   const int nt = (int)((R + tile_routes - 1) / tile_routes);
   return launch_placement(tile_routes, ids, R, E, nt, tile_hist, counts, offsets,
-                          perm, inv, stream);
+                          perm, inv, maxvio, stream);
 }
 
 int dispatch_kernels(int64_t R, int32_t E) {
@@ -571,14 +591,20 @@ size_t dispatch_workspace_bytes(int64_t R, int32_t E) {
 
 hipError_t launch_dispatch(const int32_t* ids, int64_t R, int32_t E,
                            int32_t* counts, int32_t* offsets, int32_t* perm,
-                           int32_t* inv, void* workspace, int32_t* dev_err,
-                           hipStream_t stream) {
+                           int32_t* inv, double* maxvio, void* workspace,
+                           int32_t* dev_err, hipStream_t stream) {
   int32_t* ws = static_cast<int32_t*>(workspace);
   if (R > 0) {
     switch (fused_cpw(R, E)) {
-      case 2: return launch_fused<2>(ids, R, E, counts, offsets, perm, inv, static_cast<hist_t*>(workspace), dev_err, stream);
-      case 4: return launch_fused<4>(ids, R, E, counts, offsets, perm, inv, static_cast<hist_t*>(workspace), dev_err, stream);
-      case 8: return launch_fused<8>(ids, R, E, counts, offsets, perm, inv, static_cast<hist_t*>(workspace), dev_err, stream);
+      case 2:
+        return launch_fused<2>(ids, R, E, counts, offsets, perm, inv, maxvio,
+                                 static_cast<hist_t*>(workspace), dev_err, stream);
+      case 4:
+        return launch_fused<4>(ids, R, E, counts, offsets, perm, inv, maxvio,
+                                 static_cast<hist_t*>(workspace), dev_err, stream);
+      case 8:
+        return launch_fused<8>(ids, R, E, counts, offsets, perm, inv, maxvio,
+                                 static_cast<hist_t*>(workspace), dev_err, stream);
       default: break;
     }
   }
@@ -599,7 +625,7 @@ hipError_t launch_dispatch(const int32_t* ids, int64_t R, int32_t E,
   // zero counts and offsets (totals is not read then)
   return launch_scatter<kTile, false>(ids, R, E, nt, nullptr, tile_base,
                                       nt > 0 ? totals : nullptr, counts, offsets, perm, inv,
-                                      stream);
+                                      maxvio, stream);
 }
 
 }  // namespace moe

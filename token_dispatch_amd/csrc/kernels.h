@@ -130,7 +130,7 @@ hipError_t launch_route_dispatch_small(const RouteCfg& c, const float* logits, i
                                        const int32_t* k_per_token, int32_t* ids,
                                        float* weights, int32_t* dev_err, int32_t* counts,
                                        int32_t* offsets, int32_t* perm, int32_t* inv,
-                                       hipStream_t stream);
+                                       double* maxvio, hipStream_t stream);
 
 // Hash routing: table gather (+ k gathered gate dot products and weights).
 // With `logits` (the sum of `splits` arrays [T][E], split_stride floats
@@ -149,7 +149,7 @@ hipError_t launch_hash_route(const RouteCfg& c, int32_t dtype,
 bool dispatch_hist_ok(int64_t R, int32_t E, int32_t tile_routes);
 hipError_t launch_dispatch_from_hist(const int32_t* ids, int64_t R, int32_t E,
                                      int32_t* counts, int32_t* offsets, int32_t* perm,
-                                     int32_t* inv, const hist_t* tile_hist,
+                                     int32_t* inv, double* maxvio, const hist_t* tile_hist,
                                      int32_t tile_routes, hipStream_t stream);
 
 // Combine: y[t] = sum_j weights[t][j] * Yp[inv[t*k+j]] (+ shared[t]), fp32
@@ -174,12 +174,14 @@ hipError_t launch_capacity(const int32_t* ids, int64_t R, int32_t E, int32_t C,
                            const int32_t* offsets, const int32_t* inv, int32_t* slot,
                            int32_t* kept, int32_t* dropped, hipStream_t stream);
 
-// Dispatch: tile histograms -> scan -> stable scatter.
+// Dispatch: tile histograms -> scan -> stable scatter.  maxvio (or NULL):
+// the load statistic max_e counts[e] / (R / E) - 1 in fp64 (0 when R = 0),
+// written by the kernel that writes counts.
 size_t dispatch_workspace_bytes(int64_t R, int32_t E);
 int dispatch_kernels(int64_t R, int32_t E);  // kernels launch_dispatch enqueues
 hipError_t launch_dispatch(const int32_t* ids, int64_t R, int32_t E,
                            int32_t* counts, int32_t* offsets, int32_t* perm,
-                           int32_t* inv, void* workspace, int32_t* dev_err,
+                           int32_t* inv, double* maxvio, void* workspace, int32_t* dev_err,
                            hipStream_t stream);
 
 }  // namespace moe

@@ -189,6 +189,7 @@ namespace {
 // Dispatch outputs when a small batch is routed and dispatched by one kernel.
 struct SmallDispatch {
   int32_t *counts, *offsets, *perm, *inv;
+  double* maxvio;
 };
 
 // Gate + select of moe_route on validated arguments (T > 0, ids and weights
@@ -206,7 +207,7 @@ int32_t route_core(const moe_route_params* p, const void* x, const void* W,
     if (sd)
       e = moe::launch_route_dispatch_small(c, logits, 1, 0, nullptr, logit_bias, select_bias,
                                            k_per_token, ids, weights, dev_err, sd->counts,
-                                           sd->offsets, sd->perm, sd->inv, s);
+                                           sd->offsets, sd->perm, sd->inv, sd->maxvio, s);
     else
       e = moe::launch_select(c, logits, 1, 0, nullptr, logit_bias, select_bias, k_per_token,
                              ids, weights, dev_err, hist, s);
@@ -249,7 +250,7 @@ int32_t route_core(const moe_route_params* p, const void* x, const void* W,
     e = moe::launch_route_dispatch_small(c, hand_off, g.splits, (int64_t)p->T * p->E,
                                          g.splits > 1 ? logits : nullptr, nullptr, select_bias,
                                          k_per_token, ids, weights, dev_err, sd->counts,
-                                         sd->offsets, sd->perm, sd->inv, s);
+                                         sd->offsets, sd->perm, sd->inv, sd->maxvio, s);
   else
     e = moe::launch_select(c, hand_off, g.splits, (int64_t)p->T * p->E,
                            g.splits > 1 ? logits : nullptr, nullptr, select_bias, k_per_token,
@@ -334,8 +335,8 @@ int32_t moe_route_dispatch(const moe_route_params* p, const void* x, const void*
                            const float* logit_bias, const float* select_bias,
                            const int32_t* k_per_token, float* logits, int32_t* ids,
                            float* weights, int32_t* counts, int32_t* offsets, int32_t* perm,
-                           int32_t* inv, void* workspace, size_t workspace_bytes,
-                           int32_t* dev_err, void* stream) {
+                           int32_t* inv, double* maxvio, void* workspace,
+                           size_t workspace_bytes, int32_t* dev_err, void* stream) {
   int32_t rc = check_route_call(p, x, W, logits, ids, weights);
   if (rc != MOE_OK) return rc;
   const int64_t R = (int64_t)p->T * p->k;
@@ -351,13 +352,14 @@ int32_t moe_route_dispatch(const moe_route_params* p, const void* x, const void*
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (p->T == 0) {  // zero counts and offsets only
-    e = moe::launch_dispatch(ids, 0, p->E, counts, offsets, perm, inv, nullptr, dev_err, s);
+    e = moe::launch_dispatch(ids, 0, p->E, counts, offsets, perm, inv, maxvio, nullptr, dev_err,
+                             s);
     if (e != hipSuccess) return device_fail(e, "dispatch launch");
     return MOE_OK;
   }
   const size_t route = align256(route_ws_bytes(p));
   if (moe::small_dispatch_ok(to_cfg(p)) && !std::getenv("MOE_NO_SMALL_DISPATCH")) {
-    const SmallDispatch sd{counts, offsets, perm, inv};
+    const SmallDispatch sd{counts, offsets, perm, inv, maxvio};
     return route_core(p, x, W, logit_bias, select_bias, k_per_token, logits, ids, weights,
                       workspace, route, dev_err, nullptr, s, &sd);
   }
@@ -371,11 +373,12 @@ int32_t moe_route_dispatch(const moe_route_params* p, const void* x, const void*
                   s);
   if (rc != MOE_OK) return rc;
   if (n > 0)
-    e = moe::launch_dispatch_from_hist(ids, R, p->E, counts, offsets, perm, inv,
+    e = moe::launch_dispatch_from_hist(ids, R, p->E, counts, offsets, perm, inv, maxvio,
                                        static_cast<const moe::hist_t*>(disp_ws),
                                        n * p->k, s);
   else
-    e = moe::launch_dispatch(ids, R, p->E, counts, offsets, perm, inv, disp_ws, dev_err, s);
+    e = moe::launch_dispatch(ids, R, p->E, counts, offsets, perm, inv, maxvio, disp_ws, dev_err,
+                             s);
   if (e != hipSuccess) return device_fail(e, "dispatch launch");
   return MOE_OK;
 }
@@ -482,7 +485,7 @@ size_t moe_dispatch_workspace_size(int32_t T, int32_t k_stride, int32_t E) {
 
 int32_t moe_dispatch(const int32_t* ids, int32_t T, int32_t k_stride, int32_t E,
                      int32_t* counts, int32_t* offsets, int32_t* perm,
-                     int32_t* inv, void* workspace, size_t workspace_bytes,
+                     int32_t* inv, double* maxvio, void* workspace, size_t workspace_bytes,
                      int32_t* dev_err, void* stream) {
   if (T < 0) return fail(MOE_EINVAL, "T=%d must be >= 0", T);
   if (k_stride < 1) return fail(MOE_EINVAL, "k_stride=%d must be >= 1", k_stride);
@@ -499,8 +502,8 @@ int32_t moe_dispatch(const int32_t* ids, int32_t T, int32_t k_stride, int32_t E,
                 need);
   if (need > 0 && reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
     return fail(MOE_EINVAL, "workspace must be 16-byte aligned");
-  hipError_t e = moe::launch_dispatch(ids, R, E, counts, offsets, perm, inv, workspace, dev_err,
-                                      static_cast<hipStream_t>(stream));
+  hipError_t e = moe::launch_dispatch(ids, R, E, counts, offsets, perm, inv, maxvio, workspace,
+                                      dev_err, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_fail(e, "dispatch launch");
   return MOE_OK;
 }
@@ -582,3 +585,4 @@ int32_t moe_ep_layout(const int32_t* offsets, int32_t E, int32_t n_ranks, int32_
 }
 
 }  // extern "C"
+

@@ -163,7 +163,7 @@ __global__ __launch_bounds__(small_waves(VPL, NSPLIT) * kWave) void route_dispat
     const float* __restrict__ select_bias, const int32_t* __restrict__ k_per_token,
     int32_t* __restrict__ ids, float* __restrict__ weights, int32_t* __restrict__ dev_err,
     int vec, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+    int32_t* __restrict__ perm, int32_t* __restrict__ inv, double* __restrict__ maxvio) {
   constexpr int kSmallWaves = small_waves(VPL, NSPLIT);
   constexpr int TPW = kWave / LPT;               // tokens per wavefront and pass
   constexpr int TPP = kSmallWaves * TPW;         // tokens per pass
@@ -291,6 +291,10 @@ __global__ __launch_bounds__(small_waves(VPL, NSPLIT) * kWave) void route_dispat
       offsets[2 * lane + 1] = off[2 * lane + 1] = inc - b;
     }
     if (lane == 63) offsets[E] = off[E] = inc;
+    if (maxvio) {  // MaxVio = max_e count_e / (R / E) - 1, 0 without routes
+      const int mx = (int)wave_max_u32((uint32_t)max(a, b));
+      if (lane == 63) *maxvio = inc > 0 ? (double)mx / ((double)inc / (double)E) - 1.0 : 0.0;
+    }
   }
   __syncthreads();
   for (int ch = wave; ch < nch; ch += kSmallWaves) {
@@ -472,7 +476,7 @@ hipError_t launch_route_dispatch_small(const RouteCfg& c, const float* logits, i
                                        const int32_t* k_per_token, int32_t* ids,
                                        float* weights, int32_t* dev_err, int32_t* counts,
                                        int32_t* offsets, int32_t* perm, int32_t* inv,
-                                       hipStream_t stream) {
+                                       double* maxvio, hipStream_t stream) {
   if (!small_dispatch_ok(c)) return hipErrorInvalidValue;
   const bool grouped = c.n_groups > 1 && c.topk_groups < c.n_groups;
   const bool mono = select_bias == nullptr && !grouped && c.k_per_group == 0;
@@ -487,7 +491,7 @@ hipError_t launch_route_dispatch_small(const RouteCfg& c, const float* logits, i
                   dim3(small_waves(V_, S_) * kWave), stream, c, logits, split_stride,        \
                   logits_out,                                                                  \
                   logit_bias, select_bias, k_per_token, ids, weights, dev_err, vec, counts,  \
-                  offsets, perm, inv);
+                  offsets, perm, inv, maxvio);
 #define MOE_SDV(L_, V_)   \
   MOE_SD(L_, V_, 1, true) \
   MOE_SD(L_, V_, 1, false) \
