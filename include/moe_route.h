@@ -306,6 +306,31 @@ int32_t moe_route_dispatch(const moe_route_params* p, const void* x, const void*
 size_t moe_route_dispatch_workspace_size(const moe_route_params* p);
 
 /*
+ * moe_route_dispatch_noalloc -- moe_route_dispatch with no workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).
+ * The scratch the call needs (the gate's hand-off, the dispatch's tile
+ * histograms) lives in a device array of MOE_NOALLOC_SCRATCH_BYTES inside
+ * the library: one per GPU, held until the process ends, its address looked
+ * up on the first call on that GPU (the device of `stream`).  The call
+ * allocates nothing and creates no events; it enqueues the same kernels as
+ * moe_route_dispatch and gives the same results, bit for bit.
+ *   arguments    as for moe_route_dispatch, without workspace and its size;
+ *                the caller still passes every input and output
+ * Returns MOE_EUNSUPPORTED, with the bytes needed, when
+ * moe_route_dispatch_workspace_size(p) exceeds MOE_NOALLOC_SCRATCH_BYTES.
+ * Calls that overlap on one GPU (other streams or threads) share the array
+ * and race: order them on one stream.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int32_t moe_route_dispatch_noalloc(const moe_route_params* p, const void* x, const void* W,
+                                   const float* logit_bias, const float* select_bias,
+                                   const int32_t* k_per_token, float* logits, int32_t* ids,
+                                   float* weights, int32_t* counts, int32_t* offsets,
+                                   int32_t* perm, int32_t* inv, double* maxvio,
+                                   int32_t* dev_err, void* stream);
+
+/*
  * How moe_route_dispatch runs for these parameters, with x and W given
  * (16-byte aligned when `aligned` is non-zero): host-side planning only,
  * nothing is enqueued.  For inspection and tests.  Returns MOE_OK, or the

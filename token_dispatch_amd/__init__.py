@@ -30,6 +30,7 @@ EXPORTS = ("moe_route", "moe_route_workspace_size", "moe_route_hash",
            "moe_route_hash_workspace_size",
            "moe_dispatch_workspace_size", "moe_dispatch",
            "moe_route_dispatch", "moe_route_dispatch_workspace_size",
+           "moe_route_dispatch_noalloc",
            "moe_route_dispatch_plan", "moe_combine", "moe_dispatch_capacity",
            "moe_permute_rows", "moe_ep_layout",
            "moe_profile_enable", "moe_profile_read",
@@ -85,6 +86,8 @@ def lib() -> ctypes.CDLL:
         L.moe_dispatch.restype = i32
         L.moe_route_dispatch.argtypes = [P] + [vp] * 14 + [ctypes.c_size_t, vp, vp]
         L.moe_route_dispatch.restype = i32
+        L.moe_route_dispatch_noalloc.argtypes = [P] + [vp] * 15
+        L.moe_route_dispatch_noalloc.restype = i32
         L.moe_route_dispatch_workspace_size.argtypes = [P]
         L.moe_route_dispatch_workspace_size.restype = ctypes.c_size_t
         L.moe_route_dispatch_plan.argtypes = [P, i32, ctypes.POINTER(PlanInfo)]
@@ -334,6 +337,41 @@ def route_dispatch(x: Optional[torch.Tensor], W: Optional[torch.Tensor], k: int,
                                     _p(weights), _p(counts), _p(offsets), _p(perm), _p(inv),
                                     _p(maxvio), _p(workspace), ws_bytes, _p(dev_err),
                                     _stream(device)))
+    return ids, weights, counts, offsets, perm, inv
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def route_dispatch_noalloc(x: Optional[torch.Tensor], W: Optional[torch.Tensor], k: int, *,
+                           score: str = "softmax", logit_bias=None, select_bias=None,
+                           k_per_token=None, n_groups: int = 1,
+                           topk_groups: Optional[int] = None,
+                           group_score: Optional[str] = None, renormalize: bool = True,
+                           route_scale: float = 1.0, logits: Optional[torch.Tensor] = None,
+                           E: Optional[int] = None, ids, weights, counts, offsets, perm,
+                           inv=None, maxvio=None, dev_err=None, k_per_group: int = 0):
+    """route_dispatch() through moe_route_dispatch_noalloc: the library's own
+    per-GPU scratch array instead of a workspace, so the call allocates
+    nothing.  Every output is the caller's (ids, weights, counts, offsets,
+    perm required; inv, maxvio, dev_err optional).  Shapes needing more than
+    NOALLOC_SCRATCH_BYTES of scratch raise MoeError (MOE_EUNSUPPORTED)."""
+    p, device, logits, ids, weights = _route_args(
+        x, W, k, score, logit_bias, select_bias, k_per_token, n_groups, topk_groups,
+        group_score, renormalize, route_scale, logits, E, ids, weights, dev_err, False,
+        k_per_group)
+    E_, R = p.E, p.T * p.k
+    _dev(counts, "counts", torch.int32, (E_,))
+    _dev(offsets, "offsets", torch.int32, (E_ + 1,))
+    _dev(perm, "perm", torch.int32, (R,))
+    if inv is not None:
+        _dev(inv, "inv", torch.int32, (R,))
+    if maxvio is not None:
+        _dev(maxvio, "maxvio", torch.float64, (1,))
+    _check(lib().moe_route_dispatch_noalloc(
+        ctypes.byref(p), _p(x), _p(W), _p(logit_bias), _p(select_bias), _p(k_per_token),
+        _p(logits), _p(ids), _p(weights), _p(counts), _p(offsets), _p(perm), _p(inv),
+        _p(maxvio), _p(dev_err), _stream(device)))
     return ids, weights, counts, offsets, perm, inv
 
 

@@ -84,6 +84,9 @@ struct ProfRecord {
 std::atomic<bool> g_prof_on{false};
 std::mutex g_prof_mu;
 std::vector<ProfRecord> g_prof_records;
+// Set while moe_route_dispatch_noalloc runs on this thread: its launches
+// carry no timing events (creating them would allocate).
+thread_local bool g_no_events = false;
 
 void prof_clear_locked() {
   for (auto& r : g_prof_records) {
@@ -133,7 +136,7 @@ namespace moe {
 
 void prof_events(Stage st, hipEvent_t* start, hipEvent_t* stop) {
   *start = *stop = nullptr;
-  if (!g_prof_on.load(std::memory_order_relaxed)) return;
+  if (g_no_events || !g_prof_on.load(std::memory_order_relaxed)) return;
   hipEvent_t a = nullptr, b = nullptr;
   if (hipEventCreate(&a) != hipSuccess) return;
   if (hipEventCreate(&b) != hipSuccess) {
@@ -586,3 +589,80 @@ int32_t moe_ep_layout(const int32_t* offsets, int32_t E, int32_t n_ranks, int32_
 
 }  // extern "C"
 
+// ---- moe_route_dispatch without a caller workspace ----------------------------
+// For callers that cannot allocate device memory (code under HIP graph
+// capture, tight serving loops): the gate's K-split hand-off and the
+// dispatch's tile histograms live in this file-scope device array instead of
+// a workspace.  Every GPU the library runs on holds its own copy until the
+// process ends.  No kernel needs it zeroed: each call writes every byte it
+// later reads.  Calls that overlap on one GPU (two streams, or two threads)
+// share the array and race.
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)MOE_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the device of `stream` (looked up once
+// per device, with that device current).
+int32_t scratch_for_stream(hipStream_t stream, void** out) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return device_fail(e, "get device");
+  int dev = cur;
+  if (stream) {
+    hipDevice_t sd = 0;
+    e = hipStreamGetDevice(stream, &sd);
+    if (e != hipSuccess) return device_fail(e, "stream device");
+    dev = (int)sd;
+  }
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_EUNSUPPORTED, "device %d is beyond the %d the library tracks", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return device_fail(e, "set device");
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (e != hipSuccess) return device_fail(e, "scratch symbol address");
+    if (!ptr || reinterpret_cast<uintptr_t>(ptr) % 256 != 0)
+      return fail(MOE_EDEVICE, "scratch symbol address is not 256-byte aligned");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" int32_t moe_route_dispatch_noalloc(
+    const moe_route_params* p, const void* x, const void* W, const float* logit_bias,
+    const float* select_bias, const int32_t* k_per_token, float* logits, int32_t* ids,
+    float* weights, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+    double* maxvio, int32_t* dev_err, void* stream) {
+  int32_t rc = check_route_call(p, x, W, logits, ids, weights);
+  if (rc != MOE_OK) return rc;
+  const size_t need = moe_route_dispatch_workspace_size(p);
+  if (need > kScratchBytes)
+    return fail(MOE_EUNSUPPORTED,
+                "these shapes need %zu bytes of scratch; moe_route_dispatch_noalloc holds %zu "
+                "(use moe_route_dispatch with a workspace)",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  rc = scratch_for_stream(static_cast<hipStream_t>(stream), &ws);
+  if (rc != MOE_OK) return rc;
+  g_no_events = true;
+  rc = moe_route_dispatch(p, x, W, logit_bias, select_bias, k_per_token, logits, ids, weights,
+                          counts, offsets, perm, inv, maxvio, ws, kScratchBytes, dev_err, stream);
+  g_no_events = false;
+  return rc;
+}
