@@ -608,8 +608,12 @@ def main():
     threads = host_threads()
     w = wl.WORKLOADS[args.workload]
 
-    # the other routing configurations first (their own warm-up and steps;
-    # they also bring the GPU to its working clocks before the headline)
+    # the headline's inputs first, then the other routing configurations
+    # (their own warm-up and steps), then the headline: the configurations'
+    # GPU work brings the clocks up, and no input generation idles the GPU
+    # between them and the headline's W warm-up and K timed steps
+    log(f"[bench] generating {w.name} inputs (T={w.T}, d={w.d}, E={w.E})")
+    inp = wl.make_inputs(w)
     configs, config_inputs = {}, {}
     if not args.no_configs:
         shared = {}
@@ -629,8 +633,6 @@ def main():
             config_inputs[name] = cinp
         shared.clear()
 
-    log(f"[bench] generating {w.name} inputs (T={w.T}, d={w.d}, E={w.E})")
-    inp = wl.make_inputs(w)
     head = measure(w, inp, dev, args, headline=True)
     configs[w.name] = {k: v for k, v in head.items() if k not in ("combine", "permute")}
     configs[w.name]["workload"] = describe(w)
