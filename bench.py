@@ -6,7 +6,8 @@ selection and weights of moe_route, then the histogram, offsets,
 permutation, inverse and load statistic (MaxVio) of moe_dispatch -- over
 one batch of seeded synthetic tokens (hash workloads: moe_route_hash, whose
 ids come from the token-id table and whose weights from the gathered gate
-logits, then moe_dispatch; the capacity workload adds moe_dispatch_capacity).
+logits, one moe_route_hash_dispatch call; the capacity workload adds
+moe_dispatch_capacity).
 Inputs are resident in HBM before timing; each step routes a different copy
 of x (rotating through copies totalling more than the 256 MB last-level
 cache) so the gate reads x from HBM, not from cache.
@@ -60,10 +61,12 @@ def host_threads():
     return max(1, min(n, int(env))) if env.isdigit() else n
 
 
-def kernel_work(w, T, R, R_valid, tile_bytes):
+def kernel_work(w, T, R, R_valid, tile_bytes, producer_hist=False):
     """Algorithmic (HBM bytes, flops) per launch of each kernel: inputs read
     once, outputs written once.  tile_bytes: the dispatch's per-tile
-    histogram data (written once, read once by the placement).  In a hash
+    histogram data (written once, read once by the placement); with
+    producer_hist the selection / hash kernel writes it (no disp_hist
+    launch).  In a hash
     layer the gate's work is the method's -- x and W read once and k dot
     products per token (the table replaces the selection) -- not the dense
     contraction this design performs."""
@@ -71,14 +74,15 @@ def kernel_work(w, T, R, R_valid, tile_bytes):
     E, d, k = w.E, w.d, w.k
     kt = T * 4 if w.dynamic_k else 0
     dense = 2.0 * T * d * E
+    ph = tile_bytes if producer_hist else 0
     return {
         "gate": (T * d * xb + E * d * xb, 2.0 * T * d * k) if w.hash_vocab
         else (T * d * xb + E * d * xb + T * E * 4, dense),
         # the gate kernel with the selection fused: no logits leave the chip
         "gate_select": (T * d * xb + E * d * xb + T * k * 8 + kt + tile_bytes, dense),
         # table rows, the k gathered logits, ids and weights
-        "hash": (T * 4 + T * k * 4 + T * k * 4 + T * k * 8, 0.0),
-        "select": (T * E * 4 + T * k * 8 + kt, 0.0),
+        "hash": (T * 4 + T * k * 4 + T * k * 4 + T * k * 8 + ph, 0.0),
+        "select": (T * E * 4 + T * k * 8 + kt + ph, 0.0),
         # small batches: selection and the whole dispatch in one workgroup
         "select_dispatch": (T * E * 4 + T * k * 8 + kt + R * 4 + R_valid * 4 + E * 8, 0.0),
         "disp_hist": (R * 4 + tile_bytes, 0.0),
@@ -299,18 +303,15 @@ class Case:
         self.disp_ws = ws_bytes - route_bytes  # the dispatch's tile data
         if w.hash_vocab:
             tok, tab = up(inp["token_ids"]), up(inp["tid2eid"])
-            self.disp_ws = tda.dispatch_workspace_size(T, k, E)
-            dws = torch.empty(max(1, self.disp_ws), dtype=torch.uint8, device=dev)
-            hws = torch.empty(max(1, tda.route_hash_workspace_size(T, w.d, E, k, dt, **pkw)),
-                              dtype=torch.uint8, device=dev)
-            douts = dict(counts=self.counts, offsets=self.offsets, perm=self.perm,
-                         inv=self.inv, maxvio=self.maxvio)
+            hb = tda.route_hash_dispatch_workspace_size(T, w.d, E, k, dt, **pkw)
+            hws = torch.empty(max(1, hb), dtype=torch.uint8, device=dev)
+            self.disp_ws = hb - (tda.route_hash_workspace_size(T, w.d, E, k, dt, **pkw)
+                                 + 255) // 256 * 256
 
-            def step(i):  # noqa: F811 -- moe_route_hash then moe_dispatch
-                tda.route_hash(tok, tab, E, x=xs[i % n], W=W, score=w.score, logit_bias=lb,
-                               renormalize=w.renormalize, route_scale=w.route_scale,
-                               ids=self.ids, weights=self.weights, workspace=hws)
-                tda.dispatch(self.ids, E, workspace=dws, **douts)
+            def step(i):  # noqa: F811 -- moe_route_hash_dispatch
+                tda.route_hash_dispatch(tok, tab, E, x=xs[i % n], W=W, score=w.score,
+                                        logit_bias=lb, renormalize=w.renormalize,
+                                        route_scale=w.route_scale, workspace=hws, **outs)
 
         self.step = step
         self.xbytes = xbytes
@@ -355,7 +356,8 @@ class Case:
         self.R_valid = int(self.counts.sum().item())
         two = "disp_scan" not in prof or not prof["disp_scan"][1]
         tile_bytes = self.disp_ws if two else (self.disp_ws - 4 * w.E) // 2
-        work = kernel_work(w, T, R, self.R_valid, tile_bytes)
+        work = kernel_work(w, T, R, self.R_valid, tile_bytes,
+                           producer_hist="disp_hist" not in prof or not prof["disp_hist"][1])
         stages = {}
         for name, (ms, n) in prof.items():
             if n and name in work:
@@ -386,20 +388,14 @@ def measure(w, inp, dev, args, *, headline):
     log(f"[bench] {w.name}: T={T} d={w.d} E={E} k={k}; {case.n_copies} rotating copies of x "
         f"({case.xbytes / 1e6:.1f} MB each); plan {case.plan['path']} "
         f"({case.plan['kernels']} kernels); warmup {warm}, steps {steps}")
-    for i in range(warm):
-        case.step(i)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    ms_per_step = case.timed(steps)
-    wall = time.perf_counter() - wall0
-    log(f"[bench] {w.name}: {ms_per_step * 1e3:.2f} us/step (wall {wall / steps * 1e6:.2f} us)")
-    out = {"T": T, "d": w.d, "E": E, "k_max": k, "steps": steps, "warmup": warm,
-           "ms_per_step": round(ms_per_step, 6), "tokens_per_s": round(T / (ms_per_step / 1e3), 1),
-           "plan": case.plan["path"], "kernels_per_step": case.plan["kernels"]}
-
+    out = {}
     if headline:
-        # the spread of single steps, each between its own pair of events
-        n_each = min(steps, 200)
+        # the headline's own extras first: the spread of single steps (each
+        # between its own pair of events) and the HIP-graph replays.  They
+        # run the step continuously for a while before the W warm-up steps and
+        # the K timed ones, which therefore run at working clocks (from an
+        # idle GPU the first ~80 gpt-oss-like steps take ~15 % longer)
+        n_each = min(max(steps, 20), 200)
         stream = torch.cuda.current_stream(dev)
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(n_each)]
@@ -412,8 +408,20 @@ def measure(w, inp, dev, args, *, headline):
         out["step_us"] = {"n": n_each, "median": round(float(np.median(each)), 3),
                           "p10": round(float(np.percentile(each, 10)), 3),
                           "p90": round(float(np.percentile(each, 90)), 3)}
-
-    if not args.no_graph:
+        if not args.no_graph:
+            out["graph"] = graph_replay(case, max(steps, 20), dev)
+    for i in range(warm):
+        case.step(i)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ms_per_step = case.timed(steps)
+    wall = time.perf_counter() - wall0
+    log(f"[bench] {w.name}: {ms_per_step * 1e3:.2f} us/step (wall {wall / steps * 1e6:.2f} us)")
+    out.update({"T": T, "d": w.d, "E": E, "k_max": k, "steps": steps, "warmup": warm,
+                "ms_per_step": round(ms_per_step, 6),
+                "tokens_per_s": round(T / (ms_per_step / 1e3), 1),
+                "plan": case.plan["path"], "kernels_per_step": case.plan["kernels"]})
+    if not headline and not args.no_graph:
         out["graph"] = graph_replay(case, steps, dev)
 
     stages, dom = case.kernels(min(steps, 100), args.traffic)

@@ -191,6 +191,26 @@ int32_t moe_route_hash(const moe_route_params* p, const int32_t* token_ids,
  * these parameters (16-byte aligned x and W assumed). */
 size_t moe_route_hash_workspace_size(const moe_route_params* p);
 
+/*
+ * moe_route_hash_dispatch -- moe_route_hash (with x and W, the tiled gate's
+ * logits in the workspace) followed by moe_dispatch of its ids
+ * (k_stride = p->k), with the results of the two calls (ferrox_moe docs,
+ * route_hash; the dispatch as for moe_dispatch).  The hash kernel also
+ * counts each tile's expert ids (tile histograms plus super-tile sums that
+ * the gate kernel zeroes), so the dispatch is one placement kernel.
+ *   arguments    as for moe_route_hash and moe_dispatch (x and W required)
+ *   workspace    256-byte aligned, at least
+ *                moe_route_hash_dispatch_workspace_size(p) bytes; contents
+ *                need no initialisation and are clobbered
+ */
+int32_t moe_route_hash_dispatch(const moe_route_params* p, const int32_t* token_ids,
+                                const int32_t* tid2eid, int32_t vocab, const void* x,
+                                const void* W, const float* logit_bias, int32_t* ids,
+                                float* weights, int32_t* counts, int32_t* offsets,
+                                int32_t* perm, int32_t* inv, double* maxvio, void* workspace,
+                                size_t workspace_bytes, int32_t* dev_err, void* stream);
+size_t moe_route_hash_dispatch_workspace_size(const moe_route_params* p);
+
 /* Bytes of device workspace moe_dispatch needs for these sizes. */
 size_t moe_dispatch_workspace_size(int32_t T, int32_t k_stride, int32_t E);
 
@@ -282,10 +302,14 @@ int32_t moe_dispatch_capacity(const int32_t* ids, int32_t T, int32_t k_stride, i
  * moe_route_dispatch -- moe_route followed by moe_dispatch of its ids
  * (k_stride = p->k): one pass of the router and the grouping of its routes,
  * with the results of the two calls (same arguments, same values, bit for
- * bit).  When the tokens routed by one workgroup of the selection kernel
- * form exactly one dispatch tile and the tile histograms are small (tiles x
- * E <= 32768 counts, E a multiple of 8), the selection kernel also writes
- * those histograms, saving the dispatch's counting kernel.
+ * bit).  The routing kernels count their own picks per dispatch tile (the
+ * routes of the tokens one workgroup selects), saving the dispatch's counting
+ * kernel: after the gate kernel, the selection kernel writes each tile's
+ * histogram and adds it into super-tile sums that the gate kernel zeroed, so
+ * the one placement kernel reads about 2 sqrt(tiles) rows of counts; the gate
+ * kernel with the selection fused (whole-row tiles) writes tile histograms
+ * that the placement reads in full (tiles x E <= 32768 counts, E a multiple
+ * of 8).  Other shapes use the dispatch's own kernels.
  *   workspace    256-byte aligned device memory of at least
  *                moe_route_dispatch_workspace_size(p) bytes (the gate
  *                hand-off, then the dispatch's tile data); contents need no
@@ -340,6 +364,9 @@ int32_t moe_route_dispatch_noalloc(const moe_route_params* p, const void* x, con
 #define MOE_PATH_SELECT_HIST 1 /* the select kernel writes the dispatch's tile histograms */
 #define MOE_PATH_FUSED 2       /* the gate kernel runs the selection on its tile's rows */
 #define MOE_PATH_SMALL 3       /* one workgroup selects and performs the whole dispatch */
+#define MOE_PATH_SELECT_SUPER 4 /* the select kernel writes tile histograms and super-tile
+                                   sums (zeroed by the gate kernel): the placement reads
+                                   about 2 sqrt(tiles) rows of counts, not every tile's */
 typedef struct {
   int32_t path;                    /* MOE_PATH_* */
   int32_t gate_bm, gate_bn;        /* gate tile: tokens x experts */

@@ -189,23 +189,39 @@ def test_dispatch_workspace_size_per_path(T, k, E):
         assert n == (2 * nt + 1) * E * 4
 
 
+def super_bytes(T, k, E, tokens):
+    """Tile histograms (16-bit, 256-byte aligned) plus super-tile sums (int32)
+    of the select-written super-tile path: S = ceil(sqrt(tiles))."""
+    tiles = -(-T // tokens)
+    S = 1
+    while S * S < tiles:
+        S += 1
+    return -(-tiles * E * 2 // 256) * 256 + -(-tiles // S) * E * 4
+
+
 def test_route_dispatch_workspace_size():
-    # the gate hand-off (256-byte aligned), then either the selection-written
-    # tile histograms (whole-tile shapes) or the dispatch's own workspace
+    # the gate hand-off (256-byte aligned), then the dispatch's data for the
+    # largest of the paths the call may take (gate or select-only, aligned or
+    # not): the dispatch's own workspace, tile histograms, or tile histograms
+    # plus super-tile sums
     for T, d, E, k in [(4096, 2048, 128, 16), (65536, 2880, 128, 4), (256, 1024, 8, 2),
                        (16384, 7168, 384, 6), (5, 7, 4, 1)]:
         route = tda.route_workspace_size(T, d, E, k)
         route = (route + 255) // 256 * 256
         n = tda.route_dispatch_workspace_size(T, d, E, k)
         disp = tda.dispatch_workspace_size(T, k, E)
-        assert n >= route and (n == route + disp or (n - route) % (2 * E) == 0), (T, n)
+        plan = tda.route_dispatch_plan(T, d, E, k)
+        assert n >= route + (disp if plan["path"] == "separate" else 0), (T, n)
+        if plan["path"] == "select_super":
+            assert n >= route + super_bytes(T, k, E, plan["hist_tokens"]), (T, n)
     # Qwen3-like shape: the gate hand-off holds whole T x E partial arrays
     # (one per K split); then 16-token tiles of 256 routes -> 256 histogram rows
-    # of 128 16-bit counts
+    # of 128 16-bit counts and 16 super rows of 128 int32 sums
     route = tda.route_workspace_size(4096, 2048, 128, 16)
     assert route % (4096 * 128 * 4) == 0 and 1 <= route // (4096 * 128 * 4) <= 8
+    assert tda.route_dispatch_plan(4096, 2048, 128, 16)["hist_tokens"] == 16
     assert tda.route_dispatch_workspace_size(4096, 2048, 128, 16) == \
-        (route + 255) // 256 * 256 + 256 * 128 * 2
+        (route + 255) // 256 * 256 + 256 * 128 * 2 + 16 * 128 * 4
 
 
 def test_route_dispatch_validation():
@@ -240,15 +256,15 @@ def test_plan_constants_match_binding():
 
 WORKLOAD_PLANS = {  # path, kernels per moe_route_dispatch call
     "mixtral": ("small", 2),
-    "qwen3_dynk": ("select_hist", 3),
-    "dsv3_grouped": ("separate", 4),
-    "dsv4": ("separate", 5),
+    "qwen3_dynk": ("select_super", 3),
+    "dsv3_grouped": ("select_super", 3),
+    "dsv4": ("select_super", 3),
     "gptoss_skew": ("fused", 2),
-    "dsv4_bias": ("separate", 5),
-    "olmoe": ("select_hist", 3),
-    "dsv3_groupmax": ("separate", 4),
-    "switch_top1": ("separate", 4),
-    "grouped_quota": ("separate", 4),
+    "dsv4_bias": ("select_super", 3),
+    "olmoe": ("select_super", 3),
+    "dsv3_groupmax": ("select_super", 3),
+    "switch_top1": ("select_super", 3),
+    "grouped_quota": ("select_super", 3),
 }
 
 
@@ -302,12 +318,15 @@ def test_planner_invariants_on_random_shapes():
             assert S == 1 and bn >= E and E <= 128 and dt == 1, plan
         if plan["path"] == "small":
             assert T * k <= 2048 and E <= 128 and plan["kernels"] == 2, plan
-        if plan["hist_tokens"]:
+        if plan["path"] in ("select_hist", "fused") and plan["hist_tokens"]:
             assert plan["hist_tokens"] * k in (256, 512, 1024, 2048), plan
             assert -(-T * k // (plan["hist_tokens"] * k)) * E <= 32 * 1024, plan
+        if plan["path"] == "select_super":
+            assert 1 <= plan["hist_tokens"] * k <= 2048 and plan["gate_stage_bytes"], plan
+            assert plan["kernels"] == 3, plan
         assert plan["select_lanes"] in (4, 8, 16, 64), plan
         assert plan["select_lanes"] * plan["select_experts_per_lane"] >= E, plan
-    assert {"small", "separate", "select_hist", "fused"} <= paths, paths
+    assert {"small", "separate", "select_super", "fused"} <= paths, paths
 
 
 def test_combine_validation():

@@ -2,7 +2,7 @@
 times: moe_route_dispatch (gate, scoring, selection, weights, histogram,
 offsets, permutation, inverse and MaxVio in one call; for the capacity
 workload then moe_dispatch_capacity), and for the hash workload
-moe_route_hash then moe_dispatch.  Nothing is sampled: the oracle (fp64,
+moe_route_hash_dispatch.  Nothing is sampled: the oracle (fp64,
 tokens split over host threads) routes every token and the acceptance rule
 of tests/parity.py is applied to all of them; the dispatch arrays, the
 capacity slots and MaxVio are compared bit for bit.
@@ -101,10 +101,10 @@ def test_hash_every_token():
     say("hash, full size, every token")
     mv = torch.full((1,), -7.0, dtype=torch.float64, device=DEV)
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
-    ids, wts = tda.route_hash(up(inp["token_ids"]), up(inp["tid2eid"]), w.E, x=up(inp["x"]),
-                              W=up(inp["W"]), score=w.score, renormalize=w.renormalize,
-                              route_scale=w.route_scale, dev_err=err)
-    counts, offsets, perm, inv = tda.dispatch(ids, w.E, maxvio=mv)
+    ids, wts, counts, offsets, perm, inv = tda.route_hash_dispatch(
+        up(inp["token_ids"]), up(inp["tid2eid"]), w.E, x=up(inp["x"]), W=up(inp["W"]),
+        score=w.score, renormalize=w.renormalize, route_scale=w.route_scale, maxvio=mv,
+        dev_err=err)
     torch.cuda.synchronize()
     assert int(err.item()) == 0
     gids, gw = down(ids), down(wts)

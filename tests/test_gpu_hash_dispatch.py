@@ -148,3 +148,49 @@ def test_dispatch_without_inv_and_determinism():
     c = tda.dispatch(ids, 384)
     for u, v in zip(b, c):
         assert torch.equal(u, v)
+
+
+@pytest.mark.parametrize("T,d,E,k,V,bad", [
+    (16384, 7168, 384, 6, 129280, False),  # the DeepSeek-V4-like hash layer, full size
+    (1000, 256, 384, 6, 5000, True),       # bad token ids and table entries
+    (777, 64, 8, 1, 50, True),             # k = 1 (4-lane segments)
+    (3001, 128, 100, 9, 700, False),       # 16-lane segments, E not a multiple of 8
+    (513, 64, 1000, 17, 300, True),        # one token per wavefront, 10-bit ids
+    (200, 32, 64, 32, 90, False),          # k = 32, duplicates in the table
+])
+def test_hash_dispatch_matches_separate_calls(T, d, E, k, V, bad):
+    """moe_route_hash_dispatch (the hash kernel counting the dispatch tiles)
+    equals moe_route_hash + moe_dispatch bit for bit, error counts included,
+    and the oracle's ids and dispatch."""
+    rng = np.random.default_rng([T, E, k])
+    if k <= E and not (E == 64 and k == 32):
+        tab = np.argsort(rng.random((V, E)), axis=1)[:, :k].astype(np.int32)
+    else:
+        tab = rng.integers(0, E, size=(V, k)).astype(np.int32)  # duplicates allowed
+    tok = rng.integers(0, V, size=T).astype(np.int32)
+    if bad:
+        tok[rng.choice(T, 5, replace=False)] = rng.choice([-1, V, V + 3], 5)
+        tab[rng.choice(V, 7, replace=False), rng.integers(0, k, 7)] = rng.choice([-2, E, E + 9], 7)
+    x = wl.f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+    W = wl.f32_to_bf16_bits((rng.standard_normal((E, d)) / np.sqrt(d)).astype(np.float32))
+    say("hash dispatch", T, d, E, k, V, bad)
+    e1 = torch.zeros(1, dtype=torch.int32, device=DEV)
+    e2 = torch.zeros(1, dtype=torch.int32, device=DEV)
+    m1 = torch.zeros(1, dtype=torch.float64, device=DEV)
+    m2 = torch.zeros(1, dtype=torch.float64, device=DEV)
+    a = tda.route_hash_dispatch(up(tok), up(tab), E, x=up(x), W=up(W), maxvio=m1, dev_err=e1)
+    ids, wts = tda.route_hash(up(tok), up(tab), E, x=up(x), W=up(W), dev_err=e2)
+    b = (ids, wts) + tuple(tda.dispatch(ids, E, maxvio=m2))
+    torch.cuda.synchronize()
+    n = int(a[3][-1].item())
+    for name, u, v in zip(("ids", "weights", "counts", "offsets", "perm", "inv"), a, b):
+        if name == "perm":
+            u, v = u[:n], v[:n]
+        assert torch.equal(u, v), name
+    assert int(e1.item()) == int(e2.item()) and torch.equal(m1, m2)
+    ref_ids, nerr = oracle.hash_ids(tok, tab, E)
+    assert nerr == int(e1.item())
+    np.testing.assert_array_equal(down(a[0]), ref_ids)
+    d_ref = oracle.dispatch(ref_ids, E)
+    check_dispatch(tuple(a[2:]), d_ref)
+    assert float(m1.item()) == oracle.maxvio(d_ref["counts"])

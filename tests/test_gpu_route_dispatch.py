@@ -248,12 +248,16 @@ def test_quota_random_shapes_every_path(seed):
 
 
 @pytest.mark.parametrize("path,T,d,E,k,G,kpg", [("fused", 32768, 512, 128, 4, 8, 1),
-                                                 ("select_hist", 700, 2048, 128, 16, 16, 2)])
-def test_quota_fused_paths(path, T, d, E, k, G, kpg):
+                                                 ("select_hist", 700, 2048, 128, 16, 16, 2),
+                                                 ("select_super", 700, 2048, 128, 16, 16, 2)])
+def test_quota_fused_paths(path, T, d, E, k, G, kpg, monkeypatch):
     """The gate kernel with the selection in its epilogue (whole-row 128 x 128
-    tiles), and the select kernel writing the dispatch's tile histograms, under
-    a per-group quota: equal to separate moe_route + moe_dispatch calls bit for
-    bit, and to the oracle on sampled tokens."""
+    tiles), and the select kernel writing the dispatch's tile histograms (read
+    in full by the placement, or with super-tile sums), under a per-group
+    quota: equal to separate moe_route + moe_dispatch calls bit for bit, and
+    to the oracle on sampled tokens."""
+    if path == "select_hist":
+        monkeypatch.setenv("MOE_DISPATCH_NO_SUPER", "1")
     plan = tda.route_dispatch_plan(T, d, E, k, 1, score="sigmoid", n_groups=G, topk_groups=G,
                                    k_per_group=kpg)
     assert plan["path"] == path, plan
@@ -271,3 +275,63 @@ def test_quota_fused_paths(path, T, d, E, k, G, kpg):
                        select_bias=sb, n_groups=G, k_per_group=kpg)
     check_route(down(fused[0])[pick], down(fused[1])[pick], ref, oracle, score="sigmoid",
                 n_groups=G, k_per_group=kpg, where=f"quota {path}")
+
+
+@pytest.mark.parametrize("T,d,E,k,dyn", [
+    (5000, 256, 384, 6, False),    # 16-token tiles of 96 routes (not whole chunks), 313 tiles
+    (777, 128, 1000, 5, True),     # one-token wavefronts, 16-wave tiles of 80 routes, 10-bit ids
+    (3001, 64, 100, 7, True),      # E not a multiple of 8, ragged last tile
+    (20000, 64, 64, 32, False),    # 2048-route tiles (two chunks per wave)
+    (1, 64, 256, 8, False),        # a single tile
+    (16384, 512, 384, 6, True),    # DeepSeek-V4-like tile shape with empty slots
+])
+def test_super_tile_dispatch(T, d, E, k, dyn, monkeypatch):
+    """The select-written tile histograms plus super-tile sums (zeroed by the
+    gate kernel) against the same call with that path switched off and
+    against the oracle's dispatch of the GPU's ids, bit for bit."""
+    rng = np.random.default_rng([T, E, k])
+    x = wl.f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+    W = wl.f32_to_bf16_bits((rng.standard_normal((E, d)) / np.sqrt(d)).astype(np.float32))
+    kpt = rng.integers(1, k + 1, size=T).astype(np.int32) if dyn else None
+    plan = tda.route_dispatch_plan(T, d, E, k, 1, score="sigmoid")
+    say("super-tile dispatch", T, d, E, k, dyn, plan["path"], plan["hist_tokens"])
+    assert plan["path"] == "select_super", plan
+    kw = dict(score="sigmoid", k_per_token=up(kpt))
+    outs = []
+    for off in (False, True):
+        if off:
+            monkeypatch.setenv("MOE_DISPATCH_NO_SUPER", "1")
+        mv = torch.zeros(1, dtype=torch.float64, device=DEV)
+        r = tda.route_dispatch(up(x), up(W), k, maxvio=mv, **kw)
+        torch.cuda.synchronize()
+        outs.append((r, mv))
+    monkeypatch.delenv("MOE_DISPATCH_NO_SUPER", raising=False)
+    (a, mva), (b, mvb) = outs
+    assert_same(a, b)
+    assert torch.equal(mva, mvb)
+    d_ref = oracle.dispatch(down(a[0]), E)
+    check_dispatch(tuple(a[2:]), d_ref)
+    assert float(mva.item()) == oracle.maxvio(d_ref["counts"])
+
+
+@pytest.mark.parametrize("name,T", [("qwen3_dynk", None), ("qwen3_dynk", 4091), ("olmoe", 1000)])
+def test_all_counts_placement_after_the_gate(name, T, monkeypatch):
+    """With the super-tile sums switched off the select kernel's tile
+    histograms go to the placement that reads every tile's counts: equal to
+    separate calls and to the super-tile path, bit for bit."""
+    w = wl.WORKLOADS[name]
+    inp = wl.make_inputs(w, T=T)
+    kw = route_kwargs(w)
+    if kw["group_score"] is None:
+        kw.pop("group_score")
+    kw.update(logit_bias=up(inp["logit_bias"]), select_bias=up(inp["select_bias"]),
+              k_per_token=up(inp["k_per_token"]))
+    say("all-counts placement", name, inp["x"].shape[0])
+    sup = tda.route_dispatch(up(inp["x"]), up(inp["W"]), w.k, **kw)
+    monkeypatch.setenv("MOE_DISPATCH_NO_SUPER", "1")
+    plan = tda.route_dispatch_plan(inp["x"].shape[0], w.d, w.E, w.k, 1,
+                                   **{k2: v for k2, v in route_kwargs(w).items() if v is not None})
+    assert plan["path"] == "select_hist", plan
+    fused, sep, e1, e2 = both(up(inp["x"]), up(inp["W"]), w.k, w.E, **kw)
+    assert_same(fused, sep)
+    assert_same(fused, tuple(sup))

@@ -30,12 +30,13 @@ EXPORTS = ("moe_route", "moe_route_workspace_size", "moe_route_hash",
            "moe_route_hash_workspace_size",
            "moe_dispatch_workspace_size", "moe_dispatch",
            "moe_route_dispatch", "moe_route_dispatch_workspace_size",
-           "moe_route_dispatch_noalloc",
+           "moe_route_dispatch_noalloc", "moe_route_hash_dispatch",
+           "moe_route_hash_dispatch_workspace_size",
            "moe_route_dispatch_plan", "moe_combine", "moe_dispatch_capacity",
            "moe_permute_rows", "moe_ep_layout",
            "moe_profile_enable", "moe_profile_read",
            "moe_last_error", "moe_abi_version")
-PATHS = ("separate", "select_hist", "fused", "small")
+PATHS = ("separate", "select_hist", "fused", "small", "select_super")
 PLAN_FIELDS = ("path", "gate_bm", "gate_bn", "gate_waves", "gate_splits", "gate_stage_bytes",
                "gate_ring_depth", "gate_lds_bytes", "select_lanes", "select_experts_per_lane",
                "hist_tokens", "kernels")
@@ -79,6 +80,11 @@ def lib() -> ctypes.CDLL:
         L.moe_route_hash.restype = i32
         L.moe_route_hash_workspace_size.argtypes = [P]
         L.moe_route_hash_workspace_size.restype = ctypes.c_size_t
+        L.moe_route_hash_dispatch.argtypes = [P, vp, vp, i32] + [vp] * 11 + [ctypes.c_size_t,
+                                                                           vp, vp]
+        L.moe_route_hash_dispatch.restype = i32
+        L.moe_route_hash_dispatch_workspace_size.argtypes = [P]
+        L.moe_route_hash_dispatch_workspace_size.restype = ctypes.c_size_t
         L.moe_dispatch_workspace_size.argtypes = [i32, i32, i32]
         L.moe_dispatch_workspace_size.restype = ctypes.c_size_t
         L.moe_dispatch.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
@@ -414,6 +420,57 @@ def route_hash(token_ids: torch.Tensor, tid2eid: torch.Tensor, E: int, *, x=None
                                 _p(W), _p(logit_bias), _p(ids), _p(weights), _p(ws), ws_bytes,
                                 _p(dev_err), _stream(device)))
     return ids, weights
+
+
+def route_hash_dispatch(token_ids: torch.Tensor, tid2eid: torch.Tensor, E: int, *,
+                        x: torch.Tensor, W: torch.Tensor, score: str = "sqrt_softplus",
+                        logit_bias=None, renormalize: bool = True, route_scale: float = 1.0,
+                        ids=None, weights=None, counts=None, offsets=None, perm=None, inv=None,
+                        with_inv: bool = True, maxvio=None, workspace=None, dev_err=None):
+    """route_hash() then dispatch() of its ids in one library call (the hash
+    kernel also counts the dispatch tiles).  Returns (ids, weights, counts,
+    offsets, perm, inv); ``workspace`` is allocated when not given."""
+    _dev(token_ids, "token_ids", torch.int32)
+    _dev(tid2eid, "tid2eid", torch.int32)
+    T = token_ids.shape[0]
+    vocab, k = tid2eid.shape
+    device = token_ids.device
+    _dev(x, "x")
+    _dev(W, "W", x.dtype, (E, x.shape[1]))
+    if x.shape[0] != T:
+        raise ValueError("x must have one row per token id")
+    d, dt = x.shape[1], _dtype_code(x)
+    if logit_bias is not None:
+        _dev(logit_bias, "logit_bias", torch.float32, (E,))
+    R = T * k
+    i32 = torch.int32
+    ids = torch.empty((T, k), dtype=i32, device=device) if ids is None else ids
+    weights = torch.empty((T, k), dtype=torch.float32, device=device) if weights is None else weights
+    counts = torch.empty(E, dtype=i32, device=device) if counts is None else counts
+    offsets = torch.empty(E + 1, dtype=i32, device=device) if offsets is None else offsets
+    perm = torch.empty(R, dtype=i32, device=device) if perm is None else perm
+    if inv is None and with_inv:
+        inv = torch.empty(R, dtype=i32, device=device)
+    _dev(ids, "ids", i32, (T, k))
+    _dev(weights, "weights", torch.float32, (T, k))
+    if maxvio is not None:
+        _dev(maxvio, "maxvio", torch.float64, (1,))
+    p = make_params(T, d, E, k, dt, score, 1, 1, "max", renormalize, route_scale)
+    if workspace is None:
+        nbytes = int(lib().moe_route_hash_dispatch_workspace_size(ctypes.byref(p)))
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().moe_route_hash_dispatch(ctypes.byref(p), _p(token_ids), _p(tid2eid), vocab,
+                                         _p(x), _p(W), _p(logit_bias), _p(ids), _p(weights),
+                                         _p(counts), _p(offsets), _p(perm), _p(inv), _p(maxvio),
+                                         _p(workspace), ws_bytes, _p(dev_err), _stream(device)))
+    return ids, weights, counts, offsets, perm, inv
+
+
+def route_hash_dispatch_workspace_size(T, d, E, k, dtype=1, **kw) -> int:
+    """Device bytes moe_route_hash_dispatch needs for these shapes."""
+    p = make_params(T, d, E, k, dtype, **kw)
+    return int(lib().moe_route_hash_dispatch_workspace_size(ctypes.byref(p)))
 
 
 def route_hash_workspace_size(T, d, E, k, dtype=1, **kw) -> int:

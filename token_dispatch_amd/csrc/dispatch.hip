@@ -547,6 +547,181 @@ __global__ __launch_bounds__(kThreads) void disp_capacity_kernel(
   }
 }
 
+// Placement from tile histograms plus super-tile sums ("reduce, then
+// scan").  The routing kernel that selected tile t's routes wrote the tile's
+// 16-bit histogram hist[t][E] and added it into super_sum[t / S][E] (int32
+// integer atomics, order-independent; the array was zeroed by the gate kernel
+// earlier in the same call).  Workgroup t therefore reads the ns = ceil(nt / S)
+// super rows -- every expert's total, and its count in super tiles before
+// tile t's -- and the at most S - 1 tile rows before it inside its own super
+// tile: (ns + S) * E counts instead of the nt * E the all-counts kernel reads.
+// Tiles hold TR routes (any number up to 64 * kPlaceWaves * CPW); one chunk
+// of 64 routes per wave and chunk slot, 16 waves.  J threads per expert
+// (adjacent lanes) split its rows and add their sums with DPP.
+constexpr int kPlaceWaves = 16;
+
+template <int CPW, int NB>
+__global__ __launch_bounds__(kPlaceWaves * kWave) void disp_place_super_kernel(
+    const int32_t* __restrict__ ids, int64_t R, int E, int nt, int TR, int S,
+    const hist_t* __restrict__ tile_hist, const int32_t* __restrict__ super_sum,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+    int32_t* __restrict__ inv, double* __restrict__ maxvio) {
+  constexpr int NT = kPlaceWaves * kWave;
+  static_assert(NT >= kMaxE / 4, "offsets scan: 4 experts per thread");
+  __shared__ int32_t wh[kPlaceWaves][kMaxE];
+  __shared__ int32_t tot[kMaxE];
+  __shared__ int32_t off[kMaxE];
+  __shared__ int32_t wsum[kPlaceWaves];
+  __shared__ int32_t wmax[kPlaceWaves];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tile = blockIdx.x;
+  const int64_t tbase = (int64_t)tile * TR;
+
+  // this wave's chunks of the tile: slot c = wave * CPW + ch covers routes
+  // tbase + c * 64 + lane while c * 64 + lane < TR (loads issued first)
+  int ev[CPW];
+#pragma unroll
+  for (int ch = 0; ch < CPW; ++ch) {
+    const int c = wave * CPW + ch;
+    const int64_t r = tbase + c * kWave + lane;
+    const bool mine = c * kWave + lane < TR && r < R;
+    ev[ch] = ids[mine ? r : 0];
+    if (!mine) ev[ch] = -1;
+  }
+
+  // every expert's total and its count before this tile: J threads per
+  // expert (adjacent lanes) split its super rows and tile rows, loads issued
+  // in batches, sums added with DPP
+  int J = 1;
+  while (J < 16 && 2 * J * E <= NT) J *= 2;
+  const int e_of = tid / J, j = tid % J;
+  const int st = tile / S, ns = (nt + S - 1) / S;
+  int a = 0, b = 0;
+  if (e_of < E) {
+    constexpr int B = 8;  // loads in flight per thread
+    for (int s0 = j; s0 < ns; s0 += B * J) {
+      int v[B];
+#pragma unroll
+      for (int i = 0; i < B; ++i) {
+        const int sr = s0 + i * J;
+        v[i] = sr < ns ? super_sum[(int64_t)sr * E + e_of] : 0;
+      }
+#pragma unroll
+      for (int i = 0; i < B; ++i) {
+        a += v[i];
+        b += s0 + i * J < st ? v[i] : 0;
+      }
+    }
+    for (int u0 = st * S + j; u0 < tile; u0 += B * J) {
+      int v[B];
+#pragma unroll
+      for (int i = 0; i < B; ++i) {
+        const int u = u0 + i * J;
+        v[i] = u < tile ? (int)tile_hist[(int64_t)u * E + e_of] : 0;
+      }
+#pragma unroll
+      for (int i = 0; i < B; ++i) b += v[i];
+    }
+  }
+  a = group_sum_i32(a, J);
+  b = group_sum_i32(b, J);
+  if (e_of < E && j == 0) {
+    tot[e_of] = a;
+    off[e_of] = b;
+  }
+#pragma unroll
+  for (int ch = 0; ch < CPW; ++ch)
+    if (ev[ch] >= E) ev[ch] = -1;  // (routing kernels write ids below E or -1)
+  __syncthreads();
+
+  // offsets: exclusive scan of the totals over experts (4 experts per thread)
+  int t4[4], s = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid * 4 + i;
+    t4[i] = e < E ? tot[e] : 0;
+    s += t4[i];
+  }
+  const int inc = wave_incl_scan_i32(s);
+  if (lane == 63) wsum[wave] = inc;
+  if (blockIdx.x == 0 && maxvio) {
+    const uint32_t mx = wave_max_u32((uint32_t)max(max(t4[0], t4[1]), max(t4[2], t4[3])));
+    if (lane == 0) wmax[wave] = (int32_t)mx;
+  }
+  for (int e = lane; e < E; e += kWave) wh[wave][e] = 0;
+  __syncthreads();
+  if (blockIdx.x == 0 && maxvio && tid == 0) {
+    // MaxVio = max_e count_e / (R / E) - 1 ("I modelli MoE open hanno router
+    // opposti", loss-free balancing paragraph), 0 without routes
+    int64_t R_all = 0;
+    int32_t mx = 0;
+#pragma unroll
+    for (int w = 0; w < kPlaceWaves; ++w) {
+      R_all += wsum[w];
+      mx = max(mx, wmax[w]);
+    }
+    *maxvio = R_all > 0 ? (double)mx / ((double)R_all / (double)E) - 1.0 : 0.0;
+  }
+  int base = inc - s;
+#pragma unroll
+  for (int w = 0; w < kPlaceWaves; ++w) base += w < wave ? wsum[w] : 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid * 4 + i;
+    if (e < E) {
+      off[e] = base + off[e];  // only this thread touches entry e here
+      if (blockIdx.x == 0) {
+        counts[e] = t4[i];
+        offsets[e] = base;
+      }
+    }
+    base += t4[i];
+  }
+  if (blockIdx.x == 0 && tid == NT - 1) offsets[E] = base;
+
+  // count this wave's chunks into its row, keeping each route's offset in
+  // the wave (the expert's count in earlier chunks plus the peers below it)
+  int32_t* row = wh[wave];
+  int in_wave[CPW];
+  {
+    const uint64_t below = lanemask_lt();
+#pragma unroll
+    for (int ch = 0; ch < CPW; ++ch) {
+      const int e = ev[ch];
+      const uint64_t p = peer_mask<NB>(e);
+      in_wave[ch] = 0;
+      if (e >= 0) {
+        const int start = row[e];
+        in_wave[ch] = start + __popcll(p & below);
+        if ((p & below) == 0) row[e] = start + __popcll(p);
+      }
+    }
+  }
+  __syncthreads();
+  // per-wave starting positions of each expert inside this tile
+  for (int e = tid; e < E; e += NT) {
+    int bb = off[e];
+#pragma unroll
+    for (int w = 0; w < kPlaceWaves; ++w) {
+      const int c = wh[w][e];
+      wh[w][e] = bb;
+      bb += c;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int ch = 0; ch < CPW; ++ch) {
+    const int c = wave * CPW + ch;
+    const int64_t r = tbase + c * kWave + lane;
+    const int e = ev[ch];
+    if (c * kWave + lane < TR && r < R) {
+      const int pos = e >= 0 ? row[e] + in_wave[ch] : -1;
+      if (inv) inv[r] = pos;
+      if (pos >= 0 && pos < R) perm[pos] = (int32_t)r;
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_capacity(const int32_t* ids, int64_t R, int32_t E, int32_t C,
@@ -572,6 +747,41 @@ hipError_t launch_dispatch_from_hist(const int32_t* ids, int64_t R, int32_t E,
   const int nt = (int)((R + tile_routes - 1) / tile_routes);
   return launch_placement(tile_routes, ids, R, E, nt, tile_hist, counts, offsets,
                           perm, inv, maxvio, stream);
+}
+
+bool dispatch_super_ok(int64_t R, int32_t E, int32_t tile_routes) {
+  return R > 0 && R <= 2147483647 && E >= 1 && E <= kMaxE && tile_routes >= 1 &&
+         tile_routes <= 2 * kPlaceWaves * kWave;
+}
+
+int dispatch_super_size(int64_t R, int32_t tile_routes) {
+  const int64_t nt = (R + tile_routes - 1) / tile_routes;
+  int S = 1;
+  while ((int64_t)S * S < nt) ++S;  // about sqrt(nt): ns + S rows per workgroup
+  return S;
+}
+
+hipError_t launch_dispatch_from_super(const int32_t* ids, int64_t R, int32_t E,
+                                      int32_t* counts, int32_t* offsets, int32_t* perm,
+                                      int32_t* inv, double* maxvio, const hist_t* tile_hist,
+                                      const int32_t* super_sum, int32_t tile_routes,
+                                      hipStream_t stream) {
+  if (!dispatch_super_ok(R, E, tile_routes)) return hipErrorInvalidValue;
+  const int nt = (int)((R + tile_routes - 1) / tile_routes);
+  const int S = dispatch_super_size(R, tile_routes);
+  auto go = [&](auto kernel) {
+    return launch(kStageDispScatter, kernel, dim3(nt), dim3(kPlaceWaves * kWave), stream, ids,
+                  R, E, nt, (int)tile_routes, S, tile_hist, super_sum, counts, offsets, perm,
+                  inv, maxvio);
+  };
+  const bool two = tile_routes > kPlaceWaves * kWave;
+  switch (id_bits(E)) {
+    case 7: return two ? go(disp_place_super_kernel<2, 7>) : go(disp_place_super_kernel<1, 7>);
+    case 8: return two ? go(disp_place_super_kernel<2, 8>) : go(disp_place_super_kernel<1, 8>);
+    default:
+      return two ? go(disp_place_super_kernel<2, kIdBits>)
+                 : go(disp_place_super_kernel<1, kIdBits>);
+  }
 }
 
 int dispatch_kernels(int64_t R, int32_t E) {

@@ -360,6 +360,12 @@ __global__ __launch_bounds__(WM * WN * kWave) void gate_gemm_pipe_kernel(
 
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * STAGE];
 
+  if (sa.zero_words > 0) {  // a slice of the array the next kernel adds into
+    const int per = (sa.zero_words + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int beg = (int)blockIdx.x * per, end = min(beg + per, sa.zero_words);
+    for (int i = beg + (int)threadIdx.x; i < end; i += WM * WN * kWave) sa.zero[i] = 0;
+  }
+
   // Tile order: tile ids run N tile fastest, then M tile, then K split, and
   // consecutive ids go to one XCD, so the N tiles of one (M tile, split) --
   // which read the same x rows -- share that XCD's L2.
@@ -684,35 +690,35 @@ constexpr bool depth_ok(int bm, int bn, int ns, int rb, int waves = 4) {
 
 template <typename In, int BM, int BN, int NS, int RB, int WM, int WN>
 hipError_t launch_depth(const void* x, const void* W, const float* lb, float* out, int T,
-                        int d, int E, int splits, hipStream_t s) {
+                        int d, int E, int splits, hipStream_t s, const SelectArgs& sa) {
   if constexpr (depth_ok(BM, BN, NS, RB, WM * WN))
-    return launch_pipe<In, BM, BN, NS, RB, WM, WN>(x, W, lb, out, T, d, E, splits, s);
+    return launch_pipe<In, BM, BN, NS, RB, WM, WN>(x, W, lb, out, T, d, E, splits, s, sa);
   return hipErrorInvalidValue;
 }
 
 // Ring depths 2..4; 64-byte stages (the deep rings of large tiles) also 5..8.
 template <typename In, int BM, int BN, int RB, int WM, int WN>
 hipError_t launch_rb(const GatePlan& g, const void* x, const void* W, const float* lb,
-                     float* out, int T, int d, int E, hipStream_t s) {
+                     float* out, int T, int d, int E, hipStream_t s, const SelectArgs& sa) {
   if constexpr (RB == 64) {
     switch (g.ns) {
-      case 8: return launch_depth<In, BM, BN, 8, RB, WM, WN>(x, W, lb, out, T, d, E, g.splits, s);
-      case 7: return launch_depth<In, BM, BN, 7, RB, WM, WN>(x, W, lb, out, T, d, E, g.splits, s);
-      case 6: return launch_depth<In, BM, BN, 6, RB, WM, WN>(x, W, lb, out, T, d, E, g.splits, s);
-      case 5: return launch_depth<In, BM, BN, 5, RB, WM, WN>(x, W, lb, out, T, d, E, g.splits, s);
+      case 8: return launch_depth<In, BM, BN, 8, RB, WM, WN>(x, W, lb, out, T, d, E, g.splits, s, sa);
+      case 7: return launch_depth<In, BM, BN, 7, RB, WM, WN>(x, W, lb, out, T, d, E, g.splits, s, sa);
+      case 6: return launch_depth<In, BM, BN, 6, RB, WM, WN>(x, W, lb, out, T, d, E, g.splits, s, sa);
+      case 5: return launch_depth<In, BM, BN, 5, RB, WM, WN>(x, W, lb, out, T, d, E, g.splits, s, sa);
       default: break;
     }
   }
   switch (g.ns) {
-    case 4: return launch_depth<In, BM, BN, 4, RB, WM, WN>(x, W, lb, out, T, d, E, g.splits, s);
-    case 3: return launch_depth<In, BM, BN, 3, RB, WM, WN>(x, W, lb, out, T, d, E, g.splits, s);
-    default: return launch_depth<In, BM, BN, 2, RB, WM, WN>(x, W, lb, out, T, d, E, g.splits, s);
+    case 4: return launch_depth<In, BM, BN, 4, RB, WM, WN>(x, W, lb, out, T, d, E, g.splits, s, sa);
+    case 3: return launch_depth<In, BM, BN, 3, RB, WM, WN>(x, W, lb, out, T, d, E, g.splits, s, sa);
+    default: return launch_depth<In, BM, BN, 2, RB, WM, WN>(x, W, lb, out, T, d, E, g.splits, s, sa);
   }
 }
 
 template <typename In, int BM, int BN, int KB, int WM = 2, int WN = 2>
 hipError_t launch_ns(const GatePlan& g, const void* x, const void* W, const float* lb,
-                     float* out, int T, int d, int E, hipStream_t s) {
+                     float* out, int T, int d, int E, hipStream_t s, const SelectArgs& sa) {
   if (!g.pipe) {
     if constexpr (WM == 2 && WN == 2) return launch_tile<In, BM, BN, KB>(x, W, lb, out, T, d, E, s);
     return hipErrorInvalidValue;  // 8-wave tiles are planned for the pipelined kernel only
@@ -721,26 +727,26 @@ hipError_t launch_ns(const GatePlan& g, const void* x, const void* W, const floa
     return hipErrorInvalidValue;  // 8-wave tiles: bf16 only
   } else {
     switch (g.rb) {
-      case 512: return launch_rb<In, BM, BN, 512, WM, WN>(g, x, W, lb, out, T, d, E, s);
-      case 256: return launch_rb<In, BM, BN, 256, WM, WN>(g, x, W, lb, out, T, d, E, s);
+      case 512: return launch_rb<In, BM, BN, 512, WM, WN>(g, x, W, lb, out, T, d, E, s, sa);
+      case 256: return launch_rb<In, BM, BN, 256, WM, WN>(g, x, W, lb, out, T, d, E, s, sa);
       case 64:
         if constexpr (WM * WN == 8)
-          return launch_rb<In, BM, BN, 64, WM, WN>(g, x, W, lb, out, T, d, E, s);
+          return launch_rb<In, BM, BN, 64, WM, WN>(g, x, W, lb, out, T, d, E, s, sa);
         return hipErrorInvalidValue;  // 64-byte stages: 8-wave tiles only
-      default: return launch_rb<In, BM, BN, 128, WM, WN>(g, x, W, lb, out, T, d, E, s);
+      default: return launch_rb<In, BM, BN, 128, WM, WN>(g, x, W, lb, out, T, d, E, s, sa);
     }
   }
 }
 
 template <typename In>
 hipError_t launch_choice(const GatePlan& g, const void* x, const void* W, const float* lb,
-                         float* out, int T, int d, int E, hipStream_t s) {
+                         float* out, int T, int d, int E, hipStream_t s, const SelectArgs& sa) {
 #define MOE_TILE(BM_, BN_, KB_)                                             \
   if (g.bm == BM_ && g.bn == BN_ && g.wm * g.wn == 4)                        \
-    return launch_ns<In, BM_, BN_, KB_>(g, x, W, lb, out, T, d, E, s);
+    return launch_ns<In, BM_, BN_, KB_>(g, x, W, lb, out, T, d, E, s, sa);
 #define MOE_TILE8(BM_, BN_, WM_, WN_)                                       \
   if (g.bm == BM_ && g.bn == BN_ && g.wm == WM_ && g.wn == WN_)              \
-    return launch_ns<In, BM_, BN_, 128, WM_, WN_>(g, x, W, lb, out, T, d, E, s);
+    return launch_ns<In, BM_, BN_, 128, WM_, WN_>(g, x, W, lb, out, T, d, E, s, sa);
   MOE_TILE(256, 128, 128)
   MOE_TILE(128, 256, 128)
   MOE_TILE(128, 192, 128)
@@ -1055,10 +1061,14 @@ hipError_t launch_gate_select(const GatePlan& g, int32_t dtype, const void* x, c
 
 hipError_t launch_gate_gemm(const GatePlan& g, int32_t dtype, const void* x, const void* W,
                             const float* logit_bias, float* out, int32_t T, int32_t d,
-                            int32_t E, hipStream_t stream) {
+                            int32_t E, hipStream_t stream, int32_t* zero, int32_t zero_words) {
   if (T == 0) return hipSuccess;
-  if (dtype == 1) return launch_choice<uint16_t>(g, x, W, logit_bias, out, T, d, E, stream);
-  return launch_choice<float>(g, x, W, logit_bias, out, T, d, E, stream);
+  if (zero_words > 0 && !g.pipe) return hipErrorInvalidValue;  // the pipelined kernel zeroes
+  SelectArgs sa{};
+  sa.zero = zero;
+  sa.zero_words = zero_words;
+  if (dtype == 1) return launch_choice<uint16_t>(g, x, W, logit_bias, out, T, d, E, stream, sa);
+  return launch_choice<float>(g, x, W, logit_bias, out, T, d, E, stream, sa);
 }
 
 }  // namespace moe

@@ -67,10 +67,12 @@ GatePlan plan_gate(int32_t T, int32_t d, int32_t E, int32_t dtype, bool aligned,
                    bool allow_split);
 
 // out[s][T][E] (s < g.splits) = partial x[T][d] . W[E][d]^T over the s-th K
-// range (+ logit_bias in s = 0); dtype MOE_F32 / MOE_BF16.
+// range (+ logit_bias in s = 0); dtype MOE_F32 / MOE_BF16.  zero (only with
+// g.pipe): zero_words int32 set to 0 by the same kernel.
 hipError_t launch_gate_gemm(const GatePlan& g, int32_t dtype, const void* x, const void* W,
                             const float* logit_bias, float* out, int32_t T, int32_t d,
-                            int32_t E, hipStream_t stream);
+                            int32_t E, hipStream_t stream, int32_t* zero = nullptr,
+                            int32_t zero_words = 0);
 
 // Count of one expert in one dispatch tile of the tile-major histograms
 // that the routing kernels write for the placement kernel: at most the
@@ -92,6 +94,11 @@ struct SelectArgs {
   hist_t* hist;
   int32_t write_logits;
   int32_t vec;
+  // any gate kernel of the pipelined form: zero[0 .. zero_words) is set to
+  // 0, each workgroup a slice (the super-tile sums the selection kernel that
+  // follows adds into)
+  int32_t* zero = nullptr;
+  int32_t zero_words = 0;
 };
 
 // Tokens per tile (BM) when the gate kernel of plan g can run the selection
@@ -110,15 +117,19 @@ void select_shape(const RouteCfg& c, int* lpt, int* vpl);
 // Score + (grouped) top-k + weights.  The logits are the sum of `splits`
 // fp32 partial arrays `split_stride` floats apart (summed in order); when
 // logits_out is not NULL the summed logits are written there.  With `hist`
-// (only when select_hist_tokens(c) > 0) the kernel also writes
-// hist[b][e] = picks of expert e among tokens [b*n, (b+1)*n), n =
-// select_hist_tokens(c): the per-tile histograms of a dispatch whose tiles
-// hold n*k routes.
+// the kernel also writes hist[b][e] = picks of expert e among tokens
+// [b*n, (b+1)*n): the per-tile histograms of a dispatch whose tiles hold n*k
+// routes, n = select_hist_tokens(c) (super_sum NULL: for the all-counts
+// placement) or n = select_super_tokens(c) (super_sum [ceil(tiles / S)][E]
+// int32, zeroed beforehand: each tile's counts are also added into row
+// b / S, S = dispatch_super_size(T*k, n*k)).
 hipError_t launch_select(const RouteCfg& c, const float* logits, int32_t splits,
                          int64_t split_stride, float* logits_out, const float* logit_bias,
                          const float* select_bias, const int32_t* k_per_token, int32_t* ids,
-                         float* weights, int32_t* dev_err, hist_t* hist, hipStream_t stream);
-int select_hist_tokens(const RouteCfg& c);  // 0: no histogram option
+                         float* weights, int32_t* dev_err, hist_t* hist, int32_t* super_sum,
+                         hipStream_t stream);
+int select_hist_tokens(const RouteCfg& c);   // 0: no all-counts histogram option
+int select_super_tokens(const RouteCfg& c);  // 0: no super-tile histogram option
 
 // Selection and the whole dispatch of a small batch in one workgroup (when
 // small_dispatch_ok(c)): the select kernel's outputs plus moe_dispatch's
@@ -143,6 +154,18 @@ hipError_t launch_hash_route(const RouteCfg& c, int32_t dtype,
                              int64_t split_stride, int32_t* ids, float* weights,
                              int32_t* dev_err, hipStream_t stream);
 
+// Hash routing with several tokens per wavefront, weights from the gate's
+// logits (the sum of `splits` arrays [T][E], split_stride floats apart).
+// With hist (super_sum zeroed beforehand): each workgroup's
+// hash_tile_tokens(k) tokens are one dispatch tile; the kernel writes the
+// tile's histogram and adds it into super_sum (as launch_select does).
+int hash_tile_tokens(int32_t k);
+hipError_t launch_hash_tiles(const RouteCfg& c, const int32_t* token_ids,
+                             const int32_t* tid2eid, int32_t vocab, const float* logits,
+                             int32_t splits, int64_t split_stride, int32_t* ids, float* weights,
+                             int32_t* dev_err, hist_t* hist, int32_t* super_sum,
+                             hipStream_t stream);
+
 // Dispatch placement from per-tile histograms already in tile_hist
 // ([ceil(R / tile_routes)][E] hist_t, tile-major), when dispatch_hist_ok
 // (E % 8 == 0: 16-byte rows).
@@ -151,6 +174,18 @@ hipError_t launch_dispatch_from_hist(const int32_t* ids, int64_t R, int32_t E,
                                      int32_t* counts, int32_t* offsets, int32_t* perm,
                                      int32_t* inv, double* maxvio, const hist_t* tile_hist,
                                      int32_t tile_routes, hipStream_t stream);
+
+// Dispatch placement from tile histograms plus super-tile sums: the routing
+// kernel of tile t (tile_routes routes each) wrote hist[t][E] and added it
+// into super_sum[t / S][E], S = dispatch_super_size(R, tile_routes), the
+// super sums zeroed beforehand (by the gate kernel of the same call).
+bool dispatch_super_ok(int64_t R, int32_t E, int32_t tile_routes);
+int dispatch_super_size(int64_t R, int32_t tile_routes);
+hipError_t launch_dispatch_from_super(const int32_t* ids, int64_t R, int32_t E,
+                                      int32_t* counts, int32_t* offsets, int32_t* perm,
+                                      int32_t* inv, double* maxvio, const hist_t* tile_hist,
+                                      const int32_t* super_sum, int32_t tile_routes,
+                                      hipStream_t stream);
 
 // Combine: y[t] = sum_j weights[t][j] * Yp[inv[t*k+j]] (+ shared[t]), fp32
 // accumulation, dtype 0 = fp32 / 1 = bf16 for Yp, shared and y; slots with

@@ -197,13 +197,16 @@ struct SmallDispatch {
 
 // Gate + select of moe_route on validated arguments (T > 0, ids and weights
 // set, logits set in select-only mode).  `hist`: optional per-tile expert
-// histograms for a fused dispatch (launch_select).  `sd` (small_dispatch_ok
-// batches only): the selection kernel also performs the dispatch.
+// histograms for a fused dispatch (launch_select); `super_sum`: with hist
+// and the gate, super-tile sums of super_words int32 that the gate kernel
+// zeroes and the select kernel adds into.  `sd` (small_dispatch_ok batches
+// only): the selection kernel also performs the dispatch.
 int32_t route_core(const moe_route_params* p, const void* x, const void* W,
                    const float* logit_bias, const float* select_bias,
                    const int32_t* k_per_token, float* logits, int32_t* ids, float* weights,
                    void* workspace, size_t workspace_bytes, int32_t* dev_err, moe::hist_t* hist,
-                   hipStream_t s, const SmallDispatch* sd = nullptr) {
+                   hipStream_t s, const SmallDispatch* sd = nullptr,
+                   int32_t* super_sum = nullptr, int32_t super_words = 0) {
   const moe::RouteCfg c = to_cfg(p);
   hipError_t e;
   if (x == nullptr) {  // select-only
@@ -211,9 +214,11 @@ int32_t route_core(const moe_route_params* p, const void* x, const void* W,
       e = moe::launch_route_dispatch_small(c, logits, 1, 0, nullptr, logit_bias, select_bias,
                                            k_per_token, ids, weights, dev_err, sd->counts,
                                            sd->offsets, sd->perm, sd->inv, sd->maxvio, s);
+    else if (super_sum)
+      return fail(MOE_EINVAL, "super-tile sums need the gate kernel");
     else
       e = moe::launch_select(c, logits, 1, 0, nullptr, logit_bias, select_bias, k_per_token,
-                             ids, weights, dev_err, hist, s);
+                             ids, weights, dev_err, hist, nullptr, s);
     if (e != hipSuccess) return device_fail(e, "select launch");
     return MOE_OK;
   }
@@ -247,7 +252,8 @@ int32_t route_core(const moe_route_params* p, const void* x, const void* W,
     return fail(MOE_EINVAL, "workspace of %zu bytes is below the %zu needed (or pass logits)",
                 workspace_bytes, te * g.splits);
   }
-  e = moe::launch_gate_gemm(g, p->dtype, x, W, logit_bias, hand_off, p->T, p->d, p->E, s);
+  e = moe::launch_gate_gemm(g, p->dtype, x, W, logit_bias, hand_off, p->T, p->d, p->E, s,
+                            super_sum, super_sum ? super_words : 0);
   if (e != hipSuccess) return device_fail(e, "gate GEMM launch");
   if (sd)
     e = moe::launch_route_dispatch_small(c, hand_off, g.splits, (int64_t)p->T * p->E,
@@ -257,7 +263,7 @@ int32_t route_core(const moe_route_params* p, const void* x, const void* W,
   else
     e = moe::launch_select(c, hand_off, g.splits, (int64_t)p->T * p->E,
                            g.splits > 1 ? logits : nullptr, nullptr, select_bias, k_per_token,
-                           ids, weights, dev_err, hist, s);
+                           ids, weights, dev_err, hist, super_sum, s);
   if (e != hipSuccess) return device_fail(e, "select launch");
   return MOE_OK;
 }
@@ -282,29 +288,66 @@ size_t route_ws_bytes(const moe_route_params* p) {
   return (size_t)p->T * p->E * sizeof(float) * g.splits;
 }
 
-// Tokens per dispatch tile when the routing kernels write the dispatch's
-// tile histograms themselves, else 0: the gate kernel with the selection
-// fused (tiles of BM tokens) or the select kernel.  `gate`: x and W are
-// given; `aligned`: both are 16-byte aligned.
-int fused_hist_tokens(const moe_route_params* p, bool gate, bool aligned) {
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// How moe_route_dispatch counts its routes for the dispatch.
+//   kOwn:   the dispatch's own kernels (histogram, [scan,] placement);
+//   kTiles: the routing kernels write each tile's histogram (tiles of
+//           `tokens` tokens), the placement reads every tile's counts --
+//           the gate kernel with the selection fused, or the select kernel
+//           in select-only mode;
+//   kSuper: the select kernel after the (pipelined) gate kernel also adds
+//           each tile's counts into super-tile sums, which the gate kernel
+//           zeroed; the placement reads about 2 sqrt(tiles) rows.
+// `gate`: x and W are given; `aligned`: both are 16-byte aligned.
+enum DispMode { kOwn = 0, kTiles = 1, kSuper = 2 };
+struct DispPlan {
+  int mode = kOwn;
+  int tokens = 0;
+  int64_t tiles = 0, supers = 0;
+  size_t hist_bytes = 0, super_bytes = 0;
+};
+
+DispPlan disp_plan(const moe_route_params* p, bool gate, bool aligned) {
   const moe::RouteCfg c = to_cfg(p);
-  int n = 0;
+  const int64_t R = (int64_t)p->T * p->k;
+  DispPlan d;
+  int n = 0, mode = kOwn;
   if (gate) {
     const moe::GatePlan g = moe::plan_gate(p->T, p->d, p->E, p->dtype, aligned, true);
-    n = moe::gate_select_tokens(g, p->dtype, c);
+    const int nf = moe::gate_select_tokens(g, p->dtype, c);
+    if (nf > 0) {
+      if (!moe::dispatch_hist_ok(R, p->E, nf * p->k)) return d;
+      n = nf;
+      mode = kTiles;
+    } else if (g.pipe && !std::getenv("MOE_DISPATCH_NO_SUPER")) {
+      n = moe::select_super_tokens(c);
+      mode = n > 0 ? kSuper : kOwn;
+    }
   }
-  if (n == 0) n = moe::select_hist_tokens(c);
-  if (n == 0) return 0;
-  return moe::dispatch_hist_ok((int64_t)p->T * p->k, p->E, n * p->k) ? n : 0;
+  if (mode == kOwn) {
+    n = moe::select_hist_tokens(c);
+    if (n <= 0 || !moe::dispatch_hist_ok(R, p->E, n * p->k)) return d;
+    mode = kTiles;
+  }
+  d.mode = mode;
+  d.tokens = n;
+  d.tiles = (p->T + n - 1) / n;
+  d.hist_bytes = (size_t)d.tiles * p->E * sizeof(moe::hist_t);
+  if (mode == kSuper) {
+    const int S = moe::dispatch_super_size(R, n * p->k);
+    d.supers = (d.tiles + S - 1) / S;
+    d.super_bytes = (size_t)d.supers * p->E * sizeof(int32_t);
+  }
+  return d;
 }
 
-// Dispatch part of the moe_route_dispatch workspace for a given path.
-size_t disp_ws_bytes(const moe_route_params* p, int n) {
-  return n > 0 ? (size_t)((p->T + n - 1) / n) * p->E * sizeof(moe::hist_t)
-               : moe::dispatch_workspace_bytes((int64_t)p->T * p->k, p->E);
+// Dispatch part of the moe_route_dispatch workspace for a given plan.
+size_t disp_ws_bytes(const moe_route_params* p, const DispPlan& d) {
+  if (d.mode == kOwn) return moe::dispatch_workspace_bytes((int64_t)p->T * p->k, p->E);
+  if (d.mode == kTiles) return d.hist_bytes;
+  return align256(d.hist_bytes) + d.super_bytes;
 }
-
-size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 }  // namespace
 
@@ -330,7 +373,7 @@ size_t moe_route_dispatch_workspace_size(const moe_route_params* p) {
   // enough for every path the call may take (aligned or not, gate or not)
   size_t disp = 0;
   for (int path = 0; path < 3; ++path)
-    disp = std::max(disp, disp_ws_bytes(p, fused_hist_tokens(p, path < 2, path == 0)));
+    disp = std::max(disp, disp_ws_bytes(p, disp_plan(p, path < 2, path == 0)));
   return align256(route_ws_bytes(p)) + disp;
 }
 
@@ -370,15 +413,22 @@ int32_t moe_route_dispatch(const moe_route_params* p, const void* x, const void*
   const bool gate = x != nullptr;
   const bool aligned = reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
                        reinterpret_cast<uintptr_t>(W) % 16 == 0;
-  const int n = fused_hist_tokens(p, gate, aligned);
+  const DispPlan dp = disp_plan(p, gate, aligned);
+  moe::hist_t* hist = dp.mode != kOwn ? static_cast<moe::hist_t*>(disp_ws) : nullptr;
+  int32_t* super_sum =
+      dp.mode == kSuper
+          ? reinterpret_cast<int32_t*>(static_cast<char*>(disp_ws) + align256(dp.hist_bytes))
+          : nullptr;
   rc = route_core(p, x, W, logit_bias, select_bias, k_per_token, logits, ids, weights,
-                  workspace, route, dev_err, n > 0 ? static_cast<moe::hist_t*>(disp_ws) : nullptr,
-                  s);
+                  workspace, route, dev_err, hist, s, nullptr, super_sum,
+                  (int32_t)(dp.supers * p->E));
   if (rc != MOE_OK) return rc;
-  if (n > 0)
-    e = moe::launch_dispatch_from_hist(ids, R, p->E, counts, offsets, perm, inv, maxvio,
-                                       static_cast<const moe::hist_t*>(disp_ws),
-                                       n * p->k, s);
+  if (dp.mode == kSuper)
+    e = moe::launch_dispatch_from_super(ids, R, p->E, counts, offsets, perm, inv, maxvio, hist,
+                                        super_sum, dp.tokens * p->k, s);
+  else if (dp.mode == kTiles)
+    e = moe::launch_dispatch_from_hist(ids, R, p->E, counts, offsets, perm, inv, maxvio, hist,
+                                       dp.tokens * p->k, s);
   else
     e = moe::launch_dispatch(ids, R, p->E, counts, offsets, perm, inv, maxvio, disp_ws, dev_err,
                              s);
@@ -414,11 +464,14 @@ int32_t moe_route_dispatch_plan(const moe_route_params* p, int32_t aligned,
     out->kernels = 2;
     return MOE_OK;
   }
-  const int n = fused_hist_tokens(p, true, aligned != 0);
-  out->hist_tokens = n;
+  const DispPlan dp = disp_plan(p, true, aligned != 0);
+  out->hist_tokens = dp.tokens;
   const bool fused = moe::gate_select_tokens(g, p->dtype, c) > 0;
-  out->path = fused ? MOE_PATH_FUSED : (n > 0 ? MOE_PATH_SELECT_HIST : MOE_PATH_SEPARATE);
-  out->kernels = (fused ? 1 : 2) + (n > 0 ? 1 : moe::dispatch_kernels(R, p->E));
+  out->path = fused ? MOE_PATH_FUSED
+                    : dp.mode == kSuper ? MOE_PATH_SELECT_SUPER
+                                        : dp.mode == kTiles ? MOE_PATH_SELECT_HIST
+                                                            : MOE_PATH_SEPARATE;
+  out->kernels = (fused ? 1 : 2) + (dp.mode != kOwn ? 1 : moe::dispatch_kernels(R, p->E));
   return MOE_OK;
 }
 
@@ -427,11 +480,14 @@ size_t moe_route_workspace_size(const moe_route_params* p) {
   return route_ws_bytes(p);
 }
 
-int32_t moe_route_hash(const moe_route_params* p, const int32_t* token_ids,
-                       const int32_t* tid2eid, int32_t vocab, const void* x,
-                       const void* W, const float* logit_bias, int32_t* ids,
-                       float* weights, void* workspace, size_t workspace_bytes,
-                       int32_t* dev_err, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of moe_route_hash (and of moe_route_hash_dispatch).
+int32_t check_hash_call(const moe_route_params* p, const int32_t* token_ids,
+                        const int32_t* tid2eid, int32_t vocab, const void* x, const void* W,
+                        const int32_t* ids, const float* weights) {
   const bool ids_only = (x == nullptr && W == nullptr);
   int32_t rc = check_common(p, !ids_only);
   if (rc != MOE_OK) return rc;
@@ -442,18 +498,30 @@ int32_t moe_route_hash(const moe_route_params* p, const int32_t* token_ids,
     return fail(MOE_EUNSUPPORTED,
                 "hash routing with MOE_SCORE_SOFTMAX needs renormalize=1 (the full-softmax "
                 "denominator needs every expert's logit)");
+  if ((int64_t)p->T * p->E > kI32Max) return fail(MOE_EUNSUPPORTED, "T*E must be below 2^31");
   if (p->T > 0) {
     if (!token_ids || !tid2eid || !ids)
       return fail(MOE_EINVAL, "token_ids, tid2eid and ids are required");
     if (!ids_only && !weights) return fail(MOE_EINVAL, "weights are required with x and W");
   }
-  if (p->T == 0) return MOE_OK;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  return MOE_OK;
+}
+
+// Hash routing on validated arguments, T > 0.  With a workspace holding the
+// gate's hand-off: the tiled gate contraction, then the multi-token hash
+// kernel (with `hist`: also the dispatch's tile histograms and the
+// super-tile sums the gate kernel zeroes); else the one-token-per-wavefront
+// kernel (k dot products per token, or ids only).  Sets *used_tiles when the
+// tile histograms were written.
+int32_t hash_core(const moe_route_params* p, const int32_t* token_ids, const int32_t* tid2eid,
+                  int32_t vocab, const void* x, const void* W, const float* logit_bias,
+                  int32_t* ids, float* weights, void* workspace, size_t workspace_bytes,
+                  int32_t* dev_err, hipStream_t s, moe::hist_t* hist = nullptr,
+                  int32_t* super_sum = nullptr, int32_t super_words = 0,
+                  bool* used_tiles = nullptr) {
+  const bool ids_only = (x == nullptr && W == nullptr);
   hipError_t e;
-  // logits of every expert from the tiled gate contraction when the
-  // workspace holds them, else k dot products per token in the hash kernel
-  float* lg = nullptr;
-  int32_t splits = 1;
+  if (used_tiles) *used_tiles = false;
   if (!ids_only && workspace) {
     const bool aligned = reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
                          reinterpret_cast<uintptr_t>(W) % 16 == 0;
@@ -462,16 +530,116 @@ int32_t moe_route_hash(const moe_route_params* p, const int32_t* token_ids,
     if (workspace_bytes < te * g.splits)
       g = moe::plan_gate(p->T, p->d, p->E, p->dtype, aligned, false);
     if (workspace_bytes >= te * g.splits) {
-      lg = static_cast<float*>(workspace);
-      splits = g.splits;
-      e = moe::launch_gate_gemm(g, p->dtype, x, W, logit_bias, lg, p->T, p->d, p->E, s);
+      float* lg = static_cast<float*>(workspace);
+      const bool tiles = hist && super_sum && g.pipe;
+      e = moe::launch_gate_gemm(g, p->dtype, x, W, logit_bias, lg, p->T, p->d, p->E, s,
+                                tiles ? super_sum : nullptr, tiles ? super_words : 0);
       if (e != hipSuccess) return device_fail(e, "gate GEMM launch");
+      e = moe::launch_hash_tiles(to_cfg(p), token_ids, tid2eid, vocab, lg, g.splits,
+                                 (int64_t)p->T * p->E, ids, weights, dev_err,
+                                 tiles ? hist : nullptr, tiles ? super_sum : nullptr, s);
+      if (e != hipSuccess) return device_fail(e, "hash route launch");
+      if (used_tiles) *used_tiles = tiles;
+      return MOE_OK;
     }
   }
+  // logits of the k table experts only: k dot products per token
   e = moe::launch_hash_route(to_cfg(p), p->dtype, token_ids, tid2eid, vocab, x, W, logit_bias,
-                             lg, splits, (int64_t)p->T * p->E, ids, ids_only ? nullptr : weights,
-                             dev_err, s);
+                             nullptr, 1, (int64_t)p->T * p->E, ids,
+                             ids_only ? nullptr : weights, dev_err, s);
   if (e != hipSuccess) return device_fail(e, "hash route launch");
+  return MOE_OK;
+}
+
+// Tile histograms plus super-tile sums of moe_route_hash_dispatch.
+DispPlan hash_disp_plan(const moe_route_params* p) {
+  DispPlan d;
+  const int64_t R = (int64_t)p->T * p->k;
+  const int n = moe::hash_tile_tokens(p->k);
+  if (p->T == 0 || !moe::dispatch_super_ok(R, p->E, n * p->k)) return d;
+  d.mode = kSuper;
+  d.tokens = n;
+  d.tiles = (p->T + n - 1) / n;
+  d.hist_bytes = (size_t)d.tiles * p->E * sizeof(moe::hist_t);
+  const int S = moe::dispatch_super_size(R, n * p->k);
+  d.supers = (d.tiles + S - 1) / S;
+  d.super_bytes = (size_t)d.supers * p->E * sizeof(int32_t);
+  return d;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_route_hash(const moe_route_params* p, const int32_t* token_ids,
+                       const int32_t* tid2eid, int32_t vocab, const void* x,
+                       const void* W, const float* logit_bias, int32_t* ids,
+                       float* weights, void* workspace, size_t workspace_bytes,
+                       int32_t* dev_err, void* stream) {
+  int32_t rc = check_hash_call(p, token_ids, tid2eid, vocab, x, W, ids, weights);
+  if (rc != MOE_OK || p->T == 0) return rc;
+  return hash_core(p, token_ids, tid2eid, vocab, x, W, logit_bias, ids, weights, workspace,
+                   workspace_bytes, dev_err, static_cast<hipStream_t>(stream));
+}
+
+size_t moe_route_hash_dispatch_workspace_size(const moe_route_params* p) {
+  if (check_common(p, true) != MOE_OK) return 0;
+  const int64_t R = (int64_t)p->T * p->k;
+  if ((int64_t)p->T * p->E > kI32Max) return 0;
+  if (p->T == 0) return 0;
+  const DispPlan d = hash_disp_plan(p);
+  const size_t disp = std::max(disp_ws_bytes(p, d),
+                               moe::dispatch_workspace_bytes(R, p->E));
+  return align256(route_ws_bytes(p)) + disp;
+}
+
+int32_t moe_route_hash_dispatch(const moe_route_params* p, const int32_t* token_ids,
+                                const int32_t* tid2eid, int32_t vocab, const void* x,
+                                const void* W, const float* logit_bias, int32_t* ids,
+                                float* weights, int32_t* counts, int32_t* offsets,
+                                int32_t* perm, int32_t* inv, double* maxvio, void* workspace,
+                                size_t workspace_bytes, int32_t* dev_err, void* stream) {
+  if (x == nullptr || W == nullptr) return fail(MOE_EINVAL, "x and W are required");
+  int32_t rc = check_hash_call(p, token_ids, tid2eid, vocab, x, W, ids, weights);
+  if (rc != MOE_OK) return rc;
+  if (!counts || !offsets) return fail(MOE_EINVAL, "counts and offsets are required");
+  const int64_t R = (int64_t)p->T * p->k;
+  if (R > 0 && !perm) return fail(MOE_EINVAL, "perm is required");
+  if (p->E > MOE_MAX_EXPERTS)
+    return fail(MOE_EUNSUPPORTED, "E=%d exceeds MOE_MAX_EXPERTS=%d", p->E, MOE_MAX_EXPERTS);
+  const size_t need = moe_route_hash_dispatch_workspace_size(p);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(MOE_EINVAL, "workspace of %zu bytes is below the %zu needed", workspace_bytes,
+                need);
+  if (need > 0 && reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(MOE_EINVAL, "workspace must be 256-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (p->T == 0) {  // zero counts and offsets only
+    e = moe::launch_dispatch(ids, 0, p->E, counts, offsets, perm, inv, maxvio, nullptr, dev_err,
+                             s);
+    if (e != hipSuccess) return device_fail(e, "dispatch launch");
+    return MOE_OK;
+  }
+  const size_t route = align256(route_ws_bytes(p));
+  void* disp_ws = static_cast<char*>(workspace) + route;
+  const DispPlan dp = hash_disp_plan(p);
+  moe::hist_t* hist = dp.mode == kSuper ? static_cast<moe::hist_t*>(disp_ws) : nullptr;
+  int32_t* super_sum =
+      dp.mode == kSuper
+          ? reinterpret_cast<int32_t*>(static_cast<char*>(disp_ws) + align256(dp.hist_bytes))
+          : nullptr;
+  bool tiles = false;
+  rc = hash_core(p, token_ids, tid2eid, vocab, x, W, logit_bias, ids, weights, workspace,
+                 route, dev_err, s, hist, super_sum, (int32_t)(dp.supers * p->E), &tiles);
+  if (rc != MOE_OK) return rc;
+  if (tiles)
+    e = moe::launch_dispatch_from_super(ids, R, p->E, counts, offsets, perm, inv, maxvio, hist,
+                                        super_sum, dp.tokens * p->k, s);
+  else
+    e = moe::launch_dispatch(ids, R, p->E, counts, offsets, perm, inv, maxvio, disp_ws, dev_err,
+                             s);
+  if (e != hipSuccess) return device_fail(e, "dispatch launch");
   return MOE_OK;
 }
 

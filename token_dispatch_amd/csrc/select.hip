@@ -42,7 +42,6 @@
 namespace moe {
 namespace {
 
-using sel::kHistMaxE;
 using sel::kMaxK;
 using sel::load_vals;
 
@@ -50,23 +49,26 @@ using sel::load_vals;
 // logits are the sum of NSPLIT partial arrays `split_stride` floats apart (a
 // K split of the gate), added in a fixed order.  `vec`: the logits, their
 // split stride and the bias arrays allow 16-byte loads (E % 4 == 0).
-// HIST (E <= kHistMaxE): also hist[block][e] = number of picks of expert e
-// among the workgroup's TPB tokens -- the routes t*k + j of those tokens are
-// one tile of the dispatch (counted with ballot peer masks, no atomics).
+// HIST: also hist[block][e] = number of picks of expert e among the
+// workgroup's TPB tokens -- the routes t*k + j of those tokens are one tile
+// of the dispatch (counted with ballot peer masks, no atomics) -- and, with
+// super_sum, the same counts added into super_sum[block / super_S][e]
+// (integer atomics; the placement kernel then reads super rows instead of
+// every tile's row).
 template <int LPT, int VPL, int NSPLIT, bool MONO, int WPB, bool HIST>
 __global__ __launch_bounds__(WPB * kWave) void select_kernel(
     RouteCfg c, const float* __restrict__ logits, int64_t split_stride,
     float* __restrict__ logits_out, const float* __restrict__ logit_bias,
     const float* __restrict__ select_bias, const int32_t* __restrict__ k_per_token,
     int32_t* __restrict__ ids, float* __restrict__ weights, int32_t* __restrict__ dev_err,
-    int vec, hist_t* __restrict__ hist) {
+    int vec, hist_t* __restrict__ hist, int32_t* __restrict__ super_sum, int super_S) {
   constexpr int TPW = kWave / LPT;               // tokens per wavefront
   constexpr int TPB = WPB * TPW;                 // tokens per workgroup
   constexpr int ROW = LPT * VPL;                 // >= E
   constexpr int KPL = (kMaxK + LPT - 1) / LPT;   // output slots per lane
   __shared__ __attribute__((aligned(16))) float lrow[TPB][ROW];  // logits (+ logit_bias)
   __shared__ int32_t pick[TPB][kMaxK];                          // expert of each rank
-  __shared__ int32_t whist[HIST ? WPB : 1][HIST ? kHistMaxE : 1];  // per-wave pick counts
+  __shared__ int32_t whist[HIST ? WPB : 1][HIST ? ROW : 1];  // per-wave pick counts
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -127,13 +129,14 @@ __global__ __launch_bounds__(WPB * kWave) void select_kernel(
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    sel::count_picks<LPT, sel::kHistIdBits>(pid, sl, c.k, whist[wave]);
+    sel::count_picks<LPT, sel::id_bits_for(ROW)>(pid, sl, c.k, whist[wave]);
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += WPB * kWave) {
       int n = 0;
 #pragma unroll
       for (int w8 = 0; w8 < WPB; ++w8) n += whist[w8][e];
       hist[(int64_t)blockIdx.x * E + e] = (hist_t)n;
+      if (super_sum && n) atomicAdd(&super_sum[(int64_t)(blockIdx.x / super_S) * E + e], n);
     }
   }
 }
@@ -326,50 +329,63 @@ int hist_waves(const RouteCfg& c, int lpt) {
   return 0;
 }
 
+// Waves of a workgroup that counts its picks into tile histograms and
+// super-tile sums (the placement then reads about 2 sqrt(tiles) rows, so any
+// tile size works): 8 when that still gives at least 256 workgroups (larger
+// tiles, fewer placement workgroups), else 4; 16 for one-token wavefronts;
+// tiles of at most 2048 routes.
+int super_waves(const RouteCfg& c, int lpt) {
+  const int tpw = kWave / lpt;
+  if (lpt == kWave) return 16 * c.k <= 2048 ? 16 : 0;
+  const int64_t wgs8 = ((int64_t)c.T + 8 * tpw - 1) / (8 * tpw);
+  if (wgs8 >= 256 && 8 * tpw * c.k <= 2048) return 8;
+  return 4 * tpw * c.k <= 2048 ? 4 : 0;
+}
+
 template <int LPT, int VPL, int NS, bool MONO>
 hipError_t launch_vpl(const RouteCfg& c, const float* logits, int64_t stride, float* logits_out,
                       const float* logit_bias, const float* select_bias,
                       const int32_t* k_per_token, int32_t* ids, float* weights, int32_t* dev_err,
-                      int vec, hist_t* hist, hipStream_t s) {
+                      int vec, hist_t* hist, int32_t* super_sum, hipStream_t s) {
   constexpr int tpb = 4 * (kWave / LPT);
   const int64_t blocks = ((int64_t)c.T + tpb - 1) / tpb;
-  if constexpr (LPT * VPL <= kHistMaxE) {
-    if (hist) {  // one dispatch tile per workgroup: hist_waves(c, LPT) waves
+  if (hist) {  // one dispatch tile per workgroup
+    const int hw = super_sum ? super_waves(c, LPT) : hist_waves(c, LPT);
+    const int64_t R = (int64_t)c.T * c.k;
 #define MOE_H(HW_)                                                                            \
   if (hw == HW_) {                                                                            \
     constexpr int htpb = HW_ * (kWave / LPT);                                                 \
     const int64_t hblocks = ((int64_t)c.T + htpb - 1) / htpb;                                 \
+    const int S = super_sum ? dispatch_super_size(R, htpb * c.k) : 1;                         \
     return launch(kStageSelect, select_kernel<LPT, VPL, NS, MONO, HW_, true>,                 \
                   dim3((uint32_t)hblocks), dim3(HW_ * kWave), s, c, logits, stride,          \
                   logits_out, logit_bias, select_bias, k_per_token, ids, weights, dev_err,   \
-                  vec, hist);                                                                 \
+                  vec, hist, super_sum, S);                                                   \
   }
-      const int hw = hist_waves(c, LPT);
-      if constexpr (LPT == kWave) {
-        MOE_H(16)
-      } else {
-        MOE_H(4)
-        MOE_H(8)
-      }
-#undef MOE_H
-      return hipErrorInvalidValue;
+    if constexpr (LPT == kWave) {
+      MOE_H(16)
+    } else {
+      MOE_H(4)
+      MOE_H(8)
     }
+#undef MOE_H
+    return hipErrorInvalidValue;
   }
-  if (hist) return hipErrorInvalidValue;
   return launch(kStageSelect, select_kernel<LPT, VPL, NS, MONO, 4, false>, dim3((uint32_t)blocks),
                 dim3(4 * kWave), s, c, logits, stride, logits_out, logit_bias, select_bias,
-                k_per_token, ids, weights, dev_err, vec, (hist_t*)nullptr);
+                k_per_token, ids, weights, dev_err, vec, (hist_t*)nullptr, (int32_t*)nullptr, 1);
 }
 
 template <int LPT, int VPL, bool MONO>
 hipError_t launch_splits(const RouteCfg& c, const float* logits, int splits, int64_t stride,
                          float* logits_out, const float* logit_bias, const float* select_bias,
                          const int32_t* k_per_token, int32_t* ids, float* weights,
-                         int32_t* dev_err, int vec, hist_t* hist, hipStream_t s) {
+                         int32_t* dev_err, int vec, hist_t* hist, int32_t* super_sum,
+                         hipStream_t s) {
 #define MOE_S(S_)                                                                        \
   return launch_vpl<LPT, VPL, S_, MONO>(c, logits, stride, logits_out, logit_bias,       \
                                         select_bias, k_per_token, ids, weights, dev_err, \
-                                        vec, hist, s)
+                                        vec, hist, super_sum, s)
   if (splits == 2) MOE_S(2);
   if (splits == 4) MOE_S(4);
   if (splits == 8) MOE_S(8);
@@ -383,14 +399,14 @@ hipError_t launch_mono(const RouteCfg& c, bool mono, const float* logits, int sp
                        int64_t stride, float* logits_out, const float* logit_bias,
                        const float* select_bias, const int32_t* k_per_token, int32_t* ids,
                        float* weights, int32_t* dev_err, int vec, hist_t* hist,
-                       hipStream_t s) {
+                       int32_t* super_sum, hipStream_t s) {
   if (mono)
     return launch_splits<LPT, VPL, true>(c, logits, splits, stride, logits_out, logit_bias,
                                          select_bias, k_per_token, ids, weights, dev_err, vec,
-                                         hist, s);
+                                         hist, super_sum, s);
   return launch_splits<LPT, VPL, false>(c, logits, splits, stride, logits_out, logit_bias,
                                         select_bias, k_per_token, ids, weights, dev_err, vec,
-                                        hist, s);
+                                        hist, super_sum, s);
 }
 
 bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
@@ -459,8 +475,15 @@ void select_shape(const RouteCfg& c, int* lpt, int* vpl) {
 int select_hist_tokens(const RouteCfg& c) {
   int lpt, vpl;
   select_shape(c, &lpt, &vpl);
-  if (lpt * vpl > kHistMaxE) return 0;
   return hist_waves(c, lpt) * (kWave / lpt);
+}
+
+int select_super_tokens(const RouteCfg& c) {
+  int lpt, vpl;
+  select_shape(c, &lpt, &vpl);
+  const int w = super_waves(c, lpt);
+  if (w == 0 || !dispatch_super_ok((int64_t)c.T * c.k, c.E, w * (kWave / lpt) * c.k)) return 0;
+  return w * (kWave / lpt);
 }
 
 bool small_dispatch_ok(const RouteCfg& c) {
@@ -518,7 +541,8 @@ hipError_t launch_route_dispatch_small(const RouteCfg& c, const float* logits, i
 hipError_t launch_select(const RouteCfg& c, const float* logits, int32_t splits,
                          int64_t split_stride, float* logits_out, const float* logit_bias,
                          const float* select_bias, const int32_t* k_per_token, int32_t* ids,
-                         float* weights, int32_t* dev_err, hist_t* hist, hipStream_t stream) {
+                         float* weights, int32_t* dev_err, hist_t* hist, int32_t* super_sum,
+                         hipStream_t stream) {
   if (c.T == 0) return hipSuccess;
   const int E = c.E;
   const bool grouped = c.n_groups > 1 && c.topk_groups < c.n_groups;
@@ -532,7 +556,7 @@ hipError_t launch_select(const RouteCfg& c, const float* logits, int32_t splits,
   if (lpt == LPT_ && vpl == VPL_)                                                            \
     return launch_mono<LPT_, VPL_>(c, mono, logits, splits, split_stride, logits_out,        \
                                    logit_bias, select_bias, k_per_token, ids, weights, dev_err, \
-                                   vec, hist, stream);
+                                   vec, hist, super_sum, stream);
   MOE_SEL(16, 1)
   MOE_SEL(16, 2)
   MOE_SEL(16, 4)

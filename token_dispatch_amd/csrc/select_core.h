@@ -10,8 +10,10 @@ namespace moe {
 namespace sel {
 
 constexpr int kMaxK = 32;        // MOE_MAX_K
-constexpr int kHistMaxE = 256;   // experts of the per-block histogram option
-constexpr int kHistIdBits = 8;   // bits of an expert id below kHistMaxE
+
+// Ballots per peer mask for expert ids below `row` (a row of LPT * VPL
+// experts): the bits of the largest id.
+constexpr int id_bits_for(int row) { return row <= 128 ? 7 : row <= 256 ? 8 : 10; }
 
 // ---- DPP helpers ------------------------------------------------------------
 template <int CTRL>
