@@ -391,10 +391,7 @@ def measure(w, inp, dev, args, *, headline):
     out = {}
     if headline:
         # the headline's own extras first: the spread of single steps (each
-        # between its own pair of events) and the HIP-graph replays.  They
-        # run the step continuously for a while before the W warm-up steps and
-        # the K timed ones, which therefore run at working clocks (from an
-        # idle GPU the first ~80 gpt-oss-like steps take ~15 % longer)
+        # between its own pair of events) and the HIP-graph replays
         n_each = min(max(steps, 20), 200)
         stream = torch.cuda.current_stream(dev)
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -410,6 +407,7 @@ def measure(w, inp, dev, args, *, headline):
                           "p90": round(float(np.percentile(each, 90)), 3)}
         if not args.no_graph:
             out["graph"] = graph_replay(case, max(steps, 20), dev)
+    out["settle"] = settle(case, args.settle_ms)
     for i in range(warm):
         case.step(i)
     torch.cuda.synchronize()
@@ -443,6 +441,23 @@ def measure(w, inp, dev, args, *, headline):
     del case
     torch.cuda.empty_cache()
     return out
+
+
+def settle(case, ms):
+    """Untimed steps, back to back, for at least `ms` of wall time before the
+    W warm-up steps: from an idle GPU the first few hundred gpt-oss-like
+    steps run up to ~15 % slower (the fused kernel 78-88 us for ~30 ms of
+    load, then 73.7-74.5 us for as long as the load lasts), a power-state
+    ramp that W = 5 steps do not cover.  Returns the steps and time spent."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(32):
+            case.step(n)
+            n += 1
+        torch.cuda.synchronize()
+    return {"steps": n, "ms": round((time.perf_counter() - t0) * 1e3, 1)}
 
 
 def graph_replay(case, steps, dev):
@@ -575,6 +590,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--settle-ms", type=float, default=150.0,
+                    help="untimed back-to-back steps for this long before the W warm-up "
+                         "steps of every workload (power-state ramp)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--config-cpu-seconds", type=float, default=3.0)
     ap.add_argument("--no-configs", action="store_true",
@@ -660,6 +678,7 @@ def main():
         "value": round(w.T / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
         "timing": "eager launches on one stream",
+        "settle": head["settle"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": describe(w), "T": w.T, "d": w.d, "E": w.E, "k_max": w.k},

@@ -33,9 +33,12 @@
  *    (64/128/256/512-byte stages), MOE_GATE_NS (ring depth), MOE_GATE_NOPIPE
  *    (the register-staged gate kernel), MOE_SELECT_LPT (4/8/16/64 lanes per
  *    token), MOE_NO_FUSED_SELECT (selection in its own kernel),
- *    MOE_DISPATCH_UNFUSED (the three-kernel dispatch), MOE_NO_SMALL_DISPATCH
- *    (no one-workgroup selection + dispatch for small batches).  Values that do not
- *    fit the shapes are ignored; workspace sizes follow the same variables.
+ *    MOE_DISPATCH_UNFUSED (the three-kernel dispatch), MOE_DISPATCH_NO_SUPER
+ *    (tile histograms without super-tile sums: the placement reads every
+ *    tile's counts), MOE_SELECT_SUPER_WAVES (2/4/8 wavefronts per counted
+ *    selection workgroup), MOE_NO_SMALL_DISPATCH (no one-workgroup
+ *    selection + dispatch for small batches).  Values that do not fit the
+ *    shapes are ignored; workspace sizes follow the same variables.
  */
 #ifndef MOE_ROUTE_H
 #define MOE_ROUTE_H

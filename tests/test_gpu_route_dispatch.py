@@ -314,6 +314,41 @@ def test_super_tile_dispatch(T, d, E, k, dyn, monkeypatch):
     assert float(mva.item()) == oracle.maxvio(d_ref["counts"])
 
 
+@pytest.mark.parametrize("waves", ["2", "4", "8"])
+@pytest.mark.parametrize("name,T", [("qwen3_dynk", None), ("qwen3_dynk", 1001),
+                                    ("dsv3_grouped", 3000), ("olmoe", 777),
+                                    ("grouped_quota", 2049)])
+def test_super_tile_select_workgroup_sizes(name, T, waves, monkeypatch):
+    """Selection workgroups of 2, 4 or 8 waves (one dispatch tile each, of
+    2, 4 or 8 wavefronts' tokens) on the super-tile path: the same ids and
+    weights as the path without tile counting, and the oracle's dispatch of
+    those ids, bit for bit."""
+    w = wl.WORKLOADS[name]
+    inp = wl.make_inputs(w, T=T)
+    kw = route_kwargs(w)
+    if kw["group_score"] is None:
+        kw.pop("group_score")
+    kw.update(logit_bias=up(inp["logit_bias"]), select_bias=up(inp["select_bias"]),
+              k_per_token=up(inp["k_per_token"]))
+    x, W = up(inp["x"]), up(inp["W"])
+    monkeypatch.setenv("MOE_SELECT_SUPER_WAVES", waves)
+    kw2 = {key: v for key, v in route_kwargs(w).items() if v is not None}
+    plan = tda.route_dispatch_plan(w.T if T is None else T, w.d, w.E, w.k, 1, **kw2)
+    say("super select waves", name, T, waves, plan["path"], plan["hist_tokens"])
+    assert plan["path"] == "select_super", plan
+    mv = torch.zeros(1, dtype=torch.float64, device=DEV)
+    a = tda.route_dispatch(x, W, w.k, maxvio=mv, **kw)
+    monkeypatch.delenv("MOE_SELECT_SUPER_WAVES")
+    monkeypatch.setenv("MOE_DISPATCH_UNFUSED", "1")
+    monkeypatch.setenv("MOE_DISPATCH_NO_SUPER", "1")
+    ids, wts = tda.route(x, W, w.k, **kw)[:2]
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], ids) and torch.equal(a[1], wts)
+    d_ref = oracle.dispatch(down(a[0]), w.E)
+    check_dispatch(tuple(a[2:]), d_ref)
+    assert float(mv.item()) == oracle.maxvio(d_ref["counts"])
+
+
 @pytest.mark.parametrize("name,T", [("qwen3_dynk", None), ("qwen3_dynk", 4091), ("olmoe", 1000)])
 def test_all_counts_placement_after_the_gate(name, T, monkeypatch):
     """With the super-tile sums switched off the select kernel's tile

@@ -291,7 +291,8 @@ class PlanInfo(ctypes.Structure):
 
 def route_dispatch_plan(T, d, E, k, dtype=1, aligned=True, **kw) -> dict:
     """How moe_route_dispatch runs for these shapes (host-side planning only):
-    {"path": "separate" | "select_hist" | "fused" | "small", gate tile,
+    {"path": "separate" | "select_hist" | "fused" | "small" | "select_super",
+    gate tile,
     waves, splits, stage bytes, ring depth and LDS, selection lanes and
     experts per lane, tokens per counted dispatch tile, kernels per call}."""
     p = make_params(T, d, E, k, dtype, **kw)

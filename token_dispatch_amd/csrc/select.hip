@@ -333,12 +333,19 @@ int hist_waves(const RouteCfg& c, int lpt) {
 // super-tile sums (the placement then reads about 2 sqrt(tiles) rows, so any
 // tile size works): 8 when that still gives at least 256 workgroups (larger
 // tiles, fewer placement workgroups), else 4; 16 for one-token wavefronts;
-// tiles of at most 2048 routes.
+// tiles of at most 2048 routes.  MOE_SELECT_SUPER_WAVES (2, 4 or 8)
+// overrides the choice for sweeps: 2-wave tiles (twice the placement
+// workgroups) measured slower on every shape (Qwen3-like step 23.0 ->
+// 25.8 us, DeepSeek-V4-like 119.4 -> 146.7 us).
 int super_waves(const RouteCfg& c, int lpt) {
   const int tpw = kWave / lpt;
   if (lpt == kWave) return 16 * c.k <= 2048 ? 16 : 0;
-  const int64_t wgs8 = ((int64_t)c.T + 8 * tpw - 1) / (8 * tpw);
-  if (wgs8 >= 256 && 8 * tpw * c.k <= 2048) return 8;
+  auto wgs = [&](int w) { return ((int64_t)c.T + w * tpw - 1) / (w * tpw); };
+  if (const char* env = std::getenv("MOE_SELECT_SUPER_WAVES")) {
+    const int w = std::atoi(env);
+    if ((w == 2 || w == 4 || w == 8) && w * tpw * c.k <= 2048) return w;
+  }
+  if (wgs(8) >= 256 && 8 * tpw * c.k <= 2048) return 8;
   return 4 * tpw * c.k <= 2048 ? 4 : 0;
 }
 
@@ -365,6 +372,7 @@ hipError_t launch_vpl(const RouteCfg& c, const float* logits, int64_t stride, fl
     if constexpr (LPT == kWave) {
       MOE_H(16)
     } else {
+      MOE_H(2)
       MOE_H(4)
       MOE_H(8)
     }
