@@ -390,8 +390,10 @@ def measure(w, inp, dev, args, *, headline):
         f"({case.plan['kernels']} kernels); warmup {warm}, steps {steps}")
     out = {}
     if headline:
-        # the headline's own extras first: the spread of single steps (each
-        # between its own pair of events) and the HIP-graph replays
+        # the headline's own extras first, at settled clocks: the spread of
+        # single steps (each between its own pair of events) and the HIP-graph
+        # replays
+        settle(case, args.settle_ms)
         n_each = min(max(steps, 20), 200)
         stream = torch.cuda.current_stream(dev)
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
