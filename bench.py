@@ -15,8 +15,10 @@ cache) so the gate reads x from HBM, not from cache.
 The headline (`value`) is the gpt-oss-like configuration, T = 65536 tokens
 (the largest one-GPU configuration).  The `configs` object times every other
 routing configuration in the same run (Mixtral-, Qwen3-, DeepSeek-V3-,
-DeepSeek-V4-like and the V4-like hash layer), each with its per-kernel times,
-binding roofline and the oracle's throughput on the host.
+DeepSeek-V4-like, the V4-like hash layer and the routing variants: selection
+bias, OLMoE-like softmax, group max, Switch-like top-1 with a capacity,
+per-group quota), each with its per-kernel times, binding roofline and the
+oracle's throughput on the host.
 
 Roofline of a kernel: its algorithmic HBM bytes and flops per launch give
 t_bound = max(bytes / 8 TB/s, flops / MFMA peak of its dtype); the binding
@@ -42,7 +44,9 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
 LLC_BYTES = 256 << 20
 HEADLINE = "gptoss_skew"
-CONFIGS = ("mixtral", "qwen3_dynk", "dsv3_grouped", "dsv4", "dsv4_hash", "gptoss_skew")
+CONFIGS = ("mixtral", "qwen3_dynk", "dsv3_grouped", "dsv4", "dsv4_hash", "gptoss_skew",
+           # routing variants on the same shapes
+           "dsv4_bias", "olmoe", "dsv3_groupmax", "switch_top1", "grouped_quota")
 METRIC = "routed tokens/sec (gate+select+dispatch) and % of MFMA/HBM roofline, 1 MI355X"
 
 
@@ -408,7 +412,7 @@ def measure(w, inp, dev, args, *, headline):
                           "p10": round(float(np.percentile(each, 10)), 3),
                           "p90": round(float(np.percentile(each, 90)), 3)}
         if not args.no_graph:
-            out["graph"] = graph_replay(case, max(steps, 20), dev)
+            out["graph"] = graph_replay(case, max(steps, 20), dev, args.settle_ms)
     out["settle"] = settle(case, args.settle_ms)
     for i in range(warm):
         case.step(i)
@@ -422,7 +426,7 @@ def measure(w, inp, dev, args, *, headline):
                 "tokens_per_s": round(T / (ms_per_step / 1e3), 1),
                 "plan": case.plan["path"], "kernels_per_step": case.plan["kernels"]})
     if not headline and not args.no_graph:
-        out["graph"] = graph_replay(case, steps, dev)
+        out["graph"] = graph_replay(case, steps, dev, args.settle_ms)
 
     stages, dom = case.kernels(min(steps, 100), args.traffic)
     for s, v in stages.items():
@@ -462,9 +466,9 @@ def settle(case, ms):
     return {"steps": n, "ms": round((time.perf_counter() - t0) * 1e3, 1)}
 
 
-def graph_replay(case, steps, dev):
-    """The same steps replayed from HIP graphs: one graph per step (one per
-    copy of x), and one graph holding a step for every copy of x in order."""
+def capture_graphs(case, dev):
+    """HIP graphs of the step: one per copy of x (one step each), and one
+    holding a step for every copy of x in order."""
     import torch
     n = case.n_copies
     cs = torch.cuda.Stream(dev)
@@ -483,29 +487,76 @@ def graph_replay(case, steps, dev):
     with torch.cuda.graph(many):
         for i in range(n):
             case.step(i)
+    torch.cuda.synchronize()
+    return singles, many
+
+
+def time_enqueued(fn, reps, dev, warm=20):
+    """(GPU us per rep between two events, host us per rep spent enqueuing)."""
+    import torch
     stream = torch.cuda.current_stream(dev)
+    for i in range(min(reps, warm)):
+        fn(i)
+    torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    h0 = time.perf_counter()
+    for i in range(reps):
+        fn(i)
+    h1 = time.perf_counter()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / reps * 1e3, (h1 - h0) / reps * 1e6
 
-    def run(fn, reps):
-        for i in range(min(reps, 20)):
-            fn(i)
-        torch.cuda.synchronize()
-        ev0.record(stream)
-        for i in range(reps):
-            fn(i)
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        return ev0.elapsed_time(ev1) / reps
 
-    one = run(lambda i: singles[i % n].replay(), steps)
+def graph_replay(case, steps, dev, settle_ms):
+    """The same steps replayed from HIP graphs: one graph per step (one per
+    copy of x), and one graph holding a step for every copy of x in order;
+    with the host's enqueue time per step of each form.  The capture idles
+    the GPU, so the clocks are settled again before the replays."""
+    n = case.n_copies
+    singles, many = capture_graphs(case, dev)
+    settle(case, settle_ms)
+    one, one_h = time_enqueued(lambda i: singles[i % n].replay(), steps, dev)
     reps = max(1, steps // n)
-    multi = run(lambda i: many.replay(), reps) / n
-    out = {"one_step_graphs_us": round(one * 1e3, 3), "steps_per_graph": n,
-           "multi_step_graph_us": round(multi * 1e3, 3), "multi_step_replays": reps}
+    multi, multi_h = time_enqueued(lambda i: many.replay(), reps, dev)
+    eager, eager_h = time_enqueued(case.step, steps, dev)
+    out = {"one_step_graphs_us": round(one, 3), "steps_per_graph": n,
+           "multi_step_graph_us": round(multi / n, 3), "multi_step_replays": reps,
+           "eager_us": round(eager, 3),
+           "host_enqueue_us": {"one_step_graph": round(one_h, 2),
+                               "multi_step_graph": round(multi_h / n, 2),
+                               "eager": round(eager_h, 2)}}
     log(f"[bench] {case.w.name}: graph replay {out['one_step_graphs_us']} us/step "
-        f"(one step per graph), {out['multi_step_graph_us']} us/step ({n} steps per graph)")
+        f"(one step per graph), {out['multi_step_graph_us']} us/step ({n} steps per graph), "
+        f"eager {out['eager_us']}; host enqueue per step {out['host_enqueue_us']}")
     del singles, many
     return out
+
+
+def graph_phases(case, dev, steps):
+    """Eager steps, one-step graphs and a many-step graph, each phase
+    between idle gaps of 30 ms (so that a kernel trace splits into phases),
+    twice; GPU and host-enqueue microseconds per step of each."""
+    n = case.n_copies
+    singles, many = capture_graphs(case, dev)
+    settle(case, 100.0)
+    res = []
+    for rep in range(2):
+        for name, fn, reps, per in (
+                ("eager", case.step, steps, 1),
+                ("one_step_graphs", lambda i: singles[i % n].replay(), steps, 1),
+                ("multi_step_graph", lambda i: many.replay(), max(1, steps // n), n)):
+            time.sleep(0.03)
+            g, h = time_enqueued(fn, reps, dev, warm=0)
+            res.append({"phase": name, "round": rep, "steps": reps * per,
+                        "gpu_us_per_step": round(g / per, 3),
+                        "host_enqueue_us_per_step": round(h / per, 3)})
+            log(f"[bench] {case.w.name}: {name}: {res[-1]['gpu_us_per_step']} us/step on the "
+                f"GPU, host enqueue {res[-1]['host_enqueue_us_per_step']} us/step")
+            time.sleep(0.03)
+    del singles, many
+    return res
 
 
 def row_movement(case, dev, args):
@@ -604,6 +655,9 @@ def main():
                     help="skip the separate measurement of the combine and send buffer")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches only (no HIP graph replay)")
+    ap.add_argument("--graph-phases", action="store_true",
+                    help="only time eager steps, one-step graphs and a many-step graph of "
+                         "--workload, in phases between idle gaps (for a kernel trace)")
     ap.add_argument("--calibrate-copy-mb", type=float, default=0.0,
                     help="only run a plain device copy of this many MB (counter calibration)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -642,6 +696,10 @@ def main():
     # between them and the headline's W warm-up and K timed steps
     log(f"[bench] generating {w.name} inputs (T={w.T}, d={w.d}, E={w.E})")
     inp = wl.make_inputs(w)
+    if args.graph_phases:
+        res = graph_phases(Case(w, inp, dev), dev, max(args.steps, 96))
+        print(json.dumps({"workload": describe(w), "graph_phases": res}), flush=True)
+        return
     configs, config_inputs = {}, {}
     if not args.no_configs:
         shared = {}
