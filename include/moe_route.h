@@ -220,6 +220,12 @@ size_t moe_dispatch_workspace_size(int32_t T, int32_t k_stride, int32_t E);
 /*
  * moe_dispatch -- group routes by expert (the step that sends each token only
  * to its selected experts; under expert parallelism it feeds the all-to-all).
+ * Passages: "I modelli MoE open hanno router opposti", the sentence on expert
+ * parallelism (every routing choice becomes all-to-all traffic between GPUs);
+ * "Feature Request: dynamic number of experts", Possible Implementation (only
+ * the selected experts run, and their outputs are summed with the weights).
+ * The pages fix no layout for the grouping; this is the plain stable
+ * counting sort, counts -> exclusive offsets -> positions.
  *
  * Route r = t*k_stride + j is slot j of token t.  Routes with ids[r] < 0 are
  * empty and skipped; ids[r] >= E are errors (skipped, counted in *dev_err).
