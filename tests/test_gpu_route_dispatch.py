@@ -284,6 +284,9 @@ def test_quota_fused_paths(path, T, d, E, k, G, kpg, monkeypatch):
     (20000, 64, 64, 32, False),    # 2048-route tiles (two chunks per wave)
     (1, 64, 256, 8, False),        # a single tile
     (16384, 512, 384, 6, True),    # DeepSeek-V4-like tile shape with empty slots
+    (3000, 64, 1024, 8, True),     # the largest E: 10-bit ids, one thread per expert
+    (70000, 64, 1024, 2, False),   # 4375 tiles of 32 routes: 66 super rows, S = 67
+    (5000, 128, 512, 16, True),    # 16-wave tiles of 256 routes at E = 512
 ])
 def test_super_tile_dispatch(T, d, E, k, dyn, monkeypatch):
     """The select-written tile histograms plus super-tile sums (zeroed by the
