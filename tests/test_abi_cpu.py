@@ -138,6 +138,43 @@ def test_route_hash_validation():
     assert tda.route_hash_workspace_size(0, 64, 8, 2) == 0
 
 
+def test_route_hash_dispatch_validation():
+    """moe_route_hash_dispatch rejects bad calls before enqueueing anything;
+    its workspace holds the gate hand-off (256-byte aligned) and then the
+    larger of the dispatch's own workspace and the hash kernel's tile
+    histograms plus super-tile sums."""
+    L = tda.lib()
+    T, d, E, k = 1000, 128, 384, 6
+    p = tda.make_params(T, d, E, k, score="sqrt_softplus")
+    n = tda.route_hash_dispatch_workspace_size(T, d, E, k, score="sqrt_softplus")
+    route = (tda.route_hash_workspace_size(T, d, E, k, score="sqrt_softplus") + 255) // 256 * 256
+    tiles = -(-T // 32)  # 8-lane token segments, 4 wavefronts: 32 tokens per tile
+    S = int(np.ceil(np.sqrt(tiles)))
+    hist = (tiles * E * 2 + 255) // 256 * 256
+    assert n >= route + hist + -(-tiles // S) * E * 4
+    assert n >= route + tda.dispatch_workspace_size(T, k, E)
+    ws = ctypes.c_void_p(0x1000)
+
+    def call(pp, x=FAKE, W=FAKE, counts=FAKE, offsets=FAKE, perm=FAKE, w=ws, nbytes=n,
+             vocab=50):
+        return L.moe_route_hash_dispatch(ctypes.byref(pp), FAKE, FAKE, vocab, x, W, None, FAKE,
+                                         FAKE, counts, offsets, perm, None, None, w, nbytes,
+                                         None, None)
+
+    assert call(p, x=None, W=None) == tda.MOE_EINVAL
+    assert "required" in L.moe_last_error().decode()
+    assert call(p, counts=None) == tda.MOE_EINVAL
+    assert call(p, perm=None) == tda.MOE_EINVAL
+    assert call(p, nbytes=n - 1) == tda.MOE_EINVAL
+    assert "workspace" in L.moe_last_error().decode()
+    assert call(p, w=ctypes.c_void_p(0x1010)) == tda.MOE_EINVAL
+    assert "aligned" in L.moe_last_error().decode()
+    assert call(p, vocab=0) == tda.MOE_EINVAL
+    big = tda.make_params(T, d, 4096, k, score="sqrt_softplus")
+    assert call(big) in (tda.MOE_EINVAL, tda.MOE_EUNSUPPORTED)
+    assert tda.route_hash_dispatch_workspace_size(0, d, E, k) >= 0
+
+
 def test_dispatch_validation_and_workspace_size():
     L = tda.lib()
     # two tiles of 512 routes: a [2][64] histogram of 16-bit counts

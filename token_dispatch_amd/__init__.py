@@ -454,6 +454,11 @@ def route_hash_dispatch(token_ids: torch.Tensor, tid2eid: torch.Tensor, E: int, 
         inv = torch.empty(R, dtype=i32, device=device)
     _dev(ids, "ids", i32, (T, k))
     _dev(weights, "weights", torch.float32, (T, k))
+    _dev(counts, "counts", i32, (E,))
+    _dev(offsets, "offsets", i32, (E + 1,))
+    _dev(perm, "perm", i32, (R,))
+    if inv is not None:
+        _dev(inv, "inv", i32, (R,))
     if maxvio is not None:
         _dev(maxvio, "maxvio", torch.float64, (1,))
     p = make_params(T, d, E, k, dt, score, 1, 1, "max", renormalize, route_scale)
