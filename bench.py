@@ -290,8 +290,14 @@ class Case:
                     offsets=self.offsets, perm=self.perm, inv=self.inv, maxvio=self.maxvio)
         xs, n = self.xs, self.n_copies
 
-        def step(i):  # one moe_route_dispatch call: gate, selection, dispatch
-            tda.route_dispatch(xs[i % n], W, k, workspace=ws, **outs, **rkw)
+        # the call's arguments are checked and marshalled once; each step
+        # passes the next copy of x (one moe_route_dispatch call: gate,
+        # selection, dispatch)
+        call = (None if w.hash_vocab else
+                tda.prepare_route_dispatch(xs[0], W, k, workspace=ws, **outs, **rkw))
+
+        def step(i):
+            call(xs[i % n])
 
         if w.capacity_factor:  # the dispatch ends with the capacity limit
             C = wl.capacity(w)
@@ -300,7 +306,7 @@ class Case:
             dropped = torch.empty(1, dtype=i32, device=dev)
 
             def step(i):  # noqa: F811 -- moe_route_dispatch, then the capacity limit
-                tda.route_dispatch(xs[i % n], W, k, workspace=ws, **outs, **rkw)
+                call(xs[i % n])
                 tda.dispatch_capacity(self.ids, E, C, self.offsets, self.inv, slot=slot,
                                       kept=kept, dropped=dropped)
 

@@ -82,6 +82,48 @@ def test_route_dispatch_matches_separate_calls_and_oracle(name, T, lpt, monkeypa
     check_dispatch(tuple(fused[2:]), oracle.dispatch(down(fused[0]), w.E))
 
 
+@pytest.mark.parametrize("name,T", [("qwen3_dynk", 1000), ("mixtral", None),
+                                    ("dsv3_grouped", 2000), ("gptoss_skew", 3000)])
+def test_prepared_call_matches_route_dispatch(name, T):
+    """A prepared moe_route_dispatch call (arguments marshalled once) equals
+    route_dispatch() bit for bit on two different inputs in a row, and on a
+    side stream; a wrong x is rejected on the host."""
+    w = wl.WORKLOADS[name]
+    inp = wl.make_inputs(w, T=T)
+    kw = route_kwargs(w)
+    if kw["group_score"] is None:
+        kw.pop("group_score")
+    kw.update(logit_bias=up(inp["logit_bias"]), select_bias=up(inp["select_bias"]),
+              k_per_token=up(inp["k_per_token"]))
+    x, W = up(inp["x"]), up(inp["W"])
+    x2 = torch.roll(x, 7, 0).contiguous()
+    mv = torch.zeros(1, dtype=torch.float64, device=DEV)
+    say("prepared call", name, T)
+    call = tda.prepare_route_dispatch(x, W, w.k, maxvio=mv, **kw)
+    for xi in (x, x2):
+        got = [t.clone() for t in call(xi) if t is not None]
+        mv_got = mv.clone()
+        mv_ref = torch.zeros(1, dtype=torch.float64, device=DEV)
+        ref = [t for t in tda.route_dispatch(xi, W, w.k, maxvio=mv_ref, **kw) if t is not None]
+        torch.cuda.synchronize()
+        n = int(ref[3][-1].item())
+        for i, (a, b) in enumerate(zip(got, ref)):
+            if i == 4:  # perm: the first offsets[E] entries are defined
+                a, b = a[:n], b[:n]
+            assert torch.equal(a, b), (name, i)
+        assert torch.equal(mv_got, mv_ref)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        got = [t.clone() for t in call(x) if t is not None]
+    torch.cuda.current_stream().wait_stream(s)
+    ref = [t for t in tda.route_dispatch(x, W, w.k, **kw) if t is not None]
+    torch.cuda.synchronize()
+    assert torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1])
+    with pytest.raises(ValueError):
+        call(x[:-1].contiguous())
+
+
 def test_route_dispatch_select_only_and_bad_k():
     rng = np.random.default_rng(5)
     T, E, K = 4096, 128, 16

@@ -311,7 +311,8 @@ def route_dispatch(x: Optional[torch.Tensor], W: Optional[torch.Tensor], k: int,
                    route_scale: float = 1.0, logits: Optional[torch.Tensor] = None,
                    E: Optional[int] = None, ids=None, weights=None, counts=None, offsets=None,
                    perm=None, inv=None, with_inv: bool = True, workspace=None, dev_err=None,
-                   k_per_group: int = 0, k_per_request=None, request_lens=None, maxvio=None):
+                   k_per_group: int = 0, k_per_request=None, request_lens=None, maxvio=None,
+                   _prepare: bool = False):
     """route() then dispatch() of its ids in one library call.  Returns
     (ids, weights, counts, offsets, perm, inv); ``workspace`` (256-byte
     aligned uint8 device tensor) is allocated when not given.  k_per_request
@@ -333,18 +334,61 @@ def route_dispatch(x: Optional[torch.Tensor], W: Optional[torch.Tensor], k: int,
         perm = torch.empty(R, dtype=torch.int32, device=device)
     if inv is None and with_inv:
         inv = torch.empty(R, dtype=torch.int32, device=device)
+    _dev(counts, "counts", torch.int32, (E_,))
+    _dev(offsets, "offsets", torch.int32, (E_ + 1,))
+    _dev(perm, "perm", torch.int32, (R,))
+    if inv is not None:
+        _dev(inv, "inv", torch.int32, (R,))
     if workspace is None:
         nbytes = int(lib().moe_route_dispatch_workspace_size(ctypes.byref(p)))
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
     if maxvio is not None:
         _dev(maxvio, "maxvio", torch.float64, (1,))
     ws_bytes = workspace.numel() * workspace.element_size()
-    _check(lib().moe_route_dispatch(ctypes.byref(p), _p(x), _p(W), _p(logit_bias),
-                                    _p(select_bias), _p(k_per_token), _p(logits), _p(ids),
-                                    _p(weights), _p(counts), _p(offsets), _p(perm), _p(inv),
-                                    _p(maxvio), _p(workspace), ws_bytes, _p(dev_err),
-                                    _stream(device)))
-    return ids, weights, counts, offsets, perm, inv
+    args = [ctypes.byref(p), _p(x), _p(W), _p(logit_bias), _p(select_bias), _p(k_per_token),
+            _p(logits), _p(ids), _p(weights), _p(counts), _p(offsets), _p(perm), _p(inv),
+            _p(maxvio), _p(workspace), ws_bytes, _p(dev_err), _stream(device)]
+    outs = (ids, weights, counts, offsets, perm, inv)
+    if _prepare:  # (arguments, outputs, the tensors the arguments point into)
+        return args, outs, (p, x, W, logit_bias, select_bias, k_per_token, logits, workspace,
+                            maxvio, dev_err)
+    _check(lib().moe_route_dispatch(*args))
+    return outs
+
+
+class PreparedRouteDispatch:
+    """moe_route_dispatch with every argument checked and marshalled once,
+    for loops that route batch after batch of the same shapes: ``call(x)``
+    routes and dispatches x (same shape, dtype and device as the x it was
+    prepared with) into the prepared outputs and returns them.  Only x and
+    the current stream change between calls; the per-call host work is a
+    few attribute checks and the library call."""
+
+    def __init__(self, x: torch.Tensor, W: torch.Tensor, k: int, **kw):
+        if x is None:
+            raise ValueError("a prepared call needs x (the gate input)")
+        self._args, self._outs, self._keep = route_dispatch(x, W, k, _prepare=True, **kw)
+        self._shape, self._dtype, self._device = tuple(x.shape), x.dtype, x.device
+        self._fn = lib().moe_route_dispatch
+
+    def __call__(self, x: torch.Tensor):
+        if (tuple(x.shape) != self._shape or x.dtype != self._dtype or
+                x.device != self._device or not x.is_contiguous()):
+            raise ValueError(f"x must be a contiguous {self._dtype} tensor of shape "
+                             f"{self._shape} on {self._device}")
+        args = self._args
+        args[1] = x.data_ptr()
+        args[17] = torch.cuda.current_stream(self._device).cuda_stream
+        _check(self._fn(*args))
+        return self._outs
+
+
+def prepare_route_dispatch(x: torch.Tensor, W: torch.Tensor, k: int,
+                           **kw) -> PreparedRouteDispatch:
+    """route_dispatch() checked and marshalled once (same keyword arguments;
+    pass the outputs and the workspace to keep them fixed); see
+    PreparedRouteDispatch."""
+    return PreparedRouteDispatch(x, W, k, **kw)
 
 
 NOALLOC_SCRATCH_BYTES = 64 << 20
