@@ -86,6 +86,11 @@ def kernel_work(w, T, R, R_valid, tile_bytes, producer_hist=False):
         "gate_select": (T * d * xb + E * d * xb + T * k * 8 + kt + tile_bytes, dense),
         # table rows, the k gathered logits, ids and weights
         "hash": (T * 4 + T * k * 4 + T * k * 4 + T * k * 8 + ph, 0.0),
+        # the table's ids alone: token ids and table rows read, ids written
+        "hash_ids": (T * 4 + T * k * 4 + T * k * 4, 0.0),
+        # the hash layer's k dot products: x and W read once, ids read, the
+        # k logits per token written once
+        "hash_dots": (T * d * xb + E * d * xb + T * k * 4 + T * k * 4, 2.0 * T * d * k),
         "select": (T * E * 4 + T * k * 8 + kt + ph, 0.0),
         # small batches: selection and the whole dispatch in one workgroup
         "select_dispatch": (T * E * 4 + T * k * 8 + kt + R * 4 + R_valid * 4 + E * 8, 0.0),

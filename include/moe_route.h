@@ -177,12 +177,15 @@ size_t moe_route_workspace_size(const moe_route_params* p);
  * l = x.W^T (+ logit_bias), renormalised over the row's valid slots when
  * p->renormalize, times route_scale; SOFTMAX needs renormalize = 1 (it then
  * equals SOFTMAX_TOPK).  With a workspace of at least
- * moe_route_hash_workspace_size(p) bytes the logits of every expert come
- * from the tiled gate contraction (as in moe_route; the fastest way, since
- * the rows of W are shared by many tokens); with none (NULL / 0) only the k
- * table experts' logits are computed, as k dot products per token.  When x
- * and W are NULL only ids are written (weights may be NULL).
- * Uses p->T, d, E, k, dtype, score, renormalize, route_scale.
+ * moe_route_hash_workspace_size(p) bytes: for bf16 x and W with k <= 8,
+ * E <= 768, d a multiple of 8 and 16-byte aligned rows, only the k logits
+ * a token needs are computed, as k dot products over slices of d with each
+ * slice of W held on chip (x read once; the workspace holds the per-slice
+ * partial sums, added in slice order); otherwise the logits of every expert
+ * come from the tiled gate contraction (as in moe_route).  With no
+ * workspace (NULL / 0) the k dot products are computed per token from W
+ * in memory.  When x and W are NULL only ids are written (weights may be
+ * NULL).  Uses p->T, d, E, k, dtype, score, renormalize, route_scale.
  */
 int32_t moe_route_hash(const moe_route_params* p, const int32_t* token_ids,
                        const int32_t* tid2eid, int32_t vocab, const void* x,
@@ -190,17 +193,17 @@ int32_t moe_route_hash(const moe_route_params* p, const int32_t* token_ids,
                        float* weights, void* workspace, size_t workspace_bytes,
                        int32_t* dev_err, void* stream);
 
-/* Bytes of device workspace moe_route_hash uses for the gate logits with
- * these parameters (16-byte aligned x and W assumed). */
+/* Bytes of device workspace moe_route_hash uses for its logits hand-off
+ * with these parameters (16-byte aligned x and W assumed). */
 size_t moe_route_hash_workspace_size(const moe_route_params* p);
 
 /*
- * moe_route_hash_dispatch -- moe_route_hash (with x and W, the tiled gate's
- * logits in the workspace) followed by moe_dispatch of its ids
- * (k_stride = p->k), with the results of the two calls (ferrox_moe docs,
- * route_hash; the dispatch as for moe_dispatch).  The hash kernel also
- * counts each tile's expert ids (tile histograms plus super-tile sums that
- * the gate kernel zeroes), so the dispatch is one placement kernel.
+ * moe_route_hash_dispatch -- moe_route_hash (with x and W and its
+ * workspace hand-off) followed by moe_dispatch of its ids (k_stride =
+ * p->k), with the results of the two calls (ferrox_moe docs, route_hash;
+ * the dispatch as for moe_dispatch).  The hash kernel also counts each
+ * tile's expert ids (tile histograms plus super-tile sums that the dot
+ * product or gate kernel zeroes), so the dispatch is one placement kernel.
  *   arguments    as for moe_route_hash and moe_dispatch (x and W required)
  *   workspace    256-byte aligned, at least
  *                moe_route_hash_dispatch_workspace_size(p) bytes; contents
@@ -440,7 +443,9 @@ int32_t moe_combine(int32_t T, int32_t k_stride, int32_t d, int32_t dtype, const
 #define MOE_STAGE_CAPACITY 9     /* capacity limit on a dispatch */
 #define MOE_STAGE_PERMUTE 10     /* send buffer rows */
 #define MOE_STAGE_EP_LAYOUT 11   /* per-rank send layout */
-#define MOE_NUM_STAGES 12
+#define MOE_STAGE_HASH_IDS 12    /* hash layer: the table's ids only */
+#define MOE_STAGE_HASH_DOTS 13   /* hash layer: k dot products per token */
+#define MOE_NUM_STAGES 14
 int32_t moe_profile_enable(int32_t enable);
 int32_t moe_profile_read(double* ms, int64_t* launches, int32_t n);
 

@@ -79,6 +79,55 @@ def test_hash_scores_ragged_and_duplicates(score, dtype, gate):
     assert np.max(np.abs(down(wts) - ref_w)) <= WTOL
 
 
+@pytest.mark.parametrize("T,d,E,k,bad,slice_", [
+    (77, 104, 24, 5, True, None),       # one slice wider than d (zero-filled), ragged T
+    (1000, 7168, 384, 6, False, None),  # DeepSeek-V4-like rows: 64 slices of 112 columns
+    (1000, 7168, 384, 6, False, "128"),  # 56 slices of 128 columns
+    (500, 1000, 500, 8, True, None),    # 56-column slices (E > 384), a partial last slice
+    (500, 1000, 500, 8, True, "64"),    # 64-column slices
+    (3001, 256, 768, 1, False, None),   # the largest E of the kernel, k = 1
+    (5, 64, 8, 8, True, None),          # fewer tokens than one wavefront's tile
+])
+def test_hash_dot_products_against_gate_path(T, d, E, k, bad, slice_, monkeypatch):
+    """The hash layer's k dot products per token (W slices on chip, partial
+    sums added in slice order) against the tiled gate contraction of every
+    expert (MOE_HASH_DENSE) and the oracle: ids bit for bit, weights within
+    2e-5 of each other and 1e-4 of the oracle, with a logit bias, duplicate
+    table entries, and bad token ids and table entries."""
+    rng = np.random.default_rng([T, d, E, k])
+    V = 97
+    tab = rng.integers(0, E, size=(V, k)).astype(np.int32)
+    tok = rng.integers(0, V, size=T).astype(np.int32)
+    if bad:
+        tok[rng.choice(T, min(T, 3), replace=False)] = [-1, V, V + 5][:min(T, 3)]
+        tab[rng.integers(0, V, 3), rng.integers(0, k, 3)] = [E, -3, E + 7]
+    x = wl.f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+    W = wl.f32_to_bf16_bits((rng.standard_normal((E, d)) / np.sqrt(d)).astype(np.float32))
+    lb = (0.3 * rng.standard_normal(E)).astype(np.float32)
+    say("hash dot products", T, d, E, k, bad, slice_)
+    if slice_:
+        monkeypatch.setenv("MOE_HASH_SLICE", slice_)
+    outs = []
+    for dense in (False, True):
+        if dense:
+            monkeypatch.setenv("MOE_HASH_DENSE", "1")
+        err = torch.zeros(1, dtype=torch.int32, device=DEV)
+        ids, wts = tda.route_hash(up(tok), up(tab), E, x=up(x), W=up(W), score="sqrt_softplus",
+                                  logit_bias=up(lb), route_scale=1.5, dev_err=err)
+        torch.cuda.synchronize()
+        outs.append((down(ids), down(wts), int(err.item())))
+    monkeypatch.delenv("MOE_HASH_DENSE")
+    (ia, wa, ea), (ib, wb, eb) = outs
+    ref_ids, nerr = oracle.hash_ids(tok, tab, E)
+    np.testing.assert_array_equal(ia, ref_ids)
+    np.testing.assert_array_equal(ib, ref_ids)
+    assert ea == eb == nerr
+    assert np.max(np.abs(wa - wb)) <= 2e-5
+    ref_w = oracle.weights_for_ids(oracle.gate(x, W, lb), ref_ids, score="sqrt_softplus",
+                                   route_scale=1.5)
+    assert np.max(np.abs(wa - ref_w)) <= WTOL
+
+
 def test_hash_arithmetic_table_and_errors():
     V, k, E = 1000, 6, 384
     tab = ((np.arange(V)[:, None] * k + np.arange(k)[None, :]) % E).astype(np.int32)

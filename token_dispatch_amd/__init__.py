@@ -41,7 +41,8 @@ PLAN_FIELDS = ("path", "gate_bm", "gate_bn", "gate_waves", "gate_splits", "gate_
                "gate_ring_depth", "gate_lds_bytes", "select_lanes", "select_experts_per_lane",
                "hist_tokens", "kernels")
 STAGES = ("gate", "select", "hash", "disp_hist", "disp_scan", "disp_scatter", "gate_select",
-          "select_dispatch", "combine", "capacity", "permute", "ep_layout")
+          "select_dispatch", "combine", "capacity", "permute", "ep_layout", "hash_ids",
+          "hash_dots")
 
 
 class MoeError(RuntimeError):

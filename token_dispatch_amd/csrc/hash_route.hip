@@ -6,14 +6,25 @@
 // Lanes j < k of a token's segment gather the table row (validating the
 // token id and every entry), then, when weights are wanted, lane j takes the
 // logit of slot j and the segment turns the k logits into weights with the
-// layer's score function.  The logits come either from the gate contraction
-// of every expert (the tiled matrix-core kernel, into a workspace; NSPLIT
-// K-split partial arrays added in order; several tokens per wavefront, and
-// optionally the dispatch's tile histograms) -- the k dot products alone
-// would re-read k rows of W from L2 for every token, about 64 times the
-// gate's L2 traffic at E = 384, k = 6 -- or, with no workspace, from k dot
-// products of length d computed here (one wavefront per token, the lanes
-// striding over d with 16-byte loads).
+// layer's score function.  The logits come from
+//  * the method's own work, k dot products per token (bf16, k <= 8, aligned
+//    rows): hash_dots_kernel holds one slice of W's columns for every
+//    expert in LDS and streams the matching slice of every token's x row
+//    through it, so x is read once from HBM and W once per workgroup; the
+//    per-slice partial dot products are added in slice order by the hash
+//    kernel (several tokens per wavefront, optionally the dispatch's tile
+//    histograms).  Gathering each token's k rows of W instead would re-read
+//    them from L2 for every token, about 64 times the dense gate's L2
+//    traffic at E = 384, k = 6;
+//  * or the gate contraction of every expert (the tiled matrix-core kernel,
+//    into a workspace; NSPLIT K-split partial arrays added in order) for the
+//    other shapes;
+//  * or, with no workspace, k dot products of length d computed here (one
+//    wavefront per token, the lanes striding over d with 16-byte loads).
+#include <algorithm>
+#include <cstdlib>
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 #include "select_core.h"
@@ -132,6 +143,167 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void hash_route_kernel(
   if (lane < k) weights[t * k + lane] = sel ? w * c.route_scale : 0.f;
 }
 
+// k dot products per token over one slice of d: the hash layer's own work.
+// Workgroup (s, c) holds columns [s*SL, s*SL + SL) of every expert's W row
+// in LDS (rows padded by one 16-byte piece to spread the banks) and passes
+// the tokens of chunk c through them in tiles of kDotWaves x 8 tokens,
+// wavefront w taking 8: its lanes load the 8 tokens' x slices (16-byte
+// pieces, PF tiles ahead, with the tokens' expert ids) into the wave's own
+// LDS rows, then lane (token i, slot j) forms part[s][t*k + j] = the slice's
+// share of x[t] . W[e_j] with bf16 dot2 instructions (fp32 accumulation).
+// Every x byte is read once and each workgroup reads one slice of W.  (One
+// token per lane with x in registers, reading only W from LDS, measured
+// slower: 97.7 against 65.8 us on the DeepSeek-V4-like shape.)  ids: the
+// table's experts, checked (-1 = none, whose partial is written as 0).
+// zero[0 .. zero_words): the super-tile sums the hash kernel adds into,
+// cleared here (each workgroup a slice) as the gate kernel does on the other
+// paths.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+// acc + the dot product of two 16-byte pieces of 8 bf16 (four dot2 steps).
+// The whole vectors are bit-cast: a bit cast of a subscripted 32-bit element
+// compiled to element 0 for every subscript with this compiler.
+__device__ __forceinline__ float dot8(u32x4_t a, u32x4_t b, float acc) {
+  const bf16x8_t p = __builtin_bit_cast(bf16x8_t, a), q = __builtin_bit_cast(bf16x8_t, b);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(p.s01, q.s01, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(p.s23, q.s23, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(p.s45, q.s45, acc, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(p.s67, q.s67, acc, false);
+}
+
+constexpr int kDotMaxK = 8;      // 8 lanes per token
+constexpr int kDotWaves = 16;
+constexpr int kDotLookahead = 3;  // tiles of x and ids in flight per wave
+
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (N > 0) {
+    static_for<N - 1>(f);
+    f(std::integral_constant<int, N - 1>());
+  }
+}
+
+template <int SL, int EMAX, int PF>
+__global__ __launch_bounds__(kDotWaves * kWave) void hash_dots_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ W,
+    const int32_t* __restrict__ ids, int T, int d, int E, int k, int chunk,
+    float* __restrict__ part, int32_t* __restrict__ zero, int zero_words) {
+  constexpr int PC = SL / 8;                     // 16-byte pieces per row slice
+  constexpr int PITCH = PC + 1;                  // pieces per LDS row
+  constexpr int TPW = kDotMaxK;                  // tokens per wave and tile
+  constexpr int TPT = kDotWaves * TPW;           // tokens per tile
+  constexpr int XP = TPW * PC;                   // x pieces per wave and tile
+  constexpr int XL = (XP + kWave - 1) / kWave;   // ... per lane
+  static_assert(SL % 8 == 0, "whole 16-byte pieces");
+  __shared__ u32x4_t wl[EMAX * PITCH];
+  __shared__ u32x4_t xl[kDotWaves][TPW * PITCH];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nblk = (int)(gridDim.x * gridDim.y);
+  const int blk = (int)(blockIdx.y * gridDim.x + blockIdx.x);
+  if (zero_words > 0) {
+    const int per = (zero_words + nblk - 1) / nblk;
+    const int beg = blk * per, end = min(beg + per, zero_words);
+    for (int i = beg + tid; i < end; i += kDotWaves * kWave) zero[i] = 0;
+  }
+  const int col0 = (int)blockIdx.x * SL;
+  const int64_t c0 = (int64_t)blockIdx.y * chunk;
+  const int64_t c1 = min((int64_t)T, c0 + chunk);
+  const int ntiles = c0 < c1 ? (int)((c1 - c0 + TPT - 1) / TPT) : 0;
+  const int64_t Rk = (int64_t)T * k;
+  float* __restrict__ out = part + (int64_t)blockIdx.x * Rk;
+  const u32x4_t z4 = {0u, 0u, 0u, 0u};
+
+  // this wave's first token of tile i; lane (token i8, slot j)
+  auto tok0 = [&](int i) { return c0 + (int64_t)i * TPT + wave * TPW; };
+  const int i8 = lane >> 3, j = lane & 7;
+  auto load_x = [&](int i, u32x4_t (&r)[XL]) {
+    const int64_t b = tok0(i);
+#pragma unroll
+    for (int q = 0; q < XL; ++q) {
+      const int pi = q * kWave + lane;
+      const int64_t t = b + pi / PC;
+      const int col = col0 + (pi % PC) * 8;
+      r[q] = (pi < XP && i < ntiles && t < c1 && col < d)
+                 ? *reinterpret_cast<const u32x4_t*>(x + t * d + col)
+                 : z4;
+    }
+  };
+  auto load_e = [&](int i) {
+    const int64_t t = tok0(i) + i8;
+    return (i < ntiles && j < k && t < c1) ? ids[t * k + j] : -1;
+  };
+
+  // tiles 0 .. PF-1 in flight while the W slice is loaded; a ring of PF + 1
+  // register slots
+  constexpr int RS = PF + 1;
+  u32x4_t xr[RS][XL];
+  int er[RS];
+  static_for<PF>([&](auto q) {
+    constexpr int Q = decltype(q)::value;
+    load_x(Q, xr[Q]);
+    er[Q] = load_e(Q);
+  });
+  for (int i = tid; i < E * PC; i += kDotWaves * kWave) {
+    const int e = i / PC, pc = i % PC, col = col0 + pc * 8;
+    wl[e * PITCH + pc] =
+        col < d ? *reinterpret_cast<const u32x4_t*>(W + (int64_t)e * d + col) : z4;
+  }
+  __syncthreads();
+
+  u32x4_t* xw = xl[wave];
+  // tile i from ring slot Q; the loads of tile i + PF go to slot (Q + PF) % RS
+  auto step = [&](int i, auto q) {
+    constexpr int Q = decltype(q)::value;
+    constexpr int N = (Q + PF) % RS;
+    load_x(i + PF, xr[N]);
+    er[N] = load_e(i + PF);
+#pragma unroll
+    for (int r = 0; r < XL; ++r) {
+      const int pi = r * kWave + lane;
+      if (pi < XP) xw[(pi / PC) * PITCH + pi % PC] = xr[Q][r];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int64_t t = tok0(i) + i8;
+    const int e = er[Q];
+    if (j < k && t < c1) {
+      float acc = 0.f;
+      if (e >= 0 && e < E) {
+        const u32x4_t* xv = xw + i8 * PITCH;
+        const u32x4_t* wv = wl + e * PITCH;
+#pragma unroll
+        for (int pc = 0; pc < PC; ++pc) acc = dot8(xv[pc], wv[pc], acc);
+      }
+      out[t * k + j] = acc;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();  // the x rows are rewritten by the next tile
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  for (int i = 0; i < ntiles; i += RS)
+    static_for<RS>([&](auto q) {
+      if (i + decltype(q)::value < ntiles) step(i + decltype(q)::value, q);
+    });
+}
+
+// The table's expert ids, one thread per route (checked; -1 for a bad token
+// id or entry, no error count: the hash kernel that follows counts them).
+__global__ __launch_bounds__(256) void hash_ids_kernel(const int32_t* __restrict__ token_ids,
+                                                       const int32_t* __restrict__ tid2eid,
+                                                       int32_t vocab, int64_t R, int k, int E,
+                                                       int32_t* __restrict__ ids) {
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (r >= R) return;
+  const int v = token_ids[r / k];
+  int e = -1;
+  if (v >= 0 && v < vocab) {
+    e = tid2eid[(int64_t)v * k + r % k];
+    if (e < 0 || e >= E) e = -1;
+  }
+  ids[r] = e;
+}
+
 // Hash routing from the gate's logits with several tokens per wavefront: a
 // segment of SEG lanes (SEG = 4, 8, 16 or 64, the smallest >= k) routes one
 // token, lane j < k taking slot j; WPB wavefronts per workgroup.  The
@@ -141,12 +313,16 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void hash_route_kernel(
 // their expert ids are counted with ballot peer masks into hist[block][E]
 // and added into super_sum[block / super_S][E] (zeroed by the gate kernel
 // of the same call) -- the dispatch then needs only its placement kernel.
+// NSPLIT == 0: the logits are the sum, in slice order, of n_parts arrays of
+// per-slot partial dot products part[s][t * k + j] (split_stride = T * k
+// apart, hash_dots_kernel), plus logit_bias[e].
 template <int SEG, int NSPLIT, int WPB, bool HIST, int NB>
 __global__ __launch_bounds__(WPB * kWave) void hash_route_tiles_kernel(
     RouteCfg c, const int32_t* __restrict__ token_ids, const int32_t* __restrict__ tid2eid,
-    int32_t vocab, const float* __restrict__ logits, int64_t split_stride,
-    int32_t* __restrict__ ids, float* __restrict__ weights, int32_t* __restrict__ dev_err,
-    hist_t* __restrict__ hist, int32_t* __restrict__ super_sum, int super_S) {
+    int32_t vocab, const float* __restrict__ logits, int64_t split_stride, int n_parts,
+    const float* __restrict__ logit_bias, int32_t* __restrict__ ids,
+    float* __restrict__ weights, int32_t* __restrict__ dev_err, hist_t* __restrict__ hist,
+    int32_t* __restrict__ super_sum, int super_S) {
   constexpr int TPW = kWave / SEG;
   using S = sel::Seg<SEG>;
   __shared__ int32_t whist[HIST ? WPB : 1][HIST ? 1024 : 1];
@@ -167,13 +343,28 @@ __global__ __launch_bounds__(WPB * kWave) void hash_route_tiles_kernel(
     }
   }
   float my_l = 0.f;
-  if (e >= 0) {
-    float pv[NSPLIT];
+  if constexpr (NSPLIT > 0) {
+    if (e >= 0) {
+      float pv[NSPLIT];
 #pragma unroll
-    for (int sp = 0; sp < NSPLIT; ++sp) pv[sp] = logits[sp * split_stride + t * E + e];
-    my_l = pv[0];
+      for (int sp = 0; sp < NSPLIT; ++sp) pv[sp] = logits[sp * split_stride + t * E + e];
+      my_l = pv[0];
 #pragma unroll
-    for (int sp = 1; sp < NSPLIT; ++sp) my_l += pv[sp];
+      for (int sp = 1; sp < NSPLIT; ++sp) my_l += pv[sp];
+    }
+  } else if (e >= 0) {
+    constexpr int B = 16;  // loads in flight
+    const float* src = logits + t * k + sl;
+    for (int s0 = 0; s0 < n_parts; s0 += B) {
+      float pv[B];
+#pragma unroll
+      for (int i = 0; i < B; ++i)
+        pv[i] = s0 + i < n_parts ? src[(int64_t)(s0 + i) * split_stride] : 0.f;
+#pragma unroll
+      for (int i = 0; i < B; ++i)
+        if (s0 + i < n_parts) my_l += pv[i];
+    }
+    if (logit_bias) my_l += logit_bias[e];
   }
   // errors: bad table entries, and a bad token id once per token
   const int nerr = __popcll(__ballot(bad_slot)) + __popcll(__ballot(tok_in && !tok_ok && sl == 0));
@@ -220,32 +411,35 @@ constexpr int kHashTileWaves = 4;
 
 template <int SEG, int NS, bool HIST>
 hipError_t launch_tiles_nb(const RouteCfg& c, const int32_t* tok, const int32_t* tab,
-                           int32_t vocab, const float* logits, int64_t stride, int32_t* ids,
-                           float* w, int32_t* err, hist_t* hist, int32_t* super_sum, int S,
-                           hipStream_t s) {
+                           int32_t vocab, const float* logits, int64_t stride, int n_parts,
+                           const float* lb, int32_t* ids, float* w, int32_t* err, hist_t* hist,
+                           int32_t* super_sum, int S, hipStream_t s) {
   constexpr int tpb = kHashTileWaves * (kWave / SEG);
   const dim3 grid((uint32_t)(((int64_t)c.T + tpb - 1) / tpb));
   const dim3 block(kHashTileWaves * kWave);
   auto go = [&](auto kernel) {
-    return launch(kStageHash, kernel, grid, block, s, c, tok, tab, vocab, logits, stride, ids,
-                  w, err, hist, super_sum, S);
+    return launch(kStageHash, kernel, grid, block, s, c, tok, tab, vocab, logits, stride,
+                  n_parts, lb, ids, w, err, hist, super_sum, S);
   };
   if (c.E <= 128) return go(hash_route_tiles_kernel<SEG, NS, kHashTileWaves, HIST, 7>);
   if (c.E <= 256) return go(hash_route_tiles_kernel<SEG, NS, kHashTileWaves, HIST, 8>);
   return go(hash_route_tiles_kernel<SEG, NS, kHashTileWaves, HIST, 10>);
 }
 
+// splits > 0: the gate's K-split arrays of every expert's logit; splits ==
+// 0: n_parts arrays of per-slot partial dot products (+ logit bias lb).
 template <int SEG>
 hipError_t launch_tiles_seg(const RouteCfg& c, const int32_t* tok, const int32_t* tab,
                             int32_t vocab, const float* logits, int32_t splits, int64_t stride,
-                            int32_t* ids, float* w, int32_t* err, hist_t* hist,
-                            int32_t* super_sum, int S, hipStream_t s) {
-#define MOE_HT(NS_)                                                                           \
-  if (splits == NS_)                                                                          \
-    return hist ? launch_tiles_nb<SEG, NS_, true>(c, tok, tab, vocab, logits, stride, ids, w,  \
-                                                  err, hist, super_sum, S, s)                 \
-                : launch_tiles_nb<SEG, NS_, false>(c, tok, tab, vocab, logits, stride, ids, w, \
-                                                   err, hist, super_sum, S, s);
+                            int n_parts, const float* lb, int32_t* ids, float* w, int32_t* err,
+                            hist_t* hist, int32_t* super_sum, int S, hipStream_t s) {
+#define MOE_HT(NS_)                                                                            \
+  if (splits == NS_)                                                                           \
+    return hist ? launch_tiles_nb<SEG, NS_, true>(c, tok, tab, vocab, logits, stride, n_parts,  \
+                                                  lb, ids, w, err, hist, super_sum, S, s)       \
+                : launch_tiles_nb<SEG, NS_, false>(c, tok, tab, vocab, logits, stride, n_parts, \
+                                                   lb, ids, w, err, hist, super_sum, S, s);
+  MOE_HT(0)
   MOE_HT(1)
   MOE_HT(2)
   MOE_HT(4)
@@ -303,13 +497,22 @@ hipError_t launch_hash_route(const RouteCfg& c, int32_t dtype,
 
 int hash_tile_tokens(int32_t k) { return kHashTileWaves * (kWave / hash_seg(k)); }
 
+hipError_t launch_hash_ids(const RouteCfg& c, const int32_t* token_ids, const int32_t* tid2eid,
+                           int32_t vocab, int32_t* ids, hipStream_t stream) {
+  if (c.T == 0) return hipSuccess;
+  const int64_t R = (int64_t)c.T * c.k;
+  return launch(kStageHashIds, hash_ids_kernel, dim3((uint32_t)((R + 255) / 256)), dim3(256),
+                stream, token_ids, tid2eid, vocab, R, c.k, c.E, ids);
+}
+
 hipError_t launch_hash_tiles(const RouteCfg& c, const int32_t* token_ids,
                              const int32_t* tid2eid, int32_t vocab, const float* logits,
-                             int32_t splits, int64_t split_stride, int32_t* ids, float* weights,
+                             int32_t splits, int64_t split_stride, int32_t n_parts,
+                             const float* logit_bias, int32_t* ids, float* weights,
                              int32_t* dev_err, hist_t* hist, int32_t* super_sum,
                              hipStream_t stream) {
   if (c.T == 0) return hipSuccess;
-  if (c.E > 1024 || c.k > 32) return hipErrorInvalidValue;
+  if (c.E > 1024 || c.k > 32 || (splits == 0 && n_parts < 1)) return hipErrorInvalidValue;
   int S = 1;
   if (hist) {
     const int64_t R = (int64_t)c.T * c.k;
@@ -317,17 +520,70 @@ hipError_t launch_hash_tiles(const RouteCfg& c, const int32_t* token_ids,
     if (!dispatch_super_ok(R, c.E, tr)) return hipErrorInvalidValue;
     S = dispatch_super_size(R, tr);
   }
+  const float* lb = splits == 0 ? logit_bias : nullptr;
   switch (hash_seg(c.k)) {
     case 4: return launch_tiles_seg<4>(c, token_ids, tid2eid, vocab, logits, splits, split_stride,
-                                       ids, weights, dev_err, hist, super_sum, S, stream);
+                                       n_parts, lb, ids, weights, dev_err, hist, super_sum, S,
+                                       stream);
     case 8: return launch_tiles_seg<8>(c, token_ids, tid2eid, vocab, logits, splits, split_stride,
-                                       ids, weights, dev_err, hist, super_sum, S, stream);
+                                       n_parts, lb, ids, weights, dev_err, hist, super_sum, S,
+                                       stream);
     case 16: return launch_tiles_seg<16>(c, token_ids, tid2eid, vocab, logits, splits,
-                                         split_stride, ids, weights, dev_err, hist, super_sum,
-                                         S, stream);
+                                         split_stride, n_parts, lb, ids, weights, dev_err, hist,
+                                         super_sum, S, stream);
     default: return launch_tiles_seg<64>(c, token_ids, tid2eid, vocab, logits, splits,
-                                         split_stride, ids, weights, dev_err, hist, super_sum,
-                                         S, stream);
+                                         split_stride, n_parts, lb, ids, weights, dev_err, hist,
+                                         super_sum, S, stream);
+  }
+}
+
+// The slice width of hash_dots_kernel for E experts (the W slice of every
+// expert fits the LDS beside the x rows), or 0 when the kernel does not
+// apply: bf16, k <= 8, E <= 768, d a multiple of 8, 16-byte aligned rows.
+// 112 columns (64 slices of a 7168-wide row, one workgroup per CU) measured
+// as fast as 128 (whole 128-byte lines per token, 56 slices).
+int hash_dot_slice(const RouteCfg& c, int32_t dtype, bool aligned) {
+  if (dtype != 1 || !aligned || c.k > kDotMaxK || c.d % 8 != 0 || c.E > 768 ||
+      std::getenv("MOE_HASH_DENSE"))
+    return 0;
+  const bool small = c.E <= 384;
+  if (const char* env = std::getenv("MOE_HASH_SLICE")) {  // tuning: 112/128 or 56/64
+    const int v = std::atoi(env);
+    if (small && (v == 112 || v == 128)) return v;
+    if (!small && (v == 56 || v == 64)) return v;
+  }
+  return small ? 112 : 56;
+}
+
+int hash_dot_slices(const RouteCfg& c, int32_t dtype, bool aligned) {
+  const int sl = hash_dot_slice(c, dtype, aligned);
+  return sl ? (c.d + sl - 1) / sl : 0;
+}
+
+hipError_t launch_hash_dots(const RouteCfg& c, int32_t dtype, const void* x, const void* W,
+                            const int32_t* ids, float* part, int32_t* zero, int32_t zero_words,
+                            hipStream_t stream) {
+  const bool aligned = reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
+                       reinterpret_cast<uintptr_t>(W) % 16 == 0;
+  const int sl = hash_dot_slice(c, dtype, aligned);
+  if (sl == 0) return hipErrorInvalidValue;
+  if (c.T == 0) return hipSuccess;
+  const int ns = (c.d + sl - 1) / sl;
+  // at most one workgroup per CU (the LDS holds one) over slices x token
+  // chunks: a second round of a few workgroups would double the time
+  constexpr int kDotCus = 256;
+  const int chunks = std::max(1, std::min((c.T + 255) / 256, kDotCus / ns));
+  const int chunk = (c.T + chunks - 1) / chunks;
+  const dim3 grid((uint32_t)ns, (uint32_t)chunks), block(kDotWaves * kWave);
+  auto go = [&](auto kernel) {
+    return launch(kStageHashDots, kernel, grid, block, stream, (const uint16_t*)x,
+                  (const uint16_t*)W, ids, c.T, c.d, c.E, c.k, chunk, part, zero, zero_words);
+  };
+  switch (sl) {
+    case 128: return go(hash_dots_kernel<128, 384, kDotLookahead>);
+    case 112: return go(hash_dots_kernel<112, 384, kDotLookahead>);
+    case 64: return go(hash_dots_kernel<64, 768, kDotLookahead>);
+    default: return go(hash_dots_kernel<56, 768, kDotLookahead>);
   }
 }
 

@@ -22,7 +22,9 @@ enum Stage : int32_t {
   kStageCapacity = 9,
   kStagePermute = 10,
   kStageEpLayout = 11,
-  kNumStages = 12
+  kStageHashIds = 12,
+  kStageHashDots = 13,
+  kNumStages = 14
 };
 
 // Per-kernel timing (moe_profile_enable): the start/stop events of the next
@@ -154,17 +156,35 @@ hipError_t launch_hash_route(const RouteCfg& c, int32_t dtype,
                              int64_t split_stride, int32_t* ids, float* weights,
                              int32_t* dev_err, hipStream_t stream);
 
-// Hash routing with several tokens per wavefront, weights from the gate's
-// logits (the sum of `splits` arrays [T][E], split_stride floats apart).
-// With hist (super_sum zeroed beforehand): each workgroup's
-// hash_tile_tokens(k) tokens are one dispatch tile; the kernel writes the
-// tile's histogram and adds it into super_sum (as launch_select does).
+// Hash routing with several tokens per wavefront.  Weights from the gate's
+// logits (splits > 0: the sum of `splits` arrays [T][E], split_stride floats
+// apart, logit bias included), or (splits == 0) from n_parts arrays of
+// per-slot partial dot products [T*k] (split_stride = T*k floats apart,
+// launch_hash_dots) plus logit_bias.  With hist (super_sum zeroed
+// beforehand): each workgroup's hash_tile_tokens(k) tokens are one dispatch
+// tile; the kernel writes the tile's histogram and adds it into super_sum
+// (as launch_select does).
 int hash_tile_tokens(int32_t k);
 hipError_t launch_hash_tiles(const RouteCfg& c, const int32_t* token_ids,
                              const int32_t* tid2eid, int32_t vocab, const float* logits,
-                             int32_t splits, int64_t split_stride, int32_t* ids, float* weights,
+                             int32_t splits, int64_t split_stride, int32_t n_parts,
+                             const float* logit_bias, int32_t* ids, float* weights,
                              int32_t* dev_err, hist_t* hist, int32_t* super_sum,
                              hipStream_t stream);
+
+// The table's expert ids only (checked: -1 for a bad token id or entry; no
+// error count), for launch_hash_dots.
+hipError_t launch_hash_ids(const RouteCfg& c, const int32_t* token_ids, const int32_t* tid2eid,
+                           int32_t vocab, int32_t* ids, hipStream_t stream);
+
+// The k logits a hash layer needs, as k dot products per token over slices
+// of d (bf16 x and W, k <= 8, E <= 768, d % 8 == 0, 16-byte aligned rows:
+// hash_dot_slices > 0): part[s][t*k + j] = slice s's share of x[t] . W[ids[t*k
+// + j]] (0 for ids < 0); zero[0 .. zero_words) is cleared.
+int hash_dot_slices(const RouteCfg& c, int32_t dtype, bool aligned);
+hipError_t launch_hash_dots(const RouteCfg& c, int32_t dtype, const void* x, const void* W,
+                            const int32_t* ids, float* part, int32_t* zero, int32_t zero_words,
+                            hipStream_t stream);
 
 // Dispatch placement from per-tile histograms already in tile_hist
 // ([ceil(R / tile_routes)][E] hist_t, tile-major), when dispatch_hist_ok

@@ -290,6 +290,15 @@ size_t route_ws_bytes(const moe_route_params* p) {
 
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
+// The hash layer's hand-off: the per-slice partial dot products when the
+// dot-product kernel applies (aligned rows assumed, as for route_ws_bytes),
+// else the gate's logits of every expert.
+size_t hash_ws_bytes(const moe_route_params* p) {
+  const int ns = moe::hash_dot_slices(to_cfg(p), p->dtype, true);
+  if (ns > 0) return (size_t)ns * p->T * p->k * sizeof(float);
+  return route_ws_bytes(p);
+}
+
 // How moe_route_dispatch counts its routes for the dispatch.
 //   kOwn:   the dispatch's own kernels (histogram, [scan,] placement);
 //   kTiles: the routing kernels write each tile's histogram (tiles of
@@ -507,12 +516,15 @@ int32_t check_hash_call(const moe_route_params* p, const int32_t* token_ids,
   return MOE_OK;
 }
 
-// Hash routing on validated arguments, T > 0.  With a workspace holding the
-// gate's hand-off: the tiled gate contraction, then the multi-token hash
-// kernel (with `hist`: also the dispatch's tile histograms and the
-// super-tile sums the gate kernel zeroes); else the one-token-per-wavefront
-// kernel (k dot products per token, or ids only).  Sets *used_tiles when the
-// tile histograms were written.
+// Hash routing on validated arguments, T > 0.  With a workspace: when the
+// shapes allow (hash_dot_slices > 0) the method's own work -- the table's
+// ids, k dot products per token over slices of d (partials in the
+// workspace), then the multi-token hash kernel adding them; otherwise the
+// tiled gate contraction of every expert into the workspace, then the
+// multi-token hash kernel (with `hist`: also the dispatch's tile histograms
+// and the super-tile sums the dots or gate kernel zeroes).  With no
+// workspace: the one-token-per-wavefront kernel (k dot products per token,
+// or ids only).  Sets *used_tiles when the tile histograms were written.
 int32_t hash_core(const moe_route_params* p, const int32_t* token_ids, const int32_t* tid2eid,
                   int32_t vocab, const void* x, const void* W, const float* logit_bias,
                   int32_t* ids, float* weights, void* workspace, size_t workspace_bytes,
@@ -525,6 +537,24 @@ int32_t hash_core(const moe_route_params* p, const int32_t* token_ids, const int
   if (!ids_only && workspace) {
     const bool aligned = reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
                          reinterpret_cast<uintptr_t>(W) % 16 == 0;
+    const moe::RouteCfg c = to_cfg(p);
+    const int ns = moe::hash_dot_slices(c, p->dtype, aligned);
+    const int64_t Rk = (int64_t)p->T * p->k;
+    if (ns > 0 && workspace_bytes >= (size_t)ns * Rk * sizeof(float)) {
+      float* part = static_cast<float*>(workspace);
+      const bool tiles = hist && super_sum;
+      e = moe::launch_hash_ids(c, token_ids, tid2eid, vocab, ids, s);
+      if (e != hipSuccess) return device_fail(e, "hash ids launch");
+      e = moe::launch_hash_dots(c, p->dtype, x, W, ids, part, tiles ? super_sum : nullptr,
+                                tiles ? super_words : 0, s);
+      if (e != hipSuccess) return device_fail(e, "hash dot products launch");
+      e = moe::launch_hash_tiles(c, token_ids, tid2eid, vocab, part, 0, Rk, ns, logit_bias,
+                                 ids, weights, dev_err, tiles ? hist : nullptr,
+                                 tiles ? super_sum : nullptr, s);
+      if (e != hipSuccess) return device_fail(e, "hash route launch");
+      if (used_tiles) *used_tiles = tiles;
+      return MOE_OK;
+    }
     const size_t te = (size_t)p->T * p->E * sizeof(float);
     moe::GatePlan g = moe::plan_gate(p->T, p->d, p->E, p->dtype, aligned, true);
     if (workspace_bytes < te * g.splits)
@@ -535,8 +565,8 @@ int32_t hash_core(const moe_route_params* p, const int32_t* token_ids, const int
       e = moe::launch_gate_gemm(g, p->dtype, x, W, logit_bias, lg, p->T, p->d, p->E, s,
                                 tiles ? super_sum : nullptr, tiles ? super_words : 0);
       if (e != hipSuccess) return device_fail(e, "gate GEMM launch");
-      e = moe::launch_hash_tiles(to_cfg(p), token_ids, tid2eid, vocab, lg, g.splits,
-                                 (int64_t)p->T * p->E, ids, weights, dev_err,
+      e = moe::launch_hash_tiles(c, token_ids, tid2eid, vocab, lg, g.splits,
+                                 (int64_t)p->T * p->E, 0, nullptr, ids, weights, dev_err,
                                  tiles ? hist : nullptr, tiles ? super_sum : nullptr, s);
       if (e != hipSuccess) return device_fail(e, "hash route launch");
       if (used_tiles) *used_tiles = tiles;
@@ -590,7 +620,7 @@ size_t moe_route_hash_dispatch_workspace_size(const moe_route_params* p) {
   const DispPlan d = hash_disp_plan(p);
   const size_t disp = std::max(disp_ws_bytes(p, d),
                                moe::dispatch_workspace_bytes(R, p->E));
-  return align256(route_ws_bytes(p)) + disp;
+  return align256(hash_ws_bytes(p)) + disp;
 }
 
 int32_t moe_route_hash_dispatch(const moe_route_params* p, const int32_t* token_ids,
@@ -621,7 +651,7 @@ int32_t moe_route_hash_dispatch(const moe_route_params* p, const int32_t* token_
     if (e != hipSuccess) return device_fail(e, "dispatch launch");
     return MOE_OK;
   }
-  const size_t route = align256(route_ws_bytes(p));
+  const size_t route = align256(hash_ws_bytes(p));
   void* disp_ws = static_cast<char*>(workspace) + route;
   const DispPlan dp = hash_disp_plan(p);
   moe::hist_t* hist = dp.mode == kSuper ? static_cast<moe::hist_t*>(disp_ws) : nullptr;
@@ -646,7 +676,7 @@ int32_t moe_route_hash_dispatch(const moe_route_params* p, const int32_t* token_
 size_t moe_route_hash_workspace_size(const moe_route_params* p) {
   if (check_common(p, true) != MOE_OK || p->T == 0) return 0;
   if ((int64_t)p->T * p->E > kI32Max) return 0;
-  return route_ws_bytes(p);
+  return hash_ws_bytes(p);
 }
 
 size_t moe_dispatch_workspace_size(int32_t T, int32_t k_stride, int32_t E) {
