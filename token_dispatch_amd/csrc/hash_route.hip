@@ -23,7 +23,9 @@
 //    wavefront per token, the lanes striding over d with 16-byte loads).
 #include <algorithm>
 #include <cstdlib>
+#include <mutex>
 #include <type_traits>
+#include <unordered_map>
 
 #include "device_common.h"
 #include "kernels.h"
@@ -146,15 +148,18 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void hash_route_kernel(
 // k dot products per token over one slice of d: the hash layer's own work.
 // Workgroup (s, c) holds columns [s*SL, s*SL + SL) of every expert's W row
 // in LDS (rows padded by one 16-byte piece to spread the banks) and passes
-// the tokens of chunk c through them in tiles of kDotWaves x 8 tokens,
-// wavefront w taking 8: its lanes load the 8 tokens' x slices (16-byte
-// pieces, PF tiles ahead, with the tokens' expert ids) into the wave's own
-// LDS rows, then lane (token i, slot j) forms part[s][t*k + j] = the slice's
-// share of x[t] . W[e_j] with bf16 dot2 instructions (fp32 accumulation).
+// the tokens of chunk c through them in tiles, each wavefront taking 64 / L
+// tokens: its lanes load those tokens' x slices (16-byte pieces, PF tiles
+// ahead, with the tokens' expert ids) into the wave's own LDS rows, then
+// each of the token's L lanes forms part[s][t*k + j] = the slice's share of
+// x[t] . W[e_j] for its slots j with bf16 dot2 instructions (fp32
+// accumulation), reading each x piece once for all of its slots.
 // Every x byte is read once and each workgroup reads one slice of W.  (One
 // token per lane with x in registers, reading only W from LDS, measured
 // slower: 97.7 against 65.8 us on the DeepSeek-V4-like shape.)  ids: the
-// table's experts, checked (-1 = none, whose partial is written as 0).
+// table's experts, checked (-1 = none, whose partial is written as 0), from
+// a pass of their own: gathering table rows here, in every slice's
+// workgroup, measured 72.4 against 64.4 + 4.2 us.
 // zero[0 .. zero_words): the super-tile sums the hash kernel adds into,
 // cleared here (each workgroup a slice) as the gate kernel does on the other
 // paths.
@@ -171,9 +176,7 @@ __device__ __forceinline__ float dot8(u32x4_t a, u32x4_t b, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(p.s67, q.s67, acc, false);
 }
 
-constexpr int kDotMaxK = 8;      // 8 lanes per token
-constexpr int kDotWaves = 16;
-constexpr int kDotLookahead = 3;  // tiles of x and ids in flight per wave
+constexpr int kDotMaxK = 8;
 
 template <int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -183,27 +186,31 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-template <int SL, int EMAX, int PF>
-__global__ __launch_bounds__(kDotWaves * kWave) void hash_dots_kernel(
+// L lanes per token (each taking kDotMaxK / L consecutive slots, reusing
+// each x piece it reads for all of them), NW wavefronts, PF tiles of x and
+// ids in flight per wavefront.
+template <int SL, int EMAX, int L, int NW, int PF>
+__global__ __launch_bounds__(NW * kWave) void hash_dots_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ W,
     const int32_t* __restrict__ ids, int T, int d, int E, int k, int chunk,
     float* __restrict__ part, int32_t* __restrict__ zero, int zero_words) {
   constexpr int PC = SL / 8;                     // 16-byte pieces per row slice
   constexpr int PITCH = PC + 1;                  // pieces per LDS row
-  constexpr int TPW = kDotMaxK;                  // tokens per wave and tile
-  constexpr int TPT = kDotWaves * TPW;           // tokens per tile
+  constexpr int TPW = kWave / L;                 // tokens per wave and tile
+  constexpr int SPL = kDotMaxK / L;              // slots per lane
+  constexpr int TPT = NW * TPW;                  // tokens per tile
   constexpr int XP = TPW * PC;                   // x pieces per wave and tile
   constexpr int XL = (XP + kWave - 1) / kWave;   // ... per lane
-  static_assert(SL % 8 == 0, "whole 16-byte pieces");
+  static_assert(SL % 8 == 0 && kDotMaxK % L == 0, "shapes");
   __shared__ u32x4_t wl[EMAX * PITCH];
-  __shared__ u32x4_t xl[kDotWaves][TPW * PITCH];
+  __shared__ u32x4_t xl[NW][TPW * PITCH];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nblk = (int)(gridDim.x * gridDim.y);
   const int blk = (int)(blockIdx.y * gridDim.x + blockIdx.x);
   if (zero_words > 0) {
     const int per = (zero_words + nblk - 1) / nblk;
     const int beg = blk * per, end = min(beg + per, zero_words);
-    for (int i = beg + tid; i < end; i += kDotWaves * kWave) zero[i] = 0;
+    for (int i = beg + tid; i < end; i += NW * kWave) zero[i] = 0;
   }
   const int col0 = (int)blockIdx.x * SL;
   const int64_t c0 = (int64_t)blockIdx.y * chunk;
@@ -213,9 +220,9 @@ __global__ __launch_bounds__(kDotWaves * kWave) void hash_dots_kernel(
   float* __restrict__ out = part + (int64_t)blockIdx.x * Rk;
   const u32x4_t z4 = {0u, 0u, 0u, 0u};
 
-  // this wave's first token of tile i; lane (token i8, slot j)
+  // this wave's first token of tile i; lane (token it, slots j0 .. j0+SPL-1)
   auto tok0 = [&](int i) { return c0 + (int64_t)i * TPT + wave * TPW; };
-  const int i8 = lane >> 3, j = lane & 7;
+  const int it = lane / L, j0 = (lane % L) * SPL;
   auto load_x = [&](int i, u32x4_t (&r)[XL]) {
     const int64_t b = tok0(i);
 #pragma unroll
@@ -228,22 +235,24 @@ __global__ __launch_bounds__(kDotWaves * kWave) void hash_dots_kernel(
                  : z4;
     }
   };
-  auto load_e = [&](int i) {
-    const int64_t t = tok0(i) + i8;
-    return (i < ntiles && j < k && t < c1) ? ids[t * k + j] : -1;
+  auto load_e = [&](int i, int (&ev)[SPL]) {
+    const int64_t t = tok0(i) + it;
+#pragma unroll
+    for (int m = 0; m < SPL; ++m)
+      ev[m] = (i < ntiles && j0 + m < k && t < c1) ? ids[t * k + j0 + m] : -1;
   };
 
   // tiles 0 .. PF-1 in flight while the W slice is loaded; a ring of PF + 1
   // register slots
   constexpr int RS = PF + 1;
   u32x4_t xr[RS][XL];
-  int er[RS];
+  int er[RS][SPL];
   static_for<PF>([&](auto q) {
     constexpr int Q = decltype(q)::value;
     load_x(Q, xr[Q]);
-    er[Q] = load_e(Q);
+    load_e(Q, er[Q]);
   });
-  for (int i = tid; i < E * PC; i += kDotWaves * kWave) {
+  for (int i = tid; i < E * PC; i += NW * kWave) {
     const int e = i / PC, pc = i % PC, col = col0 + pc * 8;
     wl[e * PITCH + pc] =
         col < d ? *reinterpret_cast<const u32x4_t*>(W + (int64_t)e * d + col) : z4;
@@ -256,7 +265,7 @@ __global__ __launch_bounds__(kDotWaves * kWave) void hash_dots_kernel(
     constexpr int Q = decltype(q)::value;
     constexpr int N = (Q + PF) % RS;
     load_x(i + PF, xr[N]);
-    er[N] = load_e(i + PF);
+    load_e(i + PF, er[N]);
 #pragma unroll
     for (int r = 0; r < XL; ++r) {
       const int pi = r * kWave + lane;
@@ -265,17 +274,28 @@ __global__ __launch_bounds__(kDotWaves * kWave) void hash_dots_kernel(
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const int64_t t = tok0(i) + i8;
-    const int e = er[Q];
-    if (j < k && t < c1) {
-      float acc = 0.f;
-      if (e >= 0 && e < E) {
-        const u32x4_t* xv = xw + i8 * PITCH;
-        const u32x4_t* wv = wl + e * PITCH;
+    const int64_t t = tok0(i) + it;
+    if (j0 < k && t < c1) {
+      float acc[SPL];
+      int wrow[SPL];
+      bool live[SPL];
 #pragma unroll
-        for (int pc = 0; pc < PC; ++pc) acc = dot8(xv[pc], wv[pc], acc);
+      for (int m = 0; m < SPL; ++m) {
+        acc[m] = 0.f;
+        const int e = er[Q][m];
+        live[m] = e >= 0 && e < E;  // not: an empty slot, or past k
+        wrow[m] = live[m] ? e * PITCH : 0;
       }
-      out[t * k + j] = acc;
+      const u32x4_t* xv = xw + it * PITCH;
+#pragma unroll
+      for (int pc = 0; pc < PC; ++pc) {
+        const u32x4_t xp = xv[pc];
+#pragma unroll
+        for (int m = 0; m < SPL; ++m) acc[m] = dot8(xp, wl[wrow[m] + pc], acc[m]);
+      }
+#pragma unroll
+      for (int m = 0; m < SPL; ++m)
+        if (j0 + m < k) out[t * k + j0 + m] = live[m] ? acc[m] : 0.f;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();  // the x rows are rewritten by the next tile
@@ -540,24 +560,39 @@ hipError_t launch_hash_tiles(const RouteCfg& c, const int32_t* token_ids,
 // The slice width of hash_dots_kernel for E experts (the W slice of every
 // expert fits the LDS beside the x rows), or 0 when the kernel does not
 // apply: bf16, k <= 8, E <= 768, d a multiple of 8, 16-byte aligned rows.
-// 112 columns (64 slices of a 7168-wide row, one workgroup per CU) measured
-// as fast as 128 (whole 128-byte lines per token, 56 slices).
+// 128 or 64 columns: whole 128-byte lines of each token's row (112 and 56
+// columns measured 1-2 and 50 us slower on the DeepSeek-V4-like shape).
 int hash_dot_slice(const RouteCfg& c, int32_t dtype, bool aligned) {
   if (dtype != 1 || !aligned || c.k > kDotMaxK || c.d % 8 != 0 || c.E > 768 ||
       std::getenv("MOE_HASH_DENSE"))
     return 0;
   const bool small = c.E <= 384;
-  if (const char* env = std::getenv("MOE_HASH_SLICE")) {  // tuning: 112/128 or 56/64
+  if (const char* env = std::getenv("MOE_HASH_SLICE")) {  // tuning: 56/64 (+ 112/128)
     const int v = std::atoi(env);
     if (small && (v == 112 || v == 128)) return v;
-    if (!small && (v == 56 || v == 64)) return v;
+    if (v == 56 || v == 64) return v;
   }
-  return small ? 112 : 56;
+  return small ? 128 : 64;
 }
 
 int hash_dot_slices(const RouteCfg& c, int32_t dtype, bool aligned) {
   const int sl = hash_dot_slice(c, dtype, aligned);
   return sl ? (c.d + sl - 1) / sl : 0;
+}
+
+// Workgroups of `threads` threads of this kernel one CU holds at once
+// (registers and LDS), looked up once per kernel.
+int resident_blocks(const void* kernel, int threads) {
+  static std::mutex mu;
+  static std::unordered_map<const void*, int> cache;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = cache.find(kernel);
+  if (it != cache.end()) return it->second;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n < 1)
+    n = 1;
+  cache.emplace(kernel, n);
+  return n;
 }
 
 hipError_t launch_hash_dots(const RouteCfg& c, int32_t dtype, const void* x, const void* W,
@@ -569,22 +604,37 @@ hipError_t launch_hash_dots(const RouteCfg& c, int32_t dtype, const void* x, con
   if (sl == 0) return hipErrorInvalidValue;
   if (c.T == 0) return hipSuccess;
   const int ns = (c.d + sl - 1) / sl;
-  // at most one workgroup per CU (the LDS holds one) over slices x token
-  // chunks: a second round of a few workgroups would double the time
+  // as many workgroups as the CUs hold at once (the LDS sets it) over
+  // slices x token chunks: a second round of a few workgroups would double
+  // the time
   constexpr int kDotCus = 256;
-  const int chunks = std::max(1, std::min((c.T + 255) / 256, kDotCus / ns));
-  const int chunk = (c.T + chunks - 1) / chunks;
-  const dim3 grid((uint32_t)ns, (uint32_t)chunks), block(kDotWaves * kWave);
-  auto go = [&](auto kernel) {
-    return launch(kStageHashDots, kernel, grid, block, stream, (const uint16_t*)x,
-                  (const uint16_t*)W, ids, c.T, c.d, c.E, c.k, chunk, part, zero, zero_words);
+  auto go = [&](auto kernel, int waves) {
+    const int per_cu = resident_blocks(reinterpret_cast<const void*>(kernel), waves * kWave);
+    const int chunks = std::max(1, std::min((c.T + 255) / 256, kDotCus * per_cu / ns));
+    const int chunk = (c.T + chunks - 1) / chunks;
+    return launch(kStageHashDots, kernel, dim3((uint32_t)ns, (uint32_t)chunks),
+                  dim3(waves * kWave), stream, (const uint16_t*)x, (const uint16_t*)W, ids, c.T,
+                  c.d, c.E, c.k, chunk, part, zero, zero_words);
   };
-  switch (sl) {
-    case 128: return go(hash_dots_kernel<128, 384, kDotLookahead>);
-    case 112: return go(hash_dots_kernel<112, 384, kDotLookahead>);
-    case 64: return go(hash_dots_kernel<64, 768, kDotLookahead>);
-    default: return go(hash_dots_kernel<56, 768, kDotLookahead>);
+  int lpt = 4;  // lanes per token
+  if (const char* env = std::getenv("MOE_HASH_LPT")) {  // tuning: 2, 4 or 8
+    const int v = std::atoi(env);
+    if (v == 2 || v == 4 || v == 8) lpt = v;
   }
+#define MOE_HD(SL_, EM_)                                                   \
+  if (sl == SL_ && c.E <= EM_) {                                           \
+    if (lpt == 8) return go(hash_dots_kernel<SL_, EM_, 8, 16, 3>, 16);    \
+    if (lpt == 2) return go(hash_dots_kernel<SL_, EM_, 2, 4, 3>, 4);      \
+    return go(hash_dots_kernel<SL_, EM_, 4, 8, 2>, 8);                    \
+  }
+  MOE_HD(128, 384)
+  MOE_HD(112, 384)
+  MOE_HD(64, 384)
+  MOE_HD(56, 384)
+  MOE_HD(64, 768)
+  MOE_HD(56, 768)
+#undef MOE_HD
+  return hipErrorInvalidValue;
 }
 
 }  // namespace moe
