@@ -39,10 +39,9 @@
  *    selection workgroup), MOE_NO_SMALL_DISPATCH (no one-workgroup
  *    selection + dispatch for small batches), MOE_HASH_DENSE (hash layers
  *    take the gate of every expert instead of k dot products per token),
- *    MOE_HASH_SLICE (56/64, up to 384 experts also 112/128 columns per
- *    dot-product slice), MOE_HASH_LPT (2/4/8 lanes per token in the dot
- *    products).  Values that do not fit the shapes are ignored; workspace
- *    sizes follow the same variables.
+ *    MOE_HASH_SLICE (64, up to 384 experts also 112/128/192 columns per
+ *    dot-product slice).  Values that do not fit the shapes are ignored;
+ *    workspace sizes follow the same variables.
  */
 #ifndef MOE_ROUTE_H
 #define MOE_ROUTE_H

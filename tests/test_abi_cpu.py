@@ -133,11 +133,11 @@ def test_route_hash_validation():
     assert L.moe_route_hash(ctypes.byref(p0), None, None, 10, None, None, None, None, None, None,
                             0, None, None) == tda.MOE_OK
     # bf16, k <= 8, E <= 768, d % 8 == 0: per-slice partial dot products of
-    # the k table experts (slices of 128 columns up to 384 experts, else 64)
+    # the k table experts (slices of 192 columns up to 384 experts, else 64)
     n = tda.route_hash_workspace_size(16384, 7168, 384, 6, score="sqrt_softplus")
-    assert n == 56 * 16384 * 6 * 4
+    assert n == 38 * 16384 * 6 * 4
     assert tda.route_hash_workspace_size(100, 7168, 500, 8) == 112 * 100 * 8 * 4
-    assert tda.route_hash_workspace_size(100, 1000, 384, 2) == 8 * 100 * 2 * 4
+    assert tda.route_hash_workspace_size(100, 1000, 384, 2) == 6 * 100 * 2 * 4
     # otherwise the gate logits of every expert, per K split
     for args in [(16384, 7168, 384, 6, 0), (4096, 2048, 128, 9, 1), (100, 64, 1024, 4, 1),
                  (100, 60, 64, 4, 1)]:

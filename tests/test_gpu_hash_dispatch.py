@@ -81,10 +81,12 @@ def test_hash_scores_ragged_and_duplicates(score, dtype, gate):
 
 @pytest.mark.parametrize("T,d,E,k,bad,slice_", [
     (77, 104, 24, 5, True, None),       # one slice wider than d (zero-filled), ragged T
-    (1000, 7168, 384, 6, False, None),  # DeepSeek-V4-like rows: 56 slices of 128 columns
-    (1000, 7168, 384, 6, False, "112"),  # 64 slices of 112 columns
+    (1000, 7168, 384, 6, False, None),  # DeepSeek-V4-like rows: 38 slices of 192 columns,
+                                        # the last one 64 wide
+    (1000, 7168, 384, 6, False, "128"),  # 56 slices of 128 columns
     (500, 1000, 500, 8, True, None),    # 64-column slices (E > 384), a partial last slice
-    (500, 1000, 500, 8, True, "56"),    # 56-column slices
+    (500, 1000, 300, 8, True, "64"),    # 64-column slices below 384 experts
+    (70000, 200, 64, 3, False, None),   # 2 slices (the second 8 wide) x 128 token chunks
     (3001, 256, 768, 1, False, None),   # the largest E of the kernel, k = 1
     (5, 64, 8, 8, True, None),          # fewer tokens than one wavefront's tile
 ])

@@ -145,24 +145,32 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void hash_route_kernel(
   if (lane < k) weights[t * k + lane] = sel ? w * c.route_scale : 0.f;
 }
 
-// k dot products per token over one slice of d: the hash layer's own work.
+// k dot products per token over slices of d: the hash layer's own work.
 // Workgroup (s, c) holds columns [s*SL, s*SL + SL) of every expert's W row
 // in LDS (rows padded by one 16-byte piece to spread the banks) and passes
-// the tokens of chunk c through them in tiles, each wavefront taking 64 / L
-// tokens: its lanes load those tokens' x slices (16-byte pieces, PF tiles
-// ahead, with the tokens' expert ids) into the wave's own LDS rows, then
-// each of the token's L lanes forms part[s][t*k + j] = the slice's share of
-// x[t] . W[e_j] for its slots j with bf16 dot2 instructions (fp32
-// accumulation), reading each x piece once for all of its slots.
-// Every x byte is read once and each workgroup reads one slice of W.  (One
-// token per lane with x in registers, reading only W from LDS, measured
-// slower: 97.7 against 65.8 us on the DeepSeek-V4-like shape.)  ids: the
-// table's experts, checked (-1 = none, whose partial is written as 0), from
-// a pass of their own: gathering table rows here, in every slice's
-// workgroup, measured 72.4 against 64.4 + 4.2 us.
+// the tokens of chunk c through them in tiles; the slices of one chunk are
+// neighbours in launch order, so each x row is read by all of them at about
+// the same time.  A wavefront takes 64 / L tokens per tile: lane r of a
+// token loads pieces r, r + L, ... (16 bytes each) of the token's x slice
+// straight into registers, PF tiles ahead, and forms partial sums for the
+// token's k slots with bf16 dot2 instructions (fp32 accumulation) against
+// the W rows in LDS; the L partials of each slot are added with DPP moves,
+// giving part[s][t*k + j] = slice s's share of x[t] . W[ids[t*k + j]] (0
+// for ids < 0).  The token's ids are loaded once per group (lane r holds
+// slots r, r + L, ...) and swizzled to its lanes.  Every x byte is read
+// once and each workgroup reads one slice of W.
+// Measured on the DeepSeek-V4-like shape (16384 tokens, d 7168, 384
+// experts, k 6), kernel time in us: x staged through LDS with a token's
+// lanes splitting its slots 64.4; one token per lane with x in registers
+// 97.7; the pieces split over 4, 8 or 16 lanes 61.9, 59.5, 71.9 at 16
+// wavefronts per workgroup (8 lanes at 8 wavefronts: 65.7); 192- and
+// 128-column slices 58.7-60.6 and 59.4-60.3, 112 columns (rows not cut at
+// 128-byte lines) 68.8; the (slice, token) pairs cut into equal ranges for
+// every CU instead of slices x chunks (which leaves 28-32 CUs idle) 64.7,
+// as the slices then read each x row at different times.
 // zero[0 .. zero_words): the super-tile sums the hash kernel adds into,
-// cleared here (each workgroup a slice) as the gate kernel does on the other
-// paths.
+// cleared here (each workgroup a share) as the gate kernel does on the
+// other paths.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 // acc + the dot product of two 16-byte pieces of 8 bf16 (four dot2 steps).
@@ -186,125 +194,136 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-// L lanes per token (each taking kDotMaxK / L consecutive slots, reusing
-// each x piece it reads for all of them), NW wavefronts, PF tiles of x and
-// ids in flight per wavefront.
+// Sum over the aligned groups of L lanes (L = 1, 2, 4, 8 or 16) with DPP
+// moves: a butterfly whose every step adds two equal-size halves, so each
+// lane of a group ends with the same sum.
+template <int L>
+__device__ __forceinline__ float group_sum(float v) {
+  auto mv = [](float a, auto ctrl) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a),
+                                                      decltype(ctrl)::value, 0xF, 0xF, false));
+  };
+  if constexpr (L >= 2) v += mv(v, std::integral_constant<int, 0xB1>());   // lane ^ 1
+  if constexpr (L >= 4) v += mv(v, std::integral_constant<int, 0x4E>());   // lane ^ 2
+  if constexpr (L >= 8) v += mv(v, std::integral_constant<int, 0x141>());  // 7 - lane in 8
+  if constexpr (L >= 16) v += mv(v, std::integral_constant<int, 0x140>()); // 15 - lane in 16
+  return v;
+}
+
 template <int SL, int EMAX, int L, int NW, int PF>
 __global__ __launch_bounds__(NW * kWave) void hash_dots_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ W,
-    const int32_t* __restrict__ ids, int T, int d, int E, int k, int chunk,
+    const int32_t* __restrict__ ids, int T, int d, int E, int k, int64_t per,
     float* __restrict__ part, int32_t* __restrict__ zero, int zero_words) {
   constexpr int PC = SL / 8;                     // 16-byte pieces per row slice
   constexpr int PITCH = PC + 1;                  // pieces per LDS row
   constexpr int TPW = kWave / L;                 // tokens per wave and tile
-  constexpr int SPL = kDotMaxK / L;              // slots per lane
   constexpr int TPT = NW * TPW;                  // tokens per tile
-  constexpr int XP = TPW * PC;                   // x pieces per wave and tile
-  constexpr int XL = (XP + kWave - 1) / kWave;   // ... per lane
-  static_assert(SL % 8 == 0 && kDotMaxK % L == 0, "shapes");
+  constexpr int CPL = (PC + L - 1) / L;          // pieces per lane
+  constexpr int OPL = (kDotMaxK + L - 1) / L;    // output slots per lane
+  constexpr int EPL = (kDotMaxK + L - 1) / L;    // ids per lane
+  static_assert(SL % 8 == 0 && (L & (L - 1)) == 0 && L >= 2 && L <= 16, "shapes");
   __shared__ u32x4_t wl[EMAX * PITCH];
-  __shared__ u32x4_t xl[NW][TPW * PITCH];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nblk = (int)(gridDim.x * gridDim.y);
-  const int blk = (int)(blockIdx.y * gridDim.x + blockIdx.x);
   if (zero_words > 0) {
-    const int per = (zero_words + nblk - 1) / nblk;
-    const int beg = blk * per, end = min(beg + per, zero_words);
+    const int n = (int)(gridDim.x * gridDim.y);
+    const int each = (zero_words + n - 1) / n;
+    const int beg = (int)(blockIdx.y * gridDim.x + blockIdx.x) * each;
+    const int end = min(beg + each, zero_words);
     for (int i = beg + tid; i < end; i += NW * kWave) zero[i] = 0;
   }
-  const int col0 = (int)blockIdx.x * SL;
-  const int64_t c0 = (int64_t)blockIdx.y * chunk;
-  const int64_t c1 = min((int64_t)T, c0 + chunk);
-  const int ntiles = c0 < c1 ? (int)((c1 - c0 + TPT - 1) / TPT) : 0;
   const int64_t Rk = (int64_t)T * k;
-  float* __restrict__ out = part + (int64_t)blockIdx.x * Rk;
   const u32x4_t z4 = {0u, 0u, 0u, 0u};
+  const int it = lane / L, r = lane % L;
 
-  // this wave's first token of tile i; lane (token it, slots j0 .. j0+SPL-1)
-  auto tok0 = [&](int i) { return c0 + (int64_t)i * TPT + wave * TPW; };
-  const int it = lane / L, j0 = (lane % L) * SPL;
-  auto load_x = [&](int i, u32x4_t (&r)[XL]) {
-    const int64_t b = tok0(i);
-#pragma unroll
-    for (int q = 0; q < XL; ++q) {
-      const int pi = q * kWave + lane;
-      const int64_t t = b + pi / PC;
-      const int col = col0 + (pi % PC) * 8;
-      r[q] = (pi < XP && i < ntiles && t < c1 && col < d)
-                 ? *reinterpret_cast<const u32x4_t*>(x + t * d + col)
-                 : z4;
-    }
-  };
-  auto load_e = [&](int i, int (&ev)[SPL]) {
-    const int64_t t = tok0(i) + it;
-#pragma unroll
-    for (int m = 0; m < SPL; ++m)
-      ev[m] = (i < ntiles && j0 + m < k && t < c1) ? ids[t * k + j0 + m] : -1;
-  };
+  {
+    const int sl = (int)blockIdx.x;
+    const int64_t c0 = (int64_t)blockIdx.y * per;
+    const int64_t c1 = min((int64_t)T, c0 + per);
+    if (c0 >= c1) return;  // uniform: a chunk past the last token
+    const int col0 = sl * SL;
+    const int ntiles = (int)((c1 - c0 + TPT - 1) / TPT);
+    float* __restrict__ out = part + (int64_t)sl * Rk;
 
-  // tiles 0 .. PF-1 in flight while the W slice is loaded; a ring of PF + 1
-  // register slots
-  constexpr int RS = PF + 1;
-  u32x4_t xr[RS][XL];
-  int er[RS][SPL];
-  static_for<PF>([&](auto q) {
-    constexpr int Q = decltype(q)::value;
-    load_x(Q, xr[Q]);
-    load_e(Q, er[Q]);
-  });
-  for (int i = tid; i < E * PC; i += NW * kWave) {
-    const int e = i / PC, pc = i % PC, col = col0 + pc * 8;
-    wl[e * PITCH + pc] =
-        col < d ? *reinterpret_cast<const u32x4_t*>(W + (int64_t)e * d + col) : z4;
-  }
-  __syncthreads();
-
-  u32x4_t* xw = xl[wave];
-  // tile i from ring slot Q; the loads of tile i + PF go to slot (Q + PF) % RS
-  auto step = [&](int i, auto q) {
-    constexpr int Q = decltype(q)::value;
-    constexpr int N = (Q + PF) % RS;
-    load_x(i + PF, xr[N]);
-    load_e(i + PF, er[N]);
+    auto tok = [&](int i) { return c0 + (int64_t)i * TPT + wave * TPW + it; };
+    // Loads without branches (a branch around each load made the compiler
+    // wait for every load in flight at each step): addresses past the range
+    // or the row are clamped into it and the values are discarded at use.
+    auto load_x = [&](int i, u32x4_t (&v)[CPL]) {
+      const int64_t t = min(tok(i), c1 - 1);
 #pragma unroll
-    for (int r = 0; r < XL; ++r) {
-      const int pi = r * kWave + lane;
-      if (pi < XP) xw[(pi / PC) * PITCH + pi % PC] = xr[Q][r];
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const int64_t t = tok0(i) + it;
-    if (j0 < k && t < c1) {
-      float acc[SPL];
-      int wrow[SPL];
-      bool live[SPL];
-#pragma unroll
-      for (int m = 0; m < SPL; ++m) {
-        acc[m] = 0.f;
-        const int e = er[Q][m];
-        live[m] = e >= 0 && e < E;  // not: an empty slot, or past k
-        wrow[m] = live[m] ? e * PITCH : 0;
+      for (int q = 0; q < CPL; ++q) {
+        const int col = min(col0 + (q * L + r) * 8, d - 8);
+        v[q] = *reinterpret_cast<const u32x4_t*>(x + t * d + col);
       }
-      const u32x4_t* xv = xw + it * PITCH;
+    };
+    auto load_e = [&](int i, int (&ev)[EPL]) {
+      const int64_t t = min(tok(i), c1 - 1);
 #pragma unroll
-      for (int pc = 0; pc < PC; ++pc) {
-        const u32x4_t xp = xv[pc];
-#pragma unroll
-        for (int m = 0; m < SPL; ++m) acc[m] = dot8(xp, wl[wrow[m] + pc], acc[m]);
-      }
-#pragma unroll
-      for (int m = 0; m < SPL; ++m)
-        if (j0 + m < k) out[t * k + j0 + m] = live[m] ? acc[m] : 0.f;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();  // the x rows are rewritten by the next tile
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  };
-  for (int i = 0; i < ntiles; i += RS)
-    static_for<RS>([&](auto q) {
-      if (i + decltype(q)::value < ntiles) step(i + decltype(q)::value, q);
+      for (int j = 0; j < EPL; ++j) ev[j] = ids[t * k + min(j * L + r, k - 1)];
+    };
+
+    // tiles 0 .. PF-1 in flight while the W slice is loaded; a ring of PF + 1
+    // register slots
+    constexpr int RS = PF + 1;
+    u32x4_t xr[RS][CPL];
+    int er[RS][EPL];
+    static_for<PF>([&](auto q) {
+      constexpr int Q = decltype(q)::value;
+      load_x(Q, xr[Q]);
+      load_e(Q, er[Q]);
     });
+    for (int i = tid; i < E * PC; i += NW * kWave) {
+      const int e = i / PC, pc = i % PC, col = col0 + pc * 8;
+      wl[e * PITCH + pc] =
+          col < d ? *reinterpret_cast<const u32x4_t*>(W + (int64_t)e * d + col) : z4;
+    }
+    __syncthreads();
+
+    // tile i from ring slot Q; the loads of tile i + PF go to slot (Q + PF) % RS
+    auto step = [&](int i, auto q) {
+      constexpr int Q = decltype(q)::value;
+      constexpr int N = (Q + PF) % RS;
+      load_x(i + PF, xr[N]);
+      load_e(i + PF, er[N]);
+      float acc[kDotMaxK];
+      static_for<kDotMaxK>([&](auto mm) {
+        constexpr int m = decltype(mm)::value;
+        acc[m] = 0.f;
+        if (m < k) {  // uniform
+          // slot m's id from lane m % L of the group (ds_swizzle bit mode:
+          // the and-mask keeps the group's first lane, the or-mask adds m % L)
+          constexpr int kSwz = (0x1F & ~(L - 1)) | ((m % L) << 5);
+          const int e = __builtin_amdgcn_ds_swizzle(er[Q][m / L], kSwz);
+          const bool live = e >= 0 && e < E;
+          const int row = live ? e * PITCH : 0;
+#pragma unroll
+          for (int qq = 0; qq < CPL; ++qq) {
+            const int pc = qq * L + r;
+            const u32x4_t xv = (pc < PC && col0 + pc * 8 < d) ? xr[Q][qq] : z4;
+            acc[m] = dot8(xv, wl[row + min(pc, PC - 1)], acc[m]);
+          }
+          acc[m] = group_sum<L>(acc[m]);
+          if (!live) acc[m] = 0.f;
+        }
+      });
+      const int64_t t = tok(i);
+      if (t < c1) {
+#pragma unroll
+        for (int o = 0; o < OPL; ++o) {
+          float v = acc[o * L];
+#pragma unroll
+          for (int rr = 1; rr < L; ++rr)
+            if (o * L + rr < kDotMaxK && r == rr) v = acc[o * L + rr];
+          if (o * L + r < k) out[t * k + o * L + r] = v;
+        }
+      }
+    };
+    for (int i = 0; i < ntiles; i += RS)
+      static_for<RS>([&](auto q) {
+        if (i + decltype(q)::value < ntiles) step(i + decltype(q)::value, q);
+      });
+  }
 }
 
 // The table's expert ids, one thread per route (checked; -1 for a bad token
@@ -558,21 +577,22 @@ hipError_t launch_hash_tiles(const RouteCfg& c, const int32_t* token_ids,
 }
 
 // The slice width of hash_dots_kernel for E experts (the W slice of every
-// expert fits the LDS beside the x rows), or 0 when the kernel does not
-// apply: bf16, k <= 8, E <= 768, d a multiple of 8, 16-byte aligned rows.
-// 128 or 64 columns: whole 128-byte lines of each token's row (112 and 56
-// columns measured 1-2 and 50 us slower on the DeepSeek-V4-like shape).
+// expert fits the LDS), or 0 when the kernel does not apply: bf16, k <= 8,
+// E <= 768, d a multiple of 8, 16-byte aligned rows.  192 columns up to 384
+// experts (fewer partial sums for the hash kernel to add than 128, as fast
+// in the dot products; 64 measured 76 against 60 us on the DeepSeek-V4-like
+// shape), else 64.
 int hash_dot_slice(const RouteCfg& c, int32_t dtype, bool aligned) {
   if (dtype != 1 || !aligned || c.k > kDotMaxK || c.d % 8 != 0 || c.E > 768 ||
       std::getenv("MOE_HASH_DENSE"))
     return 0;
   const bool small = c.E <= 384;
-  if (const char* env = std::getenv("MOE_HASH_SLICE")) {  // tuning: 56/64 (+ 112/128)
+  if (const char* env = std::getenv("MOE_HASH_SLICE")) {  // tuning: 64 (+ 112, 128, 192)
     const int v = std::atoi(env);
-    if (small && (v == 112 || v == 128)) return v;
-    if (v == 56 || v == 64) return v;
+    if (small && (v == 112 || v == 128 || v == 192)) return v;
+    if (v == 64) return v;
   }
-  return small ? 128 : 64;
+  return small ? 192 : 64;
 }
 
 int hash_dot_slices(const RouteCfg& c, int32_t dtype, bool aligned) {
@@ -604,36 +624,25 @@ hipError_t launch_hash_dots(const RouteCfg& c, int32_t dtype, const void* x, con
   if (sl == 0) return hipErrorInvalidValue;
   if (c.T == 0) return hipSuccess;
   const int ns = (c.d + sl - 1) / sl;
-  // as many workgroups as the CUs hold at once (the LDS sets it) over
-  // slices x token chunks: a second round of a few workgroups would double
-  // the time
-  constexpr int kDotCus = 256;
-  auto go = [&](auto kernel, int waves) {
-    const int per_cu = resident_blocks(reinterpret_cast<const void*>(kernel), waves * kWave);
+  // slices x token chunks, as many workgroups as the CUs hold at once (a
+  // second round of a few workgroups would double the time); the slices of
+  // one chunk are neighbours in launch order, so they read each x row at
+  // about the same time
+  constexpr int kDotCus = 256, kWaves = 16;
+  auto go = [&](auto kernel) {
+    const int per_cu = resident_blocks(reinterpret_cast<const void*>(kernel), kWaves * kWave);
     const int chunks = std::max(1, std::min((c.T + 255) / 256, kDotCus * per_cu / ns));
-    const int chunk = (c.T + chunks - 1) / chunks;
+    const int64_t per = (c.T + chunks - 1) / chunks;
     return launch(kStageHashDots, kernel, dim3((uint32_t)ns, (uint32_t)chunks),
-                  dim3(waves * kWave), stream, (const uint16_t*)x, (const uint16_t*)W, ids, c.T,
-                  c.d, c.E, c.k, chunk, part, zero, zero_words);
+                  dim3(kWaves * kWave), stream, (const uint16_t*)x, (const uint16_t*)W, ids,
+                  c.T, c.d, c.E, c.k, per, part, zero, zero_words);
   };
-  int lpt = 4;  // lanes per token
-  if (const char* env = std::getenv("MOE_HASH_LPT")) {  // tuning: 2, 4 or 8
-    const int v = std::atoi(env);
-    if (v == 2 || v == 4 || v == 8) lpt = v;
-  }
-#define MOE_HD(SL_, EM_)                                                   \
-  if (sl == SL_ && c.E <= EM_) {                                           \
-    if (lpt == 8) return go(hash_dots_kernel<SL_, EM_, 8, 16, 3>, 16);    \
-    if (lpt == 2) return go(hash_dots_kernel<SL_, EM_, 2, 4, 3>, 4);      \
-    return go(hash_dots_kernel<SL_, EM_, 4, 8, 2>, 8);                    \
-  }
-  MOE_HD(128, 384)
-  MOE_HD(112, 384)
-  MOE_HD(64, 384)
-  MOE_HD(56, 384)
-  MOE_HD(64, 768)
-  MOE_HD(56, 768)
-#undef MOE_HD
+  // 8 lanes per token (pieces split over them), 16 wavefronts, 3 tiles ahead
+  if (sl == 192 && c.E <= 384) return go(hash_dots_kernel<192, 384, 8, kWaves, 3>);
+  if (sl == 128 && c.E <= 384) return go(hash_dots_kernel<128, 384, 8, kWaves, 3>);
+  if (sl == 112 && c.E <= 384) return go(hash_dots_kernel<112, 384, 8, kWaves, 3>);
+  if (sl == 64 && c.E <= 384) return go(hash_dots_kernel<64, 384, 8, kWaves, 3>);
+  if (sl == 64 && c.E <= 768) return go(hash_dots_kernel<64, 768, 8, kWaves, 3>);
   return hipErrorInvalidValue;
 }
 
