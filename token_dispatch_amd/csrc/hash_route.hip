@@ -236,94 +236,92 @@ __global__ __launch_bounds__(NW * kWave) void hash_dots_kernel(
   const u32x4_t z4 = {0u, 0u, 0u, 0u};
   const int it = lane / L, r = lane % L;
 
-  {
-    const int sl = (int)blockIdx.x;
-    const int64_t c0 = (int64_t)blockIdx.y * per;
-    const int64_t c1 = min((int64_t)T, c0 + per);
-    if (c0 >= c1) return;  // uniform: a chunk past the last token
-    const int col0 = sl * SL;
-    const int ntiles = (int)((c1 - c0 + TPT - 1) / TPT);
-    float* __restrict__ out = part + (int64_t)sl * Rk;
+  const int sl = (int)blockIdx.x;  // slice of d
+  const int64_t c0 = (int64_t)blockIdx.y * per;  // chunk of tokens
+  const int64_t c1 = min((int64_t)T, c0 + per);
+  if (c0 >= c1) return;  // uniform: a chunk past the last token
+  const int col0 = sl * SL;
+  const int ntiles = (int)((c1 - c0 + TPT - 1) / TPT);
+  float* __restrict__ out = part + (int64_t)sl * Rk;
 
-    auto tok = [&](int i) { return c0 + (int64_t)i * TPT + wave * TPW + it; };
-    // Loads without branches (a branch around each load made the compiler
-    // wait for every load in flight at each step): addresses past the range
-    // or the row are clamped into it and the values are discarded at use.
-    auto load_x = [&](int i, u32x4_t (&v)[CPL]) {
-      const int64_t t = min(tok(i), c1 - 1);
+  auto tok = [&](int i) { return c0 + (int64_t)i * TPT + wave * TPW + it; };
+  // Loads without branches (a branch around each load made the compiler
+  // wait for every load in flight at each step): addresses past the range
+  // or the row are clamped into it and the values are discarded at use.
+  auto load_x = [&](int i, u32x4_t (&v)[CPL]) {
+    const int64_t t = min(tok(i), c1 - 1);
 #pragma unroll
-      for (int q = 0; q < CPL; ++q) {
-        const int col = min(col0 + (q * L + r) * 8, d - 8);
-        v[q] = *reinterpret_cast<const u32x4_t*>(x + t * d + col);
-      }
-    };
-    auto load_e = [&](int i, int (&ev)[EPL]) {
-      const int64_t t = min(tok(i), c1 - 1);
-#pragma unroll
-      for (int j = 0; j < EPL; ++j) ev[j] = ids[t * k + min(j * L + r, k - 1)];
-    };
-
-    // tiles 0 .. PF-1 in flight while the W slice is loaded; a ring of PF + 1
-    // register slots
-    constexpr int RS = PF + 1;
-    u32x4_t xr[RS][CPL];
-    int er[RS][EPL];
-    static_for<PF>([&](auto q) {
-      constexpr int Q = decltype(q)::value;
-      load_x(Q, xr[Q]);
-      load_e(Q, er[Q]);
-    });
-    for (int i = tid; i < E * PC; i += NW * kWave) {
-      const int e = i / PC, pc = i % PC, col = col0 + pc * 8;
-      wl[e * PITCH + pc] =
-          col < d ? *reinterpret_cast<const u32x4_t*>(W + (int64_t)e * d + col) : z4;
+    for (int q = 0; q < CPL; ++q) {
+      const int col = min(col0 + (q * L + r) * 8, d - 8);
+      v[q] = *reinterpret_cast<const u32x4_t*>(x + t * d + col);
     }
-    __syncthreads();
+  };
+  auto load_e = [&](int i, int (&ev)[EPL]) {
+    const int64_t t = min(tok(i), c1 - 1);
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) ev[j] = ids[t * k + min(j * L + r, k - 1)];
+  };
 
-    // tile i from ring slot Q; the loads of tile i + PF go to slot (Q + PF) % RS
-    auto step = [&](int i, auto q) {
-      constexpr int Q = decltype(q)::value;
-      constexpr int N = (Q + PF) % RS;
-      load_x(i + PF, xr[N]);
-      load_e(i + PF, er[N]);
-      float acc[kDotMaxK];
-      static_for<kDotMaxK>([&](auto mm) {
-        constexpr int m = decltype(mm)::value;
-        acc[m] = 0.f;
-        if (m < k) {  // uniform
-          // slot m's id from lane m % L of the group (ds_swizzle bit mode:
-          // the and-mask keeps the group's first lane, the or-mask adds m % L)
-          constexpr int kSwz = (0x1F & ~(L - 1)) | ((m % L) << 5);
-          const int e = __builtin_amdgcn_ds_swizzle(er[Q][m / L], kSwz);
-          const bool live = e >= 0 && e < E;
-          const int row = live ? e * PITCH : 0;
-#pragma unroll
-          for (int qq = 0; qq < CPL; ++qq) {
-            const int pc = qq * L + r;
-            const u32x4_t xv = (pc < PC && col0 + pc * 8 < d) ? xr[Q][qq] : z4;
-            acc[m] = dot8(xv, wl[row + min(pc, PC - 1)], acc[m]);
-          }
-          acc[m] = group_sum<L>(acc[m]);
-          if (!live) acc[m] = 0.f;
-        }
-      });
-      const int64_t t = tok(i);
-      if (t < c1) {
-#pragma unroll
-        for (int o = 0; o < OPL; ++o) {
-          float v = acc[o * L];
-#pragma unroll
-          for (int rr = 1; rr < L; ++rr)
-            if (o * L + rr < kDotMaxK && r == rr) v = acc[o * L + rr];
-          if (o * L + r < k) out[t * k + o * L + r] = v;
-        }
-      }
-    };
-    for (int i = 0; i < ntiles; i += RS)
-      static_for<RS>([&](auto q) {
-        if (i + decltype(q)::value < ntiles) step(i + decltype(q)::value, q);
-      });
+  // tiles 0 .. PF-1 in flight while the W slice is loaded; a ring of PF + 1
+  // register slots
+  constexpr int RS = PF + 1;
+  u32x4_t xr[RS][CPL];
+  int er[RS][EPL];
+  static_for<PF>([&](auto q) {
+    constexpr int Q = decltype(q)::value;
+    load_x(Q, xr[Q]);
+    load_e(Q, er[Q]);
+  });
+  for (int i = tid; i < E * PC; i += NW * kWave) {
+    const int e = i / PC, pc = i % PC, col = col0 + pc * 8;
+    wl[e * PITCH + pc] =
+        col < d ? *reinterpret_cast<const u32x4_t*>(W + (int64_t)e * d + col) : z4;
   }
+  __syncthreads();
+
+  // tile i from ring slot Q; the loads of tile i + PF go to slot (Q + PF) % RS
+  auto step = [&](int i, auto q) {
+    constexpr int Q = decltype(q)::value;
+    constexpr int N = (Q + PF) % RS;
+    load_x(i + PF, xr[N]);
+    load_e(i + PF, er[N]);
+    float acc[kDotMaxK];
+    static_for<kDotMaxK>([&](auto mm) {
+      constexpr int m = decltype(mm)::value;
+      acc[m] = 0.f;
+      if (m < k) {  // uniform
+        // slot m's id from lane m % L of the group (ds_swizzle bit mode:
+        // the and-mask keeps the group's first lane, the or-mask adds m % L)
+        constexpr int kSwz = (0x1F & ~(L - 1)) | ((m % L) << 5);
+        const int e = __builtin_amdgcn_ds_swizzle(er[Q][m / L], kSwz);
+        const bool live = e >= 0 && e < E;
+        const int row = live ? e * PITCH : 0;
+#pragma unroll
+        for (int qq = 0; qq < CPL; ++qq) {
+          const int pc = qq * L + r;
+          const u32x4_t xv = (pc < PC && col0 + pc * 8 < d) ? xr[Q][qq] : z4;
+          acc[m] = dot8(xv, wl[row + min(pc, PC - 1)], acc[m]);
+        }
+        acc[m] = group_sum<L>(acc[m]);
+        if (!live) acc[m] = 0.f;
+      }
+    });
+    const int64_t t = tok(i);
+    if (t < c1) {
+#pragma unroll
+      for (int o = 0; o < OPL; ++o) {
+        float v = acc[o * L];
+#pragma unroll
+        for (int rr = 1; rr < L; ++rr)
+          if (o * L + rr < kDotMaxK && r == rr) v = acc[o * L + rr];
+        if (o * L + r < k) out[t * k + o * L + r] = v;
+      }
+    }
+  };
+  for (int i = 0; i < ntiles; i += RS)
+    static_for<RS>([&](auto q) {
+      if (i + decltype(q)::value < ntiles) step(i + decltype(q)::value, q);
+    });
 }
 
 // The table's expert ids, one thread per route (checked; -1 for a bad token
