@@ -40,7 +40,8 @@
  *    selection + dispatch for small batches), MOE_HASH_DENSE (hash layers
  *    take the gate of every expert instead of k dot products per token),
  *    MOE_HASH_SLICE (64, up to 384 experts also 112/128/192 columns per
- *    dot-product slice).  Values that do not fit the shapes are ignored;
+ *    dot-product slice), MOE_PLACE_GROUP (1/2/4/8 dispatch tiles per
+ *    placement workgroup).  Values that do not fit the shapes are ignored;
  *    workspace sizes follow the same variables.
  */
 #ifndef MOE_ROUTE_H

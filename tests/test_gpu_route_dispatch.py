@@ -394,6 +394,43 @@ def test_super_tile_select_workgroup_sizes(name, T, waves, monkeypatch):
     assert float(mv.item()) == oracle.maxvio(d_ref["counts"])
 
 
+@pytest.mark.parametrize("group", ["1", "2", "4", "8"])
+@pytest.mark.parametrize("name,T", [("dsv4", 9001), ("switch_top1", 16384), ("qwen3_dynk", 3001),
+                                    ("dsv4_hash", 7777)])
+def test_placement_tile_groups(name, T, group, monkeypatch):
+    """Several dispatch tiles per placement workgroup (MOE_PLACE_GROUP; the
+    super-tile size is rounded to a multiple of the group, a ragged last
+    group included): the dispatch equals the oracle's dispatch of the GPU's
+    ids, bit for bit, and the ids and weights do not change."""
+    w = wl.WORKLOADS[name]
+    inp = wl.make_inputs(w, T=T)
+    say("placement groups", name, T, group)
+    mv = torch.zeros(1, dtype=torch.float64, device=DEV)
+    outs = []
+    for g in ("1", group):
+        monkeypatch.setenv("MOE_PLACE_GROUP", g)
+        if w.hash_vocab:
+            r = tda.route_hash_dispatch(up(inp["token_ids"]), up(inp["tid2eid"]), w.E,
+                                        x=up(inp["x"]), W=up(inp["W"]), score=w.score,
+                                        renormalize=w.renormalize, route_scale=w.route_scale,
+                                        maxvio=mv)
+        else:
+            kw = route_kwargs(w)
+            if kw["group_score"] is None:
+                kw.pop("group_score")
+            kw.update(logit_bias=up(inp["logit_bias"]), select_bias=up(inp["select_bias"]),
+                      k_per_token=up(inp["k_per_token"]))
+            r = tda.route_dispatch(up(inp["x"]), up(inp["W"]), w.k, maxvio=mv, **kw)
+        torch.cuda.synchronize()
+        outs.append(r)
+    monkeypatch.delenv("MOE_PLACE_GROUP")
+    a, b = outs
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    d_ref = oracle.dispatch(down(b[0]), w.E)
+    check_dispatch(tuple(b[2:]), d_ref)
+    assert float(mv.item()) == oracle.maxvio(d_ref["counts"])
+
+
 @pytest.mark.parametrize("name,T", [("qwen3_dynk", None), ("qwen3_dynk", 4091), ("olmoe", 1000)])
 def test_all_counts_placement_after_the_gate(name, T, monkeypatch):
     """With the super-tile sums switched off the select kernel's tile

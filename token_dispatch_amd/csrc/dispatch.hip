@@ -555,14 +555,17 @@ __global__ __launch_bounds__(kThreads) void disp_capacity_kernel(
 // super rows -- every expert's total, and its count in super tiles before
 // tile t's -- and the at most S - 1 tile rows before it inside its own super
 // tile: (ns + S) * E counts instead of the nt * E the all-counts kernel reads.
-// Tiles hold TR routes (any number up to 64 * kPlaceWaves * CPW); one chunk
-// of 64 routes per wave and chunk slot, 16 waves.  J threads per expert
-// (adjacent lanes) split its rows and add their sums with DPP.
+// Tiles hold TR routes; workgroup w places the G tiles [w*G, w*G + G) (G *
+// TR up to 64 * kPlaceWaves * CPW routes; S is a multiple of G, so they lie
+// in one super tile and the rows before the first of them are the rows
+// before each), one chunk of 64 routes per wave and chunk slot, 16 waves.
+// J threads per expert (adjacent lanes) split its rows and add their sums
+// with DPP.
 constexpr int kPlaceWaves = 16;
 
 template <int CPW, int NB>
 __global__ __launch_bounds__(kPlaceWaves * kWave) void disp_place_super_kernel(
-    const int32_t* __restrict__ ids, int64_t R, int E, int nt, int TR, int S,
+    const int32_t* __restrict__ ids, int64_t R, int E, int nt, int TR, int S, int G,
     const hist_t* __restrict__ tile_hist, const int32_t* __restrict__ super_sum,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
     int32_t* __restrict__ inv, double* __restrict__ maxvio) {
@@ -574,7 +577,8 @@ __global__ __launch_bounds__(kPlaceWaves * kWave) void disp_place_super_kernel(
   __shared__ int32_t wsum[kPlaceWaves];
   __shared__ int32_t wmax[kPlaceWaves];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int tile = blockIdx.x;
+  const int tile = (int)blockIdx.x * G;  // this workgroup's first tile (G tiles each)
+  const int TRG = TR * G;                 // its routes
   const int64_t tbase = (int64_t)tile * TR;
 
   // this wave's chunks of the tile: slot c = wave * CPW + ch covers routes
@@ -584,7 +588,7 @@ __global__ __launch_bounds__(kPlaceWaves * kWave) void disp_place_super_kernel(
   for (int ch = 0; ch < CPW; ++ch) {
     const int c = wave * CPW + ch;
     const int64_t r = tbase + c * kWave + lane;
-    const bool mine = c * kWave + lane < TR && r < R;
+    const bool mine = c * kWave + lane < TRG && r < R;
     ev[ch] = ids[mine ? r : 0];
     if (!mine) ev[ch] = -1;
   }
@@ -714,7 +718,7 @@ __global__ __launch_bounds__(kPlaceWaves * kWave) void disp_place_super_kernel(
     const int c = wave * CPW + ch;
     const int64_t r = tbase + c * kWave + lane;
     const int e = ev[ch];
-    if (c * kWave + lane < TR && r < R) {
+    if (c * kWave + lane < TRG && r < R) {
       const int pos = e >= 0 ? row[e] + in_wave[ch] : -1;
       if (inv) inv[r] = pos;
       if (pos >= 0 && pos < R) perm[pos] = (int32_t)r;
@@ -754,11 +758,29 @@ bool dispatch_super_ok(int64_t R, int32_t E, int32_t tile_routes) {
          tile_routes <= 2 * kPlaceWaves * kWave;
 }
 
+// Tiles per placement workgroup: small tiles are placed two (or more) to a
+// workgroup while there are more tiles than CUs and their routes fit the
+// workgroup's two chunks per lane.
+// Measured (placement us): DeepSeek-V4-like, 512 tiles of 192 routes, 9.35
+// at one tile per workgroup, 7.1-7.2 at two or four, 8.2 at eight; the
+// Qwen3- and DeepSeek-V3-like shapes (<= 256 tiles) slower at four and eight.
+int place_group(int64_t nt, int32_t tile_routes) {
+  int G = 1;
+  if (const char* env = std::getenv("MOE_PLACE_GROUP")) {  // tuning: 1, 2, 4, 8
+    const int want = std::atoi(env);
+    while (G < want && 2 * G * tile_routes <= 2 * kPlaceWaves * kWave) G *= 2;
+    return G;
+  }
+  while (nt > 256 * (int64_t)G && 2 * G * tile_routes <= 2 * kPlaceWaves * kWave) G *= 2;
+  return G;
+}
+
 int dispatch_super_size(int64_t R, int32_t tile_routes) {
   const int64_t nt = (R + tile_routes - 1) / tile_routes;
   int S = 1;
   while ((int64_t)S * S < nt) ++S;  // about sqrt(nt): ns + S rows per workgroup
-  return S;
+  const int G = place_group(nt, tile_routes);
+  return (S + G - 1) / G * G;       // a workgroup's tiles share one super tile
 }
 
 hipError_t launch_dispatch_from_super(const int32_t* ids, int64_t R, int32_t E,
@@ -769,12 +791,13 @@ hipError_t launch_dispatch_from_super(const int32_t* ids, int64_t R, int32_t E,
   if (!dispatch_super_ok(R, E, tile_routes)) return hipErrorInvalidValue;
   const int nt = (int)((R + tile_routes - 1) / tile_routes);
   const int S = dispatch_super_size(R, tile_routes);
+  const int G = place_group(nt, tile_routes);
   auto go = [&](auto kernel) {
-    return launch(kStageDispScatter, kernel, dim3(nt), dim3(kPlaceWaves * kWave), stream, ids,
-                  R, E, nt, (int)tile_routes, S, tile_hist, super_sum, counts, offsets, perm,
-                  inv, maxvio);
+    return launch(kStageDispScatter, kernel, dim3((nt + G - 1) / G), dim3(kPlaceWaves * kWave),
+                  stream, ids, R, E, nt, (int)tile_routes, S, G, tile_hist, super_sum, counts,
+                  offsets, perm, inv, maxvio);
   };
-  const bool two = tile_routes > kPlaceWaves * kWave;
+  const bool two = G * tile_routes > kPlaceWaves * kWave;
   switch (id_bits(E)) {
     case 7: return two ? go(disp_place_super_kernel<2, 7>) : go(disp_place_super_kernel<1, 7>);
     case 8: return two ? go(disp_place_super_kernel<2, 8>) : go(disp_place_super_kernel<1, 8>);
