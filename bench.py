@@ -65,7 +65,7 @@ def host_threads():
     return max(1, min(n, int(env))) if env.isdigit() else n
 
 
-def kernel_work(w, T, R, R_valid, tile_bytes, producer_hist=False):
+def kernel_work(w, T, R, R_valid, tile_bytes, producer_hist=False, beside_rows=0):
     """Algorithmic (HBM bytes, flops) per launch of each kernel: inputs read
     once, outputs written once.  tile_bytes: the dispatch's per-tile
     histogram data (written once, read once by the placement); with
@@ -73,7 +73,10 @@ def kernel_work(w, T, R, R_valid, tile_bytes, producer_hist=False):
     launch).  In a hash
     layer the gate's work is the method's -- x and W read once and k dot
     products per token (the table replaces the selection) -- not the dense
-    contraction this design performs."""
+    contraction this design performs.  beside_rows: the hash layer's
+    dispatch is placed inside the dot-product kernel (its free workgroups)
+    from per-tile rows of counts of that many bytes, which the ids kernel
+    writes."""
     xb = 2 if w.dtype == "bf16" else 4
     E, d, k = w.E, w.d, w.k
     kt = T * 4 if w.dynamic_k else 0
@@ -87,10 +90,14 @@ def kernel_work(w, T, R, R_valid, tile_bytes, producer_hist=False):
         # table rows, the k gathered logits, ids and weights
         "hash": (T * 4 + T * k * 4 + T * k * 4 + T * k * 8 + ph, 0.0),
         # the table's ids alone: token ids and table rows read, ids written
-        "hash_ids": (T * 4 + T * k * 4 + T * k * 4, 0.0),
+        # (+ the tiles' rows of counts)
+        "hash_ids": (T * 4 + T * k * 4 + T * k * 4 + beside_rows, 0.0),
         # the hash layer's k dot products: x and W read once, ids read, the
-        # k logits per token written once
-        "hash_dots": (T * d * xb + E * d * xb + T * k * 4 + T * k * 4, 2.0 * T * d * k),
+        # k logits per token written once (+ the placement beside them: rows
+        # of counts and ids read, inv, perm, counts and offsets written)
+        "hash_dots": (T * d * xb + E * d * xb + T * k * 4 + T * k * 4
+                      + (beside_rows + R * 4 + R * 4 + R_valid * 4 + E * 8 if beside_rows else 0),
+                      2.0 * T * d * k),
         "select": (T * E * 4 + T * k * 8 + kt + ph, 0.0),
         # small batches: selection and the whole dispatch in one workgroup
         "select_dispatch": (T * E * 4 + T * k * 8 + kt + R * 4 + R_valid * 4 + E * 8, 0.0),
@@ -371,8 +378,12 @@ class Case:
         self.R_valid = int(self.counts.sum().item())
         two = "disp_scan" not in prof or not prof["disp_scan"][1]
         tile_bytes = self.disp_ws if two else (self.disp_ws - 4 * w.E) // 2
+        ran = {name for name, (_, n) in prof.items() if n}
+        # a hash layer whose dot-product kernel placed the dispatch
+        beside = bool(w.hash_vocab) and "hash_dots" in ran and "disp_scatter" not in ran
         work = kernel_work(w, T, R, self.R_valid, tile_bytes,
-                           producer_hist="disp_hist" not in prof or not prof["disp_hist"][1])
+                           producer_hist="disp_hist" not in ran and not beside,
+                           beside_rows=-(-R // 2048) * w.E * 4 if beside else 0)
         stages = {}
         for name, (ms, n) in prof.items():
             if n and name in work:

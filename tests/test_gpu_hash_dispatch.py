@@ -245,3 +245,55 @@ def test_hash_dispatch_matches_separate_calls(T, d, E, k, V, bad):
     d_ref = oracle.dispatch(ref_ids, E)
     check_dispatch(tuple(a[2:]), d_ref)
     assert float(m1.item()) == oracle.maxvio(d_ref["counts"])
+
+
+@pytest.mark.parametrize("T,d,E,k,V,bad", [
+    (3001, 7168, 384, 6, 9000, True),     # 228 slice workgroups + 28 placement, ragged tiles
+    (20000, 7168, 384, 8, 30000, False),  # 79 tiles on 28 placement workgroups (3 rounds)
+    (5000, 1024, 64, 8, 3000, False),     # a partial last slice, 20 tiles, 20 workgroups
+    (2000, 512, 640, 5, 800, True),       # 64-column slices of 640 experts
+    (700, 256, 128, 1, 100, False),       # k = 1, one tile
+    (4096, 2048, 96, 7, 5000, True),      # odd k, E a multiple of 8 below 128
+    (3000, 1024, 100, 6, 2000, False),    # E not a multiple of 8
+])
+def test_hash_dispatch_beside_the_dot_products(T, d, E, k, V, bad, monkeypatch):
+    """The dispatch placed by the dot-product kernel's free workgroups
+    (MOE_HASH_BESIDE=1) equals the placement kernel after the hash kernel
+    (MOE_HASH_BESIDE=0) bit for bit -- ids, weights, counts, offsets, perm,
+    inv, MaxVio and the error count -- and the oracle's ids and dispatch."""
+    rng = np.random.default_rng([T, d, E, k])
+    tab = np.argsort(rng.random((V, E)), axis=1)[:, :k].astype(np.int32)
+    tok = rng.integers(0, V, size=T).astype(np.int32)
+    if bad:
+        tok[rng.choice(T, 5, replace=False)] = rng.choice([-1, V, V + 3], 5)
+        tab[rng.choice(V, 7, replace=False), rng.integers(0, k, 7)] = rng.choice([-2, E, E + 9], 7)
+    x = wl.f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+    W = wl.f32_to_bf16_bits((rng.standard_normal((E, d)) / np.sqrt(d)).astype(np.float32))
+    say("hash dispatch beside the dot products", T, d, E, k, V, bad)
+    xg, Wg, tg, tabg = up(x), up(W), up(tok), up(tab)
+    res = {}
+    for mode in ("1", "0"):
+        monkeypatch.setenv("MOE_HASH_BESIDE", mode)
+        err = torch.zeros(1, dtype=torch.int32, device=DEV)
+        mv = torch.full((1,), -7.0, dtype=torch.float64, device=DEV)
+        tda.profile_enable(True)
+        out = tda.route_hash_dispatch(tg, tabg, E, x=xg, W=Wg, maxvio=mv, dev_err=err)
+        torch.cuda.synchronize()
+        stages = {s for s, (_, n) in tda.profile_read().items() if n}
+        tda.profile_enable(False)
+        res[mode] = (out, err, mv, stages)
+    (a, e1, m1, s1), (b, e2, m2, s2) = res["1"], res["0"]
+    assert "disp_scatter" not in s1 and "hash_dots" in s1, s1  # placed beside
+    assert "disp_scatter" in s2, s2
+    n = int(a[3][-1].item())
+    for name, u, v in zip(("ids", "weights", "counts", "offsets", "perm", "inv"), a, b):
+        if name == "perm":
+            u, v = u[:n], v[:n]
+        assert torch.equal(u, v), name
+    assert int(e1.item()) == int(e2.item()) and torch.equal(m1, m2)
+    ref_ids, nerr = oracle.hash_ids(tok, tab, E)
+    assert nerr == int(e1.item())
+    np.testing.assert_array_equal(down(a[0]), ref_ids)
+    d_ref = oracle.dispatch(ref_ids, E)
+    check_dispatch(tuple(a[2:]), d_ref)
+    assert float(m1.item()) == oracle.maxvio(d_ref["counts"])

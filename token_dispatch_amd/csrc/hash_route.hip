@@ -29,6 +29,7 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "place_core.h"
 #include "select_core.h"
 
 namespace moe {
@@ -210,11 +211,16 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
-template <int SL, int EMAX, int L, int NW, int PF>
+// PLACE: a one-dimensional grid of ns x chunks slice workgroups (slice =
+// block % ns) followed by place.n_place workgroups that place the dispatch
+// tiles t = w, w + n_place, ... of the table ids (place_super_tiles with
+// every tile's own row, S = 1) and stream no x.
+template <int SL, int EMAX, int L, int NW, int PF, bool PLACE = false>
 __global__ __launch_bounds__(NW * kWave) void hash_dots_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ W,
     const int32_t* __restrict__ ids, int T, int d, int E, int k, int64_t per,
-    float* __restrict__ part, int32_t* __restrict__ zero, int zero_words) {
+    float* __restrict__ part, int32_t* __restrict__ zero, int zero_words, int ns,
+    BesidePlace place) {
   constexpr int PC = SL / 8;                     // 16-byte pieces per row slice
   constexpr int PITCH = PC + 1;                  // pieces per LDS row
   constexpr int TPW = kWave / L;                 // tokens per wave and tile
@@ -225,6 +231,20 @@ __global__ __launch_bounds__(NW * kWave) void hash_dots_kernel(
   static_assert(SL % 8 == 0 && (L & (L - 1)) == 0 && L >= 2 && L <= 16, "shapes");
   __shared__ u32x4_t wl[EMAX * PITCH];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if constexpr (PLACE) {
+    const int n_dots = place.n_dots;
+    static_assert(sizeof(PlaceLds) <= sizeof(wl) && NW == kPlaceWaves, "placement workgroup");
+    if ((int)blockIdx.x >= n_dots) {  // uniform: a placement workgroup
+      PlaceLds& sh = *reinterpret_cast<PlaceLds*>(wl);
+      for (int t = (int)blockIdx.x - n_dots; t < place.nt; t += place.n_place) {
+        place_super_tiles<kBesideTile / (kPlaceWaves * kWave), kPlaceIdBits>(
+            t, place.ids, place.R, place.E, place.nt, kBesideTile, 1, 1, nullptr, place.rows,
+            place.counts, place.offsets, place.perm, place.inv, place.maxvio, sh);
+        __syncthreads();  // LDS reused by the next tile
+      }
+      return;
+    }
+  }
   if (zero_words > 0) {
     const int n = (int)(gridDim.x * gridDim.y);
     const int each = (zero_words + n - 1) / n;
@@ -236,8 +256,8 @@ __global__ __launch_bounds__(NW * kWave) void hash_dots_kernel(
   const u32x4_t z4 = {0u, 0u, 0u, 0u};
   const int it = lane / L, r = lane % L;
 
-  const int sl = (int)blockIdx.x;  // slice of d
-  const int64_t c0 = (int64_t)blockIdx.y * per;  // chunk of tokens
+  const int sl = PLACE ? (int)blockIdx.x % ns : (int)blockIdx.x;  // slice of d
+  const int64_t c0 = (int64_t)(PLACE ? (int)blockIdx.x / ns : (int)blockIdx.y) * per;  // chunk
   const int64_t c1 = min((int64_t)T, c0 + per);
   if (c0 >= c1) return;  // uniform: a chunk past the last token
   const int col0 = sl * SL;
@@ -339,6 +359,50 @@ __global__ __launch_bounds__(256) void hash_ids_kernel(const int32_t* __restrict
     if (e < 0 || e >= E) e = -1;
   }
   ids[r] = e;
+}
+
+// The table's expert ids as hash_ids_kernel writes them, for dispatch tiles
+// of kBesideTile routes (one 16-wavefront workgroup per tile, two chunks of
+// 64 routes per wavefront), plus each tile's count of every expert:
+// rows[tile][e] (int32), counted without atomics by ballot peer masks into
+// one LDS row per wavefront and added over the wavefronts.
+template <int NB>
+__global__ __launch_bounds__(kPlaceWaves * kWave) void hash_ids_rows_kernel(
+    const int32_t* __restrict__ token_ids, const int32_t* __restrict__ tid2eid, int32_t vocab,
+    int64_t R, int k, int E, int32_t* __restrict__ ids, int32_t* __restrict__ rows) {
+  constexpr int CPW = kBesideTile / (kPlaceWaves * kWave);
+  __shared__ int32_t wh[kPlaceWaves][kPlaceMaxE];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  int ev[CPW];
+#pragma unroll
+  for (int ch = 0; ch < CPW; ++ch) {
+    const int64_t r = (int64_t)blockIdx.x * kBesideTile + (wave * CPW + ch) * kWave + lane;
+    int e = -1;
+    if (r < R) {
+      const int v = token_ids[r / k];
+      if (v >= 0 && v < vocab) {
+        e = tid2eid[(int64_t)v * k + r % k];
+        if (e < 0 || e >= E) e = -1;
+      }
+      ids[r] = e;
+    }
+    ev[ch] = e;
+  }
+  for (int e = lane; e < E; e += kWave) wh[wave][e] = 0;
+  __syncthreads();
+  const uint64_t below = lanemask_lt();
+#pragma unroll
+  for (int ch = 0; ch < CPW; ++ch) {
+    const uint64_t p = peer_mask<NB>(ev[ch]);
+    if (ev[ch] >= 0 && (p & below) == 0) wh[wave][ev[ch]] += __popcll(p);
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kPlaceWaves * kWave) {
+    int n = 0;
+#pragma unroll
+    for (int w = 0; w < kPlaceWaves; ++w) n += wh[w][e];
+    rows[(int64_t)blockIdx.x * E + e] = n;
+  }
 }
 
 // Hash routing from the gate's logits with several tokens per wavefront: a
@@ -613,6 +677,50 @@ int resident_blocks(const void* kernel, int threads) {
   return n;
 }
 
+// slices x token chunks, as many workgroups as the CUs hold at once (a
+// second round of a few workgroups would double the time); the slices of
+// one chunk are neighbours in launch order, so they read each x row at
+// about the same time
+constexpr int kDotCus = 256, kDotWaves = 16;
+struct DotsGrid {
+  int ns = 0, chunks = 0, per_cu = 1;
+  int64_t per = 0;
+};
+DotsGrid dots_grid(const RouteCfg& c, int sl, const void* kernel) {
+  DotsGrid g;
+  g.ns = (c.d + sl - 1) / sl;
+  g.per_cu = resident_blocks(kernel, kDotWaves * kWave);
+  g.chunks = std::max(1, std::min((c.T + 255) / 256, kDotCus * g.per_cu / g.ns));
+  g.per = (c.T + g.chunks - 1) / g.chunks;
+  return g;
+}
+
+// The dot-product kernel for slice width sl and E experts (nullptr: none),
+// with or without the placement workgroups.  8 lanes per token (pieces
+// split over them), 16 wavefronts, 3 tiles ahead.
+template <bool PLACE>
+const void* dots_kernel(int sl, int32_t E) {
+  auto k = [](auto kernel) { return reinterpret_cast<const void*>(kernel); };
+  if (sl == 192 && E <= 384) return k(hash_dots_kernel<192, 384, 8, kDotWaves, 3, PLACE>);
+  if (sl == 128 && E <= 384) return k(hash_dots_kernel<128, 384, 8, kDotWaves, 3, PLACE>);
+  if (sl == 112 && E <= 384) return k(hash_dots_kernel<112, 384, 8, kDotWaves, 3, PLACE>);
+  if constexpr (!PLACE)  // its 55 KB W slice holds no placement's LDS
+    if (sl == 64 && E <= 384) return k(hash_dots_kernel<64, 384, 8, kDotWaves, 3, PLACE>);
+  if (sl == 64 && E <= 768) return k(hash_dots_kernel<64, 768, 8, kDotWaves, 3, PLACE>);
+  return nullptr;
+}
+
+hipError_t launch_dots(const RouteCfg& c, const void* kernel, const DotsGrid& g, dim3 grid,
+                       const void* x, const void* W, const int32_t* ids, float* part,
+                       int32_t* zero, int32_t zero_words, const BesidePlace& place,
+                       hipStream_t stream) {
+  typedef void (*Fn)(const uint16_t*, const uint16_t*, const int32_t*, int, int, int, int,
+                     int64_t, float*, int32_t*, int, int, BesidePlace);
+  return launch(kStageHashDots, reinterpret_cast<Fn>(const_cast<void*>(kernel)), grid,
+                dim3(kDotWaves * kWave), stream, (const uint16_t*)x, (const uint16_t*)W, ids,
+                c.T, c.d, c.E, c.k, g.per, part, zero, zero_words, g.ns, place);
+}
+
 hipError_t launch_hash_dots(const RouteCfg& c, int32_t dtype, const void* x, const void* W,
                             const int32_t* ids, float* part, int32_t* zero, int32_t zero_words,
                             hipStream_t stream) {
@@ -621,27 +729,66 @@ hipError_t launch_hash_dots(const RouteCfg& c, int32_t dtype, const void* x, con
   const int sl = hash_dot_slice(c, dtype, aligned);
   if (sl == 0) return hipErrorInvalidValue;
   if (c.T == 0) return hipSuccess;
-  const int ns = (c.d + sl - 1) / sl;
-  // slices x token chunks, as many workgroups as the CUs hold at once (a
-  // second round of a few workgroups would double the time); the slices of
-  // one chunk are neighbours in launch order, so they read each x row at
-  // about the same time
-  constexpr int kDotCus = 256, kWaves = 16;
-  auto go = [&](auto kernel) {
-    const int per_cu = resident_blocks(reinterpret_cast<const void*>(kernel), kWaves * kWave);
-    const int chunks = std::max(1, std::min((c.T + 255) / 256, kDotCus * per_cu / ns));
-    const int64_t per = (c.T + chunks - 1) / chunks;
-    return launch(kStageHashDots, kernel, dim3((uint32_t)ns, (uint32_t)chunks),
-                  dim3(kWaves * kWave), stream, (const uint16_t*)x, (const uint16_t*)W, ids,
-                  c.T, c.d, c.E, c.k, per, part, zero, zero_words);
-  };
-  // 8 lanes per token (pieces split over them), 16 wavefronts, 3 tiles ahead
-  if (sl == 192 && c.E <= 384) return go(hash_dots_kernel<192, 384, 8, kWaves, 3>);
-  if (sl == 128 && c.E <= 384) return go(hash_dots_kernel<128, 384, 8, kWaves, 3>);
-  if (sl == 112 && c.E <= 384) return go(hash_dots_kernel<112, 384, 8, kWaves, 3>);
-  if (sl == 64 && c.E <= 384) return go(hash_dots_kernel<64, 384, 8, kWaves, 3>);
-  if (sl == 64 && c.E <= 768) return go(hash_dots_kernel<64, 768, 8, kWaves, 3>);
-  return hipErrorInvalidValue;
+  const void* kernel = dots_kernel<false>(sl, c.E);
+  if (!kernel) return hipErrorInvalidValue;
+  const DotsGrid g = dots_grid(c, sl, kernel);
+  return launch_dots(c, kernel, g, dim3((uint32_t)g.ns, (uint32_t)g.chunks), x, W, ids, part,
+                     zero, zero_words, BesidePlace{}, stream);
+}
+
+// Placement workgroups beside the dot products: the CUs the slices x chunks
+// grid leaves free, at most one per tile.  Taken when the placements should
+// end well inside the dot products: each round of them reads every tile's
+// row (nt * E * 4 bytes, ~50 GB/s into one CU) after a few microseconds of
+// latency, against x streaming at ~4 TB/s (DeepSeek-V4-like hash layer: 48
+// tiles on 28 free CUs, two rounds of ~4 us against ~60 us of dot products).
+int hash_beside_places(const RouteCfg& c, int32_t dtype, bool aligned) {
+  const char* env = std::getenv("MOE_HASH_BESIDE");  // tuning: 0 never, 1 whenever possible
+  if (env && env[0] == '0') return 0;
+  const int sl = hash_dot_slice(c, dtype, aligned);
+  if (sl == 0 || c.T == 0 || c.E > kPlaceMaxE) return 0;
+  const void* kernel = dots_kernel<true>(sl, c.E);
+  if (!kernel) return 0;
+  const DotsGrid g = dots_grid(c, sl, kernel);
+  const int64_t R = (int64_t)c.T * c.k;
+  const int64_t nt = (R + kBesideTile - 1) / kBesideTile;
+  const int64_t free_cus = (int64_t)kDotCus * g.per_cu - (int64_t)g.ns * g.chunks;
+  if (free_cus < 1) return 0;
+  const int n_place = (int)std::min<int64_t>(nt, free_cus);
+  if (env && env[0] == '1') return n_place;
+  const double rounds = (double)((nt + n_place - 1) / n_place);
+  const double place_us = rounds * (4.0 + (double)nt * c.E * 4 / 50e3);
+  const double dots_us = (double)c.T * c.d * 2 / 4e6;
+  return place_us <= 0.5 * dots_us ? n_place : 0;
+}
+
+hipError_t launch_hash_ids_rows(const RouteCfg& c, const int32_t* token_ids,
+                                const int32_t* tid2eid, int32_t vocab, int32_t* ids,
+                                int32_t* rows, hipStream_t stream) {
+  if (c.T == 0) return hipSuccess;
+  if (c.E > kPlaceMaxE) return hipErrorInvalidValue;
+  const int64_t R = (int64_t)c.T * c.k;
+  const dim3 grid((uint32_t)((R + kBesideTile - 1) / kBesideTile));
+  return launch(kStageHashIds, hash_ids_rows_kernel<kPlaceIdBits>, grid,
+                dim3(kPlaceWaves * kWave), stream, token_ids, tid2eid, vocab, R, c.k, c.E, ids,
+                rows);
+}
+
+hipError_t launch_hash_dots_beside(const RouteCfg& c, int32_t dtype, const void* x,
+                                   const void* W, float* part, const BesidePlace& place,
+                                   hipStream_t stream) {
+  const bool aligned = reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
+                       reinterpret_cast<uintptr_t>(W) % 16 == 0;
+  const int sl = hash_dot_slice(c, dtype, aligned);
+  const void* kernel = sl ? dots_kernel<true>(sl, c.E) : nullptr;
+  if (!kernel || c.T == 0 || place.n_place < 1 || place.E != c.E ||
+      place.R != (int64_t)c.T * c.k || place.nt != (place.R + kBesideTile - 1) / kBesideTile)
+    return hipErrorInvalidValue;
+  const DotsGrid g = dots_grid(c, sl, kernel);
+  BesidePlace pl = place;
+  pl.n_dots = g.ns * g.chunks;  // chunks past the last token return at once
+  return launch_dots(c, kernel, g, dim3((uint32_t)(pl.n_dots + pl.n_place)), x, W, pl.ids,
+                     part, nullptr, 0, pl, stream);
 }
 
 }  // namespace moe

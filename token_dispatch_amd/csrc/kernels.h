@@ -186,6 +186,34 @@ hipError_t launch_hash_dots(const RouteCfg& c, int32_t dtype, const void* x, con
                             const int32_t* ids, float* part, int32_t* zero, int32_t zero_words,
                             hipStream_t stream);
 
+// The dispatch of a hash layer placed beside its dot products: the table
+// ids are known before any logit, so the dot-product kernel's workgroups
+// past the slices x chunks grid (the CUs that grid leaves idle) place the
+// dispatch tiles of kBesideTile routes while the others stream x.
+// launch_hash_ids_rows writes the ids and each tile's count of every expert
+// (rows[tile][E], int32); the dot-product launch then takes `place`.
+// hash_beside_places gives the number of placement workgroups, or 0 when
+// this form does not apply (no free CU, tiles x E too large for the
+// placements to finish inside the dot products, or MOE_HASH_BESIDE=0;
+// MOE_HASH_BESIDE=1 takes it whenever it is possible at all).
+constexpr int kBesideTile = 2048;
+struct BesidePlace {
+  const int32_t* ids;
+  int64_t R;
+  int32_t E, nt, n_place;
+  int32_t n_dots;  // slice workgroups before the placement ones (set at launch)
+  const int32_t* rows;
+  int32_t *counts, *offsets, *perm, *inv;
+  double* maxvio;
+};
+int hash_beside_places(const RouteCfg& c, int32_t dtype, bool aligned);
+hipError_t launch_hash_ids_rows(const RouteCfg& c, const int32_t* token_ids,
+                                const int32_t* tid2eid, int32_t vocab, int32_t* ids,
+                                int32_t* rows, hipStream_t stream);
+hipError_t launch_hash_dots_beside(const RouteCfg& c, int32_t dtype, const void* x,
+                                   const void* W, float* part, const BesidePlace& place,
+                                   hipStream_t stream);
+
 // Dispatch placement from per-tile histograms already in tile_hist
 // ([ceil(R / tile_routes)][E] hist_t, tile-major), when dispatch_hist_ok
 // (E % 8 == 0: 16-byte rows).

@@ -530,10 +530,12 @@ int32_t hash_core(const moe_route_params* p, const int32_t* token_ids, const int
                   int32_t* ids, float* weights, void* workspace, size_t workspace_bytes,
                   int32_t* dev_err, hipStream_t s, moe::hist_t* hist = nullptr,
                   int32_t* super_sum = nullptr, int32_t super_words = 0,
-                  bool* used_tiles = nullptr) {
+                  bool* used_tiles = nullptr, const moe::BesidePlace* beside = nullptr,
+                  bool* used_beside = nullptr) {
   const bool ids_only = (x == nullptr && W == nullptr);
   hipError_t e;
   if (used_tiles) *used_tiles = false;
+  if (used_beside) *used_beside = false;
   if (!ids_only && workspace) {
     const bool aligned = reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
                          reinterpret_cast<uintptr_t>(W) % 16 == 0;
@@ -542,6 +544,18 @@ int32_t hash_core(const moe_route_params* p, const int32_t* token_ids, const int
     const int64_t Rk = (int64_t)p->T * p->k;
     if (ns > 0 && workspace_bytes >= (size_t)ns * Rk * sizeof(float)) {
       float* part = static_cast<float*>(workspace);
+      if (beside) {  // the dispatch placed by the dot-product kernel's free workgroups
+        e = moe::launch_hash_ids_rows(c, token_ids, tid2eid, vocab, ids,
+                                      const_cast<int32_t*>(beside->rows), s);
+        if (e != hipSuccess) return device_fail(e, "hash ids launch");
+        e = moe::launch_hash_dots_beside(c, p->dtype, x, W, part, *beside, s);
+        if (e != hipSuccess) return device_fail(e, "hash dot products launch");
+        e = moe::launch_hash_tiles(c, token_ids, tid2eid, vocab, part, 0, Rk, ns, logit_bias,
+                                   ids, weights, dev_err, nullptr, nullptr, s);
+        if (e != hipSuccess) return device_fail(e, "hash route launch");
+        if (used_beside) *used_beside = true;
+        return MOE_OK;
+      }
       const bool tiles = hist && super_sum;
       e = moe::launch_hash_ids(c, token_ids, tid2eid, vocab, ids, s);
       if (e != hipSuccess) return device_fail(e, "hash ids launch");
@@ -581,6 +595,14 @@ int32_t hash_core(const moe_route_params* p, const int32_t* token_ids, const int
   return MOE_OK;
 }
 
+// Rows of counts for the dispatch placed beside the hash layer's dot
+// products (0 when that form does not apply to these shapes).
+size_t beside_rows_bytes(const moe_route_params* p) {
+  if (moe::hash_beside_places(to_cfg(p), p->dtype, true) < 1) return 0;
+  const int64_t R = (int64_t)p->T * p->k;
+  return (size_t)((R + moe::kBesideTile - 1) / moe::kBesideTile) * p->E * sizeof(int32_t);
+}
+
 // Tile histograms plus super-tile sums of moe_route_hash_dispatch.
 DispPlan hash_disp_plan(const moe_route_params* p) {
   DispPlan d;
@@ -618,8 +640,8 @@ size_t moe_route_hash_dispatch_workspace_size(const moe_route_params* p) {
   if ((int64_t)p->T * p->E > kI32Max) return 0;
   if (p->T == 0) return 0;
   const DispPlan d = hash_disp_plan(p);
-  const size_t disp = std::max(disp_ws_bytes(p, d),
-                               moe::dispatch_workspace_bytes(R, p->E));
+  const size_t disp = std::max({disp_ws_bytes(p, d), moe::dispatch_workspace_bytes(R, p->E),
+                                beside_rows_bytes(p)});
   return align256(hash_ws_bytes(p)) + disp;
 }
 
@@ -653,6 +675,34 @@ int32_t moe_route_hash_dispatch(const moe_route_params* p, const int32_t* token_
   }
   const size_t route = align256(hash_ws_bytes(p));
   void* disp_ws = static_cast<char*>(workspace) + route;
+  const bool aligned = reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
+                       reinterpret_cast<uintptr_t>(W) % 16 == 0;
+  const int n_place = moe::hash_beside_places(to_cfg(p), p->dtype, aligned);
+  if (n_place > 0 && beside_rows_bytes(p) > 0) {
+    // every tile's row of counts in the dispatch part of the workspace
+    moe::BesidePlace bp;
+    bp.ids = ids;
+    bp.R = R;
+    bp.E = p->E;
+    bp.nt = (int32_t)((R + moe::kBesideTile - 1) / moe::kBesideTile);
+    bp.n_place = n_place;
+    bp.rows = static_cast<const int32_t*>(disp_ws);
+    bp.counts = counts;
+    bp.offsets = offsets;
+    bp.perm = perm;
+    bp.inv = inv;
+    bp.maxvio = maxvio;
+    bp.n_dots = 0;
+    bool placed = false;
+    rc = hash_core(p, token_ids, tid2eid, vocab, x, W, logit_bias, ids, weights, workspace,
+                   route, dev_err, s, nullptr, nullptr, 0, nullptr, &bp, &placed);
+    if (rc != MOE_OK || placed) return rc;
+    // routed by another kernel (no dot products): the plain dispatch of its ids
+    e = moe::launch_dispatch(ids, R, p->E, counts, offsets, perm, inv, maxvio, disp_ws, dev_err,
+                             s);
+    if (e != hipSuccess) return device_fail(e, "dispatch launch");
+    return MOE_OK;
+  }
   const DispPlan dp = hash_disp_plan(p);
   moe::hist_t* hist = dp.mode == kSuper ? static_cast<moe::hist_t*>(disp_ws) : nullptr;
   int32_t* super_sum =
