@@ -389,7 +389,8 @@ typedef struct {
   int32_t gate_waves;              /* wavefronts per gate workgroup (4 or 8) */
   int32_t gate_splits;             /* K split: partial sum arrays */
   int32_t gate_stage_bytes;        /* bytes of each tile row per stage; 0: register-staged */
-  int32_t gate_ring_depth;         /* stages of the LDS ring */
+  int32_t gate_ring_depth;         /* stages of x in the LDS ring (of W too, except for
+                                      the largest tiles, whose W ring is one stage shorter) */
   int32_t gate_lds_bytes;          /* LDS of the ring */
   int32_t select_lanes;            /* lanes per token of the selection */
   int32_t select_experts_per_lane;

@@ -305,7 +305,10 @@ def test_gate_stage_lengths_exact(rb, tile, d, monkeypatch):
     # 64-byte stages, deep rings; some split their load blocks unevenly
     ("128x192w8", "64", "5"), ("128x192w8", "64", "8"), ("256x192w8", "64", "4"),
     ("128x384w8", "64", "5"), ("256x256w8", "64", "3"), ("256x128w8", "64", "6"),
-    ("64x64w8", "64", "7"), ("128x128w8", "64", "2")])
+    ("64x64w8", "64", "7"), ("128x128w8", "64", "2"),
+    # split rings: x three stages deep, W two (the tiles whose combined ring
+    # fits only two deep)
+    ("256x192w8", "128", "3/2"), ("128x384w8", "128", "3/2")])
 @pytest.mark.parametrize("splits", ["1", "2"])
 def test_gate_eight_wave_tiles_exact(tile, rb, ns, splits, monkeypatch):
     """Eight-wavefront tiles (4 x 2 or 2 x 4 waves) at each stage length and
@@ -314,8 +317,12 @@ def test_gate_eight_wave_tiles_exact(tile, rb, ns, splits, monkeypatch):
     monkeypatch.setenv("MOE_GATE_TILE", tile)
     monkeypatch.setenv("MOE_GATE_SPLITS", splits)
     monkeypatch.setenv("MOE_GATE_RB", rb)
-    monkeypatch.setenv("MOE_GATE_NS", ns)
-    rng = np.random.default_rng([len(tile), int(splits), int(rb), int(ns)])
+    if ns == "3/2":
+        monkeypatch.setenv("MOE_GATE_NSW", "2")
+    else:
+        monkeypatch.setenv("MOE_GATE_NS", ns)
+        monkeypatch.setenv("MOE_GATE_NSW", "0")
+    rng = np.random.default_rng([len(tile), int(splits), int(rb), len(ns)])
     T, E, d = 777, 420, 1480
     x = rng.integers(-3, 4, size=(T, d)).astype(np.float32)
     Wi = rng.integers(-3, 4, size=(E, d)).astype(np.float32)

@@ -337,13 +337,21 @@ struct FusedSel {
   static constexpr int kLpt = LPT, kVpl = VPL;
 };
 
-template <typename In, int BM, int BN, int NS, int RB, int WM, int WN, class EPI = NoSel>
+// NS: stages of x in the ring; NSW: stages of W.  With NSW == NS each stage
+// is one slot (the tile's x rows, then its W rows); with NSW == NS - 1 the x
+// and W rings are separate, so that a tile too large for NS slots of both
+// still keeps NS - 1 stages of x (the rows that come from HBM) in flight
+// while W, read from L2, runs one stage ahead.
+template <typename In, int BM, int BN, int NS, int RB, int WM, int WN, class EPI, int NSW>
 __global__ __launch_bounds__(WM * WN * kWave) void gate_gemm_pipe_kernel(
     const In* __restrict__ x, const In* __restrict__ W, const float* __restrict__ logit_bias,
     float* __restrict__ out, int T, int d, int E, int n_m, int n_n, int splits, int per_xcd,
     int stages_per_split, SelectArgs sa) {
   constexpr int ROWS = BM + BN;
   constexpr int STAGE = ROWS * RB;             // bytes per stage
+  constexpr bool SPLIT_RING = NSW != NS;
+  static_assert(NSW == NS || NSW == NS - 1, "W ring depth");
+  constexpr int LDS_BYTES = NS * BM * RB + NSW * BN * RB;
   constexpr int RPI = 1024 / RB;               // rows per load instruction
   constexpr int CPR = RB / 16;                 // 16-byte chunks per row and stage
   constexpr int NW = WM * WN;                  // waves: WM along M x WN along N
@@ -356,9 +364,22 @@ __global__ __launch_bounds__(WM * WN * kWave) void gate_gemm_pipe_kernel(
   static_assert(RB == 64 || RB == 128 || RB == 256 || RB == 512, "stage row bytes");
   static_assert(BM % (16 * WM) == 0 && BN % (16 * WN) == 0 && ROWS % RPI == 0, "tile shape");
   static_assert(NS >= 2 && (NS - 2) * LPS < 64, "pipeline depth");
+  // split rings: whole 1-KB blocks of x and of W for every wave
+  constexpr int LX = BM / RPI / NW, LW = BN / RPI / NW;
+  static_assert(!SPLIT_RING || (NSW >= 2 && LX * NW * RPI == BM && LW * NW * RPI == BN &&
+                                LX + (NSW - 2) * (LX + LW) < 64),
+                "split ring shape");
   typedef typename Frag<In>::type FragT;
 
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
+  // ring slots of stage st (counted from st_begin): x rows, then W rows
+  auto x_slot = [&](int st) -> uint8_t* {
+    return SPLIT_RING ? lds + (st % NS) * (BM * RB) : lds + (st % NS) * STAGE;
+  };
+  auto w_slot = [&](int st) -> uint8_t* {
+    return SPLIT_RING ? lds + NS * BM * RB + (st % NSW) * (BN * RB)
+                      : lds + (st % NS) * STAGE + BM * RB;
+  };
 
   if (sa.zero_words > 0) {  // a slice of the array the next kernel adds into
     const int per = (sa.zero_words + (int)gridDim.x - 1) / (int)gridDim.x;
@@ -418,13 +439,19 @@ __global__ __launch_bounds__(WM * WN * kWave) void gate_gemm_pipe_kernel(
   // expert tiles (x re-read from L2) or a large W it was slower (DeepSeek-
   // V3-like 41 -> 46 us), so the other shapes keep the default policy.
   constexpr int kXPolicy = EPI::kOn ? 2 : 0;
-  auto issue = [&](int st) {  // st counts from st_begin
-    uint8_t* buf = lds + ((st - st_begin) % NS) * STAGE;
+  // copies of stage st (counted from st_begin) of x (X) and of W (!X) rows;
+  // blocks of the combined ring are the stage's x rows, then its W rows
+  auto issue_part = [&](int st, bool X) {  // X: a constant at every call
     const uint32_t koff = st < st_end ? (uint32_t)st * RB : 0x80000000u;
 #pragma unroll
     for (int i = 0; i < LPS; ++i) {
       if (i == LPS - 1 && !full) break;  // wave-uniform
-      auto* dst = (__attribute__((address_space(3))) void*)(buf + (wave + NW * i) * 1024);
+      if (SPLIT_RING && (i < LX) != X) continue;
+      const int blk = wave + NW * i;
+      uint8_t* dst8 = SPLIT_RING ? (X ? x_slot(st - st_begin) + blk * 1024
+                                      : w_slot(st - st_begin) + (blk - LX * NW) * 1024)
+                                 : x_slot(st - st_begin) + blk * 1024;
+      auto* dst = (__attribute__((address_space(3))) void*)dst8;
       const bool live = (src_off[i] | koff) < 0x80000000u && koff + chunk_b[i] < row_bytes;
       const uint32_t off = live ? src_off[i] + koff : 0x80000000u;
       if (src_is_x[i])
@@ -433,9 +460,23 @@ __global__ __launch_bounds__(WM * WN * kWave) void gate_gemm_pipe_kernel(
         __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, dst, 16, off, 0, 0, 0);
     }
   };
-  // each wave waits for its own copies: NS - 2 later stages may stay in flight
+  // the copies that refill the slots of the stage all waves just finished:
+  // stage st of x, and (split rings) stage st - (NS - NSW) of W, issued first
+  auto issue = [&](int st) {
+    if constexpr (SPLIT_RING) {
+      if (st - (NS - NSW) >= st_begin) issue_part(st - (NS - NSW), false);
+      issue_part(st, true);
+    } else {
+      issue_part(st, true);
+    }
+  };
+  // each wave waits for its own copies: the stages issued after the one about
+  // to be read may stay in flight (combined ring: NS - 2 stages; split rings:
+  // that refill's x stage, then NSW - 2 refills of W and x)
   auto barrier = [&]() {
-    if (full)
+    if constexpr (SPLIT_RING)
+      stage_barrier<LX + (NSW - 2) * (LX + LW)>();
+    else if (full)
       stage_barrier<(NS - 2) * LPS>();
     else
       stage_barrier<(NS - 2) * LPS_SHORT>();
@@ -451,19 +492,19 @@ __global__ __launch_bounds__(WM * WN * kWave) void gate_gemm_pipe_kernel(
   const int kq = lane >> 4;
   const int sw = stage_swizzle<RB>(row16);  // swz of every row this lane reads
   const int a_row = wm * (BM / WM) + row16;
-  const int b_row = BM + wn * (BN / WN) + row16;
+  const int b_row = wn * (BN / WN) + row16;  // within the stage's W rows
 
   // Operand fragments of one k-step, double-buffered so that the LDS reads
   // of the next k-step are in flight while this one's MFMAs run.
   FragT fa[2][MB], fb[2][NB];
-  auto load = [&](int p, const uint8_t* buf, int ks) {
+  auto load = [&](int p, const uint8_t* xb, const uint8_t* wb, int ks) {
     const int slot = ((ks * 4 + kq) ^ sw) * 16;
 #pragma unroll
     for (int i = 0; i < MB; ++i)
-      fa[p][i] = *reinterpret_cast<const FragT*>(buf + (a_row + i * 16) * RB + slot);
+      fa[p][i] = *reinterpret_cast<const FragT*>(xb + (a_row + i * 16) * RB + slot);
 #pragma unroll
     for (int j = 0; j < NB; ++j)
-      fb[p][j] = *reinterpret_cast<const FragT*>(buf + (b_row + j * 16) * RB + slot);
+      fb[p][j] = *reinterpret_cast<const FragT*>(wb + (b_row + j * 16) * RB + slot);
   };
   auto mma = [&](int p) {
     if constexpr (sizeof(In) == 2) {
@@ -491,19 +532,20 @@ __global__ __launch_bounds__(WM * WN * kWave) void gate_gemm_pipe_kernel(
   // so the fragment arrays stay in registers).
   auto run_stage = [&](int s, auto p0) {
     constexpr int P0 = decltype(p0)::value;
-    const uint8_t* buf = lds + ((s - st_begin) % NS) * STAGE;
+    const uint8_t* xb = x_slot(s - st_begin);
+    const uint8_t* wb = w_slot(s - st_begin);
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
       const int p = (P0 + ks) & 1;
       if (ks + 1 < KSTEPS) {
-        load(p ^ 1, buf, ks + 1);
+        load(p ^ 1, xb, wb, ks + 1);
       } else if (s + 1 < st_end) {
         // stage s + 1 is in LDS and every wave has read all of stage s (this
         // wave's last reads included): refill stage s's buffer, then read the
         // next stage's first k-step behind this one's MFMAs
         barrier();
         issue(s + NS);
-        load(p ^ 1, lds + ((s + 1 - st_begin) % NS) * STAGE, 0);
+        load(p ^ 1, x_slot(s + 1 - st_begin), w_slot(s + 1 - st_begin), 0);
       }
       __builtin_amdgcn_sched_barrier(0);
       mma(p);
@@ -515,7 +557,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void gate_gemm_pipe_kernel(
     for (int st = 0; st < NS - 1; ++st) issue(st_begin + st);
     barrier();                  // stage st_begin is in LDS
     issue(st_begin + NS - 1);   // into the one buffer not yet used
-    load(0, lds, 0);
+    load(0, x_slot(0), w_slot(0), 0);
     if constexpr (KSTEPS % 2 == 0) {
       for (int s = st_begin; s < st_end; ++s) run_stage(s, std::integral_constant<int, 0>());
     } else {  // one k-step per stage: the buffers alternate between stages
@@ -535,7 +577,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void gate_gemm_pipe_kernel(
   // groups of one accumulator write hit different banks.
   constexpr int PITCH = BN + 4;                         // floats
   constexpr int WROWS = BM / WM;                        // rows of one wave row
-  constexpr int G = NS * STAGE / (WROWS * PITCH * 4);   // wave rows per pass
+  constexpr int G = LDS_BYTES / (WROWS * PITCH * 4);    // wave rows per pass
   static_assert(!EPI::kOn || G >= WM, "the fused selection needs the whole tile in LDS");
   if constexpr (G >= 1) {
     constexpr int GP = G < WM ? G : WM;
@@ -597,7 +639,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void gate_gemm_pipe_kernel(
       constexpr int TPP = NW * (kWave / EPI::kLpt);
       constexpr int PICK_OFF = BM * PITCH * 4;
       constexpr int HIST_OFF = PICK_OFF + TPP * sel::kMaxK * 4;
-      static_assert(HIST_OFF + NW * kFusedMaxE * 4 <= NS * STAGE, "fused scratch in the ring");
+      static_assert(HIST_OFF + NW * kFusedMaxE * 4 <= LDS_BYTES, "fused scratch in the ring");
       fused_select<EPI, BM, NW, PITCH>(lo, reinterpret_cast<int32_t(*)[sel::kMaxK]>(lds + PICK_OFF),
                                        reinterpret_cast<int32_t(*)[kFusedMaxE]>(lds + HIST_OFF),
                                        m0, T, lane, wave, mt, sa);
@@ -619,7 +661,8 @@ __global__ __launch_bounds__(WM * WN * kWave) void gate_gemm_pipe_kernel(
   }
 }
 
-template <typename In, int BM, int BN, int NS, int RB, int WM, int WN, class EPI = NoSel>
+template <typename In, int BM, int BN, int NS, int RB, int WM, int WN, class EPI = NoSel,
+          int NSW = NS>
 hipError_t launch_pipe(const void* x, const void* W, const float* logit_bias, float* out,
                        int T, int d, int E, int splits, hipStream_t s,
                        const SelectArgs& sa = SelectArgs{}) {
@@ -630,7 +673,7 @@ hipError_t launch_pipe(const void* x, const void* W, const float* logit_bias, fl
   const int tiles = n_m * n_n * splits;
   const int per_xcd = (tiles + kXcds - 1) / kXcds;
   return launch(EPI::kOn ? kStageGateSelect : kStageGate,
-                gate_gemm_pipe_kernel<In, BM, BN, NS, RB, WM, WN, EPI>, dim3(per_xcd * kXcds),
+                gate_gemm_pipe_kernel<In, BM, BN, NS, RB, WM, WN, EPI, NSW>, dim3(per_xcd * kXcds),
                 dim3(WM * WN * kWave), s, (const In*)x, (const In*)W, logit_bias, out, T, d, E,
                 n_m, n_n, splits, per_xcd, per_split, sa);
 }
@@ -696,6 +739,24 @@ hipError_t launch_depth(const void* x, const void* W, const float* lb, float* ou
   return hipErrorInvalidValue;
 }
 
+// Split rings (x three stages deep, W two) for the eight-wave tiles whose
+// combined ring fits only two stages deep in the LDS budget: every wave
+// copies whole 1-KB blocks of x and of W.
+constexpr bool split_ring_ok(int bm, int bn, int rb, int waves) {
+  const int rpi = 1024 / rb;
+  return waves == 8 && rb == 128 && bm % (rpi * waves) == 0 && bn % (rpi * waves) == 0 &&
+         (3 * bm + 2 * bn) * rb <= kLdsBudget && 3 * (bm + bn) * rb > kLdsBudget;
+}
+
+template <typename In, int BM, int BN, int RB, int WM, int WN>
+hipError_t launch_split(const void* x, const void* W, const float* lb, float* out, int T,
+                        int d, int E, int splits, hipStream_t s, const SelectArgs& sa) {
+  if constexpr (split_ring_ok(BM, BN, RB, WM * WN))
+    return launch_pipe<In, BM, BN, 3, RB, WM, WN, NoSel, 2>(x, W, lb, out, T, d, E, splits, s,
+                                                            sa);
+  return hipErrorInvalidValue;
+}
+
 // Ring depths 2..4; 64-byte stages (the deep rings of large tiles) also 5..8.
 template <typename In, int BM, int BN, int RB, int WM, int WN>
 hipError_t launch_rb(const GatePlan& g, const void* x, const void* W, const float* lb,
@@ -711,7 +772,10 @@ hipError_t launch_rb(const GatePlan& g, const void* x, const void* W, const floa
   }
   switch (g.ns) {
     case 4: return launch_depth<In, BM, BN, 4, RB, WM, WN>(x, W, lb, out, T, d, E, g.splits, s, sa);
-    case 3: return launch_depth<In, BM, BN, 3, RB, WM, WN>(x, W, lb, out, T, d, E, g.splits, s, sa);
+    case 3:
+      if (g.nsw == 2)
+        return launch_split<In, BM, BN, RB, WM, WN>(x, W, lb, out, T, d, E, g.splits, s, sa);
+      return launch_depth<In, BM, BN, 3, RB, WM, WN>(x, W, lb, out, T, d, E, g.splits, s, sa);
     default: return launch_depth<In, BM, BN, 2, RB, WM, WN>(x, W, lb, out, T, d, E, g.splits, s, sa);
   }
 }
@@ -887,6 +951,13 @@ void choose_ring(GatePlan& g, long wgs) {
       if (depth_ok(g.bm, g.bn, ns, 128, 8) && ns * (g.bm + g.bn) * 128 <= budget) {
         g.rb = 128;
         g.ns = ns;
+        // two stages of a large tile leave one stage of x in flight: the
+        // loop then waits on each stage's round trip (DeepSeek-V4-like gate,
+        // 256 x 192); x three deep and W two deep keep two x stages in flight
+        if (ns == 2 && budget == kLdsBudget && split_ring_ok(g.bm, g.bn, 128, 8)) {
+          g.ns = 3;
+          g.nsw = 2;
+        }
         return;
       }
     g.rb = 64;
@@ -972,14 +1043,26 @@ GatePlan plan_gate(int32_t T, int32_t d, int32_t E, int32_t dtype, bool aligned,
   if (const char* env = std::getenv("MOE_GATE_RB")) {
     const int rb = std::atoi(env);
     if ((rb == 128 || rb == 256 || rb == 512 || (rb == 64 && waves == 8)) &&
-        depth_ok(g.bm, g.bn, 2, rb, waves))
+        depth_ok(g.bm, g.bn, 2, rb, waves)) {
       g.rb = rb;
+      g.nsw = 0;
+    }
   }
   if (const char* env = std::getenv("MOE_GATE_NS")) {
     const int ns = std::atoi(env);
-    if (ns >= 2 && ns <= (g.rb == 64 ? 8 : 4)) g.ns = ns;
+    if (ns >= 2 && ns <= (g.rb == 64 ? 8 : 4)) {
+      g.ns = ns;
+      g.nsw = 0;
+    }
   }
-  if (!depth_ok(g.bm, g.bn, g.ns, g.rb, waves)) g.ns = 2;
+  if (const char* env = std::getenv("MOE_GATE_NSW")) {  // tuning: 0 one ring, 2 split
+    g.nsw = 0;
+    if (std::atoi(env) == 2 && split_ring_ok(g.bm, g.bn, g.rb, waves)) {
+      g.ns = 3;
+      g.nsw = 2;
+    }
+  }
+  if (g.nsw == 0 && !depth_ok(g.bm, g.bn, g.ns, g.rb, waves)) g.ns = 2;
   return g;
 }
 

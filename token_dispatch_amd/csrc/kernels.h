@@ -64,6 +64,7 @@ struct GatePlan {
   int bm, bn, ns, rb, splits;
   int wm = 2, wn = 2;
   bool pipe;
+  int nsw = 0;  // stages of W in the ring when fewer than of x (0: ns, one ring)
 };
 GatePlan plan_gate(int32_t T, int32_t d, int32_t E, int32_t dtype, bool aligned,
                    bool allow_split);

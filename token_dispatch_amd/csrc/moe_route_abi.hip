@@ -461,7 +461,7 @@ int32_t moe_route_dispatch_plan(const moe_route_params* p, int32_t aligned,
   out->gate_splits = g.pipe ? g.splits : 1;
   out->gate_stage_bytes = g.pipe ? g.rb : 0;
   out->gate_ring_depth = g.pipe ? g.ns : 2;
-  out->gate_lds_bytes = g.pipe ? g.ns * (g.bm + g.bn) * g.rb : 0;
+  out->gate_lds_bytes = g.pipe ? (g.ns * g.bm + (g.nsw > 0 ? g.nsw : g.ns) * g.bn) * g.rb : 0;
   moe::select_shape(c, &out->select_lanes, &out->select_experts_per_lane);
   if (p->T == 0) {
     out->path = MOE_PATH_SEPARATE;
