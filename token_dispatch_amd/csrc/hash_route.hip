@@ -222,7 +222,13 @@ __global__ __launch_bounds__(NW * kWave) void hash_dots_kernel(
     float* __restrict__ part, int32_t* __restrict__ zero, int zero_words, int ns,
     BesidePlace place) {
   constexpr int PC = SL / 8;                     // 16-byte pieces per row slice
-  constexpr int PITCH = PC + 1;                  // pieces per LDS row
+  // Pieces per LDS row.  The two tokens of a 16-lane LDS cycle read 128 bytes
+  // each from two unrelated W rows: rows of an odd number of 128-byte lines
+  // start in alternate halves of the 64 banks, so only rows of the same
+  // parity collide (a one-piece pad made nearly every pair overlap: 54 % of
+  // the kernel's LDS cycles were bank conflicts on the DeepSeek-V4-like
+  // layer); other widths keep the pad.
+  constexpr int PITCH = (PC % 16 == 8) ? PC : PC + 1;
   constexpr int TPW = kWave / L;                 // tokens per wave and tile
   constexpr int TPT = NW * TPW;                  // tokens per tile
   constexpr int CPL = (PC + L - 1) / L;          // pieces per lane
@@ -273,7 +279,7 @@ __global__ __launch_bounds__(NW * kWave) void hash_dots_kernel(
 #pragma unroll
     for (int q = 0; q < CPL; ++q) {
       const int col = min(col0 + (q * L + r) * 8, d - 8);
-      v[q] = *reinterpret_cast<const u32x4_t*>(x + t * d + col);
+      v[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(x + t * d + col));
     }
   };
   auto load_e = [&](int i, int (&ev)[EPL]) {
@@ -704,7 +710,7 @@ const void* dots_kernel(int sl, int32_t E) {
   if (sl == 192 && E <= 384) return k(hash_dots_kernel<192, 384, 8, kDotWaves, 3, PLACE>);
   if (sl == 128 && E <= 384) return k(hash_dots_kernel<128, 384, 8, kDotWaves, 3, PLACE>);
   if (sl == 112 && E <= 384) return k(hash_dots_kernel<112, 384, 8, kDotWaves, 3, PLACE>);
-  if constexpr (!PLACE)  // its 55 KB W slice holds no placement's LDS
+  if constexpr (!PLACE)  // its 48 KB W slice holds no placement's LDS
     if (sl == 64 && E <= 384) return k(hash_dots_kernel<64, 384, 8, kDotWaves, 3, PLACE>);
   if (sl == 64 && E <= 768) return k(hash_dots_kernel<64, 768, 8, kDotWaves, 3, PLACE>);
   return nullptr;
