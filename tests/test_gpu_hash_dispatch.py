@@ -84,6 +84,8 @@ def test_hash_scores_ragged_and_duplicates(score, dtype, gate):
     (1000, 7168, 384, 6, False, None),  # DeepSeek-V4-like rows: 38 slices of 192 columns,
                                         # the last one 64 wide
     (1000, 7168, 384, 6, False, "128"),  # 56 slices of 128 columns
+    (2000, 2880, 128, 4, True, None),   # k = 4 compiled in (192-column slices)
+    (900, 2880, 200, 5, True, None),    # k only at run time (192-column slices)
     (500, 1000, 500, 8, True, None),    # 64-column slices (E > 384), a partial last slice
     (500, 1000, 300, 8, True, "64"),    # 64-column slices below 384 experts
     (70000, 200, 64, 3, False, None),   # 2 slices (the second 8 wide) x 128 token chunks
