@@ -155,6 +155,9 @@ def test_route_dispatch_empty():
     (1777, 124, "128x128w8", "4", "softmax", False, True),         # ragged T and E, padded tile
     (16500, 128, "256x128w8", "3", "sqrt_softplus", True, False),  # 8 lanes x 16
     (16500, 128, "128x128w8", "4", "softmax", False, True),
+    # k = 4 compiled into the 256-row tiles' selection, tokens asking 1-4
+    (2000, 128, "256x128w8", "3", "softmax_topk", False, "k4"),
+    (16500, 128, "256x128w8", "3", "softmax", False, "k4"),
 ])
 def test_fused_gate_select_matches_separate_kernels(T, E, tile, ns, score, bias_groups, dynk,
                                                     monkeypatch):
@@ -167,13 +170,14 @@ def test_fused_gate_select_matches_separate_kernels(T, E, tile, ns, score, bias_
     monkeypatch.setenv("MOE_GATE_RB", "128")
     monkeypatch.setenv("MOE_GATE_NS", ns)
     rng = np.random.default_rng([T, E])
-    d, k = 1024, (8 if dynk else 4)
+    d, k = 1024, (8 if dynk is True else 4)
     x = rng.standard_normal((T, d)).astype(np.float32)
     Wf = (rng.standard_normal((E, d)) / np.sqrt(d)).astype(np.float32)
     xb, Wb = wl.f32_to_bf16_bits(x), wl.f32_to_bf16_bits(Wf)
     lb = (0.1 * rng.standard_normal(E)).astype(np.float32)
     sb = (0.01 * rng.standard_normal(E)).astype(np.float32) if bias_groups else None
-    kpt = rng.choice([2, 4, 8], size=T).astype(np.int32) if dynk else None
+    kpt = (rng.choice([2, 4, 8], size=T).astype(np.int32) if dynk is True else
+           rng.integers(1, 5, size=T).astype(np.int32) if dynk == "k4" else None)
     rkw = dict(score=score, select_bias=sb, k_per_token=kpt,
                n_groups=4 if bias_groups else 1, topk_groups=2 if bias_groups else None,
                group_score="top2_sum" if bias_groups else None, renormalize=True,

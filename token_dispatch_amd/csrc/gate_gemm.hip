@@ -309,7 +309,7 @@ __device__ __forceinline__ void fused_select(const float* lo, int32_t (*pick)[se
     for (int j = 0; j < VPL; ++j) lv[j] = (tok_ok && j < nval) ? row[e0 + j] : -INFINITY;
     const int kraw = sa.k_per_token ? sa.k_per_token[trow] : sa.c.k;
     int pid[KPL];
-    sel::select_token<LPT, VPL, EPI::kMono>(sa.c, sl, seg, tok_ok, t, lv, nval, sb, kraw, row,
+    sel::select_token<LPT, VPL, EPI::kMono, EPI::kK>(sa.c, sl, seg, tok_ok, t, lv, nval, sb, kraw, row,
                                             pick[wave * TPW + seg], sa.ids, sa.weights,
                                             sa.dev_err, pid);
     if constexpr (EPI::kHist) sel::count_picks<LPT, kFusedIdBits>(pid, sl, sa.c.k, whist[wave]);
@@ -331,10 +331,10 @@ __device__ __forceinline__ void fused_select(const float* lo, int32_t (*pick)[se
 struct NoSel {
   static constexpr bool kOn = false;
 };
-template <int LPT, int VPL, bool MONO, bool HIST>
+template <int LPT, int VPL, bool MONO, bool HIST, int KC = 0>
 struct FusedSel {
   static constexpr bool kOn = true, kMono = MONO, kHist = HIST;
-  static constexpr int kLpt = LPT, kVpl = VPL;
+  static constexpr int kLpt = LPT, kVpl = VPL, kK = KC;  // kK > 0: k == kK
 };
 
 // NS: stages of x in the ring; NSW: stages of W.  With NSW == NS each stage
@@ -1081,6 +1081,17 @@ template <int BM, int BN, int WM, int WN, int NS, int RB, int LPT, int VPL>
 hipError_t launch_fused_shape(bool mono, bool hist, const void* x, const void* W,
                               const float* lb, float* logits, int T, int d, int E,
                               const SelectArgs& sa, hipStream_t s) {
+  // k = 4 compiled into the selection of the 256-row tiles' monotone case
+  // (top-4 over raw or softmax scores, as gpt-oss routes); other k at run time
+  if constexpr (BM == 256) {
+    if (mono && sa.c.k == 4) {
+      if (hist)
+        return launch_pipe<uint16_t, BM, BN, NS, RB, WM, WN, FusedSel<LPT, VPL, true, true, 4>>(
+            x, W, lb, logits, T, d, E, 1, s, sa);
+      return launch_pipe<uint16_t, BM, BN, NS, RB, WM, WN, FusedSel<LPT, VPL, true, false, 4>>(
+          x, W, lb, logits, T, d, E, 1, s, sa);
+    }
+  }
 #define MOE_F(M_, H_)                                                                   \
   if (mono == M_ && hist == H_)                                                         \
     return launch_pipe<uint16_t, BM, BN, NS, RB, WM, WN, FusedSel<LPT, VPL, M_, H_>>(   \

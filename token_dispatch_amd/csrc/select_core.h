@@ -184,8 +184,11 @@ __device__ __forceinline__ void load_sbias(const float* __restrict__ select_bias
 // (the picks' logits are read back from it); pick: kMaxK ints of LDS for the
 // token.  Writes ids[t][*] and weights[t][*] and leaves in pid the experts
 // this lane wrote (ranks sl, sl + LPT, ...; -1: none).  Every lane of the
-// wavefront takes part.
-template <int LPT, int VPL, bool MONO>
+// wavefront takes part.  KC > 0: k == KC, known when compiling -- the rounds
+// are unrolled and the weights' slot loops fold (the fused gate + selection
+// at k = 4: selection 11.4 -> 8.8 us of its 74-77 us); a token whose k_t is
+// below KC gets no pick in its later rounds (r < k_t fails there).
+template <int LPT, int VPL, bool MONO, int KC = 0>
 __device__ __forceinline__ void select_token(
     const RouteCfg& c, int sl, int seg, bool tok_ok, int64_t t, const float (&lv)[VPL],
     int nval, const float (&sb)[VPL], int kraw, const float* lrow, int32_t* pick,
@@ -193,7 +196,7 @@ __device__ __forceinline__ void select_token(
     int (&pid)[(kMaxK + LPT - 1) / LPT]) {
   using S = Seg<LPT>;
   constexpr int KPL = (kMaxK + LPT - 1) / LPT;  // output slots per lane
-  const int E = c.E, K = c.k;
+  const int E = c.E, K = KC > 0 ? KC : c.k;
   const int e0 = sl * VPL;
   const bool need_full_softmax = c.score == kSoftmax && (!MONO || !c.renormalize);
 
@@ -309,7 +312,13 @@ __device__ __forceinline__ void select_token(
   const int g_lo = sl * gsz;  // this lane's group: experts [g_lo, g_lo + gsz)
   int gcount = 0;
 
-  for (int r = 0; r < k_rounds; ++r) {
+  // KC == 0: k_rounds rounds, the loop as it was compiled before the
+  // compile-time case existed (unrolling or outlining it slowed the select
+  // kernel); KC > 0: KC rounds, unrolled.
+  constexpr int kUnroll = KC > 0 ? KC : 1;
+  const int n_rounds = KC > 0 ? KC : k_rounds;
+#pragma unroll kUnroll
+  for (int r = 0; r < n_rounds; ++r) {
     uint32_t head = key[0];
     int hs = 0;
 #pragma unroll
