@@ -30,7 +30,9 @@
  *    is fixed per plan; plans are chosen from the shapes.  For tuning, these
  *    environment variables override the choice: MOE_GATE_TILE ("BMxBN", or
  *    "BMxBNw8" for eight wavefronts), MOE_GATE_SPLITS (1-8), MOE_GATE_RB
- *    (64/128/256/512-byte stages), MOE_GATE_NS (ring depth), MOE_GATE_NOPIPE
+ *    (64/128/256/512-byte stages), MOE_GATE_NS (ring depth), MOE_GATE_NSW
+ *    (0: one ring of x and W stages; 2: W two stages deep under three of x,
+ *    where the tile fits that), MOE_GATE_NOPIPE
  *    (the register-staged gate kernel), MOE_SELECT_LPT (4/8/16/64 lanes per
  *    token), MOE_NO_FUSED_SELECT (selection in its own kernel),
  *    MOE_DISPATCH_UNFUSED (the three-kernel dispatch), MOE_DISPATCH_NO_SUPER
@@ -40,8 +42,10 @@
  *    selection + dispatch for small batches), MOE_HASH_DENSE (hash layers
  *    take the gate of every expert instead of k dot products per token),
  *    MOE_HASH_SLICE (64, up to 384 experts also 112/128/192 columns per
- *    dot-product slice), MOE_PLACE_GROUP (1/2/4/8 dispatch tiles per
- *    placement workgroup).  Values that do not fit the shapes are ignored;
+ *    dot-product slice), MOE_HASH_BESIDE (0: the hash layer's dispatch in
+ *    its own placement kernel; 1: on the dot-product kernel's spare
+ *    workgroups whenever possible), MOE_PLACE_GROUP (1/2/4/8 dispatch tiles
+ *    per placement workgroup).  Values that do not fit the shapes are ignored;
  *    workspace sizes follow the same variables.
  */
 #ifndef MOE_ROUTE_H
